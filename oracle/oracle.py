@@ -1,0 +1,148 @@
+"""ctypes front end of ``pkm_oracle.c`` (the plain fp64 CPU oracle).
+
+TEST INFRASTRUCTURE ONLY: only the test suite, the smoke check and the CPU
+baseline leg of the benchmark may import this module.  The arithmetic lives in
+``pkm_oracle.c``; this file only marshals numpy arrays.
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "pkm_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+VALUE_TYPES = {"f32": 0, "bf16": 1, "e4m3": 2}
+
+
+def lib_path():
+    return _LIB
+
+
+def build():
+    """Compile the oracle with gcc: -O2, no -ffast-math, so every fp64 sum
+    keeps the order written in the source."""
+    compile_source(_SRC, _LIB + ".tmp")
+    os.replace(_LIB + ".tmp", _LIB)
+    global _lib
+    _lib = None
+    return _LIB
+
+
+class _Model(ctypes.Structure):
+    _fields_ = [
+        ("D", ctypes.c_int32), ("H", ctypes.c_int32), ("n", ctypes.c_int32), ("k", ctypes.c_int32),
+        ("value_type", ctypes.c_int32), ("pad_", ctypes.c_int32), ("eps", ctypes.c_double),
+        ("wq", ctypes.c_void_p), ("mean", ctypes.c_void_p), ("var", ctypes.c_void_p),
+        ("gamma", ctypes.c_void_p), ("beta", ctypes.c_void_p), ("subkeys", ctypes.c_void_p),
+        ("values", ctypes.c_void_p), ("scale", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def load_library(path):
+    """Open a compiled oracle (the default one, or a variant built from an
+    edited copy of the source by the tests that check the pins)."""
+    lib = ctypes.CDLL(path)
+    lib.pkmo_run.restype = ctypes.c_int
+    lib.pkmo_run.argtypes = [ctypes.POINTER(_Model), ctypes.c_int64, ctypes.c_void_p, ctypes.c_int] + \
+        [ctypes.c_void_p] * 6 + [ctypes.c_int]
+    lib.pkmo_bf16_to_f64.restype = ctypes.c_double
+    lib.pkmo_bf16_to_f64.argtypes = [ctypes.c_uint16]
+    lib.pkmo_e4m3_to_f64.restype = ctypes.c_double
+    lib.pkmo_e4m3_to_f64.argtypes = [ctypes.c_uint8]
+    return lib
+
+
+def compile_source(src, out):
+    """gcc -O2 (no -ffast-math: every fp64 sum keeps its source order)."""
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-Wall", "-shared", "-fPIC", "-pthread", src, "-o", out, "-lm"])
+    return out
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        _lib = load_library(_LIB)
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a)
+    assert a.dtype == dtype, (a.dtype, dtype)
+    return a
+
+
+class Model:
+    """The lookup's parameters as the oracle reads them (numpy, host memory).
+
+    wq [H,D,D] f32 (row f = output feature f), mean/var/gamma/beta [H,D] f32,
+    subkeys [H,2,n,D/2] f32, values [n*n,D] as f32 / uint16 (bf16 bits) /
+    uint8 (E4M3 bits), scale [n*n] f32 for E4M3 tables.
+    """
+
+    def __init__(self, wq, mean, var, gamma, beta, subkeys, values, scale, k, table, eps=1e-5):
+        H, D, D2 = wq.shape
+        assert D == D2 and D % 2 == 0
+        n = subkeys.shape[2]
+        assert subkeys.shape == (H, 2, n, D // 2)
+        self.H, self.D, self.n, self.k, self.table, self.eps = H, D, n, int(k), table, float(eps)
+        vt = np.dtype({"f32": np.float32, "bf16": np.uint16, "e4m3": np.uint8}[table])
+        self._keep = [
+            _c(wq, np.float32), _c(mean, np.float32), _c(var, np.float32), _c(gamma, np.float32),
+            _c(beta, np.float32), _c(subkeys, np.float32), _c(values, vt),
+            None if scale is None else _c(scale, np.float32),
+        ]
+        assert self._keep[6].shape == (n * n, D)
+        if table == "e4m3":
+            assert self._keep[7] is not None and self._keep[7].shape == (n * n,)
+        k_ = self._keep
+        self._s = _Model(D, H, n, int(k), VALUE_TYPES[table], 0, float(eps), *[_ptr(a) for a in k_])
+
+    @classmethod
+    def from_params(cls, p, k, table, eps=1e-5):
+        return cls(p["wq"], p["mean"], p["var"], p["gamma"], p["beta"], p["subkeys"], p["values"],
+                   p.get("scale"), k, table, eps)
+
+
+def run(model, x, kk=None, want=("out", "idx", "top", "w"), nthreads=None, lib=None):
+    """Run the oracle over every row of x [B,D] (f32).
+
+    kk is the search depth (default: the model's k).  Returns a dict with the
+    requested arrays among out [B,D] f64, idx [B,H,kk] i32, top [B,H,kk] f64,
+    w [B,H,kk] f64, qhat [B,H,D] f64, ncand [B,H] i32.
+    """
+    lib = lib or _load()
+    x = _c(x, np.float32)
+    B = x.shape[0]
+    assert x.shape == (B, model.D)
+    kk = model.k if kk is None else int(kk)
+    H, D = model.H, model.D
+    shapes = {"out": ((B, D), np.float64), "idx": ((B, H, kk), np.int32), "top": ((B, H, kk), np.float64),
+              "w": ((B, H, kk), np.float64), "qhat": ((B, H, D), np.float64), "ncand": ((B, H), np.int32)}
+    res = {name: np.empty(*shapes[name]) for name in want}
+    if nthreads is None:
+        nthreads = len(os.sched_getaffinity(0))
+    rc = lib.pkmo_run(ctypes.byref(model._s), B, _ptr(x), kk, *[_ptr(res.get(nm)) for nm in
+                      ("out", "idx", "top", "w", "qhat", "ncand")], int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return res
+
+
+def bf16_to_f64(bits, lib=None):
+    return (lib or _load()).pkmo_bf16_to_f64(int(bits))
+
+
+def e4m3_to_f64(bits, lib=None):
+    return (lib or _load()).pkmo_e4m3_to_f64(int(bits))

@@ -1,0 +1,243 @@
+"""Pins of the fp64 oracle to things other than itself.
+
+Each ``pin_*`` function raises AssertionError when the oracle (the default
+build, or a variant passed as ``lib``) disagrees with:
+  - library routines that define a step: torch's Linear, BatchNorm1d
+    (inference), softmax and embedding_bag(mode="sum", per_sample_weights),
+    the bf16 / float8_e4m3fn casts;
+  - the flat exact search the "Product-Key Memory" page contrasts the method
+    with (§Factorising the key space): every one of the N = n_keys^2
+    concatenated keys (c0_a, c1_b) is scored with one full-length dot product
+    and the best k kept -- the page's exactness argument says the product
+    search must return the same winners;
+  - hand-worked closed forms (tests/golden/hand_example.json) and the page's
+    operation counts (tests/golden/op_counts.json);
+  - special cases: k = n_keys (every key is a candidate), k = 1 (argmax of
+    each half), exact integer ties (lower index wins).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+import oracle
+import synthetic
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def dequant_table(values, scale, table):
+    """fp64 copy of a stored table, decoded by torch's own casts."""
+    if table == "f32":
+        return torch.from_numpy(values).double()
+    if table == "bf16":
+        return torch.from_numpy(values.view(np.int16)).view(torch.bfloat16).double()
+    v = torch.from_numpy(values).view(torch.float8_e4m3fn).double()
+    return v * torch.from_numpy(scale).double()[:, None]
+
+
+def flat_search(params, x, k, eps=1e-5, table="f32", with_values=True):
+    """The flat exact search, written with torch CPU library routines in fp64.
+
+    Returns idx [B,H,k] (score desc, flat asc), top [B,H,k], w [B,H,k],
+    qhat [B,H,D] and (if with_values) out [B,D]."""
+    wq = torch.from_numpy(params["wq"]).double()
+    H, D, _ = wq.shape
+    sub = torch.from_numpy(params["subkeys"]).double()
+    n = sub.shape[2]
+    xt = torch.from_numpy(np.ascontiguousarray(x)).double()
+    B = xt.shape[0]
+    vals = dequant_table(params["values"], params.get("scale"), table) if with_values else None
+    out = torch.zeros(B, D, dtype=torch.float64)
+    idx = torch.empty(B, H, k, dtype=torch.int64)
+    top = torch.empty(B, H, k, dtype=torch.float64)
+    w = torch.empty(B, H, k, dtype=torch.float64)
+    qhat = torch.empty(B, H, D, dtype=torch.float64)
+    for h in range(H):
+        q = F.linear(xt, wq[h])
+        qh = F.batch_norm(q, torch.from_numpy(params["mean"][h]).double(), torch.from_numpy(params["var"][h]).double(),
+                          torch.from_numpy(params["gamma"][h]).double(), torch.from_numpy(params["beta"][h]).double(),
+                          training=False, eps=eps)
+        qhat[:, h] = qh
+        # key a*n + b is the concatenation (c0_a, c1_b); scored in chunks of a
+        scores = torch.empty(B, n * n, dtype=torch.float64)
+        step = max(1, (1 << 22) // (n * D))
+        for a0 in range(0, n, step):
+            a1 = min(n, a0 + step)
+            keys = torch.cat([sub[h, 0, a0:a1].repeat_interleave(n, 0), sub[h, 1].repeat(a1 - a0, 1)], dim=1)
+            scores[:, a0 * n:a1 * n] = qh @ keys.T
+        order = torch.sort(scores, dim=1, descending=True, stable=True).indices[:, :k]
+        t = torch.gather(scores, 1, order)
+        idx[:, h], top[:, h] = order, t
+        w[:, h] = torch.softmax(t, dim=-1)
+        if with_values:
+            out += F.embedding_bag(order, vals, per_sample_weights=w[:, h], mode="sum")
+    res = {"idx": idx.numpy().astype(np.int32), "top": top.numpy(), "w": w.numpy(), "qhat": qhat.numpy()}
+    if with_values:
+        res["out"] = out.numpy()
+    return res
+
+
+def _model(params, k, table, eps=1e-5):
+    return oracle.Model.from_params(params, k, table, eps)
+
+
+def _assert_same_winners(got, ref, top_ref, tol_gap=1e-9):
+    """Same sets; same order wherever neighbours differ by more than rounding."""
+    assert (np.sort(got, -1) == np.sort(ref, -1)).all(), "winner sets differ"
+    gaps = top_ref[..., :-1] - top_ref[..., 1:]
+    pinned = np.concatenate([gaps > tol_gap, np.ones(gaps.shape[:-1] + (1,), bool)], -1)
+    pinned &= np.concatenate([np.ones(gaps.shape[:-1] + (1,), bool), gaps > tol_gap], -1)
+    assert (got[pinned] == ref[pinned]).all(), "winner order differs"
+
+
+def pin_against_flat_search(wl, seed=0, tokens=None, gamma_beta=False, lib=None, rtol=1e-10):
+    """Oracle == flat exact search with library routines, on one workload."""
+    params = synthetic.make_params(wl, seed)
+    if gamma_beta:
+        rng = np.random.default_rng([seed, 1234])
+        params["gamma"] = rng.uniform(0.5, 1.5, params["gamma"].shape).astype(np.float32)
+        params["beta"] = rng.normal(0, 0.3, params["beta"].shape).astype(np.float32)
+    x = synthetic.make_x(wl, seed)
+    if tokens is not None:
+        x = x[tokens]
+    r = oracle.run(_model(params, wl.k, wl.table), x, want=("out", "idx", "top", "w", "qhat", "ncand"), lib=lib)
+    f = flat_search(params, x, wl.k, table=wl.table)
+    np.testing.assert_allclose(r["qhat"], f["qhat"], rtol=1e-12, atol=1e-12)
+    _assert_same_winners(r["idx"], f["idx"], f["top"])
+    np.testing.assert_allclose(r["top"], f["top"], rtol=1e-12, atol=1e-10)
+    np.testing.assert_allclose(r["w"], f["w"], rtol=rtol, atol=1e-12)
+    np.testing.assert_allclose(r["out"], f["out"], rtol=rtol, atol=1e-10)
+    assert (r["ncand"] == wl.k * wl.k).all()
+    return r
+
+
+def pin_hand_example(lib=None):
+    """The worked example of tests/golden/hand_example.json."""
+    g = json.load(open(os.path.join(GOLDEN, "hand_example.json")))
+    inp = g["inputs"]
+    D, n = inp["D"], inp["n"]
+    values = np.array([[r, 1.0, -r, r / 2.0] for r in range(n * n)], np.float32)
+    params = {key: np.array(inp[key], np.float32) for key in ("wq", "mean", "var", "gamma", "beta", "subkeys")}
+    params["values"], params["scale"] = values, None
+    x = np.array(inp["x"], np.float32)
+    e = g["expected"]
+    r2 = oracle.run(_model(params, 2, "f32", inp["eps"]), x, want=("out", "idx", "top", "w", "ncand"), lib=lib)
+    assert r2["idx"][0, 0].tolist() == e["k2"]["idx"]
+    np.testing.assert_allclose(r2["top"][0, 0], e["k2"]["top"], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(r2["w"][0, 0], e["k2"]["w"], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(r2["out"][0], e["k2"]["out"], rtol=0, atol=1e-14)
+    assert r2["ncand"][0, 0] == 4
+    r3 = oracle.run(_model(params, 3, "f32", inp["eps"]), x, want=("out", "idx", "top", "w", "ncand"), lib=lib)
+    a = 1.0 / (2.0 + math.exp(-1.0))
+    c = math.exp(-1.0) / (2.0 + math.exp(-1.0))
+    assert r3["idx"][0, 0].tolist() == e["k3"]["idx"]
+    np.testing.assert_allclose(r3["top"][0, 0], e["k3"]["top"], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(r3["w"][0, 0], [a, a, c], rtol=1e-15, atol=0)
+    np.testing.assert_allclose(r3["out"][0], [13 * a, 1.0, -13 * a, 6.5 * a], rtol=1e-14, atol=1e-15)
+    assert r3["ncand"][0, 0] == 9
+
+
+def integer_tie_params(H=2, D=8, n=6, seed=5):
+    """Small integer-valued inputs with duplicated subkeys.  Every score is
+    an exact small integer, so ties are exact whatever the summation order."""
+    rng = np.random.default_rng(seed)
+    half = D // 2
+    sub = rng.integers(-2, 3, size=(H, 2, n, half)).astype(np.float32)
+    sub[:, 0, n - 1] = sub[:, 0, 1]  # duplicate subkeys -> exact ties
+    sub[:, 1, 3] = sub[:, 1, 0]
+    sub[:, 1, n - 1] = sub[:, 1, 2]
+    p = {
+        "wq": np.stack([np.eye(D, dtype=np.float32)] * H),
+        "mean": np.zeros((H, D), np.float32),
+        "var": np.full((H, D), 0.75, np.float32),  # var + eps = 1 exactly (eps = 0.25)
+        "gamma": np.ones((H, D), np.float32),
+        "beta": np.zeros((H, D), np.float32),
+        "subkeys": sub,
+        "values": rng.standard_normal((n * n, D)).astype(np.float32),
+        "scale": None,
+    }
+    x = rng.integers(-2, 3, size=(16, D)).astype(np.float32)
+    return p, x
+
+
+def pin_integer_ties(lib=None):
+    """Exact ties: the lowest index must win, in both halves and in the grid,
+    for every k from 1 to n_keys."""
+    p, x = integer_tie_params()
+    n = p["subkeys"].shape[2]
+    for k in range(1, n + 1):
+        r = oracle.run(_model(p, k, "f32", 0.25), x, want=("idx", "top", "w", "out"), lib=lib)
+        f = flat_search(p, x, k, eps=0.25)
+        assert (r["idx"] == f["idx"]).all(), f"tie order differs at k={k}"
+        np.testing.assert_array_equal(r["top"], f["top"])
+        np.testing.assert_allclose(r["w"], f["w"], rtol=1e-14)
+        np.testing.assert_allclose(r["out"], f["out"], rtol=1e-12, atol=1e-12)
+
+
+def pin_k_equals_1(lib=None):
+    """k = 1: the winner is (argmax of half 0, argmax of half 1), weight 1."""
+    wl = synthetic.Workload("k1", 32, 32, 2, 12, 1, "f32", "random")
+    params = synthetic.make_params(wl, 3)
+    x = synthetic.make_x(wl, 3)
+    r = oracle.run(_model(params, 1, "f32"), x, want=("idx", "w", "out", "qhat"), lib=lib)
+    f = flat_search(params, x, 1)
+    half = wl.D // 2
+    for h in range(wl.H):
+        s0 = f["qhat"][:, h, :half] @ params["subkeys"][h, 0].astype(np.float64).T
+        s1 = f["qhat"][:, h, half:] @ params["subkeys"][h, 1].astype(np.float64).T
+        assert (r["idx"][:, h, 0] == s0.argmax(1) * wl.n + s1.argmax(1)).all()
+    assert (r["w"] == 1.0).all()
+    np.testing.assert_allclose(r["out"], f["out"], rtol=1e-12, atol=1e-12)
+
+
+def pin_codecs(lib=None):
+    """Decoders vs torch's casts on every bf16 and E4M3 code."""
+    b = np.arange(1 << 16, dtype=np.uint16)
+    ref = torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).double().numpy()
+    got = np.array([oracle.bf16_to_f64(v, lib) for v in b])
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert (got[ok] == ref[ok]).all(), "bf16 decoder differs from torch"
+    e = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(e).view(torch.float8_e4m3fn).double().numpy()
+    got = np.array([oracle.e4m3_to_f64(v, lib) for v in e])
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert (got[ok] == ref[ok]).all(), "E4M3 decoder differs from torch"
+    # format landmarks: largest finite 448, smallest normal 2^-6, smallest subnormal 2^-9
+    assert oracle.e4m3_to_f64(0x7E, lib) == 448.0
+    assert oracle.e4m3_to_f64(0x08, lib) == 2.0 ** -6
+    assert oracle.e4m3_to_f64(0x01, lib) == 2.0 ** -9
+    assert oracle.e4m3_to_f64(0xB8, lib) == -1.0
+
+
+def pin_softmax_large_scores(lib=None):
+    """Scores in the thousands: the max-subtracted softmax stays finite and
+    matches torch.softmax."""
+    wl = synthetic.Workload("big", 8, 32, 1, 8, 4, "f32", "unit")
+    params = synthetic.make_params(wl, 1)
+    params["subkeys"] = params["subkeys"] * np.float32(400.0)
+    x = synthetic.make_x(wl, 1)
+    r = oracle.run(_model(params, wl.k, "f32"), x, want=("w", "top", "out"), lib=lib)
+    assert np.isfinite(r["w"]).all() and np.isfinite(r["out"]).all()
+    assert r["top"].max() > 1000.0
+    f = flat_search(params, x, wl.k)
+    np.testing.assert_allclose(r["w"], f["w"], rtol=1e-9, atol=1e-300)
+
+
+def pin_op_counts(lib=None):
+    """The page's counts at n_keys = 1024, k = 32: 2048 subkey scores (two
+    halves of 1024) and 1024 candidates."""
+    g = json.load(open(os.path.join(GOLDEN, "op_counts.json")))
+    n, k = g["n_keys"], g["k"]
+    wl = synthetic.Workload("counts", 2, 8, 1, n, k, "f32", "unit")
+    params = synthetic.make_params(wl, 0, with_values=False)
+    params["values"] = np.zeros((n * n, wl.D), np.float32)
+    r = oracle.run(_model(params, k, "f32"), synthetic.make_x(wl, 0), want=("ncand", "idx"), lib=lib)
+    assert 2 * n == g["subkey_scores"]
+    assert (r["ncand"] == g["candidates"]).all()
+    assert r["idx"].shape[-1] == k

@@ -1,0 +1,102 @@
+"""Shared helpers for the tests: gap-clean inputs and comparison rules.
+
+Index parity between the fp64 oracle and an fp32 GPU path is only meaningful
+when no score near the k | k+1 boundary is closer than the fp32 error.  For
+each (token, head) the gap between the k-th and (k+1)-th best full scores
+(the oracle's product search at depth k+1, which is the exact top-(k+1) by the
+exactness argument of "Product-Key Memory", §Factorising the key space) must
+be at least
+
+    tau = max(TAU_ABS, TAU_REL * sum_i |q^_i| * |key_i|)
+
+where key is the concatenated key of the k-th winner: the fp32 rounding error
+of a dot product is proportional to that L1 mass, not to the score itself.
+Tokens that fail are re-drawn from their own seeded stream.
+"""
+import numpy as np
+
+import oracle
+import synthetic
+
+TAU_ABS = 1e-6
+TAU_REL = 1e-6
+
+
+def model_for(wl, params, eps=1e-5):
+    return oracle.Model.from_params(params, wl.k, wl.table, eps)
+
+
+def key_l1_mass(wl, params, qhat, flat, h):
+    """sum_i |q^_i| |key_i| for the concatenated key of flat row `flat`."""
+    half, n = wl.D // 2, wl.n
+    a, b = int(flat) // n, int(flat) % n
+    c0 = params["subkeys"][h, 0, a].astype(np.float64)
+    c1 = params["subkeys"][h, 1, b].astype(np.float64)
+    return float(np.abs(qhat[:half]) @ np.abs(c0) + np.abs(qhat[half:]) @ np.abs(c1))
+
+
+def gaps_and_tau(wl, params, x, model=None):
+    """Per (token, head): fp64 gap between the k-th and (k+1)-th full scores,
+    and the tau it must clear.  Both [B, H]."""
+    model = model or model_for(wl, params)
+    k = wl.k
+    r = oracle.run(model, x, kk=k + 1, want=("top", "idx", "qhat"))
+    gap = r["top"][:, :, k - 1] - r["top"][:, :, k]
+    B = x.shape[0]
+    tau = np.empty((B, wl.H))
+    for b in range(B):
+        for h in range(wl.H):
+            tau[b, h] = max(TAU_ABS, TAU_REL * key_l1_mass(wl, params, r["qhat"][b, h], r["idx"][b, h, k - 1], h))
+    return gap, tau
+
+
+def gap_clean(wl, params, x, tokens=None, seed=0, max_attempts=60):
+    """Re-draw rows of x (in place) until every listed token clears tau on
+    every head.  Returns the per-token attempt counts."""
+    model = model_for(wl, params)
+    todo = np.arange(x.shape[0]) if tokens is None else np.asarray(tokens)
+    attempts = np.zeros(x.shape[0], dtype=np.int64)
+    if wl.k >= wl.n:
+        return attempts  # no (k+1)-th key: every key is a winner
+    for _ in range(max_attempts):
+        gap, tau = gaps_and_tau(wl, params, x[todo], model)
+        bad = todo[(gap < tau).any(axis=1)]
+        if bad.size == 0:
+            return attempts
+        for b in bad:
+            attempts[b] += 1
+            x[b] = synthetic.redraw_row(wl, seed, b, attempts[b])
+        todo = bad
+    raise RuntimeError("gap-clean draw did not converge")
+
+
+def rel_rowmax_err(got, ref):
+    """Per row: max |got - ref| / max |ref|."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    return np.abs(got - ref).max(axis=-1) / np.maximum(np.abs(ref).max(axis=-1), 1e-300)
+
+
+def check_indices(idx, ref_idx, ref_top, tau):
+    """Index parity: identical winner sets per (token, head); the order must
+    agree wherever adjacent fp64 winners are at least tau apart (inside a
+    run of nearer scores the order is not pinned).  idx/ref_idx [B,H,k],
+    ref_top [B,H,k] fp64, tau [B,H] or a scalar."""
+    idx = np.asarray(idx)
+    ref_idx = np.asarray(ref_idx)
+    assert idx.shape == ref_idx.shape
+    same_set = (np.sort(idx, -1) == np.sort(ref_idx, -1)).all(-1)
+    bad = np.argwhere(~same_set)
+    assert bad.size == 0, f"winner sets differ at (token, head) {bad[:5].tolist()}"
+    tau = np.broadcast_to(np.asarray(tau, np.float64), ref_top.shape[:-1])[..., None]
+    # a gap of at least tau between reference positions p-1 and p starts a new
+    # block; blocks must appear in the same order, members in any order
+    gaps = ref_top[..., :-1] - ref_top[..., 1:]
+    cut = np.concatenate([np.ones(gaps.shape[:-1] + (1,), bool), gaps >= tau], axis=-1)
+    block = np.cumsum(cut, axis=-1)
+    B, H, _ = idx.shape
+    for b in range(B):
+        for h in range(H):
+            pos = {int(v): i for i, v in enumerate(ref_idx[b, h])}
+            got_blocks = np.array([block[b, h, pos[int(v)]] for v in idx[b, h]])
+            assert (got_blocks == block[b, h]).all(), f"order differs at token {b} head {h}"

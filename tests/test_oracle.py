@@ -1,0 +1,123 @@
+"""CPU: the fp64 oracle against its pins (library routines, the flat exact
+search, closed forms, special cases) and the input generator's encoders."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic
+from tests import pins
+from tests import support
+
+
+def test_hand_example():
+    pins.pin_hand_example()
+
+
+def test_codecs_all_codes():
+    pins.pin_codecs()
+
+
+def test_flat_search_tiny_all_tokens():
+    pins.pin_against_flat_search(synthetic.WORKLOADS["tiny"])
+
+
+def test_flat_search_mid_sample():
+    wl = synthetic.WORKLOADS["mid"]
+    pins.pin_against_flat_search(wl, tokens=np.arange(0, wl.B, 16))
+
+
+def test_flat_search_random_gamma_beta():
+    wl = synthetic.Workload("gb", 24, 64, 3, 20, 5, "f32", "random")
+    pins.pin_against_flat_search(wl, gamma_beta=True)
+
+
+@pytest.mark.parametrize("table", ["bf16", "e4m3"])
+def test_flat_search_quantised_tables(table):
+    wl = synthetic.Workload("q", 24, 128, 2, 24, 8, table, "random")
+    pins.pin_against_flat_search(wl, seed=2)
+
+
+def test_integer_ties_every_k():
+    pins.pin_integer_ties()
+
+
+def test_k_equals_1():
+    pins.pin_k_equals_1()
+
+
+def test_k_equals_n_keys():
+    wl = synthetic.Workload("kn", 12, 32, 2, 6, 6, "f32", "random")
+    pins.pin_against_flat_search(wl, seed=4)
+
+
+def test_softmax_large_scores():
+    pins.pin_softmax_large_scores()
+
+
+def test_op_counts():
+    pins.pin_op_counts()
+
+
+def test_invariants_mid():
+    """Sum of weights is 1, k^2 candidates, distinct in-range indices sorted
+    by non-increasing score, non-increasing weights."""
+    wl = synthetic.WORKLOADS["mid"]
+    params = synthetic.make_params(wl)
+    x = synthetic.make_x(wl)[:128]
+    r = oracle.run(support.model_for(wl, params), x, want=("idx", "top", "w", "ncand"))
+    np.testing.assert_allclose(r["w"].sum(-1), 1.0, rtol=0, atol=1e-12)
+    assert (r["ncand"] == wl.k ** 2).all()
+    assert ((r["idx"] >= 0) & (r["idx"] < wl.N)).all()
+    s = np.sort(r["idx"], -1)
+    assert (s[..., 1:] != s[..., :-1]).all()
+    assert (np.diff(r["top"], axis=-1) <= 0).all()
+    assert (np.diff(r["w"], axis=-1) <= 0).all()
+
+
+def test_gap_clean_redraws_and_converges():
+    wl = synthetic.WORKLOADS["mid"]
+    params = synthetic.make_params(wl)
+    x = synthetic.make_x(wl)[:256].copy()
+    x0 = x.copy()
+    attempts = support.gap_clean(wl, params, x)
+    gap, tau = support.gaps_and_tau(wl, params, x)
+    assert (gap >= tau).all()
+    changed = (x != x0).any(1)
+    assert (changed == (attempts > 0)).all()
+
+
+def test_bf16_encoder_matches_torch():
+    a = np.random.default_rng(0).standard_normal(1 << 16).astype(np.float32) * 3
+    a[:4] = [0.0, -0.0, 1e-40, -3.3895314e38]
+    got = synthetic.f32_to_bf16_bits(a)
+    ref = torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert (got == ref).all()
+
+
+def test_e4m3_encoder_is_nearest_code():
+    """Each stored code is the nearest E4M3 value to a/scale (ties to even),
+    scale = row max / 448."""
+    a = np.random.default_rng(1).standard_normal((64, 96)).astype(np.float32)
+    codes, scale = synthetic.f32_to_e4m3_rows(a)
+    np.testing.assert_allclose(scale, np.abs(a).max(1) / 448.0, rtol=1e-7)
+    table = np.array([oracle.e4m3_to_f64(c) for c in range(256)])
+    finite = ~np.isnan(table)
+    y = (a / scale[:, None]).astype(np.float64)
+    dist = np.abs(y[..., None] - np.where(finite, table, np.inf)[None, None, :])
+    best = dist.min(-1)
+    got = np.abs(y - table[codes])
+    assert (got <= best + 1e-12).all()
+    assert (np.abs(table[codes]) <= 448).all()
+
+
+def test_generator_is_deterministic_and_seeded():
+    wl = synthetic.Workload("g", 4, 64, 2, 64, 4, "bf16", "random")
+    p1, p2, p3 = synthetic.make_params(wl, 0), synthetic.make_params(wl, 0), synthetic.make_params(wl, 1)
+    for key in p1:
+        if p1[key] is None:
+            continue
+        assert (p1[key] == p2[key]).all()
+    assert not (p1["wq"] == p3["wq"]).all()
+    assert (synthetic.redraw_row(wl, 0, 3, 1) == synthetic.redraw_row(wl, 0, 3, 1)).all()
+    assert not (synthetic.redraw_row(wl, 0, 3, 1) == synthetic.redraw_row(wl, 0, 3, 2)).all()

@@ -1,0 +1,64 @@
+"""CPU: each plausible mistake planted in a copy of the oracle's source must
+make at least one pin fail.  This checks the pins, not the oracle."""
+import os
+
+import pytest
+
+import oracle
+from tests import pins
+
+SRC = os.path.join(os.path.dirname(oracle.lib_path()), "pkm_oracle.c")
+
+MUTATIONS = {
+    "transposed_wq": ("q += (double)wrow[d] * (double)x_b[d];",
+                      "q += (double)M->wq[((int64_t)h * D + d) * D + f] * (double)x_b[d];"),
+    "bn_no_sqrt": ("/ sqrt((double)M->var[pf] + M->eps)", "/ ((double)M->var[pf] + M->eps)"),
+    "bn_no_eps": ("sqrt((double)M->var[pf] + M->eps)", "sqrt((double)M->var[pf])"),
+    "bn_beta_sign": ("(double)M->beta[pf];", "-(double)M->beta[pf];"),
+    "bn_mean_dropped": ("(q - (double)M->mean[pf])", "(q)"),
+    "swapped_halves": ("const double *qp = qhat + p * half;", "const double *qp = qhat + (1 - p) * half;"),
+    "flat_index_swapped": ("grid[c].i = (int64_t)idx0[i] * n + idx1[j];", "grid[c].i = (int64_t)idx1[j] * n + idx0[i];"),
+    "second_half_dropped": ("grid[c].v = top0[i] + top1[j];", "grid[c].v = top0[i];"),
+    "ties_to_higher_index": ("if (a->i < b->i) return -1;\n    if (a->i > b->i) return 1;",
+                             "if (a->i < b->i) return 1;\n    if (a->i > b->i) return -1;"),
+    "ascending_scores": ("if (a->v > b->v) return -1;\n    if (a->v < b->v) return 1;",
+                         "if (a->v > b->v) return 1;\n    if (a->v < b->v) return -1;"),
+    "softmax_unnormalised": ("w[j] /= sum;", "w[j] /= 1.0;"),
+    "softmax_no_max_shift": ("w[j] = exp(top[j] - mx);", "w[j] = exp(top[j]);"),
+    "gather_unweighted": ("out_b[d] += w[j] * value_at(M, rows[j], d);", "out_b[d] += value_at(M, rows[j], d);"),
+    "e4m3_bias": ("v = ldexp(1.0 + (double)m / 8.0, e - 7);", "v = ldexp(1.0 + (double)m / 8.0, e - 8);"),
+    "e4m3_no_scale": ("* (double)M->scale[row];", ";"),
+    "bf16_subnormal": ("v = ldexp((double)m / 128.0, -126);", "v = ldexp((double)m / 128.0, -127);"),
+    "candidate_count": ("    return c;\n}", "    return c - 1;\n}"),
+    "half_topk_from_wrong_row": ("pkmo_topk_sorted(n, s + n, kk, t1, i1);", "pkmo_topk_sorted(n, s, kk, t1, i1);"),
+}
+
+PINS = [
+    pins.pin_hand_example,
+    pins.pin_codecs,
+    pins.pin_integer_ties,
+    pins.pin_k_equals_1,
+    pins.pin_softmax_large_scores,
+    pins.pin_op_counts,
+    lambda lib: pins.pin_against_flat_search(pins.synthetic.WORKLOADS["tiny"], lib=lib),
+    lambda lib: pins.pin_against_flat_search(pins.synthetic.Workload("gb", 24, 64, 3, 20, 5, "f32", "random"),
+                                             gamma_beta=True, lib=lib),
+    lambda lib: pins.pin_against_flat_search(pins.synthetic.Workload("q", 24, 128, 2, 24, 8, "e4m3", "random"),
+                                             seed=2, lib=lib),
+]
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, tmp_path):
+    old, new = MUTATIONS[name]
+    text = open(SRC).read()
+    assert text.count(old) == 1, f"mutation anchor for {name} not found exactly once"
+    src = tmp_path / "mutant.c"
+    src.write_text(text.replace(old, new))
+    lib = oracle.load_library(oracle.compile_source(str(src), str(tmp_path / "libmutant.so")))
+    for pin in PINS:
+        try:
+            pin(lib)
+        except (AssertionError, ValueError, RuntimeError):
+            return
+    pytest.fail(f"no pin caught the planted mistake {name}")
