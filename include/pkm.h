@@ -1,0 +1,169 @@
+/*
+ * pkm.h -- C ABI of the MI355X (gfx950) product-key memory lookup library.
+ *
+ * The library computes the inference forward pass of a product-key memory
+ * layer ("Product-Key Memory", aiwiki: §Factorising the key space and the
+ * ProductKeyMemory module of its code listing), for H heads that share one
+ * value table:
+ *
+ *   a1  q[b,h,:]  = Wq[h] . x[b,:]                          (Linear, no bias)
+ *   a2  q^[b,h,:] = (q - mean[h]) / sqrt(var[h] + eps) * gamma[h] + beta[h]
+ *                                       (BatchNorm1d with running statistics)
+ *   a3  s[b,h,p,j] = q^[b,h, p*D/2 : (p+1)*D/2] . subkeys[h,p,j,:],  p = 0,1
+ *   a4  each half keeps its k best subkeys (score desc, index asc)
+ *   a5  the k*k candidates s0[i] + s1[j] with flat row i0[i]*n_keys + i1[j];
+ *       the k best of them (score desc, flat index asc)
+ *   a6  w = softmax of the k winning scores (no temperature)
+ *   a7  out[b,:] = sum_h sum_j w[b,h,j] * scale[row] * values[row,:],
+ *       row = idx[b,h,j]                (EmbeddingBag "sum", per-sample
+ *                                        weights; scale = 1 unless E4M3)
+ *
+ * The winners are the exact top-k over all n_keys^2 concatenated keys (the
+ * exactness argument of §Factorising the key space); a5-a7 follow the top-k
+ * then softmax read of "Memory Retrieval Mechanisms: From Soft to
+ * Efficient" (top-k section).  Scores, softmax and the accumulation run in
+ * fp32; the value table may be fp32, bf16 or OCP FP8 E4M3 (E4M3FN) with one
+ * fp32 scale per row (the page's note that the table suits a lower
+ * precision).
+ *
+ * Conventions for every call:
+ *   - Pointers to tensors are DEVICE pointers, owned by the caller, row-major
+ *     and contiguous, 16-byte aligned.  The library never frees or keeps them
+ *     past the call.
+ *   - Calls that take a stream (a hipStream_t, NULL = the default stream)
+ *     only enqueue work: they return before it runs and never synchronise the
+ *     device.  Inputs must stay alive and outputs untouched until the stream
+ *     reaches that point.  Results are deterministic (bitwise) for identical
+ *     inputs and configuration.
+ *   - One context serves one stream at a time: the workspace is shared by
+ *     every call on a context.  Use one context per concurrent stream.
+ *   - Argument errors are detected on the host before anything is enqueued
+ *     and return PKM_E_ARG (or PKM_E_UNSUPPORTED for shapes the kernels do
+ *     not handle).  A failed launch returns PKM_E_DEVICE.  Errors raised by
+ *     the device while the work runs surface at the caller's next
+ *     synchronisation.  pkm_last_error() gives a thread-local description of
+ *     the last error.  No C++ exception crosses this interface; nothing is
+ *     printed unless the environment sets PKM_LOG=1.
+ *   - Non-finite inputs give undefined (but memory-safe) results.
+ */
+#ifndef PKM_H
+#define PKM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PKM_OK = 0,
+    PKM_E_ARG = 1,         /* invalid argument or configuration */
+    PKM_E_UNSUPPORTED = 2, /* valid for the method, not handled by the kernels or this device */
+    PKM_E_NOMEM = 3,       /* device allocation failed */
+    PKM_E_DEVICE = 4       /* HIP runtime or launch error */
+} pkm_status;
+
+typedef enum {
+    PKM_VALUES_F32 = 0,     /* float32 rows */
+    PKM_VALUES_BF16 = 1,    /* bfloat16 rows (uint16 bit patterns) */
+    PKM_VALUES_FP8_E4M3 = 2 /* OCP E4M3FN bytes, row r scaled by value_scale[r] */
+} pkm_value_type;
+
+typedef struct {
+    int32_t dim;        /* D: model width.  The query is split in two halves
+                           (chunk(2) in the listing), so D is even; the kernels
+                           need D % 64 == 0 (PKM_E_UNSUPPORTED otherwise). */
+    int32_t heads;      /* H >= 1 independent queries sharing one table */
+    int32_t n_keys;     /* n: subkeys per half; the table has N = n*n rows.
+                           2 <= n and n*n < 2^31. The select kernel handles
+                           n <= 4096 (PKM_E_UNSUPPORTED above). */
+    int32_t k;          /* winners per head: 1 <= k <= n (topk needs k <= n);
+                           the kernels handle k <= 64 (PKM_E_UNSUPPORTED above) */
+    int32_t value_type; /* a pkm_value_type */
+    float bn_eps;       /* BatchNorm epsilon, > 0 (BatchNorm1d's default is 1e-5) */
+    int64_t max_batch;  /* tokens per internal chunk: pkm_forward processes any
+                           B in chunks of at most this many tokens; the
+                           workspace is sized for one chunk.  >= 1. */
+} pkm_config;
+
+typedef struct {
+    const float *wq;          /* [H, D, D]: Wq[h] row f = output feature f
+                                 (nn.Linear weight layout), q = Wq[h] . x */
+    const float *bn_mean;     /* [H, D] running mean */
+    const float *bn_var;      /* [H, D] running variance, >= 0 */
+    const float *bn_gamma;    /* [H, D] */
+    const float *bn_beta;     /* [H, D] */
+    const float *subkeys;     /* [H, 2, n, D/2]: half p of head h */
+    const void *values;       /* [N, D] of value_type, N = n*n */
+    const float *value_scale; /* [N] for PKM_VALUES_FP8_E4M3, else ignored (may be NULL) */
+} pkm_params;
+
+typedef struct pkm_ctx pkm_ctx; /* opaque; owned by the library */
+
+/* Validates a configuration without touching any device.  PKM_OK, PKM_E_ARG
+ * or PKM_E_UNSUPPORTED. */
+pkm_status pkm_config_check(const pkm_config *cfg);
+
+/* Bytes of device workspace pkm_create allocates for cfg (written to *bytes).
+ * Touches no device. */
+pkm_status pkm_workspace_bytes(const pkm_config *cfg, size_t *bytes);
+
+/* Creates a context on the current HIP device: checks that the device is
+ * gfx950 (PKM_E_UNSUPPORTED otherwise) and allocates the workspace
+ * (PKM_E_NOMEM on failure): the normalised queries [max_batch, H, D] fp32,
+ * the half scores [max_batch, H, 2, n] fp32 and idx/weight buffers
+ * [max_batch, H, k] for pkm_forward calls that pass NULL for them.
+ * *out receives the context, or NULL on error. */
+pkm_status pkm_create(const pkm_config *cfg, pkm_ctx **out);
+
+/* Releases the workspace and the context.  NULL is a no-op.  The caller must
+ * make sure no enqueued work still uses the context. */
+void pkm_destroy(pkm_ctx *ctx);
+
+/* The whole lookup (a1-a7) for B >= 0 tokens.
+ *   x        [B, D] fp32 input
+ *   out      [B, D] fp32, overwritten with the weighted row sums (a7)
+ *   idx      [B, H, k] int32 winning flat rows in (score desc, flat index
+ *            asc) order, or NULL to keep them in the workspace
+ *   weights  [B, H, k] fp32 softmax weights in the same order, or NULL
+ *   stream   hipStream_t (NULL = default stream)
+ * B == 0 enqueues nothing.  out must not alias any input. */
+pkm_status pkm_forward(pkm_ctx *ctx, const pkm_params *p, int64_t B, const float *x, float *out, int32_t *idx,
+                       float *weights, void *stream);
+
+/* Steps a1-a2 only: qhat [B, H, D] fp32 = BN_h(Wq[h] . x[b]).  Uses wq and
+ * the four BN arrays of p.  No workspace is used. */
+pkm_status pkm_query(pkm_ctx *ctx, const pkm_params *p, int64_t B, const float *x, float *qhat, void *stream);
+
+/* Step a3 only: scores [B, H, 2, n] fp32 from qhat [B, H, D] and p->subkeys.
+ * No workspace is used. */
+pkm_status pkm_score(pkm_ctx *ctx, const pkm_params *p, int64_t B, const float *qhat, float *scores,
+                     void *stream);
+
+/* Steps a4-a6 only: from scores [B, H, 2, n] fp32 write idx [B, H, k] int32
+ * and weights [B, H, k] fp32 (both required), as pkm_forward orders them.
+ * No workspace is used. */
+pkm_status pkm_select(pkm_ctx *ctx, int64_t B, const float *scores, int32_t *idx, float *weights, void *stream);
+
+/* Step a7 only: out [B, D] fp32 = sum over the rows_per_token (row, weight)
+ * pairs of token b of weight * scale[row] * values[row, :].  idx and weights
+ * are [B, rows_per_token] (pkm_forward uses rows_per_token = H * k, the
+ * [B, H, k] layout).  Rows should lie in [0, N); the kernel clamps a row
+ * outside that range into it (memory-safe, meaningless result).  Uses
+ * p->values and p->value_scale only. */
+pkm_status pkm_gather(pkm_ctx *ctx, const pkm_params *p, int64_t B, int32_t rows_per_token, const int32_t *idx,
+                      const float *weights, float *out, void *stream);
+
+/* A static description of a status code. */
+const char *pkm_status_str(pkm_status s);
+
+/* Thread-local description of the last error returned to this thread (""
+ * if none). */
+const char *pkm_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKM_H */

@@ -55,6 +55,10 @@ def load_library(path):
     lib.pkmo_bf16_to_f64.argtypes = [ctypes.c_uint16]
     lib.pkmo_e4m3_to_f64.restype = ctypes.c_double
     lib.pkmo_e4m3_to_f64.argtypes = [ctypes.c_uint8]
+    lib.pkmo_select.restype = ctypes.c_int
+    lib.pkmo_select.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int] + [ctypes.c_void_p] * 4
+    lib.pkmo_gather.restype = ctypes.c_int
+    lib.pkmo_gather.argtypes = [ctypes.POINTER(_Model), ctypes.c_int64, ctypes.c_int] + [ctypes.c_void_p] * 3
     return lib
 
 
@@ -146,3 +150,35 @@ def bf16_to_f64(bits, lib=None):
 
 def e4m3_to_f64(bits, lib=None):
     return (lib or _load()).pkmo_e4m3_to_f64(int(bits))
+
+
+def select(scores, k, lib=None):
+    """Steps 4-6 from given half scores [..., 2, n] (any float dtype, read
+    as fp64).  Returns idx, top, w, each [..., k]."""
+    lib = lib or _load()
+    scores = np.ascontiguousarray(scores, dtype=np.float64)
+    lead, n = scores.shape[:-2], scores.shape[-1]
+    assert scores.shape[-2] == 2
+    P = int(np.prod(lead)) if lead else 1
+    idx = np.empty(lead + (k,), np.int32)
+    top = np.empty(lead + (k,), np.float64)
+    w = np.empty(lead + (k,), np.float64)
+    if lib.pkmo_select(P, n, int(k), _ptr(scores), _ptr(idx), _ptr(top), _ptr(w)) != 0:
+        raise ValueError("oracle rejected its arguments")
+    return idx, top, w
+
+
+def gather(model, rows, w, lib=None):
+    """Step 7 from given rows [B, R] (int32) and weights [B, R] (read as
+    fp64).  Returns out [B, D] fp64."""
+    lib = lib or _load()
+    rows = _c(np.asarray(rows, np.int32), np.int32)
+    w = np.ascontiguousarray(w, dtype=np.float64)
+    B, R = rows.shape
+    assert w.shape == (B, R)
+    if B and (rows.min() < 0 or rows.max() >= model.n * model.n):
+        raise ValueError("row index out of range")
+    out = np.empty((B, model.D), np.float64)
+    if lib.pkmo_gather(ctypes.byref(model._s), B, R, _ptr(rows), _ptr(w), _ptr(out)) != 0:
+        raise ValueError("oracle rejected its arguments")
+    return out

@@ -329,3 +329,45 @@ int pkmo_run(const pkmo_model *M, int64_t B, const float *x, int kk, double *out
     free(jobs);
     return 0;
 }
+
+/*
+ * Steps 4-6 alone, from given half scores: scores [P][2][n] (P = tokens x
+ * heads, half 0 then half 1).  Writes idx/top/w [P][k] (any may be NULL).
+ * Returns 0, or -1 on bad arguments.
+ */
+int pkmo_select(int64_t P, int n, int k, const double *scores, int32_t *idx, double *top, double *w)
+{
+    if (P < 0 || n < 1 || k < 1 || k > n || !scores) return -1;
+    double *t0 = (double *)malloc(sizeof(double) * (size_t)k);
+    double *t1 = (double *)malloc(sizeof(double) * (size_t)k);
+    int32_t *i0 = (int32_t *)malloc(sizeof(int32_t) * (size_t)k);
+    int32_t *i1 = (int32_t *)malloc(sizeof(int32_t) * (size_t)k);
+    double *tp = (double *)malloc(sizeof(double) * (size_t)k);
+    int32_t *fl = (int32_t *)malloc(sizeof(int32_t) * (size_t)k);
+    for (int64_t p = 0; p < P; ++p) {
+        const double *s = scores + p * 2 * n;
+        pkmo_topk_sorted(n, s, k, t0, i0);
+        pkmo_topk_sorted(n, s + n, k, t1, i1);
+        pkmo_candidates_topk(n, k, t0, i0, t1, i1, k, tp, fl);
+        if (idx) memcpy(idx + p * k, fl, sizeof(int32_t) * (size_t)k);
+        if (top) memcpy(top + p * k, tp, sizeof(double) * (size_t)k);
+        if (w) pkmo_softmax(k, tp, w + p * k);
+    }
+    free(t0); free(t1); free(i0); free(i1); free(tp); free(fl);
+    return 0;
+}
+
+/*
+ * Step 7 alone: out[b] = sum_r w[b][r] * V[rows[b][r]] for b < B, r < R,
+ * rows [B][R] int32, w [B][R] fp64, out [B][D] fp64 (overwritten).
+ */
+int pkmo_gather(const pkmo_model *M, int64_t B, int R, const int32_t *rows, const double *w, double *out)
+{
+    if (!M || B < 0 || R < 0 || !rows || !w || !out) return -1;
+    for (int64_t b = 0; b < B; ++b) {
+        for (int d = 0; d < M->D; ++d)
+            out[b * M->D + d] = 0.0;
+        pkmo_gather_add(M, R, rows + b * R, w + b * R, out + b * M->D);
+    }
+    return 0;
+}

@@ -1,0 +1,278 @@
+"""ctypes binding of libpkm.so (the C ABI declared in include/pkm.h).
+
+Argument marshalling only: torch tensors supply device memory and the current
+stream, every step of the lookup runs in the library's HIP kernels.  There is
+no fallback: if libpkm.so is missing or cannot be loaded, every call raises.
+"""
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libpkm.so")
+
+PKM_OK, PKM_E_ARG, PKM_E_UNSUPPORTED, PKM_E_NOMEM, PKM_E_DEVICE = range(5)
+VALUE_TYPES = {"f32": 0, "bf16": 1, "e4m3": 2}
+
+# Every symbol include/pkm.h declares.
+EXPORTS = (
+    "pkm_config_check", "pkm_workspace_bytes", "pkm_create", "pkm_destroy", "pkm_forward", "pkm_query",
+    "pkm_score", "pkm_select", "pkm_gather", "pkm_status_str", "pkm_last_error",
+)
+
+
+class PkmError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{status_str(status)}: {message}")
+        self.status = status
+
+
+class Config(ctypes.Structure):
+    _fields_ = [
+        ("dim", ctypes.c_int32), ("heads", ctypes.c_int32), ("n_keys", ctypes.c_int32), ("k", ctypes.c_int32),
+        ("value_type", ctypes.c_int32), ("bn_eps", ctypes.c_float), ("max_batch", ctypes.c_int64),
+    ]
+
+
+class ParamsStruct(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in
+                ("wq", "bn_mean", "bn_var", "bn_gamma", "bn_beta", "subkeys", "values", "value_scale")]
+
+
+_lib = None
+
+
+def load_library(path=LIB_PATH):
+    """Load libpkm.so (once).  Raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built: run `python -m product_key_memory_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    cfg_p = ctypes.POINTER(Config)
+    par_p = ctypes.POINTER(ParamsStruct)
+    sigs = {
+        "pkm_config_check": (ctypes.c_int, [cfg_p]),
+        "pkm_workspace_bytes": (ctypes.c_int, [cfg_p, ctypes.POINTER(ctypes.c_size_t)]),
+        "pkm_create": (ctypes.c_int, [cfg_p, ctypes.POINTER(vp)]),
+        "pkm_destroy": (None, [vp]),
+        "pkm_forward": (ctypes.c_int, [vp, par_p, i64, vp, vp, vp, vp, vp]),
+        "pkm_query": (ctypes.c_int, [vp, par_p, i64, vp, vp, vp]),
+        "pkm_score": (ctypes.c_int, [vp, par_p, i64, vp, vp, vp]),
+        "pkm_select": (ctypes.c_int, [vp, i64, vp, vp, vp, vp]),
+        "pkm_gather": (ctypes.c_int, [vp, par_p, i64, i32, vp, vp, vp, vp]),
+        "pkm_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+        "pkm_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def status_str(status):
+    return load_library().pkm_status_str(int(status)).decode()
+
+
+def last_error():
+    return load_library().pkm_last_error().decode()
+
+
+def _check(status):
+    if status != PKM_OK:
+        raise PkmError(status, last_error())
+
+
+def make_config(dim, heads, n_keys, k, value_type="bf16", bn_eps=1e-5, max_batch=16384):
+    vt = VALUE_TYPES[value_type] if isinstance(value_type, str) else int(value_type)
+    return Config(int(dim), int(heads), int(n_keys), int(k), vt, float(bn_eps), int(max_batch))
+
+
+def config_check(cfg):
+    """PKM status code for a Config (touches no device)."""
+    return load_library().pkm_config_check(ctypes.byref(cfg))
+
+
+def workspace_bytes(cfg):
+    out = ctypes.c_size_t(0)
+    _check(load_library().pkm_workspace_bytes(ctypes.byref(cfg), ctypes.byref(out)))
+    return out.value
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _stream_handle(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+# Accepted storage dtypes of the value table (bit patterns are what matter).
+_DT = {"f32": ("float32",), "bf16": ("bfloat16", "int16", "uint16"), "e4m3": ("float8_e4m3fn", "uint8", "int8")}
+
+
+def _expect(t, name, shape, dtype, device=None):
+    """Shape / dtype / contiguity / device check of one tensor argument."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    dtypes = (dtype,) if isinstance(dtype, str) else dtype
+    if str(t.dtype) not in ["torch." + d for d in dtypes]:
+        raise ValueError(f"{name}: expected one of {dtypes}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device.type != "cuda" or (device is not None and t.device != device):
+        raise ValueError(f"{name} must live on {device or 'the GPU'}, got {t.device}")
+    if t.data_ptr() % 16:
+        raise ValueError(f"{name} must be 16-byte aligned")
+
+
+class Params:
+    """Device tensors of one lookup's parameters (kept alive by this object).
+
+    wq [H,D,D] f32; bn_mean/bn_var/bn_gamma/bn_beta [H,D] f32;
+    subkeys [H,2,n,D/2] f32; values [N,D] float32 / bfloat16 / float8_e4m3fn
+    (or an integer type of the same width holding the bits); value_scale [N]
+    f32 for E4M3 tables (else None)."""
+
+    def __init__(self, wq, bn_mean, bn_var, bn_gamma, bn_beta, subkeys, values, value_scale=None):
+        self.tensors = dict(wq=wq, bn_mean=bn_mean, bn_var=bn_var, bn_gamma=bn_gamma, bn_beta=bn_beta,
+                            subkeys=subkeys, values=values, value_scale=value_scale)
+        self.struct = ParamsStruct(*[None if t is None else t.data_ptr() for t in self.tensors.values()])
+
+    def __getitem__(self, name):
+        return self.tensors[name]
+
+
+class Memory:
+    """A library context for one (D, H, n_keys, k, table type) on the current
+    device.  Calls enqueue on the given stream (default: torch's current
+    stream) and return without synchronising."""
+
+    def __init__(self, dim, heads, n_keys, k, value_type="bf16", bn_eps=1e-5, max_batch=16384):
+        self.lib = load_library()
+        self.cfg = make_config(dim, heads, n_keys, k, value_type, bn_eps, max_batch)
+        self.dim, self.heads, self.n_keys, self.k = int(dim), int(heads), int(n_keys), int(k)
+        self.value_type = value_type
+        handle = ctypes.c_void_p()
+        _check(self.lib.pkm_create(ctypes.byref(self.cfg), ctypes.byref(handle)))
+        self._ctx = handle
+
+    def close(self):
+        if getattr(self, "_ctx", None):
+            self.lib.pkm_destroy(self._ctx)
+            self._ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    # ------------------------------------------------------------- helpers
+    def _new(self, shape, dtype, like):
+        torch = _torch()
+        return torch.empty(shape, dtype=dtype, device=like.device)
+
+    def check_params(self, params, parts=("query", "subkeys", "values")):
+        """Checks params against this context's shapes before any launch."""
+        D, H, n = self.dim, self.heads, self.n_keys
+        t = params.tensors
+        dev = t["wq"].device if t.get("wq") is not None else None
+        if "query" in parts:
+            _expect(t["wq"], "wq", (H, D, D), "float32")
+            for name in ("bn_mean", "bn_var", "bn_gamma", "bn_beta"):
+                _expect(t[name], name, (H, D), "float32", dev)
+        if "subkeys" in parts:
+            _expect(t["subkeys"], "subkeys", (H, 2, n, D // 2), "float32", dev)
+        if "values" in parts:
+            vt = self.value_type
+            _expect(t["values"], "values", (n * n, D), _DT[vt], dev)
+            if vt == "e4m3":
+                _expect(t["value_scale"], "value_scale", (n * n,), "float32", t["values"].device)
+
+    def forward(self, params, x, out=None, idx=None, weights=None, stream=None, keep_selection=True):
+        """The whole lookup.  Returns (out [B,D] f32, idx [B,H,k] i32,
+        weights [B,H,k] f32); idx/weights are None when keep_selection is
+        False and none were given."""
+        torch = _torch()
+        B = x.shape[0]
+        self.check_params(params)
+        _expect(x, "x", (B, self.dim), "float32", params["wq"].device)
+        out = self._new((B, self.dim), torch.float32, x) if out is None else out
+        _expect(out, "out", (B, self.dim), "float32", x.device)
+        if keep_selection:
+            idx = self._new((B, self.heads, self.k), torch.int32, x) if idx is None else idx
+            weights = self._new((B, self.heads, self.k), torch.float32, x) if weights is None else weights
+        for t, name, dt in ((idx, "idx", "int32"), (weights, "weights", "float32")):
+            if t is not None:
+                _expect(t, name, (B, self.heads, self.k), dt, x.device)
+        _check(self.lib.pkm_forward(self._ctx, ctypes.byref(params.struct), B, _ptr(x), _ptr(out), _ptr(idx),
+                                    _ptr(weights), _stream_handle(stream)))
+        return out, idx, weights
+
+    def query(self, params, x, qhat=None, stream=None):
+        torch = _torch()
+        self.check_params(params, ("query",))
+        _expect(x, "x", (x.shape[0], self.dim), "float32", params["wq"].device)
+        qhat = self._new((x.shape[0], self.heads, self.dim), torch.float32, x) if qhat is None else qhat
+        _expect(qhat, "qhat", (x.shape[0], self.heads, self.dim), "float32", x.device)
+        _check(self.lib.pkm_query(self._ctx, ctypes.byref(params.struct), x.shape[0], _ptr(x), _ptr(qhat),
+                                  _stream_handle(stream)))
+        return qhat
+
+    def score(self, params, qhat, scores=None, stream=None):
+        torch = _torch()
+        B = qhat.shape[0]
+        self.check_params(params, ("subkeys",))
+        _expect(qhat, "qhat", (B, self.heads, self.dim), "float32", params["subkeys"].device)
+        scores = self._new((B, self.heads, 2, self.n_keys), torch.float32, qhat) if scores is None else scores
+        _expect(scores, "scores", (B, self.heads, 2, self.n_keys), "float32", qhat.device)
+        _check(self.lib.pkm_score(self._ctx, ctypes.byref(params.struct), B, _ptr(qhat), _ptr(scores),
+                                  _stream_handle(stream)))
+        return scores
+
+    def select(self, scores, idx=None, weights=None, stream=None):
+        torch = _torch()
+        B = scores.shape[0]
+        _expect(scores, "scores", (B, self.heads, 2, self.n_keys), "float32")
+        idx = self._new((B, self.heads, self.k), torch.int32, scores) if idx is None else idx
+        weights = self._new((B, self.heads, self.k), torch.float32, scores) if weights is None else weights
+        _expect(idx, "idx", (B, self.heads, self.k), "int32", scores.device)
+        _expect(weights, "weights", (B, self.heads, self.k), "float32", scores.device)
+        _check(self.lib.pkm_select(self._ctx, B, _ptr(scores), _ptr(idx), _ptr(weights), _stream_handle(stream)))
+        return idx, weights
+
+    def gather(self, params, idx, weights, out=None, stream=None):
+        """idx / weights [B, R] (or [B, H, k]); out [B, D] f32."""
+        torch = _torch()
+        B = idx.shape[0]
+        R = idx.numel() // max(B, 1)
+        self.check_params(params, ("values",))
+        _expect(idx, "idx", tuple(idx.shape), "int32", params["values"].device)
+        _expect(weights, "weights", tuple(idx.shape), "float32", idx.device)
+        if B and idx.numel() != B * R:
+            raise ValueError("idx must hold the same number of rows for every token")
+        out = self._new((B, self.dim), torch.float32, idx) if out is None else out
+        _expect(out, "out", (B, self.dim), "float32", idx.device)
+        _check(self.lib.pkm_gather(self._ctx, ctypes.byref(params.struct), B, R, _ptr(idx), _ptr(weights),
+                                   _ptr(out), _stream_handle(stream)))
+        return out

@@ -1,0 +1,154 @@
+// Step a7: out[b,:] = sum_r w[b,r] * scale[row] * values[row,:], row = idx[b,r]
+// -- the gather and weighted sum EmbeddingBag(mode="sum", per_sample_weights)
+// performs in one pass ("Product-Key Memory", the note after the code
+// listing: the table is never touched as a dense matrix, only the selected
+// rows are read).
+//
+// This is the HBM-bound step: every selected row is a random 1-4 KiB read.
+// A wave64 owns one (token, column slice): each lane reads 16 contiguous bytes
+// of a row (4 fp32, 8 bf16 or 16 E4M3 values), so one row-slice is one fully
+// coalesced 1 KiB request, and keeps its fp32 partial sums in registers.  The
+// token's (row, weight) pairs are read once into lanes and broadcast with
+// v_readlane, so every row address is a scalar base plus the lane offset.
+// Sixteen row loads are issued before any is consumed to keep enough bytes in
+// flight per wave.  Rows are summed in their given order, so results are
+// bitwise reproducible.  A row index outside [0, N) is clamped into range
+// (memory-safe; the result for such a row is meaningless).
+#include "pkm_internal.h"
+
+namespace pkm {
+namespace {
+
+constexpr int WAVES = 4;
+constexpr int UNROLL = 16;  // row loads in flight per wave
+
+template <int VT>
+struct Fmt;
+template <>
+struct Fmt<0> {  // fp32
+    static constexpr int EPL = 4;
+    static constexpr int BYTES = 4;
+};
+template <>
+struct Fmt<1> {  // bf16
+    static constexpr int EPL = 8;
+    static constexpr int BYTES = 2;
+};
+template <>
+struct Fmt<2> {  // OCP E4M3 + row scale
+    static constexpr int EPL = 16;
+    static constexpr int BYTES = 1;
+};
+
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+
+template <int VT>
+__device__ __forceinline__ void accumulate(float (&acc)[Fmt<VT>::EPL], const uint4 &v, float wt)
+{
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    if constexpr (VT == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = fmaf(wt, __uint_as_float(w[i]), acc[i]);
+    } else if constexpr (VT == 1) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc[2 * i] = fmaf(wt, __uint_as_float(w[i] << 16), acc[2 * i]);
+            acc[2 * i + 1] = fmaf(wt, __uint_as_float(w[i] & 0xFFFF0000u), acc[2 * i + 1]);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const floatx2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
+            const floatx2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);
+            acc[4 * i + 0] = fmaf(wt, lo.x, acc[4 * i + 0]);
+            acc[4 * i + 1] = fmaf(wt, lo.y, acc[4 * i + 1]);
+            acc[4 * i + 2] = fmaf(wt, hi.x, acc[4 * i + 2]);
+            acc[4 * i + 3] = fmaf(wt, hi.y, acc[4 * i + 3]);
+        }
+    }
+}
+
+template <int VT>
+__global__ __launch_bounds__(64 * WAVES) void gather_kernel(const uint8_t *__restrict__ values,
+                                                            const float *__restrict__ scale, int D, int N, int64_t B, int R,
+                                                            int slices, const int32_t *__restrict__ idx,
+                                                            const float *__restrict__ w, float *__restrict__ out)
+{
+    constexpr int EPL = Fmt<VT>::EPL;
+    constexpr int BYTES = Fmt<VT>::BYTES;
+    const int lane = threadIdx.x & 63;
+    const int64_t wid = (int64_t)blockIdx.x * WAVES + (threadIdx.x >> 6);
+    if (wid >= B * slices) return;
+    const int64_t b = wid / slices;
+    const int s = (int)(wid - b * slices);
+    const int c0 = (s * 64 + lane) * EPL;  // first column of this lane
+    const bool active = c0 < D;
+    const int64_t row_bytes = (int64_t)D * BYTES;
+    const uint8_t *col = values + (active ? (int64_t)c0 * BYTES : 0);
+
+    float acc[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
+
+    const int32_t *ib = idx + b * R;
+    const float *wb = w + b * R;
+    for (int r0 = 0; r0 < R; r0 += 64) {
+        const int nr = min(64, R - r0);
+        const int my_row = lane < nr ? ib[r0 + lane] : 0;
+        const float my_w = lane < nr ? wb[r0 + lane] : 0.0f;
+        int r = 0;
+        for (; r + UNROLL <= nr; r += UNROLL) {
+            uint4 v[UNROLL];
+            float wt[UNROLL];
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                const int row = min(max(__builtin_amdgcn_readlane(my_row, r + u), 0), N - 1);
+                wt[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), r + u));
+                if constexpr (VT == 2) wt[u] *= scale[row];
+                v[u] = active ? *reinterpret_cast<const uint4 *>(col + (int64_t)row * row_bytes) : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) accumulate<VT>(acc, v[u], wt[u]);
+        }
+        for (; r < nr; ++r) {
+            const int row = min(max(__builtin_amdgcn_readlane(my_row, r), 0), N - 1);
+            float wt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), r));
+            if constexpr (VT == 2) wt *= scale[row];
+            const uint4 v = active ? *reinterpret_cast<const uint4 *>(col + (int64_t)row * row_bytes) : make_uint4(0, 0, 0, 0);
+            accumulate<VT>(acc, v, wt);
+        }
+    }
+    if (active) {
+        float4 *o = reinterpret_cast<float4 *>(out + b * D + c0);
+#pragma unroll
+        for (int e = 0; e < EPL / 4; ++e) o[e] = make_float4(acc[4 * e], acc[4 * e + 1], acc[4 * e + 2], acc[4 * e + 3]);
+    }
+}
+
+template <int VT>
+hipError_t launch(const void *values, const float *scale, int D, int N, int64_t B, int R, const int32_t *idx,
+                  const float *w, float *out, hipStream_t stream)
+{
+    const int width = 64 * Fmt<VT>::EPL;  // columns per wave
+    const int slices = (D + width - 1) / width;
+    const int64_t waves = B * slices;
+    const int64_t blocks = (waves + WAVES - 1) / WAVES;
+    hipLaunchKernelGGL(gather_kernel<VT>, dim3((unsigned)blocks), dim3(64 * WAVES), 0, stream,
+                       static_cast<const uint8_t *>(values), scale, D, N, B, R, slices, idx, w, out);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gather(const void *values, const float *scale, int value_type, int D, int N, int64_t B, int R,
+                         const int32_t *idx, const float *w, float *out, hipStream_t stream)
+{
+    if (B <= 0) return hipSuccess;
+    switch (value_type) {
+    case 0: return launch<0>(values, scale, D, N, B, R, idx, w, out, stream);
+    case 1: return launch<1>(values, scale, D, N, B, R, idx, w, out, stream);
+    default: return launch<2>(values, scale, D, N, B, R, idx, w, out, stream);
+    }
+}
+
+}  // namespace pkm

@@ -1,0 +1,378 @@
+// Host side of the C ABI declared in include/pkm.h: argument validation,
+// workspace, batch chunking and the launch sequence on the caller's stream.
+#include "pkm.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "pkm_internal.h"
+
+struct pkm_ctx {
+    pkm_config cfg;
+    int device;
+    void *workspace;
+    float *qhat;     // [max_batch, H, D]
+    float *scores;   // [max_batch, H, 2, n]
+    int32_t *idx;    // [max_batch, H, k]
+    float *weights;  // [max_batch, H, k]
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+// Launch grids are sized from B (one wave per token-slice or per token-head):
+// keep every grid well inside 2^31 workgroups.
+constexpr int64_t kMaxBatch = (int64_t)1 << 30;
+
+pkm_status fail(pkm_status s, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    if (const char *log = getenv("PKM_LOG"); log && log[0] == '1') fprintf(stderr, "pkm: %s\n", buf);
+    return s;
+}
+
+pkm_status ok()
+{
+    g_last_error.clear();
+    return PKM_OK;
+}
+
+bool log_on()
+{
+    const char *log = getenv("PKM_LOG");
+    return log && log[0] == '1';
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Workspace pieces for one chunk of mb tokens; false on size overflow.
+bool workspace_layout(const pkm_config &c, size_t sizes[4])
+{
+    const double mb = (double)c.max_batch;
+    const double total = mb * c.heads * ((double)c.dim + 2.0 * c.n_keys + 2.0 * c.k) * 4.0;
+    if (total > 1.0e15) return false;
+    const size_t m = (size_t)c.max_batch, H = (size_t)c.heads;
+    sizes[0] = round_up(m * H * (size_t)c.dim * sizeof(float));
+    sizes[1] = round_up(m * H * 2 * (size_t)c.n_keys * sizeof(float));
+    sizes[2] = round_up(m * H * (size_t)c.k * sizeof(int32_t));
+    sizes[3] = round_up(m * H * (size_t)c.k * sizeof(float));
+    return true;
+}
+
+pkm_status check_config(const pkm_config *c)
+{
+    if (!c) return fail(PKM_E_ARG, "config is NULL");
+    if (c->dim < 2 || (c->dim & 1)) return fail(PKM_E_ARG, "dim must be even and >= 2 (got %d)", c->dim);
+    if (c->heads < 1) return fail(PKM_E_ARG, "heads must be >= 1 (got %d)", c->heads);
+    if (c->n_keys < 2) return fail(PKM_E_ARG, "n_keys must be >= 2 (got %d)", c->n_keys);
+    if ((int64_t)c->n_keys * c->n_keys >= ((int64_t)1 << 31))
+        return fail(PKM_E_ARG, "n_keys^2 must be < 2^31 (got n_keys = %d)", c->n_keys);
+    if (c->k < 1 || c->k > c->n_keys) return fail(PKM_E_ARG, "k must be in [1, n_keys] (got %d)", c->k);
+    if (c->value_type < PKM_VALUES_F32 || c->value_type > PKM_VALUES_FP8_E4M3)
+        return fail(PKM_E_ARG, "unknown value_type %d", c->value_type);
+    if (!(c->bn_eps > 0.0f) || !(c->bn_eps < 1.0e30f)) return fail(PKM_E_ARG, "bn_eps must be finite and > 0");
+    if (c->max_batch < 1 || c->max_batch > kMaxBatch || c->max_batch * c->heads > ((int64_t)1 << 31))
+        return fail(PKM_E_ARG, "max_batch must be in [1, 2^30] with max_batch * heads <= 2^31");
+    if ((int64_t)c->heads * c->dim >= ((int64_t)1 << 30)) return fail(PKM_E_ARG, "heads * dim too large");
+    size_t sizes[4];
+    if (!workspace_layout(*c, sizes)) return fail(PKM_E_ARG, "workspace size overflows");
+    if (c->dim % 64 != 0) return fail(PKM_E_UNSUPPORTED, "dim must be a multiple of 64 (got %d)", c->dim);
+    if (c->k > 64) return fail(PKM_E_UNSUPPORTED, "k > 64 is not supported (got %d)", c->k);
+    if (c->n_keys > 4096) return fail(PKM_E_UNSUPPORTED, "n_keys > 4096 is not supported (got %d)", c->n_keys);
+    return ok();
+}
+
+pkm_status check_ctx(const pkm_ctx *ctx)
+{
+    if (!ctx) return fail(PKM_E_ARG, "context is NULL");
+    return PKM_OK;
+}
+
+pkm_status check_batch(const pkm_config &c, int64_t B)
+{
+    if (B < 0) return fail(PKM_E_ARG, "B must be >= 0 (got %lld)", (long long)B);
+    if (B > kMaxBatch || B * c.heads > ((int64_t)1 << 31))
+        return fail(PKM_E_ARG, "B = %lld is too large for one call (B <= 2^30 and B * heads <= 2^31)", (long long)B);
+    return PKM_OK;
+}
+
+pkm_status need(const void *p, const char *name)
+{
+    if (!p) return fail(PKM_E_ARG, "%s is NULL", name);
+    if (!aligned16(p)) return fail(PKM_E_ARG, "%s is not 16-byte aligned", name);
+    return PKM_OK;
+}
+
+pkm_status check_query_params(const pkm_params *p)
+{
+    if (!p) return fail(PKM_E_ARG, "params is NULL");
+    pkm_status s;
+    if ((s = need(p->wq, "wq")) || (s = need(p->bn_mean, "bn_mean")) || (s = need(p->bn_var, "bn_var")) ||
+        (s = need(p->bn_gamma, "bn_gamma")) || (s = need(p->bn_beta, "bn_beta")))
+        return s;
+    return PKM_OK;
+}
+
+pkm_status check_value_params(const pkm_config &c, const pkm_params *p)
+{
+    if (!p) return fail(PKM_E_ARG, "params is NULL");
+    pkm_status s;
+    if ((s = need(p->values, "values"))) return s;
+    if (c.value_type == PKM_VALUES_FP8_E4M3 && (s = need(p->value_scale, "value_scale"))) return s;
+    return PKM_OK;
+}
+
+pkm_status launched(hipError_t e, const char *what)
+{
+    if (e != hipSuccess) return fail(PKM_E_DEVICE, "%s launch failed: %s", what, hipGetErrorString(e));
+    return PKM_OK;
+}
+
+pkm::GemmArgs query_args(const pkm_config &c, const pkm_params *p, int64_t B, const float *x, float *qhat)
+{
+    pkm::GemmArgs a{};
+    a.A = x;
+    a.lda = c.dim;
+    a.strideA = 0;
+    a.B = p->wq;
+    a.ldb = c.dim;
+    a.strideB = 0;
+    a.C = qhat;
+    a.ldc = (int64_t)c.heads * c.dim;
+    a.strideC = 0;
+    a.M = (int)B;
+    a.N = c.heads * c.dim;
+    a.K = c.dim;
+    a.batch = 1;
+    a.bn_mean = p->bn_mean;
+    a.bn_var = p->bn_var;
+    a.bn_gamma = p->bn_gamma;
+    a.bn_beta = p->bn_beta;
+    a.bn_eps = c.bn_eps;
+    return a;
+}
+
+pkm::GemmArgs score_args(const pkm_config &c, const pkm_params *p, int64_t B, const float *qhat, float *scores)
+{
+    const int half = c.dim / 2;
+    pkm::GemmArgs a{};
+    a.A = qhat;  // head h, half p starts at column (2h + p) * D/2
+    a.lda = (int64_t)c.heads * c.dim;
+    a.strideA = half;
+    a.B = p->subkeys;  // [2H][n][D/2]
+    a.ldb = half;
+    a.strideB = (int64_t)c.n_keys * half;
+    a.C = scores;  // [B][2H][n]
+    a.ldc = (int64_t)2 * c.heads * c.n_keys;
+    a.strideC = c.n_keys;
+    a.M = (int)B;
+    a.N = c.n_keys;
+    a.K = half;
+    a.batch = 2 * c.heads;
+    return a;
+}
+
+// The GEMM launcher takes M as int; B <= 2^30 keeps one launch per call.
+constexpr int64_t kGemmRows = kMaxBatch;
+
+pkm_status run_query(const pkm_config &c, const pkm_params *p, int64_t B, const float *x, float *qhat,
+                     hipStream_t st)
+{
+    for (int64_t b0 = 0; b0 < B; b0 += kGemmRows) {
+        const int64_t nb = B - b0 < kGemmRows ? B - b0 : kGemmRows;
+        pkm::GemmArgs a = query_args(c, p, nb, x + b0 * c.dim, qhat + b0 * (int64_t)c.heads * c.dim);
+        if (pkm_status s = launched(pkm::launch_gemm_nt_f32(a, st), "query projection")) return s;
+    }
+    return PKM_OK;
+}
+
+pkm_status run_score(const pkm_config &c, const pkm_params *p, int64_t B, const float *qhat, float *scores,
+                     hipStream_t st)
+{
+    for (int64_t b0 = 0; b0 < B; b0 += kGemmRows) {
+        const int64_t nb = B - b0 < kGemmRows ? B - b0 : kGemmRows;
+        pkm::GemmArgs a = score_args(c, p, nb, qhat + b0 * (int64_t)c.heads * c.dim,
+                                     scores + b0 * (int64_t)2 * c.heads * c.n_keys);
+        if (pkm_status s = launched(pkm::launch_gemm_nt_f32(a, st), "subkey scoring")) return s;
+    }
+    return PKM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pkm_status pkm_config_check(const pkm_config *cfg) { return check_config(cfg); }
+
+pkm_status pkm_workspace_bytes(const pkm_config *cfg, size_t *bytes)
+{
+    if (pkm_status s = check_config(cfg)) return s;
+    if (!bytes) return fail(PKM_E_ARG, "bytes is NULL");
+    size_t sizes[4];
+    workspace_layout(*cfg, sizes);
+    *bytes = sizes[0] + sizes[1] + sizes[2] + sizes[3];
+    return ok();
+}
+
+pkm_status pkm_create(const pkm_config *cfg, pkm_ctx **out)
+{
+    if (!out) return fail(PKM_E_ARG, "out is NULL");
+    *out = nullptr;
+    if (pkm_status s = check_config(cfg)) return s;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(PKM_E_DEVICE, "no HIP device: %s", hipGetErrorString(e));
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail(PKM_E_DEVICE, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+        return fail(PKM_E_UNSUPPORTED, "device %d is %s; the kernels are built for gfx950", dev, prop.gcnArchName);
+    size_t sizes[4];
+    workspace_layout(*cfg, sizes);
+    const size_t total = sizes[0] + sizes[1] + sizes[2] + sizes[3];
+    void *ws = nullptr;
+    e = hipMalloc(&ws, total);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(PKM_E_NOMEM, "workspace of %zu bytes: %s", total, hipGetErrorString(e));
+    }
+    pkm_ctx *ctx = new (std::nothrow) pkm_ctx;
+    if (!ctx) {
+        (void)hipFree(ws);
+        return fail(PKM_E_NOMEM, "host allocation failed");
+    }
+    ctx->cfg = *cfg;
+    ctx->device = dev;
+    ctx->workspace = ws;
+    char *w = static_cast<char *>(ws);
+    ctx->qhat = reinterpret_cast<float *>(w);
+    ctx->scores = reinterpret_cast<float *>(w + sizes[0]);
+    ctx->idx = reinterpret_cast<int32_t *>(w + sizes[0] + sizes[1]);
+    ctx->weights = reinterpret_cast<float *>(w + sizes[0] + sizes[1] + sizes[2]);
+    if (log_on())
+        fprintf(stderr, "pkm: context on device %d (%s): D=%d H=%d n=%d k=%d values=%d max_batch=%lld workspace=%zu\n",
+                dev, prop.gcnArchName, cfg->dim, cfg->heads, cfg->n_keys, cfg->k, cfg->value_type,
+                (long long)cfg->max_batch, total);
+    *out = ctx;
+    return ok();
+}
+
+void pkm_destroy(pkm_ctx *ctx)
+{
+    if (!ctx) return;
+    (void)hipFree(ctx->workspace);
+    delete ctx;
+}
+
+pkm_status pkm_forward(pkm_ctx *ctx, const pkm_params *p, int64_t B, const float *x, float *out, int32_t *idx,
+                       float *weights, void *stream)
+{
+    pkm_status s;
+    if ((s = check_ctx(ctx)) || (s = check_batch(ctx->cfg, B))) return s;
+    if (B == 0) return ok();
+    const pkm_config &c = ctx->cfg;
+    if ((s = check_query_params(p)) || (s = need(p->subkeys, "subkeys")) || (s = check_value_params(c, p))) return s;
+    if ((s = need(x, "x")) || (s = need(out, "out"))) return s;
+    if ((idx && !aligned16(idx)) || (weights && !aligned16(weights)))
+        return fail(PKM_E_ARG, "idx / weights must be 16-byte aligned");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int64_t H = c.heads, D = c.dim, k = c.k;
+    for (int64_t b0 = 0; b0 < B; b0 += c.max_batch) {
+        const int64_t nb = B - b0 < c.max_batch ? B - b0 : c.max_batch;
+        int32_t *ci = idx ? idx + b0 * H * k : ctx->idx;
+        float *cw = weights ? weights + b0 * H * k : ctx->weights;
+        if ((s = run_query(c, p, nb, x + b0 * D, ctx->qhat, st))) return s;
+        if ((s = run_score(c, p, nb, ctx->qhat, ctx->scores, st))) return s;
+        if ((s = launched(pkm::launch_select(ctx->scores, nb, c.heads, c.n_keys, c.k, ci, cw, st), "select")))
+            return s;
+        if ((s = launched(pkm::launch_gather(p->values, p->value_scale, c.value_type, c.dim, c.n_keys * c.n_keys, nb, (int)(H * k), ci, cw,
+                                             out + b0 * D, st),
+                          "gather")))
+            return s;
+    }
+    return ok();
+}
+
+pkm_status pkm_query(pkm_ctx *ctx, const pkm_params *p, int64_t B, const float *x, float *qhat, void *stream)
+{
+    pkm_status s;
+    if ((s = check_ctx(ctx)) || (s = check_batch(ctx->cfg, B))) return s;
+    if (B == 0) return ok();
+    if ((s = check_query_params(p))) return s;
+    if ((s = need(x, "x")) || (s = need(qhat, "qhat"))) return s;
+    if ((s = run_query(ctx->cfg, p, B, x, qhat, static_cast<hipStream_t>(stream)))) return s;
+    return ok();
+}
+
+pkm_status pkm_score(pkm_ctx *ctx, const pkm_params *p, int64_t B, const float *qhat, float *scores, void *stream)
+{
+    pkm_status s;
+    if ((s = check_ctx(ctx)) || (s = check_batch(ctx->cfg, B))) return s;
+    if (B == 0) return ok();
+    if (!p) return fail(PKM_E_ARG, "params is NULL");
+    if ((s = need(p->subkeys, "subkeys")) || (s = need(qhat, "qhat")) || (s = need(scores, "scores"))) return s;
+    if ((s = run_score(ctx->cfg, p, B, qhat, scores, static_cast<hipStream_t>(stream)))) return s;
+    return ok();
+}
+
+pkm_status pkm_select(pkm_ctx *ctx, int64_t B, const float *scores, int32_t *idx, float *weights, void *stream)
+{
+    pkm_status s;
+    if ((s = check_ctx(ctx)) || (s = check_batch(ctx->cfg, B))) return s;
+    if (B == 0) return ok();
+    if ((s = need(scores, "scores")) || (s = need(idx, "idx")) || (s = need(weights, "weights"))) return s;
+    const pkm_config &c = ctx->cfg;
+    if ((s = launched(pkm::launch_select(scores, B, c.heads, c.n_keys, c.k, idx, weights,
+                                         static_cast<hipStream_t>(stream)),
+                      "select")))
+        return s;
+    return ok();
+}
+
+pkm_status pkm_gather(pkm_ctx *ctx, const pkm_params *p, int64_t B, int32_t rows_per_token, const int32_t *idx,
+                      const float *weights, float *out, void *stream)
+{
+    pkm_status s;
+    if ((s = check_ctx(ctx)) || (s = check_batch(ctx->cfg, B))) return s;
+    if (B == 0) return ok();
+    const pkm_config &c = ctx->cfg;
+    if ((s = check_value_params(c, p))) return s;
+    if (rows_per_token < 1) return fail(PKM_E_ARG, "rows_per_token must be >= 1 (got %d)", rows_per_token);
+    if ((s = need(idx, "idx")) || (s = need(weights, "weights")) || (s = need(out, "out"))) return s;
+    if ((s = launched(pkm::launch_gather(p->values, p->value_scale, c.value_type, c.dim, c.n_keys * c.n_keys, B,
+                                         rows_per_token, idx,
+                                         weights, out, static_cast<hipStream_t>(stream)),
+                      "gather")))
+        return s;
+    return ok();
+}
+
+const char *pkm_status_str(pkm_status s)
+{
+    switch (s) {
+    case PKM_OK: return "ok";
+    case PKM_E_ARG: return "invalid argument";
+    case PKM_E_UNSUPPORTED: return "unsupported configuration or device";
+    case PKM_E_NOMEM: return "device allocation failed";
+    case PKM_E_DEVICE: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char *pkm_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,40 @@
+// Internal launch interface between the host library (pkm_api.cpp) and the
+// gfx950 kernels.  Every launcher enqueues on `stream` and returns the
+// hipError_t of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkm {
+
+// C[g][m][n] = sum_k A[g][m][k] * B[g][n][k]  (both operands K-contiguous),
+// for g < batch, m < M, n < N; K % 32 == 0.  With bn_* non-null the epilogue
+// applies inference BatchNorm to column n:
+//   (c - mean[n]) / sqrt(var[n] + eps) * gamma[n] + beta[n].
+struct GemmArgs {
+    const float *A;
+    int64_t lda, strideA;
+    const float *B;
+    int64_t ldb, strideB;
+    float *C;
+    int64_t ldc, strideC;
+    int M, N, K, batch;
+    const float *bn_mean, *bn_var, *bn_gamma, *bn_beta;
+    float bn_eps;
+};
+hipError_t launch_gemm_nt_f32(const GemmArgs &a, hipStream_t stream);
+
+// Per (token, head): exact top-k of each half's n scores, the k*k candidate
+// grid, its exact top-k and the softmax.  scores [B][H][2][n] -> idx, w
+// [B][H][k].  k <= 64, n <= 4096.
+hipError_t launch_select(const float *scores, int64_t B, int H, int n, int k, int32_t *idx, float *w,
+                         hipStream_t stream);
+
+// out[b][:] = sum_r w[b][r] * scale[row] * values[row][:], row = idx[b][r],
+// r < R, N table rows (rows are clamped into [0, N)).  value_type: 0 f32,
+// 1 bf16, 2 E4M3 (+ row scale).
+hipError_t launch_gather(const void *values, const float *scale, int value_type, int D, int N, int64_t B, int R,
+                         const int32_t *idx, const float *w, float *out, hipStream_t stream);
+
+}  // namespace pkm

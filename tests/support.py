@@ -38,9 +38,16 @@ def key_l1_mass(wl, params, qhat, flat, h):
 def gaps_and_tau(wl, params, x, model=None):
     """Per (token, head): fp64 gap between the k-th and (k+1)-th full scores,
     and the tau it must clear.  Both [B, H]."""
-    model = model or model_for(wl, params)
     k = wl.k
-    r = oracle.run(model, x, kk=k + 1, want=("top", "idx", "qhat"))
+    if k + 1 <= wl.n:
+        model = model or model_for(wl, params)
+        r = oracle.run(model, x, kk=k + 1, want=("top", "idx", "qhat"))
+    else:
+        # k = n_keys: a half has no (k+1)-th subkey, so take the exact
+        # top-(k+1) from the flat search over all n_keys^2 keys instead
+        from tests import pins
+
+        r = pins.flat_search(params, x, k + 1, with_values=False)
     gap = r["top"][:, :, k - 1] - r["top"][:, :, k]
     B = x.shape[0]
     tau = np.empty((B, wl.H))
@@ -56,7 +63,7 @@ def gap_clean(wl, params, x, tokens=None, seed=0, max_attempts=60):
     model = model_for(wl, params)
     todo = np.arange(x.shape[0]) if tokens is None else np.asarray(tokens)
     attempts = np.zeros(x.shape[0], dtype=np.int64)
-    if wl.k >= wl.n:
+    if wl.k >= wl.N:
         return attempts  # no (k+1)-th key: every key is a winner
     for _ in range(max_attempts):
         gap, tau = gaps_and_tau(wl, params, x[todo], model)
@@ -100,3 +107,44 @@ def check_indices(idx, ref_idx, ref_top, tau):
             pos = {int(v): i for i, v in enumerate(ref_idx[b, h])}
             got_blocks = np.array([block[b, h, pos[int(v)]] for v in idx[b, h]])
             assert (got_blocks == block[b, h]).all(), f"order differs at token {b} head {h}"
+
+
+# ------------------------------------------------------------------ GPU side
+
+def device():
+    import torch
+
+    if not torch.cuda.is_available():
+        raise RuntimeError("GPU tests need a GPU")
+    return torch.device("cuda:0")
+
+
+def say(*args):
+    """Names the case about to touch the GPU (flushed, so a lost box still
+    tells which case was running)."""
+    print("[gpu]", *args, flush=True)
+
+
+def gpu_forward(wl, params, x, max_batch=16384, mem=None, dev_params=None):
+    """Runs the whole lookup on the GPU; returns numpy (out, idx, w)."""
+    import torch
+
+    import product_key_memory_amd as pk
+
+    say("forward", wl, "B =", x.shape[0], "max_batch =", max_batch)
+    mem = mem or pk.Memory(wl.D, wl.H, wl.n, wl.k, wl.table, max_batch=max_batch)
+    P = dev_params or pk.params_to_device(params, wl.table, device())
+    xt = torch.from_numpy(np.ascontiguousarray(x)).to(device())
+    out, idx, w = mem.forward(P, xt)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy()
+
+
+def weights_by_index(idx, w, ref_idx):
+    """Reorders w [B,H,k] so that entry j belongs to ref_idx[..., j] (the
+    winner sets are already known to be equal)."""
+    order = np.argsort(idx, -1)
+    ref_order = np.argsort(ref_idx, -1)
+    sorted_w = np.take_along_axis(w, order, -1)
+    inv = np.argsort(ref_order, -1)
+    return np.take_along_axis(sorted_w, inv, -1)

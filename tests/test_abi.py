@@ -1,0 +1,111 @@
+"""CPU: the C-ABI library loads, exports every symbol include/pkm.h declares,
+and rejects bad configurations and arguments on the host, before any device
+work.  Nothing here launches a kernel or touches a GPU."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import product_key_memory_amd as pk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkm.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkm_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(pk.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = pk.load_library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", pk.LIB_PATH], capture_output=True, text=True, check=True)
+    exported = set(re.findall(r"\sT\s(pkm_\w+)", out.stdout))
+    assert set(declared_functions()) <= exported
+
+
+def test_library_has_gfx950_code_object():
+    """Each kernel source contributes one gfx950 offload bundle entry."""
+    blob = open(pk.LIB_PATH, "rb").read()
+    assert blob.count(b"hipv4-amdgcn-amd-amdhsa--gfx950") >= 3
+
+
+def test_status_strings():
+    assert pk.status_str(pk.PKM_OK) == "ok"
+    assert "argument" in pk.status_str(pk.PKM_E_ARG)
+    assert "unsupported" in pk.status_str(pk.PKM_E_UNSUPPORTED)
+    assert pk.status_str(99) == "unknown status"
+
+
+GOOD = dict(dim=1024, heads=4, n_keys=1024, k=32, value_type="bf16", bn_eps=1e-5, max_batch=16384)
+
+
+@pytest.mark.parametrize("change,status", [
+    ({}, pk.PKM_OK),
+    (dict(dim=63), pk.PKM_E_ARG),                  # odd: the query cannot be halved
+    (dict(dim=0), pk.PKM_E_ARG),
+    (dict(dim=96), pk.PKM_E_UNSUPPORTED),          # even but not a multiple of 64
+    (dict(heads=0), pk.PKM_E_ARG),
+    (dict(n_keys=1), pk.PKM_E_ARG),
+    (dict(n_keys=46341), pk.PKM_E_ARG),            # n^2 >= 2^31
+    (dict(n_keys=4097), pk.PKM_E_UNSUPPORTED),
+    (dict(k=0), pk.PKM_E_ARG),
+    (dict(n_keys=16, k=17), pk.PKM_E_ARG),         # topk needs k <= n_keys
+    (dict(k=65), pk.PKM_E_UNSUPPORTED),
+    (dict(value_type=3), pk.PKM_E_ARG),
+    (dict(bn_eps=0.0), pk.PKM_E_ARG),
+    (dict(bn_eps=-1.0), pk.PKM_E_ARG),
+    (dict(bn_eps=float("nan")), pk.PKM_E_ARG),
+    (dict(max_batch=0), pk.PKM_E_ARG),
+    (dict(max_batch=(1 << 30) + 1), pk.PKM_E_ARG),
+    (dict(n_keys=4096, k=64, dim=64, heads=1, value_type="e4m3"), pk.PKM_OK),
+    (dict(n_keys=16, k=16, dim=64, heads=1, value_type="f32"), pk.PKM_OK),
+])
+def test_config_check(change, status):
+    cfg = pk.make_config(**{**GOOD, **change})
+    assert pk.config_check(cfg) == status, pk.last_error()
+    if status != pk.PKM_OK:
+        assert pk.last_error() != ""
+
+
+def test_workspace_bytes():
+    cfg = pk.make_config(**GOOD)
+    mb, H, D, n, k = 16384, 4, 1024, 1024, 32
+    assert pk.workspace_bytes(cfg) == 4 * mb * H * (D + 2 * n + 2 * k)
+    with pytest.raises(pk.PkmError):
+        pk.workspace_bytes(pk.make_config(**{**GOOD, "k": 0}))
+
+
+def test_null_arguments_rejected_before_any_launch():
+    lib = pk.load_library()
+    null = ctypes.c_void_p()
+    params = pk._binding.ParamsStruct()
+    assert lib.pkm_forward(null, ctypes.byref(params), 1, null, null, null, null, null) == pk.PKM_E_ARG
+    assert lib.pkm_query(null, ctypes.byref(params), 1, null, null, null) == pk.PKM_E_ARG
+    assert lib.pkm_score(null, ctypes.byref(params), 1, null, null, null) == pk.PKM_E_ARG
+    assert lib.pkm_select(null, 1, null, null, null, null) == pk.PKM_E_ARG
+    assert lib.pkm_gather(null, ctypes.byref(params), 1, 1, null, null, null, null) == pk.PKM_E_ARG
+    assert lib.pkm_create(None, ctypes.byref(ctypes.c_void_p())) == pk.PKM_E_ARG
+    assert lib.pkm_create(ctypes.byref(pk.make_config(**GOOD)), None) == pk.PKM_E_ARG
+    assert "NULL" in pk.last_error()
+    lib.pkm_destroy(null)  # NULL-safe
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+
+    with pytest.raises(ValueError, match="GPU"):
+        pk._binding._expect(torch.zeros(4, 4), "x", (4, 4), "float32")
+    with pytest.raises(ValueError, match="shape"):
+        pk._binding._expect(torch.zeros(4, 4), "x", (4, 5), "float32")
+    with pytest.raises(ValueError, match="expected one of"):
+        pk._binding._expect(torch.zeros(4, 4, dtype=torch.float64), "x", (4, 4), "float32")

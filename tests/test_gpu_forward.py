@@ -1,0 +1,190 @@
+"""GPU: the whole lookup through the C ABI against the fp64 oracle.
+
+Index parity rule: identical winner sets for every compared (token, head),
+and identical order wherever adjacent fp64 winners are at least tau apart
+(tests/support.py).  Output tolerance, per token, max-norm relative:
+1e-4 for fp32 tables, 2e-2 for bf16 / E4M3 tables (both sides decode the
+same stored bits, so the table format adds no error of its own; the bound
+covers fp32 scoring, softmax and accumulation).  Weights: |w - w_ref| within
+the same tolerance, matched by index.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import product_key_memory_amd as pk
+import synthetic
+from tests import support
+from tests.support import say
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2, "e4m3": 2e-2}
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+
+    support.device()
+    pk.load_library()
+    return t
+
+
+def compare(wl, params, x, out, idx, w, tokens=None):
+    """Oracle on the listed tokens (all by default) vs the GPU results."""
+    tokens = np.arange(x.shape[0]) if tokens is None else np.asarray(tokens)
+    model = support.model_for(wl, params)
+    r = oracle.run(model, x[tokens], want=("out", "idx", "top", "w"))
+    _, tau = support.gaps_and_tau(wl, params, x[tokens], model)
+    support.check_indices(idx[tokens], r["idx"], r["top"], tau)
+    tol = TOL[wl.table]
+    wm = support.weights_by_index(idx[tokens], w[tokens], r["idx"])
+    assert np.abs(wm - r["w"]).max() <= tol
+    err = support.rel_rowmax_err(out[tokens], r["out"])
+    assert err.max() <= tol, (err.max(), int(err.argmax()))
+    return err
+
+
+def invariants(wl, idx, w):
+    """Properties every (token, head) must satisfy whatever the inputs."""
+    assert ((idx >= 0) & (idx < wl.N)).all()
+    s = np.sort(idx, -1)
+    assert (s[..., 1:] != s[..., :-1]).all()
+    np.testing.assert_allclose(w.sum(-1), 1.0, atol=1e-5)
+    assert (np.diff(w, axis=-1) <= 1e-7).all()
+
+
+@pytest.mark.parametrize("name", ["tiny", "mid"])
+def test_forward_small_workloads_every_token(torch, name):
+    wl = synthetic.WORKLOADS[name]
+    params = synthetic.make_params(wl)
+    x = synthetic.make_x(wl)
+    support.gap_clean(wl, params, x)
+    out, idx, w = support.gpu_forward(wl, params, x)
+    invariants(wl, idx, w)
+    compare(wl, params, x, out, idx, w)
+
+
+def test_tiny_product_search_equals_flat_search(torch):
+    """The exactness argument on the GPU: Tiny's winners equal the top-k of
+    all 256 concatenated keys (brute force, fp64)."""
+    from tests import pins
+
+    wl = synthetic.WORKLOADS["tiny"]
+    params = synthetic.make_params(wl)
+    x = synthetic.make_x(wl)
+    support.gap_clean(wl, params, x)
+    out, idx, w = support.gpu_forward(wl, params, x)
+    f = pins.flat_search(params, x, wl.k)
+    assert (np.sort(idx, -1) == np.sort(f["idx"], -1)).all()
+
+
+@pytest.mark.parametrize("shape", [
+    dict(B=1000, D=64, H=2, n=100, k=7, table="f32"),      # ragged tiles, n not a multiple of 64
+    dict(B=129, D=128, H=3, n=64, k=64, table="bf16"),     # k = n_keys: every key is a candidate
+    dict(B=77, D=192, H=1, n=300, k=1, table="e4m3"),      # k = 1: argmax of each half
+    dict(B=64, D=64, H=2, n=2048, k=64, table="bf16"),     # large n with the largest k
+    dict(B=1, D=64, H=1, n=2, k=2, table="f32"),           # smallest memory
+    dict(B=300, D=320, H=5, n=33, k=33, table="e4m3"),     # k = n, odd sizes, random BN
+])
+def test_forward_edge_shapes(torch, shape):
+    wl = synthetic.Workload("edge", shape["B"], shape["D"], shape["H"], shape["n"], shape["k"], shape["table"],
+                            "random")
+    params = synthetic.make_params(wl, seed=3)
+    x = synthetic.make_x(wl, seed=3)
+    support.gap_clean(wl, params, x, seed=3)
+    out, idx, w = support.gpu_forward(wl, params, x)
+    invariants(wl, idx, w)
+    compare(wl, params, x, out, idx, w)
+
+
+def test_forward_random_gamma_beta(torch):
+    wl = synthetic.Workload("gb", 200, 256, 2, 128, 16, "f32", "random")
+    params = synthetic.make_params(wl, seed=9)
+    rng = np.random.default_rng(9)
+    params["gamma"] = rng.uniform(0.5, 1.5, params["gamma"].shape).astype(np.float32)
+    params["beta"] = rng.normal(0, 0.3, params["beta"].shape).astype(np.float32)
+    x = synthetic.make_x(wl, seed=9)
+    support.gap_clean(wl, params, x, seed=9)
+    out, idx, w = support.gpu_forward(wl, params, x)
+    compare(wl, params, x, out, idx, w)
+
+
+def test_chunking_stages_and_determinism(torch):
+    """Chunked (max_batch < B) and unchunked runs, a second identical run and
+    the four stage calls composed by hand all give bitwise identical
+    results."""
+    wl = synthetic.Workload("chunk", 1000, 256, 2, 128, 16, "bf16", "random")
+    params = synthetic.make_params(wl, seed=5)
+    x = synthetic.make_x(wl, seed=5)
+    P = pk.params_to_device(params, wl.table, support.device())
+    a = support.gpu_forward(wl, params, x, max_batch=16384, dev_params=P)
+    b = support.gpu_forward(wl, params, x, max_batch=16384, dev_params=P)
+    c = support.gpu_forward(wl, params, x, max_batch=96, dev_params=P)
+    for u, v in zip(a, b):
+        assert (u == v).all()
+    for u, v in zip(a, c):
+        assert (u == v).all()
+    say("stages by hand")
+    mem = pk.Memory(wl.D, wl.H, wl.n, wl.k, wl.table)
+    xt = torch.from_numpy(x).to(support.device())
+    q = mem.query(P, xt)
+    s = mem.score(P, q)
+    idx, w = mem.select(s)
+    out = mem.gather(P, idx, w)
+    torch.cuda.synchronize()
+    assert (idx.cpu().numpy() == a[1]).all()
+    assert (w.cpu().numpy() == a[2]).all()
+    assert (out.cpu().numpy() == a[0]).all()
+
+
+def test_empty_batch_and_argument_errors(torch):
+    wl = synthetic.Workload("err", 4, 64, 1, 16, 4, "e4m3", "unit")
+    params = synthetic.make_params(wl)
+    P = pk.params_to_device(params, wl.table, support.device())
+    mem = pk.Memory(wl.D, wl.H, wl.n, wl.k, wl.table)
+    say("empty batch")
+    x0 = torch.zeros((0, wl.D), device=support.device())
+    out, idx, w = mem.forward(P, x0)
+    torch.cuda.synchronize()
+    assert out.shape == (0, wl.D)
+    # misaligned x: rejected on the host by the C ABI, nothing launched
+    import ctypes
+
+    xt = torch.zeros((5, wl.D), device=support.device())
+    outt = torch.zeros((4, wl.D), device=support.device())
+    st = torch.cuda.current_stream().cuda_stream
+    rc = mem.lib.pkm_forward(mem._ctx, ctypes.byref(P.struct), 4, ctypes.c_void_p(xt.data_ptr() + 4),
+                             ctypes.c_void_p(outt.data_ptr()), None, None, ctypes.c_void_p(st))
+    assert rc == pk.PKM_E_ARG and "aligned" in pk.last_error()
+    # an E4M3 table without row scales
+    bad = pk.Params(*[P[name] for name in ("wq", "bn_mean", "bn_var", "bn_gamma", "bn_beta", "subkeys", "values")],
+                    None)
+    rc = mem.lib.pkm_forward(mem._ctx, ctypes.byref(bad.struct), 4, ctypes.c_void_p(xt.data_ptr()),
+                             ctypes.c_void_p(outt.data_ptr()), None, None, ctypes.c_void_p(st))
+    assert rc == pk.PKM_E_ARG and "value_scale" in pk.last_error()
+    with pytest.raises(ValueError):
+        mem.forward(P, torch.zeros((4, wl.D + 64), device=support.device()))
+
+
+# Full-size workloads: the GPU runs every token; the oracle checks a sample
+# (the first and last tokens, chunk edges and a spread in between), each
+# re-drawn until gap-clean; every token is checked against the invariants.
+def _sample(B):
+    s = set([0, 1, B - 1, B // 2, 16383, 16384]) | set(np.linspace(0, B - 1, 26).astype(int).tolist())
+    return np.array(sorted(t for t in s if 0 <= t < B))
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["default", "large_batch", "large_memory"])
+def test_forward_full_size_sampled(torch, name):
+    wl = synthetic.WORKLOADS[name]
+    params = synthetic.make_params(wl)
+    x = synthetic.make_x(wl)
+    tokens = _sample(wl.B)
+    support.gap_clean(wl, params, x, tokens=tokens)
+    out, idx, w = support.gpu_forward(wl, params, x)
+    invariants(wl, idx, w)
+    err = compare(wl, params, x, out, idx, w, tokens=tokens)
+    print(f"{name}: max row error {err.max():.3g} over {len(tokens)} sampled tokens", flush=True)
