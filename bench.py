@@ -1,0 +1,200 @@
+"""Throughput of the product-key memory lookup on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload default]
+
+One step = the whole lookup (projection + BN, subkey scoring, per-half top-k,
+candidate top-k, softmax, value gather) over one batch of synthetic tokens,
+inputs resident in HBM.  Prints one JSON line: tokens/s for the workload,
+per-kernel times from HIP events recorded on the stream the library launches
+on, the roofline of the dominant kernel and of the value gather, and the fp64
+CPU oracle timed on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+import synthetic
+
+METRIC = "PKM lookups(tokens)/sec + value-gather HBM GB/s, N=1M, k=32, 4 heads"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+FP32_MFMA_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix
+ELT_BYTES = {"f32": 4, "bf16": 2, "e4m3": 1}
+
+
+def per_token_work(wl):
+    """Algorithmic work per token (lookups are per token, all heads)."""
+    return {
+        "query_flop": 2.0 * wl.H * wl.D * wl.D,              # a1: Wq[h] . x for every head
+        "score_flop": 2.0 * wl.H * wl.n * wl.D,              # a3: 2 halves x n subkeys x D/2
+        "select_bytes": wl.H * (2 * wl.n * 4 + wl.k * 8),    # a4-a6: read half scores, write idx + w
+        # a7: the gathered rows (+ one fp32 scale per row for E4M3 tables)
+        "gather_bytes": wl.H * wl.k * (wl.D * ELT_BYTES[wl.table] + (4 if wl.table == "e4m3" else 0)),
+    }
+
+
+def timed_steps(torch, fn, steps, warmup):
+    """Average ms per call of fn over `steps` calls after `warmup` calls,
+    bracketed by device synchronisation, timed with events on the current
+    stream (the stream the library launches on)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        fn()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps
+
+
+def kernel_times(torch, mem, P, xt, steps, warmup):
+    """Average ms of each stage's kernel: events between consecutive stage
+    calls on one stream, every iteration enqueued before one final sync."""
+    B = xt.shape[0]
+    q = torch.empty((B, mem.heads, mem.dim), dtype=torch.float32, device=xt.device)
+    s = torch.empty((B, mem.heads, 2, mem.n_keys), dtype=torch.float32, device=xt.device)
+    idx = torch.empty((B, mem.heads, mem.k), dtype=torch.int32, device=xt.device)
+    w = torch.empty((B, mem.heads, mem.k), dtype=torch.float32, device=xt.device)
+    out = torch.empty((B, mem.dim), dtype=torch.float32, device=xt.device)
+    stages = [lambda: mem.query(P, xt, q), lambda: mem.score(P, q, s), lambda: mem.select(s, idx, w),
+              lambda: mem.gather(P, idx, w, out)]
+    for _ in range(warmup):
+        for f in stages:
+            f()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(steps)]
+    for it in range(steps):
+        ev[it][0].record()
+        for j, f in enumerate(stages):
+            f()
+            ev[it][j + 1].record()
+    torch.cuda.synchronize()
+    names = ["query_gemm", "score_gemm", "select", "gather"]
+    return {nm: float(np.mean([ev[it][j].elapsed_time(ev[it][j + 1]) for it in range(steps)]))
+            for j, nm in enumerate(names)}
+
+
+def gather_uniform_ms(torch, mem, P, wl, steps, warmup):
+    """The gather alone on uniformly random rows (no pipeline locality)."""
+    rows, wts = synthetic.uniform_rows(wl, 1, wl.B, wl.H * wl.k)
+    idx = torch.from_numpy(rows).cuda()
+    w = torch.from_numpy(wts).cuda()
+    out = torch.empty((wl.B, wl.D), dtype=torch.float32, device="cuda")
+    return timed_steps(torch, lambda: mem.gather(P, idx, w, out), steps, warmup)
+
+
+def cpu_baseline(wl, params, x, seconds=10.0):
+    """The fp64 oracle on host cores over a bounded sample of the tokens."""
+    import oracle
+
+    cores = min(16, len(os.sched_getaffinity(0)))
+    model = oracle.Model.from_params(params, wl.k, wl.table)
+    probe = min(x.shape[0], 2 * cores)
+    t0 = time.perf_counter()
+    oracle.run(model, x[:probe], want=("out",), nthreads=cores)
+    rate = probe / max(time.perf_counter() - t0, 1e-9)
+    sample = int(min(x.shape[0], max(cores, rate * seconds)))
+    t0 = time.perf_counter()
+    oracle.run(model, x[:sample], want=("out",), nthreads=cores)
+    dt = time.perf_counter() - t0
+    return {"value": sample / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {sample} of the {wl.B} tokens of the {wl.name} workload, full lookup in fp64, "
+                      f"{dt:.1f} s wall on {cores} threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="default", choices=sorted(synthetic.WORKLOADS))
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target wall time of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (reference for HBM byte counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the lookup is data-parallel "
+              "over tokens with a replicated table, so N GPUs would run N independent copies).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import product_key_memory_amd as pk
+
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib << 18
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_each_way": n * 4}))
+        return
+
+    wl = synthetic.WORKLOADS[args.workload]
+    params = synthetic.make_params(wl)
+    x = synthetic.make_x(wl)
+    P = pk.params_to_device(params, wl.table, "cuda")
+    xt = torch.from_numpy(x).cuda()
+    mem = pk.Memory(wl.D, wl.H, wl.n, wl.k, wl.table, max_batch=wl.B)
+    out = torch.empty((wl.B, wl.D), dtype=torch.float32, device="cuda")
+    idx = torch.empty((wl.B, wl.H, wl.k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((wl.B, wl.H, wl.k), dtype=torch.float32, device="cuda")
+
+    ms = timed_steps(torch, lambda: mem.forward(P, xt, out, idx, wts), args.steps, args.warmup)
+    kt = kernel_times(torch, mem, P, xt, args.steps, args.warmup)
+    g_uniform_ms = gather_uniform_ms(torch, mem, P, wl, args.steps, args.warmup)
+
+    work = per_token_work(wl)
+    B = wl.B
+    rl = {
+        "query_gemm": ("mfma", work["query_flop"] * B / (kt["query_gemm"] * 1e-3) / 1e12, FP32_MFMA_PEAK_TFLOPS,
+                       "TFLOP/s"),
+        "score_gemm": ("mfma", work["score_flop"] * B / (kt["score_gemm"] * 1e-3) / 1e12, FP32_MFMA_PEAK_TFLOPS,
+                       "TFLOP/s"),
+        "select": ("hbm", work["select_bytes"] * B / (kt["select"] * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"),
+        "gather": ("hbm", work["gather_bytes"] * B / (kt["gather"] * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"),
+    }
+    dominant = max(kt, key=kt.get)
+
+    def roof(name):
+        bound, achieved, peak, unit = rl[name]
+        return {"kernel": name, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4), "traffic": None, "avg_ms": round(kt[name], 4)}
+
+    line = {
+        "metric": METRIC,
+        "value": round(B / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "tokens_per_step": B, "dim": wl.D, "heads": wl.H, "n_keys": wl.n,
+                   "rows": wl.N, "k": wl.k, "value_table": wl.table, "seed": 0},
+        "roofline": roof(dominant),
+        "gather_roofline": roof("gather"),
+        "gather_uniform_rows_gbs": round(work["gather_bytes"] * B / (g_uniform_ms * 1e-3) / 1e9, 1),
+        "kernels_ms": {nm: round(v, 4) for nm, v in kt.items()},
+        "kernel_rooflines": {nm: {"achieved": round(rl[nm][1], 2), "unit": rl[nm][3],
+                                  "frac": round(rl[nm][1] / rl[nm][2], 4)} for nm in rl},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, params, x, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
