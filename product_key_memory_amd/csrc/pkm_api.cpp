@@ -20,6 +20,7 @@ struct pkm_ctx {
     float *scores;   // [max_batch, H, 2, n]
     int32_t *idx;    // [max_batch, H, k]
     float *weights;  // [max_batch, H, k]
+    uint32_t *stair; // staircase cells of the candidate grid for this k
 };
 
 namespace {
@@ -60,7 +61,8 @@ constexpr size_t kAlign = 256;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // Workspace pieces for one chunk of mb tokens; false on size overflow.
-bool workspace_layout(const pkm_config &c, size_t sizes[4])
+constexpr int kPieces = 5;
+bool workspace_layout(const pkm_config &c, size_t sizes[kPieces])
 {
     const double mb = (double)c.max_batch;
     const double total = mb * c.heads * ((double)c.dim + 2.0 * c.n_keys + 2.0 * c.k) * 4.0;
@@ -70,6 +72,7 @@ bool workspace_layout(const pkm_config &c, size_t sizes[4])
     sizes[1] = round_up(m * H * 2 * (size_t)c.n_keys * sizeof(float));
     sizes[2] = round_up(m * H * (size_t)c.k * sizeof(int32_t));
     sizes[3] = round_up(m * H * (size_t)c.k * sizeof(float));
+    sizes[4] = round_up(pkm::kMaxStaircaseCells * sizeof(uint32_t));
     return true;
 }
 
@@ -88,7 +91,7 @@ pkm_status check_config(const pkm_config *c)
     if (c->max_batch < 1 || c->max_batch > kMaxBatch || c->max_batch * c->heads > ((int64_t)1 << 31))
         return fail(PKM_E_ARG, "max_batch must be in [1, 2^30] with max_batch * heads <= 2^31");
     if ((int64_t)c->heads * c->dim >= ((int64_t)1 << 30)) return fail(PKM_E_ARG, "heads * dim too large");
-    size_t sizes[4];
+    size_t sizes[kPieces];
     if (!workspace_layout(*c, sizes)) return fail(PKM_E_ARG, "workspace size overflows");
     if (c->dim % 64 != 0) return fail(PKM_E_UNSUPPORTED, "dim must be a multiple of 64 (got %d)", c->dim);
     if (c->k > 64) return fail(PKM_E_UNSUPPORTED, "k > 64 is not supported (got %d)", c->k);
@@ -222,9 +225,10 @@ pkm_status pkm_workspace_bytes(const pkm_config *cfg, size_t *bytes)
 {
     if (pkm_status s = check_config(cfg)) return s;
     if (!bytes) return fail(PKM_E_ARG, "bytes is NULL");
-    size_t sizes[4];
+    size_t sizes[kPieces];
     workspace_layout(*cfg, sizes);
-    *bytes = sizes[0] + sizes[1] + sizes[2] + sizes[3];
+    *bytes = 0;
+    for (size_t piece : sizes) *bytes += piece;
     return ok();
 }
 
@@ -241,9 +245,10 @@ pkm_status pkm_create(const pkm_config *cfg, pkm_ctx **out)
     if (e != hipSuccess) return fail(PKM_E_DEVICE, "hipGetDeviceProperties: %s", hipGetErrorString(e));
     if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
         return fail(PKM_E_UNSUPPORTED, "device %d is %s; the kernels are built for gfx950", dev, prop.gcnArchName);
-    size_t sizes[4];
+    size_t sizes[kPieces];
     workspace_layout(*cfg, sizes);
-    const size_t total = sizes[0] + sizes[1] + sizes[2] + sizes[3];
+    size_t total = 0;
+    for (size_t piece : sizes) total += piece;
     void *ws = nullptr;
     e = hipMalloc(&ws, total);
     if (e != hipSuccess) {
@@ -263,6 +268,15 @@ pkm_status pkm_create(const pkm_config *cfg, pkm_ctx **out)
     ctx->scores = reinterpret_cast<float *>(w + sizes[0]);
     ctx->idx = reinterpret_cast<int32_t *>(w + sizes[0] + sizes[1]);
     ctx->weights = reinterpret_cast<float *>(w + sizes[0] + sizes[1] + sizes[2]);
+    ctx->stair = reinterpret_cast<uint32_t *>(w + sizes[0] + sizes[1] + sizes[2] + sizes[3]);
+    uint32_t stair[pkm::kMaxStaircaseCells] = {};
+    pkm::staircase_table(cfg->k, stair);
+    e = hipMemcpy(ctx->stair, stair, sizeof stair, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+        (void)hipFree(ws);
+        delete ctx;
+        return fail(PKM_E_DEVICE, "uploading the candidate staircase: %s", hipGetErrorString(e));
+    }
     if (log_on())
         fprintf(stderr, "pkm: context on device %d (%s): D=%d H=%d n=%d k=%d values=%d max_batch=%lld workspace=%zu\n",
                 dev, prop.gcnArchName, cfg->dim, cfg->heads, cfg->n_keys, cfg->k, cfg->value_type,
@@ -297,7 +311,7 @@ pkm_status pkm_forward(pkm_ctx *ctx, const pkm_params *p, int64_t B, const float
         float *cw = weights ? weights + b0 * H * k : ctx->weights;
         if ((s = run_query(c, p, nb, x + b0 * D, ctx->qhat, st))) return s;
         if ((s = run_score(c, p, nb, ctx->qhat, ctx->scores, st))) return s;
-        if ((s = launched(pkm::launch_select(ctx->scores, nb, c.heads, c.n_keys, c.k, ci, cw, st), "select")))
+        if ((s = launched(pkm::launch_select(ctx->scores, nb, c.heads, c.n_keys, c.k, ctx->stair, ci, cw, st), "select")))
             return s;
         if ((s = launched(pkm::launch_gather(p->values, p->value_scale, c.value_type, c.dim, c.n_keys * c.n_keys, nb, (int)(H * k), ci, cw,
                                              out + b0 * D, st),
@@ -336,7 +350,7 @@ pkm_status pkm_select(pkm_ctx *ctx, int64_t B, const float *scores, int32_t *idx
     if (B == 0) return ok();
     if ((s = need(scores, "scores")) || (s = need(idx, "idx")) || (s = need(weights, "weights"))) return s;
     const pkm_config &c = ctx->cfg;
-    if ((s = launched(pkm::launch_select(scores, B, c.heads, c.n_keys, c.k, idx, weights,
+    if ((s = launched(pkm::launch_select(scores, B, c.heads, c.n_keys, c.k, ctx->stair, idx, weights,
                                          static_cast<hipStream_t>(stream)),
                       "select")))
         return s;

@@ -1,44 +1,55 @@
 // Steps a4-a6 of the lookup in one kernel, one wave64 per (token, head):
 //   a4  exact top-k of each half's n subkey scores,
-//   a5  the k*k candidate grid s0[i] + s1[j] (flat row i0[i]*n + i1[j]) and
-//       its exact top-k,
+//   a5  the exact top-k of the k*k candidates s0[i] + s1[j] (flat row
+//       i0[i]*n + i1[j]),
 //   a6  softmax over the k winners.
 // ("Product-Key Memory", §Factorising the key space and the code listing's
 // forward; "Memory Retrieval Mechanisms: From Soft to Efficient", top-k
 // section.)
 //
-// Ordering.  Each element becomes a 64-bit key: the high word maps the fp32
-// score to an unsigned integer with the same order (-0 folded onto +0), the
-// low word is ~index, so comparing keys compares (score desc, index asc),
-// the tie rule of the whole lookup, and no two keys are equal.
+// Ordering.  An element's order key maps its fp32 score to an unsigned
+// integer with the same order (-0 folded onto +0); packed with ~index below
+// it, comparing 64-bit keys compares (score desc, index asc), the tie rule of
+// the whole lookup, and no two packed keys are equal.
 //
-// Selection (no sort of all n elements).  Lane l holds elements l, l+64, ...
-// 1. T = k-th largest of the 64 lane maxima (bitonic sort of 64 words): at
-//    least k elements are >= T, so every winner is >= T.
-// 2. The elements >= T are counted with ballots.  For random scores about
-//    1.35 k of them survive; if they fit in 64 they are compacted into LDS
-//    (ballot + mbcnt) and one bitonic sort of 64 keys orders them.
-// 3. Otherwise (heavy ties, unusual inputs) the exact k-th key is found by
-//    MSB-first bisection with ballot counts, then the last index kept among
-//    elements tied at it, so exactly k elements are compacted and sorted.
-// Lane j then holds the j-th best key, j < k.
+// Per-half top-k (no sort of all n elements).  Lane l holds elements l,
+// l + 64, ... of the half in registers.  T = the k-th largest of the 64 lane maxima (one
+// bitonic sort of 64 words): at least k elements are >= T, so every winner
+// is.  The elements >= T (about 1.35 k for random scores) are compacted into
+// LDS with ballot + mbcnt and one 64-lane bitonic sort of packed keys orders
+// them.  If more than 64 survive (heavy ties), the exact k-th key is found
+// by MSB-first bisection with ballot counts, then the last index kept among
+// the ties, and exactly k are compacted.  The halves are selected one after
+// the other; every row load is issued before the first is consumed.
+//
+// Candidates.  With both halves sorted, s0[i] + s1[j] can only be beaten by
+// the cells above and left of it, so a cell with (i+1)(j+1) > k has at
+// least k cells of the "staircase" {(i+1)(j+1) <= k} at or above it: the
+// k-th best score v_k of the full grid is the k-th best of the staircase
+// (119 of 1024 cells at k = 32), and every cell scoring above v_k lies in
+// it.  The staircase's top-k is therefore the answer unless a cell outside
+// it ties v_k; the best outside cell of column j is (floor(k/(j+1)), j), so
+// one comparison per column certifies the result.  Otherwise (ties) the full
+// k*k grid is ranked.  All scores stay fp32; the candidate sums are the same
+// fp32 additions whichever path runs.
 #include "pkm_internal.h"
+#include "wave_ops.h"
 
 namespace pkm {
 namespace {
 
-constexpr int WAVES = 4;  // (token, head) pairs per 256-thread workgroup
+constexpr int WAVES = 4;        // (token, head) pairs per 256-thread workgroup
+constexpr int STAIR_SLOTS = 5;  // staircase cells per lane: 280 cells at k = 64
 
 __device__ __forceinline__ uint32_t order_key(float f)
 {
-    f = f + 0.0f;  // -0 -> +0: equal scores must give equal keys
-    const uint32_t u = __float_as_uint(f);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    const uint32_t u = __float_as_uint(f + 0.0f);  // -0 -> +0: equal scores give equal keys
+    return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
 __device__ __forceinline__ float key_score(uint32_t k)
 {
-    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+    return __uint_as_float(k ^ ((uint32_t)((int32_t)~k >> 31) | 0x80000000u));
 }
 
 __device__ __forceinline__ uint64_t pack(uint32_t key, uint32_t id)
@@ -48,32 +59,14 @@ __device__ __forceinline__ uint64_t pack(uint32_t key, uint32_t id)
 
 __device__ __forceinline__ uint32_t unpack_id(uint64_t c) { return 0xFFFFFFFFu - (uint32_t)c; }
 
-__device__ __forceinline__ uint32_t shfl_xor32(uint32_t v, int m) { return (uint32_t)__shfl_xor((int)v, m, 64); }
-
-__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m)
+__device__ __forceinline__ uint32_t read_lane(uint32_t v, int src)
 {
-    const uint32_t lo = shfl_xor32((uint32_t)v, m), hi = shfl_xor32((uint32_t)(v >> 32), m);
-    return ((uint64_t)hi << 32) | lo;
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, src);
 }
 
-__device__ __forceinline__ uint32_t xchg(uint32_t v, int m) { return shfl_xor32(v, m); }
-__device__ __forceinline__ uint64_t xchg(uint64_t v, int m) { return shfl_xor64(v, m); }
-
-// Bitonic sort of one value per lane over the wave, descending by lane.
-template <typename T>
-__device__ __forceinline__ T sort64_desc(T v, int lane)
+__device__ __forceinline__ int below_me(uint64_t mask)
 {
-#pragma unroll
-    for (int size = 2; size <= 64; size <<= 1) {
-#pragma unroll
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            const T o = xchg(v, stride);
-            const bool desc = (lane & size) == 0;  // direction of this block
-            const bool lower = (lane & stride) == 0;
-            v = (lower == desc) ? (v > o ? v : o) : (v < o ? v : o);
-        }
-    }
-    return v;
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
 }
 
 // Orders this wave's LDS writes before its later LDS reads by other lanes (a
@@ -85,79 +78,209 @@ __device__ __forceinline__ void wave_sync_lds()
     __builtin_amdgcn_wave_barrier();
 }
 
-// Exact top-k (k <= 64) of the wave's elements: element t of lane l has order
-// key key[t] (0 = absent) and index id[t].  Returns, in lane j < k, the j-th
-// best packed key.  buf: 64 slots of this wave's LDS.
-template <int MAXM>
-__device__ uint64_t wave_topk(const uint32_t (&key)[MAXM], const uint32_t (&id)[MAXM], int k, uint64_t *buf,
+// Per-wave LDS: 64 compaction slots plus one discard slot per lane, so the
+// compaction stores unconditionally and never branches.
+struct Stage {
+    uint64_t slot[128];
+};
+
+// Appends the packed key of element t to the compaction when `keep`.
+__device__ __forceinline__ void append(bool keep, uint32_t key, uint32_t id, int &base, Stage &st, int lane)
+{
+    const uint64_t mask = __ballot(keep);
+    const int pos = base + below_me(mask);
+    st.slot[keep && pos < 64 ? pos : 64 + lane] = pack(key, id);
+    base += __popcll(mask);
+}
+
+__device__ __forceinline__ bool kept(uint32_t key, uint32_t id, uint32_t kth, uint32_t last)
+{
+    return key > kth || (key == kth && id <= last);
+}
+
+// Exact k-th largest key and, among elements tied at it, the largest index
+// to keep so that exactly k elements are kept.  count(key >= x) does not
+// increase with x, so the MSB-first greedy finds the largest x with at least
+// k elements >= x: the k-th largest key.  Rolled loops over the m slots with
+// keys recomputed by key_of: this path is rare and must not hold registers.
+template <typename KeyOf, typename IdOf>
+__device__ void exact_cut(KeyOf key_of, IdOf id_of, int m, int k, uint32_t &kth, uint32_t &last)
+{
+    kth = 0;
+#pragma unroll 1
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = kth | (1u << bit);
+        int c = 0;
+#pragma unroll 1
+        for (int t = 0; t < m; ++t) c += __popcll(__ballot(key_of(t) >= cand));
+        if (c >= k) kth = cand;
+    }
+    int gt = 0;
+#pragma unroll 1
+    for (int t = 0; t < m; ++t) gt += __popcll(__ballot(key_of(t) > kth));
+    const int need = k - gt;  // lowest indices to take among the ties
+    last = 0;
+#pragma unroll 1
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = last | (1u << bit);
+        int c = 0;
+#pragma unroll 1
+        for (int t = 0; t < m; ++t) c += __popcll(__ballot(key_of(t) == kth && id_of(t) < cand));
+        if (c < need) last = cand;
+    }
+}
+
+// Rolled compaction with recomputed keys (rare paths).
+template <typename KeyOf, typename IdOf>
+__device__ int compact_rolled(KeyOf key_of, IdOf id_of, int m, uint32_t kth, uint32_t last, Stage &st, int lane)
+{
+    int base = 0;
+#pragma unroll 1
+    for (int t = 0; t < m; ++t) {
+        const uint32_t key = key_of(t), id = id_of(t);
+        append(kept(key, id, kth, last), key, id, base, st, lane);
+    }
+    return base;
+}
+
+// Reads back the count (<= 64) compacted keys, one per lane, and sorts them.
+__device__ __forceinline__ uint64_t sorted_survivors(int count, Stage &st, int lane)
+{
+    wave_sync_lds();
+    const uint64_t v = lane < count ? st.slot[lane] : 0ull;
+    wave_sync_lds();
+    return sort64_desc(v);
+}
+
+// Exact top-k (k <= 64) of m slots per lane, keys held in registers key[M]
+// (0 = absent), recomputed by slow_key on the rare tie path; lane j < k
+// receives the j-th best packed key.
+template <int M, typename SlowKey, typename IdOf>
+__device__ uint64_t wave_topk(const uint32_t (&key)[M], SlowKey slow_key, IdOf id_of, int m, int k, Stage &st,
                               int lane)
 {
     uint32_t lane_max = 0;
 #pragma unroll
-    for (int t = 0; t < MAXM; ++t) lane_max = key[t] > lane_max ? key[t] : lane_max;
-    // Kept: key > kth, or key == kth and id <= last.
-    uint32_t kth = (uint32_t)__shfl((int)sort64_desc(lane_max, lane), k - 1, 64);
+    for (int t = 0; t < M; ++t) lane_max = key[t] > lane_max ? key[t] : lane_max;
+    uint32_t kth = read_lane(sort64_desc(lane_max), k - 1);
     uint32_t last = 0xFFFFFFFFu;
-
     int count = 0;
 #pragma unroll
-    for (int t = 0; t < MAXM; ++t) count += __popcll(__ballot(key[t] >= kth));
-
+    for (int t = 0; t < M; ++t) append(kept(key[t], id_of(t), kth, last), key[t], id_of(t), count, st, lane);
     if (count > 64) {
-        // Too many survivors for one sort (ties or unusual inputs): find the
-        // exact k-th key by MSB-first bisection over the score key, then the
-        // last index to keep among the elements tied at it.  count(key >= x)
-        // is non-increasing in x, so the largest x with count >= k is the
-        // k-th best score key.
-        kth = 0;
-#pragma unroll 1
-        for (int bit = 31; bit >= 0; --bit) {
-            const uint32_t cand = kth | (1u << bit);
-            int c = 0;
-#pragma unroll
-            for (int t = 0; t < MAXM; ++t) c += __popcll(__ballot(key[t] >= cand));
-            if (c >= k) kth = cand;
-        }
-        int gt = 0;
-#pragma unroll
-        for (int t = 0; t < MAXM; ++t) gt += __popcll(__ballot(key[t] > kth));
-        const int need = k - gt;  // lowest indices to take among the ties
-        last = 0;
-#pragma unroll 1
-        for (int bit = 31; bit >= 0; --bit) {
-            const uint32_t cand = last | (1u << bit);
-            int c = 0;
-#pragma unroll
-            for (int t = 0; t < MAXM; ++t) c += __popcll(__ballot(key[t] == kth && id[t] < cand));
-            if (c < need) last = cand;
-        }
-        count = k;
+        exact_cut(slow_key, id_of, m, k, kth, last);
+        count = compact_rolled(slow_key, id_of, m, kth, last, st, lane);
     }
-
-    int base = 0;
-#pragma unroll
-    for (int t = 0; t < MAXM; ++t) {
-        const bool keep = key[t] > kth || (key[t] == kth && id[t] <= last);
-        const uint64_t mask = __ballot(keep);
-        if (keep) {
-            const int below =
-                __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
-            if (base + below < 64) buf[base + below] = pack(key[t], id[t]);  // never more than count <= 64
-        }
-        base += __popcll(mask);
-    }
-    wave_sync_lds();
-    const uint64_t v = lane < count ? buf[lane] : 0ull;
-    wave_sync_lds();
-    return sort64_desc(v, lane);
+    return sorted_survivors(count, st, lane);
 }
 
-template <int MAXM>
+// Exact top-k with every key recomputed by key_of in rolled loops (the rare
+// full-grid path).
+template <typename KeyOf, typename IdOf>
+__device__ uint64_t wave_topk_rolled(KeyOf key_of, IdOf id_of, int m, int k, Stage &st, int lane)
+{
+    uint32_t lane_max = 0;
+#pragma unroll 1
+    for (int t = 0; t < m; ++t) {
+        const uint32_t key = key_of(t);
+        lane_max = key > lane_max ? key : lane_max;
+    }
+    uint32_t kth = read_lane(sort64_desc(lane_max), k - 1);
+    uint32_t last = 0xFFFFFFFFu;
+    int count = compact_rolled(key_of, id_of, m, kth, last, st, lane);
+    if (count > 64) {
+        exact_cut(key_of, id_of, m, k, kth, last);
+        count = compact_rolled(key_of, id_of, m, kth, last, st, lane);
+    }
+    return sorted_survivors(count, st, lane);
+}
+
+// Loads the order keys of one half row: element t*64 + lane in slot t (0 past
+// the end of the row).  The loads are unconditional (clamped index), so all
+// of them are in flight together instead of one exec-masked load at a time.
+template <int MH>
+__device__ __forceinline__ void load_keys(const float *row, int n, int lane, uint32_t (&key)[MH])
+{
+    float v[MH];
+#pragma unroll
+    for (int t = 0; t < MH; ++t) v[t] = row[min(t * 64 + lane, n - 1)];
+#pragma unroll
+    for (int t = 0; t < MH; ++t) key[t] = t * 64 + lane < n ? order_key(v[t]) : 0u;
+}
+
+// Top-k of one half from keys already in registers; writes the sorted result
+// to (hs[p][j], hi[p][j]), j < k.
+template <int MH>
+__device__ __forceinline__ void half_select(const uint32_t (&key)[MH], const float *row, int p, int n, int k,
+                                            Stage &st, float (*hs)[64], uint32_t (*hi)[64], int lane)
+{
+    const auto id_of = [lane](int t) { return (uint32_t)(t * 64 + lane); };
+    const auto reread = [=](int t) {
+        const int e = t * 64 + lane;
+        return e < n ? order_key(row[e]) : 0u;
+    };
+    const uint64_t v = wave_topk(key, reread, id_of, (n + 63) >> 6, k, st, lane);
+    if (lane < k) {
+        hs[p][lane] = key_score((uint32_t)(v >> 32));
+        hi[p][lane] = unpack_id(v);
+    }
+}
+
+// a4 for both halves of one (token, head), one after the other.  Short rows
+// (MH <= 16 slots) load both halves before selecting, so the second row's
+// loads overlap the first selection; longer rows load each half in turn to
+// bound the live registers.
+template <int MH>
+__device__ void half_topk(const float *row0, int n, int k, Stage &st, float (*hs)[64], uint32_t (*hi)[64], int lane)
+{
+    const float *row1 = row0 + n;
+    if constexpr (MH <= 16) {
+        uint32_t key0[MH], key1[MH];
+        load_keys(row0, n, lane, key0);
+        load_keys(row1, n, lane, key1);
+        half_select(key0, row0, 0, n, k, st, hs, hi, lane);
+        half_select(key1, row1, 1, n, k, st, hs, hi, lane);
+    } else {
+#pragma unroll 1
+        for (int p = 0; p < 2; ++p) {
+            uint32_t key[MH];
+            const float *row = p ? row1 : row0;
+            load_keys(row, n, lane, key);
+            half_select(key, row, p, n, k, st, hs, hi, lane);
+        }
+    }
+}
+
+// a5 over the whole k*k grid (when the staircase cannot be certified): cell
+// (i, j) lives in lane (i % R) * k + j, slot i / R, R = floor(64 / k); keys
+// are recomputed from the LDS half lists.
+__device__ uint64_t full_grid_topk(int n, int k, float (*hs)[64], uint32_t (*hi)[64], Stage &st, int lane)
+{
+    const int R = 64 / k;
+    const int q = lane / k;
+    const int j = lane - q * k;
+    const bool lane_ok = q < R;
+    const int jj = lane_ok ? j : 0;
+    const int slots = (k + R - 1) / R;
+    const auto key_of = [=](int t) {
+        const int i = t * R + q;
+        const bool ok = lane_ok && i < k;
+        return ok ? order_key(hs[0][ok ? i : 0] + hs[1][jj]) : 0u;
+    };
+    const auto id_of = [=](int t) {
+        const int i = min(t * R + q, k - 1);
+        return hi[0][i] * (uint32_t)n + hi[1][jj];
+    };
+    return wave_topk_rolled(key_of, id_of, slots, k, st, lane);
+}
+
+template <int MH>
 __global__ __launch_bounds__(64 * WAVES) void select_kernel(const float *__restrict__ scores, int64_t pairs, int n,
-                                                            int k, int32_t *__restrict__ idx_out,
+                                                            int k, const uint32_t *__restrict__ stair,
+                                                            int stair_cells, int32_t *__restrict__ idx_out,
                                                             float *__restrict__ w_out)
 {
-    __shared__ uint64_t buf[WAVES][64];
+    __shared__ Stage stage[WAVES];
     __shared__ float half_score[WAVES][2][64];
     __shared__ uint32_t half_index[WAVES][2][64];
 
@@ -165,88 +288,93 @@ __global__ __launch_bounds__(64 * WAVES) void select_kernel(const float *__restr
     const int wv = threadIdx.x >> 6;
     const int64_t pair = (int64_t)blockIdx.x * WAVES + wv;  // b * H + h
     if (pair >= pairs) return;
-    float *hs = &half_score[wv][0][0];
-    uint32_t *hi = &half_index[wv][0][0];
+    float(*hs)[64] = half_score[wv];
+    uint32_t(*hi)[64] = half_index[wv];
 
-    // a4: each half's top-k, kept in LDS as (score, subkey index), best first.
-    const int m = (n + 63) >> 6;
-#pragma unroll 1
-    for (int p = 0; p < 2; ++p) {
-        const float *row = scores + (pair * 2 + p) * (int64_t)n;
-        uint32_t key[MAXM], id[MAXM];
-#pragma unroll
-        for (int t = 0; t < MAXM; ++t) {
-            const int e = t * 64 + lane;
-            const bool ok = t < m && e < n;
-            key[t] = ok ? order_key(row[e]) : 0u;
-            id[t] = (uint32_t)e;
-        }
-        const uint64_t c = wave_topk<MAXM>(key, id, k, &buf[wv][0], lane);
-        if (lane < k) {
-            hs[p * 64 + lane] = key_score((uint32_t)(c >> 32));
-            hi[p * 64 + lane] = unpack_id(c);
-        }
-    }
+    // a4
+    half_topk<MH>(scores + pair * 2 * (int64_t)n, n, k, stage[wv], hs, hi, lane);
     wave_sync_lds();
 
-    // a5: candidate (i, j) lives in lane (i % R) * k + j, slot i / R, with
-    // R = floor(64 / k) grid rows per slot.
-    const int R = 64 / k;
-    const int q = lane / k;
-    const int j = lane - q * k;
-    const bool lane_ok = q < R;
-    const float s1 = lane_ok ? hs[64 + j] : 0.0f;
-    const uint32_t i1 = lane_ok ? hi[64 + j] : 0u;
-    const int slots = (k + R - 1) / R;
-    uint32_t key[MAXM], id[MAXM];
+    // a5 on the staircase: stair[c] = (i << 16) | j for c < stair_cells,
+    // 0xFFFFFFFF up to STAIR_SLOTS * 64 (loaded unconditionally)
+    const auto cell_of = [=](int t) { return stair[t * 64 + lane]; };
+    const auto stair_key = [=](int t) {
+        const uint32_t ij = cell_of(t);
+        return ij != 0xFFFFFFFFu ? order_key(hs[0][ij >> 16] + hs[1][ij & 0xFFFFu]) : 0u;
+    };
+    const auto stair_id = [=](int t) {
+        const uint32_t ij = cell_of(t);
+        return ij != 0xFFFFFFFFu ? hi[0][ij >> 16] * (uint32_t)n + hi[1][ij & 0xFFFFu] : 0u;
+    };
+    uint32_t cell[STAIR_SLOTS], key[STAIR_SLOTS];
 #pragma unroll
-    for (int t = 0; t < MAXM; ++t) {
-        const int i = t * R + q;
-        const bool ok = lane_ok && t < slots && i < k;
-        const float s0 = ok ? hs[i] : 0.0f;
-        const uint32_t i0 = ok ? hi[i] : 0u;
-        key[t] = ok ? order_key(s0 + s1) : 0u;
-        id[t] = i0 * (uint32_t)n + i1;
+    for (int t = 0; t < STAIR_SLOTS; ++t) cell[t] = cell_of(t);
+#pragma unroll
+    for (int t = 0; t < STAIR_SLOTS; ++t)
+        key[t] = cell[t] != 0xFFFFFFFFu ? order_key(hs[0][cell[t] >> 16] + hs[1][cell[t] & 0xFFFFu]) : 0u;
+    uint64_t c = wave_topk(key, stair_key, stair_id, STAIR_SLOTS, k, stage[wv], lane);
+
+    // certificate: no cell outside the staircase reaches the k-th score
+    const uint32_t vk = read_lane((uint32_t)(c >> 32), k - 1);
+    bool reach = false;
+    if (lane < k) {
+        const int i_out = k / (lane + 1);  // first row of column `lane` outside the staircase
+        if (i_out < k) reach = order_key(hs[0][i_out] + hs[1][lane]) >= vk;
     }
-    const uint64_t c = wave_topk<MAXM>(key, id, k, &buf[wv][0], lane);
+    if (__ballot(reach) != 0ull) c = full_grid_topk(n, k, hs, hi, stage[wv], lane);
 
     // a6: softmax over the k winners; lane 0 holds the largest score.
     const float top = key_score((uint32_t)(c >> 32));
-    const float mx = __shfl(top, 0, 64);
+    const float mx = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(top), 0));
     const float e = lane < k ? expf(top - mx) : 0.0f;
-    float sum = e;
-#pragma unroll
-    for (int s = 32; s > 0; s >>= 1) sum += __shfl_xor(sum, s, 64);
+    const float sum = wave_sum(e);
     if (lane < k) {
         idx_out[pair * k + lane] = (int32_t)unpack_id(c);
         w_out[pair * k + lane] = e / sum;
     }
 }
 
-template <int MAXM>
-hipError_t launch(const float *scores, int64_t pairs, int n, int k, int32_t *idx, float *w, hipStream_t stream)
+template <int MH>
+hipError_t launch(const float *scores, int64_t pairs, int n, int k, const uint32_t *stair, int cells, int32_t *idx,
+                  float *w, hipStream_t stream)
 {
     const int64_t blocks = (pairs + WAVES - 1) / WAVES;
-    hipLaunchKernelGGL(select_kernel<MAXM>, dim3((unsigned)blocks), dim3(64 * WAVES), 0, stream, scores, pairs, n, k,
-                       idx, w);
+    hipLaunchKernelGGL(select_kernel<MH>, dim3((unsigned)blocks), dim3(64 * WAVES), 0, stream, scores, pairs, n, k,
+                       stair, cells, idx, w);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_select(const float *scores, int64_t B, int H, int n, int k, int32_t *idx, float *w,
-                         hipStream_t stream)
+int staircase_cells(int k)
+{
+    int c = 0;
+    for (int j = 0; j < k; ++j) c += k / (j + 1);
+    return c;
+}
+
+void staircase_table(int k, uint32_t *out)
+{
+    for (int c = 0; c < kMaxStaircaseCells; ++c) out[c] = 0xFFFFFFFFu;
+    int c = 0;
+    for (int i = 0; i < k; ++i)
+        for (int j = 0; j < k; ++j)
+            if ((i + 1) * (j + 1) <= k) out[c++] = ((uint32_t)i << 16) | (uint32_t)j;
+}
+
+hipError_t launch_select(const float *scores, int64_t B, int H, int n, int k, const uint32_t *stair,
+                         int32_t *idx, float *w, hipStream_t stream)
 {
     const int64_t pairs = B * H;
     if (pairs <= 0) return hipSuccess;
-    const int R = 64 / k;
-    const int m_half = (n + 63) / 64;
-    const int m_cand = (k + R - 1) / R;
-    const int m = m_half > m_cand ? m_half : m_cand;
-    if (m <= 4) return launch<4>(scores, pairs, n, k, idx, w, stream);
-    if (m <= 16) return launch<16>(scores, pairs, n, k, idx, w, stream);
-    if (m <= 32) return launch<32>(scores, pairs, n, k, idx, w, stream);
-    return launch<64>(scores, pairs, n, k, idx, w, stream);
+    const int cells = staircase_cells(k);
+    static_assert(STAIR_SLOTS * 64 <= kMaxStaircaseCells, "the kernel reads the whole padded table");
+    if (cells > STAIR_SLOTS * 64) return hipErrorInvalidValue;
+    const int mh = (n + 63) / 64;
+    if (mh <= 4) return launch<4>(scores, pairs, n, k, stair, cells, idx, w, stream);
+    if (mh <= 16) return launch<16>(scores, pairs, n, k, stair, cells, idx, w, stream);
+    if (mh <= 32) return launch<32>(scores, pairs, n, k, stair, cells, idx, w, stream);
+    return launch<64>(scores, pairs, n, k, stair, cells, idx, w, stream);
 }
 
 }  // namespace pkm

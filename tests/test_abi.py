@@ -80,7 +80,8 @@ def test_config_check(change, status):
 def test_workspace_bytes():
     cfg = pk.make_config(**GOOD)
     mb, H, D, n, k = 16384, 4, 1024, 1024, 32
-    assert pk.workspace_bytes(cfg) == 4 * mb * H * (D + 2 * n + 2 * k)
+    stair = 320 * 4  # staircase cells of the candidate grid
+    assert pk.workspace_bytes(cfg) == 4 * mb * H * (D + 2 * n + 2 * k) + stair
     with pytest.raises(pk.PkmError):
         pk.workspace_bytes(pk.make_config(**{**GOOD, "k": 0}))
 
