@@ -149,6 +149,8 @@ def main():
     wts = torch.empty((wl.B, wl.H, wl.k), dtype=torch.float32, device="cuda")
 
     ms = timed_steps(torch, lambda: mem.forward(P, xt, out, idx, wts), args.steps, args.warmup)
+    rows = idx.cpu().numpy().ravel()
+    distinct = float(np.unique(rows).size) / rows.size
     kt = kernel_times(torch, mem, P, xt, args.steps, args.warmup)
     g_uniform_ms = gather_uniform_ms(torch, mem, P, wl, args.steps, args.warmup)
 
@@ -187,6 +189,7 @@ def main():
         "roofline": roof(dominant),
         "gather_roofline": roof("gather"),
         "gather_uniform_rows_gbs": round(work["gather_bytes"] * B / (g_uniform_ms * 1e-3) / 1e9, 1),
+        "gathered_rows_distinct_frac": round(distinct, 4),
         "kernels_ms": {nm: round(v, 4) for nm, v in kt.items()},
         "kernel_rooflines": {nm: {"achieved": round(rl[nm][1], 2), "unit": rl[nm][3],
                                   "frac": round(rl[nm][1] / rl[nm][2], 4)} for nm in rl},
