@@ -110,11 +110,12 @@ def cpu_baseline(wl, params, x, seconds=10.0):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="default", choices=sorted(synthetic.WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target wall time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--max-batch", type=int, default=0, help="tokens per internal chunk (0: the whole batch)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -143,7 +144,8 @@ def main():
     x = synthetic.make_x(wl)
     P = pk.params_to_device(params, wl.table, "cuda")
     xt = torch.from_numpy(x).cuda()
-    mem = pk.Memory(wl.D, wl.H, wl.n, wl.k, wl.table, max_batch=wl.B)
+    max_batch = args.max_batch or wl.B
+    mem = pk.Memory(wl.D, wl.H, wl.n, wl.k, wl.table, max_batch=max_batch)
     out = torch.empty((wl.B, wl.D), dtype=torch.float32, device="cuda")
     idx = torch.empty((wl.B, wl.H, wl.k), dtype=torch.int32, device="cuda")
     wts = torch.empty((wl.B, wl.H, wl.k), dtype=torch.float32, device="cuda")
@@ -185,7 +187,7 @@ def main():
         "dtype": "fp32",
         "data": "synthetic",
         "config": {"workload": wl.name, "tokens_per_step": B, "dim": wl.D, "heads": wl.H, "n_keys": wl.n,
-                   "rows": wl.N, "k": wl.k, "value_table": wl.table, "seed": 0},
+                   "rows": wl.N, "k": wl.k, "value_table": wl.table, "seed": 0, "max_batch": max_batch},
         "roofline": roof(dominant),
         "gather_roofline": roof("gather"),
         "gather_uniform_rows_gbs": round(work["gather_bytes"] * B / (g_uniform_ms * 1e-3) / 1e9, 1),

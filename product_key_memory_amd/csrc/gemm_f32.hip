@@ -9,134 +9,162 @@
 // so C = A . B^T with no transposes.  Scores decide the winners, so the
 // contraction stays in fp32: v_mfma_f32_32x32x2_f32, fp32 accumulate.
 //
-// Tiling for CDNA4: a 256-thread workgroup owns a 128x128 tile of C; its four
-// wave64s each own 64x64 (2x2 MFMA blocks of 32x32, 64 accumulators per
-// lane).  K advances 32 at a time through one LDS stage per operand
-// (128 rows x 32 floats, rows padded to 36 floats so the 16-byte fragment
-// reads of consecutive rows fall on distinct banks); the next stage is
-// prefetched into registers while the MFMAs run.  Within a 32-wide K chunk
-// MFMA step t pairs k = t (lanes 0-31) with k = 16 + t (lanes 32-63), which
-// makes every lane's fragments 16 contiguous floats (four ds_read_b128).
+// Tiling for CDNA4.  A workgroup owns a BM x BN tile of C; each of its
+// WM x WN wave64s owns (BM/WM) x (BN/WN) as 32x32 MFMA blocks.  K advances
+// BK at a time through LDS stages (rows padded by 4 floats so the 16-byte
+// fragment reads of consecutive rows land on distinct banks); the next chunk
+// is loaded into registers while the MFMAs run, and with two stages one
+// barrier per chunk suffices.  Within a chunk, MFMA step t pairs k = t
+// (lanes 0-31) with k = BK/2 + t (lanes 32-63), so each lane's fragment is
+// BK/2 contiguous floats (ds_read_b128 only).
+//   Large grids: 256x256 tiles, 8 waves of 64x128, BK 32, two stages
+//   (147 KB of LDS, one workgroup per CU: operand traffic per flop halves
+//   against 128x128).
+//   Small grids (fewer tiles than CUs at 256x256): 128x128, 4 waves of
+//   64x64, BK 32, one stage.
 #include "pkm_internal.h"
 
 namespace pkm {
 namespace {
 
-constexpr int BM = 128;
-constexpr int BN = 128;
-constexpr int BK = 32;
-constexpr int LDS_STRIDE = BK + 4;  // floats per LDS row
-constexpr int THREADS = 256;
-
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float fx4 __attribute__((ext_vector_type(4)));
 
-template <bool BN_EPILOGUE>
-__global__ __launch_bounds__(THREADS, 2) void gemm_nt_f32_kernel(GemmArgs a)
+constexpr int kCUs = 256;  // MI355X compute units
+
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_>
+struct Tile {
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, STAGES = STAGES_;
+    static constexpr int THREADS = 64 * WM * WN;
+    static constexpr int LDS = BK + 4;                          // floats per LDS row
+    static constexpr int TM = BM / WM / 32, TN = BN / WN / 32;  // 32x32 blocks per wave
+    static constexpr int HK = BK / 2;                           // k per lane half within a chunk
+    static constexpr int C4 = BK / 4;                           // float4 per row chunk
+    static constexpr int RPP = THREADS / C4;                    // rows moved per pass
+    static constexpr int PA = BM / RPP, PB = BN / RPP;          // passes per operand
+    static constexpr size_t LDS_BYTES = (size_t)STAGES * (BM + BN) * LDS * sizeof(float);
+    static_assert(BM % RPP == 0 && BN % RPP == 0 && BK % 8 == 0, "tile shape");
+};
+
+using BigTile = Tile<256, 256, 32, 4, 2, 2>;
+using SmallTile = Tile<128, 128, 32, 2, 2, 1>;
+
+template <typename T>
+__device__ __forceinline__ void load_chunk(fx4 (&ra)[T::PA], fx4 (&rb)[T::PB], const float *const (&ap)[T::PA],
+                                           const float *const (&bp)[T::PB], int kt)
 {
-    __shared__ __attribute__((aligned(16))) float As[BM * LDS_STRIDE];
-    __shared__ __attribute__((aligned(16))) float Bs[BN * LDS_STRIDE];
+#pragma unroll
+    for (int i = 0; i < T::PA; ++i) ra[i] = *reinterpret_cast<const fx4 *>(ap[i] + kt * T::BK);
+#pragma unroll
+    for (int i = 0; i < T::PB; ++i) rb[i] = *reinterpret_cast<const fx4 *>(bp[i] + kt * T::BK);
+}
 
-    const int tiles_n = (a.N + BN - 1) / BN;
+template <typename T>
+__device__ __forceinline__ void store_chunk(const fx4 (&ra)[T::PA], const fx4 (&rb)[T::PB], float *as, float *bs,
+                                            int lr, int lc4)
+{
+#pragma unroll
+    for (int i = 0; i < T::PA; ++i) *reinterpret_cast<fx4 *>(&as[(lr + T::RPP * i) * T::LDS + lc4 * 4]) = ra[i];
+#pragma unroll
+    for (int i = 0; i < T::PB; ++i) *reinterpret_cast<fx4 *>(&bs[(lr + T::RPP * i) * T::LDS + lc4 * 4]) = rb[i];
+}
+
+template <typename T>
+__device__ __forceinline__ void mfma_chunk(floatx16 (&acc)[T::TM][T::TN], const float *as, const float *bs, int wm,
+                                           int wn, int il, int kk)
+{
+#pragma unroll
+    for (int q = 0; q < T::HK / 4; ++q) {
+        fx4 af[T::TM], bf[T::TN];
+#pragma unroll
+        for (int i = 0; i < T::TM; ++i)
+            af[i] = *reinterpret_cast<const fx4 *>(&as[(wm * T::TM * 32 + i * 32 + il) * T::LDS + kk * T::HK + q * 4]);
+#pragma unroll
+        for (int j = 0; j < T::TN; ++j)
+            bf[j] = *reinterpret_cast<const fx4 *>(&bs[(wn * T::TN * 32 + j * 32 + il) * T::LDS + kk * T::HK + q * 4]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+                for (int j = 0; j < T::TN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i][e], bf[j][e], acc[i][j], 0, 0, 0);
+    }
+}
+
+template <typename T, bool BN_EPILOGUE>
+__global__ __launch_bounds__(T::THREADS) void gemm_nt_f32_kernel(GemmArgs a)
+{
+    extern __shared__ __attribute__((aligned(16))) float smem[];
+    float *As = smem;
+    float *Bs = smem + T::STAGES * T::BM * T::LDS;
+
+    const int tiles_n = (a.N + T::BN - 1) / T::BN;
     const int tm = blockIdx.x / tiles_n;
     const int tn = blockIdx.x - tm * tiles_n;
     const int g = blockIdx.y;
     const float *A = a.A + (int64_t)g * a.strideA;
     const float *Bmat = a.B + (int64_t)g * a.strideB;
     float *C = a.C + (int64_t)g * a.strideC;
-    const int m0 = tm * BM, n0 = tn * BN;
+    const int m0 = tm * T::BM, n0 = tn * T::BN;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / T::WN, wn = wave % T::WN;
 
-    // Global -> register mapping: thread t moves float4 column (t & 7) of
-    // rows (t >> 3) + 32 i, i < 4, of both operand tiles.  Rows past the
-    // matrix edge re-read the last row; their results are never stored.
-    const int lc4 = tid & 7;
-    const int lr = tid >> 3;
-    const float *ap[4];
-    const float *bp[4];
+    // Global -> register mapping: thread t moves float4 column (t % C4) of
+    // rows t / C4 + RPP * i of both operand tiles.  Rows past the matrix
+    // edge re-read the last row; their results are never stored.
+    const int lc4 = tid % T::C4;
+    const int lr = tid / T::C4;
+    const float *ap[T::PA];
+    const float *bp[T::PB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        int am = min(m0 + lr + 32 * i, a.M - 1);
-        int bn = min(n0 + lr + 32 * i, a.N - 1);
-        ap[i] = A + (int64_t)am * a.lda + lc4 * 4;
-        bp[i] = Bmat + (int64_t)bn * a.ldb + lc4 * 4;
-    }
-    float4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
-#define PKM_GLOAD(k0)                                                  \
-    do {                                                               \
-        ra0 = *reinterpret_cast<const float4 *>(ap[0] + (k0));         \
-        ra1 = *reinterpret_cast<const float4 *>(ap[1] + (k0));         \
-        ra2 = *reinterpret_cast<const float4 *>(ap[2] + (k0));         \
-        ra3 = *reinterpret_cast<const float4 *>(ap[3] + (k0));         \
-        rb0 = *reinterpret_cast<const float4 *>(bp[0] + (k0));         \
-        rb1 = *reinterpret_cast<const float4 *>(bp[1] + (k0));         \
-        rb2 = *reinterpret_cast<const float4 *>(bp[2] + (k0));         \
-        rb3 = *reinterpret_cast<const float4 *>(bp[3] + (k0));         \
-    } while (0)
-    float *as_w = &As[lr * LDS_STRIDE + lc4 * 4];
-    float *bs_w = &Bs[lr * LDS_STRIDE + lc4 * 4];
-#define PKM_SSTORE()                                                                   \
-    do {                                                                               \
-        *reinterpret_cast<float4 *>(as_w + 0 * 32 * LDS_STRIDE) = ra0;                 \
-        *reinterpret_cast<float4 *>(as_w + 1 * 32 * LDS_STRIDE) = ra1;                 \
-        *reinterpret_cast<float4 *>(as_w + 2 * 32 * LDS_STRIDE) = ra2;                 \
-        *reinterpret_cast<float4 *>(as_w + 3 * 32 * LDS_STRIDE) = ra3;                 \
-        *reinterpret_cast<float4 *>(bs_w + 0 * 32 * LDS_STRIDE) = rb0;                 \
-        *reinterpret_cast<float4 *>(bs_w + 1 * 32 * LDS_STRIDE) = rb1;                 \
-        *reinterpret_cast<float4 *>(bs_w + 2 * 32 * LDS_STRIDE) = rb2;                 \
-        *reinterpret_cast<float4 *>(bs_w + 3 * 32 * LDS_STRIDE) = rb3;                 \
-    } while (0)
+    for (int i = 0; i < T::PA; ++i) ap[i] = A + (int64_t)min(m0 + lr + T::RPP * i, a.M - 1) * a.lda + lc4 * 4;
+#pragma unroll
+    for (int i = 0; i < T::PB; ++i) bp[i] = Bmat + (int64_t)min(n0 + lr + T::RPP * i, a.N - 1) * a.ldb + lc4 * 4;
+    fx4 ra[T::PA], rb[T::PB];
 
-    floatx16 acc[2][2];
+    floatx16 acc[T::TM][T::TN];
 #pragma unroll
-    for (int si = 0; si < 2; ++si)
+    for (int i = 0; i < T::TM; ++i)
 #pragma unroll
-        for (int sj = 0; sj < 2; ++sj)
+        for (int j = 0; j < T::TN; ++j)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) acc[si][sj][v] = 0.0f;
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
     const int il = lane & 31;  // row (A) / column (B) inside a 32x32 block
     const int kk = lane >> 5;  // which k of the MFMA's pair this lane feeds
+    const int KT = a.K / T::BK;
 
-    PKM_GLOAD(0);
-    PKM_SSTORE();
+    load_chunk<T>(ra, rb, ap, bp, 0);
+    store_chunk<T>(ra, rb, As, Bs, lr, lc4);
     __syncthreads();
-    const int KT = a.K / BK;
     for (int kt = 0; kt < KT; ++kt) {
-        if (kt + 1 < KT) PKM_GLOAD((kt + 1) * BK);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            float4 af[2], bf[2];
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                af[s] = *reinterpret_cast<const float4 *>(&As[(wm * 64 + s * 32 + il) * LDS_STRIDE + kk * 16 + q * 4]);
-                bf[s] = *reinterpret_cast<const float4 *>(&Bs[(wn * 64 + s * 32 + il) * LDS_STRIDE + kk * 16 + q * 4]);
+        const int s = T::STAGES == 1 ? 0 : (kt & 1);
+        if (kt + 1 < KT) load_chunk<T>(ra, rb, ap, bp, kt + 1);
+        mfma_chunk<T>(acc, As + s * T::BM * T::LDS, Bs + s * T::BN * T::LDS, wm, wn, il, kk);
+        if constexpr (T::STAGES == 1) {
+            __syncthreads();
+            if (kt + 1 < KT) {
+                store_chunk<T>(ra, rb, As, Bs, lr, lc4);
+                __syncthreads();
             }
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-#pragma unroll
-                for (int si = 0; si < 2; ++si)
-#pragma unroll
-                    for (int sj = 0; sj < 2; ++sj)
-                        acc[si][sj] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[si][e], bf[sj][e], acc[si][sj], 0, 0, 0);
-        }
-        __syncthreads();
-        if (kt + 1 < KT) {
-            PKM_SSTORE();
+        } else {
+            // stage s ^ 1 was last read in the previous chunk, before the
+            // barrier that closed it
+            if (kt + 1 < KT)
+                store_chunk<T>(ra, rb, As + (s ^ 1) * T::BM * T::LDS, Bs + (s ^ 1) * T::BN * T::LDS, lr, lc4);
             __syncthreads();
         }
     }
-#undef PKM_GLOAD
-#undef PKM_SSTORE
 
     // 32x32 accumulator layout: register v of lane l holds row
     // 8*(v/4) + 4*(l/32) + v%4, column l%32.
 #pragma unroll
-    for (int sj = 0; sj < 2; ++sj) {
-        const int col = n0 + wn * 64 + sj * 32 + il;
+    for (int j = 0; j < T::TN; ++j) {
+        const int col = n0 + wn * T::TN * 32 + j * 32 + il;
         if (col >= a.N) continue;
         float mean = 0.0f, mul = 1.0f, beta = 0.0f;
         if (BN_EPILOGUE) {
@@ -145,12 +173,12 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_nt_f32_kernel(GemmArgs a)
             beta = a.bn_beta[col];
         }
 #pragma unroll
-        for (int si = 0; si < 2; ++si) {
+        for (int i = 0; i < T::TM; ++i) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int row = m0 + wm * 64 + si * 32 + (v >> 2) * 8 + kk * 4 + (v & 3);
+                const int row = m0 + wm * T::TM * 32 + i * 32 + (v >> 2) * 8 + kk * 4 + (v & 3);
                 if (row < a.M) {
-                    float c = acc[si][sj][v];
+                    float c = acc[i][j][v];
                     if (BN_EPILOGUE) c = (c - mean) * mul + beta;
                     C[(int64_t)row * a.ldc + col] = c;
                 }
@@ -159,19 +187,46 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_nt_f32_kernel(GemmArgs a)
     }
 }
 
+template <typename T>
+int64_t tile_count(const GemmArgs &a)
+{
+    return (int64_t)((a.M + T::BM - 1) / T::BM) * ((a.N + T::BN - 1) / T::BN);
+}
+
+template <typename T>
+hipError_t launch_tile(const GemmArgs &a, hipStream_t stream)
+{
+    const int64_t tiles = tile_count<T>(a);
+    if (tiles > 0x7FFFFFFF || a.batch > 65535) return hipErrorInvalidConfiguration;
+    if (T::LDS_BYTES > 65536) {
+        // Dynamic LDS above 64 KiB must be allowed per kernel (gfx950 has
+        // 160 KiB per CU); done once per kernel per process.
+        static const hipError_t allowed = [] {
+            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_nt_f32_kernel<T, true>),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)T::LDS_BYTES);
+            if (e == hipSuccess)
+                e = hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_nt_f32_kernel<T, false>),
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)T::LDS_BYTES);
+            return e;
+        }();
+        if (allowed != hipSuccess) return allowed;
+    }
+    const dim3 grid((unsigned)tiles, a.batch);
+    if (a.bn_mean)
+        hipLaunchKernelGGL((gemm_nt_f32_kernel<T, true>), grid, dim3(T::THREADS), T::LDS_BYTES, stream, a);
+    else
+        hipLaunchKernelGGL((gemm_nt_f32_kernel<T, false>), grid, dim3(T::THREADS), T::LDS_BYTES, stream, a);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_gemm_nt_f32(const GemmArgs &a, hipStream_t stream)
 {
     if (a.M <= 0 || a.N <= 0 || a.batch <= 0) return hipSuccess;
-    const int64_t tiles = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-    if (tiles > 0x7FFFFFFF || a.batch > 65535) return hipErrorInvalidConfiguration;
-    dim3 grid((unsigned)tiles, a.batch);
-    if (a.bn_mean)
-        hipLaunchKernelGGL(gemm_nt_f32_kernel<true>, grid, dim3(THREADS), 0, stream, a);
-    else
-        hipLaunchKernelGGL(gemm_nt_f32_kernel<false>, grid, dim3(THREADS), 0, stream, a);
-    return hipGetLastError();
+    if (a.K % 32 != 0) return hipErrorInvalidValue;
+    if (tile_count<BigTile>(a) * a.batch >= kCUs) return launch_tile<BigTile>(a, stream);
+    return launch_tile<SmallTile>(a, stream);
 }
 
 }  // namespace pkm
