@@ -17,9 +17,10 @@
 // bitonic sort of 64 words): at least k elements are >= T, so every winner
 // is.  The elements >= T (about 1.35 k for random scores) are compacted into
 // LDS with ballot + mbcnt and one 64-lane bitonic sort of packed keys orders
-// them.  If more than 64 survive (heavy ties), the exact k-th key is found
-// by MSB-first bisection with ballot counts, then the last index kept among
-// the ties, and exactly k are compacted.  The halves are selected one after
+// them (65 to 128 survivors: two sorts and one bitonic merge).  If more than
+// 128 survive (heavy exact ties), the exact k-th key is found by MSB-first
+// bisection with ballot counts, then the last index kept among the ties,
+// and exactly k are compacted.  The halves are selected one after
 // the other; every row load is issued before the first is consumed.
 //
 // Candidates.  With both halves sorted, s0[i] + s1[j] can only be beaten by
@@ -78,18 +79,19 @@ __device__ __forceinline__ void wave_sync_lds()
     __builtin_amdgcn_wave_barrier();
 }
 
-// Per-wave LDS: 64 compaction slots plus one discard slot per lane, so the
+// Per-wave LDS: 128 compaction slots plus one discard slot per lane, so the
 // compaction stores unconditionally and never branches.
+constexpr int kSlots = 128;
 struct Stage {
-    uint64_t slot[128];
+    uint64_t slot[kSlots + 64];
 };
 
-// Appends the packed key of element t to the compaction when `keep`.
+// Appends the packed key of an element to the compaction when `keep`.
 __device__ __forceinline__ void append(bool keep, uint32_t key, uint32_t id, int &base, Stage &st, int lane)
 {
     const uint64_t mask = __ballot(keep);
     const int pos = base + below_me(mask);
-    st.slot[keep && pos < 64 ? pos : 64 + lane] = pack(key, id);
+    st.slot[keep && pos < kSlots ? pos : kSlots + lane] = pack(key, id);
     base += __popcll(mask);
 }
 
@@ -102,7 +104,9 @@ __device__ __forceinline__ bool kept(uint32_t key, uint32_t id, uint32_t kth, ui
 // to keep so that exactly k elements are kept.  count(key >= x) does not
 // increase with x, so the MSB-first greedy finds the largest x with at least
 // k elements >= x: the k-th largest key.  Rolled loops over the m slots with
-// keys recomputed by key_of: this path is rare and must not hold registers.
+// keys recomputed by key_of: only inputs with more than 128 keys at or above
+// the first threshold (heavy exact ties) come here, and it must not hold
+// registers.
 template <typename KeyOf, typename IdOf>
 __device__ void exact_cut(KeyOf key_of, IdOf id_of, int m, int k, uint32_t &kth, uint32_t &last)
 {
@@ -130,7 +134,7 @@ __device__ void exact_cut(KeyOf key_of, IdOf id_of, int m, int k, uint32_t &kth,
     }
 }
 
-// Rolled compaction with recomputed keys (rare paths).
+// Rolled compaction with recomputed keys.
 template <typename KeyOf, typename IdOf>
 __device__ int compact_rolled(KeyOf key_of, IdOf id_of, int m, uint32_t kth, uint32_t last, Stage &st, int lane)
 {
@@ -143,18 +147,31 @@ __device__ int compact_rolled(KeyOf key_of, IdOf id_of, int m, uint32_t kth, uin
     return base;
 }
 
-// Reads back the count (<= 64) compacted keys, one per lane, and sorts them.
+__device__ __forceinline__ uint64_t max64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// Sorts the count (<= 128) compacted keys; lane j receives the j-th best.
+// Up to 64: one 64-lane bitonic sort.  Up to 128: both halves sorted, the
+// second reversed and merged elementwise (a bitonic sequence holding the
+// best 64 of both), then one bitonic clean.
 __device__ __forceinline__ uint64_t sorted_survivors(int count, Stage &st, int lane)
 {
     wave_sync_lds();
-    const uint64_t v = lane < count ? st.slot[lane] : 0ull;
+    uint64_t v = lane < count ? st.slot[lane] : 0ull;
+    uint64_t u = count > 64 && lane + 64 < count ? st.slot[lane + 64] : 0ull;
     wave_sync_lds();
-    return sort64_desc(v);
+    v = sort64_desc(v);
+    if (count > 64) {
+        u = sort64_desc(u);
+        const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)u, 63 - lane, 64);
+        const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(u >> 32), 63 - lane, 64);
+        v = merge_steps<32>(max64(v, ((uint64_t)hi << 32) | lo), true);
+    }
+    return v;
 }
 
-// Exact top-k (k <= 64) of m slots per lane, keys held in registers key[M]
-// (0 = absent), recomputed by slow_key on the rare tie path; lane j < k
-// receives the j-th best packed key.
+// Exact top-k (k <= 64) of the wave's elements, keys in registers key[M]
+// (0 = absent) and recomputed by slow_key for the rare heavy-tie path: lane
+// j < k receives the j-th best packed key.
 template <int M, typename SlowKey, typename IdOf>
 __device__ uint64_t wave_topk(const uint32_t (&key)[M], SlowKey slow_key, IdOf id_of, int m, int k, Stage &st,
                               int lane)
@@ -167,7 +184,7 @@ __device__ uint64_t wave_topk(const uint32_t (&key)[M], SlowKey slow_key, IdOf i
     int count = 0;
 #pragma unroll
     for (int t = 0; t < M; ++t) append(kept(key[t], id_of(t), kth, last), key[t], id_of(t), count, st, lane);
-    if (count > 64) {
+    if (count > kSlots) {
         exact_cut(slow_key, id_of, m, k, kth, last);
         count = compact_rolled(slow_key, id_of, m, kth, last, st, lane);
     }
@@ -188,38 +205,59 @@ __device__ uint64_t wave_topk_rolled(KeyOf key_of, IdOf id_of, int m, int k, Sta
     uint32_t kth = read_lane(sort64_desc(lane_max), k - 1);
     uint32_t last = 0xFFFFFFFFu;
     int count = compact_rolled(key_of, id_of, m, kth, last, st, lane);
-    if (count > 64) {
+    if (count > kSlots) {
         exact_cut(key_of, id_of, m, k, kth, last);
         count = compact_rolled(key_of, id_of, m, kth, last, st, lane);
     }
     return sorted_survivors(count, st, lane);
 }
 
-// Loads the order keys of one half row: element t*64 + lane in slot t (0 past
-// the end of the row).  The loads are unconditional (clamped index), so all
-// of them are in flight together instead of one exec-masked load at a time.
-template <int MH>
+// Element held in slot t of a lane.  With VEC4 (rows of a multiple of 256
+// scores) slot t holds element (t/4)*256 + 4*lane + t%4, so each lane reads
+// float4s; otherwise element t*64 + lane.
+template <bool VEC4>
+__device__ __forceinline__ int slot_element(int t, int lane)
+{
+    return VEC4 ? ((t >> 2) << 8) + (lane << 2) + (t & 3) : t * 64 + lane;
+}
+
+// Loads the order keys of one half row (0 past the end of the row).  The
+// loads are unconditional (clamped index), so all of them are in flight
+// together instead of one exec-masked load at a time.
+template <int MH, bool VEC4>
 __device__ __forceinline__ void load_keys(const float *row, int n, int lane, uint32_t (&key)[MH])
 {
     float v[MH];
+    if constexpr (VEC4) {
+        static_assert(MH % 4 == 0, "whole float4s");
 #pragma unroll
-    for (int t = 0; t < MH; ++t) v[t] = row[min(t * 64 + lane, n - 1)];
+        for (int q = 0; q < MH / 4; ++q) {
+            const float4 f = *reinterpret_cast<const float4 *>(row + min(q * 256 + lane * 4, n - 4));
+            v[4 * q] = f.x;
+            v[4 * q + 1] = f.y;
+            v[4 * q + 2] = f.z;
+            v[4 * q + 3] = f.w;
+        }
+    } else {
 #pragma unroll
-    for (int t = 0; t < MH; ++t) key[t] = t * 64 + lane < n ? order_key(v[t]) : 0u;
+        for (int t = 0; t < MH; ++t) v[t] = row[min(t * 64 + lane, n - 1)];
+    }
+#pragma unroll
+    for (int t = 0; t < MH; ++t) key[t] = slot_element<VEC4>(t, lane) < n ? order_key(v[t]) : 0u;
 }
 
 // Top-k of one half from keys already in registers; writes the sorted result
 // to (hs[p][j], hi[p][j]), j < k.
-template <int MH>
+template <int MH, bool VEC4>
 __device__ __forceinline__ void half_select(const uint32_t (&key)[MH], const float *row, int p, int n, int k,
                                             Stage &st, float (*hs)[64], uint32_t (*hi)[64], int lane)
 {
-    const auto id_of = [lane](int t) { return (uint32_t)(t * 64 + lane); };
+    const auto id_of = [lane](int t) { return (uint32_t)slot_element<VEC4>(t, lane); };
     const auto reread = [=](int t) {
-        const int e = t * 64 + lane;
+        const int e = slot_element<VEC4>(t, lane);
         return e < n ? order_key(row[e]) : 0u;
     };
-    const uint64_t v = wave_topk(key, reread, id_of, (n + 63) >> 6, k, st, lane);
+    const uint64_t v = wave_topk(key, reread, id_of, VEC4 ? MH : (n + 63) >> 6, k, st, lane);
     if (lane < k) {
         hs[p][lane] = key_score((uint32_t)(v >> 32));
         hi[p][lane] = unpack_id(v);
@@ -230,23 +268,23 @@ __device__ __forceinline__ void half_select(const uint32_t (&key)[MH], const flo
 // (MH <= 16 slots) load both halves before selecting, so the second row's
 // loads overlap the first selection; longer rows load each half in turn to
 // bound the live registers.
-template <int MH>
+template <int MH, bool VEC4>
 __device__ void half_topk(const float *row0, int n, int k, Stage &st, float (*hs)[64], uint32_t (*hi)[64], int lane)
 {
     const float *row1 = row0 + n;
     if constexpr (MH <= 16) {
         uint32_t key0[MH], key1[MH];
-        load_keys(row0, n, lane, key0);
-        load_keys(row1, n, lane, key1);
-        half_select(key0, row0, 0, n, k, st, hs, hi, lane);
-        half_select(key1, row1, 1, n, k, st, hs, hi, lane);
+        load_keys<MH, VEC4>(row0, n, lane, key0);
+        load_keys<MH, VEC4>(row1, n, lane, key1);
+        half_select<MH, VEC4>(key0, row0, 0, n, k, st, hs, hi, lane);
+        half_select<MH, VEC4>(key1, row1, 1, n, k, st, hs, hi, lane);
     } else {
 #pragma unroll 1
         for (int p = 0; p < 2; ++p) {
             uint32_t key[MH];
             const float *row = p ? row1 : row0;
-            load_keys(row, n, lane, key);
-            half_select(key, row, p, n, k, st, hs, hi, lane);
+            load_keys<MH, VEC4>(row, n, lane, key);
+            half_select<MH, VEC4>(key, row, p, n, k, st, hs, hi, lane);
         }
     }
 }
@@ -274,7 +312,7 @@ __device__ uint64_t full_grid_topk(int n, int k, float (*hs)[64], uint32_t (*hi)
     return wave_topk_rolled(key_of, id_of, slots, k, st, lane);
 }
 
-template <int MH>
+template <int MH, bool VEC4>
 __global__ __launch_bounds__(64 * WAVES) void select_kernel(const float *__restrict__ scores, int64_t pairs, int n,
                                                             int k, const uint32_t *__restrict__ stair,
                                                             int stair_cells, int32_t *__restrict__ idx_out,
@@ -292,27 +330,27 @@ __global__ __launch_bounds__(64 * WAVES) void select_kernel(const float *__restr
     uint32_t(*hi)[64] = half_index[wv];
 
     // a4
-    half_topk<MH>(scores + pair * 2 * (int64_t)n, n, k, stage[wv], hs, hi, lane);
+    half_topk<MH, VEC4>(scores + pair * 2 * (int64_t)n, n, k, stage[wv], hs, hi, lane);
     wave_sync_lds();
 
     // a5 on the staircase: stair[c] = (i << 16) | j for c < stair_cells,
     // 0xFFFFFFFF up to STAIR_SLOTS * 64 (loaded unconditionally)
     const auto cell_of = [=](int t) { return stair[t * 64 + lane]; };
+    uint32_t cell[STAIR_SLOTS], key[STAIR_SLOTS], id[STAIR_SLOTS];
+#pragma unroll
+    for (int t = 0; t < STAIR_SLOTS; ++t) cell[t] = cell_of(t);
+#pragma unroll
+    for (int t = 0; t < STAIR_SLOTS; ++t) {
+        const bool ok = cell[t] != 0xFFFFFFFFu;
+        const uint32_t i = ok ? cell[t] >> 16 : 0u, j = ok ? cell[t] & 0xFFFFu : 0u;
+        key[t] = ok ? order_key(hs[0][i] + hs[1][j]) : 0u;
+        id[t] = hi[0][i] * (uint32_t)n + hi[1][j];
+    }
     const auto stair_key = [=](int t) {
         const uint32_t ij = cell_of(t);
         return ij != 0xFFFFFFFFu ? order_key(hs[0][ij >> 16] + hs[1][ij & 0xFFFFu]) : 0u;
     };
-    const auto stair_id = [=](int t) {
-        const uint32_t ij = cell_of(t);
-        return ij != 0xFFFFFFFFu ? hi[0][ij >> 16] * (uint32_t)n + hi[1][ij & 0xFFFFu] : 0u;
-    };
-    uint32_t cell[STAIR_SLOTS], key[STAIR_SLOTS];
-#pragma unroll
-    for (int t = 0; t < STAIR_SLOTS; ++t) cell[t] = cell_of(t);
-#pragma unroll
-    for (int t = 0; t < STAIR_SLOTS; ++t)
-        key[t] = cell[t] != 0xFFFFFFFFu ? order_key(hs[0][cell[t] >> 16] + hs[1][cell[t] & 0xFFFFu]) : 0u;
-    uint64_t c = wave_topk(key, stair_key, stair_id, STAIR_SLOTS, k, stage[wv], lane);
+    uint64_t c = wave_topk(key, stair_key, [&](int t) { return id[t]; }, STAIR_SLOTS, k, stage[wv], lane);
 
     // certificate: no cell outside the staircase reaches the k-th score
     const uint32_t vk = read_lane((uint32_t)(c >> 32), k - 1);
@@ -339,8 +377,13 @@ hipError_t launch(const float *scores, int64_t pairs, int n, int k, const uint32
                   float *w, hipStream_t stream)
 {
     const int64_t blocks = (pairs + WAVES - 1) / WAVES;
-    hipLaunchKernelGGL(select_kernel<MH>, dim3((unsigned)blocks), dim3(64 * WAVES), 0, stream, scores, pairs, n, k,
-                       stair, cells, idx, w);
+    const dim3 grid((unsigned)blocks), block(64 * WAVES);
+    if (n % 256 == 0 && n == MH * 64)
+        hipLaunchKernelGGL((select_kernel<MH, true>), grid, block, 0, stream, scores, pairs, n, k, stair, cells, idx,
+                           w);
+    else
+        hipLaunchKernelGGL((select_kernel<MH, false>), grid, block, 0, stream, scores, pairs, n, k, stair, cells, idx,
+                           w);
     return hipGetLastError();
 }
 
