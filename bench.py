@@ -10,6 +10,7 @@ on, the roofline of the dominant kernel and of the value gather, and the fp64
 CPU oracle timed on a bounded sample of the same workload.
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -23,6 +24,29 @@ METRIC = "PKM lookups(tokens)/sec + value-gather HBM GB/s, N=1M, k=32, 4 heads"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 FP32_MFMA_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix
 ELT_BYTES = {"f32": 4, "bf16": 2, "e4m3": 1}
+ROOT = os.path.dirname(os.path.abspath(__file__))
+# Sources of each kernel: measured HBM traffic is only reported while they
+# are unchanged since the counters were taken.
+KERNEL_SOURCES = {"query_gemm": ["gemm_f32.hip"], "score_gemm": ["gemm_f32.hip"],
+                  "select": ["select.hip", "wave_ops.h"], "gather": ["gather.hip"]}
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch from profiles/traffic.json (rocprofv3 FETCH_SIZE
+    and WRITE_SIZE runs, scaled by a plain copy's counts), or None."""
+    try:
+        with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+            rec = json.load(f)
+        entry = rec["kernels"][kernel]
+    except (OSError, ValueError, KeyError):
+        return None
+    if rec.get("workload") != workload:
+        return None
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "product_key_memory_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return entry["bytes"] if h.hexdigest() == entry["source_sha256"] else None
 
 
 def per_token_work(wl):
@@ -171,7 +195,8 @@ def main():
     def roof(name):
         bound, achieved, peak, unit = rl[name]
         return {"kernel": name, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-                "frac": round(achieved / peak, 4), "traffic": None, "avg_ms": round(kt[name], 4)}
+                "frac": round(achieved / peak, 4), "traffic": measured_traffic(wl.name, name),
+                "avg_ms": round(kt[name], 4)}
 
     line = {
         "metric": METRIC,

@@ -92,7 +92,8 @@ class Model:
 
     wq [H,D,D] f32 (row f = output feature f), mean/var/gamma/beta [H,D] f32,
     subkeys [H,2,n,D/2] f32, values [n*n,D] as f32 / uint16 (bf16 bits) /
-    uint8 (E4M3 bits), scale [n*n] f32 for E4M3 tables.
+    uint8 (E4M3 bits), scale [n*n] f32 for E4M3 tables.  values may be None
+    when only the selection (idx, top, w, qhat) is wanted.
     """
 
     def __init__(self, wq, mean, var, gamma, beta, subkeys, values, scale, k, table, eps=1e-5):
@@ -104,18 +105,19 @@ class Model:
         vt = np.dtype({"f32": np.float32, "bf16": np.uint16, "e4m3": np.uint8}[table])
         self._keep = [
             _c(wq, np.float32), _c(mean, np.float32), _c(var, np.float32), _c(gamma, np.float32),
-            _c(beta, np.float32), _c(subkeys, np.float32), _c(values, vt),
+            _c(beta, np.float32), _c(subkeys, np.float32), None if values is None else _c(values, vt),
             None if scale is None else _c(scale, np.float32),
         ]
-        assert self._keep[6].shape == (n * n, D)
-        if table == "e4m3":
+        self.has_values = values is not None
+        assert not self.has_values or self._keep[6].shape == (n * n, D)
+        if table == "e4m3" and self.has_values:
             assert self._keep[7] is not None and self._keep[7].shape == (n * n,)
         k_ = self._keep
         self._s = _Model(D, H, n, int(k), VALUE_TYPES[table], 0, float(eps), *[_ptr(a) for a in k_])
 
     @classmethod
     def from_params(cls, p, k, table, eps=1e-5):
-        return cls(p["wq"], p["mean"], p["var"], p["gamma"], p["beta"], p["subkeys"], p["values"],
+        return cls(p["wq"], p["mean"], p["var"], p["gamma"], p["beta"], p["subkeys"], p.get("values"),
                    p.get("scale"), k, table, eps)
 
 
@@ -131,6 +133,8 @@ def run(model, x, kk=None, want=("out", "idx", "top", "w"), nthreads=None, lib=N
     B = x.shape[0]
     assert x.shape == (B, model.D)
     kk = model.k if kk is None else int(kk)
+    if "out" in want and not model.has_values:
+        raise ValueError("the model holds no value table")
     H, D = model.H, model.D
     shapes = {"out": ((B, D), np.float64), "idx": ((B, H, kk), np.int32), "top": ((B, H, kk), np.float64),
               "w": ((B, H, kk), np.float64), "qhat": ((B, H, D), np.float64), "ncand": ((B, H), np.int32)}
