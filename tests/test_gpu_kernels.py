@@ -165,3 +165,36 @@ def test_query_and_score_parity(torch, name):
             ref = qp @ sub[h, p].T
             m = np.abs(qp) @ np.abs(sub[h, p]).T
             assert (np.abs(scores[:, h, p] - ref) <= 1e-5 * m + 1e-7).all()
+
+
+@pytest.mark.parametrize("name", ["mid", "default", "large_memory"])
+def test_score_error_guard(torch, name):
+    """The index-parity rule needs tau to exceed twice the largest full-score
+    error of the fp32 path (a gap above 2 * (e0 + e1) keeps the winner set).
+    Measured here on the GPU's own projection + scoring of sampled tokens
+    against fp64: for every (token, head), max|ds0| + max|ds1| <= tau / 2."""
+    wl = synthetic.WORKLOADS[name]
+    params = synthetic.make_params(wl, with_values=False)
+    x = synthetic.make_x(wl)[:: max(1, wl.B // 96)][:96].copy()
+    say("score error guard", name, "tokens", x.shape[0])
+    mem = pk.Memory(wl.D, wl.H, wl.n, wl.k, "bf16")
+    # query and score read only Wq, the BN arrays and the subkeys
+    P = pk.Params(*[_to(torch, params[key]) for key in ("wq", "mean", "var", "gamma", "beta", "subkeys")], None)
+    q = mem.query(P, _to(torch, x))
+    s = mem.score(P, q).cpu().numpy().astype(np.float64)
+    r = oracle.run(support.model_for(wl, params), x, kk=wl.k + 1, want=("qhat", "idx", "top"))
+    half = wl.D // 2
+    sub = params["subkeys"].astype(np.float64)
+    worst = 0.0
+    for h in range(wl.H):
+        e = []
+        for p in range(2):
+            ref = r["qhat"][:, h, p * half:(p + 1) * half] @ sub[h, p].T
+            e.append(np.abs(s[:, h, p] - ref).max(axis=1))
+        err_full = e[0] + e[1]
+        for b in range(x.shape[0]):
+            tau = max(support.TAU_ABS, support.TAU_REL * support.key_l1_mass(wl, params, r["qhat"][b, h],
+                                                                           r["idx"][b, h, wl.k - 1], h))
+            worst = max(worst, err_full[b] / tau)
+    print(f"{name}: max over (token, head) of full-score error / tau = {worst:.3f}", flush=True)
+    assert worst <= 0.5
