@@ -22,6 +22,9 @@
 //   against 128x128).
 //   Small grids (fewer tiles than CUs at 256x256): 128x128, 4 waves of
 //   64x64, BK 32, one stage.
+// A result that the next kernel reads once (the subkey scores) is stored
+// non-temporally: it reaches HBM during this compute-bound kernel rather than
+// being written back from the caches while the memory-bound gather runs.
 #include "pkm_internal.h"
 
 namespace pkm {
@@ -92,7 +95,7 @@ __device__ __forceinline__ void mfma_chunk(floatx16 (&acc)[T::TM][T::TN], const 
     }
 }
 
-template <typename T, bool BN_EPILOGUE>
+template <typename T, bool BN_EPILOGUE, bool STREAM_OUT>
 __global__ __launch_bounds__(T::THREADS) void gemm_nt_f32_kernel(GemmArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) float smem[];
@@ -180,7 +183,10 @@ __global__ __launch_bounds__(T::THREADS) void gemm_nt_f32_kernel(GemmArgs a)
                 if (row < a.M) {
                     float c = acc[i][j][v];
                     if (BN_EPILOGUE) c = (c - mean) * mul + beta;
-                    C[(int64_t)row * a.ldc + col] = c;
+                    if (STREAM_OUT)
+                        __builtin_nontemporal_store(c, &C[(int64_t)row * a.ldc + col]);
+                    else
+                        C[(int64_t)row * a.ldc + col] = c;
                 }
             }
         }
@@ -193,30 +199,32 @@ int64_t tile_count(const GemmArgs &a)
     return (int64_t)((a.M + T::BM - 1) / T::BM) * ((a.N + T::BN - 1) / T::BN);
 }
 
-template <typename T>
-hipError_t launch_tile(const GemmArgs &a, hipStream_t stream)
+template <typename T, bool BN_EPILOGUE, bool STREAM_OUT>
+hipError_t launch_variant(const GemmArgs &a, hipStream_t stream)
 {
-    const int64_t tiles = tile_count<T>(a);
-    if (tiles > 0x7FFFFFFF || a.batch > 65535) return hipErrorInvalidConfiguration;
+    const auto kernel = &gemm_nt_f32_kernel<T, BN_EPILOGUE, STREAM_OUT>;
     if (T::LDS_BYTES > 65536) {
         // Dynamic LDS above 64 KiB must be allowed per kernel (gfx950 has
         // 160 KiB per CU); done once per kernel per process.
-        static const hipError_t allowed = [] {
-            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_nt_f32_kernel<T, true>),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)T::LDS_BYTES);
-            if (e == hipSuccess)
-                e = hipFuncSetAttribute(reinterpret_cast<const void *>(&gemm_nt_f32_kernel<T, false>),
-                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)T::LDS_BYTES);
-            return e;
-        }();
+        static const hipError_t allowed = hipFuncSetAttribute(
+            reinterpret_cast<const void *>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize, (int)T::LDS_BYTES);
         if (allowed != hipSuccess) return allowed;
     }
-    const dim3 grid((unsigned)tiles, a.batch);
-    if (a.bn_mean)
-        hipLaunchKernelGGL((gemm_nt_f32_kernel<T, true>), grid, dim3(T::THREADS), T::LDS_BYTES, stream, a);
-    else
-        hipLaunchKernelGGL((gemm_nt_f32_kernel<T, false>), grid, dim3(T::THREADS), T::LDS_BYTES, stream, a);
+    const dim3 grid((unsigned)tile_count<T>(a), a.batch);
+    hipLaunchKernelGGL(kernel, grid, dim3(T::THREADS), T::LDS_BYTES, stream, a);
     return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_tile(const GemmArgs &a, hipStream_t stream)
+{
+    if (tile_count<T>(a) > 0x7FFFFFFF || a.batch > 65535) return hipErrorInvalidConfiguration;
+    if (a.bn_mean) {
+        if (a.stream_out) return launch_variant<T, true, true>(a, stream);
+        return launch_variant<T, true, false>(a, stream);
+    }
+    if (a.stream_out) return launch_variant<T, false, true>(a, stream);
+    return launch_variant<T, false, false>(a, stream);
 }
 
 }  // namespace

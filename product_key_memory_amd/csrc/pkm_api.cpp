@@ -186,6 +186,7 @@ pkm::GemmArgs score_args(const pkm_config &c, const pkm_params *p, int64_t B, co
     a.N = c.n_keys;
     a.K = half;
     a.batch = 2 * c.heads;
+    a.stream_out = true;  // read once, by the select
     return a;
 }
 

@@ -12,6 +12,10 @@ namespace pkm {
 // for g < batch, m < M, n < N; K % 32 == 0.  With bn_* non-null the epilogue
 // applies inference BatchNorm to column n:
 //   (c - mean[n]) / sqrt(var[n] + eps) * gamma[n] + beta[n].
+// stream_out: store C with non-temporal stores (for a result read once by a
+// later kernel: it is written through to HBM while the GEMM is compute-bound
+// instead of staying dirty in the caches and being written back during
+// whatever memory-bound kernel runs next).
 struct GemmArgs {
     const float *A;
     int64_t lda, strideA;
@@ -22,6 +26,7 @@ struct GemmArgs {
     int M, N, K, batch;
     const float *bn_mean, *bn_var, *bn_gamma, *bn_beta;
     float bn_eps;
+    bool stream_out;
 };
 hipError_t launch_gemm_nt_f32(const GemmArgs &a, hipStream_t stream);
 
