@@ -60,6 +60,35 @@ def per_token_work(wl):
     }
 
 
+def stage_bytes(wl):
+    """Algorithmic HBM bytes of each stage for the whole batch: operands read
+    once, results written once."""
+    B, D, H, n, k = wl.B, wl.D, wl.H, wl.n, wl.k
+    work = per_token_work(wl)
+    return {
+        "query_gemm": 4 * (B * D + H * D * D + 4 * H * D + B * H * D),
+        "score_gemm": 4 * (B * H * D + H * n * D + B * H * 2 * n),
+        "select": work["select_bytes"] * B,
+        "gather": work["gather_bytes"] * B + B * H * k * 8 + B * D * 4,
+    }
+
+
+def end_to_end(wl, ms):
+    """Whole-step tokens/s against two bounds: the value gather alone at HBM
+    peak, and the composite roofline sum over stages of max(flop / MFMA peak,
+    bytes / HBM peak)."""
+    work = per_token_work(wl)
+    nbytes = stage_bytes(wl)
+    flops = {"query_gemm": work["query_flop"] * wl.B, "score_gemm": work["score_flop"] * wl.B,
+             "select": 0.0, "gather": 0.0}
+    ideal = sum(max(flops[s] / (FP32_MFMA_PEAK_TFLOPS * 1e12), nbytes[s] / (HBM_PEAK_GBS * 1e9)) for s in flops)
+    hbm_only = work["gather_bytes"] * wl.B / (HBM_PEAK_GBS * 1e9)
+    value = wl.B / (ms * 1e-3)
+    return {"hbm_roofline_tokens_per_s": round(wl.B / hbm_only, 1), "hbm_frac": round(value * hbm_only / wl.B, 4),
+            "composite_roofline_tokens_per_s": round(wl.B / ideal, 1),
+            "composite_frac": round(value * ideal / wl.B, 4), "composite_ideal_us": round(ideal * 1e6, 2)}
+
+
 def timed_steps(torch, fn, steps, warmup):
     """Average ms per call of fn over `steps` calls after `warmup` calls,
     bracketed by device synchronisation, timed with events on the current
@@ -126,9 +155,16 @@ def cpu_baseline(wl, params, x, seconds=10.0):
     t0 = time.perf_counter()
     oracle.run(model, x[:sample], want=("out",), nthreads=cores)
     dt = time.perf_counter() - t0
+    # one core, on a sample a tenth of the time budget long
+    one = max(1, int(sample / dt / cores * seconds / 10))
+    t0 = time.perf_counter()
+    oracle.run(model, x[:one], want=("out",), nthreads=1)
+    dt1 = time.perf_counter() - t0
     return {"value": sample / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"first {sample} of the {wl.B} tokens of the {wl.name} workload, full lookup in fp64, "
-                      f"{dt:.1f} s wall on {cores} threads"}
+                      f"{dt:.1f} s wall on {cores} threads",
+            "single_core_value": one / dt1,
+            "single_core_sample": f"first {one} tokens on 1 thread, {dt1:.1f} s wall"}
 
 
 def main():
@@ -217,6 +253,7 @@ def main():
         "gather_roofline": roof("gather"),
         "gather_uniform_rows_gbs": round(work["gather_bytes"] * B / (g_uniform_ms * 1e-3) / 1e9, 1),
         "gathered_rows_distinct_frac": round(distinct, 4),
+        "end_to_end": end_to_end(wl, ms),
         "kernels_ms": {nm: round(v, 4) for nm, v in kt.items()},
         "kernel_rooflines": {nm: {"achieved": round(rl[nm][1], 2), "unit": rl[nm][3],
                                   "frac": round(rl[nm][1] / rl[nm][2], 4)} for nm in rl},
