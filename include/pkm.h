@@ -155,6 +155,26 @@ pkm_status pkm_select(pkm_ctx *ctx, int64_t B, const float *scores, int32_t *idx
 pkm_status pkm_gather(pkm_ctx *ctx, const pkm_params *p, int64_t B, int32_t rows_per_token, const int32_t *idx,
                       const float *weights, float *out, void *stream);
 
+/* Flat exact search: the brute-force search the product search replaces
+ * ("Product-Key Memory", §Factorising the key space: the product search
+ * returns exactly the k best of all N = n^2 concatenated keys, with 2n
+ * subkey scores instead of N key scores).  For each token b and head h,
+ * every concatenated key key(a, c) = [subkeys[h,0,a,:]; subkeys[h,1,c,:]]
+ * is scored against qhat[b,h,:] with one D-long fp32 dot product (the
+ * product structure is not used), and the k best are written:
+ *   qhat  [B, H, D] fp32 normalised queries (pkm_query's output)
+ *   idx   [B, H, k] int32 flat rows a * n + c, in (score desc, flat index
+ *         asc) order — the order pkm_forward uses
+ *   top   [B, H, k] fp32 the scores of those keys
+ * workspace is caller-owned device memory of at least
+ * pkm_flat_workspace_bytes(cfg, B) bytes (16-byte aligned): it holds the
+ * B * H * n^2 fp32 key scores and the top-k merge buffers, so the call
+ * allocates nothing.  Work: 2 * B * H * n^2 * D flop.  B <= 65536; a
+ * smaller workspace is PKM_E_ARG. */
+pkm_status pkm_flat_workspace_bytes(const pkm_config *cfg, int64_t B, size_t *bytes);
+pkm_status pkm_flat_search(pkm_ctx *ctx, const pkm_params *p, int64_t B, const float *qhat, void *workspace,
+                           size_t workspace_bytes, int32_t *idx, float *top, void *stream);
+
 /* A static description of a status code. */
 const char *pkm_status_str(pkm_status s);
 

@@ -16,7 +16,8 @@ VALUE_TYPES = {"f32": 0, "bf16": 1, "e4m3": 2}
 # Every symbol include/pkm.h declares.
 EXPORTS = (
     "pkm_config_check", "pkm_workspace_bytes", "pkm_create", "pkm_destroy", "pkm_forward", "pkm_query",
-    "pkm_score", "pkm_select", "pkm_gather", "pkm_status_str", "pkm_last_error",
+    "pkm_score", "pkm_select", "pkm_gather", "pkm_flat_workspace_bytes", "pkm_flat_search", "pkm_status_str",
+    "pkm_last_error",
 )
 
 
@@ -62,6 +63,8 @@ def load_library(path=LIB_PATH):
         "pkm_score": (ctypes.c_int, [vp, par_p, i64, vp, vp, vp]),
         "pkm_select": (ctypes.c_int, [vp, i64, vp, vp, vp, vp]),
         "pkm_gather": (ctypes.c_int, [vp, par_p, i64, i32, vp, vp, vp, vp]),
+        "pkm_flat_workspace_bytes": (ctypes.c_int, [cfg_p, i64, ctypes.POINTER(ctypes.c_size_t)]),
+        "pkm_flat_search": (ctypes.c_int, [vp, par_p, i64, vp, vp, ctypes.c_size_t, vp, vp, vp]),
         "pkm_status_str": (ctypes.c_char_p, [ctypes.c_int]),
         "pkm_last_error": (ctypes.c_char_p, []),
     }
@@ -276,3 +279,29 @@ class Memory:
         _check(self.lib.pkm_gather(self._ctx, ctypes.byref(params.struct), B, R, _ptr(idx), _ptr(weights),
                                    _ptr(out), _stream_handle(stream)))
         return out
+
+    def flat_workspace_bytes(self, B):
+        n = ctypes.c_size_t()
+        _check(self.lib.pkm_flat_workspace_bytes(ctypes.byref(self.cfg), int(B), ctypes.byref(n)))
+        return n.value
+
+    def flat_search(self, params, qhat, idx=None, top=None, workspace=None, stream=None):
+        """Brute-force top-k over all n_keys^2 concatenated keys from qhat
+        [B, H, D]: (idx [B, H, k] int32, top [B, H, k] f32).  workspace: a
+        uint8 device tensor of at least flat_workspace_bytes(B) bytes, or
+        None to allocate one."""
+        torch = _torch()
+        B = qhat.shape[0]
+        self.check_params(params, ("subkeys",))
+        _expect(qhat, "qhat", (B, self.heads, self.dim), "float32", params["subkeys"].device)
+        need = self.flat_workspace_bytes(B)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=qhat.device)
+        _expect(workspace, "workspace", (workspace.numel(),), "uint8", qhat.device)
+        idx = self._new((B, self.heads, self.k), torch.int32, qhat) if idx is None else idx
+        top = self._new((B, self.heads, self.k), torch.float32, qhat) if top is None else top
+        _expect(idx, "idx", (B, self.heads, self.k), "int32", qhat.device)
+        _expect(top, "top", (B, self.heads, self.k), "float32", qhat.device)
+        _check(self.lib.pkm_flat_search(self._ctx, ctypes.byref(params.struct), B, _ptr(qhat), _ptr(workspace),
+                                        workspace.numel(), _ptr(idx), _ptr(top), _stream_handle(stream)))
+        return idx, top

@@ -25,6 +25,14 @@
 // A result that the next kernel reads once (the subkey scores) is stored
 // non-temporally: it reaches HBM during this compute-bound kernel rather than
 // being written back from the caches while the memory-bound gather runs.
+//
+// Flat exact search (the comparator for the product search of
+// §Factorising the key space: every one of the n^2 concatenated keys
+// scored by one full-length dot product).  The B operand is the virtual
+// key matrix: row j = (a, c) is [C0[a]; C1[c]], read from the two subkey
+// sets as K advances (a chunk never straddles the halves).  M is a few
+// dozen tokens, so this uses 32 x 256 tiles: 4 waves of 32 x 64, one LDS
+// stage (41 KiB, three workgroups per CU).
 #include "pkm_internal.h"
 
 namespace pkm {
@@ -51,15 +59,29 @@ struct Tile {
 
 using BigTile = Tile<256, 256, 32, 4, 2, 2>;
 using SmallTile = Tile<128, 128, 32, 2, 2, 1>;
+using KeyTile = Tile<32, 256, 32, 1, 4, 1>;
 
-template <typename T>
+// B row pointers of a thread: plain rows, or the two halves of product keys
+// (k < split reads the first half's row at k, else the second's at k - split).
+template <typename T, bool PRODUCT_B>
+struct BRows {
+    const float *p0[T::PB];
+    const float *p1[PRODUCT_B ? T::PB : 1];
+    __device__ __forceinline__ const float *at(int i, int k, int split) const
+    {
+        if constexpr (PRODUCT_B) return k < split ? p0[i] + k : p1[i] + (k - split);
+        return p0[i] + k;
+    }
+};
+
+template <typename T, bool PRODUCT_B>
 __device__ __forceinline__ void load_chunk(fx4 (&ra)[T::PA], fx4 (&rb)[T::PB], const float *const (&ap)[T::PA],
-                                           const float *const (&bp)[T::PB], int kt)
+                                           const BRows<T, PRODUCT_B> &bp, int kt, int split)
 {
 #pragma unroll
     for (int i = 0; i < T::PA; ++i) ra[i] = *reinterpret_cast<const fx4 *>(ap[i] + kt * T::BK);
 #pragma unroll
-    for (int i = 0; i < T::PB; ++i) rb[i] = *reinterpret_cast<const fx4 *>(bp[i] + kt * T::BK);
+    for (int i = 0; i < T::PB; ++i) rb[i] = *reinterpret_cast<const fx4 *>(bp.at(i, kt * T::BK, split));
 }
 
 template <typename T>
@@ -95,7 +117,7 @@ __device__ __forceinline__ void mfma_chunk(floatx16 (&acc)[T::TM][T::TN], const 
     }
 }
 
-template <typename T, bool BN_EPILOGUE, bool STREAM_OUT>
+template <typename T, bool BN_EPILOGUE, bool STREAM_OUT, bool PRODUCT_B = false>
 __global__ __launch_bounds__(T::THREADS) void gemm_nt_f32_kernel(GemmArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) float smem[];
@@ -122,11 +144,20 @@ __global__ __launch_bounds__(T::THREADS) void gemm_nt_f32_kernel(GemmArgs a)
     const int lc4 = tid % T::C4;
     const int lr = tid / T::C4;
     const float *ap[T::PA];
-    const float *bp[T::PB];
+    BRows<T, PRODUCT_B> bp;
 #pragma unroll
     for (int i = 0; i < T::PA; ++i) ap[i] = A + (int64_t)min(m0 + lr + T::RPP * i, a.M - 1) * a.lda + lc4 * 4;
 #pragma unroll
-    for (int i = 0; i < T::PB; ++i) bp[i] = Bmat + (int64_t)min(n0 + lr + T::RPP * i, a.N - 1) * a.ldb + lc4 * 4;
+    for (int i = 0; i < T::PB; ++i) {
+        const int j = min(n0 + lr + T::RPP * i, a.N - 1);
+        if constexpr (PRODUCT_B) {
+            const int ka = j / a.key_n, kc = j - ka * a.key_n;
+            bp.p0[i] = Bmat + (int64_t)ka * a.ldb + lc4 * 4;
+            bp.p1[i] = a.B2 + (int64_t)g * a.strideB + (int64_t)kc * a.ldb + lc4 * 4;
+        } else {
+            bp.p0[i] = Bmat + (int64_t)j * a.ldb + lc4 * 4;
+        }
+    }
     fx4 ra[T::PA], rb[T::PB];
 
     floatx16 acc[T::TM][T::TN];
@@ -141,12 +172,12 @@ __global__ __launch_bounds__(T::THREADS) void gemm_nt_f32_kernel(GemmArgs a)
     const int kk = lane >> 5;  // which k of the MFMA's pair this lane feeds
     const int KT = a.K / T::BK;
 
-    load_chunk<T>(ra, rb, ap, bp, 0);
+    load_chunk<T, PRODUCT_B>(ra, rb, ap, bp, 0, a.split_k);
     store_chunk<T>(ra, rb, As, Bs, lr, lc4);
     __syncthreads();
     for (int kt = 0; kt < KT; ++kt) {
         const int s = T::STAGES == 1 ? 0 : (kt & 1);
-        if (kt + 1 < KT) load_chunk<T>(ra, rb, ap, bp, kt + 1);
+        if (kt + 1 < KT) load_chunk<T, PRODUCT_B>(ra, rb, ap, bp, kt + 1, a.split_k);
         mfma_chunk<T>(acc, As + s * T::BM * T::LDS, Bs + s * T::BN * T::LDS, wm, wn, il, kk);
         if constexpr (T::STAGES == 1) {
             __syncthreads();
@@ -199,10 +230,10 @@ int64_t tile_count(const GemmArgs &a)
     return (int64_t)((a.M + T::BM - 1) / T::BM) * ((a.N + T::BN - 1) / T::BN);
 }
 
-template <typename T, bool BN_EPILOGUE, bool STREAM_OUT>
+template <typename T, bool BN_EPILOGUE, bool STREAM_OUT, bool PRODUCT_B = false>
 hipError_t launch_variant(const GemmArgs &a, hipStream_t stream)
 {
-    const auto kernel = &gemm_nt_f32_kernel<T, BN_EPILOGUE, STREAM_OUT>;
+    const auto kernel = &gemm_nt_f32_kernel<T, BN_EPILOGUE, STREAM_OUT, PRODUCT_B>;
     if (T::LDS_BYTES > 65536) {
         // Dynamic LDS above 64 KiB must be allowed per kernel (gfx950 has
         // 160 KiB per CU); done once per kernel per process.
@@ -235,6 +266,16 @@ hipError_t launch_gemm_nt_f32(const GemmArgs &a, hipStream_t stream)
     if (a.K % 32 != 0) return hipErrorInvalidValue;
     if (tile_count<BigTile>(a) * a.batch >= kCUs) return launch_tile<BigTile>(a, stream);
     return launch_tile<SmallTile>(a, stream);
+}
+
+hipError_t launch_gemm_nt_f32_product(const GemmArgs &a, hipStream_t stream)
+{
+    if (a.M <= 0 || a.N <= 0 || a.batch <= 0) return hipSuccess;
+    if (a.K % 32 != 0 || a.split_k % 32 != 0 || a.split_k <= 0 || a.split_k >= a.K || !a.B2 || a.key_n <= 0 ||
+        (int64_t)a.key_n * a.key_n < a.N || a.bn_mean)
+        return hipErrorInvalidValue;
+    if (tile_count<KeyTile>(a) > 0x7FFFFFFF || a.batch > 65535) return hipErrorInvalidConfiguration;
+    return launch_variant<KeyTile, false, false, true>(a, stream);
 }
 
 }  // namespace pkm

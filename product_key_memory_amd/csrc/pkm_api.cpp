@@ -216,6 +216,44 @@ pkm_status run_score(const pkm_config &c, const pkm_params *p, int64_t B, const 
     return PKM_OK;
 }
 
+// Flat search workspace for B tokens: key scores [B, H, n^2] fp32 and the two
+// top-k merge buffers of packed keys; false if B is out of range.
+constexpr int64_t kFlatMaxBatch = 65536;
+bool flat_layout(const pkm_config &c, int64_t B, size_t sizes[3])
+{
+    if (B < 0 || B > kFlatMaxBatch) return false;
+    const int64_t rows = B * c.heads, N = (int64_t)c.n_keys * c.n_keys;
+    const int64_t keys = pkm::flat_topk_keys_per_row(N, c.k);
+    if ((double)rows * (double)N * 4.0 > 1.0e15) return false;
+    sizes[0] = round_up((size_t)(rows * N) * sizeof(float));
+    sizes[1] = round_up((size_t)(rows * keys) * sizeof(uint64_t));
+    sizes[2] = round_up((size_t)(rows * ((keys + 2047) / 2048) * c.k) * sizeof(uint64_t));
+    return true;
+}
+
+pkm::GemmArgs flat_args(const pkm_config &c, const pkm_params *p, int64_t B, const float *qhat, float *scores)
+{
+    const int half = c.dim / 2;
+    pkm::GemmArgs a{};
+    a.A = qhat;  // head h starts at column h * D
+    a.lda = (int64_t)c.heads * c.dim;
+    a.strideA = c.dim;
+    a.B = p->subkeys;                               // first halves: [h][0][a][:]
+    a.B2 = p->subkeys + (int64_t)c.n_keys * half;   // second halves: [h][1][c][:]
+    a.ldb = half;
+    a.strideB = (int64_t)c.n_keys * c.dim;          // one head's two subkey sets
+    a.split_k = half;
+    a.key_n = c.n_keys;
+    a.C = scores;  // [B][H][n^2]
+    a.ldc = (int64_t)c.heads * c.n_keys * c.n_keys;
+    a.strideC = (int64_t)c.n_keys * c.n_keys;
+    a.M = (int)B;
+    a.N = c.n_keys * c.n_keys;
+    a.K = c.dim;
+    a.batch = c.heads;
+    return a;
+}
+
 }  // namespace
 
 extern "C" {
@@ -372,6 +410,46 @@ pkm_status pkm_gather(pkm_ctx *ctx, const pkm_params *p, int64_t B, int32_t rows
                                          rows_per_token, idx,
                                          weights, out, static_cast<hipStream_t>(stream)),
                       "gather")))
+        return s;
+    return ok();
+}
+
+pkm_status pkm_flat_workspace_bytes(const pkm_config *cfg, int64_t B, size_t *bytes)
+{
+    if (pkm_status s = check_config(cfg)) return s;
+    if (!bytes) return fail(PKM_E_ARG, "bytes is NULL");
+    size_t sizes[3];
+    if (!flat_layout(*cfg, B, sizes)) return fail(PKM_E_ARG, "flat search B must be in [0, %lld]", (long long)kFlatMaxBatch);
+    *bytes = sizes[0] + sizes[1] + sizes[2];
+    return ok();
+}
+
+pkm_status pkm_flat_search(pkm_ctx *ctx, const pkm_params *p, int64_t B, const float *qhat, void *workspace,
+                           size_t workspace_bytes, int32_t *idx, float *top, void *stream)
+{
+    pkm_status s;
+    if ((s = check_ctx(ctx))) return s;
+    const pkm_config &c = ctx->cfg;
+    size_t sizes[3];
+    if (!flat_layout(c, B, sizes)) return fail(PKM_E_ARG, "flat search B must be in [0, %lld]", (long long)kFlatMaxBatch);
+    if (B == 0) return ok();
+    if (!p) return fail(PKM_E_ARG, "params is NULL");
+    if ((s = need(p->subkeys, "subkeys")) || (s = need(qhat, "qhat")) || (s = need(workspace, "workspace")) ||
+        (s = need(idx, "idx")) || (s = need(top, "top")))
+        return s;
+    if (workspace_bytes < sizes[0] + sizes[1] + sizes[2])
+        return fail(PKM_E_ARG, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes,
+                    sizes[0] + sizes[1] + sizes[2]);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char *w = static_cast<char *>(workspace);
+    float *scores = reinterpret_cast<float *>(w);
+    uint64_t *buf0 = reinterpret_cast<uint64_t *>(w + sizes[0]);
+    uint64_t *buf1 = reinterpret_cast<uint64_t *>(w + sizes[0] + sizes[1]);
+    if ((s = launched(pkm::launch_gemm_nt_f32_product(flat_args(c, p, B, qhat, scores), st), "flat key scoring")))
+        return s;
+    if ((s = launched(pkm::launch_flat_topk(scores, B * c.heads, (int64_t)c.n_keys * c.n_keys, c.k, buf0, buf1, idx,
+                                            top, st),
+                      "flat top-k")))
         return s;
     return ok();
 }

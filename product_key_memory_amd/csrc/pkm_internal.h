@@ -27,8 +27,16 @@ struct GemmArgs {
     const float *bn_mean, *bn_var, *bn_gamma, *bn_beta;
     float bn_eps;
     bool stream_out;
+    // Product-key B operand (B2 non-null): row j of B is the concatenation
+    // [B[j / key_n][0, split_k), B2[j % key_n][0, K - split_k)], both with
+    // row stride ldb and batch stride strideB; split_k % 32 == 0.
+    const float *B2;
+    int split_k, key_n;
 };
 hipError_t launch_gemm_nt_f32(const GemmArgs &a, hipStream_t stream);
+// The same contraction with a product-key B operand and a 32 x 256 tile
+// suited to a few dozen rows of A (the flat exact search over all keys).
+hipError_t launch_gemm_nt_f32_product(const GemmArgs &a, hipStream_t stream);
 
 // Per (token, head): exact top-k of each half's n scores, the exact top-k of
 // the k*k candidates and the softmax.  scores [B][H][2][n] -> idx, w
@@ -47,6 +55,14 @@ void staircase_table(int k, uint32_t *out);
 // out[b][:] = sum_r w[b][r] * scale[row] * values[row][:], row = idx[b][r],
 // r < R, N table rows (rows are clamped into [0, N)).  value_type: 0 f32,
 // 1 bf16, 2 E4M3 (+ row scale).
+// Exact top-k (k <= 64, k <= len) of each of `rows` rows of `len` fp32
+// scores, by (score desc, index asc): idx [rows][k] int32 and top [rows][k].
+// buf0 holds rows * flat_topk_keys_per_row(len, k) packed keys, buf1 rows *
+// ceil(flat_topk_keys_per_row(len, k) / 2048) * k.
+int64_t flat_topk_keys_per_row(int64_t len, int k);
+hipError_t launch_flat_topk(const float *scores, int64_t rows, int64_t len, int k, uint64_t *buf0, uint64_t *buf1,
+                            int32_t *idx, float *top, hipStream_t stream);
+
 hipError_t launch_gather(const void *values, const float *scale, int value_type, int D, int N, int64_t B, int R,
                          const int32_t *idx, const float *w, float *out, hipStream_t stream);
 

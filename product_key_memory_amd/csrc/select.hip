@@ -372,6 +372,102 @@ __global__ __launch_bounds__(64 * WAVES) void select_kernel(const float *__restr
     }
 }
 
+// Flat exact search: top-k over rows of up to n^2 scores, in passes.  Pass 1
+// reads scores: one wave per (row, segment of 4096), the segment's k best
+// as packed keys (0 where a short segment has fewer than k elements).
+// Later passes read those packed keys, 2048 per wave.  Packed keys are
+// unique, so the k best of a row are among the k best of its segments; the
+// pass with one segment per row writes the flat indices and scores.
+constexpr int kFlatScoreSeg = 4096;
+constexpr int kFlatKeySeg = 2048;
+
+template <bool FROM_SCORES, bool VEC4>
+__global__ __launch_bounds__(64 * WAVES) void flat_topk_kernel(const void *__restrict__ in, int64_t rows, int64_t len,
+                                                               int segs, int k, uint64_t *__restrict__ out_keys,
+                                                               int32_t *__restrict__ idx_out,
+                                                               float *__restrict__ top_out)
+{
+    constexpr int SEG = FROM_SCORES ? kFlatScoreSeg : kFlatKeySeg;
+    constexpr int MH = SEG / 64;
+    __shared__ Stage stage[WAVES];
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    const int64_t item = (int64_t)blockIdx.x * WAVES + wv;  // row * segs + segment
+    if (item >= rows * segs) return;
+    const int64_t row = item / segs;
+    const int seg = (int)(item - row * segs);
+    const int64_t base = (int64_t)seg * SEG;
+    const int m = (int)min((int64_t)SEG, len - base);  // elements in this segment, >= 1
+
+    uint64_t c;
+    if constexpr (FROM_SCORES) {
+        const float *seg_row = static_cast<const float *>(in) + row * len + base;
+        uint32_t key[MH];
+        load_keys<MH, VEC4>(seg_row, m, lane, key);
+        const auto id_of = [=](int t) { return (uint32_t)(base + slot_element<VEC4>(t, lane)); };
+        const auto reread = [=](int t) {
+            const int e = slot_element<VEC4>(t, lane);
+            return e < m ? order_key(seg_row[e]) : 0u;
+        };
+        c = wave_topk(key, reread, id_of, VEC4 ? MH : (m + 63) >> 6, k, stage[wv], lane);
+    } else {
+        const uint64_t *seg_row = static_cast<const uint64_t *>(in) + row * len + base;
+        uint64_t v[MH];
+#pragma unroll
+        for (int t = 0; t < MH; ++t) v[t] = seg_row[min(t * 64 + lane, m - 1)];
+        uint32_t key[MH], id[MH];
+#pragma unroll
+        for (int t = 0; t < MH; ++t) {
+            const bool ok = t * 64 + lane < m;
+            key[t] = ok ? (uint32_t)(v[t] >> 32) : 0u;
+            id[t] = ok ? unpack_id(v[t]) : 0xFFFFFFFFu;
+        }
+        const auto reread = [=](int t) {
+            const int e = t * 64 + lane;
+            return e < m ? (uint32_t)(seg_row[e] >> 32) : 0u;
+        };
+        const auto id_again = [=](int t) {
+            const int e = t * 64 + lane;
+            return e < m ? unpack_id(seg_row[e]) : 0xFFFFFFFFu;
+        };
+        // registers for the common path, re-reads for the heavy-tie path
+        uint32_t lane_max = 0;
+#pragma unroll
+        for (int t = 0; t < MH; ++t) lane_max = key[t] > lane_max ? key[t] : lane_max;
+        uint32_t kth = read_lane(sort64_desc(lane_max), k - 1);
+        uint32_t last = 0xFFFFFFFFu;
+        int count = 0;
+#pragma unroll
+        for (int t = 0; t < MH; ++t) append(kept(key[t], id[t], kth, last), key[t], id[t], count, stage[wv], lane);
+        if (count > kSlots) {
+            exact_cut(reread, id_again, (m + 63) >> 6, k, kth, last);
+            count = compact_rolled(reread, id_again, (m + 63) >> 6, kth, last, stage[wv], lane);
+        }
+        c = sorted_survivors(count, stage[wv], lane);
+    }
+    if (lane < k) {
+        if (out_keys) {
+            out_keys[item * k + lane] = (c >> 32) != 0u ? c : 0ull;
+        } else {
+            idx_out[row * k + lane] = (int32_t)unpack_id(c);
+            top_out[row * k + lane] = key_score((uint32_t)(c >> 32));
+        }
+    }
+}
+
+template <bool FROM_SCORES, bool VEC4>
+hipError_t launch_flat_pass(const void *in, int64_t rows, int64_t len, int k, uint64_t *out_keys, int32_t *idx,
+                            float *top, hipStream_t stream)
+{
+    const int seg = FROM_SCORES ? kFlatScoreSeg : kFlatKeySeg;
+    const int64_t segs = (len + seg - 1) / seg;
+    const int64_t blocks = (rows * segs + WAVES - 1) / WAVES;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((flat_topk_kernel<FROM_SCORES, VEC4>), dim3((unsigned)blocks), dim3(64 * WAVES), 0, stream, in,
+                       rows, len, (int)segs, k, out_keys, idx, top);
+    return hipGetLastError();
+}
+
 template <int MH>
 hipError_t launch(const float *scores, int64_t pairs, int n, int k, const uint32_t *stair, int cells, int32_t *idx,
                   float *w, hipStream_t stream)
@@ -388,6 +484,35 @@ hipError_t launch(const float *scores, int64_t pairs, int n, int k, const uint32
 }
 
 }  // namespace
+
+int64_t flat_topk_keys_per_row(int64_t len, int k)
+{
+    return (len + kFlatScoreSeg - 1) / kFlatScoreSeg * k;
+}
+
+hipError_t launch_flat_topk(const float *scores, int64_t rows, int64_t len, int k, uint64_t *buf0, uint64_t *buf1,
+                            int32_t *idx, float *top, hipStream_t stream)
+{
+    if (rows <= 0) return hipSuccess;
+    if (k < 1 || k > 64 || len < k) return hipErrorInvalidValue;
+    const bool vec4 = len % 4 == 0;
+    if (len <= kFlatScoreSeg)
+        return vec4 ? launch_flat_pass<true, true>(scores, rows, len, k, nullptr, idx, top, stream)
+                    : launch_flat_pass<true, false>(scores, rows, len, k, nullptr, idx, top, stream);
+    hipError_t e = vec4 ? launch_flat_pass<true, true>(scores, rows, len, k, buf0, nullptr, nullptr, stream)
+                        : launch_flat_pass<true, false>(scores, rows, len, k, buf0, nullptr, nullptr, stream);
+    int64_t klen = flat_topk_keys_per_row(len, k);
+    uint64_t *src = buf0, *dst = buf1;
+    while (e == hipSuccess) {
+        if (klen <= kFlatKeySeg) return launch_flat_pass<false, false>(src, rows, klen, k, nullptr, idx, top, stream);
+        e = launch_flat_pass<false, false>(src, rows, klen, k, dst, nullptr, nullptr, stream);
+        klen = (klen + kFlatKeySeg - 1) / kFlatKeySeg * k;
+        uint64_t *t = src;
+        src = dst;
+        dst = t;
+    }
+    return e;
+}
 
 int staircase_cells(int k)
 {

@@ -86,6 +86,28 @@ def test_workspace_bytes():
         pk.workspace_bytes(pk.make_config(**{**GOOD, "k": 0}))
 
 
+def test_flat_workspace_bytes():
+    """Key scores [B, H, n^2] fp32, then the merge buffers: ceil(n^2 / 4096) * k
+    packed keys per row and ceil(that / 2048) * k, each rounded to 256 bytes."""
+    lib = pk.load_library()
+    cfg = pk.make_config(**GOOD)
+    H, n, k = 4, 1024, 32
+
+    def rnd(x):
+        return (x + 255) // 256 * 256
+
+    for B in (1, 16, 100):
+        rows = B * H
+        keys = (n * n + 4095) // 4096 * k
+        want = rnd(rows * n * n * 4) + rnd(rows * keys * 8) + rnd(rows * ((keys + 2047) // 2048) * k * 8)
+        got = ctypes.c_size_t()
+        assert lib.pkm_flat_workspace_bytes(ctypes.byref(cfg), B, ctypes.byref(got)) == pk.PKM_OK
+        assert got.value == want
+    got = ctypes.c_size_t()
+    assert lib.pkm_flat_workspace_bytes(ctypes.byref(cfg), 65537, ctypes.byref(got)) == pk.PKM_E_ARG
+    assert lib.pkm_flat_workspace_bytes(ctypes.byref(cfg), -1, ctypes.byref(got)) == pk.PKM_E_ARG
+
+
 def test_null_arguments_rejected_before_any_launch():
     lib = pk.load_library()
     null = ctypes.c_void_p()
@@ -95,6 +117,7 @@ def test_null_arguments_rejected_before_any_launch():
     assert lib.pkm_score(null, ctypes.byref(params), 1, null, null, null) == pk.PKM_E_ARG
     assert lib.pkm_select(null, 1, null, null, null, null) == pk.PKM_E_ARG
     assert lib.pkm_gather(null, ctypes.byref(params), 1, 1, null, null, null, null) == pk.PKM_E_ARG
+    assert lib.pkm_flat_search(null, ctypes.byref(params), 1, null, null, 0, null, null, null) == pk.PKM_E_ARG
     assert lib.pkm_create(None, ctypes.byref(ctypes.c_void_p())) == pk.PKM_E_ARG
     assert lib.pkm_create(ctypes.byref(pk.make_config(**GOOD)), None) == pk.PKM_E_ARG
     assert "NULL" in pk.last_error()
