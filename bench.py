@@ -141,6 +141,34 @@ def gather_uniform_ms(torch, mem, P, wl, steps, warmup):
     return timed_steps(torch, lambda: mem.gather(P, idx, w, out), steps, warmup)
 
 
+def flat_vs_product(torch, pk, wl, P, xt, kt, tokens=64, steps=5, warmup=2):
+    """The comparison the product keys exist for, measured: the brute-force
+    search (every one of the N concatenated keys scored by a D-long dot
+    product, exact top-k) against the product search (2 n half-key scores,
+    per-half top-k, k^2 candidates), both from the same q^ of `tokens` tokens."""
+    mem = pk.Memory(wl.D, wl.H, wl.n, wl.k, wl.table, max_batch=tokens)
+    q = mem.query(P, xt[:tokens].contiguous())
+    ws = torch.empty(mem.flat_workspace_bytes(tokens), dtype=torch.uint8, device="cuda")
+    fidx = torch.empty((tokens, wl.H, wl.k), dtype=torch.int32, device="cuda")
+    ftop = torch.empty((tokens, wl.H, wl.k), dtype=torch.float32, device="cuda")
+    s = torch.empty((tokens, wl.H, 2, wl.n), dtype=torch.float32, device="cuda")
+    pidx = torch.empty_like(fidx)
+    pw = torch.empty_like(ftop)
+    flat_ms = timed_steps(torch, lambda: mem.flat_search(P, q, fidx, ftop, ws), steps, warmup)
+    prod_ms = timed_steps(torch, lambda: (mem.score(P, q, s), mem.select(s, pidx, pw)), 50, 10)
+    same = bool((torch.sort(fidx, -1).values == torch.sort(pidx, -1).values).all().item())
+    flat_flop = 2.0 * tokens * wl.H * wl.N * wl.D
+    full_batch_us = (kt["score_gemm"] + kt["select"]) * 1e3 / wl.B
+    return {"tokens": tokens, "flat_ms": round(flat_ms, 4), "product_ms": round(prod_ms, 4),
+            "speedup_same_tokens": round(flat_ms / prod_ms, 1),
+            "flat_us_per_token": round(flat_ms * 1e3 / tokens, 3),
+            "product_us_per_token_full_batch": round(full_batch_us, 5),
+            "speedup_per_token": round(flat_ms * 1e3 / tokens / full_batch_us, 1),
+            "flat_gemm_tflops": round(flat_flop / (flat_ms * 1e-3) / 1e12, 2),
+            "same_winner_sets": same,
+            "key_scores_per_token_head": {"flat": wl.N, "product": 2 * wl.n}, "candidates_per_token_head": wl.k ** 2}
+
+
 def cpu_baseline(wl, params, x, seconds=10.0):
     """The fp64 oracle on host cores over a bounded sample of the tokens."""
     import oracle
@@ -176,6 +204,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target wall time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--max-batch", type=int, default=0, help="tokens per internal chunk (0: the whole batch)")
+    ap.add_argument("--no-flat", action="store_true", help="skip the flat (brute-force) search comparison")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -258,6 +287,8 @@ def main():
         "kernel_rooflines": {nm: {"achieved": round(rl[nm][1], 2), "unit": rl[nm][3],
                                   "frac": round(rl[nm][1] / rl[nm][2], 4)} for nm in rl},
     }
+    if not args.no_flat:
+        line["flat_vs_product"] = flat_vs_product(torch, pk, wl, P, xt, kt)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, params, x, args.cpu_seconds)
     print(json.dumps(line), flush=True)
