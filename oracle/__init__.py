@@ -1,8 +1,9 @@
-"""fp64 CPU oracle for the product-key memory lookup forward pass.
+"""fp64 CPU oracle for the product-key memory lookup: the forward pass and its
+gradients.
 
 TEST INFRASTRUCTURE ONLY: imported by the test suite, the smoke check and the
 CPU-baseline leg of the benchmark, never by the product path.  It shares no
 code with the HIP library.
 """
 from .oracle import (Model, run, bf16_to_f64, e4m3_to_f64, build, lib_path, load_library,  # noqa: F401
-                     compile_source, select, gather)
+                     compile_source, select, gather, backward, GRADS)

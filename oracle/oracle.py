@@ -59,6 +59,8 @@ def load_library(path):
     lib.pkmo_select.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int] + [ctypes.c_void_p] * 4
     lib.pkmo_gather.restype = ctypes.c_int
     lib.pkmo_gather.argtypes = [ctypes.POINTER(_Model), ctypes.c_int64, ctypes.c_int] + [ctypes.c_void_p] * 3
+    lib.pkmo_backward.restype = ctypes.c_int
+    lib.pkmo_backward.argtypes = [ctypes.POINTER(_Model), ctypes.c_int64] + [ctypes.c_void_p] * 8 + [ctypes.c_int]
     return lib
 
 
@@ -186,3 +188,31 @@ def gather(model, rows, w, lib=None):
     if lib.pkmo_gather(ctypes.byref(model._s), B, R, _ptr(rows), _ptr(w), _ptr(out)) != 0:
         raise ValueError("oracle rejected its arguments")
     return out
+
+
+GRADS = ("dx", "dwq", "dgamma", "dbeta", "dsub", "dval")
+
+
+def backward(model, x, dout, want=GRADS, nthreads=None, lib=None):
+    """Gradients of sum(dout * out) for x [B,D] (f32) and dout [B,D] (f32):
+    dx [B,D], dwq [H,D,D], dgamma / dbeta [H,D], dsub [H,2,n,D/2] and dval
+    [n*n,D] (w.r.t. the dequantised value rows), all fp64, the requested
+    ones only.  The model must hold its value table."""
+    lib = lib or _load()
+    if not model.has_values:
+        raise ValueError("the backward reads the value table")
+    x = _c(x, np.float32)
+    dout = _c(dout, np.float32)
+    B = x.shape[0]
+    assert x.shape == (B, model.D) and dout.shape == (B, model.D)
+    H, D, n = model.H, model.D, model.n
+    shapes = {"dx": (B, D), "dwq": (H, D, D), "dgamma": (H, D), "dbeta": (H, D), "dsub": (H, 2, n, D // 2),
+              "dval": (n * n, D)}
+    res = {name: np.empty(shapes[name]) for name in want}
+    if nthreads is None:
+        nthreads = len(os.sched_getaffinity(0))
+    rc = lib.pkmo_backward(ctypes.byref(model._s), B, _ptr(x), _ptr(dout), *[_ptr(res.get(nm)) for nm in GRADS],
+                           int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments" if rc == -1 else "oracle ran out of memory")
+    return res

@@ -42,6 +42,9 @@
  *     wins in the candidate grid;
  *   - non-finite inputs are undefined (never generated).
  *
+ * The backward direction (gradients of a loss through steps 7 -> 1 for
+ * the winners the forward selected) is at the end of the file.
+ *
  * Every floating-point step is fp64; a product of two fp32 inputs is exact
  * in fp64.  Tokens are independent (running-statistics BN), so tokens may be
  * spread over threads; each token's arithmetic is the same plain loop
@@ -369,5 +372,248 @@ int pkmo_gather(const pkmo_model *M, int64_t B, int R, const int32_t *rows, cons
             out[b * M->D + d] = 0.0;
         pkmo_gather_add(M, R, rows + b * R, w + b * R, out + b * M->D);
     }
+    return 0;
+}
+
+/* ---------------------------------------------------------------- backward */
+
+/*
+ * Gradients of L = sum_b dout_b . out_b through steps 7 -> 1.  The top-k
+ * selections are piecewise constant in their inputs, so only the winning
+ * scores receive gradient (the code listing's topk values feed the softmax;
+ * its indices only select).  For token b, head h, winners j < k with flat
+ * rows r_j = i0_j * n + i1_j and weights w_j:
+ *   g_j     = dout_b . V[r_j]                         (step 7, d/dw_j)
+ *   dt_j    = w_j (g_j - sum_l w_l g_l)               (step 6, softmax)
+ *   ds_0[i0_j] += dt_j ;  ds_1[i1_j] += dt_j          (step 5: t_j = s_0 + s_1)
+ *   dq^_p   = sum_i ds_p[i] C[h,p,i] ;  dC[h,p,i] += ds_p[i] q^_p   (step 3)
+ *   xhat    = (q - mean) / sqrt(var + eps)
+ *   dgamma += dq^ * xhat ;  dbeta += dq^ ;  dq = dq^ * gamma / sqrt(var + eps)
+ *                                                     (step 2, running statistics)
+ *   dWq[h] += dq x_b^T ;  dx_b += Wq[h]^T dq           (step 1)
+ *   dV[r_j] += w_j dout_b                             (step 7, d/dV of the
+ *                                                      dequantised rows)
+ * Per-token quantities are computed in parallel over tokens; every
+ * parameter gradient element is then summed over tokens in token order by
+ * the one thread that owns it, so the result does not depend on the thread
+ * count.
+ */
+
+typedef struct {
+    const pkmo_model *M;
+    const float *x, *dout;
+    double *dx;
+    /* per (token, head): */
+    double *qhat, *xhat, *dqhat; /* [B][H][D] */
+    double *dt, *w;              /* [B][H][k] */
+    int32_t *rows;               /* [B][H][k] */
+    int64_t b0, b1;
+} bwd_job;
+
+static void *backward_tokens(void *arg)
+{
+    bwd_job *J = (bwd_job *)arg;
+    const pkmo_model *M = J->M;
+    const int D = M->D, H = M->H, n = M->n, k = M->k, half = D / 2;
+    double *s = (double *)malloc(sizeof(double) * 2 * (size_t)n);
+    double *t0 = (double *)malloc(sizeof(double) * (size_t)k);
+    double *t1 = (double *)malloc(sizeof(double) * (size_t)k);
+    int32_t *i0 = (int32_t *)malloc(sizeof(int32_t) * (size_t)k);
+    int32_t *i1 = (int32_t *)malloc(sizeof(int32_t) * (size_t)k);
+    double *top = (double *)malloc(sizeof(double) * (size_t)k);
+    double *g = (double *)malloc(sizeof(double) * (size_t)k);
+    double *dq = (double *)malloc(sizeof(double) * (size_t)D);
+    for (int64_t b = J->b0; b < J->b1; ++b) {
+        const float *xb = J->x + b * D, *gb = J->dout + b * D;
+        if (J->dx)
+            for (int d = 0; d < D; ++d)
+                J->dx[b * D + d] = 0.0;
+        for (int h = 0; h < H; ++h) {
+            const int64_t bh = b * H + h;
+            double *qh = J->qhat + bh * D, *xh = J->xhat + bh * D, *dqh = J->dqhat + bh * D;
+            double *dtj = J->dt + bh * k, *wj = J->w + bh * k;
+            int32_t *rj = J->rows + bh * k;
+            /* forward again: steps 1-6 */
+            pkmo_project_bn(M, h, xb, qh);
+            pkmo_half_scores(M, h, qh, s);
+            pkmo_topk_sorted(n, s, k, t0, i0);
+            pkmo_topk_sorted(n, s + n, k, t1, i1);
+            pkmo_candidates_topk(n, k, t0, i0, t1, i1, k, top, rj);
+            pkmo_softmax(k, top, wj);
+            /* step 7 and the softmax, backwards */
+            double wg = 0.0;
+            for (int j = 0; j < k; ++j) {
+                double acc = 0.0;
+                for (int d = 0; d < D; ++d)
+                    acc += (double)gb[d] * value_at(M, rj[j], d);
+                g[j] = acc;
+                wg += wj[j] * acc;
+            }
+            for (int j = 0; j < k; ++j)
+                dtj[j] = wj[j] * (g[j] - wg);
+            /* step 5 then 3: dq^_p = sum_j dt_j C[h,p,i_p(j)] */
+            for (int d = 0; d < D; ++d)
+                dqh[d] = 0.0;
+            for (int j = 0; j < k; ++j) {
+                const int a = rj[j] / n, c = rj[j] % n;
+                const float *c0 = M->subkeys + (((int64_t)h * 2 + 0) * n + a) * half;
+                const float *c1 = M->subkeys + (((int64_t)h * 2 + 1) * n + c) * half;
+                for (int d = 0; d < half; ++d) {
+                    dqh[d] += dtj[j] * (double)c0[d];
+                    dqh[half + d] += dtj[j] * (double)c1[d];
+                }
+            }
+            /* step 2 backwards (running statistics) and step 1's dx */
+            for (int f = 0; f < D; ++f) {
+                const int64_t pf = (int64_t)h * D + f;
+                const double inv = 1.0 / sqrt(M->eps + (double)M->var[pf]);
+                double q = 0.0;
+                const float *wrow = M->wq + pf * D;
+                for (int d = 0; d < D; ++d)
+                    q += (double)wrow[d] * (double)xb[d];
+                const double mu = M->mean[pf];
+                xh[f] = inv * (q - mu);
+                dq[f] = dqh[f] * (double)M->gamma[pf] * inv;
+            }
+            if (J->dx)
+                for (int f = 0; f < D; ++f) {
+                    const float *wrow = M->wq + ((int64_t)h * D + f) * D;
+                    for (int d = 0; d < D; ++d)
+                        J->dx[b * D + d] += dq[f] * (double)wrow[d];
+                }
+        }
+    }
+    free(s); free(t0); free(t1); free(i0); free(i1); free(top); free(g); free(dq);
+    return NULL;
+}
+
+typedef struct {
+    const pkmo_model *M;
+    int64_t B;
+    const float *x, *dout;
+    const double *qhat, *xhat, *dqhat, *dt, *w;
+    const int32_t *rows;
+    double *dwq, *dgamma, *dbeta, *dsub, *dval;
+    int t, nthreads; /* thread t owns the t-th of nthreads equal ranges of the
+                        features [H*D], the subkey rows [H*2*n] and the value
+                        rows [n*n] */
+} own_job;
+
+static void *owner_sums(void *arg)
+{
+    own_job *J = (own_job *)arg;
+    const pkmo_model *M = J->M;
+    const int D = M->D, H = M->H, n = M->n, k = M->k, half = D / 2;
+    const int64_t B = J->B, N = (int64_t)n * n;
+    const int64_t HD = (int64_t)H * D, HS = (int64_t)H * 2 * n;
+    const int64_t f0 = HD * J->t / J->nthreads, f1 = HD * (J->t + 1) / J->nthreads;
+    const int64_t s0 = HS * J->t / J->nthreads, s1 = HS * (J->t + 1) / J->nthreads;
+    const int64_t r0 = N * J->t / J->nthreads, r1 = N * (J->t + 1) / J->nthreads;
+    /* features (h, f) in [f0, f1): dWq rows, dgamma, dbeta */
+    for (int64_t pf = f0; pf < f1; ++pf) {
+        const int h = (int)(pf / D);
+        const double scale = (double)M->gamma[pf] / sqrt(M->eps + (double)M->var[pf]);
+        if (J->dwq)
+            for (int d = 0; d < D; ++d)
+                J->dwq[pf * D + d] = 0.0;
+        if (J->dgamma) J->dgamma[pf] = 0.0;
+        if (J->dbeta) J->dbeta[pf] = 0.0;
+        for (int64_t b = 0; b < B; ++b) {
+            const int64_t at = (b * H + h) * D + (pf - (int64_t)h * D);
+            const double dqh = J->dqhat[at];
+            if (J->dgamma) J->dgamma[pf] += dqh * J->xhat[at];
+            if (J->dbeta) J->dbeta[pf] += dqh;
+            if (J->dwq) {
+                const double dq = dqh * scale;
+                const float *xb = J->x + b * D;
+                for (int d = 0; d < D; ++d)
+                    J->dwq[pf * D + d] += dq * (double)xb[d];
+            }
+        }
+    }
+    /* subkey rows (h, p, i) in [s0, s1) */
+    if (J->dsub)
+        for (int64_t sr = s0; sr < s1; ++sr) {
+            const int h = (int)(sr / (2 * n)), p = (int)((sr / n) % 2), i = (int)(sr % n);
+            double *out = J->dsub + sr * half;
+            for (int d = 0; d < half; ++d)
+                out[d] = 0.0;
+            for (int64_t b = 0; b < B; ++b) {
+                const int64_t bh = b * H + h;
+                for (int j = 0; j < k; ++j) {
+                    const int32_t r = J->rows[bh * k + j];
+                    if ((p == 0 ? r / n : r % n) != i) continue;
+                    const double *qp = J->qhat + bh * D + p * half;
+                    for (int d = 0; d < half; ++d)
+                        out[d] += J->dt[bh * k + j] * qp[d];
+                }
+            }
+        }
+    /* value rows in [r0, r1) */
+    if (J->dval) {
+        for (int64_t r = r0; r < r1; ++r)
+            for (int d = 0; d < D; ++d)
+                J->dval[r * D + d] = 0.0;
+        for (int64_t bh = 0; bh < B * H; ++bh)
+            for (int j = 0; j < k; ++j) {
+                const int64_t r = J->rows[bh * k + j];
+                if (r < r0 || r >= r1) continue;
+                const float *gb = J->dout + (bh / H) * D;
+                for (int d = 0; d < D; ++d)
+                    J->dval[r * D + d] += J->w[bh * k + j] * (double)gb[d];
+            }
+    }
+    return NULL;
+}
+
+/*
+ * Gradients for tokens [0, B) of x [B][D] given dout [B][D] (dL/dout).  Each
+ * output is overwritten, or skipped when NULL:
+ *   dx      [B][D]          dgamma, dbeta [H][D]
+ *   dwq     [H][D][D]       dsub          [H][2][n][D/2]
+ *   dval    [n*n][D]  (w.r.t. the dequantised value rows)
+ * Returns 0, -1 on bad arguments, -2 if memory runs out.
+ */
+int pkmo_backward(const pkmo_model *M, int64_t B, const float *x, const float *dout, double *dx, double *dwq,
+                  double *dgamma, double *dbeta, double *dsub, double *dval, int nthreads)
+{
+    if (!M || !x || !dout || B < 0 || (M->D & 1) || M->H < 1 || M->k < 1 || M->k > M->n) return -1;
+    if (!M->values) return -1; /* step 7's g_j reads the value rows */
+    if (nthreads < 1) nthreads = 1;
+    const int D = M->D, H = M->H, k = M->k;
+    const size_t bhd = (size_t)B * H * D, bhk = (size_t)B * H * k;
+    double *qhat = (double *)malloc(sizeof(double) * (bhd ? bhd : 1));
+    double *xhat = (double *)malloc(sizeof(double) * (bhd ? bhd : 1));
+    double *dqhat = (double *)malloc(sizeof(double) * (bhd ? bhd : 1));
+    double *dt = (double *)malloc(sizeof(double) * (bhk ? bhk : 1));
+    double *w = (double *)malloc(sizeof(double) * (bhk ? bhk : 1));
+    int32_t *rows = (int32_t *)malloc(sizeof(int32_t) * (bhk ? bhk : 1));
+    pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
+    bwd_job *bj = (bwd_job *)malloc(sizeof(bwd_job) * (size_t)nthreads);
+    own_job *oj = (own_job *)malloc(sizeof(own_job) * (size_t)nthreads);
+    if (!qhat || !xhat || !dqhat || !dt || !w || !rows || !th || !bj || !oj) {
+        free(qhat); free(xhat); free(dqhat); free(dt); free(w); free(rows); free(th); free(bj); free(oj);
+        return -2;
+    }
+    const int tt = (int)(nthreads < (B > 0 ? B : 1) ? nthreads : (B > 0 ? B : 1));
+    for (int t = 0; t < tt; ++t) {
+        bwd_job J = {M, x, dout, dx, qhat, xhat, dqhat, dt, w, rows, B * t / tt, B * (t + 1) / tt};
+        bj[t] = J;
+    }
+    for (int t = 1; t < tt; ++t)
+        pthread_create(&th[t], NULL, backward_tokens, &bj[t]);
+    backward_tokens(&bj[0]);
+    for (int t = 1; t < tt; ++t)
+        pthread_join(th[t], NULL);
+    for (int t = 0; t < nthreads; ++t) {
+        own_job J = {M, B, x, dout, qhat, xhat, dqhat, dt, w, rows, dwq, dgamma, dbeta, dsub, dval, t, nthreads};
+        oj[t] = J;
+    }
+    for (int t = 1; t < nthreads; ++t)
+        pthread_create(&th[t], NULL, owner_sums, &oj[t]);
+    owner_sums(&oj[0]);
+    for (int t = 1; t < nthreads; ++t)
+        pthread_join(th[t], NULL);
+    free(qhat); free(xhat); free(dqhat); free(dt); free(w); free(rows); free(th); free(bj); free(oj);
     return 0;
 }

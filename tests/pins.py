@@ -14,6 +14,15 @@ build, or a variant passed as ``lib``) disagrees with:
     operation counts (tests/golden/op_counts.json);
   - special cases: k = n_keys (every key is a candidate), k = 1 (argmax of
     each half), exact integer ties (lower index wins).
+The backward direction (gradients of sum(dout * out)) is pinned to:
+  - torch autograd in fp64 through the page's code listing composed per
+    head (Linear, BatchNorm1d in eval mode, chunk, the two subkey products,
+    topk of each half, the k x k grid, topk, softmax, embedding_bag);
+  - central finite differences of the oracle's own forward output, with
+    steps that are exact in fp32 and small enough not to change the winners;
+  - identities: the value gradient sums to H * sum_b dout_b (each head's
+    weights sum to 1); each subkey set's gradient sums to zero over its rows
+    (the softmax Jacobian's rows sum to zero); zero dout gives zero gradients.
 """
 import json
 import math
@@ -241,3 +250,118 @@ def pin_op_counts(lib=None):
     assert 2 * n == g["subkey_scores"]
     assert (r["ncand"] == g["candidates"]).all()
     assert r["idx"].shape[-1] == k
+
+
+# ------------------------------------------------------------------ backward
+
+def module_autograd(params, x, dout, k, table="f32", eps=1e-5):
+    """Gradients of sum(dout * out) by torch autograd in fp64 through the
+    page's code listing, composed per head and summed over heads."""
+    leaf = lambda a: torch.from_numpy(np.ascontiguousarray(a)).double().requires_grad_()  # noqa: E731
+    wq, gamma, beta, sub = leaf(params["wq"]), leaf(params["gamma"]), leaf(params["beta"]), leaf(params["subkeys"])
+    vals = dequant_table(params["values"], params.get("scale"), table).clone().requires_grad_()
+    xt = leaf(x)
+    mean = torch.from_numpy(params["mean"]).double()
+    var = torch.from_numpy(params["var"]).double()
+    H, D, _ = wq.shape
+    n = sub.shape[2]
+    out = torch.zeros(x.shape[0], D, dtype=torch.float64)
+    for h in range(H):
+        q = F.linear(xt, wq[h])
+        qh = F.batch_norm(q, mean[h], var[h], gamma[h], beta[h], training=False, eps=eps)
+        q1, q2 = qh.chunk(2, dim=1)
+        s1, i1 = (q1 @ sub[h, 0].T).topk(k, dim=1)
+        s2, i2 = (q2 @ sub[h, 1].T).topk(k, dim=1)
+        all_scores = (s1[:, :, None] + s2[:, None, :]).reshape(-1, k * k)
+        all_idx = (i1[:, :, None] * n + i2[:, None, :]).reshape(-1, k * k)
+        top, pos = all_scores.topk(k, dim=1)
+        w = top.softmax(dim=-1)
+        out = out + F.embedding_bag(all_idx.gather(1, pos), vals, per_sample_weights=w, mode="sum")
+    (out * torch.from_numpy(dout).double()).sum().backward()
+    return {"dx": xt.grad.numpy(), "dwq": wq.grad.numpy(), "dgamma": gamma.grad.numpy(),
+            "dbeta": beta.grad.numpy(), "dsub": sub.grad.numpy(), "dval": vals.grad.numpy()}
+
+
+def backward_case(wl, seed=0, gamma_beta=False):
+    params = synthetic.make_params(wl, seed)
+    if gamma_beta:
+        rng = np.random.default_rng([seed, 1234])
+        params["gamma"] = rng.uniform(0.5, 1.5, params["gamma"].shape).astype(np.float32)
+        params["beta"] = rng.normal(0, 0.3, params["beta"].shape).astype(np.float32)
+    x = synthetic.make_x(wl, seed)
+    dout = np.random.default_rng([seed, 77]).standard_normal(x.shape).astype(np.float32)
+    return params, x, dout
+
+
+def pin_backward_autograd(wl, seed=0, gamma_beta=False, lib=None):
+    """Oracle gradients == torch autograd through the page's module."""
+    params, x, dout = backward_case(wl, seed, gamma_beta)
+    g = oracle.backward(_model(params, wl.k, wl.table), x, dout, lib=lib)
+    ref = module_autograd(params, x, dout, wl.k, wl.table)
+    for name in oracle.GRADS:
+        scale = max(np.abs(ref[name]).max(), 1e-300)
+        err = np.abs(g[name] - ref[name]).max() / scale
+        assert err <= 1e-10, f"{name}: max error {err:.3g} of its largest entry"
+    return g
+
+
+def _loss(params, x, dout, k, table, lib, eps=1e-5):
+    r = oracle.run(_model(params, k, table, eps), x, want=("out", "idx"), lib=lib)
+    return float((r["out"] * dout.astype(np.float64)).sum()), r["idx"]
+
+
+def pin_backward_finite_differences(lib=None, coords=10):
+    """Central differences of the oracle's forward loss against its
+    gradients, on a small fp32 workload with random gamma / beta.  Steps are
+    powers of two, so theta +- step is exact in fp32; a coordinate whose
+    step changes the winners is skipped (at most a fifth of them)."""
+    wl = synthetic.Workload("fd", 6, 16, 2, 8, 3, "f32", "random")
+    params, x, dout = backward_case(wl, 4, gamma_beta=True)
+    g = oracle.backward(_model(params, wl.k, wl.table), x, dout, lib=lib)
+    _, idx0 = _loss(params, x, dout, wl.k, wl.table, lib)
+    rng = np.random.default_rng(9)
+    targets = {"dx": ("x", None), "dwq": ("wq", None), "dgamma": ("gamma", None), "dbeta": ("beta", None),
+               "dsub": ("subkeys", None), "dval": ("values", None)}
+    checked = skipped = 0
+    for gname, (pname, _) in targets.items():
+        grad = g[gname]
+        flat = grad.reshape(-1)
+        # the largest gradients and a few random coordinates (zero ones too)
+        pick = list(np.argsort(-np.abs(flat))[:coords // 2]) + list(rng.integers(0, flat.size, coords // 2))
+        for c in pick:
+            arr = x if pname == "x" else params[pname]
+            base = arr.reshape(-1)[c]
+            step = np.float32(2.0 ** -14)
+            hi, lo = np.float32(base + step), np.float32(base - step)
+            assert hi - base == step and base - lo == step
+            def loss_at(v):
+                saved = arr.reshape(-1)[c]
+                arr.reshape(-1)[c] = v
+                try:
+                    return _loss(params, x, dout, wl.k, wl.table, lib)
+                finally:
+                    arr.reshape(-1)[c] = saved
+            lp, ip = loss_at(hi)
+            lm, im = loss_at(lo)
+            if not (np.array_equal(ip, idx0) and np.array_equal(im, idx0)):
+                skipped += 1
+                continue
+            fd = (lp - lm) / (2.0 * float(step))
+            assert abs(fd - flat[c]) <= 1e-6 + 1e-5 * abs(flat[c]), f"{gname}[{c}]: fd {fd} vs {flat[c]}"
+            checked += 1
+    assert skipped * 5 <= checked + skipped, f"{skipped} of {checked + skipped} coordinates changed the winners"
+
+
+def pin_backward_identities(lib=None):
+    """Sum of the value gradient, zero-sum subkey gradients, zero dout."""
+    wl = synthetic.Workload("ident", 40, 32, 3, 12, 5, "bf16", "random")
+    params, x, dout = backward_case(wl, 6, gamma_beta=True)
+    model = _model(params, wl.k, wl.table)
+    g = oracle.backward(model, x, dout, lib=lib)
+    want = wl.H * dout.astype(np.float64).sum(0)
+    np.testing.assert_allclose(g["dval"].sum(0), want, rtol=1e-12, atol=1e-12 * np.abs(want).max())
+    sums = g["dsub"].sum(axis=2)  # over the subkeys of each (head, half)
+    assert np.abs(sums).max() <= 1e-12 * max(np.abs(g["dsub"]).max(), 1e-300)
+    z = oracle.backward(model, x, np.zeros_like(dout), lib=lib)
+    for name in oracle.GRADS:
+        assert not z[name].any(), name

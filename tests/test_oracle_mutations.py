@@ -31,6 +31,19 @@ MUTATIONS = {
     "bf16_subnormal": ("v = ldexp((double)m / 128.0, -126);", "v = ldexp((double)m / 128.0, -127);"),
     "candidate_count": ("    return c;\n}", "    return c - 1;\n}"),
     "half_topk_from_wrong_row": ("pkmo_topk_sorted(n, s + n, kk, t1, i1);", "pkmo_topk_sorted(n, s, kk, t1, i1);"),
+    # backward direction
+    "bwd_softmax_no_centering": ("dtj[j] = wj[j] * (g[j] - wg);", "dtj[j] = wj[j] * g[j];"),
+    "bwd_dqhat_halves_swapped": ("dqh[half + d] += dtj[j] * (double)c1[d];", "dqh[half + d] += dtj[j] * (double)c0[d];"),
+    "bwd_dq_without_gamma": ("dq[f] = dqh[f] * (double)M->gamma[pf] * inv;", "dq[f] = dqh[f] * inv;"),
+    "bwd_dx_transposed": ("J->dx[b * D + d] += dq[f] * (double)wrow[d];",
+                          "J->dx[b * D + d] += dq[f] * (double)M->wq[((int64_t)h * D + d) * D + f];"),
+    "bwd_dgamma_from_qhat": ("J->dgamma[pf] += dqh * J->xhat[at];", "J->dgamma[pf] += dqh * J->qhat[at];"),
+    "bwd_dwq_skips_bn_scale": ("const double dq = dqh * scale;", "const double dq = dqh;"),
+    "bwd_dsub_wrong_half": ("const double *qp = J->qhat + bh * D + p * half;",
+                            "const double *qp = J->qhat + bh * D + (1 - p) * half;"),
+    "bwd_dval_unweighted": ("J->dval[r * D + d] += J->w[bh * k + j] * (double)gb[d];",
+                            "J->dval[r * D + d] += (double)gb[d];"),
+    "bwd_g_from_first_row": ("acc += (double)gb[d] * value_at(M, rj[j], d);", "acc += (double)gb[d] * value_at(M, rj[0], d);"),
 }
 
 PINS = [
@@ -45,6 +58,10 @@ PINS = [
                                              gamma_beta=True, lib=lib),
     lambda lib: pins.pin_against_flat_search(pins.synthetic.Workload("q", 24, 128, 2, 24, 8, "e4m3", "random"),
                                              seed=2, lib=lib),
+    pins.pin_backward_identities,
+    lambda lib: pins.pin_backward_autograd(pins.synthetic.Workload("gb", 24, 64, 3, 20, 5, "f32", "random"),
+                                           gamma_beta=True, lib=lib),
+    pins.pin_backward_finite_differences,
 ]
 
 
