@@ -175,6 +175,42 @@ pkm_status pkm_flat_workspace_bytes(const pkm_config *cfg, int64_t B, size_t *by
 pkm_status pkm_flat_search(pkm_ctx *ctx, const pkm_params *p, int64_t B, const float *qhat, void *workspace,
                            size_t workspace_bytes, int32_t *idx, float *top, void *stream);
 
+/* Gradients written by pkm_backward.  Parameter gradients are ADDED to what
+ * the buffers hold (zero them for one batch's gradient); dx is overwritten.
+ * Any member may be NULL to skip that gradient (dbn_gamma and dbn_beta go
+ * together).  All are fp32 device buffers, 16-byte aligned. */
+typedef struct {
+    float *dx;        /* [B, D] */
+    float *dwq;       /* [H, D, D] */
+    float *dbn_gamma; /* [H, D] */
+    float *dbn_beta;  /* [H, D] */
+    float *dsubkeys;  /* [H, 2, n_keys, D/2] */
+    float *dvalues;   /* [n_keys^2, D]: w.r.t. the dequantised value rows
+                         (scale[row] * stored value for E4M3 tables) */
+} pkm_grads;
+
+/* Bytes of caller-owned device workspace pkm_backward needs for cfg (it
+ * works through the batch in chunks of cfg->max_batch tokens). */
+pkm_status pkm_backward_workspace_bytes(const pkm_config *cfg, size_t *bytes);
+
+/* The backward direction: gradients of a loss L given dout = dL/dout [B, D]
+ * fp32, through steps a7 -> a1 for the winners a forward call selected
+ * (idx, weights [B, H, k] as pkm_forward wrote them for the same x and p).
+ * The top-k selections pass gradient only to the winning scores ("Product-
+ * Key Memory", code listing: topk values feed the softmax, its indices only
+ * select), and BN uses its running statistics, as in the forward:
+ *   dL/dw_j = dout_b . V[r_j];  softmax backward to the winning scores;
+ *   each score s_0[i0] + s_1[i1] passes its gradient to both half scores;
+ *   half scores -> q^ (subkey rows) and -> subkeys (q^ halves);
+ *   q^ -> dgamma, dbeta and q;  q -> dWq (outer products with x) and dx;
+ *   dV[r_j] += w_j dout_b.
+ * Every sum runs in a fixed order: results are bitwise reproducible.
+ * workspace: caller-owned, >= pkm_backward_workspace_bytes(cfg) bytes,
+ * 16-byte aligned; the call allocates nothing. */
+pkm_status pkm_backward(pkm_ctx *ctx, const pkm_params *p, int64_t B, const float *x, const int32_t *idx,
+                        const float *weights, const float *dout, const pkm_grads *grads, void *workspace,
+                        size_t workspace_bytes, void *stream);
+
 /* A static description of a status code. */
 const char *pkm_status_str(pkm_status s);
 

@@ -16,8 +16,8 @@ VALUE_TYPES = {"f32": 0, "bf16": 1, "e4m3": 2}
 # Every symbol include/pkm.h declares.
 EXPORTS = (
     "pkm_config_check", "pkm_workspace_bytes", "pkm_create", "pkm_destroy", "pkm_forward", "pkm_query",
-    "pkm_score", "pkm_select", "pkm_gather", "pkm_flat_workspace_bytes", "pkm_flat_search", "pkm_status_str",
-    "pkm_last_error",
+    "pkm_score", "pkm_select", "pkm_gather", "pkm_flat_workspace_bytes", "pkm_flat_search",
+    "pkm_backward_workspace_bytes", "pkm_backward", "pkm_status_str", "pkm_last_error",
 )
 
 
@@ -65,6 +65,9 @@ def load_library(path=LIB_PATH):
         "pkm_gather": (ctypes.c_int, [vp, par_p, i64, i32, vp, vp, vp, vp]),
         "pkm_flat_workspace_bytes": (ctypes.c_int, [cfg_p, i64, ctypes.POINTER(ctypes.c_size_t)]),
         "pkm_flat_search": (ctypes.c_int, [vp, par_p, i64, vp, vp, ctypes.c_size_t, vp, vp, vp]),
+        "pkm_backward_workspace_bytes": (ctypes.c_int, [cfg_p, ctypes.POINTER(ctypes.c_size_t)]),
+        "pkm_backward": (ctypes.c_int, [vp, par_p, i64, vp, vp, vp, vp, ctypes.POINTER(GradsStruct), vp,
+                                        ctypes.c_size_t, vp]),
         "pkm_status_str": (ctypes.c_char_p, [ctypes.c_int]),
         "pkm_last_error": (ctypes.c_char_p, []),
     }
@@ -140,6 +143,13 @@ def _expect(t, name, shape, dtype, device=None):
         raise ValueError(f"{name} must live on {device or 'the GPU'}, got {t.device}")
     if t.data_ptr() % 16:
         raise ValueError(f"{name} must be 16-byte aligned")
+
+
+class GradsStruct(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in ("dx", "dwq", "dbn_gamma", "dbn_beta", "dsubkeys", "dvalues")]
+
+
+GRAD_NAMES = ("dx", "dwq", "dbn_gamma", "dbn_beta", "dsubkeys", "dvalues")
 
 
 class Params:
@@ -279,6 +289,44 @@ class Memory:
         _check(self.lib.pkm_gather(self._ctx, ctypes.byref(params.struct), B, R, _ptr(idx), _ptr(weights),
                                    _ptr(out), _stream_handle(stream)))
         return out
+
+    def backward_workspace_bytes(self):
+        n = ctypes.c_size_t()
+        _check(self.lib.pkm_backward_workspace_bytes(ctypes.byref(self.cfg), ctypes.byref(n)))
+        return n.value
+
+    def backward(self, params, x, idx, weights, dout, grads=None, workspace=None, stream=None):
+        """Gradients of a loss given dout = dL/dout [B, D] for the winners
+        (idx, weights) a forward call returned.  grads: dict name -> fp32
+        tensor (parameter gradients are added to, dx is overwritten; a
+        missing name is skipped), or None for freshly zeroed buffers of every
+        gradient.  Returns the dict."""
+        torch = _torch()
+        B = x.shape[0]
+        D, H, n, k = self.dim, self.heads, self.n_keys, self.k
+        self.check_params(params)
+        dev = params["wq"].device
+        _expect(x, "x", (B, D), "float32", dev)
+        _expect(dout, "dout", (B, D), "float32", dev)
+        _expect(idx, "idx", (B, H, k), "int32", dev)
+        _expect(weights, "weights", (B, H, k), "float32", dev)
+        shapes = {"dx": (B, D), "dwq": (H, D, D), "dbn_gamma": (H, D), "dbn_beta": (H, D),
+                  "dsubkeys": (H, 2, n, D // 2), "dvalues": (n * n, D)}
+        if grads is None:
+            grads = {name: torch.zeros(shape, dtype=torch.float32, device=dev) for name, shape in shapes.items()}
+        for name, t in grads.items():
+            if name not in shapes:
+                raise ValueError(f"unknown gradient {name}")
+            _expect(t, name, shapes[name], "float32", dev)
+        need = self.backward_workspace_bytes()
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        _expect(workspace, "workspace", (workspace.numel(),), "uint8", dev)
+        gs = GradsStruct(*[None if grads.get(nm) is None else grads[nm].data_ptr() for nm in GRAD_NAMES])
+        _check(self.lib.pkm_backward(self._ctx, ctypes.byref(params.struct), B, _ptr(x), _ptr(idx), _ptr(weights),
+                                     _ptr(dout), ctypes.byref(gs), _ptr(workspace), workspace.numel(),
+                                     _stream_handle(stream)))
+        return grads
 
     def flat_workspace_bytes(self, B):
         n = ctypes.c_size_t()

@@ -117,7 +117,7 @@ __device__ __forceinline__ void mfma_chunk(floatx16 (&acc)[T::TM][T::TN], const 
     }
 }
 
-template <typename T, bool BN_EPILOGUE, bool STREAM_OUT, bool PRODUCT_B = false>
+template <typename T, bool BN_EPILOGUE, bool STREAM_OUT, bool PRODUCT_B = false, bool ACCUMULATE = false>
 __global__ __launch_bounds__(T::THREADS) void gemm_nt_f32_kernel(GemmArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) float smem[];
@@ -214,6 +214,7 @@ __global__ __launch_bounds__(T::THREADS) void gemm_nt_f32_kernel(GemmArgs a)
                 if (row < a.M) {
                     float c = acc[i][j][v];
                     if (BN_EPILOGUE) c = (c - mean) * mul + beta;
+                    if (ACCUMULATE) c += C[(int64_t)row * a.ldc + col];
                     if (STREAM_OUT)
                         __builtin_nontemporal_store(c, &C[(int64_t)row * a.ldc + col]);
                     else
@@ -230,10 +231,10 @@ int64_t tile_count(const GemmArgs &a)
     return (int64_t)((a.M + T::BM - 1) / T::BM) * ((a.N + T::BN - 1) / T::BN);
 }
 
-template <typename T, bool BN_EPILOGUE, bool STREAM_OUT, bool PRODUCT_B = false>
+template <typename T, bool BN_EPILOGUE, bool STREAM_OUT, bool PRODUCT_B = false, bool ACCUMULATE = false>
 hipError_t launch_variant(const GemmArgs &a, hipStream_t stream)
 {
-    const auto kernel = &gemm_nt_f32_kernel<T, BN_EPILOGUE, STREAM_OUT, PRODUCT_B>;
+    const auto kernel = &gemm_nt_f32_kernel<T, BN_EPILOGUE, STREAM_OUT, PRODUCT_B, ACCUMULATE>;
     if (T::LDS_BYTES > 65536) {
         // Dynamic LDS above 64 KiB must be allowed per kernel (gfx950 has
         // 160 KiB per CU); done once per kernel per process.
@@ -250,6 +251,10 @@ template <typename T>
 hipError_t launch_tile(const GemmArgs &a, hipStream_t stream)
 {
     if (tile_count<T>(a) > 0x7FFFFFFF || a.batch > 65535) return hipErrorInvalidConfiguration;
+    if (a.accumulate) {
+        if (a.bn_mean || a.stream_out) return hipErrorInvalidValue;
+        return launch_variant<T, false, false, false, true>(a, stream);
+    }
     if (a.bn_mean) {
         if (a.stream_out) return launch_variant<T, true, true>(a, stream);
         return launch_variant<T, true, false>(a, stream);

@@ -254,6 +254,46 @@ pkm::GemmArgs flat_args(const pkm_config &c, const pkm_params *p, int64_t B, con
     return a;
 }
 
+// Backward workspace for chunks of mb = max_batch tokens (mb32 = mb rounded
+// up to 32, the GEMMs' K granularity).
+constexpr int kBwdPieces = 16;
+bool backward_layout(const pkm_config &c, size_t sizes[kBwdPieces])
+{
+    const size_t mb = (size_t)c.max_batch, mb32 = (mb + 31) / 32 * 32, H = (size_t)c.heads, D = (size_t)c.dim;
+    const size_t HD = H * D, k = (size_t)c.k, n = (size_t)c.n_keys, N = n * n;
+    const double total = (double)mb32 * (double)HD * 7.0 + 2.0 * H * n * mb32 + 4.0 * N;
+    if (total * 4.0 > 1.0e15) return false;
+    const size_t f = sizeof(float), u = sizeof(uint32_t);
+    sizes[0] = round_up(mb * HD * f);       // q (before BN)
+    sizes[1] = round_up(mb * H * k * f);    // dt
+    sizes[2] = round_up(mb * HD * f);       // dq^
+    sizes[3] = round_up(mb * HD * f);       // dq
+    sizes[4] = round_up(HD * mb32 * f);     // dq transposed
+    sizes[5] = round_up(D * mb32 * f);      // x transposed
+    sizes[6] = round_up(D * HD * f);        // Wq transposed
+    sizes[7] = round_up(HD * mb32 * f);     // q^ transposed
+    sizes[8] = round_up(2 * H * n * mb32 * f);  // half-score gradients G
+    sizes[9] = round_up((size_t)pkm::colsum_chunks((int64_t)mb) * HD * f);
+    sizes[10] = sizes[9];
+    sizes[11] = round_up(N * u);            // per-row counts
+    sizes[12] = round_up(N * u);            // fill cursors
+    sizes[13] = round_up(N * u);            // row offsets
+    sizes[14] = round_up((size_t)pkm::scan_blocks((int)N) * u);
+    sizes[15] = round_up(mb * H * k * u);   // occurrence lists
+    return true;
+}
+
+pkm_status check_grads(const pkm_grads *g)
+{
+    if (!g) return fail(PKM_E_ARG, "grads is NULL");
+    const void *ptrs[] = {g->dx, g->dwq, g->dbn_gamma, g->dbn_beta, g->dsubkeys, g->dvalues};
+    for (const void *q : ptrs)
+        if (q && !aligned16(q)) return fail(PKM_E_ARG, "gradient buffers must be 16-byte aligned");
+    if ((g->dbn_gamma == nullptr) != (g->dbn_beta == nullptr))
+        return fail(PKM_E_ARG, "dbn_gamma and dbn_beta go together");
+    return PKM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -451,6 +491,154 @@ pkm_status pkm_flat_search(pkm_ctx *ctx, const pkm_params *p, int64_t B, const f
                                             top, st),
                       "flat top-k")))
         return s;
+    return ok();
+}
+
+pkm_status pkm_backward_workspace_bytes(const pkm_config *cfg, size_t *bytes)
+{
+    if (pkm_status s = check_config(cfg)) return s;
+    if (!bytes) return fail(PKM_E_ARG, "bytes is NULL");
+    size_t sizes[kBwdPieces];
+    if (!backward_layout(*cfg, sizes)) return fail(PKM_E_ARG, "backward workspace size overflows");
+    *bytes = 0;
+    for (size_t piece : sizes) *bytes += piece;
+    return ok();
+}
+
+pkm_status pkm_backward(pkm_ctx *ctx, const pkm_params *p, int64_t B, const float *x, const int32_t *idx,
+                        const float *weights, const float *dout, const pkm_grads *grads, void *workspace,
+                        size_t workspace_bytes, void *stream)
+{
+    pkm_status s;
+    if ((s = check_ctx(ctx)) || (s = check_batch(ctx->cfg, B))) return s;
+    const pkm_config &c = ctx->cfg;
+    size_t sizes[kBwdPieces];
+    if (!backward_layout(c, sizes)) return fail(PKM_E_ARG, "backward workspace size overflows");
+    size_t need_bytes = 0;
+    for (size_t piece : sizes) need_bytes += piece;
+    if (B == 0) return ok();
+    if ((s = check_query_params(p)) || (s = need(p->subkeys, "subkeys")) || (s = check_value_params(c, p))) return s;
+    if ((s = need(x, "x")) || (s = need(idx, "idx")) || (s = need(weights, "weights")) || (s = need(dout, "dout")) ||
+        (s = need(workspace, "workspace")) || (s = check_grads(grads)))
+        return s;
+    if (workspace_bytes < need_bytes)
+        return fail(PKM_E_ARG, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, need_bytes);
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char *w = static_cast<char *>(workspace);
+    void *piece[kBwdPieces];
+    for (int i = 0; i < kBwdPieces; ++i) {
+        piece[i] = w;
+        w += sizes[i];
+    }
+    float *Q = static_cast<float *>(piece[0]), *dt = static_cast<float *>(piece[1]);
+    float *dqh = static_cast<float *>(piece[2]), *dq = static_cast<float *>(piece[3]);
+    float *dqT = static_cast<float *>(piece[4]), *xT = static_cast<float *>(piece[5]);
+    float *wqT = static_cast<float *>(piece[6]), *qhT = static_cast<float *>(piece[7]);
+    float *G = static_cast<float *>(piece[8]);
+    float *part_g = static_cast<float *>(piece[9]), *part_b = static_cast<float *>(piece[10]);
+    uint32_t *count = static_cast<uint32_t *>(piece[11]), *cursor = static_cast<uint32_t *>(piece[12]);
+    uint32_t *offs = static_cast<uint32_t *>(piece[13]), *block_sum = static_cast<uint32_t *>(piece[14]);
+    uint32_t *list = static_cast<uint32_t *>(piece[15]);
+
+    const int H = c.heads, D = c.dim, k = c.k, n = c.n_keys, half = D / 2, HD = H * D, N = n * n;
+    if (grads->dx &&
+        (s = launched(pkm::launch_transpose(p->wq, D, HD, D, wqT, HD, HD, nullptr, nullptr, nullptr, nullptr, 0.0f, st),
+                      "Wq transpose")))
+        return s;
+    for (int64_t b0 = 0; b0 < B; b0 += c.max_batch) {
+        const int64_t nb = B - b0 < c.max_batch ? B - b0 : c.max_batch;
+        const int nb32 = (int)((nb + 31) / 32 * 32);
+        const float *xc = x + b0 * D, *doutc = dout + b0 * D, *wc = weights + b0 * H * k;
+        const int32_t *ic = idx + b0 * H * k;
+        // q before BN
+        pkm::GemmArgs qa = query_args(c, p, nb, xc, Q);
+        qa.bn_mean = qa.bn_var = qa.bn_gamma = qa.bn_beta = nullptr;
+        if ((s = launched(pkm::launch_gemm_nt_f32(qa, st), "query recompute"))) return s;
+        if ((s = launched(pkm::launch_value_backward(p->values, p->value_scale, c.value_type, D, N, nb, H, k, ic, wc,
+                                                     doutc, dt, st),
+                          "value backward")))
+            return s;
+        if (grads->dsubkeys &&
+            (s = launched(pkm::launch_fill(reinterpret_cast<uint32_t *>(G), (int64_t)2 * H * n * nb32, 0u, st),
+                          "clear")))
+            return s;
+        if ((s = launched(pkm::launch_dqhat(p->subkeys, p->bn_var, p->bn_gamma, c.bn_eps, D, n, nb, H, k, ic, dt, dqh,
+                                            dq, G, nb32, st),
+                          "query gradient")))
+            return s;
+        if (grads->dbn_gamma &&
+            (s = launched(pkm::launch_bn_grads(dqh, Q, p->bn_mean, p->bn_var, c.bn_eps, nb, HD, part_g, part_b,
+                                               grads->dbn_gamma, grads->dbn_beta, st),
+                          "BN gradients")))
+            return s;
+        if (grads->dwq) {
+            if ((s = launched(pkm::launch_transpose(dq, HD, (int)nb, HD, dqT, nb32, nb32, nullptr, nullptr, nullptr,
+                                                    nullptr, 0.0f, st),
+                              "dq transpose")) ||
+                (s = launched(pkm::launch_transpose(xc, D, (int)nb, D, xT, nb32, nb32, nullptr, nullptr, nullptr,
+                                                    nullptr, 0.0f, st),
+                              "x transpose")))
+                return s;
+            pkm::GemmArgs a{};
+            a.A = dqT;
+            a.lda = nb32;
+            a.strideA = (int64_t)D * nb32;
+            a.B = xT;
+            a.ldb = nb32;
+            a.strideB = 0;
+            a.C = grads->dwq;
+            a.ldc = D;
+            a.strideC = (int64_t)D * D;
+            a.M = D;
+            a.N = D;
+            a.K = nb32;
+            a.batch = H;
+            a.accumulate = true;
+            if ((s = launched(pkm::launch_gemm_nt_f32(a, st), "dWq"))) return s;
+        }
+        if (grads->dsubkeys) {
+            if ((s = launched(pkm::launch_transpose(Q, HD, (int)nb, HD, qhT, nb32, nb32, p->bn_mean, p->bn_var,
+                                                    p->bn_gamma, p->bn_beta, c.bn_eps, st),
+                              "q^ transpose")))
+                return s;
+            pkm::GemmArgs a{};
+            a.A = G;
+            a.lda = nb32;
+            a.strideA = (int64_t)n * nb32;
+            a.B = qhT;
+            a.ldb = nb32;
+            a.strideB = (int64_t)half * nb32;
+            a.C = grads->dsubkeys;
+            a.ldc = half;
+            a.strideC = (int64_t)n * half;
+            a.M = n;
+            a.N = half;
+            a.K = nb32;
+            a.batch = 2 * H;
+            a.accumulate = true;
+            if ((s = launched(pkm::launch_gemm_nt_f32(a, st), "dsubkeys"))) return s;
+        }
+        if (grads->dx) {
+            pkm::GemmArgs a{};
+            a.A = dq;
+            a.lda = HD;
+            a.B = wqT;
+            a.ldb = HD;
+            a.C = grads->dx + b0 * D;
+            a.ldc = D;
+            a.M = (int)nb;
+            a.N = D;
+            a.K = HD;
+            a.batch = 1;
+            if ((s = launched(pkm::launch_gemm_nt_f32(a, st), "dx"))) return s;
+        }
+        if (grads->dvalues &&
+            (s = launched(pkm::launch_value_grad(ic, nb * H * k, N, D, H * k, wc, doutc, count, cursor, offs,
+                                                 block_sum, list, grads->dvalues, st),
+                          "value gradient")))
+            return s;
+    }
     return ok();
 }
 

@@ -32,6 +32,8 @@ struct GemmArgs {
     // row stride ldb and batch stride strideB; split_k % 32 == 0.
     const float *B2;
     int split_k, key_n;
+    // accumulate: C += A . B^T instead of C = A . B^T (no BN, no streaming).
+    bool accumulate;
 };
 hipError_t launch_gemm_nt_f32(const GemmArgs &a, hipStream_t stream);
 // The same contraction with a product-key B operand and a 32 x 256 tile
@@ -65,5 +67,36 @@ hipError_t launch_flat_topk(const float *scores, int64_t rows, int64_t len, int 
 
 hipError_t launch_gather(const void *values, const float *scale, int value_type, int D, int N, int64_t B, int R,
                          const int32_t *idx, const float *w, float *out, hipStream_t stream);
+
+// ---- backward direction (backward.hip)
+hipError_t launch_fill(uint32_t *p, int64_t count, uint32_t value, hipStream_t st);
+// out[c][r] = in[r][c] (optionally BN of column c) for r < R, c < C; zero for
+// R <= r < Rp.
+hipError_t launch_transpose(const float *in, int64_t ld_in, int R, int C, float *out, int64_t ld_out, int Rp,
+                            const float *mean, const float *var, const float *gamma, const float *beta, float eps,
+                            hipStream_t st);
+// dt [B][H][k]: softmax backward of g_j = dout_b . V[idx_j].
+hipError_t launch_value_backward(const void *values, const float *scale, int value_type, int D, int N, int64_t B,
+                                 int H, int k, const int32_t *idx, const float *w, const float *dout, float *dt,
+                                 hipStream_t st);
+// dqhat, dq [B][H][D] and the half-score gradients G [2H][n][ldG] (columns
+// b < B; G must be zero beforehand).
+hipError_t launch_dqhat(const float *subkeys, const float *var, const float *gamma, float eps, int D, int n, int64_t B,
+                        int H, int k, const int32_t *idx, const float *dt, float *dqhat, float *dq, float *G,
+                        int64_t ldG, hipStream_t st);
+// dgamma, dbeta [cols] += column sums over B rows of dqhat * xhat and dqhat,
+// xhat = (q - mean) / sqrt(var + eps); part_g / part_b hold
+// colsum_chunks(B) * cols floats each.
+int colsum_chunks(int64_t B);
+hipError_t launch_bn_grads(const float *dqhat, const float *q, const float *mean, const float *var, float eps,
+                           int64_t B, int cols, float *part_g, float *part_b, float *dgamma, float *dbeta,
+                           hipStream_t st);
+// dval [N][D] += sum over the M occurrences o (row idx[o]) of w[o] *
+// dout[o / per_token]; count, cursor, offs [N], block_sum [scan_blocks(N)],
+// list [M] are scratch.
+int64_t scan_blocks(int N);
+hipError_t launch_value_grad(const int32_t *idx, int64_t M, int N, int D, int per_token, const float *w,
+                             const float *dout, uint32_t *count, uint32_t *cursor, uint32_t *offs,
+                             uint32_t *block_sum, uint32_t *list, float *dval, hipStream_t st);
 
 }  // namespace pkm

@@ -108,6 +108,26 @@ def test_flat_workspace_bytes():
     assert lib.pkm_flat_workspace_bytes(ctypes.byref(cfg), -1, ctypes.byref(got)) == pk.PKM_E_ARG
 
 
+def test_backward_workspace_bytes():
+    """Chunks of max_batch tokens: q, dq^, dq [mb, H*D] and three transposed
+    [.., mb32] operands, x^T, Wq^T, the half-score gradients [2H, n, mb32],
+    the BN partial sums, per-row counts / cursors / offsets and the lists."""
+    lib = pk.load_library()
+    cfg = pk.make_config(**{**GOOD, "max_batch": 1000})
+    mb, mb32, H, D, n, k = 1000, 1024, 4, 1024, 1024, 32
+    HD, N = H * D, n * n
+
+    def rnd(x):
+        return (x + 255) // 256 * 256
+
+    want = (3 * rnd(mb * HD * 4) + rnd(mb * H * k * 4) + 2 * rnd(HD * mb32 * 4) + rnd(D * mb32 * 4)
+            + rnd(D * HD * 4) + rnd(2 * H * n * mb32 * 4) + 2 * rnd(((mb + 63) // 64) * HD * 4)
+            + 3 * rnd(N * 4) + rnd(((N + 4095) // 4096) * 4) + rnd(mb * H * k * 4))
+    got = ctypes.c_size_t()
+    assert lib.pkm_backward_workspace_bytes(ctypes.byref(cfg), ctypes.byref(got)) == pk.PKM_OK
+    assert got.value == want
+
+
 def test_null_arguments_rejected_before_any_launch():
     lib = pk.load_library()
     null = ctypes.c_void_p()
@@ -118,6 +138,9 @@ def test_null_arguments_rejected_before_any_launch():
     assert lib.pkm_select(null, 1, null, null, null, null) == pk.PKM_E_ARG
     assert lib.pkm_gather(null, ctypes.byref(params), 1, 1, null, null, null, null) == pk.PKM_E_ARG
     assert lib.pkm_flat_search(null, ctypes.byref(params), 1, null, null, 0, null, null, null) == pk.PKM_E_ARG
+    grads = pk._binding.GradsStruct()
+    assert lib.pkm_backward(null, ctypes.byref(params), 1, null, null, null, null, ctypes.byref(grads), null, 0,
+                            null) == pk.PKM_E_ARG
     assert lib.pkm_create(None, ctypes.byref(ctypes.c_void_p())) == pk.PKM_E_ARG
     assert lib.pkm_create(ctypes.byref(pk.make_config(**GOOD)), None) == pk.PKM_E_ARG
     assert "NULL" in pk.last_error()

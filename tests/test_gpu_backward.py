@@ -1,0 +1,196 @@
+"""GPU: the backward direction (pkm_backward) through the C ABI against the
+fp64 oracle's gradients (oracle.backward, pinned in tests/pins.py).
+
+The GPU backward takes the winners of the GPU forward; on gap-clean inputs
+they are the oracle's (tests/support.py), so both differentiate the same
+function.  Tolerance: every gradient tensor within 1e-4 of its largest
+entry (max-norm); the backward is fp32 throughout and every table format is
+decoded from the same stored bits on both sides.  dx is also checked per
+token, within 1e-4 of max(the token's largest entry, the batch median of
+that): where a head's softmax is nearly one-hot, dt_j = w_j (g_j - sum w g)
+cancels and the token's gradient can fall far below its rounding scale,
+which is set by dout and the value rows and is alike across tokens (seen:
+a token with weights 1 - 5e-8 whose dx is 1/1500 of the median).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import product_key_memory_amd as pk
+import synthetic
+from tests import pins, support
+from tests.support import say
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-4
+# oracle name -> binding name
+NAMES = {"dx": "dx", "dwq": "dwq", "dgamma": "dbn_gamma", "dbeta": "dbn_beta", "dsub": "dsubkeys",
+         "dval": "dvalues"}
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+
+    support.device()
+    pk.load_library()
+    return t
+
+
+def _to(torch, a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(support.device())
+
+
+def case(wl, seed=0, gamma_beta=False):
+    params, x, dout = pins.backward_case(wl, seed, gamma_beta)
+    support.gap_clean(wl, params, x, seed=seed)
+    return params, x, dout
+
+
+def gpu_backward(torch, wl, params, x, dout, max_batch=16384, grads=None, mem=None):
+    mem = mem or pk.Memory(wl.D, wl.H, wl.n, wl.k, wl.table, max_batch=max_batch)
+    P = pk.params_to_device(params, wl.table, support.device())
+    xt, dt = _to(torch, x), _to(torch, dout)
+    say("backward", wl, "B =", x.shape[0], "max_batch =", max_batch)
+    _, idx, w = mem.forward(P, xt)
+    g = mem.backward(P, xt, idx, w, dt, grads=grads)
+    torch.cuda.synchronize()
+    return {name: t.cpu().numpy() for name, t in g.items()}, idx.cpu().numpy()
+
+
+def compare(got, ref, names=NAMES):
+    errs = {}
+    for oname, gname in names.items():
+        if oname not in ref or gname not in got:
+            continue
+        r, g = ref[oname], got[gname].astype(np.float64)
+        scale = max(np.abs(r).max(), 1e-30)
+        errs[oname] = float(np.abs(g - r).max() / scale)
+        assert errs[oname] <= TOL, (oname, errs[oname])
+        if oname == "dx" and r.shape[0]:
+            mag = np.abs(r).max(1)
+            floor = np.maximum(mag, np.median(mag))
+            row = np.abs(g - r).max(1) / np.maximum(floor, 1e-30)
+            assert row.max() <= TOL, ("dx per token", float(row.max()), int(row.argmax()))
+    return errs
+
+
+@pytest.mark.parametrize("wl,gamma_beta", [
+    (synthetic.WORKLOADS["tiny"], False),
+    (synthetic.WORKLOADS["mid"], False),
+    (synthetic.Workload("bgb", 100, 128, 3, 20, 5, "f32", "random"), True),   # ragged B, random BN, gamma, beta
+    (synthetic.Workload("bbf", 64, 256, 2, 48, 16, "bf16", "unit"), False),  # bf16 table
+    (synthetic.Workload("be4", 77, 192, 2, 33, 9, "e4m3", "random"), True),  # E4M3 + row scales, D = 3 * 64
+    (synthetic.Workload("bkn", 40, 64, 1, 12, 12, "f32", "random"), False),  # k = n_keys
+    (synthetic.Workload("bk1", 50, 64, 2, 30, 1, "bf16", "random"), True),   # k = 1: no gradient to the scores
+])
+def test_backward_against_oracle(torch, wl, gamma_beta):
+    params, x, dout = case(wl, 2, gamma_beta)
+    got, _ = gpu_backward(torch, wl, params, x, dout)
+    ref = oracle.backward(support.model_for(wl, params), x, dout)
+    errs = compare(got, ref)
+    print(wl.name, {k: f"{v:.2g}" for k, v in errs.items()}, flush=True)
+
+
+def test_backward_chunks_accumulate_and_repeat_bitwise(torch):
+    """max_batch smaller than B: the chunks add into the parameter gradients;
+    a second call adds the same again (to rounding: each chunk's sum is
+    added to what the buffer holds, so g + g is not summed as 2 g); two runs
+    give the same bits."""
+    wl = synthetic.Workload("bch", 150, 128, 2, 24, 6, "bf16", "random")
+    params, x, dout = case(wl, 3, True)
+    ref = oracle.backward(support.model_for(wl, params), x, dout)
+    one, _ = gpu_backward(torch, wl, params, x, dout, max_batch=64)
+    compare(one, ref)
+    again, _ = gpu_backward(torch, wl, params, x, dout, max_batch=64)
+    for name in one:
+        assert np.array_equal(one[name], again[name]), name
+    mem = pk.Memory(wl.D, wl.H, wl.n, wl.k, wl.table, max_batch=64)
+    twice, _ = gpu_backward(torch, wl, params, x, dout, mem=mem)
+    grads = {name: _to(torch, t) for name, t in twice.items()}
+    P = pk.params_to_device(params, wl.table, support.device())
+    xt = _to(torch, x)
+    _, idx, w = mem.forward(P, xt)
+    mem.backward(P, xt, idx, w, _to(torch, dout), grads=grads)
+    torch.cuda.synchronize()
+    for name, t in grads.items():
+        t = t.cpu().numpy()
+        if name == "dx":
+            assert np.array_equal(t, twice[name])
+        else:
+            want = 2 * twice[name].astype(np.float64)
+            assert np.abs(t - want).max() <= 1e-6 * max(np.abs(want).max(), 1e-30), name
+
+
+def test_backward_subset_of_gradients(torch):
+    """Skipped gradients leave no trace; the computed ones are unchanged."""
+    wl = synthetic.Workload("bsub", 40, 64, 2, 16, 4, "f32", "random")
+    params, x, dout = case(wl, 4, True)
+    full, _ = gpu_backward(torch, wl, params, x, dout)
+    for subset in (("dvalues",), ("dx",), ("dbn_gamma", "dbn_beta"), ("dsubkeys", "dwq")):
+        grads = {name: torch.zeros(full[name].shape, dtype=torch.float32, device=support.device())
+                 for name in subset}
+        part, _ = gpu_backward(torch, wl, params, x, dout, grads=grads)
+        for name in subset:
+            assert np.array_equal(part[name], full[name]), (subset, name)
+
+
+def test_backward_hot_rows(torch):
+    """One token repeated 100 times: every selected row occurs 100 * H / H =
+    100 times per head set, past the 64-occurrence sort, so the value
+    gradient walks its occurrences by repeated minimum search."""
+    wl = synthetic.Workload("bhot", 1, 64, 2, 16, 4, "f32", "random")
+    params, x1, _ = case(wl, 5, True)
+    x = np.repeat(x1, 100, axis=0)
+    dout = np.random.default_rng(6).standard_normal(x.shape).astype(np.float32)
+    wl = wl.with_(B=100)
+    got, idx = gpu_backward(torch, wl, params, x, dout)
+    assert np.bincount(idx.ravel()).max() >= 100
+    ref = oracle.backward(support.model_for(wl, params), x, dout)
+    compare(got, ref)
+
+
+def test_backward_arguments(torch):
+    wl = synthetic.Workload("berr", 4, 64, 1, 16, 4, "f32", "unit")
+    params = synthetic.make_params(wl)
+    mem = pk.Memory(wl.D, wl.H, wl.n, wl.k, wl.table, max_batch=8)
+    P = pk.params_to_device(params, wl.table, support.device())
+    x = torch.zeros((4, wl.D), device=support.device())
+    _, idx, w = mem.forward(P, x)
+    say("backward arguments")
+    small = torch.empty(mem.backward_workspace_bytes() - 256, dtype=torch.uint8, device=support.device())
+    with pytest.raises(pk.PkmError) as e:
+        mem.backward(P, x, idx, w, x, workspace=small)
+    assert e.value.status == pk.PKM_E_ARG
+    with pytest.raises(pk.PkmError):
+        mem.backward(P, x, idx, w, x, grads={"dbn_gamma": torch.zeros((1, wl.D), device=support.device())})
+    g = mem.backward(P, x[:0], idx[:0], w[:0], x[:0])
+    torch.cuda.synchronize()
+    assert g["dx"].shape == (0, wl.D)
+
+
+@pytest.mark.slow
+def test_backward_default_shape(torch):
+    """The pages' default shape (1M-row bf16 table) on 1024 gap-clean tokens;
+    the value gradient is compared on the rows the batch touched and checked
+    whole by its column sums (H * sum_b dout_b)."""
+    wl = synthetic.WORKLOADS["default"].with_(B=1024)
+    params = synthetic.make_params(wl)
+    x = synthetic.make_x(wl)[:1024].copy()
+    support.gap_clean(wl, params, x)
+    dout = np.random.default_rng(1).standard_normal(x.shape).astype(np.float32)
+    got, idx = gpu_backward(torch, wl, params, x, dout, max_batch=512)
+    ref = oracle.backward(support.model_for(wl, params), x, dout)
+    rows = np.unique(idx)
+    touched = dict(got)
+    touched["dvalues"] = got["dvalues"][rows]
+    reff = dict(ref)
+    reff["dval"] = ref["dval"][rows]
+    errs = compare(touched, reff)
+    untouched = np.ones(wl.N, bool)
+    untouched[rows] = False
+    assert not got["dvalues"][untouched].any()
+    want = wl.H * dout.astype(np.float64).sum(0)
+    assert np.abs(got["dvalues"].sum(0, dtype=np.float64) - want).max() <= 1e-4 * np.abs(want).max()
+    print("default backward", {k: f"{v:.2g}" for k, v in errs.items()}, flush=True)
