@@ -169,6 +169,23 @@ def flat_vs_product(torch, pk, wl, P, xt, kt, tokens=64, steps=5, warmup=2):
             "key_scores_per_token_head": {"flat": wl.N, "product": 2 * wl.n}, "candidates_per_token_head": wl.k ** 2}
 
 
+def backward_step(torch, mem, wl, P, xt, idx, wts, fwd_ms, steps, warmup):
+    """The gradients of a loss through the same batch (pkm_backward): every
+    parameter gradient, dx and the dense fp32 value-table gradient."""
+    dout = torch.randn((wl.B, wl.D), dtype=torch.float32, device="cuda", generator=torch.Generator("cuda").manual_seed(1))
+    grads = {"dx": (wl.B, wl.D), "dwq": (wl.H, wl.D, wl.D), "dbn_gamma": (wl.H, wl.D), "dbn_beta": (wl.H, wl.D),
+             "dsubkeys": (wl.H, 2, wl.n, wl.D // 2), "dvalues": (wl.N, wl.D)}
+    grads = {name: torch.zeros(shape, dtype=torch.float32, device="cuda") for name, shape in grads.items()}
+    ws = torch.empty(mem.backward_workspace_bytes(), dtype=torch.uint8, device="cuda")
+    ms = timed_steps(torch, lambda: mem.backward(P, xt, idx, wts, dout, grads, ws), steps, warmup)
+    # GEMM work of the backward: the recomputed q, dWq and dx (2 B H D^2 each)
+    flop = 2.0 * wl.B * wl.H * wl.D * wl.D * 3
+    return {"ms": round(ms, 4), "tokens_per_s": round(wl.B / (ms * 1e-3), 1),
+            "forward_backward_tokens_per_s": round(wl.B / ((ms + fwd_ms) * 1e-3), 1),
+            "gemm_flop": flop, "gemm_tflops_if_all_time": round(flop / (ms * 1e-3) / 1e12, 2),
+            "workspace_bytes": mem.backward_workspace_bytes()}
+
+
 def cpu_baseline(wl, params, x, seconds=10.0):
     """The fp64 oracle on host cores over a bounded sample of the tokens."""
     import oracle
@@ -205,6 +222,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--max-batch", type=int, default=0, help="tokens per internal chunk (0: the whole batch)")
     ap.add_argument("--no-flat", action="store_true", help="skip the flat (brute-force) search comparison")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward (gradient) timing")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -289,6 +307,9 @@ def main():
     }
     if not args.no_flat:
         line["flat_vs_product"] = flat_vs_product(torch, pk, wl, P, xt, kt)
+    if not args.no_backward:
+        line["backward"] = backward_step(torch, mem, wl, P, xt, idx, wts, ms, max(5, args.steps // 5),
+                                         max(2, args.warmup // 5))
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, params, x, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -11,7 +11,9 @@
 //   dq    = dq^ gamma / sqrt(var + eps)           dqhat_kernel
 //   dgamma += dq^ xhat, dbeta += dq^              colsum kernels (token order)
 //   dWq[h] += dq^T x, dx = dq Wq                  fp32 MFMA GEMMs
-//   dC[h,p] += G[h,p] . q^_p                      fp32 MFMA GEMM
+//   dC[h,p,i] += sum_b G[h,p][i][b] q^_p[b]       dsub_kernel (G is ~k/n
+//                                                 dense: a scan per subkey
+//                                                 row, not a GEMM)
 //   dV[r] += sum over the occurrences of r of w dout_b
 //                                                 counting sort by row, then
 //                                                 one owner per row
@@ -179,12 +181,14 @@ __global__ __launch_bounds__(64 * WAVES) void value_backward_kernel(const uint8_
     if (lane < k) dt[pair * k + lane] = my_w * (my_g - wg);
 }
 
-// One wave per (token b, head h) of the chunk:
-//   dq^[d] = sum_j dt_j C[h, p(d), i_p(j), d - p(d) D/2]  (j in order)
-//   dq[d]  = dq^[d] gamma / sqrt(var + eps)
-// and the half-score gradients G[2h+p][i][b] = sum of dt_j over the winners
-// whose half-p index is i (written once, by the first such winner; G is
-// zero elsewhere).  Lane l owns elements l + 64 t.
+// One wave per (token b, head h) of the chunk.  First the half-score
+// gradients: for half p the winners sharing a subkey index i add up,
+//   ds_p[i] = sum of dt_j over the winners j with i_p(j) = i  (j in order),
+// kept by the winner that first uses i (G[2h+p][i][b] = ds_p[i]; G is zero
+// elsewhere).  Then, over the distinct subkeys only (in order of first use),
+//   dq^[d] = sum_i ds_p(d)[i] C[h, p(d), i, d - p(d) D/2]
+//   dq[d]  = dq^[d] gamma / sqrt(var + eps).
+// Lane l owns columns 4 l + 256 t (float4 loads and stores).
 __global__ __launch_bounds__(64 * WAVES) void dqhat_kernel(const float *__restrict__ subkeys,
                                                           const float *__restrict__ var,
                                                           const float *__restrict__ gamma, float eps, int D, int n,
@@ -205,22 +209,8 @@ __global__ __launch_bounds__(64 * WAVES) void dqhat_kernel(const float *__restri
     const float my_dt = lane < k ? dt[pair * k + lane] : 0.0f;
     const int my_a = my_row / n, my_c = my_row - (my_row / n) * n;
 
-    for (int d = lane; d < D; d += 64) {
-        const int p = d >= half;
-        const float *base = subkeys + ((int64_t)h * 2 + p) * n * half + (d - p * half);
-        float acc = 0.0f;
-        for (int j = 0; j < k; ++j) {
-            const int aj = __builtin_amdgcn_readlane(my_a, j), cj = __builtin_amdgcn_readlane(my_c, j);
-            const float dj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_dt), j));
-            acc = fmaf(dj, base[(int64_t)(p ? cj : aj) * half], acc);
-        }
-        const int64_t hd = (int64_t)h * D + d;
-        dqhat[pair * D + d] = acc;
-        dq[pair * D + d] = acc * (gamma[hd] / sqrtf(var[hd] + eps));
-    }
-
     float s0 = 0.0f, s1 = 0.0f;
-    bool first0 = true, first1 = true;
+    bool first0 = lane < k, first1 = lane < k;
     for (int l = 0; l < k; ++l) {
         const int al = __builtin_amdgcn_readlane(my_a, l), cl = __builtin_amdgcn_readlane(my_c, l);
         const float dl = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_dt), l));
@@ -233,9 +223,126 @@ __global__ __launch_bounds__(64 * WAVES) void dqhat_kernel(const float *__restri
             if (l < lane) first1 = false;
         }
     }
-    if (lane < k) {
-        if (first0) G[(((int64_t)h * 2 + 0) * n + my_a) * ldG + b] = s0;
-        if (first1) G[(((int64_t)h * 2 + 1) * n + my_c) * ldG + b] = s1;
+    if (first0) G[(((int64_t)h * 2 + 0) * n + my_a) * ldG + b] = s0;
+    if (first1) G[(((int64_t)h * 2 + 1) * n + my_c) * ldG + b] = s1;
+    const uint64_t distinct0 = __ballot(first0), distinct1 = __ballot(first1);
+
+    const float *c0base = subkeys + ((int64_t)h * 2 + 0) * n * half;
+    const float *c1base = subkeys + ((int64_t)h * 2 + 1) * n * half;
+    for (int col0 = 0; col0 < D; col0 += 256) {
+        const int col = col0 + 4 * lane;
+        const bool active = col < D;
+        const int p = col >= half;
+        const int sub_col = active ? col - p * half : 0;
+        float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        // both halves' lists; a lane takes the entries of its own half
+        for (int q = 0; q < 2; ++q) {
+            uint64_t m = q ? distinct1 : distinct0;
+            const float *base = q ? c1base : c0base;
+            const bool mine = active && p == q;
+            while (m) {
+                const int l = __builtin_ctzll(m);
+                m &= m - 1;
+                const int i = __builtin_amdgcn_readlane(q ? my_c : my_a, l);
+                const float sv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(q ? s1 : s0), l));
+                if (mine) {
+                    const float4 cv = *reinterpret_cast<const float4 *>(base + (int64_t)i * half + sub_col);
+                    acc.x = fmaf(sv, cv.x, acc.x);
+                    acc.y = fmaf(sv, cv.y, acc.y);
+                    acc.z = fmaf(sv, cv.z, acc.z);
+                    acc.w = fmaf(sv, cv.w, acc.w);
+                }
+            }
+        }
+        if (active) {
+            const int64_t hd = (int64_t)h * D + col;
+            const float4 vv = *reinterpret_cast<const float4 *>(var + hd);
+            const float4 gg = *reinterpret_cast<const float4 *>(gamma + hd);
+            *reinterpret_cast<float4 *>(dqhat + pair * D + col) = acc;
+            *reinterpret_cast<float4 *>(dq + pair * D + col) =
+                make_float4(acc.x * (gg.x / sqrtf(vv.x + eps)), acc.y * (gg.y / sqrtf(vv.y + eps)),
+                            acc.z * (gg.z / sqrtf(vv.z + eps)), acc.w * (gg.w / sqrtf(vv.w + eps)));
+        }
+    }
+}
+
+// dC[h,p,i] += sum over tokens b (in order) of G[2h+p][i][b] * q^_p[b]:
+// one wave per subkey row (g = 2h + p, i).  The wave scans its row of G
+// (one token per lane, four 64-token chunks in flight) and, for each
+// non-zero entry, adds ds * q^ with q^ = BN(q) of that token's half p
+// computed on the fly from q.  Columns: lane l owns 4 l + 256 t of the
+// D/2, in passes of 1024.
+__global__ __launch_bounds__(64 * WAVES) void dsub_kernel(const float *__restrict__ G, int64_t ldG, int64_t B,
+                                                         const float *__restrict__ q, int H, int D, int n,
+                                                         const float *__restrict__ mean,
+                                                         const float *__restrict__ var,
+                                                         const float *__restrict__ gamma,
+                                                         const float *__restrict__ beta, float eps,
+                                                         float *__restrict__ dsub)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * WAVES + (threadIdx.x >> 6);  // g * n + i
+    if (row >= (int64_t)2 * H * n) return;
+    const int g = (int)(row / n);
+    const int h = g >> 1, p = g & 1;
+    const int half = D / 2;
+    const int64_t qcol0 = (int64_t)h * D + (int64_t)p * half;  // this half's first column in q's rows
+    const int64_t ldq = (int64_t)H * D;
+    const float *grow = G + row * ldG;
+    float *out = dsub + row * half;
+    for (int c1 = 0; c1 < half; c1 += 1024) {
+        int col[4];
+        bool act[4];
+        float4 mu[4], sc[4], be[4], acc[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int c = c1 + 256 * t + 4 * lane;
+            act[t] = c < half;
+            col[t] = act[t] ? c : 0;
+            const int64_t hd = qcol0 + col[t];
+            const float4 m4 = *reinterpret_cast<const float4 *>(mean + hd);
+            const float4 v4 = *reinterpret_cast<const float4 *>(var + hd);
+            const float4 g4 = *reinterpret_cast<const float4 *>(gamma + hd);
+            mu[t] = m4;
+            sc[t] = make_float4(g4.x / sqrtf(v4.x + eps), g4.y / sqrtf(v4.y + eps), g4.z / sqrtf(v4.z + eps),
+                                g4.w / sqrtf(v4.w + eps));
+            be[t] = *reinterpret_cast<const float4 *>(beta + hd);
+            acc[t] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        }
+        for (int64_t b0 = 0; b0 < B; b0 += 256) {
+            float gv[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int64_t b = b0 + 64 * c + lane;
+                gv[c] = b < B ? grow[b] : 0.0f;
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                uint64_t nz = __ballot(gv[c] != 0.0f);
+                while (nz) {
+                    const int l = __builtin_ctzll(nz);
+                    nz &= nz - 1;
+                    const float ds = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv[c]), l));
+                    const float *qrow = q + (b0 + 64 * c + l) * ldq + qcol0;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const float4 v = act[t] ? *reinterpret_cast<const float4 *>(qrow + col[t])
+                                                : make_float4(0, 0, 0, 0);
+                        acc[t].x = fmaf(ds, (v.x - mu[t].x) * sc[t].x + be[t].x, acc[t].x);
+                        acc[t].y = fmaf(ds, (v.y - mu[t].y) * sc[t].y + be[t].y, acc[t].y);
+                        acc[t].z = fmaf(ds, (v.z - mu[t].z) * sc[t].z + be[t].z, acc[t].z);
+                        acc[t].w = fmaf(ds, (v.w - mu[t].w) * sc[t].w + be[t].w, acc[t].w);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            if (act[t]) {
+                const float4 o = *reinterpret_cast<const float4 *>(out + col[t]);
+                *reinterpret_cast<float4 *>(out + col[t]) =
+                    make_float4(o.x + acc[t].x, o.y + acc[t].y, o.z + acc[t].z, o.w + acc[t].w);
+            }
     }
 }
 
@@ -369,10 +476,13 @@ __global__ __launch_bounds__(256) void fill_lists_kernel(const int32_t *__restri
 }
 
 // dV[r] += sum over the occurrences o of r, in increasing o (token, head,
-// winner), of w[o] * dout[token(o)].  One wave per 64 rows; the wave takes
-// its non-empty rows in turn.  Up to 64 occurrences are put in order by a
-// 64-lane bitonic sort and summed before the row is updated; more are walked
-// by repeated minimum search, each added into the row in turn.
+// winner), of w[o] * dout[token(o)].  One wave per kGradRows rows; the wave
+// takes its non-empty rows in turn.  Up to 64 occurrences are put in order
+// by a 64-lane bitonic sort (lane t holds the t-th) and summed over passes
+// of 1024 columns (lane l: columns 4 l + 256 q, q < 4; the old row and two
+// occurrences' dout rows in flight), then added to the row; more are
+// walked by repeated minimum search, each added into the row in turn.
+constexpr int kGradRows = 16;
 __global__ __launch_bounds__(64 * WAVES) void value_grad_kernel(const uint32_t *__restrict__ count,
                                                                const uint32_t *__restrict__ offs,
                                                                const uint32_t *__restrict__ list, int N, int D,
@@ -382,27 +492,64 @@ __global__ __launch_bounds__(64 * WAVES) void value_grad_kernel(const uint32_t *
 {
     const int lane = threadIdx.x & 63;
     const int64_t group = (int64_t)blockIdx.x * WAVES + (threadIdx.x >> 6);
-    const int64_t r_lane = group * 64 + lane;
-    if (group * 64 >= N) return;
-    const uint32_t my_count = r_lane < N ? count[r_lane] : 0u;
+    if (group * kGradRows >= N) return;
+    const int64_t r_lane = group * kGradRows + lane;
+    const bool mine = lane < kGradRows && r_lane < N;
+    const uint32_t my_count = mine ? count[r_lane] : 0u;
+    const uint32_t my_start = mine ? offs[r_lane] : 0u;
     uint64_t pending = __ballot(my_count > 0);
     while (pending) {
         const int src = __builtin_ctzll(pending);
         pending &= pending - 1;
-        const int64_t r = group * 64 + src;
+        const int64_t r = group * kGradRows + src;
         const uint32_t m = (uint32_t)__builtin_amdgcn_readlane((int)my_count, src);
-        const uint32_t start = offs[r];
+        const uint32_t start = (uint32_t)__builtin_amdgcn_readlane((int)my_start, src);
         float *out = dval + r * D;
         if (m <= 64) {
             const uint32_t id = lane < (int)m ? list[start + lane] : 0xFFFFFFFFu;
-            const uint32_t asc = ~sort64_desc(~id);  // lane t: the t-th smallest id
-            for (int d = lane; d < D; d += 64) {
-                float acc = 0.0f;
-                for (uint32_t t = 0; t < m; ++t) {
-                    const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)asc, (int)t);
-                    acc = fmaf(w[o], dout[(int64_t)(o / per_token) * D + d], acc);
+            const uint32_t asc = m == 1 ? id : ~sort64_desc(~id);  // lane t: the t-th smallest id
+            const float wt = lane < (int)m ? w[asc] : 0.0f;
+            const uint32_t tok = lane < (int)m ? asc / (uint32_t)per_token : 0u;
+            for (int c1 = 0; c1 < D; c1 += 1024) {
+                int col[4];
+                bool act[4];
+                float4 old[4], acc[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int c = c1 + 256 * q + 4 * lane;
+                    act[q] = c < D;
+                    col[q] = act[q] ? c : 0;
+                    old[q] = act[q] ? *reinterpret_cast<const float4 *>(out + col[q]) : make_float4(0, 0, 0, 0);
+                    acc[q] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
                 }
-                out[d] += acc;
+                for (uint32_t t0 = 0; t0 < m; t0 += 2) {
+                    float4 v[2][4];
+                    float wv[2];
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        const int t = (int)min(t0 + u, m - 1);
+                        const float *src_row = dout + (int64_t)(uint32_t)__builtin_amdgcn_readlane((int)tok, t) * D;
+                        wv[u] = t0 + u < m ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wt), t)) : 0.0f;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            v[u][q] = act[q] ? *reinterpret_cast<const float4 *>(src_row + col[q])
+                                             : make_float4(0, 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int u = 0; u < 2; ++u)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            acc[q].x = fmaf(wv[u], v[u][q].x, acc[q].x);
+                            acc[q].y = fmaf(wv[u], v[u][q].y, acc[q].y);
+                            acc[q].z = fmaf(wv[u], v[u][q].z, acc[q].z);
+                            acc[q].w = fmaf(wv[u], v[u][q].w, acc[q].w);
+                        }
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (act[q])
+                        *reinterpret_cast<float4 *>(out + col[q]) = make_float4(
+                            old[q].x + acc[q].x, old[q].y + acc[q].y, old[q].z + acc[q].z, old[q].w + acc[q].w);
             }
         } else {
             // more than 64: walk the occurrences in increasing id (one wave
@@ -417,8 +564,8 @@ __global__ __launch_bounds__(64 * WAVES) void value_grad_kernel(const uint32_t *
                 const uint32_t o = ~(uint32_t)__builtin_amdgcn_readlane((int)sort64_desc(~best), 0);
                 last = o;
                 const float wo = w[o];
-                const float *src = dout + (int64_t)(o / per_token) * D;
-                for (int d = lane; d < D; d += 64) out[d] = fmaf(wo, src[d], out[d]);
+                const float *src_row = dout + (int64_t)(o / per_token) * D;
+                for (int d = lane; d < D; d += 64) out[d] = fmaf(wo, src_row[d], out[d]);
             }
         }
     }
@@ -488,6 +635,16 @@ hipError_t launch_dqhat(const float *subkeys, const float *var, const float *gam
     return hipGetLastError();
 }
 
+hipError_t launch_dsub(const float *G, int64_t ldG, int64_t B, const float *q, int H, int D, int n, const float *mean,
+                       const float *var, const float *gamma, const float *beta, float eps, float *dsub,
+                       hipStream_t st)
+{
+    if (B <= 0) return hipSuccess;
+    hipLaunchKernelGGL(dsub_kernel, dim3(grid_of((int64_t)2 * H * n, WAVES)), dim3(64 * WAVES), 0, st, G, ldG, B, q, H,
+                       D, n, mean, var, gamma, beta, eps, dsub);
+    return hipGetLastError();
+}
+
 int colsum_chunks(int64_t B) { return (int)((B + kColChunk - 1) / kColChunk); }
 
 hipError_t launch_bn_grads(const float *dqhat, const float *q, const float *mean, const float *var, float eps,
@@ -521,8 +678,8 @@ hipError_t launch_value_grad(const int32_t *idx, int64_t M, int N, int D, int pe
     hipLaunchKernelGGL(scan_top_kernel, dim3(1), dim3(256), 0, st, block_sum, (int)nb);
     hipLaunchKernelGGL(scan_apply_kernel, dim3((unsigned)nb), dim3(256), 0, st, count, N, block_sum, offs);
     hipLaunchKernelGGL(fill_lists_kernel, dim3(grid_of(M, 256)), dim3(256), 0, st, idx, M, N, offs, cursor, list);
-    hipLaunchKernelGGL(value_grad_kernel, dim3(grid_of((N + 63) / 64, WAVES)), dim3(64 * WAVES), 0, st, count, offs,
-                       list, N, D, per_token, w, dout, dval);
+    hipLaunchKernelGGL(value_grad_kernel, dim3(grid_of((N + kGradRows - 1) / kGradRows, WAVES)), dim3(64 * WAVES), 0,
+                       st, count, offs, list, N, D, per_token, w, dout, dval);
     return hipGetLastError();
 }
 

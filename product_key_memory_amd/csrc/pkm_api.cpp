@@ -271,7 +271,7 @@ bool backward_layout(const pkm_config &c, size_t sizes[kBwdPieces])
     sizes[4] = round_up(HD * mb32 * f);     // dq transposed
     sizes[5] = round_up(D * mb32 * f);      // x transposed
     sizes[6] = round_up(D * HD * f);        // Wq transposed
-    sizes[7] = round_up(HD * mb32 * f);     // q^ transposed
+    sizes[7] = 0;                           // (unused)
     sizes[8] = round_up(2 * H * n * mb32 * f);  // half-score gradients G
     sizes[9] = round_up((size_t)pkm::colsum_chunks((int64_t)mb) * HD * f);
     sizes[10] = sizes[9];
@@ -534,14 +534,14 @@ pkm_status pkm_backward(pkm_ctx *ctx, const pkm_params *p, int64_t B, const floa
     float *Q = static_cast<float *>(piece[0]), *dt = static_cast<float *>(piece[1]);
     float *dqh = static_cast<float *>(piece[2]), *dq = static_cast<float *>(piece[3]);
     float *dqT = static_cast<float *>(piece[4]), *xT = static_cast<float *>(piece[5]);
-    float *wqT = static_cast<float *>(piece[6]), *qhT = static_cast<float *>(piece[7]);
+    float *wqT = static_cast<float *>(piece[6]);
     float *G = static_cast<float *>(piece[8]);
     float *part_g = static_cast<float *>(piece[9]), *part_b = static_cast<float *>(piece[10]);
     uint32_t *count = static_cast<uint32_t *>(piece[11]), *cursor = static_cast<uint32_t *>(piece[12]);
     uint32_t *offs = static_cast<uint32_t *>(piece[13]), *block_sum = static_cast<uint32_t *>(piece[14]);
     uint32_t *list = static_cast<uint32_t *>(piece[15]);
 
-    const int H = c.heads, D = c.dim, k = c.k, n = c.n_keys, half = D / 2, HD = H * D, N = n * n;
+    const int H = c.heads, D = c.dim, k = c.k, n = c.n_keys, HD = H * D, N = n * n;
     if (grads->dx &&
         (s = launched(pkm::launch_transpose(p->wq, D, HD, D, wqT, HD, HD, nullptr, nullptr, nullptr, nullptr, 0.0f, st),
                       "Wq transpose")))
@@ -597,28 +597,11 @@ pkm_status pkm_backward(pkm_ctx *ctx, const pkm_params *p, int64_t B, const floa
             a.accumulate = true;
             if ((s = launched(pkm::launch_gemm_nt_f32(a, st), "dWq"))) return s;
         }
-        if (grads->dsubkeys) {
-            if ((s = launched(pkm::launch_transpose(Q, HD, (int)nb, HD, qhT, nb32, nb32, p->bn_mean, p->bn_var,
-                                                    p->bn_gamma, p->bn_beta, c.bn_eps, st),
-                              "q^ transpose")))
-                return s;
-            pkm::GemmArgs a{};
-            a.A = G;
-            a.lda = nb32;
-            a.strideA = (int64_t)n * nb32;
-            a.B = qhT;
-            a.ldb = nb32;
-            a.strideB = (int64_t)half * nb32;
-            a.C = grads->dsubkeys;
-            a.ldc = half;
-            a.strideC = (int64_t)n * half;
-            a.M = n;
-            a.N = half;
-            a.K = nb32;
-            a.batch = 2 * H;
-            a.accumulate = true;
-            if ((s = launched(pkm::launch_gemm_nt_f32(a, st), "dsubkeys"))) return s;
-        }
+        if (grads->dsubkeys &&
+            (s = launched(pkm::launch_dsub(G, nb32, nb, Q, H, D, n, p->bn_mean, p->bn_var, p->bn_gamma, p->bn_beta,
+                                           c.bn_eps, grads->dsubkeys, st),
+                          "subkey gradient")))
+            return s;
         if (grads->dx) {
             pkm::GemmArgs a{};
             a.A = dq;

@@ -84,6 +84,11 @@ hipError_t launch_value_backward(const void *values, const float *scale, int val
 hipError_t launch_dqhat(const float *subkeys, const float *var, const float *gamma, float eps, int D, int n, int64_t B,
                         int H, int k, const int32_t *idx, const float *dt, float *dqhat, float *dq, float *G,
                         int64_t ldG, hipStream_t st);
+// dsub [2H][n][D/2] += sum over b < B (in order) of G[g][i][b] * BN(q)[b]
+// restricted to head h = g / 2, half p = g % 2; q [B][H*D] before BN.
+hipError_t launch_dsub(const float *G, int64_t ldG, int64_t B, const float *q, int H, int D, int n, const float *mean,
+                       const float *var, const float *gamma, const float *beta, float eps, float *dsub,
+                       hipStream_t st);
 // dgamma, dbeta [cols] += column sums over B rows of dqhat * xhat and dqhat,
 // xhat = (q - mean) / sqrt(var + eps); part_g / part_b hold
 // colsum_chunks(B) * cols floats each.

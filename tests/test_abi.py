@@ -109,8 +109,8 @@ def test_flat_workspace_bytes():
 
 
 def test_backward_workspace_bytes():
-    """Chunks of max_batch tokens: q, dq^, dq [mb, H*D] and three transposed
-    [.., mb32] operands, x^T, Wq^T, the half-score gradients [2H, n, mb32],
+    """Chunks of max_batch tokens: q, dq^, dq [mb, H*D], dq^T [H*D, mb32],
+    x^T [D, mb32], Wq^T, the half-score gradients [2H, n, mb32],
     the BN partial sums, per-row counts / cursors / offsets and the lists."""
     lib = pk.load_library()
     cfg = pk.make_config(**{**GOOD, "max_batch": 1000})
@@ -120,7 +120,7 @@ def test_backward_workspace_bytes():
     def rnd(x):
         return (x + 255) // 256 * 256
 
-    want = (3 * rnd(mb * HD * 4) + rnd(mb * H * k * 4) + 2 * rnd(HD * mb32 * 4) + rnd(D * mb32 * 4)
+    want = (3 * rnd(mb * HD * 4) + rnd(mb * H * k * 4) + rnd(HD * mb32 * 4) + rnd(D * mb32 * 4)
             + rnd(D * HD * 4) + rnd(2 * H * n * mb32 * 4) + 2 * rnd(((mb + 63) // 64) * HD * 4)
             + 3 * rnd(N * 4) + rnd(((N + 4095) // 4096) * 4) + rnd(mb * H * k * 4))
     got = ctypes.c_size_t()
