@@ -6,4 +6,5 @@ CPU-baseline leg of the benchmark, never by the product path.  It shares no
 code with the HIP library.
 """
 from .oracle import (Model, run, bf16_to_f64, e4m3_to_f64, build, lib_path, load_library,  # noqa: F401
-                     compile_source, select, gather, backward, GRADS)
+                     compile_source, select, gather, backward, GRADS, batch_stats, run_batch_stats,
+                     backward_batch_stats)

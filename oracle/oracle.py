@@ -61,6 +61,12 @@ def load_library(path):
     lib.pkmo_gather.argtypes = [ctypes.POINTER(_Model), ctypes.c_int64, ctypes.c_int] + [ctypes.c_void_p] * 3
     lib.pkmo_backward.restype = ctypes.c_int
     lib.pkmo_backward.argtypes = [ctypes.POINTER(_Model), ctypes.c_int64] + [ctypes.c_void_p] * 8 + [ctypes.c_int]
+    lib.pkmo_batch_stats.restype = ctypes.c_int
+    lib.pkmo_batch_stats.argtypes = [ctypes.POINTER(_Model), ctypes.c_int64] + [ctypes.c_void_p] * 3
+    lib.pkmo_run_batch_stats.restype = ctypes.c_int
+    lib.pkmo_run_batch_stats.argtypes = [ctypes.POINTER(_Model), ctypes.c_int64] + [ctypes.c_void_p] * 7
+    lib.pkmo_backward_batch_stats.restype = ctypes.c_int
+    lib.pkmo_backward_batch_stats.argtypes = [ctypes.POINTER(_Model), ctypes.c_int64] + [ctypes.c_void_p] * 10
     return lib
 
 
@@ -213,6 +219,56 @@ def backward(model, x, dout, want=GRADS, nthreads=None, lib=None):
         nthreads = len(os.sched_getaffinity(0))
     rc = lib.pkmo_backward(ctypes.byref(model._s), B, _ptr(x), _ptr(dout), *[_ptr(res.get(nm)) for nm in GRADS],
                            int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments" if rc == -1 else "oracle ran out of memory")
+    return res
+
+
+def batch_stats(model, x, lib=None):
+    """Training-mode BN statistics of the batch x [B,D]: mean, biased var,
+    each [H,D] fp64."""
+    lib = lib or _load()
+    x = _c(x, np.float32)
+    mean = np.empty((model.H, model.D))
+    var = np.empty((model.H, model.D))
+    if lib.pkmo_batch_stats(ctypes.byref(model._s), x.shape[0], _ptr(x), _ptr(mean), _ptr(var)) != 0:
+        raise ValueError("oracle rejected its arguments")
+    return mean, var
+
+
+def run_batch_stats(model, x, mean, var, want=("out", "idx", "top", "w"), lib=None):
+    """The lookup normalising with the given fp64 statistics [H,D]."""
+    lib = lib or _load()
+    x = _c(x, np.float32)
+    B, H, k = x.shape[0], model.H, model.k
+    if "out" in want and not model.has_values:
+        raise ValueError("the model holds no value table")
+    shapes = {"out": ((B, model.D), np.float64), "idx": ((B, H, k), np.int32), "top": ((B, H, k), np.float64),
+              "w": ((B, H, k), np.float64)}
+    res = {name: np.empty(*shapes[name]) for name in want}
+    mean, var = _c(mean, np.float64), _c(var, np.float64)
+    rc = lib.pkmo_run_batch_stats(ctypes.byref(model._s), B, _ptr(x), _ptr(mean), _ptr(var),
+                                  *[_ptr(res.get(nm)) for nm in ("out", "idx", "top", "w")])
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return res
+
+
+def backward_batch_stats(model, x, dout, mean, var, want=GRADS, lib=None):
+    """Gradients of sum(dout * out) for the lookup with batch statistics
+    (mean, var [H,D] fp64 of this batch): as backward()."""
+    lib = lib or _load()
+    if not model.has_values:
+        raise ValueError("the backward reads the value table")
+    x, dout = _c(x, np.float32), _c(dout, np.float32)
+    B = x.shape[0]
+    H, D, n = model.H, model.D, model.n
+    shapes = {"dx": (B, D), "dwq": (H, D, D), "dgamma": (H, D), "dbeta": (H, D), "dsub": (H, 2, n, D // 2),
+              "dval": (n * n, D)}
+    res = {name: np.empty(shapes[name]) for name in want}
+    mean, var = _c(mean, np.float64), _c(var, np.float64)
+    rc = lib.pkmo_backward_batch_stats(ctypes.byref(model._s), B, _ptr(x), _ptr(dout), _ptr(mean), _ptr(var),
+                                       *[_ptr(res.get(nm)) for nm in GRADS])
     if rc != 0:
         raise ValueError("oracle rejected its arguments" if rc == -1 else "oracle ran out of memory")
     return res

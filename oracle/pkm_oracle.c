@@ -617,3 +617,231 @@ int pkmo_backward(const pkmo_model *M, int64_t B, const float *x, const float *d
     free(qhat); free(xhat); free(dqhat); free(dt); free(w); free(rows); free(th); free(bj); free(oj);
     return 0;
 }
+
+/* ------------------------------------------------- batch-statistics BN */
+
+/*
+ * Training-mode BatchNorm1d ("Product-Key Memory", §Keeping the memory in
+ * use: batch normalisation of the query, computed over the batch):
+ * per head h and feature f, over the B tokens,
+ *   mean = (1/B) sum_b q_bf,   var = (1/B) sum_b (q_bf - mean)^2  (biased,
+ * the normaliser BatchNorm1d uses), q = Wq[h] . x_b in fp64, two passes.
+ * mean, var: [H][D] fp64.  Returns 0, or -1 on bad arguments (B < 1).
+ */
+int pkmo_batch_stats(const pkmo_model *M, int64_t B, const float *x, double *mean, double *var)
+{
+    if (!M || !x || !mean || !var || B < 1) return -1;
+    const int D = M->D, H = M->H;
+    double *col = (double *)malloc(sizeof(double) * (size_t)B);
+    if (!col) return -1;
+    for (int h = 0; h < H; ++h)
+        for (int f = 0; f < D; ++f) {
+            const float *wrow = M->wq + ((int64_t)h * D + f) * D;
+            double sum = 0.0;
+            for (int64_t b = 0; b < B; ++b) {
+                double acc = 0.0;
+                for (int d = 0; d < D; ++d)
+                    acc += (double)wrow[d] * (double)x[b * D + d];
+                col[b] = acc;
+                sum += acc;
+            }
+            const double mu = sum / (double)B;
+            double ss = 0.0;
+            for (int64_t b = 0; b < B; ++b)
+                ss += (col[b] - mu) * (col[b] - mu);
+            mean[(int64_t)h * D + f] = mu;
+            var[(int64_t)h * D + f] = ss / (double)B;
+        }
+    free(col);
+    return 0;
+}
+
+/* A copy of the model whose BN statistics are the given fp64 ones: the
+ * per-token steps read them through these arrays instead. */
+typedef struct {
+    const double *mean, *var; /* [H][D] */
+} stats64;
+
+static void project_bn_stats(const pkmo_model *M, const stats64 *S, int h, const float *x_b, double *qhat,
+                             double *xhat)
+{
+    const int D = M->D;
+    for (int f = 0; f < D; ++f) {
+        const float *wrow = M->wq + ((int64_t)h * D + f) * D;
+        double acc = 0.0;
+        for (int d = 0; d < D; ++d)
+            acc += (double)wrow[d] * (double)x_b[d];
+        const int64_t at = (int64_t)h * D + f;
+        const double xh = (acc - S->mean[at]) / sqrt(S->var[at] + M->eps);
+        if (xhat) xhat[f] = xh;
+        qhat[f] = xh * (double)M->gamma[at] + (double)M->beta[at];
+    }
+}
+
+/*
+ * The lookup with batch statistics: steps 1-2 normalise with mean / var
+ * (from pkmo_batch_stats), steps 3-7 are the same as pkmo_run's.  Outputs as
+ * pkmo_run (out [B][D], idx / top / w [B][H][k]; any may be NULL).
+ */
+int pkmo_run_batch_stats(const pkmo_model *M, int64_t B, const float *x, const double *mean, const double *var,
+                         double *out, int32_t *idx, double *top, double *w)
+{
+    if (!M || !x || !mean || !var || B < 1) return -1;
+    if (out && !M->values) return -1;
+    const int D = M->D, H = M->H, n = M->n, k = M->k;
+    const stats64 S = {mean, var};
+    double *q = (double *)malloc(sizeof(double) * (size_t)D);
+    double *s = (double *)malloc(sizeof(double) * 2 * (size_t)n);
+    double *t0 = (double *)malloc(sizeof(double) * (size_t)k), *t1 = (double *)malloc(sizeof(double) * (size_t)k);
+    int32_t *i0 = (int32_t *)malloc(sizeof(int32_t) * (size_t)k), *i1 = (int32_t *)malloc(sizeof(int32_t) * (size_t)k);
+    double *tp = (double *)malloc(sizeof(double) * (size_t)k), *wj = (double *)malloc(sizeof(double) * (size_t)k);
+    int32_t *fl = (int32_t *)malloc(sizeof(int32_t) * (size_t)k);
+    for (int64_t b = 0; b < B; ++b) {
+        if (out)
+            for (int d = 0; d < D; ++d)
+                out[b * D + d] = 0.0;
+        for (int h = 0; h < H; ++h) {
+            project_bn_stats(M, &S, h, x + b * D, q, NULL);
+            pkmo_half_scores(M, h, q, s);
+            pkmo_topk_sorted(n, s, k, t0, i0);
+            pkmo_topk_sorted(n, s + n, k, t1, i1);
+            pkmo_candidates_topk(n, k, t0, i0, t1, i1, k, tp, fl);
+            pkmo_softmax(k, tp, wj);
+            const int64_t bh = b * H + h;
+            if (idx) memcpy(idx + bh * k, fl, sizeof(int32_t) * (size_t)k);
+            if (top) memcpy(top + bh * k, tp, sizeof(double) * (size_t)k);
+            if (w) memcpy(w + bh * k, wj, sizeof(double) * (size_t)k);
+            if (out) pkmo_gather_add(M, k, fl, wj, out + b * D);
+        }
+    }
+    free(q); free(s); free(t0); free(t1); free(i0); free(i1); free(tp); free(wj); free(fl);
+    return 0;
+}
+
+/*
+ * Gradients of sum(dout * out) for the lookup with batch statistics.  The
+ * statistics depend on every token, so BN's backward couples them: with
+ * xhat = (q - mean)/sqrt(var + eps) and, per feature, the batch means
+ *   m1 = (1/B) sum_b dq^_b ,   m2 = (1/B) sum_b dq^_b xhat_b ,
+ *   dgamma = B m2 ,  dbeta = B m1 ,
+ *   dq_b = gamma / sqrt(var + eps) * (dq^_b - m1 - xhat_b m2).
+ * Everything else is the running-statistics backward (pkmo_backward).
+ * Outputs as pkmo_backward (overwritten; any may be NULL).
+ */
+int pkmo_backward_batch_stats(const pkmo_model *M, int64_t B, const float *x, const float *dout, const double *mean,
+                              const double *var, double *dx, double *dwq, double *dgamma, double *dbeta,
+                              double *dsub, double *dval)
+{
+    if (!M || !x || !dout || !mean || !var || B < 1 || !M->values) return -1;
+    const int D = M->D, H = M->H, n = M->n, k = M->k, half = D / 2;
+    const int64_t N = (int64_t)n * n;
+    const stats64 S = {mean, var};
+    const size_t bhd = (size_t)B * H * D;
+    double *qhat = (double *)malloc(sizeof(double) * bhd), *xhat = (double *)malloc(sizeof(double) * bhd);
+    double *dqh = (double *)malloc(sizeof(double) * bhd);
+    double *dtv = (double *)malloc(sizeof(double) * (size_t)B * H * k), *wv = (double *)malloc(sizeof(double) * (size_t)B * H * k);
+    int32_t *rows = (int32_t *)malloc(sizeof(int32_t) * (size_t)B * H * k);
+    double *s = (double *)malloc(sizeof(double) * 2 * (size_t)n);
+    double *t0 = (double *)malloc(sizeof(double) * (size_t)k), *t1 = (double *)malloc(sizeof(double) * (size_t)k);
+    int32_t *i0 = (int32_t *)malloc(sizeof(int32_t) * (size_t)k), *i1 = (int32_t *)malloc(sizeof(int32_t) * (size_t)k);
+    double *tp = (double *)malloc(sizeof(double) * (size_t)k), *g = (double *)malloc(sizeof(double) * (size_t)k);
+    double *m1 = (double *)malloc(sizeof(double) * (size_t)H * D), *m2 = (double *)malloc(sizeof(double) * (size_t)H * D);
+    if (!qhat || !xhat || !dqh || !dtv || !wv || !rows || !s || !t0 || !t1 || !i0 || !i1 || !tp || !g || !m1 || !m2)
+        return -2;
+    /* per token: forward again, then back to dq^ (as pkmo_backward) */
+    for (int64_t b = 0; b < B; ++b)
+        for (int h = 0; h < H; ++h) {
+            const int64_t bh = b * H + h;
+            double *qh = qhat + bh * D, *xh = xhat + bh * D, *dq_h = dqh + bh * D;
+            double *dtj = dtv + bh * k, *wj = wv + bh * k;
+            int32_t *rj = rows + bh * k;
+            project_bn_stats(M, &S, h, x + b * D, qh, xh);
+            pkmo_half_scores(M, h, qh, s);
+            pkmo_topk_sorted(n, s, k, t0, i0);
+            pkmo_topk_sorted(n, s + n, k, t1, i1);
+            pkmo_candidates_topk(n, k, t0, i0, t1, i1, k, tp, rj);
+            pkmo_softmax(k, tp, wj);
+            double wg = 0.0;
+            for (int j = 0; j < k; ++j) {
+                double acc = 0.0;
+                for (int d = 0; d < D; ++d)
+                    acc += (double)dout[b * D + d] * value_at(M, rj[j], d);
+                g[j] = acc;
+                wg += wj[j] * acc;
+            }
+            for (int j = 0; j < k; ++j)
+                dtj[j] = wj[j] * g[j] - wj[j] * wg;
+            for (int d = 0; d < D; ++d)
+                dq_h[d] = 0.0;
+            for (int j = 0; j < k; ++j) {
+                const float *c0 = M->subkeys + (((int64_t)h * 2 + 0) * n + rj[j] / n) * half;
+                const float *c1 = M->subkeys + (((int64_t)h * 2 + 1) * n + rj[j] % n) * half;
+                for (int d = 0; d < half; ++d) {
+                    dq_h[d] += dtj[j] * (double)c0[d];
+                    dq_h[half + d] += dtj[j] * (double)c1[d];
+                }
+            }
+        }
+    /* batch means of dq^ and dq^ xhat, in token order */
+    for (int64_t hf = 0; hf < (int64_t)H * D; ++hf) {
+        const int h = (int)(hf / D), f = (int)(hf % D);
+        double a = 0.0, c = 0.0;
+        for (int64_t b = 0; b < B; ++b) {
+            const int64_t at = (b * H + h) * D + f;
+            a += dqh[at];
+            c += dqh[at] * xhat[at];
+        }
+        m1[hf] = a / (double)B;
+        m2[hf] = c / (double)B;
+        if (dbeta) dbeta[hf] = a;
+        if (dgamma) dgamma[hf] = c;
+    }
+    /* dq, then dx and dWq */
+    if (dx)
+        for (int64_t i = 0; i < B * D; ++i)
+            dx[i] = 0.0;
+    if (dwq)
+        for (int64_t i = 0; i < (int64_t)H * D * D; ++i)
+            dwq[i] = 0.0;
+    for (int64_t b = 0; b < B; ++b)
+        for (int h = 0; h < H; ++h)
+            for (int f = 0; f < D; ++f) {
+                const int64_t hf = (int64_t)h * D + f, at = (b * H + h) * D + f;
+                const double dq = (double)M->gamma[hf] / sqrt(var[hf] + M->eps) *
+                                  (dqh[at] - m1[hf] - xhat[at] * m2[hf]);
+                const float *wrow = M->wq + hf * D;
+                for (int d = 0; d < D; ++d) {
+                    if (dx) dx[b * D + d] += dq * (double)wrow[d];
+                    if (dwq) dwq[hf * D + d] += dq * (double)x[b * D + d];
+                }
+            }
+    /* subkeys and values: as with running statistics */
+    if (dsub) {
+        for (int64_t i = 0; i < (int64_t)H * 2 * n * half; ++i)
+            dsub[i] = 0.0;
+        for (int64_t b = 0; b < B; ++b)
+            for (int h = 0; h < H; ++h) {
+                const int64_t bh = b * H + h;
+                for (int j = 0; j < k; ++j) {
+                    const int r = rows[bh * k + j];
+                    double *o0 = dsub + (((int64_t)h * 2 + 0) * n + r / n) * half;
+                    double *o1 = dsub + (((int64_t)h * 2 + 1) * n + r % n) * half;
+                    for (int d = 0; d < half; ++d) {
+                        o0[d] += dtv[bh * k + j] * qhat[bh * D + d];
+                        o1[d] += dtv[bh * k + j] * qhat[bh * D + half + d];
+                    }
+                }
+            }
+    }
+    if (dval) {
+        for (int64_t i = 0; i < N * D; ++i)
+            dval[i] = 0.0;
+        for (int64_t bh = 0; bh < B * H; ++bh)
+            for (int j = 0; j < k; ++j)
+                for (int d = 0; d < D; ++d)
+                    dval[(int64_t)rows[bh * k + j] * D + d] += wv[bh * k + j] * (double)dout[(bh / H) * D + d];
+    }
+    free(qhat); free(xhat); free(dqh); free(dtv); free(wv); free(rows); free(s); free(t0); free(t1);
+    free(i0); free(i1); free(tp); free(g); free(m1); free(m2);
+    return 0;
+}

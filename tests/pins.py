@@ -254,9 +254,11 @@ def pin_op_counts(lib=None):
 
 # ------------------------------------------------------------------ backward
 
-def module_autograd(params, x, dout, k, table="f32", eps=1e-5):
+def module_autograd(params, x, dout, k, table="f32", eps=1e-5, training=False):
     """Gradients of sum(dout * out) by torch autograd in fp64 through the
-    page's code listing, composed per head and summed over heads."""
+    page's code listing, composed per head and summed over heads.  With
+    training=True BatchNorm1d normalises with the batch's statistics (and
+    the result holds "out", "mean" and "var" too)."""
     leaf = lambda a: torch.from_numpy(np.ascontiguousarray(a)).double().requires_grad_()  # noqa: E731
     wq, gamma, beta, sub = leaf(params["wq"]), leaf(params["gamma"]), leaf(params["beta"]), leaf(params["subkeys"])
     vals = dequant_table(params["values"], params.get("scale"), table).clone().requires_grad_()
@@ -266,9 +268,15 @@ def module_autograd(params, x, dout, k, table="f32", eps=1e-5):
     H, D, _ = wq.shape
     n = sub.shape[2]
     out = torch.zeros(x.shape[0], D, dtype=torch.float64)
+    stats = ([], [])
     for h in range(H):
         q = F.linear(xt, wq[h])
-        qh = F.batch_norm(q, mean[h], var[h], gamma[h], beta[h], training=False, eps=eps)
+        if training:
+            stats[0].append(q.detach().mean(0))
+            stats[1].append(q.detach().var(0, unbiased=False))
+            qh = F.batch_norm(q, None, None, gamma[h], beta[h], training=True, eps=eps)
+        else:
+            qh = F.batch_norm(q, mean[h], var[h], gamma[h], beta[h], training=False, eps=eps)
         q1, q2 = qh.chunk(2, dim=1)
         s1, i1 = (q1 @ sub[h, 0].T).topk(k, dim=1)
         s2, i2 = (q2 @ sub[h, 1].T).topk(k, dim=1)
@@ -278,8 +286,11 @@ def module_autograd(params, x, dout, k, table="f32", eps=1e-5):
         w = top.softmax(dim=-1)
         out = out + F.embedding_bag(all_idx.gather(1, pos), vals, per_sample_weights=w, mode="sum")
     (out * torch.from_numpy(dout).double()).sum().backward()
-    return {"dx": xt.grad.numpy(), "dwq": wq.grad.numpy(), "dgamma": gamma.grad.numpy(),
-            "dbeta": beta.grad.numpy(), "dsub": sub.grad.numpy(), "dval": vals.grad.numpy()}
+    res = {"dx": xt.grad.numpy(), "dwq": wq.grad.numpy(), "dgamma": gamma.grad.numpy(),
+           "dbeta": beta.grad.numpy(), "dsub": sub.grad.numpy(), "dval": vals.grad.numpy()}
+    if training:
+        res.update(out=out.detach().numpy(), mean=torch.stack(stats[0]).numpy(), var=torch.stack(stats[1]).numpy())
+    return res
 
 
 def backward_case(wl, seed=0, gamma_beta=False):
@@ -365,3 +376,62 @@ def pin_backward_identities(lib=None):
     z = oracle.backward(model, x, np.zeros_like(dout), lib=lib)
     for name in oracle.GRADS:
         assert not z[name].any(), name
+
+
+
+def pin_batch_stats_autograd(wl, seed=0, lib=None):
+    """Batch-statistics BN: the oracle's statistics, forward output and
+    gradients == torch (F.batch_norm(training=True)) in fp64 through the
+    page's module."""
+    params, x, dout = backward_case(wl, seed, gamma_beta=True)
+    model = _model(params, wl.k, wl.table)
+    mean, var = oracle.batch_stats(model, x, lib=lib)
+    ref = module_autograd(params, x, dout, wl.k, wl.table, training=True)
+    np.testing.assert_allclose(mean, ref["mean"], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(var, ref["var"], rtol=1e-12, atol=1e-12)
+    r = oracle.run_batch_stats(model, x, mean, var, lib=lib)
+    np.testing.assert_allclose(r["out"], ref["out"], rtol=1e-10, atol=1e-12)
+    g = oracle.backward_batch_stats(model, x, dout, mean, var, lib=lib)
+    for name in oracle.GRADS:
+        scale = max(np.abs(ref[name]).max(), 1e-300)
+        err = np.abs(g[name] - ref[name]).max() / scale
+        assert err <= 1e-10, f"{name}: max error {err:.3g} of its largest entry"
+    return g
+
+
+def pin_batch_stats_finite_differences(lib=None, coords=8):
+    """Central differences of the batch-statistics loss (statistics
+    recomputed at every step) against the batch-statistics gradients."""
+    wl = synthetic.Workload("fdb", 6, 16, 2, 8, 3, "f32", "unit")
+    params, x, dout = backward_case(wl, 7, gamma_beta=True)
+
+    def loss():
+        model = _model(params, wl.k, wl.table)
+        mean, var = oracle.batch_stats(model, x, lib=lib)
+        r = oracle.run_batch_stats(model, x, mean, var, want=("out", "idx"), lib=lib)
+        return float((r["out"] * dout.astype(np.float64)).sum()), r["idx"]
+
+    model = _model(params, wl.k, wl.table)
+    mean, var = oracle.batch_stats(model, x, lib=lib)
+    g = oracle.backward_batch_stats(model, x, dout, mean, var, lib=lib)
+    _, idx0 = loss()
+    rng = np.random.default_rng(13)
+    checked = skipped = 0
+    for gname, arr in (("dx", x), ("dwq", params["wq"]), ("dgamma", params["gamma"]), ("dbeta", params["beta"]),
+                       ("dsub", params["subkeys"])):
+        flat = g[gname].reshape(-1)
+        for c in list(np.argsort(-np.abs(flat))[:coords // 2]) + list(rng.integers(0, flat.size, coords // 2)):
+            base = arr.reshape(-1)[c]
+            step = np.float32(2.0 ** -14)
+            vals = []
+            for v in (np.float32(base + step), np.float32(base - step)):
+                arr.reshape(-1)[c] = v
+                vals.append(loss())
+            arr.reshape(-1)[c] = base
+            if not (np.array_equal(vals[0][1], idx0) and np.array_equal(vals[1][1], idx0)):
+                skipped += 1
+                continue
+            fd = (vals[0][0] - vals[1][0]) / (2.0 * float(step))
+            assert abs(fd - flat[c]) <= 1e-6 + 1e-5 * abs(flat[c]), f"{gname}[{c}]: fd {fd} vs {flat[c]}"
+            checked += 1
+    assert skipped * 5 <= checked + skipped

@@ -46,3 +46,16 @@ def test_backward_thread_count_does_not_change_bits():
     b = oracle.backward(model, x, dout, nthreads=7)
     for name in oracle.GRADS:
         assert np.array_equal(a[name], b[name]), name
+
+
+@pytest.mark.parametrize("wl", [
+    synthetic.Workload("bs1", 24, 64, 3, 20, 5, "f32", "random"),
+    synthetic.Workload("bs2", 16, 128, 2, 24, 6, "e4m3", "random"),
+    synthetic.Workload("bs3", 2, 32, 1, 8, 4, "bf16", "unit"),     # the smallest batch with a variance
+])
+def test_batch_stats_match_torch(wl):
+    pins.pin_batch_stats_autograd(wl)
+
+
+def test_batch_stats_finite_differences():
+    pins.pin_batch_stats_finite_differences()

@@ -44,6 +44,11 @@ MUTATIONS = {
     "bwd_dval_unweighted": ("J->dval[r * D + d] += J->w[bh * k + j] * (double)gb[d];",
                             "J->dval[r * D + d] += (double)gb[d];"),
     "bwd_g_from_first_row": ("acc += (double)gb[d] * value_at(M, rj[j], d);", "acc += (double)gb[d] * value_at(M, rj[0], d);"),
+    # batch statistics
+    "bs_unbiased_var": ("var[(int64_t)h * D + f] = ss / (double)B;", "var[(int64_t)h * D + f] = ss / (double)(B - 1);"),
+    "bs_xhat_no_eps": ("/ sqrt(S->var[at] + M->eps);", "/ sqrt(S->var[at]);"),
+    "bs_dq_without_mean_term": ("(dqh[at] - m1[hf] - xhat[at] * m2[hf])", "(dqh[at] - xhat[at] * m2[hf])"),
+    "bs_dq_without_xhat_term": ("(dqh[at] - m1[hf] - xhat[at] * m2[hf])", "(dqh[at] - m1[hf])"),
 }
 
 PINS = [
@@ -62,6 +67,8 @@ PINS = [
     lambda lib: pins.pin_backward_autograd(pins.synthetic.Workload("gb", 24, 64, 3, 20, 5, "f32", "random"),
                                            gamma_beta=True, lib=lib),
     pins.pin_backward_finite_differences,
+    lambda lib: pins.pin_batch_stats_autograd(pins.synthetic.Workload("bs", 24, 64, 3, 20, 5, "f32", "random"),
+                                              lib=lib),
 ]
 
 
