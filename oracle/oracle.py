@@ -24,8 +24,9 @@ def lib_path():
 def build():
     """Compile the oracle with gcc: -O2, no -ffast-math, so every fp64 sum
     keeps the order written in the source."""
-    compile_source(_SRC, _LIB + ".tmp")
-    os.replace(_LIB + ".tmp", _LIB)
+    tmp = f"{_LIB}.{os.getpid()}.tmp"  # parallel test workers may build at once
+    compile_source(_SRC, tmp)
+    os.replace(tmp, _LIB)
     global _lib
     _lib = None
     return _LIB
@@ -64,7 +65,8 @@ def load_library(path):
     lib.pkmo_batch_stats.restype = ctypes.c_int
     lib.pkmo_batch_stats.argtypes = [ctypes.POINTER(_Model), ctypes.c_int64] + [ctypes.c_void_p] * 3
     lib.pkmo_run_batch_stats.restype = ctypes.c_int
-    lib.pkmo_run_batch_stats.argtypes = [ctypes.POINTER(_Model), ctypes.c_int64] + [ctypes.c_void_p] * 7
+    lib.pkmo_run_batch_stats.argtypes = [ctypes.POINTER(_Model), ctypes.c_int64, ctypes.c_void_p, ctypes.c_int] + \
+        [ctypes.c_void_p] * 7
     lib.pkmo_backward_batch_stats.restype = ctypes.c_int
     lib.pkmo_backward_batch_stats.argtypes = [ctypes.POINTER(_Model), ctypes.c_int64] + [ctypes.c_void_p] * 10
     return lib
@@ -236,19 +238,22 @@ def batch_stats(model, x, lib=None):
     return mean, var
 
 
-def run_batch_stats(model, x, mean, var, want=("out", "idx", "top", "w"), lib=None):
-    """The lookup normalising with the given fp64 statistics [H,D]."""
+def run_batch_stats(model, x, mean, var, kk=None, want=("out", "idx", "top", "w"), lib=None):
+    """The lookup normalising with the given fp64 statistics [H,D], at
+    search depth kk (default k).  out [B,D], idx / top / w [B,H,kk],
+    qhat [B,H,D] as requested."""
     lib = lib or _load()
     x = _c(x, np.float32)
-    B, H, k = x.shape[0], model.H, model.k
+    B, H = x.shape[0], model.H
+    kk = model.k if kk is None else int(kk)
     if "out" in want and not model.has_values:
         raise ValueError("the model holds no value table")
-    shapes = {"out": ((B, model.D), np.float64), "idx": ((B, H, k), np.int32), "top": ((B, H, k), np.float64),
-              "w": ((B, H, k), np.float64)}
+    shapes = {"out": ((B, model.D), np.float64), "idx": ((B, H, kk), np.int32), "top": ((B, H, kk), np.float64),
+              "w": ((B, H, kk), np.float64), "qhat": ((B, H, model.D), np.float64)}
     res = {name: np.empty(*shapes[name]) for name in want}
     mean, var = _c(mean, np.float64), _c(var, np.float64)
-    rc = lib.pkmo_run_batch_stats(ctypes.byref(model._s), B, _ptr(x), _ptr(mean), _ptr(var),
-                                  *[_ptr(res.get(nm)) for nm in ("out", "idx", "top", "w")])
+    rc = lib.pkmo_run_batch_stats(ctypes.byref(model._s), B, _ptr(x), kk, _ptr(mean), _ptr(var),
+                                  *[_ptr(res.get(nm)) for nm in ("out", "idx", "top", "w", "qhat")])
     if rc != 0:
         raise ValueError("oracle rejected its arguments")
     return res

@@ -680,22 +680,24 @@ static void project_bn_stats(const pkmo_model *M, const stats64 *S, int h, const
 
 /*
  * The lookup with batch statistics: steps 1-2 normalise with mean / var
- * (from pkmo_batch_stats), steps 3-7 are the same as pkmo_run's.  Outputs as
- * pkmo_run (out [B][D], idx / top / w [B][H][k]; any may be NULL).
+ * (from pkmo_batch_stats), steps 3-7 are the same as pkmo_run's, at search
+ * depth kk (out and w need kk == k).  Outputs as pkmo_run: out [B][D],
+ * idx / top / w [B][H][kk], qhat [B][H][D]; any may be NULL.
  */
-int pkmo_run_batch_stats(const pkmo_model *M, int64_t B, const float *x, const double *mean, const double *var,
-                         double *out, int32_t *idx, double *top, double *w)
+int pkmo_run_batch_stats(const pkmo_model *M, int64_t B, const float *x, int kk, const double *mean,
+                         const double *var, double *out, int32_t *idx, double *top, double *w, double *qhat)
 {
-    if (!M || !x || !mean || !var || B < 1) return -1;
+    if (!M || !x || !mean || !var || B < 1 || kk < 1 || kk > M->n) return -1;
+    if ((out || w) && kk != M->k) return -1;
     if (out && !M->values) return -1;
-    const int D = M->D, H = M->H, n = M->n, k = M->k;
+    const int D = M->D, H = M->H, n = M->n;
     const stats64 S = {mean, var};
     double *q = (double *)malloc(sizeof(double) * (size_t)D);
     double *s = (double *)malloc(sizeof(double) * 2 * (size_t)n);
-    double *t0 = (double *)malloc(sizeof(double) * (size_t)k), *t1 = (double *)malloc(sizeof(double) * (size_t)k);
-    int32_t *i0 = (int32_t *)malloc(sizeof(int32_t) * (size_t)k), *i1 = (int32_t *)malloc(sizeof(int32_t) * (size_t)k);
-    double *tp = (double *)malloc(sizeof(double) * (size_t)k), *wj = (double *)malloc(sizeof(double) * (size_t)k);
-    int32_t *fl = (int32_t *)malloc(sizeof(int32_t) * (size_t)k);
+    double *t0 = (double *)malloc(sizeof(double) * (size_t)kk), *t1 = (double *)malloc(sizeof(double) * (size_t)kk);
+    int32_t *i0 = (int32_t *)malloc(sizeof(int32_t) * (size_t)kk), *i1 = (int32_t *)malloc(sizeof(int32_t) * (size_t)kk);
+    double *tp = (double *)malloc(sizeof(double) * (size_t)kk), *wj = (double *)malloc(sizeof(double) * (size_t)kk);
+    int32_t *fl = (int32_t *)malloc(sizeof(int32_t) * (size_t)kk);
     for (int64_t b = 0; b < B; ++b) {
         if (out)
             for (int d = 0; d < D; ++d)
@@ -703,15 +705,18 @@ int pkmo_run_batch_stats(const pkmo_model *M, int64_t B, const float *x, const d
         for (int h = 0; h < H; ++h) {
             project_bn_stats(M, &S, h, x + b * D, q, NULL);
             pkmo_half_scores(M, h, q, s);
-            pkmo_topk_sorted(n, s, k, t0, i0);
-            pkmo_topk_sorted(n, s + n, k, t1, i1);
-            pkmo_candidates_topk(n, k, t0, i0, t1, i1, k, tp, fl);
-            pkmo_softmax(k, tp, wj);
+            pkmo_topk_sorted(n, s, kk, t0, i0);
+            pkmo_topk_sorted(n, &s[n], kk, t1, i1);
+            pkmo_candidates_topk(n, kk, t0, i0, t1, i1, kk, tp, fl);
             const int64_t bh = b * H + h;
-            if (idx) memcpy(idx + bh * k, fl, sizeof(int32_t) * (size_t)k);
-            if (top) memcpy(top + bh * k, tp, sizeof(double) * (size_t)k);
-            if (w) memcpy(w + bh * k, wj, sizeof(double) * (size_t)k);
-            if (out) pkmo_gather_add(M, k, fl, wj, out + b * D);
+            if (qhat) memcpy(qhat + bh * D, q, sizeof(double) * (size_t)D);
+            if (idx) memcpy(idx + bh * kk, fl, sizeof(int32_t) * (size_t)kk);
+            if (top) memcpy(top + bh * kk, tp, sizeof(double) * (size_t)kk);
+            if (w || out) {
+                pkmo_softmax(kk, tp, wj);
+                if (w) memcpy(w + bh * kk, wj, sizeof(double) * (size_t)kk);
+                if (out) pkmo_gather_add(M, kk, fl, wj, out + b * D);
+            }
         }
     }
     free(q); free(s); free(t0); free(t1); free(i0); free(i1); free(tp); free(wj); free(fl);

@@ -77,6 +77,31 @@ def gap_clean(wl, params, x, tokens=None, seed=0, max_attempts=60):
     raise RuntimeError("gap-clean draw did not converge")
 
 
+def gap_clean_batch_stats(wl, params, x, seed=0, max_rounds=60):
+    """gap_clean for the lookup with batch statistics: re-drawing a token
+    moves every token's statistics, so the gaps of the whole batch are
+    measured again after each round of re-draws.  Returns (mean, var) of
+    the final batch (fp64 [H,D]) and the tau of every (token, head)."""
+    model = model_for(wl, params)
+    attempts = np.zeros(x.shape[0], dtype=np.int64)
+    k = wl.k
+    for _ in range(max_rounds):
+        mean, var = oracle.batch_stats(model, x)
+        r = oracle.run_batch_stats(model, x, mean, var, kk=k + 1, want=("top", "idx", "qhat"))
+        gap = r["top"][:, :, k - 1] - r["top"][:, :, k]
+        tau = np.empty((x.shape[0], wl.H))
+        for b in range(x.shape[0]):
+            for h in range(wl.H):
+                tau[b, h] = max(TAU_ABS, TAU_REL * key_l1_mass(wl, params, r["qhat"][b, h], r["idx"][b, h, k - 1], h))
+        bad = np.nonzero((gap < tau).any(axis=1))[0]
+        if bad.size == 0:
+            return mean, var, tau
+        for b in bad:
+            attempts[b] += 1
+            x[b] = synthetic.redraw_row(wl, seed, b, attempts[b])
+    raise RuntimeError("gap-clean draw with batch statistics did not converge")
+
+
 def rel_rowmax_err(got, ref):
     """Per row: max |got - ref| / max |ref|."""
     got = np.asarray(got, np.float64)
