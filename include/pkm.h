@@ -211,6 +211,34 @@ pkm_status pkm_backward(pkm_ctx *ctx, const pkm_params *p, int64_t B, const floa
                         const float *weights, const float *dout, const pkm_grads *grads, void *workspace,
                         size_t workspace_bytes, void *stream);
 
+/* The lookup with training-mode BatchNorm: the query is normalised with the
+ * statistics of this batch ("Product-Key Memory", §Keeping the memory in
+ * use: batch normalisation of the queries), the one step that couples the
+ * tokens.  Per head h and feature f over the B tokens: mean and biased
+ * variance of q = Wq[h] . x_b (two passes, fixed order), then
+ * q^ = (q - mean) / sqrt(var + eps) * gamma + beta; steps a3-a7 as in
+ * pkm_forward.  2 <= B <= max_batch (one pass over the whole batch).
+ *   batch_mean, batch_var  [H, D] fp32, written (biased variance)
+ *   running_mean, running_var  [H, D] fp32 or both NULL: updated as
+ *       r = (1 - momentum) r + momentum s, the variance unbiased (s * B/(B-1))
+ *   momentum  in [0, 1] (BatchNorm1d's default is 0.1)
+ * p->bn_mean and p->bn_var are not read.  Other arguments as pkm_forward. */
+pkm_status pkm_forward_batch_stats(pkm_ctx *ctx, const pkm_params *p, int64_t B, const float *x, float *out,
+                                   int32_t *idx, float *weights, float *batch_mean, float *batch_var,
+                                   float *running_mean, float *running_var, float momentum, void *stream);
+
+/* pkm_backward for a forward with batch statistics (batch_mean, batch_var
+ * as pkm_forward_batch_stats wrote them).  BN's backward then couples the
+ * tokens: with xhat = (q - mean)/sqrt(var + eps) and the batch sums
+ * sb = sum_b dq^_b, sg = sum_b dq^_b xhat_b,
+ *   dq_b = gamma / sqrt(var + eps) * (dq^_b - sb/B - xhat_b sg/B),
+ * dgamma += sg, dbeta += sb.  2 <= B <= max_batch.  p->bn_mean and
+ * p->bn_var are not read.  Other arguments as pkm_backward. */
+pkm_status pkm_backward_batch_stats(pkm_ctx *ctx, const pkm_params *p, int64_t B, const float *x,
+                                    const int32_t *idx, const float *weights, const float *dout,
+                                    const float *batch_mean, const float *batch_var, const pkm_grads *grads,
+                                    void *workspace, size_t workspace_bytes, void *stream);
+
 /* A static description of a status code. */
 const char *pkm_status_str(pkm_status s);
 

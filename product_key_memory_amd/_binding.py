@@ -17,7 +17,8 @@ VALUE_TYPES = {"f32": 0, "bf16": 1, "e4m3": 2}
 EXPORTS = (
     "pkm_config_check", "pkm_workspace_bytes", "pkm_create", "pkm_destroy", "pkm_forward", "pkm_query",
     "pkm_score", "pkm_select", "pkm_gather", "pkm_flat_workspace_bytes", "pkm_flat_search",
-    "pkm_backward_workspace_bytes", "pkm_backward", "pkm_status_str", "pkm_last_error",
+    "pkm_backward_workspace_bytes", "pkm_backward", "pkm_forward_batch_stats", "pkm_backward_batch_stats",
+    "pkm_status_str", "pkm_last_error",
 )
 
 
@@ -66,6 +67,9 @@ def load_library(path=LIB_PATH):
         "pkm_flat_workspace_bytes": (ctypes.c_int, [cfg_p, i64, ctypes.POINTER(ctypes.c_size_t)]),
         "pkm_flat_search": (ctypes.c_int, [vp, par_p, i64, vp, vp, ctypes.c_size_t, vp, vp, vp]),
         "pkm_backward_workspace_bytes": (ctypes.c_int, [cfg_p, ctypes.POINTER(ctypes.c_size_t)]),
+        "pkm_forward_batch_stats": (ctypes.c_int, [vp, par_p, i64, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp]),
+        "pkm_backward_batch_stats": (ctypes.c_int, [vp, par_p, i64, vp, vp, vp, vp, vp, vp,
+                                                    ctypes.POINTER(GradsStruct), vp, ctypes.c_size_t, vp]),
         "pkm_backward": (ctypes.c_int, [vp, par_p, i64, vp, vp, vp, vp, ctypes.POINTER(GradsStruct), vp,
                                         ctypes.c_size_t, vp]),
         "pkm_status_str": (ctypes.c_char_p, [ctypes.c_int]),
@@ -210,9 +214,11 @@ class Memory:
         D, H, n = self.dim, self.heads, self.n_keys
         t = params.tensors
         dev = t["wq"].device if t.get("wq") is not None else None
-        if "query" in parts:
+        if "query" in parts or "query_affine" in parts:
+            # query_affine: batch statistics replace the running mean / var
             _expect(t["wq"], "wq", (H, D, D), "float32")
-            for name in ("bn_mean", "bn_var", "bn_gamma", "bn_beta"):
+            names = ("bn_gamma", "bn_beta") if "query_affine" in parts else ("bn_mean", "bn_var", "bn_gamma", "bn_beta")
+            for name in names:
                 _expect(t[name], name, (H, D), "float32", dev)
         if "subkeys" in parts:
             _expect(t["subkeys"], "subkeys", (H, 2, n, D // 2), "float32", dev)
@@ -295,16 +301,46 @@ class Memory:
         _check(self.lib.pkm_backward_workspace_bytes(ctypes.byref(self.cfg), ctypes.byref(n)))
         return n.value
 
-    def backward(self, params, x, idx, weights, dout, grads=None, workspace=None, stream=None):
+    def forward_batch_stats(self, params, x, out=None, idx=None, weights=None, running=None, momentum=0.1,
+                            stream=None):
+        """The lookup with training-mode BN (statistics of this batch).
+        running: (mean, var) [H, D] f32 tensors updated in place, or None.
+        Returns (out, idx, weights, batch_mean, batch_var)."""
+        torch = _torch()
+        B = x.shape[0]
+        H, D, k = self.heads, self.dim, self.k
+        self.check_params(params, ("query_affine", "subkeys", "values"))
+        dev = params["subkeys"].device
+        _expect(x, "x", (B, D), "float32", dev)
+        out = self._new((B, D), torch.float32, x) if out is None else out
+        idx = self._new((B, H, k), torch.int32, x) if idx is None else idx
+        weights = self._new((B, H, k), torch.float32, x) if weights is None else weights
+        mean = self._new((H, D), torch.float32, x)
+        var = self._new((H, D), torch.float32, x)
+        _expect(out, "out", (B, D), "float32", dev)
+        _expect(idx, "idx", (B, H, k), "int32", dev)
+        _expect(weights, "weights", (B, H, k), "float32", dev)
+        rm, rv = running if running is not None else (None, None)
+        for t, name in ((rm, "running_mean"), (rv, "running_var")):
+            if t is not None:
+                _expect(t, name, (H, D), "float32", dev)
+        _check(self.lib.pkm_forward_batch_stats(self._ctx, ctypes.byref(params.struct), B, _ptr(x), _ptr(out),
+                                                _ptr(idx), _ptr(weights), _ptr(mean), _ptr(var), _ptr(rm), _ptr(rv),
+                                                float(momentum), _stream_handle(stream)))
+        return out, idx, weights, mean, var
+
+    def backward(self, params, x, idx, weights, dout, grads=None, workspace=None, stream=None, batch_stats=None):
         """Gradients of a loss given dout = dL/dout [B, D] for the winners
         (idx, weights) a forward call returned.  grads: dict name -> fp32
         tensor (parameter gradients are added to, dx is overwritten; a
         missing name is skipped), or None for freshly zeroed buffers of every
-        gradient.  Returns the dict."""
+        gradient.  batch_stats: (mean, var) from forward_batch_stats for the
+        training-mode BN backward, or None (running statistics).  Returns
+        the dict."""
         torch = _torch()
         B = x.shape[0]
         D, H, n, k = self.dim, self.heads, self.n_keys, self.k
-        self.check_params(params)
+        self.check_params(params, ("query_affine" if batch_stats is not None else "query", "subkeys", "values"))
         dev = params["wq"].device
         _expect(x, "x", (B, D), "float32", dev)
         _expect(dout, "dout", (B, D), "float32", dev)
@@ -323,9 +359,18 @@ class Memory:
             workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
         _expect(workspace, "workspace", (workspace.numel(),), "uint8", dev)
         gs = GradsStruct(*[None if grads.get(nm) is None else grads[nm].data_ptr() for nm in GRAD_NAMES])
-        _check(self.lib.pkm_backward(self._ctx, ctypes.byref(params.struct), B, _ptr(x), _ptr(idx), _ptr(weights),
-                                     _ptr(dout), ctypes.byref(gs), _ptr(workspace), workspace.numel(),
-                                     _stream_handle(stream)))
+        if batch_stats is None:
+            _check(self.lib.pkm_backward(self._ctx, ctypes.byref(params.struct), B, _ptr(x), _ptr(idx),
+                                         _ptr(weights), _ptr(dout), ctypes.byref(gs), _ptr(workspace),
+                                         workspace.numel(), _stream_handle(stream)))
+        else:
+            mean, var = batch_stats
+            _expect(mean, "batch_mean", (H, D), "float32", dev)
+            _expect(var, "batch_var", (H, D), "float32", dev)
+            _check(self.lib.pkm_backward_batch_stats(self._ctx, ctypes.byref(params.struct), B, _ptr(x), _ptr(idx),
+                                                     _ptr(weights), _ptr(dout), _ptr(mean), _ptr(var),
+                                                     ctypes.byref(gs), _ptr(workspace), workspace.numel(),
+                                                     _stream_handle(stream)))
         return grads
 
     def flat_workspace_bytes(self, B):

@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpkm.so")
-SOURCES = ["gemm_f32.hip", "select.hip", "gather.hip", "backward.hip", "pkm_api.cpp"]
+SOURCES = ["gemm_f32.hip", "select.hip", "gather.hip", "backward.hip", "batch_norm.hip", "pkm_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -370,10 +370,12 @@ __global__ __launch_bounds__(256) void colsum_partial_kernel(const float *__rest
     part_b[(int64_t)blockIdx.y * cols + col] = sb;
 }
 
-// pass 2: dgamma += sum of the partials in chunk order (dbeta likewise).
+// pass 2: the sums of the partials in chunk order, added to dgamma / dbeta
+// and stored to sum_g / sum_b (each pair optional).
 __global__ __launch_bounds__(256) void colsum_final_kernel(const float *__restrict__ part_g,
                                                            const float *__restrict__ part_b, int chunks, int cols,
-                                                           float *__restrict__ dgamma, float *__restrict__ dbeta)
+                                                           float *__restrict__ dgamma, float *__restrict__ dbeta,
+                                                           float *__restrict__ sum_g, float *__restrict__ sum_b)
 {
     const int col = blockIdx.x * 256 + threadIdx.x;
     if (col >= cols) return;
@@ -382,8 +384,14 @@ __global__ __launch_bounds__(256) void colsum_final_kernel(const float *__restri
         sg += part_g[(int64_t)c * cols + col];
         sb += part_b[(int64_t)c * cols + col];
     }
-    dgamma[col] += sg;
-    dbeta[col] += sb;
+    if (dgamma) {
+        dgamma[col] += sg;
+        dbeta[col] += sb;
+    }
+    if (sum_g) {
+        sum_g[col] = sg;
+        sum_b[col] = sb;
+    }
 }
 
 // ---- value gradient: counting sort of the occurrences by row.
@@ -649,7 +657,7 @@ int colsum_chunks(int64_t B) { return (int)((B + kColChunk - 1) / kColChunk); }
 
 hipError_t launch_bn_grads(const float *dqhat, const float *q, const float *mean, const float *var, float eps,
                            int64_t B, int cols, float *part_g, float *part_b, float *dgamma, float *dbeta,
-                           hipStream_t st)
+                           float *sum_g, float *sum_b, hipStream_t st)
 {
     if (B <= 0) return hipSuccess;
     const int chunks = colsum_chunks(B);
@@ -657,7 +665,7 @@ hipError_t launch_bn_grads(const float *dqhat, const float *q, const float *mean
     hipLaunchKernelGGL(colsum_partial_kernel, dim3(grid_of(cols, 256), chunks), dim3(256), 0, st, dqhat, q, mean, var,
                        eps, B, cols, part_g, part_b);
     hipLaunchKernelGGL(colsum_final_kernel, dim3(grid_of(cols, 256)), dim3(256), 0, st, part_g, part_b, chunks, cols,
-                       dgamma, dbeta);
+                       dgamma, dbeta, sum_g, sum_b);
     return hipGetLastError();
 }
 

@@ -21,6 +21,7 @@ struct pkm_ctx {
     int32_t *idx;    // [max_batch, H, k]
     float *weights;  // [max_batch, H, k]
     uint32_t *stair; // staircase cells of the candidate grid for this k
+    float *stat_part; // batch-statistics partial sums [chunks, H * D]
 };
 
 namespace {
@@ -61,7 +62,7 @@ constexpr size_t kAlign = 256;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // Workspace pieces for one chunk of mb tokens; false on size overflow.
-constexpr int kPieces = 5;
+constexpr int kPieces = 6;
 bool workspace_layout(const pkm_config &c, size_t sizes[kPieces])
 {
     const double mb = (double)c.max_batch;
@@ -73,6 +74,7 @@ bool workspace_layout(const pkm_config &c, size_t sizes[kPieces])
     sizes[2] = round_up(m * H * (size_t)c.k * sizeof(int32_t));
     sizes[3] = round_up(m * H * (size_t)c.k * sizeof(float));
     sizes[4] = round_up(pkm::kMaxStaircaseCells * sizeof(uint32_t));
+    sizes[5] = round_up((size_t)pkm::stat_chunks(c.max_batch) * H * (size_t)c.dim * sizeof(float));
     return true;
 }
 
@@ -271,7 +273,7 @@ bool backward_layout(const pkm_config &c, size_t sizes[kBwdPieces])
     sizes[4] = round_up(HD * mb32 * f);     // dq transposed
     sizes[5] = round_up(D * mb32 * f);      // x transposed
     sizes[6] = round_up(D * HD * f);        // Wq transposed
-    sizes[7] = 0;                           // (unused)
+    sizes[7] = round_up(2 * HD * f);        // this batch's sums of dq^ xhat and dq^
     sizes[8] = round_up(2 * H * n * mb32 * f);  // half-score gradients G
     sizes[9] = round_up((size_t)pkm::colsum_chunks((int64_t)mb) * HD * f);
     sizes[10] = sizes[9];
@@ -348,6 +350,7 @@ pkm_status pkm_create(const pkm_config *cfg, pkm_ctx **out)
     ctx->idx = reinterpret_cast<int32_t *>(w + sizes[0] + sizes[1]);
     ctx->weights = reinterpret_cast<float *>(w + sizes[0] + sizes[1] + sizes[2]);
     ctx->stair = reinterpret_cast<uint32_t *>(w + sizes[0] + sizes[1] + sizes[2] + sizes[3]);
+    ctx->stat_part = reinterpret_cast<float *>(w + sizes[0] + sizes[1] + sizes[2] + sizes[3] + sizes[4]);
     uint32_t stair[pkm::kMaxStaircaseCells] = {};
     pkm::staircase_table(cfg->k, stair);
     e = hipMemcpy(ctx->stair, stair, sizeof stair, hipMemcpyHostToDevice);
@@ -505,25 +508,21 @@ pkm_status pkm_backward_workspace_bytes(const pkm_config *cfg, size_t *bytes)
     return ok();
 }
 
-pkm_status pkm_backward(pkm_ctx *ctx, const pkm_params *p, int64_t B, const float *x, const int32_t *idx,
-                        const float *weights, const float *dout, const pkm_grads *grads, void *workspace,
-                        size_t workspace_bytes, void *stream)
+}  // extern "C"
+
+namespace {
+
+// The backward for running statistics (mean, var = p's) or, with batch
+// true, for the statistics of this batch (mean, var given; one chunk).
+pkm_status run_backward(pkm_ctx *ctx, const pkm_params *p, int64_t B, const float *x, const int32_t *idx,
+                        const float *weights, const float *dout, const float *mean, const float *var, bool batch,
+                        const pkm_grads *grads, void *workspace, size_t workspace_bytes, void *stream)
 {
     pkm_status s;
-    if ((s = check_ctx(ctx)) || (s = check_batch(ctx->cfg, B))) return s;
     const pkm_config &c = ctx->cfg;
     size_t sizes[kBwdPieces];
-    if (!backward_layout(c, sizes)) return fail(PKM_E_ARG, "backward workspace size overflows");
-    size_t need_bytes = 0;
-    for (size_t piece : sizes) need_bytes += piece;
-    if (B == 0) return ok();
-    if ((s = check_query_params(p)) || (s = need(p->subkeys, "subkeys")) || (s = check_value_params(c, p))) return s;
-    if ((s = need(x, "x")) || (s = need(idx, "idx")) || (s = need(weights, "weights")) || (s = need(dout, "dout")) ||
-        (s = need(workspace, "workspace")) || (s = check_grads(grads)))
-        return s;
-    if (workspace_bytes < need_bytes)
-        return fail(PKM_E_ARG, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, need_bytes);
-
+    backward_layout(c, sizes);  // checked by the caller
+    (void)workspace_bytes;
     hipStream_t st = static_cast<hipStream_t>(stream);
     char *w = static_cast<char *>(workspace);
     void *piece[kBwdPieces];
@@ -535,6 +534,7 @@ pkm_status pkm_backward(pkm_ctx *ctx, const pkm_params *p, int64_t B, const floa
     float *dqh = static_cast<float *>(piece[2]), *dq = static_cast<float *>(piece[3]);
     float *dqT = static_cast<float *>(piece[4]), *xT = static_cast<float *>(piece[5]);
     float *wqT = static_cast<float *>(piece[6]);
+    float *sum_g = static_cast<float *>(piece[7]), *sum_b = sum_g + (size_t)c.heads * c.dim;
     float *G = static_cast<float *>(piece[8]);
     float *part_g = static_cast<float *>(piece[9]), *part_b = static_cast<float *>(piece[10]);
     uint32_t *count = static_cast<uint32_t *>(piece[11]), *cursor = static_cast<uint32_t *>(piece[12]);
@@ -563,14 +563,18 @@ pkm_status pkm_backward(pkm_ctx *ctx, const pkm_params *p, int64_t B, const floa
             (s = launched(pkm::launch_fill(reinterpret_cast<uint32_t *>(G), (int64_t)2 * H * n * nb32, 0u, st),
                           "clear")))
             return s;
-        if ((s = launched(pkm::launch_dqhat(p->subkeys, p->bn_var, p->bn_gamma, c.bn_eps, D, n, nb, H, k, ic, dt, dqh,
-                                            dq, G, nb32, st),
+        if ((s = launched(pkm::launch_dqhat(p->subkeys, var, p->bn_gamma, c.bn_eps, D, n, nb, H, k, ic, dt, dqh, dq, G,
+                                            nb32, st),
                           "query gradient")))
             return s;
-        if (grads->dbn_gamma &&
-            (s = launched(pkm::launch_bn_grads(dqh, Q, p->bn_mean, p->bn_var, c.bn_eps, nb, HD, part_g, part_b,
-                                               grads->dbn_gamma, grads->dbn_beta, st),
+        if ((grads->dbn_gamma || batch) &&
+            (s = launched(pkm::launch_bn_grads(dqh, Q, mean, var, c.bn_eps, nb, HD, part_g, part_b, grads->dbn_gamma,
+                                               grads->dbn_beta, batch ? sum_g : nullptr, batch ? sum_b : nullptr, st),
                           "BN gradients")))
+            return s;
+        if (batch && (s = launched(pkm::launch_bn_batch_dq(dqh, Q, nb, HD, mean, var, p->bn_gamma, c.bn_eps, sum_g,
+                                                           sum_b, dq, st),
+                                   "batch BN backward")))
             return s;
         if (grads->dwq) {
             if ((s = launched(pkm::launch_transpose(dq, HD, (int)nb, HD, dqT, nb32, nb32, nullptr, nullptr, nullptr,
@@ -598,8 +602,8 @@ pkm_status pkm_backward(pkm_ctx *ctx, const pkm_params *p, int64_t B, const floa
             if ((s = launched(pkm::launch_gemm_nt_f32(a, st), "dWq"))) return s;
         }
         if (grads->dsubkeys &&
-            (s = launched(pkm::launch_dsub(G, nb32, nb, Q, H, D, n, p->bn_mean, p->bn_var, p->bn_gamma, p->bn_beta,
-                                           c.bn_eps, grads->dsubkeys, st),
+            (s = launched(pkm::launch_dsub(G, nb32, nb, Q, H, D, n, mean, var, p->bn_gamma, p->bn_beta, c.bn_eps,
+                                           grads->dsubkeys, st),
                           "subkey gradient")))
             return s;
         if (grads->dx) {
@@ -622,6 +626,113 @@ pkm_status pkm_backward(pkm_ctx *ctx, const pkm_params *p, int64_t B, const floa
                           "value gradient")))
             return s;
     }
+    return ok();
+}
+
+// Arguments of either backward; batch: the BN statistics come from the
+// caller, not from p.
+pkm_status check_backward_args(pkm_ctx *ctx, const pkm_params *p, int64_t B, const float *x, const int32_t *idx,
+                               const float *weights, const float *dout, const pkm_grads *grads, void *workspace,
+                               size_t workspace_bytes, bool batch)
+{
+    pkm_status s;
+    if ((s = check_ctx(ctx)) || (s = check_batch(ctx->cfg, B))) return s;
+    const pkm_config &c = ctx->cfg;
+    size_t sizes[kBwdPieces];
+    if (!backward_layout(c, sizes)) return fail(PKM_E_ARG, "backward workspace size overflows");
+    size_t need_bytes = 0;
+    for (size_t piece : sizes) need_bytes += piece;
+    if (B == 0) return PKM_OK;
+    if (!p) return fail(PKM_E_ARG, "params is NULL");
+    if (batch) {
+        if ((s = need(p->wq, "wq")) || (s = need(p->bn_gamma, "bn_gamma")) || (s = need(p->bn_beta, "bn_beta")))
+            return s;
+    } else if ((s = check_query_params(p))) {
+        return s;
+    }
+    if ((s = need(p->subkeys, "subkeys")) || (s = check_value_params(c, p))) return s;
+    if ((s = need(x, "x")) || (s = need(idx, "idx")) || (s = need(weights, "weights")) || (s = need(dout, "dout")) ||
+        (s = need(workspace, "workspace")) || (s = check_grads(grads)))
+        return s;
+    if (workspace_bytes < need_bytes)
+        return fail(PKM_E_ARG, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, need_bytes);
+    return PKM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pkm_status pkm_backward(pkm_ctx *ctx, const pkm_params *p, int64_t B, const float *x, const int32_t *idx,
+                        const float *weights, const float *dout, const pkm_grads *grads, void *workspace,
+                        size_t workspace_bytes, void *stream)
+{
+    if (pkm_status s = check_backward_args(ctx, p, B, x, idx, weights, dout, grads, workspace, workspace_bytes, false))
+        return s;
+    if (B == 0) return ok();
+    return run_backward(ctx, p, B, x, idx, weights, dout, p->bn_mean, p->bn_var, false, grads, workspace,
+                        workspace_bytes, stream);
+}
+
+pkm_status pkm_backward_batch_stats(pkm_ctx *ctx, const pkm_params *p, int64_t B, const float *x,
+                                    const int32_t *idx, const float *weights, const float *dout,
+                                    const float *batch_mean, const float *batch_var, const pkm_grads *grads,
+                                    void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (pkm_status s = check_backward_args(ctx, p, B, x, idx, weights, dout, grads, workspace, workspace_bytes, true))
+        return s;
+    if (B == 0) return ok();
+    if (B < 2 || B > ctx->cfg.max_batch)
+        return fail(PKM_E_ARG, "batch statistics need 2 <= B <= max_batch (got B = %lld)", (long long)B);
+    pkm_status s;
+    if ((s = need(batch_mean, "batch_mean")) || (s = need(batch_var, "batch_var"))) return s;
+    return run_backward(ctx, p, B, x, idx, weights, dout, batch_mean, batch_var, true, grads, workspace,
+                        workspace_bytes, stream);
+}
+
+pkm_status pkm_forward_batch_stats(pkm_ctx *ctx, const pkm_params *p, int64_t B, const float *x, float *out,
+                                   int32_t *idx, float *weights, float *batch_mean, float *batch_var,
+                                   float *running_mean, float *running_var, float momentum, void *stream)
+{
+    pkm_status s;
+    if ((s = check_ctx(ctx)) || (s = check_batch(ctx->cfg, B))) return s;
+    if (B == 0) return ok();
+    const pkm_config &c = ctx->cfg;
+    if (B < 2 || B > c.max_batch)
+        return fail(PKM_E_ARG, "batch statistics need 2 <= B <= max_batch (got B = %lld)", (long long)B);
+    if (!p) return fail(PKM_E_ARG, "params is NULL");
+    if ((s = need(p->wq, "wq")) || (s = need(p->bn_gamma, "bn_gamma")) || (s = need(p->bn_beta, "bn_beta")) ||
+        (s = need(p->subkeys, "subkeys")) || (s = check_value_params(c, p)))
+        return s;
+    if ((s = need(x, "x")) || (s = need(out, "out")) || (s = need(batch_mean, "batch_mean")) ||
+        (s = need(batch_var, "batch_var")))
+        return s;
+    if ((idx && !aligned16(idx)) || (weights && !aligned16(weights)))
+        return fail(PKM_E_ARG, "idx / weights must be 16-byte aligned");
+    if ((running_mean == nullptr) != (running_var == nullptr))
+        return fail(PKM_E_ARG, "running_mean and running_var go together");
+    if ((running_mean && !aligned16(running_mean)) || (running_var && !aligned16(running_var)))
+        return fail(PKM_E_ARG, "running statistics must be 16-byte aligned");
+    if (!(momentum >= 0.0f && momentum <= 1.0f)) return fail(PKM_E_ARG, "momentum must be in [0, 1]");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int HD = c.heads * c.dim;
+    int32_t *ci = idx ? idx : ctx->idx;
+    float *cw = weights ? weights : ctx->weights;
+    pkm::GemmArgs qa = query_args(c, p, B, x, ctx->qhat);
+    qa.bn_mean = qa.bn_var = qa.bn_gamma = qa.bn_beta = nullptr;
+    if ((s = launched(pkm::launch_gemm_nt_f32(qa, st), "query projection")) ||
+        (s = launched(pkm::launch_batch_stats(ctx->qhat, B, HD, ctx->stat_part, batch_mean, batch_var, running_mean,
+                                              running_var, momentum, st),
+                      "batch statistics")) ||
+        (s = launched(pkm::launch_bn_apply(ctx->qhat, B, HD, batch_mean, batch_var, p->bn_gamma, p->bn_beta, c.bn_eps,
+                                           st),
+                      "batch normalisation")) ||
+        (s = run_score(c, p, B, ctx->qhat, ctx->scores, st)) ||
+        (s = launched(pkm::launch_select(ctx->scores, B, c.heads, c.n_keys, c.k, ctx->stair, ci, cw, st), "select")) ||
+        (s = launched(pkm::launch_gather(p->values, p->value_scale, c.value_type, c.dim, c.n_keys * c.n_keys, B,
+                                         c.heads * c.k, ci, cw, out, st),
+                      "gather")))
+        return s;
     return ok();
 }
 

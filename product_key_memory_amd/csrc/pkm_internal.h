@@ -89,13 +89,30 @@ hipError_t launch_dqhat(const float *subkeys, const float *var, const float *gam
 hipError_t launch_dsub(const float *G, int64_t ldG, int64_t B, const float *q, int H, int D, int n, const float *mean,
                        const float *var, const float *gamma, const float *beta, float eps, float *dsub,
                        hipStream_t st);
+// ---- batch statistics (batch_norm.hip)
+// mean, var [cols] of q [B][cols] (biased var; B >= 2); part holds
+// stat_chunks(B) * cols floats; running stats updated when non-NULL.
+int stat_chunks(int64_t B);
+hipError_t launch_batch_stats(const float *q, int64_t B, int cols, float *part, float *mean, float *var,
+                              float *running_mean, float *running_var, float momentum, hipStream_t st);
+// q = BN(q) in place with the given statistics (cols % 4 == 0)
+hipError_t launch_bn_apply(float *q, int64_t B, int cols, const float *mean, const float *var, const float *gamma,
+                           const float *beta, float eps, hipStream_t st);
+// BN backward with batch statistics: dq from dq^, q and the column sums
+// sum_g = sum dq^ xhat, sum_b = sum dq^ of the batch
+hipError_t launch_bn_batch_dq(const float *dqh, const float *q, int64_t B, int cols, const float *mean,
+                              const float *var, const float *gamma, float eps, const float *sum_g, const float *sum_b,
+                              float *dq, hipStream_t st);
+
 // dgamma, dbeta [cols] += column sums over B rows of dqhat * xhat and dqhat,
 // xhat = (q - mean) / sqrt(var + eps); part_g / part_b hold
 // colsum_chunks(B) * cols floats each.
 int colsum_chunks(int64_t B);
+// (either may be NULL), and the sums themselves are written to sum_g /
+// sum_b when those are non-NULL.
 hipError_t launch_bn_grads(const float *dqhat, const float *q, const float *mean, const float *var, float eps,
                            int64_t B, int cols, float *part_g, float *part_b, float *dgamma, float *dbeta,
-                           hipStream_t st);
+                           float *sum_g, float *sum_b, hipStream_t st);
 // dval [N][D] += sum over the M occurrences o (row idx[o]) of w[o] *
 // dout[o / per_token]; count, cursor, offs [N], block_sum [scan_blocks(N)],
 // list [M] are scratch.

@@ -81,7 +81,8 @@ def test_workspace_bytes():
     cfg = pk.make_config(**GOOD)
     mb, H, D, n, k = 16384, 4, 1024, 1024, 32
     stair = 320 * 4  # staircase cells of the candidate grid
-    assert pk.workspace_bytes(cfg) == 4 * mb * H * (D + 2 * n + 2 * k) + stair
+    stat_part = (mb // 64) * H * D * 4  # batch-statistics partial sums
+    assert pk.workspace_bytes(cfg) == 4 * mb * H * (D + 2 * n + 2 * k) + stair + stat_part
     with pytest.raises(pk.PkmError):
         pk.workspace_bytes(pk.make_config(**{**GOOD, "k": 0}))
 
@@ -121,7 +122,7 @@ def test_backward_workspace_bytes():
         return (x + 255) // 256 * 256
 
     want = (3 * rnd(mb * HD * 4) + rnd(mb * H * k * 4) + rnd(HD * mb32 * 4) + rnd(D * mb32 * 4)
-            + rnd(D * HD * 4) + rnd(2 * H * n * mb32 * 4) + 2 * rnd(((mb + 63) // 64) * HD * 4)
+            + rnd(D * HD * 4) + rnd(2 * HD * 4) + rnd(2 * H * n * mb32 * 4) + 2 * rnd(((mb + 63) // 64) * HD * 4)
             + 3 * rnd(N * 4) + rnd(((N + 4095) // 4096) * 4) + rnd(mb * H * k * 4))
     got = ctypes.c_size_t()
     assert lib.pkm_backward_workspace_bytes(ctypes.byref(cfg), ctypes.byref(got)) == pk.PKM_OK
