@@ -178,10 +178,24 @@ def backward_step(torch, mem, wl, P, xt, idx, wts, fwd_ms, steps, warmup):
     grads = {name: torch.zeros(shape, dtype=torch.float32, device="cuda") for name, shape in grads.items()}
     ws = torch.empty(mem.backward_workspace_bytes(), dtype=torch.uint8, device="cuda")
     ms = timed_steps(torch, lambda: mem.backward(P, xt, idx, wts, dout, grads, ws), steps, warmup)
+    # the same step with training-mode BN (statistics of this batch, running statistics updated)
+    out = torch.empty((wl.B, wl.D), dtype=torch.float32, device="cuda")
+    running = (torch.zeros((wl.H, wl.D), device="cuda"), torch.ones((wl.H, wl.D), device="cuda"))
+    stats = {}
+
+    def fwd_bs():
+        stats["r"] = mem.forward_batch_stats(P, xt, out, idx, wts, running=running)
+
+    fwd_bs_ms = timed_steps(torch, fwd_bs, steps, warmup)
+    bm, bv = stats["r"][3], stats["r"][4]
+    bwd_bs_ms = timed_steps(torch, lambda: mem.backward(P, xt, idx, wts, dout, grads, ws, batch_stats=(bm, bv)),
+                            steps, warmup)
     # GEMM work of the backward: the recomputed q, dWq and dx (2 B H D^2 each)
     flop = 2.0 * wl.B * wl.H * wl.D * wl.D * 3
     return {"ms": round(ms, 4), "tokens_per_s": round(wl.B / (ms * 1e-3), 1),
             "forward_backward_tokens_per_s": round(wl.B / ((ms + fwd_ms) * 1e-3), 1),
+            "batch_stats_forward_ms": round(fwd_bs_ms, 4), "batch_stats_backward_ms": round(bwd_bs_ms, 4),
+            "batch_stats_forward_backward_tokens_per_s": round(wl.B / ((fwd_bs_ms + bwd_bs_ms) * 1e-3), 1),
             "gemm_flop": flop, "gemm_tflops_if_all_time": round(flop / (ms * 1e-3) / 1e12, 2),
             "workspace_bytes": mem.backward_workspace_bytes()}
 
