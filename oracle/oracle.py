@@ -14,7 +14,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "pkm_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-VALUE_TYPES = {"f32": 0, "bf16": 1, "e4m3": 2}
+VALUE_TYPES = {"f32": 0, "bf16": 1, "e4m3": 2, "int8": 3, "int4": 4}
+SCALED = ("e4m3", "int8", "int4")  # tables with a per-row fp32 scale
 
 
 def lib_path():
@@ -56,6 +57,12 @@ def load_library(path):
     lib.pkmo_bf16_to_f64.argtypes = [ctypes.c_uint16]
     lib.pkmo_e4m3_to_f64.restype = ctypes.c_double
     lib.pkmo_e4m3_to_f64.argtypes = [ctypes.c_uint8]
+    lib.pkmo_int8_to_f64.restype = ctypes.c_double
+    lib.pkmo_int8_to_f64.argtypes = [ctypes.c_int8]
+    lib.pkmo_int4_to_f64.restype = ctypes.c_double
+    lib.pkmo_int4_to_f64.argtypes = [ctypes.c_uint8]
+    lib.pkmo_usage.restype = ctypes.c_int
+    lib.pkmo_usage.argtypes = [ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
     lib.pkmo_select.restype = ctypes.c_int
     lib.pkmo_select.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int] + [ctypes.c_void_p] * 4
     lib.pkmo_gather.restype = ctypes.c_int
@@ -102,8 +109,10 @@ class Model:
 
     wq [H,D,D] f32 (row f = output feature f), mean/var/gamma/beta [H,D] f32,
     subkeys [H,2,n,D/2] f32, values [n*n,D] as f32 / uint16 (bf16 bits) /
-    uint8 (E4M3 bits), scale [n*n] f32 for E4M3 tables.  values may be None
-    when only the selection (idx, top, w, qhat) is wanted.
+    uint8 (E4M3 bits) / int8 codes, or [n*n,D/2] uint8 of packed int4 codes
+    (even element in the low nibble); scale [n*n] f32 for E4M3, int8 and
+    int4 tables.  values may be None when only the selection (idx, top, w,
+    qhat) is wanted.
     """
 
     def __init__(self, wq, mean, var, gamma, beta, subkeys, values, scale, k, table, eps=1e-5):
@@ -112,15 +121,15 @@ class Model:
         n = subkeys.shape[2]
         assert subkeys.shape == (H, 2, n, D // 2)
         self.H, self.D, self.n, self.k, self.table, self.eps = H, D, n, int(k), table, float(eps)
-        vt = np.dtype({"f32": np.float32, "bf16": np.uint16, "e4m3": np.uint8}[table])
+        vt = np.dtype({"f32": np.float32, "bf16": np.uint16, "e4m3": np.uint8, "int8": np.int8, "int4": np.uint8}[table])
         self._keep = [
             _c(wq, np.float32), _c(mean, np.float32), _c(var, np.float32), _c(gamma, np.float32),
             _c(beta, np.float32), _c(subkeys, np.float32), None if values is None else _c(values, vt),
             None if scale is None else _c(scale, np.float32),
         ]
         self.has_values = values is not None
-        assert not self.has_values or self._keep[6].shape == (n * n, D)
-        if table == "e4m3" and self.has_values:
+        assert not self.has_values or self._keep[6].shape == (n * n, D // 2 if table == "int4" else D)
+        if table in SCALED and self.has_values:
             assert self._keep[7] is not None and self._keep[7].shape == (n * n,)
         k_ = self._keep
         self._s = _Model(D, H, n, int(k), VALUE_TYPES[table], 0, float(eps), *[_ptr(a) for a in k_])
@@ -164,6 +173,14 @@ def bf16_to_f64(bits, lib=None):
 
 def e4m3_to_f64(bits, lib=None):
     return (lib or _load()).pkmo_e4m3_to_f64(int(bits))
+
+
+def int8_to_f64(code, lib=None):
+    return (lib or _load()).pkmo_int8_to_f64(int(code))
+
+
+def int4_to_f64(nibble, lib=None):
+    return (lib or _load()).pkmo_int4_to_f64(int(nibble))
 
 
 def select(scores, k, lib=None):
@@ -277,3 +294,14 @@ def backward_batch_stats(model, x, dout, mean, var, want=GRADS, lib=None):
     if rc != 0:
         raise ValueError("oracle rejected its arguments" if rc == -1 else "oracle ran out of memory")
     return res
+
+
+def usage(rows, N, counts=None, lib=None):
+    """Slot usage: counts [N] uint32 (+= when given) of the rows in rows."""
+    lib = lib or _load()
+    rows = _c(np.asarray(rows, np.int32).reshape(-1), np.int32)
+    counts = np.zeros(N, np.uint32) if counts is None else counts
+    assert counts.dtype == np.uint32 and counts.shape == (N,) and counts.flags.c_contiguous
+    if lib.pkmo_usage(rows.size, _ptr(rows), N, _ptr(counts)) != 0:
+        raise ValueError("oracle rejected its arguments")
+    return counts

@@ -59,13 +59,15 @@
 #define PKMO_F32 0
 #define PKMO_BF16 1
 #define PKMO_E4M3 2
+#define PKMO_INT8 3
+#define PKMO_INT4 4
 
 typedef struct {
     int32_t D;          /* model width; even */
     int32_t H;          /* heads */
     int32_t n;          /* subkeys per half; the table has n*n rows */
     int32_t k;          /* winners per head */
-    int32_t value_type; /* PKMO_F32 / PKMO_BF16 / PKMO_E4M3 */
+    int32_t value_type; /* PKMO_F32 / PKMO_BF16 / PKMO_E4M3 / PKMO_INT8 / PKMO_INT4 */
     int32_t pad_;
     double eps;         /* BatchNorm epsilon */
     const float *wq;    /* [H][D][D]: row f of head h is output feature f */
@@ -74,7 +76,7 @@ typedef struct {
     const float *gamma; /* [H][D] */
     const float *beta;  /* [H][D] */
     const float *subkeys; /* [H][2][n][D/2] */
-    const void *values;   /* [n*n][D] of value_type */
+    const void *values;   /* [n*n][D] of value_type ([n*n][D/2] bytes for INT4) */
     const float *scale;   /* [n*n] row scales (E4M3 only) */
 } pkmo_model;
 
@@ -113,8 +115,20 @@ double pkmo_e4m3_to_f64(uint8_t bits)
     return sign ? -v : v;
 }
 
+/* Symmetric integer codes ("a good candidate for keeping in a lower
+ * precision", the note after the code listing): int8 is an ordinary two's
+ * complement byte; int4 is a two's complement nibble, two per byte, the
+ * element with the even index in the low nibble. */
+double pkmo_int8_to_f64(int8_t code) { return (double)code; }
+
+double pkmo_int4_to_f64(uint8_t nibble)
+{
+    int v = nibble & 0xF;
+    return (double)(v >= 8 ? v - 16 : v);
+}
+
 /* Value-table element V[row][d] as an exact fp64 number (times the row scale
- * for E4M3 tables). */
+ * for E4M3, int8 and int4 tables). */
 static double value_at(const pkmo_model *M, int64_t row, int d)
 {
     int64_t off = row * (int64_t)M->D + d;
@@ -123,6 +137,12 @@ static double value_at(const pkmo_model *M, int64_t row, int d)
         return (double)((const float *)M->values)[off];
     case PKMO_BF16:
         return pkmo_bf16_to_f64(((const uint16_t *)M->values)[off]);
+    case PKMO_INT8:
+        return (double)M->scale[row] * pkmo_int8_to_f64(((const int8_t *)M->values)[off]);
+    case PKMO_INT4: {
+        const uint8_t byte = ((const uint8_t *)M->values)[off / 2];
+        return (double)M->scale[row] * pkmo_int4_to_f64((uint8_t)(d & 1 ? byte >> 4 : byte));
+    }
     default:
         return pkmo_e4m3_to_f64(((const uint8_t *)M->values)[off]) * (double)M->scale[row];
     }
@@ -848,5 +868,21 @@ int pkmo_backward_batch_stats(const pkmo_model *M, int64_t B, const float *x, co
     }
     free(qhat); free(xhat); free(dqh); free(dtv); free(wv); free(rows); free(s); free(t0); free(t1);
     free(i0); free(i1); free(tp); free(g); free(m1); free(m2);
+    return 0;
+}
+
+/* ------------------------------------------------------------ slot usage */
+
+/* Slot usage ("Product-Key Memory", §Keeping the memory in use: a slot that
+ * is never selected receives no gradient): counts[r] += the number of
+ * entries of rows [M] equal to r, for r < N.  Returns 0, or -1 on bad
+ * arguments (a row outside [0, N)). */
+int pkmo_usage(int64_t M, const int32_t *rows, int64_t N, uint32_t *counts)
+{
+    if (M < 0 || N < 1 || (M > 0 && !rows) || !counts) return -1;
+    for (int64_t i = 0; i < M; ++i) {
+        if (rows[i] < 0 || rows[i] >= N) return -1;
+        counts[rows[i]] += 1;
+    }
     return 0;
 }

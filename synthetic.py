@@ -42,7 +42,7 @@ class Workload:
     H: int
     n: int
     k: int
-    table: str  # "f32" | "bf16" | "e4m3"
+    table: str  # "f32" | "bf16" | "e4m3" | "int8" | "int4"
     bn: str  # "unit" | "random"
 
     @property
@@ -99,13 +99,43 @@ def f32_to_e4m3_rows(a):
     return codes, scale
 
 
+def f32_to_int8_rows(a):
+    """Per-row symmetric int8: scale_r = max|a_r| / 127 (1 for an all-zero
+    row), codes a_r / scale_r rounded to nearest even, in [-127, 127].
+    Returns (int8 codes, float32 scales)."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    amax = np.abs(a).max(axis=1)
+    scale = np.where(amax > 0, amax / np.float32(127.0), np.float32(1.0)).astype(np.float32)
+    q = np.clip(np.rint(a / scale[:, None]), -127, 127).astype(np.int8)
+    return q, scale
+
+
+def f32_to_int4_rows(a):
+    """Per-row symmetric int4: scale_r = max|a_r| / 7, codes in [-7, 7]
+    rounded to nearest even, two per byte (even element in the low nibble).
+    Returns (uint8 [rows, D/2], float32 scales)."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    amax = np.abs(a).max(axis=1)
+    scale = np.where(amax > 0, amax / np.float32(7.0), np.float32(1.0)).astype(np.float32)
+    q = np.clip(np.rint(a / scale[:, None]), -7, 7).astype(np.int8).view(np.uint8) & np.uint8(0xF)
+    return (q[:, 0::2] | (q[:, 1::2] << np.uint8(4))).astype(np.uint8), scale
+
+
+SCALED_TABLES = ("e4m3", "int8", "int4")  # tables stored with a per-row fp32 scale
+
+
+def table_shape(wl):
+    return (wl.N, wl.D // 2) if wl.table == "int4" else (wl.N, wl.D)
+
+
 def make_values(wl, seed=0):
-    """Value table [N, D] in the workload's storage format (+ row scales)."""
+    """Value table [N, D] in the workload's storage format (+ row scales);
+    int4 tables are [N, D/2] bytes."""
     N, D = wl.N, wl.D
     std = float(D) ** -0.25
-    dtype = {"f32": np.float32, "bf16": np.uint16, "e4m3": np.uint8}[wl.table]
-    values = np.empty((N, D), dtype=dtype)
-    scale = np.empty((N,), dtype=np.float32) if wl.table == "e4m3" else None
+    dtype = {"f32": np.float32, "bf16": np.uint16, "e4m3": np.uint8, "int8": np.int8, "int4": np.uint8}[wl.table]
+    values = np.empty(table_shape(wl), dtype=dtype)
+    scale = np.empty((N,), dtype=np.float32) if wl.table in SCALED_TABLES else None
     nchunks = (N + _CHUNK_ROWS - 1) // _CHUNK_ROWS
 
     def fill(c):
@@ -115,6 +145,10 @@ def make_values(wl, seed=0):
             values[r0:r1] = v
         elif wl.table == "bf16":
             values[r0:r1] = f32_to_bf16_bits(v)
+        elif wl.table == "int8":
+            values[r0:r1], scale[r0:r1] = f32_to_int8_rows(v)
+        elif wl.table == "int4":
+            values[r0:r1], scale[r0:r1] = f32_to_int4_rows(v)
         else:
             values[r0:r1], scale[r0:r1] = f32_to_e4m3_rows(v)
 

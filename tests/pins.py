@@ -4,7 +4,8 @@ Each ``pin_*`` function raises AssertionError when the oracle (the default
 build, or a variant passed as ``lib``) disagrees with:
   - library routines that define a step: torch's Linear, BatchNorm1d
     (inference), softmax and embedding_bag(mode="sum", per_sample_weights),
-    the bf16 / float8_e4m3fn casts;
+    the bf16 / float8_e4m3fn / int8 casts, and an arithmetic-shift decode of
+    two's complement nibbles for int4;
   - the flat exact search the "Product-Key Memory" page contrasts the method
     with (§Factorising the key space): every one of the N = n_keys^2
     concatenated keys (c0_a, c1_b) is scored with one full-length dot product
@@ -38,12 +39,28 @@ import synthetic
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 
+def unpack_int4(packed):
+    """[rows, D/2] bytes -> [rows, D] int8: each nibble sign-extended by an
+    arithmetic right shift of the byte that holds it in its high half."""
+    b = np.ascontiguousarray(packed, dtype=np.uint8)
+    low = (b << np.uint8(4)).view(np.int8) >> 4
+    high = b.view(np.int8) >> 4
+    out = np.empty((b.shape[0], 2 * b.shape[1]), np.int8)
+    out[:, 0::2], out[:, 1::2] = low, high
+    return out
+
+
 def dequant_table(values, scale, table):
-    """fp64 copy of a stored table, decoded by torch's own casts."""
+    """fp64 copy of a stored table, decoded by torch's own casts (int4:
+    unpack_int4)."""
     if table == "f32":
         return torch.from_numpy(values).double()
     if table == "bf16":
         return torch.from_numpy(values.view(np.int16)).view(torch.bfloat16).double()
+    if table == "int8":
+        return torch.from_numpy(values.view(np.int8)).double() * torch.from_numpy(scale).double()[:, None]
+    if table == "int4":
+        return torch.from_numpy(unpack_int4(values)).double() * torch.from_numpy(scale).double()[:, None]
     v = torch.from_numpy(values).view(torch.float8_e4m3fn).double()
     return v * torch.from_numpy(scale).double()[:, None]
 
@@ -222,6 +239,13 @@ def pin_codecs(lib=None):
     assert oracle.e4m3_to_f64(0x08, lib) == 2.0 ** -6
     assert oracle.e4m3_to_f64(0x01, lib) == 2.0 ** -9
     assert oracle.e4m3_to_f64(0xB8, lib) == -1.0
+    codes = np.arange(-128, 128, dtype=np.int8)
+    ref = torch.from_numpy(codes).double().numpy()
+    assert (np.array([oracle.int8_to_f64(int(c), lib) for c in codes]) == ref).all(), "int8 decoder"
+    nib = np.arange(16, dtype=np.uint8)
+    ref = unpack_int4(nib[:, None])[:, 0].astype(np.float64)  # each code in a low nibble
+    assert (np.array([oracle.int4_to_f64(int(c), lib) for c in nib]) == ref).all(), "int4 decoder"
+    assert oracle.int4_to_f64(0x8, lib) == -8.0 and oracle.int4_to_f64(0x7, lib) == 7.0
 
 
 def pin_softmax_large_scores(lib=None):

@@ -32,7 +32,7 @@ def test_flat_search_random_gamma_beta():
     pins.pin_against_flat_search(wl, gamma_beta=True)
 
 
-@pytest.mark.parametrize("table", ["bf16", "e4m3"])
+@pytest.mark.parametrize("table", ["bf16", "e4m3", "int8", "int4"])
 def test_flat_search_quantised_tables(table):
     wl = synthetic.Workload("q", 24, 128, 2, 24, 8, table, "random")
     pins.pin_against_flat_search(wl, seed=2)
@@ -111,6 +111,27 @@ def test_e4m3_encoder_is_nearest_code():
     assert (np.abs(table[codes]) <= 448).all()
 
 
+@pytest.mark.parametrize("bits,qmax", [(8, 127), (4, 7)])
+def test_integer_encoders_are_nearest_codes(bits, qmax):
+    """int8 / int4 codes: the nearest integer to a / scale (ties to even) in
+    [-qmax, qmax], scale = row max / qmax; int4 codes two per byte."""
+    a = np.random.default_rng(2).standard_normal((64, 96)).astype(np.float32)
+    a[3] = 0.0  # an all-zero row: scale 1, codes 0
+    if bits == 8:
+        codes, scale = synthetic.f32_to_int8_rows(a)
+        q = codes.astype(np.float64)
+    else:
+        packed, scale = synthetic.f32_to_int4_rows(a)
+        assert packed.shape == (64, 48)
+        q = pins.unpack_int4(packed).astype(np.float64)
+    amax = np.abs(a).max(1)
+    np.testing.assert_allclose(scale, np.where(amax > 0, amax / qmax, 1.0), rtol=1e-7)
+    y = (a / scale[:, None]).astype(np.float64)
+    assert (np.abs(q) <= qmax).all()
+    assert (np.abs(y - q) <= 0.5 + 1e-6).all()
+    assert not q[3].any()
+
+
 def test_generator_is_deterministic_and_seeded():
     wl = synthetic.Workload("g", 4, 64, 2, 64, 4, "bf16", "random")
     p1, p2, p3 = synthetic.make_params(wl, 0), synthetic.make_params(wl, 0), synthetic.make_params(wl, 1)
@@ -121,3 +142,16 @@ def test_generator_is_deterministic_and_seeded():
     assert not (p1["wq"] == p3["wq"]).all()
     assert (synthetic.redraw_row(wl, 0, 3, 1) == synthetic.redraw_row(wl, 0, 3, 1)).all()
     assert not (synthetic.redraw_row(wl, 0, 3, 1) == synthetic.redraw_row(wl, 0, 3, 2)).all()
+
+
+def test_usage_counts_match_bincount():
+    """Slot usage against numpy's bincount, accumulated over two calls."""
+    rng = np.random.default_rng(4)
+    N = 5000
+    a = rng.integers(0, N, 30000).astype(np.int32)
+    b = rng.integers(0, 40, 777).astype(np.int32)  # hot rows
+    got = oracle.usage(b, N, oracle.usage(a, N))
+    ref = np.bincount(np.concatenate([a, b]), minlength=N)
+    assert (got == ref).all()
+    with pytest.raises(ValueError):
+        oracle.usage(np.array([N], np.int32), N)

@@ -29,6 +29,8 @@ MUTATIONS = {
     "e4m3_bias": ("v = ldexp(1.0 + (double)m / 8.0, e - 7);", "v = ldexp(1.0 + (double)m / 8.0, e - 8);"),
     "e4m3_no_scale": ("* (double)M->scale[row];", ";"),
     "bf16_subnormal": ("v = ldexp((double)m / 128.0, -126);", "v = ldexp((double)m / 128.0, -127);"),
+    "int4_unsigned": ("return (double)(v >= 8 ? v - 16 : v);", "return (double)v;"),
+    "int4_nibble_order": ("(uint8_t)(d & 1 ? byte >> 4 : byte)", "(uint8_t)(d & 1 ? byte : byte >> 4)"),
     "candidate_count": ("    return c;\n}", "    return c - 1;\n}"),
     "half_topk_from_wrong_row": ("pkmo_topk_sorted(n, s + n, kk, t1, i1);", "pkmo_topk_sorted(n, s, kk, t1, i1);"),
     # backward direction
@@ -62,6 +64,8 @@ PINS = [
     lambda lib: pins.pin_against_flat_search(pins.synthetic.Workload("gb", 24, 64, 3, 20, 5, "f32", "random"),
                                              gamma_beta=True, lib=lib),
     lambda lib: pins.pin_against_flat_search(pins.synthetic.Workload("q", 24, 128, 2, 24, 8, "e4m3", "random"),
+                                             seed=2, lib=lib),
+    lambda lib: pins.pin_against_flat_search(pins.synthetic.Workload("q4", 24, 128, 2, 24, 8, "int4", "random"),
                                              seed=2, lib=lib),
     pins.pin_backward_identities,
     lambda lib: pins.pin_backward_autograd(pins.synthetic.Workload("gb", 24, 64, 3, 20, 5, "f32", "random"),
