@@ -23,7 +23,8 @@ import synthetic
 METRIC = "PKM lookups(tokens)/sec + value-gather HBM GB/s, N=1M, k=32, 4 heads"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 FP32_MFMA_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix
-ELT_BYTES = {"f32": 4, "bf16": 2, "e4m3": 1}
+ELT_BYTES = {"f32": 4, "bf16": 2, "e4m3": 1, "int8": 1, "int4": 0.5}
+SCALED = ("e4m3", "int8", "int4")  # tables with a per-row fp32 scale
 ROOT = os.path.dirname(os.path.abspath(__file__))
 # Sources of each kernel: measured HBM traffic is only reported while they
 # are unchanged since the counters were taken.
@@ -55,8 +56,8 @@ def per_token_work(wl):
         "query_flop": 2.0 * wl.H * wl.D * wl.D,              # a1: Wq[h] . x for every head
         "score_flop": 2.0 * wl.H * wl.n * wl.D,              # a3: 2 halves x n subkeys x D/2
         "select_bytes": wl.H * (2 * wl.n * 4 + wl.k * 8),    # a4-a6: read half scores, write idx + w
-        # a7: the gathered rows (+ one fp32 scale per row for E4M3 tables)
-        "gather_bytes": wl.H * wl.k * (wl.D * ELT_BYTES[wl.table] + (4 if wl.table == "e4m3" else 0)),
+        # a7: the gathered rows (+ one fp32 scale per row for the scaled tables)
+        "gather_bytes": wl.H * wl.k * (wl.D * ELT_BYTES[wl.table] + (4 if wl.table in SCALED else 0)),
     }
 
 

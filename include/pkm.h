@@ -64,10 +64,18 @@ typedef enum {
     PKM_E_DEVICE = 4       /* HIP runtime or launch error */
 } pkm_status;
 
+/* Storage of the value table.  The table is the whole memory cost of the
+ * layer and suits a lower precision than the rest of the model ("Product-Key
+ * Memory", the note after the code listing); every format is decoded to
+ * fp32 in registers and accumulated in fp32. */
 typedef enum {
-    PKM_VALUES_F32 = 0,     /* float32 rows */
-    PKM_VALUES_BF16 = 1,    /* bfloat16 rows (uint16 bit patterns) */
-    PKM_VALUES_FP8_E4M3 = 2 /* OCP E4M3FN bytes, row r scaled by value_scale[r] */
+    PKM_VALUES_F32 = 0,      /* float32 rows */
+    PKM_VALUES_BF16 = 1,     /* bfloat16 rows (uint16 bit patterns) */
+    PKM_VALUES_FP8_E4M3 = 2, /* OCP E4M3FN bytes, row r scaled by value_scale[r] */
+    PKM_VALUES_INT8 = 3,     /* two's complement int8 codes, row r scaled by value_scale[r] */
+    PKM_VALUES_INT4 = 4      /* two's complement int4 codes, two per byte (element 2i in the
+                                low nibble of byte i, 2i+1 in the high one): a row is D/2
+                                bytes; row r scaled by value_scale[r] */
 } pkm_value_type;
 
 typedef struct {
@@ -95,8 +103,9 @@ typedef struct {
     const float *bn_gamma;    /* [H, D] */
     const float *bn_beta;     /* [H, D] */
     const float *subkeys;     /* [H, 2, n, D/2]: half p of head h */
-    const void *values;       /* [N, D] of value_type, N = n*n */
-    const float *value_scale; /* [N] for PKM_VALUES_FP8_E4M3, else ignored (may be NULL) */
+    const void *values;       /* [N, D] of value_type ([N, D/2] bytes for int4), N = n*n */
+    const float *value_scale; /* [N] for the E4M3, int8 and int4 tables, else ignored
+                                 (may be NULL) */
 } pkm_params;
 
 typedef struct pkm_ctx pkm_ctx; /* opaque; owned by the library */
@@ -238,6 +247,16 @@ pkm_status pkm_backward_batch_stats(pkm_ctx *ctx, const pkm_params *p, int64_t B
                                     const int32_t *idx, const float *weights, const float *dout,
                                     const float *batch_mean, const float *batch_var, const pkm_grads *grads,
                                     void *workspace, size_t workspace_bytes, void *stream);
+
+/* Slot usage ("Product-Key Memory", §Keeping the memory in use: a slot that
+ * is never selected receives no gradient, and usage can collapse to a few
+ * thousand live rows out of a million): counts[r] += the number of entries
+ * of idx [B, rows_per_token] (e.g. pkm_forward's [B, H, k]) equal to r.
+ * counts [n_keys^2] uint32, caller-owned, accumulated across calls.  Rows
+ * outside [0, N) are clamped into it (memory-safe).  Integer counts: the
+ * result does not depend on the order of the updates. */
+pkm_status pkm_usage(pkm_ctx *ctx, int64_t B, int32_t rows_per_token, const int32_t *idx, uint32_t *counts,
+                     void *stream);
 
 /* A static description of a status code. */
 const char *pkm_status_str(pkm_status s);

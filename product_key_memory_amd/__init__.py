@@ -9,7 +9,7 @@ package is the thin Python binding: torch provides device memory and
 streams, nothing else.
 """
 from ._binding import (  # noqa: F401
-    EXPORTS, LIB_PATH, PKM_E_ARG, PKM_E_DEVICE, PKM_E_NOMEM, PKM_E_UNSUPPORTED, PKM_OK, VALUE_TYPES, Config,
+    EXPORTS, LIB_PATH, PKM_E_ARG, PKM_E_DEVICE, PKM_E_NOMEM, PKM_E_UNSUPPORTED, PKM_OK, SCALED, VALUE_TYPES, Config,
     Memory, Params, PkmError, config_check, last_error, load_library, make_config, status_str, workspace_bytes,
 )
 
@@ -18,7 +18,9 @@ def params_to_device(p, table, device="cuda"):
     """Copies host (numpy) parameters to device tensors and wraps them.
 
     p: dict with wq, mean, var, gamma, beta, subkeys, values and (E4M3 tables)
-    scale; values hold fp32 numbers, bf16 bits (uint16) or E4M3 bits (uint8).
+    scale; values hold fp32 numbers, bf16 bits (uint16), E4M3 bits (uint8),
+    int8 codes or packed int4 codes ([N, D/2] uint8); E4M3, int8 and int4
+    tables carry row scales.
     """
     import numpy as np
     import torch
@@ -31,8 +33,12 @@ def params_to_device(p, table, device="cuda"):
         v = dev(values.view(np.int16)).view(torch.bfloat16)
     elif table == "e4m3":
         v = dev(values.view(np.uint8)).view(torch.float8_e4m3fn)
+    elif table == "int8":
+        v = dev(values.view(np.int8))
+    elif table == "int4":
+        v = dev(values.view(np.uint8))  # [N, D/2]: two codes per byte
     else:
         v = dev(values.astype(np.float32, copy=False))
-    scale = dev(p["scale"]) if table == "e4m3" else None
+    scale = dev(p["scale"]) if table in SCALED else None
     return Params(dev(p["wq"]), dev(p["mean"]), dev(p["var"]), dev(p["gamma"]), dev(p["beta"]), dev(p["subkeys"]), v,
                   scale)

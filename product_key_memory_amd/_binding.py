@@ -11,14 +11,15 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libpkm.so")
 
 PKM_OK, PKM_E_ARG, PKM_E_UNSUPPORTED, PKM_E_NOMEM, PKM_E_DEVICE = range(5)
-VALUE_TYPES = {"f32": 0, "bf16": 1, "e4m3": 2}
+VALUE_TYPES = {"f32": 0, "bf16": 1, "e4m3": 2, "int8": 3, "int4": 4}
+SCALED = ("e4m3", "int8", "int4")  # tables with a per-row fp32 scale
 
 # Every symbol include/pkm.h declares.
 EXPORTS = (
     "pkm_config_check", "pkm_workspace_bytes", "pkm_create", "pkm_destroy", "pkm_forward", "pkm_query",
     "pkm_score", "pkm_select", "pkm_gather", "pkm_flat_workspace_bytes", "pkm_flat_search",
     "pkm_backward_workspace_bytes", "pkm_backward", "pkm_forward_batch_stats", "pkm_backward_batch_stats",
-    "pkm_status_str", "pkm_last_error",
+    "pkm_usage", "pkm_status_str", "pkm_last_error",
 )
 
 
@@ -67,6 +68,7 @@ def load_library(path=LIB_PATH):
         "pkm_flat_workspace_bytes": (ctypes.c_int, [cfg_p, i64, ctypes.POINTER(ctypes.c_size_t)]),
         "pkm_flat_search": (ctypes.c_int, [vp, par_p, i64, vp, vp, ctypes.c_size_t, vp, vp, vp]),
         "pkm_backward_workspace_bytes": (ctypes.c_int, [cfg_p, ctypes.POINTER(ctypes.c_size_t)]),
+        "pkm_usage": (ctypes.c_int, [vp, i64, i32, vp, vp, vp]),
         "pkm_forward_batch_stats": (ctypes.c_int, [vp, par_p, i64, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp]),
         "pkm_backward_batch_stats": (ctypes.c_int, [vp, par_p, i64, vp, vp, vp, vp, vp, vp,
                                                     ctypes.POINTER(GradsStruct), vp, ctypes.c_size_t, vp]),
@@ -129,7 +131,8 @@ def _ptr(t):
 
 
 # Accepted storage dtypes of the value table (bit patterns are what matter).
-_DT = {"f32": ("float32",), "bf16": ("bfloat16", "int16", "uint16"), "e4m3": ("float8_e4m3fn", "uint8", "int8")}
+_DT = {"f32": ("float32",), "bf16": ("bfloat16", "int16", "uint16"), "e4m3": ("float8_e4m3fn", "uint8", "int8"),
+       "int8": ("int8", "uint8"), "int4": ("uint8", "int8")}
 
 
 def _expect(t, name, shape, dtype, device=None):
@@ -224,8 +227,8 @@ class Memory:
             _expect(t["subkeys"], "subkeys", (H, 2, n, D // 2), "float32", dev)
         if "values" in parts:
             vt = self.value_type
-            _expect(t["values"], "values", (n * n, D), _DT[vt], dev)
-            if vt == "e4m3":
+            _expect(t["values"], "values", (n * n, D // 2 if vt == "int4" else D), _DT[vt], dev)
+            if vt in SCALED:
                 _expect(t["value_scale"], "value_scale", (n * n,), "float32", t["values"].device)
 
     def forward(self, params, x, out=None, idx=None, weights=None, stream=None, keep_selection=True):
@@ -295,6 +298,20 @@ class Memory:
         _check(self.lib.pkm_gather(self._ctx, ctypes.byref(params.struct), B, R, _ptr(idx), _ptr(weights),
                                    _ptr(out), _stream_handle(stream)))
         return out
+
+    def usage(self, idx, counts=None, stream=None):
+        """Slot usage: counts [n_keys^2] uint32 (int32 accepted) += how often
+        each row occurs in idx [B, ...] (int32).  counts None: fresh zeros."""
+        torch = _torch()
+        B = idx.shape[0]
+        R = idx.numel() // max(B, 1)
+        N = self.n_keys * self.n_keys
+        _expect(idx, "idx", tuple(idx.shape), "int32")
+        if counts is None:
+            counts = torch.zeros(N, dtype=torch.int32, device=idx.device)
+        _expect(counts, "counts", (N,), ("int32", "uint32"), idx.device)
+        _check(self.lib.pkm_usage(self._ctx, B, max(R, 1), _ptr(idx), _ptr(counts), _stream_handle(stream)))
+        return counts
 
     def backward_workspace_bytes(self):
         n = ctypes.c_size_t()

@@ -44,6 +44,22 @@ struct Fmt<2> {  // OCP E4M3 + row scale
     static constexpr int EPL = 16;
     static constexpr int BYTES = 1;
 };
+template <>
+struct Fmt<3> {  // int8 + row scale
+    static constexpr int EPL = 16;
+    static constexpr int BYTES = 1;
+};
+template <>
+struct Fmt<4> {  // int4, two per byte (even element low) + row scale
+    static constexpr int EPL = 32;
+    static constexpr int BYTES = 0;  // half a byte per element: see elem_bytes
+};
+
+template <int VT>
+__host__ __device__ __forceinline__ int64_t elem_bytes(int64_t c)
+{
+    return VT == 4 ? c / 2 : c * Fmt<VT>::BYTES;
+}
 
 typedef float floatx2 __attribute__((ext_vector_type(2)));
 
@@ -62,7 +78,7 @@ __device__ __forceinline__ float dot_row(const uint4 &v, const float *d)
             s = fmaf(__uint_as_float(w[i] << 16), d[2 * i], s);
             s = fmaf(__uint_as_float(w[i] & 0xFFFF0000u), d[2 * i + 1], s);
         }
-    } else {
+    } else if constexpr (VT == 2) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const floatx2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
@@ -72,6 +88,16 @@ __device__ __forceinline__ float dot_row(const uint4 &v, const float *d)
             s = fmaf(hi.x, d[4 * i + 2], s);
             s = fmaf(hi.y, d[4 * i + 3], s);
         }
+    } else if constexpr (VT == 3) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) s = fmaf((float)((int32_t)(w[i] << (24 - 8 * j)) >> 24), d[4 * i + j], s);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) s = fmaf((float)((int32_t)(w[i] << (28 - 4 * j)) >> 28), d[8 * i + j], s);
     }
     return s;
 }
@@ -133,12 +159,12 @@ __global__ __launch_bounds__(64 * WAVES) void value_backward_kernel(const uint8_
                                                                      const float *__restrict__ dout,
                                                                      float *__restrict__ dt)
 {
-    constexpr int EPL = Fmt<VT>::EPL, BYTES = Fmt<VT>::BYTES, U = 8;
+    constexpr int EPL = Fmt<VT>::EPL, U = 8;
     const int lane = threadIdx.x & 63;
     const int64_t pair = (int64_t)blockIdx.x * WAVES + (threadIdx.x >> 6);
     if (pair >= pairs) return;
     const int64_t b = pair / H;
-    const int64_t row_bytes = (int64_t)D * BYTES;
+    const int64_t row_bytes = elem_bytes<VT>(D);
     const int my_row = lane < k ? min(max(idx[pair * k + lane], 0), N - 1) : 0;
     const float my_w = lane < k ? w[pair * k + lane] : 0.0f;
     float my_g = 0.0f;
@@ -163,7 +189,7 @@ __global__ __launch_bounds__(64 * WAVES) void value_backward_kernel(const uint8_
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int r = __builtin_amdgcn_readlane(my_row, min(j0 + u, k - 1));
-                v[u] = active ? *reinterpret_cast<const uint4 *>(values + (int64_t)r * row_bytes + (int64_t)c0 * BYTES)
+                v[u] = active ? *reinterpret_cast<const uint4 *>(values + (int64_t)r * row_bytes + elem_bytes<VT>(c0))
                               : make_uint4(0, 0, 0, 0);
             }
 #pragma unroll
@@ -173,7 +199,7 @@ __global__ __launch_bounds__(64 * WAVES) void value_backward_kernel(const uint8_
         for (int u = 0; u < U; ++u) {
             if (j0 + u >= k) break;
             float g = wave_sum(part[u]);
-            if constexpr (VT == 2) g *= scale[__builtin_amdgcn_readlane(my_row, j0 + u)];
+            if constexpr (VT >= 2) g *= scale[__builtin_amdgcn_readlane(my_row, j0 + u)];
             if (lane == j0 + u) my_g = g;
         }
     }
@@ -583,7 +609,7 @@ template <int VT>
 hipError_t launch_value_backward(const void *values, const float *scale, int D, int N, int64_t pairs, int H, int k,
                                  const int32_t *idx, const float *w, const float *dout, float *dt, hipStream_t st)
 {
-    const int slices = (D * Fmt<VT>::BYTES + 1023) / 1024;
+    const int slices = (int)((elem_bytes<VT>(D) + 1023) / 1024);
     const int64_t blocks = (pairs + WAVES - 1) / WAVES;
     hipLaunchKernelGGL(value_backward_kernel<VT>, dim3((unsigned)blocks), dim3(64 * WAVES), 0, st,
                        static_cast<const uint8_t *>(values), scale, D, N, pairs, H, k, slices, idx, w, dout, dt);
@@ -628,7 +654,9 @@ hipError_t launch_value_backward(const void *values, const float *scale, int val
     switch (value_type) {
     case 0: return launch_value_backward<0>(values, scale, D, N, pairs, H, k, idx, w, dout, dt, st);
     case 1: return launch_value_backward<1>(values, scale, D, N, pairs, H, k, idx, w, dout, dt, st);
-    default: return launch_value_backward<2>(values, scale, D, N, pairs, H, k, idx, w, dout, dt, st);
+    case 2: return launch_value_backward<2>(values, scale, D, N, pairs, H, k, idx, w, dout, dt, st);
+    case 3: return launch_value_backward<3>(values, scale, D, N, pairs, H, k, idx, w, dout, dt, st);
+    default: return launch_value_backward<4>(values, scale, D, N, pairs, H, k, idx, w, dout, dt, st);
     }
 }
 
@@ -670,6 +698,13 @@ hipError_t launch_bn_grads(const float *dqhat, const float *q, const float *mean
 }
 
 int64_t scan_blocks(int N) { return (N + kScanBlock - 1) / kScanBlock; }
+
+hipError_t launch_usage(const int32_t *idx, int64_t M, int N, uint32_t *counts, hipStream_t st)
+{
+    if (M <= 0) return hipSuccess;
+    hipLaunchKernelGGL(count_rows_kernel, dim3(grid_of(M, 256)), dim3(256), 0, st, idx, M, N, counts);
+    return hipGetLastError();
+}
 
 hipError_t launch_value_grad(const int32_t *idx, int64_t M, int N, int D, int per_token, const float *w,
                              const float *dout, uint32_t *count, uint32_t *cursor, uint32_t *offs,

@@ -4,10 +4,12 @@
 // listing: the table is never touched as a dense matrix, only the selected
 // rows are read).
 //
-// This is the HBM-bound step: every selected row is a random 1-4 KiB read.
+// This is the HBM-bound step: every selected row is a random 0.5-4 KiB read.
 // A wave64 owns one (token, column slice): each lane reads 16 contiguous bytes
-// of a row (4 fp32, 8 bf16 or 16 E4M3 values), so one row-slice is one fully
-// coalesced 1 KiB request, and keeps its fp32 partial sums in registers.  The
+// of a row (4 fp32, 8 bf16, 16 E4M3 or int8, or 32 int4 values), so one
+// row-slice is one fully coalesced 1 KiB request, and keeps its fp32 partial
+// sums in registers.  Scaled formats (E4M3, int8, int4) fold the row's scale
+// into the weight.  The
 // token's (row, weight) pairs are read once into lanes and broadcast with
 // v_readlane, so every row address is a scalar base plus the lane offset.
 // Sixteen row loads are issued before any is consumed to keep enough bytes in
@@ -39,6 +41,23 @@ struct Fmt<2> {  // OCP E4M3 + row scale
     static constexpr int EPL = 16;
     static constexpr int BYTES = 1;
 };
+template <>
+struct Fmt<3> {  // int8 + row scale
+    static constexpr int EPL = 16;
+    static constexpr int BYTES = 1;
+};
+template <>
+struct Fmt<4> {  // two's complement int4, two per byte (even element low) + row scale
+    static constexpr int EPL = 32;
+    static constexpr int BYTES = 0;  // half a byte per element: see elem_bytes
+};
+
+// bytes of a row up to element c (c a multiple of EPL)
+template <int VT>
+__host__ __device__ __forceinline__ int64_t elem_bytes(int64_t c)
+{
+    return VT == 4 ? c / 2 : c * Fmt<VT>::BYTES;
+}
 
 typedef float floatx2 __attribute__((ext_vector_type(2)));
 
@@ -55,7 +74,7 @@ __device__ __forceinline__ void accumulate(float (&acc)[Fmt<VT>::EPL], const uin
             acc[2 * i] = fmaf(wt, __uint_as_float(w[i] << 16), acc[2 * i]);
             acc[2 * i + 1] = fmaf(wt, __uint_as_float(w[i] & 0xFFFF0000u), acc[2 * i + 1]);
         }
-    } else {
+    } else if constexpr (VT == 2) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const floatx2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
@@ -65,6 +84,20 @@ __device__ __forceinline__ void accumulate(float (&acc)[Fmt<VT>::EPL], const uin
             acc[4 * i + 2] = fmaf(wt, hi.x, acc[4 * i + 2]);
             acc[4 * i + 3] = fmaf(wt, hi.y, acc[4 * i + 3]);
         }
+    } else if constexpr (VT == 3) {
+        // byte j of a word, sign-extended: shift it to the top, then arithmetic shift down
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[4 * i + j] = fmaf(wt, (float)((int32_t)(w[i] << (24 - 8 * j)) >> 24), acc[4 * i + j]);
+    } else {
+        // nibble j of a word (element 8 i + j), sign-extended the same way
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                acc[8 * i + j] = fmaf(wt, (float)((int32_t)(w[i] << (28 - 4 * j)) >> 28), acc[8 * i + j]);
     }
 }
 
@@ -75,7 +108,7 @@ __global__ __launch_bounds__(64 * WAVES) void gather_kernel(const uint8_t *__res
                                                             const float *__restrict__ w, float *__restrict__ out)
 {
     constexpr int EPL = Fmt<VT>::EPL;
-    constexpr int BYTES = Fmt<VT>::BYTES;
+    constexpr bool SCALED = VT >= 2;
     const int lane = threadIdx.x & 63;
     const int64_t wid = (int64_t)blockIdx.x * WAVES + (threadIdx.x >> 6);
     if (wid >= B * slices) return;
@@ -83,8 +116,8 @@ __global__ __launch_bounds__(64 * WAVES) void gather_kernel(const uint8_t *__res
     const int s = (int)(wid - b * slices);
     const int c0 = (s * 64 + lane) * EPL;  // first column of this lane
     const bool active = c0 < D;
-    const int64_t row_bytes = (int64_t)D * BYTES;
-    const uint8_t *col = values + (active ? (int64_t)c0 * BYTES : 0);
+    const int64_t row_bytes = elem_bytes<VT>(D);
+    const uint8_t *col = values + (active ? elem_bytes<VT>(c0) : 0);
 
     float acc[EPL];
 #pragma unroll
@@ -104,7 +137,7 @@ __global__ __launch_bounds__(64 * WAVES) void gather_kernel(const uint8_t *__res
             for (int u = 0; u < UNROLL; ++u) {
                 const int row = min(max(__builtin_amdgcn_readlane(my_row, r + u), 0), N - 1);
                 wt[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), r + u));
-                if constexpr (VT == 2) wt[u] *= scale[row];
+                if constexpr (SCALED) wt[u] *= scale[row];
                 v[u] = active ? *reinterpret_cast<const uint4 *>(col + (int64_t)row * row_bytes) : make_uint4(0, 0, 0, 0);
             }
 #pragma unroll
@@ -113,7 +146,7 @@ __global__ __launch_bounds__(64 * WAVES) void gather_kernel(const uint8_t *__res
         for (; r < nr; ++r) {
             const int row = min(max(__builtin_amdgcn_readlane(my_row, r), 0), N - 1);
             float wt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), r));
-            if constexpr (VT == 2) wt *= scale[row];
+            if constexpr (SCALED) wt *= scale[row];
             const uint4 v = active ? *reinterpret_cast<const uint4 *>(col + (int64_t)row * row_bytes) : make_uint4(0, 0, 0, 0);
             accumulate<VT>(acc, v, wt);
         }
@@ -147,7 +180,9 @@ hipError_t launch_gather(const void *values, const float *scale, int value_type,
     switch (value_type) {
     case 0: return launch<0>(values, scale, D, N, B, R, idx, w, out, stream);
     case 1: return launch<1>(values, scale, D, N, B, R, idx, w, out, stream);
-    default: return launch<2>(values, scale, D, N, B, R, idx, w, out, stream);
+    case 2: return launch<2>(values, scale, D, N, B, R, idx, w, out, stream);
+    case 3: return launch<3>(values, scale, D, N, B, R, idx, w, out, stream);
+    default: return launch<4>(values, scale, D, N, B, R, idx, w, out, stream);
     }
 }
 

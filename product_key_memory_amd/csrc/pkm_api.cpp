@@ -87,7 +87,7 @@ pkm_status check_config(const pkm_config *c)
     if ((int64_t)c->n_keys * c->n_keys >= ((int64_t)1 << 31))
         return fail(PKM_E_ARG, "n_keys^2 must be < 2^31 (got n_keys = %d)", c->n_keys);
     if (c->k < 1 || c->k > c->n_keys) return fail(PKM_E_ARG, "k must be in [1, n_keys] (got %d)", c->k);
-    if (c->value_type < PKM_VALUES_F32 || c->value_type > PKM_VALUES_FP8_E4M3)
+    if (c->value_type < PKM_VALUES_F32 || c->value_type > PKM_VALUES_INT4)
         return fail(PKM_E_ARG, "unknown value_type %d", c->value_type);
     if (!(c->bn_eps > 0.0f) || !(c->bn_eps < 1.0e30f)) return fail(PKM_E_ARG, "bn_eps must be finite and > 0");
     if (c->max_batch < 1 || c->max_batch > kMaxBatch || c->max_batch * c->heads > ((int64_t)1 << 31))
@@ -137,7 +137,7 @@ pkm_status check_value_params(const pkm_config &c, const pkm_params *p)
     if (!p) return fail(PKM_E_ARG, "params is NULL");
     pkm_status s;
     if ((s = need(p->values, "values"))) return s;
-    if (c.value_type == PKM_VALUES_FP8_E4M3 && (s = need(p->value_scale, "value_scale"))) return s;
+    if (c.value_type >= PKM_VALUES_FP8_E4M3 && (s = need(p->value_scale, "value_scale"))) return s;
     return PKM_OK;
 }
 
@@ -732,6 +732,22 @@ pkm_status pkm_forward_batch_stats(pkm_ctx *ctx, const pkm_params *p, int64_t B,
         (s = launched(pkm::launch_gather(p->values, p->value_scale, c.value_type, c.dim, c.n_keys * c.n_keys, B,
                                          c.heads * c.k, ci, cw, out, st),
                       "gather")))
+        return s;
+    return ok();
+}
+
+pkm_status pkm_usage(pkm_ctx *ctx, int64_t B, int32_t rows_per_token, const int32_t *idx, uint32_t *counts,
+                     void *stream)
+{
+    pkm_status s;
+    if ((s = check_ctx(ctx)) || (s = check_batch(ctx->cfg, B))) return s;
+    if (rows_per_token < 1) return fail(PKM_E_ARG, "rows_per_token must be >= 1 (got %d)", rows_per_token);
+    if (B == 0) return ok();
+    if ((s = need(idx, "idx")) || (s = need(counts, "counts"))) return s;
+    const pkm_config &c = ctx->cfg;
+    if ((s = launched(pkm::launch_usage(idx, B * rows_per_token, c.n_keys * c.n_keys, counts,
+                                        static_cast<hipStream_t>(stream)),
+                      "usage")))
         return s;
     return ok();
 }

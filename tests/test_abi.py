@@ -61,7 +61,9 @@ GOOD = dict(dim=1024, heads=4, n_keys=1024, k=32, value_type="bf16", bn_eps=1e-5
     (dict(k=0), pk.PKM_E_ARG),
     (dict(n_keys=16, k=17), pk.PKM_E_ARG),         # topk needs k <= n_keys
     (dict(k=65), pk.PKM_E_UNSUPPORTED),
-    (dict(value_type=3), pk.PKM_E_ARG),
+    (dict(value_type=5), pk.PKM_E_ARG),            # no such table format
+    (dict(value_type="int8"), pk.PKM_OK),
+    (dict(value_type="int4"), pk.PKM_OK),
     (dict(bn_eps=0.0), pk.PKM_E_ARG),
     (dict(bn_eps=-1.0), pk.PKM_E_ARG),
     (dict(bn_eps=float("nan")), pk.PKM_E_ARG),

@@ -84,6 +84,8 @@ def compare(got, ref, names=NAMES):
     (synthetic.Workload("be4", 77, 192, 2, 33, 9, "e4m3", "random"), True),  # E4M3 + row scales, D = 3 * 64
     (synthetic.Workload("bkn", 40, 64, 1, 12, 12, "f32", "random"), False),  # k = n_keys
     (synthetic.Workload("bk1", 50, 64, 2, 30, 1, "bf16", "random"), True),   # k = 1: no gradient to the scores
+    (synthetic.Workload("bi8", 60, 128, 2, 24, 8, "int8", "random"), True),  # int8 table + row scales
+    (synthetic.Workload("bi4", 60, 192, 2, 24, 8, "int4", "random"), True),  # int4 table
 ])
 def test_backward_against_oracle(torch, wl, gamma_beta):
     params, x, dout = case(wl, 2, gamma_beta)

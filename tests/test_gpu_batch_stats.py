@@ -24,7 +24,7 @@ from tests.test_gpu_backward import compare
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"f32": 1e-4, "bf16": 2e-2, "e4m3": 2e-2}
+TOL = {"f32": 1e-4, "bf16": 2e-2, "e4m3": 2e-2, "int8": 2e-2, "int4": 2e-2}
 
 
 @pytest.fixture(scope="module")

@@ -19,7 +19,7 @@ from tests.support import say
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"f32": 1e-4, "bf16": 2e-2, "e4m3": 2e-2}
+TOL = {"f32": 1e-4, "bf16": 2e-2, "e4m3": 2e-2, "int8": 2e-2, "int4": 2e-2}
 
 
 @pytest.fixture(scope="module")
@@ -87,6 +87,8 @@ def test_tiny_product_search_equals_flat_search(torch):
     dict(B=64, D=64, H=2, n=2048, k=64, table="bf16"),     # large n with the largest k
     dict(B=1, D=64, H=1, n=2, k=2, table="f32"),           # smallest memory
     dict(B=300, D=320, H=5, n=33, k=33, table="e4m3"),     # k = n, odd sizes, random BN
+    dict(B=200, D=256, H=2, n=50, k=10, table="int8"),     # int8 table + row scales
+    dict(B=150, D=192, H=3, n=40, k=16, table="int4"),     # int4 table: a row is D/2 bytes, half-active lanes
 ])
 def test_forward_edge_shapes(torch, shape):
     wl = synthetic.Workload("edge", shape["B"], shape["D"], shape["H"], shape["n"], shape["k"], shape["table"],
@@ -188,3 +190,23 @@ def test_forward_full_size_sampled(torch, name):
     invariants(wl, idx, w)
     err = compare(wl, params, x, out, idx, w, tokens=tokens)
     print(f"{name}: max row error {err.max():.3g} over {len(tokens)} sampled tokens", flush=True)
+
+
+def test_usage_counts(torch):
+    """pkm_usage on the forward's winners equals the oracle's counts; a
+    second call adds; rows repeated by identical tokens count each time."""
+    wl = synthetic.WORKLOADS["mid"]
+    params = synthetic.make_params(wl)
+    x = synthetic.make_x(wl)
+    x[500:600] = x[7]  # a hot token: its rows occur 101 times per head
+    _, idx, _ = support.gpu_forward(wl, params, x)
+    mem = pk.Memory(wl.D, wl.H, wl.n, wl.k, wl.table)
+    say("usage counts")
+    it = torch.from_numpy(idx).to(support.device())
+    counts = mem.usage(it)
+    counts = mem.usage(it, counts)
+    torch.cuda.synchronize()
+    got = counts.cpu().numpy().astype(np.int64)
+    ref = oracle.usage(idx, wl.N, oracle.usage(idx, wl.N)).astype(np.int64)
+    assert (got == ref).all()
+    assert got.sum() == 2 * idx.size and got.max() >= 2 * 101

@@ -49,6 +49,46 @@ def test_e4m3_decode_every_code(torch):
     assert (out[1][ok[::-1]] == 0.5 * ref[::-1][ok[::-1]]).all()
 
 
+@pytest.mark.parametrize("table", ["int8", "int4"])
+def test_integer_decode_every_code(torch, table):
+    """Every int8 code (and every int4 code in both nibbles of a byte)
+    through the gather, row scale 1 then 0.25, equals the oracle's decoder
+    times the scale exactly."""
+    say("gather", table, "all codes")
+    D = 256 if table == "int8" else 512
+    mem = pk.Memory(D, 1, 2, 1, table)
+    if table == "int8":
+        codes = np.arange(-128, 128, dtype=np.int8)
+        values = np.zeros((4, D), np.int8)
+        values[0], values[1] = codes, codes[::-1]
+        ref0 = np.array([oracle.int8_to_f64(int(c)) for c in codes])
+        ref1 = ref0[::-1]
+    else:
+        lo, hi = np.meshgrid(np.arange(16, dtype=np.uint8), np.arange(16, dtype=np.uint8), indexing="ij")
+        byte = (lo | (hi << np.uint8(4))).reshape(-1)  # all 256 (low, high) pairs
+        values = np.zeros((4, D // 2), np.uint8)
+        values[0], values[1] = byte, byte[::-1]
+        dec = np.array([oracle.int4_to_f64(c) for c in range(16)])
+
+        def expand(b):
+            out = np.empty(2 * b.size)
+            out[0::2], out[1::2] = dec[b & 0xF], dec[b >> 4]
+            return out
+
+        ref0, ref1 = expand(byte), expand(byte[::-1])
+    scale = np.array([1.0, 0.25, 1.0, 1.0], np.float32)
+    p = {"wq": np.zeros((1, D, D), np.float32), "mean": np.zeros((1, D), np.float32),
+         "var": np.ones((1, D), np.float32), "gamma": np.ones((1, D), np.float32),
+         "beta": np.zeros((1, D), np.float32), "subkeys": np.zeros((1, 2, 2, D // 2), np.float32),
+         "values": values, "scale": scale}
+    P = pk.params_to_device(p, table, support.device())
+    idx = _to(torch, np.array([[0], [1]], np.int32))
+    w = _to(torch, np.ones((2, 1), np.float32))
+    out = mem.gather(P, idx, w).cpu().numpy()
+    assert (out[0] == ref0).all()
+    assert (out[1] == 0.25 * ref1).all()
+
+
 def test_bf16_decode_every_code(torch):
     """All 65536 bf16 codes (16 rows of 4096) decode exactly; non-finite codes
     are skipped."""
@@ -68,7 +108,7 @@ def test_bf16_decode_every_code(torch):
     assert (out[ok] == ref[ok]).all()
 
 
-@pytest.mark.parametrize("table", ["f32", "bf16", "e4m3"])
+@pytest.mark.parametrize("table", ["f32", "bf16", "e4m3", "int8", "int4"])
 @pytest.mark.parametrize("D,n,B,R", [(64, 16, 5, 4), (512, 64, 33, 16), (1024, 32, 17, 128), (1024, 32, 9, 130),
                                      (192, 8, 7, 1), (2048, 16, 3, 67)])
 def test_gather_parity(torch, table, D, n, B, R):
