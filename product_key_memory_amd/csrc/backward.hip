@@ -92,12 +92,12 @@ __device__ __forceinline__ float dot_row(const uint4 &v, const float *d)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) s = fmaf((float)((int32_t)(w[i] << (24 - 8 * j)) >> 24), d[4 * i + j], s);
+            for (int j = 0; j < 4; ++j) s = fmaf((float)(int32_t)__builtin_amdgcn_sbfe((int)w[i], 8 * j, 8), d[4 * i + j], s);
     } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) s = fmaf((float)((int32_t)(w[i] << (28 - 4 * j)) >> 28), d[8 * i + j], s);
+            for (int j = 0; j < 8; ++j) s = fmaf((float)(int32_t)__builtin_amdgcn_sbfe((int)w[i], 4 * j, 4), d[8 * i + j], s);
     }
     return s;
 }

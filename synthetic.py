@@ -13,6 +13,8 @@ has N = n*n rows, k winners per head):
                                                  Memory" module's defaults)
   large_batch   B=65536  D=1024 H=4 n=1024 k=32  bf16 table
   large_memory  B=16384  D=1024 H=4 n=2048 k=32  E4M3 table + fp32 row scale
+  default_int8 / default_int4: the default shape with an int8 / int4 table
+                + fp32 row scale
 
 Distributions (second argument of N is the variance):
   x ~ N(0,1); Wq[h] ~ N(0,1/D); subkeys ~ N(0,1); values ~ N(0,1/sqrt(D));
@@ -61,6 +63,9 @@ WORKLOADS = {
         Workload("default", 4096, 1024, 4, 1024, 32, "bf16", "unit"),
         Workload("large_batch", 65536, 1024, 4, 1024, 32, "bf16", "unit"),
         Workload("large_memory", 16384, 1024, 4, 2048, 32, "e4m3", "unit"),
+        # the default shape with the lower-precision tables
+        Workload("default_int8", 4096, 1024, 4, 1024, 32, "int8", "unit"),
+        Workload("default_int4", 4096, 1024, 4, 1024, 32, "int4", "unit"),
     ]
 }
 

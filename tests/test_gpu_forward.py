@@ -179,7 +179,7 @@ def _sample(B):
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("name", ["default", "large_batch", "large_memory"])
+@pytest.mark.parametrize("name", ["default", "large_batch", "large_memory", "default_int8", "default_int4"])
 def test_forward_full_size_sampled(torch, name):
     wl = synthetic.WORKLOADS[name]
     params = synthetic.make_params(wl)
