@@ -510,13 +510,13 @@ __global__ __launch_bounds__(256) void fill_lists_kernel(const int32_t *__restri
 }
 
 // dV[r] += sum over the occurrences o of r, in increasing o (token, head,
-// winner), of w[o] * dout[token(o)].  One wave per kGradRows rows; the wave
+// winner), of w[o] * dout[token(o)].  One wave per kGradRows (8) rows; the wave
 // takes its non-empty rows in turn.  Up to 64 occurrences are put in order
 // by a 64-lane bitonic sort (lane t holds the t-th) and summed over passes
 // of 1024 columns (lane l: columns 4 l + 256 q, q < 4; the old row and two
 // occurrences' dout rows in flight), then added to the row; more are
 // walked by repeated minimum search, each added into the row in turn.
-constexpr int kGradRows = 16;
+constexpr int kGradRows = 8;
 __global__ __launch_bounds__(64 * WAVES) void value_grad_kernel(const uint32_t *__restrict__ count,
                                                                const uint32_t *__restrict__ offs,
                                                                const uint32_t *__restrict__ list, int N, int D,
@@ -581,9 +581,14 @@ __global__ __launch_bounds__(64 * WAVES) void value_grad_kernel(const uint32_t *
                 }
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    if (act[q])
-                        *reinterpret_cast<float4 *>(out + col[q]) = make_float4(
-                            old[q].x + acc[q].x, old[q].y + acc[q].y, old[q].z + acc[q].z, old[q].w + acc[q].w);
+                    if (act[q]) {
+                        const float4 nv = make_float4(old[q].x + acc[q].x, old[q].y + acc[q].y, old[q].z + acc[q].z,
+                                                      old[q].w + acc[q].w);
+                        // written once per call: stream it out of the caches
+                        typedef float f4v __attribute__((ext_vector_type(4)));
+                        const f4v nvv = {nv.x, nv.y, nv.z, nv.w};
+                        __builtin_nontemporal_store(nvv, reinterpret_cast<f4v *>(out + col[q]));
+                    }
             }
         } else {
             // more than 64: walk the occurrences in increasing id (one wave

@@ -35,6 +35,8 @@
 // stage (41 KiB, three workgroups per CU).
 #include "pkm_internal.h"
 
+#include <atomic>
+
 namespace pkm {
 namespace {
 
@@ -237,10 +239,18 @@ hipError_t launch_variant(const GemmArgs &a, hipStream_t stream)
     const auto kernel = &gemm_nt_f32_kernel<T, BN_EPILOGUE, STREAM_OUT, PRODUCT_B, ACCUMULATE>;
     if (T::LDS_BYTES > 65536) {
         // Dynamic LDS above 64 KiB must be allowed per kernel (gfx950 has
-        // 160 KiB per CU); done once per kernel per process.
-        static const hipError_t allowed = hipFuncSetAttribute(
-            reinterpret_cast<const void *>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize, (int)T::LDS_BYTES);
-        if (allowed != hipSuccess) return allowed;
+        // 160 KiB per CU); done once per kernel and device.
+        static std::atomic<uint64_t> allowed_on{0};
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return e;
+        const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
+        if (!bit || !(allowed_on.load(std::memory_order_acquire) & bit)) {
+            e = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    (int)T::LDS_BYTES);
+            if (e != hipSuccess) return e;
+            allowed_on.fetch_or(bit, std::memory_order_acq_rel);
+        }
     }
     const dim3 grid((unsigned)tile_count<T>(a), a.batch);
     hipLaunchKernelGGL(kernel, grid, dim3(T::THREADS), T::LDS_BYTES, stream, a);

@@ -551,6 +551,16 @@ pkm_status run_backward(pkm_ctx *ctx, const pkm_params *p, int64_t B, const floa
         const int nb32 = (int)((nb + 31) / 32 * 32);
         const float *xc = x + b0 * D, *doutc = dout + b0 * D, *wc = weights + b0 * H * k;
         const int32_t *ic = idx + b0 * H * k;
+        // everything but the value gradient flows through the scores
+        const bool through_scores = grads->dx || grads->dwq || grads->dbn_gamma || grads->dsubkeys;
+        if (!through_scores) {
+            if (grads->dvalues &&
+                (s = launched(pkm::launch_value_grad(ic, nb * H * k, N, D, H * k, wc, doutc, count, cursor, offs,
+                                                     block_sum, list, grads->dvalues, st),
+                              "value gradient")))
+                return s;
+            continue;
+        }
         // q before BN
         pkm::GemmArgs qa = query_args(c, p, nb, xc, Q);
         qa.bn_mean = qa.bn_var = qa.bn_gamma = qa.bn_beta = nullptr;
