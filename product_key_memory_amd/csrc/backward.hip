@@ -10,7 +10,7 @@
 //   dq^_p = sum_j dt_j C[h,p,i_p(j)]              dqhat_kernel
 //   dq    = dq^ gamma / sqrt(var + eps)           dqhat_kernel
 //   dgamma += dq^ xhat, dbeta += dq^              colsum kernels (token order)
-//   dWq[h] += dq^T x, dx = dq Wq                  fp32 MFMA GEMMs
+//   dWq[h] += dq^T x, dx = dq Wq                  fp32-accurate MFMA GEMMs
 //   dC[h,p,i] += sum_b G[h,p][i][b] q^_p[b]       dsub_kernel (G is ~k/n
 //                                                 dense: a scan per subkey
 //                                                 row, not a GEMM)

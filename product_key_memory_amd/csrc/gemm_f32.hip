@@ -1,4 +1,5 @@
-// fp32 MFMA GEMM for the two dense contractions of the lookup:
+// fp32-accurate GEMM on the matrix cores for the two dense contractions of
+// the lookup:
 //   a1+a2  qhat = BN(x . Wq^T)         M = tokens, N = H*D,     K = D
 //   a3     s_g  = qhat_g . C_g^T       M = tokens, N = n_keys,  K = D/2,
 //                                      one batch entry g = 2h + p per half
@@ -7,32 +8,52 @@
 //
 // Both operands are K-contiguous (x rows, Wq rows, qhat rows, subkey rows),
 // so C = A . B^T with no transposes.  Scores decide the winners, so the
-// contraction stays in fp32: v_mfma_f32_32x32x2_f32, fp32 accumulate.
+// contraction must be as accurate as fp32.
+//
+// Engine: three-piece bf16 splitting (the "bf16x6" product of Henry, Tang
+// and Heinecke, "Leveraging the bfloat16 Artificial Intelligence Datatype
+// For Higher-Precision Computations", ARITH 2019).  Each fp32 operand is
+// split while it is staged into LDS: a0 = bf16(a), a1 = bf16(a - a0),
+// a2 = bf16(a - a0 - a1), round to nearest.  Both subtractions are exact and
+// a - a0 - a1 has at most 8 significant bits, so a = a0 + a1 + a2 exactly
+// (|a1| <= 2^-8 |a|, |a2| <= 2^-16 |a|).  a.b is accumulated in fp32 from the
+// six products of weight >= 2^-16: a0b0, a0b1, a1b0, a0b2, a1b1, a2b0, each
+// exact in the MFMA's fp32 accumulator; the three dropped ones (a1b2, a2b1,
+// a2b2) sum to at most 2^-23 |a||b| (and are random in sign), the size of
+// one fp32 rounding.  v_mfma_f32_32x32x16_bf16 does 16x the work of
+// v_mfma_f32_32x32x2_f32 per cycle, so the six products cost 6/16 of the
+// fp32 instruction's time.
 //
 // Tiling for CDNA4.  A workgroup owns a BM x BN tile of C; each of its
 // WM x WN wave64s owns (BM/WM) x (BN/WN) as 32x32 MFMA blocks.  K advances
-// BK at a time through LDS stages (rows padded by 4 floats so the 16-byte
-// fragment reads of consecutive rows land on distinct banks); the next chunk
-// is loaded into registers while the MFMAs run, and with two stages one
-// barrier per chunk suffices.  Within a chunk, MFMA step t pairs k = t
-// (lanes 0-31) with k = BK/2 + t (lanes 32-63), so each lane's fragment is
-// BK/2 contiguous floats (ds_read_b128 only).
-//   Large grids: 256x256 tiles, 8 waves of 64x128, BK 32, two stages
-//   (147 KB of LDS, one workgroup per CU: operand traffic per flop halves
-//   against 128x128).
+// 16 at a time (one MFMA step) through two LDS stages; chunk t + 1 is split
+// and stored while chunk t is multiplied, and chunk t + 2 is loaded into
+// registers.  An LDS row holds the three pieces' 16 bf16 each (96 bytes)
+// plus 16 bytes of padding, so 16-byte accesses to consecutive rows fall on
+// distinct banks.  Lane l of an MFMA step feeds row (or column) l % 32 with
+// k = 8 (l / 32) .. 8 (l / 32) + 7 of the chunk (one ds_read_b128 per
+// piece); A and B use the same k order, which is all a dot product needs.
+// Staging uses the same lane -> (row, k) pattern, so its 16-byte LDS stores
+// are conflict-free as well.
+//   Large grids: 256x256 tiles, 8 waves of 64x128 (112 KiB of LDS, one
+//   workgroup per CU, two waves per SIMD), run ping-pong: the second half
+//   of the waves starts one barrier later, so on each SIMD one wave issues
+//   MFMAs (at raised priority) while the other does the LDS and VALU work.
 //   Small grids (fewer tiles than CUs at 256x256): 128x128, 4 waves of
-//   64x64, BK 32, one stage.
-// A result that the next kernel reads once (the subkey scores) is stored
-// non-temporally: it reaches HBM during this compute-bound kernel rather than
-// being written back from the caches while the memory-bound gather runs.
+//   64x64 (56 KiB).
+// Epilogue: BN (a1) and accumulated results are staged through LDS a few
+// dozen rows at a time so each store instruction writes whole rows of C in
+// 16-byte runs.  A result that the next kernel reads once (the subkey
+// scores) is stored non-temporally, straight from the accumulators: it
+// reaches HBM during this compute-bound kernel rather than being written
+// back from the caches while the memory-bound gather runs.
 //
 // Flat exact search (the comparator for the product search of
 // §Factorising the key space: every one of the n^2 concatenated keys
 // scored by one full-length dot product).  The B operand is the virtual
 // key matrix: row j = (a, c) is [C0[a]; C1[c]], read from the two subkey
 // sets as K advances (a chunk never straddles the halves).  M is a few
-// dozen tokens, so this uses 32 x 256 tiles: 4 waves of 32 x 64, one LDS
-// stage (41 KiB, three workgroups per CU).
+// dozen tokens, so this uses 32 x 256 tiles: 4 waves of 32 x 64.
 #include "pkm_internal.h"
 
 #include <atomic>
@@ -42,89 +63,136 @@ namespace {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float fx4 __attribute__((ext_vector_type(4)));
+typedef float fx2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
-constexpr int kCUs = 256;  // MI355X compute units
+constexpr int kCUs = 256;     // MI355X compute units
+constexpr int kBK = 16;       // k per chunk: one v_mfma_f32_32x32x16_bf16 step
+constexpr int kPieces = 3;    // bf16 pieces per fp32 operand
+constexpr int kPieceDw = 8;   // dwords per piece in an LDS row (16 bf16)
+constexpr int kRowDw = kPieces * kPieceDw + 4;  // + 16 bytes of padding
 
-template <int BM_, int BN_, int BK_, int WM_, int WN_, int STAGES_>
+template <int BM_, int BN_, int WM_, int WN_>
 struct Tile {
-    static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, STAGES = STAGES_;
-    static constexpr int THREADS = 64 * WM * WN;
-    static constexpr int LDS = BK + 4;                          // floats per LDS row
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, STAGES = 2;
+    static constexpr int WAVES = WM * WN, THREADS = 64 * WAVES;
     static constexpr int TM = BM / WM / 32, TN = BN / WN / 32;  // 32x32 blocks per wave
-    static constexpr int HK = BK / 2;                           // k per lane half within a chunk
-    static constexpr int C4 = BK / 4;                           // float4 per row chunk
-    static constexpr int RPP = THREADS / C4;                    // rows moved per pass
-    static constexpr int PA = BM / RPP, PB = BN / RPP;          // passes per operand
-    static constexpr size_t LDS_BYTES = (size_t)STAGES * (BM + BN) * LDS * sizeof(float);
-    static_assert(BM % RPP == 0 && BN % RPP == 0 && BK % 8 == 0, "tile shape");
+    // Operand rows are staged in groups of 32: lane l of a wave moves row
+    // l % 32 of its group, k = 8 (l / 32) .. + 7 of the chunk (the same
+    // row/k assignment as an MFMA fragment read).  Group g of a chunk is
+    // moved by wave g % WAVES.
+    static constexpr int GROUPS = (BM + BN) / 32;
+    static constexpr int UNITS = (GROUPS + WAVES - 1) / WAVES;  // groups per wave
+    static constexpr size_t LDS_BYTES = (size_t)STAGES * (BM + BN) * kRowDw * sizeof(uint32_t);
+    // Ping-pong when two waves share each SIMD: the second half of the waves
+    // runs one phase behind the first, so on every SIMD one wave issues MFMAs
+    // while the other reads fragments and splits, stores and loads chunks.
+    static constexpr bool PING_PONG = WAVES == 8;
+    // rows of C staged through LDS per epilogue pass
+    static constexpr int EPI_ROWS = BM < 64 ? BM : 64;
+    static_assert(BM % 32 == 0 && BN % 32 == 0 && BM % EPI_ROWS == 0, "tile shape");
+    static_assert((size_t)EPI_ROWS * (BN + 8) * sizeof(float) <= LDS_BYTES, "epilogue staging fits");
+    static_assert(EPI_ROWS * BN / 4 % THREADS == 0 && THREADS % (BN / 4) == 0, "epilogue work divides");
 };
 
-using BigTile = Tile<256, 256, 32, 4, 2, 2>;
-using SmallTile = Tile<128, 128, 32, 2, 2, 1>;
-using KeyTile = Tile<32, 256, 32, 1, 4, 1>;
+using BigTile = Tile<256, 256, 4, 2>;
+using SmallTile = Tile<128, 128, 2, 2>;
+using KeyTile = Tile<32, 256, 1, 4>;
 
-// B row pointers of a thread: plain rows, or the two halves of product keys
-// (k < split reads the first half's row at k, else the second's at k - split).
+// The staging work of one thread: UNITS groups; for each, the global source
+// of its 8 k-values (product-key B rows keep both halves' rows) and its LDS
+// destination in stage 0 (dwords) with the stride between stages.
 template <typename T, bool PRODUCT_B>
-struct BRows {
-    const float *p0[T::PB];
-    const float *p1[PRODUCT_B ? T::PB : 1];
-    __device__ __forceinline__ const float *at(int i, int k, int split) const
+struct Stager {
+    const float *src[T::UNITS];
+    const float *src2[PRODUCT_B ? T::UNITS : 1];
+    int lds[T::UNITS], stage_stride[T::UNITS];
+    bool valid[T::UNITS];
+    fx4 v[T::UNITS][2];
+
+    __device__ __forceinline__ void load(int kt, int split)
     {
-        if constexpr (PRODUCT_B) return k < split ? p0[i] + k : p1[i] + (k - split);
-        return p0[i] + k;
+#pragma unroll
+        for (int u = 0; u < T::UNITS; ++u) {
+            if (!valid[u]) continue;
+            const int k = kt * kBK;
+            const float *q = src[u] + k;
+            if constexpr (PRODUCT_B)
+                if (src2[u] && k >= split) q = src2[u] + (k - split);
+            v[u][0] = *reinterpret_cast<const fx4 *>(q);
+            v[u][1] = *reinterpret_cast<const fx4 *>(q + 4);
+        }
+    }
+
+    // Split the 8 values into their three bf16 pieces; each piece's 16 bytes
+    // go to that piece's part of the LDS row.
+    __device__ __forceinline__ void store(uint32_t *smem, int s) const
+    {
+#pragma unroll
+        for (int u = 0; u < T::UNITS; ++u) {
+            if (!valid[u]) continue;
+            fx2 e[4] = {{v[u][0][0], v[u][0][1]}, {v[u][0][2], v[u][0][3]},
+                        {v[u][1][0], v[u][1][1]}, {v[u][1][2], v[u][1][3]}};
+            uint32_t *dst = smem + lds[u] + s * stage_stride[u];
+#pragma unroll
+            for (int p = 0; p < kPieces; ++p) {
+                u4 w;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const bf2 h = __builtin_convertvector(e[q], bf2);
+                    w[q] = __builtin_bit_cast(uint32_t, h);
+                    e[q] -= __builtin_convertvector(h, fx2);
+                }
+                *reinterpret_cast<u4 *>(dst + p * kPieceDw) = w;
+            }
+        }
     }
 };
 
-template <typename T, bool PRODUCT_B>
-__device__ __forceinline__ void load_chunk(fx4 (&ra)[T::PA], fx4 (&rb)[T::PB], const float *const (&ap)[T::PA],
-                                           const BRows<T, PRODUCT_B> &bp, int kt, int split)
+template <typename T>
+__device__ __forceinline__ void read_frags(bf8 (&af)[T::TM][kPieces], bf8 (&bf)[T::TN][kPieces], const uint32_t *as,
+                                           const uint32_t *bs, int wm, int wn, int il, int kk)
 {
 #pragma unroll
-    for (int i = 0; i < T::PA; ++i) ra[i] = *reinterpret_cast<const fx4 *>(ap[i] + kt * T::BK);
+    for (int i = 0; i < T::TM; ++i)
 #pragma unroll
-    for (int i = 0; i < T::PB; ++i) rb[i] = *reinterpret_cast<const fx4 *>(bp.at(i, kt * T::BK, split));
+        for (int p = 0; p < kPieces; ++p)
+            af[i][p] = __builtin_bit_cast(bf8, *reinterpret_cast<const u4 *>(
+                                                   &as[(wm * T::TM * 32 + i * 32 + il) * kRowDw + p * kPieceDw + kk * 4]));
+#pragma unroll
+    for (int j = 0; j < T::TN; ++j)
+#pragma unroll
+        for (int p = 0; p < kPieces; ++p)
+            bf[j][p] = __builtin_bit_cast(bf8, *reinterpret_cast<const u4 *>(
+                                                   &bs[(wn * T::TN * 32 + j * 32 + il) * kRowDw + p * kPieceDw + kk * 4]));
 }
 
+// The six products of one chunk, smallest weights first:
+// (a2,b0) (a1,b1) (a0,b2) (a1,b0) (a0,b1) (a0,b0).
 template <typename T>
-__device__ __forceinline__ void store_chunk(const fx4 (&ra)[T::PA], const fx4 (&rb)[T::PB], float *as, float *bs,
-                                            int lr, int lc4)
+__device__ __forceinline__ void mfma_frags(floatx16 (&acc)[T::TM][T::TN], const bf8 (&af)[T::TM][kPieces],
+                                           const bf8 (&bf)[T::TN][kPieces])
 {
+    constexpr int pa[6] = {2, 1, 0, 1, 0, 0};
+    constexpr int pb[6] = {0, 1, 2, 0, 1, 0};
 #pragma unroll
-    for (int i = 0; i < T::PA; ++i) *reinterpret_cast<fx4 *>(&as[(lr + T::RPP * i) * T::LDS + lc4 * 4]) = ra[i];
-#pragma unroll
-    for (int i = 0; i < T::PB; ++i) *reinterpret_cast<fx4 *>(&bs[(lr + T::RPP * i) * T::LDS + lc4 * 4]) = rb[i];
-}
-
-template <typename T>
-__device__ __forceinline__ void mfma_chunk(floatx16 (&acc)[T::TM][T::TN], const float *as, const float *bs, int wm,
-                                           int wn, int il, int kk)
-{
-#pragma unroll
-    for (int q = 0; q < T::HK / 4; ++q) {
-        fx4 af[T::TM], bf[T::TN];
+    for (int t = 0; t < 6; ++t)
 #pragma unroll
         for (int i = 0; i < T::TM; ++i)
-            af[i] = *reinterpret_cast<const fx4 *>(&as[(wm * T::TM * 32 + i * 32 + il) * T::LDS + kk * T::HK + q * 4]);
 #pragma unroll
-        for (int j = 0; j < T::TN; ++j)
-            bf[j] = *reinterpret_cast<const fx4 *>(&bs[(wn * T::TN * 32 + j * 32 + il) * T::LDS + kk * T::HK + q * 4]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-#pragma unroll
-            for (int i = 0; i < T::TM; ++i)
-#pragma unroll
-                for (int j = 0; j < T::TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i][e], bf[j][e], acc[i][j], 0, 0, 0);
-    }
+            for (int j = 0; j < T::TN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i][pa[t]], bf[j][pb[t]], acc[i][j], 0, 0, 0);
 }
 
 template <typename T, bool BN_EPILOGUE, bool STREAM_OUT, bool PRODUCT_B = false, bool ACCUMULATE = false>
 __global__ __launch_bounds__(T::THREADS) void gemm_nt_f32_kernel(GemmArgs a)
 {
-    extern __shared__ __attribute__((aligned(16))) float smem[];
-    float *As = smem;
-    float *Bs = smem + T::STAGES * T::BM * T::LDS;
+    extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
+    uint32_t *As = smem;
+    uint32_t *Bs = smem + T::STAGES * T::BM * kRowDw;
 
     const int tiles_n = (a.N + T::BN - 1) / T::BN;
     const int tm = blockIdx.x / tiles_n;
@@ -139,28 +207,35 @@ __global__ __launch_bounds__(T::THREADS) void gemm_nt_f32_kernel(GemmArgs a)
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wm = wave / T::WN, wn = wave % T::WN;
+    const int il = lane & 31;  // row (A) / column (B) inside a 32x32 block
+    const int kk = lane >> 5;  // which half of the chunk's k this lane feeds
 
-    // Global -> register mapping: thread t moves float4 column (t % C4) of
-    // rows t / C4 + RPP * i of both operand tiles.  Rows past the matrix
-    // edge re-read the last row; their results are never stored.
-    const int lc4 = tid % T::C4;
-    const int lr = tid / T::C4;
-    const float *ap[T::PA];
-    BRows<T, PRODUCT_B> bp;
+    // Rows past the matrix edge re-read the last row; their results are
+    // never stored.
+    Stager<T, PRODUCT_B> st;
 #pragma unroll
-    for (int i = 0; i < T::PA; ++i) ap[i] = A + (int64_t)min(m0 + lr + T::RPP * i, a.M - 1) * a.lda + lc4 * 4;
-#pragma unroll
-    for (int i = 0; i < T::PB; ++i) {
-        const int j = min(n0 + lr + T::RPP * i, a.N - 1);
-        if constexpr (PRODUCT_B) {
-            const int ka = j / a.key_n, kc = j - ka * a.key_n;
-            bp.p0[i] = Bmat + (int64_t)ka * a.ldb + lc4 * 4;
-            bp.p1[i] = a.B2 + (int64_t)g * a.strideB + (int64_t)kc * a.ldb + lc4 * 4;
+    for (int u = 0; u < T::UNITS; ++u) {
+        const int grp = wave + T::WAVES * u;
+        st.valid[u] = grp < T::GROUPS;
+        const int r = min(grp, T::GROUPS - 1) * 32 + il;  // row of the A tile, then of the B tile
+        if (r < T::BM) {
+            st.src[u] = A + (int64_t)min(m0 + r, a.M - 1) * a.lda + kk * 8;
+            if constexpr (PRODUCT_B) st.src2[u] = nullptr;
+            st.lds[u] = r * kRowDw + kk * 4;
+            st.stage_stride[u] = T::BM * kRowDw;
         } else {
-            bp.p0[i] = Bmat + (int64_t)j * a.ldb + lc4 * 4;
+            const int j = min(n0 + r - T::BM, a.N - 1);
+            if constexpr (PRODUCT_B) {
+                const int ka = j / a.key_n, kc = j - ka * a.key_n;
+                st.src[u] = Bmat + (int64_t)ka * a.ldb + kk * 8;
+                st.src2[u] = a.B2 + (int64_t)g * a.strideB + (int64_t)kc * a.ldb + kk * 8;
+            } else {
+                st.src[u] = Bmat + (int64_t)j * a.ldb + kk * 8;
+            }
+            st.lds[u] = (T::STAGES * T::BM + r - T::BM) * kRowDw + kk * 4;
+            st.stage_stride[u] = T::BN * kRowDw;
         }
     }
-    fx4 ra[T::PA], rb[T::PB];
 
     floatx16 acc[T::TM][T::TN];
 #pragma unroll
@@ -170,60 +245,126 @@ __global__ __launch_bounds__(T::THREADS) void gemm_nt_f32_kernel(GemmArgs a)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-    const int il = lane & 31;  // row (A) / column (B) inside a 32x32 block
-    const int kk = lane >> 5;  // which k of the MFMA's pair this lane feeds
-    const int KT = a.K / T::BK;
-
-    load_chunk<T, PRODUCT_B>(ra, rb, ap, bp, 0, a.split_k);
-    store_chunk<T>(ra, rb, As, Bs, lr, lc4);
+    const int KT = a.K / kBK;
+    st.load(0, a.split_k);
+    st.store(smem, 0);
+    if (KT > 1) st.load(1, a.split_k);
     __syncthreads();
+    const bool late = T::PING_PONG && wave >= T::WAVES / 2;
+    if (late) __builtin_amdgcn_s_barrier();
     for (int kt = 0; kt < KT; ++kt) {
-        const int s = T::STAGES == 1 ? 0 : (kt & 1);
-        if (kt + 1 < KT) load_chunk<T, PRODUCT_B>(ra, rb, ap, bp, kt + 1, a.split_k);
-        mfma_chunk<T>(acc, As + s * T::BM * T::LDS, Bs + s * T::BN * T::LDS, wm, wn, il, kk);
-        if constexpr (T::STAGES == 1) {
+        const int s = kt & 1;
+        bf8 af[T::TM][kPieces], bf[T::TN][kPieces];
+        read_frags<T>(af, bf, As + s * T::BM * kRowDw, Bs + s * T::BN * kRowDw, wm, wn, il, kk);
+        // chunk kt + 1 into the other stage (last read in chunk kt - 1,
+        // before the barrier that closed it), then fetch chunk kt + 2
+        if (kt + 1 < KT) {
+            st.store(smem, s ^ 1);
+            if (kt + 2 < KT) st.load(kt + 2, a.split_k);
+        }
+        if constexpr (T::PING_PONG) {
             __syncthreads();
-            if (kt + 1 < KT) {
-                store_chunk<T>(ra, rb, As, Bs, lr, lc4);
-                __syncthreads();
-            }
+            __builtin_amdgcn_s_setprio(1);
+            mfma_frags<T>(acc, af, bf);
+            __builtin_amdgcn_s_setprio(0);
+            __syncthreads();
         } else {
-            // stage s ^ 1 was last read in the previous chunk, before the
-            // barrier that closed it
-            if (kt + 1 < KT)
-                store_chunk<T>(ra, rb, As + (s ^ 1) * T::BM * T::LDS, Bs + (s ^ 1) * T::BN * T::LDS, lr, lc4);
+            mfma_frags<T>(acc, af, bf);
             __syncthreads();
         }
     }
+    if (T::PING_PONG && !late) __builtin_amdgcn_s_barrier();
 
-    // 32x32 accumulator layout: register v of lane l holds row
-    // 8*(v/4) + 4*(l/32) + v%4, column l%32.
+    if constexpr (STREAM_OUT) {
+        // A streamed result (read once by the next kernel) is stored straight
+        // from the accumulators, non-temporally.  32x32 accumulator layout:
+        // register v of lane l holds row 8*(v/4) + 4*(l/32) + v%4, column
+        // l%32 of its block.
 #pragma unroll
-    for (int j = 0; j < T::TN; ++j) {
-        const int col = n0 + wn * T::TN * 32 + j * 32 + il;
-        if (col >= a.N) continue;
-        float mean = 0.0f, mul = 1.0f, beta = 0.0f;
-        if (BN_EPILOGUE) {
-            mean = a.bn_mean[col];
-            mul = a.bn_gamma[col] / sqrtf(a.bn_var[col] + a.bn_eps);
-            beta = a.bn_beta[col];
-        }
+        for (int j = 0; j < T::TN; ++j) {
+            const int col = n0 + wn * T::TN * 32 + j * 32 + il;
+            if (col >= a.N) continue;
+            float mean = 0.0f, mul = 1.0f, beta = 0.0f;
+            if (BN_EPILOGUE) {
+                mean = a.bn_mean[col];
+                mul = a.bn_gamma[col] / sqrtf(a.bn_var[col] + a.bn_eps);
+                beta = a.bn_beta[col];
+            }
 #pragma unroll
-        for (int i = 0; i < T::TM; ++i) {
+            for (int i = 0; i < T::TM; ++i) {
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int row = m0 + wm * T::TM * 32 + i * 32 + (v >> 2) * 8 + kk * 4 + (v & 3);
-                if (row < a.M) {
-                    float c = acc[i][j][v];
-                    if (BN_EPILOGUE) c = (c - mean) * mul + beta;
-                    if (ACCUMULATE) c += C[(int64_t)row * a.ldc + col];
-                    if (STREAM_OUT)
+                for (int v = 0; v < 16; ++v) {
+                    const int row = m0 + wm * T::TM * 32 + i * 32 + (v >> 2) * 8 + kk * 4 + (v & 3);
+                    if (row < a.M) {
+                        float c = acc[i][j][v];
+                        if (BN_EPILOGUE) c = (c - mean) * mul + beta;
                         __builtin_nontemporal_store(c, &C[(int64_t)row * a.ldc + col]);
-                    else
-                        C[(int64_t)row * a.ldc + col] = c;
+                    }
                 }
             }
         }
+        return;
+    }
+    // Otherwise the epilogue goes through LDS (free after the last chunk's barrier): PR rows
+    // of the tile at a time, the waves holding them write their
+    // accumulators row-major, then every thread stores whole 16-byte runs of
+    // columns, so each store instruction covers contiguous kilobytes of C.
+    constexpr int CS = T::BN + 8;  // floats per staged row (rows 4 apart on other banks)
+    constexpr int PR = T::EPI_ROWS;
+    float *stage = reinterpret_cast<float *>(smem);
+    const bool vec = a.ldc % 4 == 0 && (reinterpret_cast<uintptr_t>(C) & 15) == 0;
+    // every pass gives a thread the same four columns: c0 .. c0 + 3
+    const int c0 = (tid % (T::BN / 4)) * 4;
+    const int ncol = min(4, a.N - (n0 + c0));
+    fx4 bn_mean = {0.0f, 0.0f, 0.0f, 0.0f}, bn_mul = {1.0f, 1.0f, 1.0f, 1.0f}, bn_beta = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (BN_EPILOGUE) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (e < ncol) {
+                const int cc = n0 + c0 + e;
+                bn_mean[e] = a.bn_mean[cc];
+                bn_mul[e] = a.bn_gamma[cc] / sqrtf(a.bn_var[cc] + a.bn_eps);
+                bn_beta[e] = a.bn_beta[cc];
+            }
+        }
+    }
+#pragma unroll
+    for (int pass = 0; pass < T::BM / PR; ++pass) {
+#pragma unroll
+        for (int i = 0; i < T::TM; ++i) {
+            const int rb = wm * T::TM * 32 + i * 32 - pass * PR;  // block's first row in the pass
+            if (rb < 0 || rb >= PR) continue;
+#pragma unroll
+            for (int j = 0; j < T::TN; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    stage[(rb + (v >> 2) * 8 + kk * 4 + (v & 3)) * CS + wn * T::TN * 32 + j * 32 + il] = acc[i][j][v];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < PR * T::BN / 4 / T::THREADS; ++q) {
+            const int f = tid + T::THREADS * q;
+            const int r = f / (T::BN / 4);
+            const int row = m0 + pass * PR + r, col = n0 + c0;
+            if (row < a.M && ncol > 0) {
+                fx4 x = *reinterpret_cast<const fx4 *>(&stage[r * CS + c0]);
+                float *dst = &C[(int64_t)row * a.ldc + col];
+                if (BN_EPILOGUE) x = (x - bn_mean) * bn_mul + bn_beta;
+                if (vec && ncol == 4) {
+                    if (ACCUMULATE) x += *reinterpret_cast<const fx4 *>(dst);
+                    *reinterpret_cast<fx4 *>(dst) = x;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        if (e >= ncol) break;
+                        float y = x[e];
+                        if (ACCUMULATE) y += dst[e];
+                        dst[e] = y;
+                    }
+                }
+            }
+        }
+        if (pass + 1 < T::BM / PR) __syncthreads();
     }
 }
 
