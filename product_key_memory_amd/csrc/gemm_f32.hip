@@ -198,9 +198,12 @@ __global__ __launch_bounds__(T::THREADS) void gemm_nt_f32_kernel(GemmArgs a)
     const int tm = blockIdx.x / tiles_n;
     const int tn = blockIdx.x - tm * tiles_n;
     const int g = blockIdx.y;
-    const float *A = a.A + (int64_t)g * a.strideA;
-    const float *Bmat = a.B + (int64_t)g * a.strideB;
-    float *C = a.C + (int64_t)g * a.strideC;
+    // split-K: this block's range of K (the operands are K-contiguous)
+    const int kbeg = a.k_chunk ? (int)blockIdx.z * a.k_chunk : 0;
+    const int klen = a.k_chunk ? min(a.k_chunk, a.K - kbeg) : a.K;
+    const float *A = a.A + (int64_t)g * a.strideA + kbeg;
+    const float *Bmat = a.B + (int64_t)g * a.strideB + kbeg;
+    float *C = a.C + (int64_t)g * a.strideC + (int64_t)blockIdx.z * a.batch * a.strideC;
     const int m0 = tm * T::BM, n0 = tn * T::BN;
 
     const int tid = threadIdx.x;
@@ -245,7 +248,7 @@ __global__ __launch_bounds__(T::THREADS) void gemm_nt_f32_kernel(GemmArgs a)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-    const int KT = a.K / kBK;
+    const int KT = klen / kBK;
     st.load(0, a.split_k);
     st.store(smem, 0);
     if (KT > 1) st.load(1, a.split_k);
@@ -393,7 +396,7 @@ hipError_t launch_variant(const GemmArgs &a, hipStream_t stream)
             allowed_on.fetch_or(bit, std::memory_order_acq_rel);
         }
     }
-    const dim3 grid((unsigned)tile_count<T>(a), a.batch);
+    const dim3 grid((unsigned)tile_count<T>(a), a.batch, a.k_chunk ? (a.K + a.k_chunk - 1) / a.k_chunk : 1);
     hipLaunchKernelGGL(kernel, grid, dim3(T::THREADS), T::LDS_BYTES, stream, a);
     return hipGetLastError();
 }
@@ -414,13 +417,54 @@ hipError_t launch_tile(const GemmArgs &a, hipStream_t stream)
     return launch_variant<T, false, false>(a, stream);
 }
 
+// C[g][m][n] (+)= sum over s of P[s][g][m][n], s in order: the split-K
+// partial products (P has row stride N, batch stride M * N).
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *P, int splits, int M, int N, int batch,
+                                                            float *C, int64_t ldc, int64_t strideC, bool accumulate)
+{
+    const int64_t per = (int64_t)M * N, total = per * batch;
+    const int64_t zs = total;  // stride between splits
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
+        const int g = (int)(e / per);
+        const int64_t r = e - g * per;
+        const int m = (int)(r / N), n = (int)(r - (int64_t)m * N);
+        float sum = P[e];
+        for (int s = 1; s < splits; ++s) sum += P[e + s * zs];
+        float *c = &C[(int64_t)g * strideC + (int64_t)m * ldc + n];
+        *c = accumulate ? *c + sum : sum;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_gemm_nt_f32(const GemmArgs &a, hipStream_t stream)
 {
     if (a.M <= 0 || a.N <= 0 || a.batch <= 0) return hipSuccess;
-    if (a.K % 32 != 0) return hipErrorInvalidValue;
-    if (tile_count<BigTile>(a) * a.batch >= kCUs) return launch_tile<BigTile>(a, stream);
+    if (a.K % 32 != 0 || a.k_chunk != 0) return hipErrorInvalidValue;
+    const int64_t tiles = tile_count<BigTile>(a) * a.batch;
+    if (tiles >= kCUs) return launch_tile<BigTile>(a, stream);
+    // Split K when the contraction is long enough (at least 512 per split)
+    // and a workspace for the partial products was given.
+    int splits = (int)((kCUs + tiles - 1) / tiles);
+    if (splits > kMaxKSplits) splits = kMaxKSplits;
+    if (splits > a.K / 512) splits = a.K / 512;
+    const int64_t need = (int64_t)splits * a.batch * a.M * a.N;
+    if (splits >= 2 && a.partial && need <= a.partial_floats && !a.bn_mean && !a.stream_out) {
+        GemmArgs p = a;
+        p.k_chunk = (a.K / 32 + splits - 1) / splits * 32;
+        p.C = a.partial;
+        p.ldc = a.N;
+        p.strideC = (int64_t)a.M * a.N;
+        p.accumulate = false;
+        hipError_t e = launch_tile<BigTile>(p, stream);
+        if (e != hipSuccess) return e;
+        const int used = (a.K + p.k_chunk - 1) / p.k_chunk;
+        const int64_t total = (int64_t)a.batch * a.M * a.N;
+        const int blocks = (int)((total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096);
+        hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks), dim3(256), 0, stream, a.partial, used, a.M, a.N,
+                           a.batch, a.C, a.ldc, a.strideC, a.accumulate);
+        return hipGetLastError();
+    }
     return launch_tile<SmallTile>(a, stream);
 }
 

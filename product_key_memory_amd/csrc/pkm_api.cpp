@@ -258,12 +258,13 @@ pkm::GemmArgs flat_args(const pkm_config &c, const pkm_params *p, int64_t B, con
 
 // Backward workspace for chunks of mb = max_batch tokens (mb32 = mb rounded
 // up to 32, the GEMMs' K granularity).
-constexpr int kBwdPieces = 16;
+constexpr int kBwdPieces = 17;
 bool backward_layout(const pkm_config &c, size_t sizes[kBwdPieces])
 {
     const size_t mb = (size_t)c.max_batch, mb32 = (mb + 31) / 32 * 32, H = (size_t)c.heads, D = (size_t)c.dim;
     const size_t HD = H * D, k = (size_t)c.k, n = (size_t)c.n_keys, N = n * n;
-    const double total = (double)mb32 * (double)HD * 7.0 + 2.0 * H * n * mb32 + 4.0 * N;
+    const double total = (double)mb32 * (double)HD * 7.0 + 2.0 * H * n * mb32 + 4.0 * N +
+                         (double)pkm::kMaxKSplits * ((double)HD * D + (double)mb * D);
     if (total * 4.0 > 1.0e15) return false;
     const size_t f = sizeof(float), u = sizeof(uint32_t);
     sizes[0] = round_up(mb * HD * f);       // q (before BN)
@@ -282,6 +283,8 @@ bool backward_layout(const pkm_config &c, size_t sizes[kBwdPieces])
     sizes[13] = round_up(N * u);            // row offsets
     sizes[14] = round_up((size_t)pkm::scan_blocks((int)N) * u);
     sizes[15] = round_up(mb * H * k * u);   // occurrence lists
+    // split-K partial products of the dWq and dx GEMMs
+    sizes[16] = round_up((size_t)pkm::kMaxKSplits * (HD * D > mb * D ? HD * D : mb * D) * f);
     return true;
 }
 
@@ -540,6 +543,8 @@ pkm_status run_backward(pkm_ctx *ctx, const pkm_params *p, int64_t B, const floa
     uint32_t *count = static_cast<uint32_t *>(piece[11]), *cursor = static_cast<uint32_t *>(piece[12]);
     uint32_t *offs = static_cast<uint32_t *>(piece[13]), *block_sum = static_cast<uint32_t *>(piece[14]);
     uint32_t *list = static_cast<uint32_t *>(piece[15]);
+    float *partial = static_cast<float *>(piece[16]);
+    const int64_t partial_floats = (int64_t)(sizes[16] / sizeof(float));
 
     const int H = c.heads, D = c.dim, k = c.k, n = c.n_keys, HD = H * D, N = n * n;
     if (grads->dx &&
@@ -609,6 +614,8 @@ pkm_status run_backward(pkm_ctx *ctx, const pkm_params *p, int64_t B, const floa
             a.K = nb32;
             a.batch = H;
             a.accumulate = true;
+            a.partial = partial;
+            a.partial_floats = partial_floats;
             if ((s = launched(pkm::launch_gemm_nt_f32(a, st), "dWq"))) return s;
         }
         if (grads->dsubkeys &&
@@ -628,6 +635,8 @@ pkm_status run_backward(pkm_ctx *ctx, const pkm_params *p, int64_t B, const floa
             a.N = D;
             a.K = HD;
             a.batch = 1;
+            a.partial = partial;
+            a.partial_floats = partial_floats;
             if ((s = launched(pkm::launch_gemm_nt_f32(a, st), "dx"))) return s;
         }
         if (grads->dvalues &&

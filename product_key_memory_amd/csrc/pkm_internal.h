@@ -34,7 +34,17 @@ struct GemmArgs {
     int split_k, key_n;
     // accumulate: C += A . B^T instead of C = A . B^T (no BN, no streaming).
     bool accumulate;
+    // Optional split-K workspace (plain or accumulate contractions only):
+    // when the 256x256 grid has fewer tiles than CUs, K is cut into up to
+    // kMaxKSplits ranges whose partial products go to `partial` and are then
+    // summed in split order (bitwise reproducible).  Needs
+    // splits * batch * M * N floats; with partial == nullptr or too small a
+    // capacity the contraction runs unsplit on smaller tiles.
+    float *partial;
+    int64_t partial_floats;
+    int k_chunk;  // set by the launcher: K per split (0: no split)
 };
+constexpr int kMaxKSplits = 4;
 hipError_t launch_gemm_nt_f32(const GemmArgs &a, hipStream_t stream);
 // The same contraction with a product-key B operand and a 32 x 256 tile
 // suited to a few dozen rows of A (the flat exact search over all keys).

@@ -114,7 +114,8 @@ def test_flat_workspace_bytes():
 def test_backward_workspace_bytes():
     """Chunks of max_batch tokens: q, dq^, dq [mb, H*D], dq^T [H*D, mb32],
     x^T [D, mb32], Wq^T, the half-score gradients [2H, n, mb32],
-    the BN partial sums, per-row counts / cursors / offsets and the lists."""
+    the BN partial sums, per-row counts / cursors / offsets and the lists,
+    then up to four split-K partial products of the dWq / dx GEMMs."""
     lib = pk.load_library()
     cfg = pk.make_config(**{**GOOD, "max_batch": 1000})
     mb, mb32, H, D, n, k = 1000, 1024, 4, 1024, 1024, 32
@@ -125,7 +126,8 @@ def test_backward_workspace_bytes():
 
     want = (3 * rnd(mb * HD * 4) + rnd(mb * H * k * 4) + rnd(HD * mb32 * 4) + rnd(D * mb32 * 4)
             + rnd(D * HD * 4) + rnd(2 * HD * 4) + rnd(2 * H * n * mb32 * 4) + 2 * rnd(((mb + 63) // 64) * HD * 4)
-            + 3 * rnd(N * 4) + rnd(((N + 4095) // 4096) * 4) + rnd(mb * H * k * 4))
+            + 3 * rnd(N * 4) + rnd(((N + 4095) // 4096) * 4) + rnd(mb * H * k * 4)
+            + rnd(4 * max(HD * D, mb * D) * 4))
     got = ctypes.c_size_t()
     assert lib.pkm_backward_workspace_bytes(ctypes.byref(cfg), ctypes.byref(got)) == pk.PKM_OK
     assert got.value == want

@@ -86,6 +86,8 @@ def compare(got, ref, names=NAMES):
     (synthetic.Workload("bk1", 50, 64, 2, 30, 1, "bf16", "random"), True),   # k = 1: no gradient to the scores
     (synthetic.Workload("bi8", 60, 128, 2, 24, 8, "int8", "random"), True),  # int8 table + row scales
     (synthetic.Workload("bi4", 60, 192, 2, 24, 8, "int4", "random"), True),  # int4 table
+    # 2048 tokens in one chunk: dWq (K = tokens) runs split-K on 256x256 tiles
+    (synthetic.Workload("bsk", 2048, 256, 2, 32, 8, "bf16", "random"), True),
 ])
 def test_backward_against_oracle(torch, wl, gamma_beta):
     params, x, dout = case(wl, 2, gamma_beta)
