@@ -145,6 +145,27 @@ def gather_uniform_ms(torch, mem, P, wl, steps, warmup):
     return timed_steps(torch, lambda: mem.gather(P, idx, w, out), steps, warmup)
 
 
+def hbm_measured(torch, mem, P, wl, steps, warmup, mib=1024):
+    """Streaming references on this machine: torch's device copy of a tensor far
+    larger than the caches (read + write bytes), and the gather kernel itself
+    on sequential rows (every row read once, in order: the same kernel
+    without the random access)."""
+    n = mib << 18
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    copy_ms = timed_steps(torch, lambda: b.copy_(a), steps, warmup)
+    del a, b
+    R = wl.H * wl.k
+    rows = (torch.arange(wl.B * R, dtype=torch.int64, device="cuda") % wl.N).to(torch.int32).reshape(wl.B, R)
+    w = torch.full((wl.B, R), 1.0 / R, dtype=torch.float32, device="cuda")
+    out = torch.empty((wl.B, wl.D), dtype=torch.float32, device="cuda")
+    seq_ms = timed_steps(torch, lambda: mem.gather(P, rows, w, out), steps, warmup)
+    gathered = per_token_work(wl)["gather_bytes"] * wl.B
+    return {"torch_copy_gbs": round(2 * n * 4 / (copy_ms * 1e-3) / 1e9, 1),
+            "gather_sequential_rows_gbs": round(gathered / (seq_ms * 1e-3) / 1e9, 1),
+            "sample": f"torch copy of {mib} MiB fp32; gather of rows 0..B*H*k-1 in order"}
+
+
 def flat_vs_product(torch, pk, wl, P, xt, kt, tokens=64, steps=5, warmup=2):
     """The comparison the product keys exist for, measured: the brute-force
     search (every one of the N concatenated keys scored by a D-long dot
@@ -280,6 +301,7 @@ def main():
     distinct = float(np.unique(rows).size) / rows.size
     kt = kernel_times(torch, mem, P, xt, args.steps, args.warmup)
     g_uniform_ms = gather_uniform_ms(torch, mem, P, wl, args.steps, args.warmup)
+    hbm = hbm_measured(torch, mem, P, wl, args.steps, args.warmup)
 
     work = per_token_work(wl)
     B = wl.B
@@ -316,6 +338,8 @@ def main():
                    "rows": wl.N, "k": wl.k, "value_table": wl.table, "seed": 0, "max_batch": max_batch},
         "roofline": roof(dominant),
         "gather_roofline": roof("gather"),
+        "hbm_measured": dict(hbm, gather_frac_of_sequential=round(rl["gather"][1] / hbm["gather_sequential_rows_gbs"],
+                                                                    4)),
         "gather_uniform_rows_gbs": round(work["gather_bytes"] * B / (g_uniform_ms * 1e-3) / 1e9, 1),
         "gathered_rows_distinct_frac": round(distinct, 4),
         "end_to_end": end_to_end(wl, ms),
