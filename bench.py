@@ -22,10 +22,11 @@ import synthetic
 
 METRIC = "PKM lookups(tokens)/sec + value-gather HBM GB/s, N=1M, k=32, 4 heads"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
-# The GEMMs are fp32-accurate products built from six bf16 matrix-core
-# products per fp32 product (three-piece bf16 splitting), so their ceiling is
-# a sixth of MI355X's dense bf16 matrix peak of 2.5 PFLOP/s.
-GEMM_PEAK_TFLOPS = 2500.0 / 6
+# The GEMMs are fp32-accurate products built from three fp16 matrix-core
+# products per fp32 product (two-piece fp16 splitting of power-of-two scaled
+# rows), so their ceiling is a third of MI355X's dense fp16 matrix peak of
+# 2.5 PFLOP/s.
+GEMM_PEAK_TFLOPS = 2500.0 / 3
 ELT_BYTES = {"f32": 4, "bf16": 2, "e4m3": 1, "int8": 1, "int4": 0.5}
 SCALED = ("e4m3", "int8", "int4")  # tables with a per-row fp32 scale
 ROOT = os.path.dirname(os.path.abspath(__file__))

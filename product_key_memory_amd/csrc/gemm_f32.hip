@@ -1,46 +1,52 @@
-// fp32-accurate GEMM on the matrix cores for the two dense contractions of
-// the lookup:
+// fp32-accurate GEMM on the matrix cores for the dense contractions of the
+// lookup:
 //   a1+a2  qhat = BN(x . Wq^T)         M = tokens, N = H*D,     K = D
 //   a3     s_g  = qhat_g . C_g^T       M = tokens, N = n_keys,  K = D/2,
 //                                      one batch entry g = 2h + p per half
 // ("Product-Key Memory", code listing: the Linear + BatchNorm1d query and the
-// two subkey products; §Factorising the key space for the split).
+// two subkey products; §Factorising the key space for the split), and of the
+// backward (dWq, dx) and the flat exact search.
 //
 // Both operands are K-contiguous (x rows, Wq rows, qhat rows, subkey rows),
 // so C = A . B^T with no transposes.  Scores decide the winners, so the
 // contraction must be as accurate as fp32.
 //
-// Engine: three-piece bf16 splitting (the "bf16x6" product of Henry, Tang
-// and Heinecke, "Leveraging the bfloat16 Artificial Intelligence Datatype
-// For Higher-Precision Computations", ARITH 2019).  Each fp32 operand is
-// split while it is staged into LDS: a0 = bf16(a), a1 = bf16(a - a0),
-// a2 = bf16(a - a0 - a1), round to nearest.  Both subtractions are exact and
-// a - a0 - a1 has at most 8 significant bits, so a = a0 + a1 + a2 exactly
-// (|a1| <= 2^-8 |a|, |a2| <= 2^-16 |a|).  a.b is accumulated in fp32 from the
-// six products of weight >= 2^-16: a0b0, a0b1, a1b0, a0b2, a1b1, a2b0, each
-// exact in the MFMA's fp32 accumulator; the three dropped ones (a1b2, a2b1,
-// a2b2) sum to at most 2^-23 |a||b| (and are random in sign), the size of
-// one fp32 rounding.  v_mfma_f32_32x32x16_bf16 does 16x the work of
-// v_mfma_f32_32x32x2_f32 per cycle, so the six products cost 6/16 of the
-// fp32 instruction's time.
+// Engine: two-piece fp16 splitting with three products (the method of
+// Ootomo and Yokota, "Recovering single precision accuracy from Tensor Cores
+// while surpassing the FP32 theoretical peak performance", IJHPCA 2022,
+// here without their scaling of the low piece, so that one fp32 accumulator
+// takes all three products).  Every row of A and of B is first scaled by a
+// power of two that brings its largest magnitude into [2^14, 2^15) (exact;
+// computed per call by row_exponent_kernel), so fp16's range holds every
+// row whatever its size.  Each scaled value is split while it is staged into
+// LDS: hi = fp16(a), lo = fp16(a - hi), round to nearest; a - hi is exact and
+// a = hi + lo + e with |e| <= 2^-22 |a| (+ 2^-25 absolute where lo falls
+// below fp16's normal range, i.e. for entries below 2^-17 of the row's
+// largest).  a.b is accumulated in fp32 from lo*hi, hi*lo and hi*hi, each
+// exact in the accumulator; what is left out (lo*lo and the two e terms) is
+// at most about 3 * 2^-22 |a||b| per product and random in sign.  The
+// epilogue multiplies by 2^-(e_row + e_col).  v_mfma_f32_32x32x16_f16 runs
+// at the bf16 rate, 16x the fp32 MFMA's, so the three products cost 3/16 of
+// the fp32 instruction's time, with fewer accumulator roundings per k than
+// that instruction.
 //
 // Tiling for CDNA4.  A workgroup owns a BM x BN tile of C; each of its
 // WM x WN wave64s owns (BM/WM) x (BN/WN) as 32x32 MFMA blocks.  K advances
 // 16 at a time (one MFMA step) through two LDS stages; chunk t + 1 is split
 // and stored while chunk t is multiplied, and chunk t + 2 is loaded into
-// registers.  An LDS row holds the three pieces' 16 bf16 each (96 bytes)
-// plus 16 bytes of padding, so 16-byte accesses to consecutive rows fall on
+// registers.  An LDS row holds the two pieces' 16 fp16 each (64 bytes) plus
+// 16 bytes of padding, so 16-byte accesses to consecutive rows fall on
 // distinct banks.  Lane l of an MFMA step feeds row (or column) l % 32 with
 // k = 8 (l / 32) .. 8 (l / 32) + 7 of the chunk (one ds_read_b128 per
 // piece); A and B use the same k order, which is all a dot product needs.
 // Staging uses the same lane -> (row, k) pattern, so its 16-byte LDS stores
 // are conflict-free as well.
-//   Large grids: 256x256 tiles, 8 waves of 64x128 (112 KiB of LDS, one
+//   Large grids: 256x256 tiles, 8 waves of 64x128 (80 KiB of LDS, one
 //   workgroup per CU, two waves per SIMD), run ping-pong: the second half
 //   of the waves starts one barrier later, so on each SIMD one wave issues
 //   MFMAs (at raised priority) while the other does the LDS and VALU work.
 //   Small grids (fewer tiles than CUs at 256x256): 128x128, 4 waves of
-//   64x64 (56 KiB).
+//   64x64; plain or accumulated products with a workspace split K instead.
 // Epilogue: BN (a1) and accumulated results are staged through LDS a few
 // dozen rows at a time so each store instruction writes whole rows of C in
 // 16-byte runs.  A result that the next kernel reads once (the subkey
@@ -52,9 +58,11 @@
 // §Factorising the key space: every one of the n^2 concatenated keys
 // scored by one full-length dot product).  The B operand is the virtual
 // key matrix: row j = (a, c) is [C0[a]; C1[c]], read from the two subkey
-// sets as K advances (a chunk never straddles the halves).  M is a few
-// dozen tokens, so this uses 32 x 256 tiles: 4 waves of 32 x 64.
+// sets as K advances (a chunk never straddles the halves), with the smaller
+// of the two rows' exponents.  M is a few dozen tokens, so this uses 32 x 256
+// tiles: 4 waves of 32 x 64.
 #include "pkm_internal.h"
+#include "wave_ops.h"
 
 #include <atomic>
 
@@ -64,16 +72,17 @@ namespace {
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float fx4 __attribute__((ext_vector_type(4)));
 typedef float fx2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
-typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+typedef _Float16 hx2 __attribute__((ext_vector_type(2)));
+typedef _Float16 hx8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef int32_t i4 __attribute__((ext_vector_type(4)));
 
 constexpr int kCUs = 256;     // MI355X compute units
-constexpr int kBK = 16;       // k per chunk: one v_mfma_f32_32x32x16_bf16 step
-constexpr int kPieces = 3;    // bf16 pieces per fp32 operand
-constexpr int kPieceDw = 8;   // dwords per piece in an LDS row (16 bf16)
+constexpr int kBK = 16;       // k per chunk: one v_mfma_f32_32x32x16_f16 step
+constexpr int kPieces = 2;    // fp16 pieces per fp32 operand
+constexpr int kPieceDw = 8;   // dwords per piece in an LDS row (16 fp16)
 constexpr int kRowDw = kPieces * kPieceDw + 4;  // + 16 bytes of padding
+constexpr int kRowTop = 14;   // a row's largest magnitude is scaled into [2^14, 2^15)
 
 template <int BM_, int BN_, int WM_, int WN_>
 struct Tile {
@@ -94,7 +103,9 @@ struct Tile {
     // rows of C staged through LDS per epilogue pass
     static constexpr int EPI_ROWS = BM < 64 ? BM : 64;
     static_assert(BM % 32 == 0 && BN % 32 == 0 && BM % EPI_ROWS == 0, "tile shape");
-    static_assert((size_t)EPI_ROWS * (BN + 8) * sizeof(float) <= LDS_BYTES, "epilogue staging fits");
+    // epilogue LDS: the staged rows, then the tile's row and column exponents
+    static constexpr int EX_OFF = EPI_ROWS * (BN + 8);
+    static_assert((size_t)(EX_OFF + BM + BN) * sizeof(float) <= LDS_BYTES, "epilogue staging fits");
     static_assert(EPI_ROWS * BN / 4 % THREADS == 0 && THREADS % (BN / 4) == 0, "epilogue work divides");
 };
 
@@ -103,13 +114,14 @@ using SmallTile = Tile<128, 128, 2, 2>;
 using KeyTile = Tile<32, 256, 1, 4>;
 
 // The staging work of one thread: UNITS groups; for each, the global source
-// of its 8 k-values (product-key B rows keep both halves' rows) and its LDS
-// destination in stage 0 (dwords) with the stride between stages.
+// of its 8 k-values (product-key B rows keep both halves' rows), the row's
+// exponent, and its LDS destination in stage 0 (dwords) with the stride
+// between stages.
 template <typename T, bool PRODUCT_B>
 struct Stager {
     const float *src[T::UNITS];
     const float *src2[PRODUCT_B ? T::UNITS : 1];
-    int lds[T::UNITS], stage_stride[T::UNITS];
+    int lds[T::UNITS], stage_stride[T::UNITS], ex[T::UNITS];
     bool valid[T::UNITS];
     fx4 v[T::UNITS][2];
 
@@ -127,22 +139,26 @@ struct Stager {
         }
     }
 
-    // Split the 8 values into their three bf16 pieces; each piece's 16 bytes
-    // go to that piece's part of the LDS row.
+    // Scale the 8 values by the row's power of two and split them into
+    // their two fp16 pieces; each piece's 16 bytes go to that piece's part of
+    // the LDS row.
     __device__ __forceinline__ void store(uint32_t *smem, int s) const
     {
 #pragma unroll
         for (int u = 0; u < T::UNITS; ++u) {
             if (!valid[u]) continue;
-            fx2 e[4] = {{v[u][0][0], v[u][0][1]}, {v[u][0][2], v[u][0][3]},
-                        {v[u][1][0], v[u][1][1]}, {v[u][1][2], v[u][1][3]}};
+            fx2 e[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                e[q] = fx2{__builtin_ldexpf(v[u][q >> 1][2 * (q & 1)], ex[u]),
+                           __builtin_ldexpf(v[u][q >> 1][2 * (q & 1) + 1], ex[u])};
             uint32_t *dst = smem + lds[u] + s * stage_stride[u];
 #pragma unroll
             for (int p = 0; p < kPieces; ++p) {
                 u4 w;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const bf2 h = __builtin_convertvector(e[q], bf2);
+                    const hx2 h = __builtin_convertvector(e[q], hx2);
                     w[q] = __builtin_bit_cast(uint32_t, h);
                     e[q] -= __builtin_convertvector(h, fx2);
                 }
@@ -153,38 +169,38 @@ struct Stager {
 };
 
 template <typename T>
-__device__ __forceinline__ void read_frags(bf8 (&af)[T::TM][kPieces], bf8 (&bf)[T::TN][kPieces], const uint32_t *as,
+__device__ __forceinline__ void read_frags(hx8 (&af)[T::TM][kPieces], hx8 (&bf)[T::TN][kPieces], const uint32_t *as,
                                            const uint32_t *bs, int wm, int wn, int il, int kk)
 {
 #pragma unroll
     for (int i = 0; i < T::TM; ++i)
 #pragma unroll
         for (int p = 0; p < kPieces; ++p)
-            af[i][p] = __builtin_bit_cast(bf8, *reinterpret_cast<const u4 *>(
+            af[i][p] = __builtin_bit_cast(hx8, *reinterpret_cast<const u4 *>(
                                                    &as[(wm * T::TM * 32 + i * 32 + il) * kRowDw + p * kPieceDw + kk * 4]));
 #pragma unroll
     for (int j = 0; j < T::TN; ++j)
 #pragma unroll
         for (int p = 0; p < kPieces; ++p)
-            bf[j][p] = __builtin_bit_cast(bf8, *reinterpret_cast<const u4 *>(
+            bf[j][p] = __builtin_bit_cast(hx8, *reinterpret_cast<const u4 *>(
                                                    &bs[(wn * T::TN * 32 + j * 32 + il) * kRowDw + p * kPieceDw + kk * 4]));
 }
 
-// The six products of one chunk, smallest weights first:
-// (a2,b0) (a1,b1) (a0,b2) (a1,b0) (a0,b1) (a0,b0).
+// The three products of one chunk, the small ones first: (lo,hi) (hi,lo)
+// (hi,hi); piece 0 is hi, piece 1 lo.
 template <typename T>
-__device__ __forceinline__ void mfma_frags(floatx16 (&acc)[T::TM][T::TN], const bf8 (&af)[T::TM][kPieces],
-                                           const bf8 (&bf)[T::TN][kPieces])
+__device__ __forceinline__ void mfma_frags(floatx16 (&acc)[T::TM][T::TN], const hx8 (&af)[T::TM][kPieces],
+                                           const hx8 (&bf)[T::TN][kPieces])
 {
-    constexpr int pa[6] = {2, 1, 0, 1, 0, 0};
-    constexpr int pb[6] = {0, 1, 2, 0, 1, 0};
+    constexpr int pa[3] = {1, 0, 0};
+    constexpr int pb[3] = {0, 1, 0};
 #pragma unroll
-    for (int t = 0; t < 6; ++t)
+    for (int t = 0; t < 3; ++t)
 #pragma unroll
         for (int i = 0; i < T::TM; ++i)
 #pragma unroll
             for (int j = 0; j < T::TN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i][pa[t]], bf[j][pb[t]], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i][pa[t]], bf[j][pb[t]], acc[i][j], 0, 0, 0);
 }
 
 template <typename T, bool BN_EPILOGUE, bool STREAM_OUT, bool PRODUCT_B = false, bool ACCUMULATE = false>
@@ -204,6 +220,9 @@ __global__ __launch_bounds__(T::THREADS) void gemm_nt_f32_kernel(GemmArgs a)
     const float *A = a.A + (int64_t)g * a.strideA + kbeg;
     const float *Bmat = a.B + (int64_t)g * a.strideB + kbeg;
     float *C = a.C + (int64_t)g * a.strideC + (int64_t)blockIdx.z * a.batch * a.strideC;
+    const int32_t *a_exp = a.a_exp + (int64_t)g * a.M;
+    const int32_t *b_exp = a.b_exp + (int64_t)g * (PRODUCT_B ? a.key_n : a.N);
+    const int32_t *b2_exp = PRODUCT_B ? a.b2_exp + (int64_t)g * a.key_n : nullptr;
     const int m0 = tm * T::BM, n0 = tn * T::BN;
 
     const int tid = threadIdx.x;
@@ -222,8 +241,10 @@ __global__ __launch_bounds__(T::THREADS) void gemm_nt_f32_kernel(GemmArgs a)
         st.valid[u] = grp < T::GROUPS;
         const int r = min(grp, T::GROUPS - 1) * 32 + il;  // row of the A tile, then of the B tile
         if (r < T::BM) {
-            st.src[u] = A + (int64_t)min(m0 + r, a.M - 1) * a.lda + kk * 8;
+            const int m = min(m0 + r, a.M - 1);
+            st.src[u] = A + (int64_t)m * a.lda + kk * 8;
             if constexpr (PRODUCT_B) st.src2[u] = nullptr;
+            st.ex[u] = a_exp[m];
             st.lds[u] = r * kRowDw + kk * 4;
             st.stage_stride[u] = T::BM * kRowDw;
         } else {
@@ -232,13 +253,23 @@ __global__ __launch_bounds__(T::THREADS) void gemm_nt_f32_kernel(GemmArgs a)
                 const int ka = j / a.key_n, kc = j - ka * a.key_n;
                 st.src[u] = Bmat + (int64_t)ka * a.ldb + kk * 8;
                 st.src2[u] = a.B2 + (int64_t)g * a.strideB + (int64_t)kc * a.ldb + kk * 8;
+                st.ex[u] = min(b_exp[ka], b2_exp[kc]);
             } else {
                 st.src[u] = Bmat + (int64_t)j * a.ldb + kk * 8;
+                st.ex[u] = b_exp[j];
             }
             st.lds[u] = (T::STAGES * T::BM + r - T::BM) * kRowDw + kk * 4;
             st.stage_stride[u] = T::BN * kRowDw;
         }
     }
+    // exponent of output column n (its B row's)
+    const auto col_exp = [&](int n) {
+        if constexpr (PRODUCT_B) {
+            const int ka = n / a.key_n;
+            return min(b_exp[ka], b2_exp[n - ka * a.key_n]);
+        }
+        return b_exp[n];
+    };
 
     floatx16 acc[T::TM][T::TN];
 #pragma unroll
@@ -257,7 +288,7 @@ __global__ __launch_bounds__(T::THREADS) void gemm_nt_f32_kernel(GemmArgs a)
     if (late) __builtin_amdgcn_s_barrier();
     for (int kt = 0; kt < KT; ++kt) {
         const int s = kt & 1;
-        bf8 af[T::TM][kPieces], bf[T::TN][kPieces];
+        hx8 af[T::TM][kPieces], bf[T::TN][kPieces];
         read_frags<T>(af, bf, As + s * T::BM * kRowDw, Bs + s * T::BN * kRowDw, wm, wn, il, kk);
         // chunk kt + 1 into the other stage (last read in chunk kt - 1,
         // before the barrier that closed it), then fetch chunk kt + 2
@@ -278,6 +309,13 @@ __global__ __launch_bounds__(T::THREADS) void gemm_nt_f32_kernel(GemmArgs a)
     }
     if (T::PING_PONG && !late) __builtin_amdgcn_s_barrier();
 
+    // The exponents of the tile's rows and columns, once, into LDS (every
+    // wave is past its last fragment read).
+    int32_t *ex_lds = reinterpret_cast<int32_t *>(smem) + T::EX_OFF;
+    for (int t = tid; t < T::BM + T::BN; t += T::THREADS)
+        ex_lds[t] = t < T::BM ? a_exp[min(m0 + t, a.M - 1)] : col_exp(min(n0 + t - T::BM, a.N - 1));
+    __syncthreads();
+
     if constexpr (STREAM_OUT) {
         // A streamed result (read once by the next kernel) is stored straight
         // from the accumulators, non-temporally.  32x32 accumulator layout:
@@ -287,6 +325,7 @@ __global__ __launch_bounds__(T::THREADS) void gemm_nt_f32_kernel(GemmArgs a)
         for (int j = 0; j < T::TN; ++j) {
             const int col = n0 + wn * T::TN * 32 + j * 32 + il;
             if (col >= a.N) continue;
+            const int ecol = ex_lds[T::BM + col - n0];
             float mean = 0.0f, mul = 1.0f, beta = 0.0f;
             if (BN_EPILOGUE) {
                 mean = a.bn_mean[col];
@@ -296,22 +335,29 @@ __global__ __launch_bounds__(T::THREADS) void gemm_nt_f32_kernel(GemmArgs a)
 #pragma unroll
             for (int i = 0; i < T::TM; ++i) {
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int row = m0 + wm * T::TM * 32 + i * 32 + (v >> 2) * 8 + kk * 4 + (v & 3);
-                    if (row < a.M) {
-                        float c = acc[i][j][v];
-                        if (BN_EPILOGUE) c = (c - mean) * mul + beta;
-                        __builtin_nontemporal_store(c, &C[(int64_t)row * a.ldc + col]);
+                for (int v4 = 0; v4 < 4; ++v4) {
+                    // rows 8 v4 + 4 kk .. + 3 of the block: four row exponents
+                    const int rb = m0 + wm * T::TM * 32 + i * 32 + v4 * 8 + kk * 4;
+                    const i4 er = *reinterpret_cast<const i4 *>(&ex_lds[rb - m0]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int row = rb + e;
+                        if (row < a.M) {
+                            float c = __builtin_ldexpf(acc[i][j][v4 * 4 + e], -(er[e] + ecol));
+                            if (BN_EPILOGUE) c = (c - mean) * mul + beta;
+                            __builtin_nontemporal_store(c, &C[(int64_t)row * a.ldc + col]);
+                        }
                     }
                 }
             }
         }
         return;
     }
-    // Otherwise the epilogue goes through LDS (free after the last chunk's barrier): PR rows
-    // of the tile at a time, the waves holding them write their
-    // accumulators row-major, then every thread stores whole 16-byte runs of
-    // columns, so each store instruction covers contiguous kilobytes of C.
+    // Otherwise the epilogue goes through LDS (free after the last chunk's
+    // barrier): PR rows of the tile at a time, the waves holding them write
+    // their accumulators row-major, then every thread stores whole 16-byte
+    // runs of columns, so each store instruction covers contiguous kilobytes
+    // of C.
     constexpr int CS = T::BN + 8;  // floats per staged row (rows 4 apart on other banks)
     constexpr int PR = T::EPI_ROWS;
     float *stage = reinterpret_cast<float *>(smem);
@@ -320,11 +366,13 @@ __global__ __launch_bounds__(T::THREADS) void gemm_nt_f32_kernel(GemmArgs a)
     const int c0 = (tid % (T::BN / 4)) * 4;
     const int ncol = min(4, a.N - (n0 + c0));
     fx4 bn_mean = {0.0f, 0.0f, 0.0f, 0.0f}, bn_mul = {1.0f, 1.0f, 1.0f, 1.0f}, bn_beta = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (BN_EPILOGUE) {
+    i4 ecol = {0, 0, 0, 0};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            if (e < ncol) {
-                const int cc = n0 + c0 + e;
+    for (int e = 0; e < 4; ++e) {
+        if (e < ncol) {
+            const int cc = n0 + c0 + e;
+            ecol[e] = ex_lds[T::BM + c0 + e];
+            if (BN_EPILOGUE) {
                 bn_mean[e] = a.bn_mean[cc];
                 bn_mul[e] = a.bn_gamma[cc] / sqrtf(a.bn_var[cc] + a.bn_eps);
                 bn_beta[e] = a.bn_beta[cc];
@@ -349,10 +397,37 @@ __global__ __launch_bounds__(T::THREADS) void gemm_nt_f32_kernel(GemmArgs a)
             const int f = tid + T::THREADS * q;
             const int r = f / (T::BN / 4);
             const int row = m0 + pass * PR + r, col = n0 + c0;
-            if (row < a.M && ncol > 0) {
-                fx4 x = *reinterpret_cast<const fx4 *>(&stage[r * CS + c0]);
+            const bool live = row < a.M && ncol > 0;
+            fx4 x = *reinterpret_cast<const fx4 *>(&stage[r * CS + c0]);
+            const int erow = ex_lds[pass * PR + r];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = __builtin_ldexpf(x[e], -(erow + ecol[e]));
+            if (BN_EPILOGUE) x = (x - bn_mean) * bn_mul + bn_beta;
+            if (a.row_seg_max) {
+                // the row's largest |C| per segment: lanes of one row hold
+                // consecutive columns, 4 each; a segment spans whole groups
+                // of 8 lanes, or all of the row's lanes
+                float m4 = 0.0f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (live && e < ncol) m4 = fmaxf(m4, fabsf(x[e]));
+                m4 = fmaxf(m4, __uint_as_float(xor_lane<1>(__float_as_uint(m4))));
+                m4 = fmaxf(m4, __uint_as_float(xor_lane<2>(__float_as_uint(m4))));
+                m4 = fmaxf(m4, __uint_as_float(xor_lane<4>(__float_as_uint(m4))));
+                constexpr int RL = T::BN / 4 < 64 ? T::BN / 4 : 64;  // lanes of one row
+                int group = 8;
+                if (a.seg_cols % (4 * RL) == 0) {
+                    if constexpr (RL > 8) m4 = fmaxf(m4, __uint_as_float(xor_lane<8>(__float_as_uint(m4))));
+                    if constexpr (RL > 16) m4 = fmaxf(m4, __uint_as_float(xor_lane<16>(__float_as_uint(m4))));
+                    if constexpr (RL > 32) m4 = fmaxf(m4, __uint_as_float(xor_lane<32>(__float_as_uint(m4))));
+                    group = RL;
+                }
+                if (live && lane % group == 0)
+                    atomicMax(&a.row_seg_max[(int64_t)row * (a.N / a.seg_cols) + col / a.seg_cols],
+                              __float_as_uint(m4));
+            }
+            if (live) {
                 float *dst = &C[(int64_t)row * a.ldc + col];
-                if (BN_EPILOGUE) x = (x - bn_mean) * bn_mul + bn_beta;
                 if (vec && ncol == 4) {
                     if (ACCUMULATE) x += *reinterpret_cast<const fx4 *>(dst);
                     *reinterpret_cast<fx4 *>(dst) = x;
@@ -369,6 +444,169 @@ __global__ __launch_bounds__(T::THREADS) void gemm_nt_f32_kernel(GemmArgs a)
         }
         if (pass + 1 < T::BM / PR) __syncthreads();
     }
+}
+
+// Row exponents: for each row of a K-long fp32 matrix, the power of two that
+// scales the row's largest magnitude into [2^14, 2^15); 0 for a row of
+// zeros (or a non-finite largest magnitude, which no scaling helps).  One
+// launch covers up to three such matrices (A, B and a product key's second
+// half); a wave takes kExpRows consecutive rows of one of them, every load
+// issued before the maxima are formed.
+struct ExpJob {
+    const float *base;
+    int64_t stride, ld;
+    uint32_t rows, per_batch;  // rows = per_batch * batch < 2^31
+    int K;
+    int32_t *out;
+    // row maxima given instead (float bits): row m of batch entry g has
+    // maxbits[m * ld + g]
+    const uint32_t *maxbits;
+};
+struct ExpJobs {
+    ExpJob job[3];
+    int64_t first_wave[4];  // wave index where each job starts; [3] = rows' total
+    uint32_t *zero_ptr;     // then zero_n uint32s to clear, 1024 per wave
+    int64_t zero_n;
+};
+constexpr int kExpRows = 4;
+
+__device__ __forceinline__ float wave_max(float x)
+{
+    x = fmaxf(x, __uint_as_float(xor_lane<1>(__float_as_uint(x))));
+    x = fmaxf(x, __uint_as_float(xor_lane<2>(__float_as_uint(x))));
+    x = fmaxf(x, __uint_as_float(xor_lane<4>(__float_as_uint(x))));
+    x = fmaxf(x, __uint_as_float(xor_lane<8>(__float_as_uint(x))));
+    x = fmaxf(x, __uint_as_float(xor_lane<16>(__float_as_uint(x))));
+    x = fmaxf(x, __uint_as_float(xor_lane<32>(__float_as_uint(x))));
+    return x;
+}
+
+__device__ __forceinline__ int row_exponent(float m)
+{
+    int ex = 0;
+    if (m > 0.0f && m <= 3.402823466e38f) {
+        int p;
+        (void)__builtin_frexpf(m, &p);  // m = f 2^p, f in [0.5, 1)
+        ex = kRowTop + 1 - p;
+    }
+    return ex;
+}
+
+__global__ __launch_bounds__(256) void row_exponent_kernel(ExpJobs jobs)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t wv = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (wv >= jobs.first_wave[3]) {
+        const int64_t z0 = (wv - jobs.first_wave[3]) * 1024 + lane * 16;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            if (z0 + i < jobs.zero_n) jobs.zero_ptr[z0 + i] = 0u;
+        return;
+    }
+    const int j = wv >= jobs.first_wave[2] ? 2 : wv >= jobs.first_wave[1] ? 1 : 0;
+    const ExpJob &jb = jobs.job[j];
+    const uint32_t r0 = (uint32_t)(wv - jobs.first_wave[j]) * kExpRows;
+    if (jb.maxbits) {
+        if (lane < kExpRows && r0 + lane < jb.rows) {
+            const uint32_t r = r0 + lane, g = r / jb.per_batch;
+            jb.out[r] = row_exponent(__uint_as_float(jb.maxbits[(int64_t)(r - g * jb.per_batch) * jb.ld + g]));
+        }
+        return;
+    }
+    const float *row[kExpRows];
+#pragma unroll
+    for (int i = 0; i < kExpRows; ++i) {
+        const uint32_t r = min(r0 + i, jb.rows - 1), g = r / jb.per_batch;
+        row[i] = jb.base + (int64_t)g * jb.stride + (int64_t)(r - g * jb.per_batch) * jb.ld;
+    }
+    float mx[kExpRows];
+#pragma unroll
+    for (int i = 0; i < kExpRows; ++i) mx[i] = 0.0f;
+    const bool vec = jb.K % 4 == 0 && jb.ld % 4 == 0 && jb.stride % 4 == 0 &&
+                     (reinterpret_cast<uintptr_t>(jb.base) & 15) == 0;
+    if (vec) {
+        for (int c0 = 4 * lane; c0 < jb.K; c0 += 512) {
+            fx4 v[kExpRows][2];
+#pragma unroll
+            for (int i = 0; i < kExpRows; ++i)
+#pragma unroll
+                for (int q = 0; q < 2; ++q)
+                    v[i][q] = c0 + 256 * q < jb.K ? *reinterpret_cast<const fx4 *>(row[i] + c0 + 256 * q)
+                                                  : fx4{0, 0, 0, 0};
+#pragma unroll
+            for (int i = 0; i < kExpRows; ++i)
+#pragma unroll
+                for (int q = 0; q < 2; ++q)
+                    mx[i] = fmaxf(fmaxf(mx[i], fmaxf(fabsf(v[i][q][0]), fabsf(v[i][q][1]))),
+                                  fmaxf(fabsf(v[i][q][2]), fabsf(v[i][q][3])));
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < kExpRows; ++i)
+            for (int c = lane; c < jb.K; c += 64) mx[i] = fmaxf(mx[i], fabsf(row[i][c]));
+    }
+#pragma unroll
+    for (int i = 0; i < kExpRows; ++i) {
+        const float m = wave_max(mx[i]);
+        if (lane == i && r0 + i < jb.rows) jb.out[r0 + i] = row_exponent(m);
+    }
+}
+
+ExpJob exp_job(const float *base, int64_t rows_per_batch, int batch, int64_t stride, int64_t ld, int K, int32_t *out)
+{
+    return ExpJob{base, stride, ld, (uint32_t)(rows_per_batch * batch), (uint32_t)rows_per_batch, K, out, nullptr};
+}
+
+hipError_t launch_exponents(const ExpJob *jobs, int count, uint32_t *zero_ptr, int64_t zero_n, hipStream_t stream)
+{
+    ExpJobs j{};
+    j.zero_ptr = zero_ptr;
+    j.zero_n = zero_ptr ? zero_n : 0;
+    int64_t w = 0;
+    for (int i = 0; i < 3; ++i) {
+        j.first_wave[i] = w;
+        if (i < count) {
+            j.job[i] = jobs[i];
+            w += ((int64_t)jobs[i].rows + kExpRows - 1) / kExpRows;
+        } else {
+            j.job[i] = jobs[0];
+        }
+    }
+    j.first_wave[3] = w;
+    w += (j.zero_n + 1023) / 1024;
+    if (w <= 0) return hipSuccess;
+    const int64_t blocks = (w + 3) / 4;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(row_exponent_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, j);
+    return hipGetLastError();
+}
+
+// The row exponents of both operands into the workspace, in one launch;
+// sets a_exp, b_exp (and b2_exp for a product-key B operand).
+hipError_t prepare_exponents(GemmArgs &a, bool product_b, hipStream_t stream)
+{
+    if (!a.exp_ws || a.exp_ws_ints < gemm_exp_ints(a)) return hipErrorInvalidValue;
+    if (gemm_exp_ints(a) >= ((int64_t)1 << 31)) return hipErrorInvalidConfiguration;
+    int32_t *w = a.exp_ws;
+    ExpJob jobs[3];
+    a.a_exp = w;
+    jobs[0] = exp_job(a.A, a.M, a.batch, a.strideA, a.lda, a.K, w);
+    if (a.a_rowmax) {
+        jobs[0].maxbits = a.a_rowmax;
+        jobs[0].ld = a.a_rowmax_ld;
+    }
+    w += (int64_t)a.batch * a.M;
+    if (product_b) {
+        a.b_exp = w;
+        jobs[1] = exp_job(a.B, a.key_n, a.batch, a.strideB, a.ldb, a.split_k, w);
+        w += (int64_t)a.batch * a.key_n;
+        a.b2_exp = w;
+        jobs[2] = exp_job(a.B2, a.key_n, a.batch, a.strideB, a.ldb, a.K - a.split_k, w);
+        return launch_exponents(jobs, 3, a.zero_ptr, a.zero_n, stream);
+    }
+    a.b_exp = w;
+    jobs[1] = exp_job(a.B, a.N, a.batch, a.strideB, a.ldb, a.K, w);
+    return launch_exponents(jobs, 2, a.zero_ptr, a.zero_n, stream);
 }
 
 template <typename T>
@@ -437,10 +675,19 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *P, int 
 
 }  // namespace
 
-hipError_t launch_gemm_nt_f32(const GemmArgs &a, hipStream_t stream)
+int64_t gemm_exp_ints(const GemmArgs &a)
 {
-    if (a.M <= 0 || a.N <= 0 || a.batch <= 0) return hipSuccess;
-    if (a.K % 32 != 0 || a.k_chunk != 0) return hipErrorInvalidValue;
+    const int64_t b_rows = a.B2 ? 2 * (int64_t)a.key_n : (int64_t)a.N;
+    return (int64_t)a.batch * ((int64_t)a.M + b_rows);
+}
+
+hipError_t launch_gemm_nt_f32(const GemmArgs &args, hipStream_t stream)
+{
+    if (args.M <= 0 || args.N <= 0 || args.batch <= 0) return hipSuccess;
+    if (args.K % 32 != 0 || args.k_chunk != 0 || args.B2) return hipErrorInvalidValue;
+    GemmArgs a = args;
+    hipError_t e = prepare_exponents(a, false, stream);
+    if (e != hipSuccess) return e;
     const int64_t tiles = tile_count<BigTile>(a) * a.batch;
     if (tiles >= kCUs) return launch_tile<BigTile>(a, stream);
     // Split K when the contraction is long enough (at least 512 per split)
@@ -456,7 +703,7 @@ hipError_t launch_gemm_nt_f32(const GemmArgs &a, hipStream_t stream)
         p.ldc = a.N;
         p.strideC = (int64_t)a.M * a.N;
         p.accumulate = false;
-        hipError_t e = launch_tile<BigTile>(p, stream);
+        e = launch_tile<BigTile>(p, stream);
         if (e != hipSuccess) return e;
         const int used = (a.K + p.k_chunk - 1) / p.k_chunk;
         const int64_t total = (int64_t)a.batch * a.M * a.N;
@@ -468,13 +715,16 @@ hipError_t launch_gemm_nt_f32(const GemmArgs &a, hipStream_t stream)
     return launch_tile<SmallTile>(a, stream);
 }
 
-hipError_t launch_gemm_nt_f32_product(const GemmArgs &a, hipStream_t stream)
+hipError_t launch_gemm_nt_f32_product(const GemmArgs &args, hipStream_t stream)
 {
-    if (a.M <= 0 || a.N <= 0 || a.batch <= 0) return hipSuccess;
-    if (a.K % 32 != 0 || a.split_k % 32 != 0 || a.split_k <= 0 || a.split_k >= a.K || !a.B2 || a.key_n <= 0 ||
-        (int64_t)a.key_n * a.key_n < a.N || a.bn_mean)
+    if (args.M <= 0 || args.N <= 0 || args.batch <= 0) return hipSuccess;
+    if (args.K % 32 != 0 || args.split_k % 32 != 0 || args.split_k <= 0 || args.split_k >= args.K || !args.B2 ||
+        args.key_n <= 0 || (int64_t)args.key_n * args.key_n < args.N || args.bn_mean || args.k_chunk != 0)
         return hipErrorInvalidValue;
-    if (tile_count<KeyTile>(a) > 0x7FFFFFFF || a.batch > 65535) return hipErrorInvalidConfiguration;
+    if (tile_count<KeyTile>(args) > 0x7FFFFFFF || args.batch > 65535) return hipErrorInvalidConfiguration;
+    GemmArgs a = args;
+    hipError_t e = prepare_exponents(a, true, stream);
+    if (e != hipSuccess) return e;
     return launch_variant<KeyTile, false, false, true>(a, stream);
 }
 

@@ -22,6 +22,9 @@ struct pkm_ctx {
     float *weights;  // [max_batch, H, k]
     uint32_t *stair; // staircase cells of the candidate grid for this k
     float *stat_part; // batch-statistics partial sums [chunks, H * D]
+    int32_t *gemm_exp; // row exponents of the GEMM operands
+    int64_t gemm_exp_ints;
+    uint32_t *qmax;    // largest |q^| per (token, half of a head) [max_batch, 2H], float bits
 };
 
 namespace {
@@ -61,8 +64,16 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 constexpr size_t kAlign = 256;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+// Row exponents the forward's contractions need for a chunk of mb tokens:
+// the query projection (mb + H*D rows) or the subkey scoring (2H (mb + n)).
+int64_t forward_exp_ints(const pkm_config &c)
+{
+    const int64_t q = c.max_batch + (int64_t)c.heads * c.dim, sc = 2 * (int64_t)c.heads * (c.max_batch + c.n_keys);
+    return q > sc ? q : sc;
+}
+
 // Workspace pieces for one chunk of mb tokens; false on size overflow.
-constexpr int kPieces = 6;
+constexpr int kPieces = 8;
 bool workspace_layout(const pkm_config &c, size_t sizes[kPieces])
 {
     const double mb = (double)c.max_batch;
@@ -75,6 +86,8 @@ bool workspace_layout(const pkm_config &c, size_t sizes[kPieces])
     sizes[3] = round_up(m * H * (size_t)c.k * sizeof(float));
     sizes[4] = round_up(pkm::kMaxStaircaseCells * sizeof(uint32_t));
     sizes[5] = round_up((size_t)pkm::stat_chunks(c.max_batch) * H * (size_t)c.dim * sizeof(float));
+    sizes[6] = round_up((size_t)forward_exp_ints(c) * sizeof(int32_t));
+    sizes[7] = round_up(m * 2 * H * sizeof(uint32_t));
     return true;
 }
 
@@ -147,9 +160,12 @@ pkm_status launched(hipError_t e, const char *what)
     return PKM_OK;
 }
 
-pkm::GemmArgs query_args(const pkm_config &c, const pkm_params *p, int64_t B, const float *x, float *qhat)
+pkm::GemmArgs query_args(const pkm_config &c, const pkm_params *p, int64_t B, const float *x, float *qhat,
+                         int32_t *exp_ws, int64_t exp_ints)
 {
     pkm::GemmArgs a{};
+    a.exp_ws = exp_ws;
+    a.exp_ws_ints = exp_ints;
     a.A = x;
     a.lda = c.dim;
     a.strideA = 0;
@@ -171,10 +187,13 @@ pkm::GemmArgs query_args(const pkm_config &c, const pkm_params *p, int64_t B, co
     return a;
 }
 
-pkm::GemmArgs score_args(const pkm_config &c, const pkm_params *p, int64_t B, const float *qhat, float *scores)
+pkm::GemmArgs score_args(const pkm_config &c, const pkm_params *p, int64_t B, const float *qhat, float *scores,
+                         int32_t *exp_ws, int64_t exp_ints)
 {
     const int half = c.dim / 2;
     pkm::GemmArgs a{};
+    a.exp_ws = exp_ws;
+    a.exp_ws_ints = exp_ints;
     a.A = qhat;  // head h, half p starts at column (2h + p) * D/2
     a.lda = (int64_t)c.heads * c.dim;
     a.strideA = half;
@@ -192,27 +211,41 @@ pkm::GemmArgs score_args(const pkm_config &c, const pkm_params *p, int64_t B, co
     return a;
 }
 
-// The GEMM launcher takes M as int; B <= 2^30 keeps one launch per call.
-constexpr int64_t kGemmRows = kMaxBatch;
-
-pkm_status run_query(const pkm_config &c, const pkm_params *p, int64_t B, const float *x, float *qhat,
-                     hipStream_t st)
+// In chunks of max_batch tokens: the context's row-exponent workspace is
+// sized for one.  With qmax (B <= max_batch), the projection also records
+// the largest |q^| of every (token, half of a head) there, and the scoring
+// takes its row exponents from it instead of reading q^ once more.
+pkm_status run_query(const pkm_ctx *ctx, const pkm_params *p, int64_t B, const float *x, float *qhat,
+                     uint32_t *qmax, hipStream_t st)
 {
-    for (int64_t b0 = 0; b0 < B; b0 += kGemmRows) {
-        const int64_t nb = B - b0 < kGemmRows ? B - b0 : kGemmRows;
-        pkm::GemmArgs a = query_args(c, p, nb, x + b0 * c.dim, qhat + b0 * (int64_t)c.heads * c.dim);
+    const pkm_config &c = ctx->cfg;
+    for (int64_t b0 = 0; b0 < B; b0 += c.max_batch) {
+        const int64_t nb = B - b0 < c.max_batch ? B - b0 : c.max_batch;
+        pkm::GemmArgs a = query_args(c, p, nb, x + b0 * c.dim, qhat + b0 * (int64_t)c.heads * c.dim, ctx->gemm_exp,
+                                     ctx->gemm_exp_ints);
+        if (qmax) {
+            a.row_seg_max = qmax;
+            a.seg_cols = c.dim / 2;
+            a.zero_ptr = qmax;
+            a.zero_n = nb * 2 * c.heads;
+        }
         if (pkm_status s = launched(pkm::launch_gemm_nt_f32(a, st), "query projection")) return s;
     }
     return PKM_OK;
 }
 
-pkm_status run_score(const pkm_config &c, const pkm_params *p, int64_t B, const float *qhat, float *scores,
-                     hipStream_t st)
+pkm_status run_score(const pkm_ctx *ctx, const pkm_params *p, int64_t B, const float *qhat, float *scores,
+                     const uint32_t *qmax, hipStream_t st)
 {
-    for (int64_t b0 = 0; b0 < B; b0 += kGemmRows) {
-        const int64_t nb = B - b0 < kGemmRows ? B - b0 : kGemmRows;
+    const pkm_config &c = ctx->cfg;
+    for (int64_t b0 = 0; b0 < B; b0 += c.max_batch) {
+        const int64_t nb = B - b0 < c.max_batch ? B - b0 : c.max_batch;
         pkm::GemmArgs a = score_args(c, p, nb, qhat + b0 * (int64_t)c.heads * c.dim,
-                                     scores + b0 * (int64_t)2 * c.heads * c.n_keys);
+                                     scores + b0 * (int64_t)2 * c.heads * c.n_keys, ctx->gemm_exp, ctx->gemm_exp_ints);
+        if (qmax) {
+            a.a_rowmax = qmax;
+            a.a_rowmax_ld = 2 * c.heads;
+        }
         if (pkm_status s = launched(pkm::launch_gemm_nt_f32(a, st), "subkey scoring")) return s;
     }
     return PKM_OK;
@@ -221,7 +254,8 @@ pkm_status run_score(const pkm_config &c, const pkm_params *p, int64_t B, const 
 // Flat search workspace for B tokens: key scores [B, H, n^2] fp32 and the two
 // top-k merge buffers of packed keys; false if B is out of range.
 constexpr int64_t kFlatMaxBatch = 65536;
-bool flat_layout(const pkm_config &c, int64_t B, size_t sizes[3])
+constexpr int kFlatPieces = 4;
+bool flat_layout(const pkm_config &c, int64_t B, size_t sizes[kFlatPieces])
 {
     if (B < 0 || B > kFlatMaxBatch) return false;
     const int64_t rows = B * c.heads, N = (int64_t)c.n_keys * c.n_keys;
@@ -230,13 +264,17 @@ bool flat_layout(const pkm_config &c, int64_t B, size_t sizes[3])
     sizes[0] = round_up((size_t)(rows * N) * sizeof(float));
     sizes[1] = round_up((size_t)(rows * keys) * sizeof(uint64_t));
     sizes[2] = round_up((size_t)(rows * ((keys + 2047) / 2048) * c.k) * sizeof(uint64_t));
+    sizes[3] = round_up((size_t)(c.heads * (B + 2 * (int64_t)c.n_keys)) * sizeof(int32_t));  // row exponents
     return true;
 }
 
-pkm::GemmArgs flat_args(const pkm_config &c, const pkm_params *p, int64_t B, const float *qhat, float *scores)
+pkm::GemmArgs flat_args(const pkm_config &c, const pkm_params *p, int64_t B, const float *qhat, float *scores,
+                        int32_t *exp_ws, int64_t exp_ints)
 {
     const int half = c.dim / 2;
     pkm::GemmArgs a{};
+    a.exp_ws = exp_ws;
+    a.exp_ws_ints = exp_ints;
     a.A = qhat;  // head h starts at column h * D
     a.lda = (int64_t)c.heads * c.dim;
     a.strideA = c.dim;
@@ -258,7 +296,7 @@ pkm::GemmArgs flat_args(const pkm_config &c, const pkm_params *p, int64_t B, con
 
 // Backward workspace for chunks of mb = max_batch tokens (mb32 = mb rounded
 // up to 32, the GEMMs' K granularity).
-constexpr int kBwdPieces = 17;
+constexpr int kBwdPieces = 18;
 bool backward_layout(const pkm_config &c, size_t sizes[kBwdPieces])
 {
     const size_t mb = (size_t)c.max_batch, mb32 = (mb + 31) / 32 * 32, H = (size_t)c.heads, D = (size_t)c.dim;
@@ -285,6 +323,10 @@ bool backward_layout(const pkm_config &c, size_t sizes[kBwdPieces])
     sizes[15] = round_up(mb * H * k * u);   // occurrence lists
     // split-K partial products of the dWq and dx GEMMs
     sizes[16] = round_up((size_t)pkm::kMaxKSplits * (HD * D > mb * D ? HD * D : mb * D) * f);
+    // row exponents of the GEMM operands: q recompute (mb + HD rows), dWq
+    // (H (D + D)), dx (mb + D)
+    const size_t e_q = mb + HD, e_w = H * 2 * D, e_x = mb + D;
+    sizes[17] = round_up((e_q > e_w ? (e_q > e_x ? e_q : e_x) : (e_w > e_x ? e_w : e_x)) * sizeof(int32_t));
     return true;
 }
 
@@ -354,6 +396,10 @@ pkm_status pkm_create(const pkm_config *cfg, pkm_ctx **out)
     ctx->weights = reinterpret_cast<float *>(w + sizes[0] + sizes[1] + sizes[2]);
     ctx->stair = reinterpret_cast<uint32_t *>(w + sizes[0] + sizes[1] + sizes[2] + sizes[3]);
     ctx->stat_part = reinterpret_cast<float *>(w + sizes[0] + sizes[1] + sizes[2] + sizes[3] + sizes[4]);
+    ctx->gemm_exp = reinterpret_cast<int32_t *>(w + sizes[0] + sizes[1] + sizes[2] + sizes[3] + sizes[4] + sizes[5]);
+    ctx->gemm_exp_ints = (int64_t)(sizes[6] / sizeof(int32_t));
+    ctx->qmax = reinterpret_cast<uint32_t *>(w + sizes[0] + sizes[1] + sizes[2] + sizes[3] + sizes[4] + sizes[5] +
+                                             sizes[6]);
     uint32_t stair[pkm::kMaxStaircaseCells] = {};
     pkm::staircase_table(cfg->k, stair);
     e = hipMemcpy(ctx->stair, stair, sizeof stair, hipMemcpyHostToDevice);
@@ -394,8 +440,8 @@ pkm_status pkm_forward(pkm_ctx *ctx, const pkm_params *p, int64_t B, const float
         const int64_t nb = B - b0 < c.max_batch ? B - b0 : c.max_batch;
         int32_t *ci = idx ? idx + b0 * H * k : ctx->idx;
         float *cw = weights ? weights + b0 * H * k : ctx->weights;
-        if ((s = run_query(c, p, nb, x + b0 * D, ctx->qhat, st))) return s;
-        if ((s = run_score(c, p, nb, ctx->qhat, ctx->scores, st))) return s;
+        if ((s = run_query(ctx, p, nb, x + b0 * D, ctx->qhat, ctx->qmax, st))) return s;
+        if ((s = run_score(ctx, p, nb, ctx->qhat, ctx->scores, ctx->qmax, st))) return s;
         if ((s = launched(pkm::launch_select(ctx->scores, nb, c.heads, c.n_keys, c.k, ctx->stair, ci, cw, st), "select")))
             return s;
         if ((s = launched(pkm::launch_gather(p->values, p->value_scale, c.value_type, c.dim, c.n_keys * c.n_keys, nb, (int)(H * k), ci, cw,
@@ -413,7 +459,7 @@ pkm_status pkm_query(pkm_ctx *ctx, const pkm_params *p, int64_t B, const float *
     if (B == 0) return ok();
     if ((s = check_query_params(p))) return s;
     if ((s = need(x, "x")) || (s = need(qhat, "qhat"))) return s;
-    if ((s = run_query(ctx->cfg, p, B, x, qhat, static_cast<hipStream_t>(stream)))) return s;
+    if ((s = run_query(ctx, p, B, x, qhat, nullptr, static_cast<hipStream_t>(stream)))) return s;
     return ok();
 }
 
@@ -424,7 +470,7 @@ pkm_status pkm_score(pkm_ctx *ctx, const pkm_params *p, int64_t B, const float *
     if (B == 0) return ok();
     if (!p) return fail(PKM_E_ARG, "params is NULL");
     if ((s = need(p->subkeys, "subkeys")) || (s = need(qhat, "qhat")) || (s = need(scores, "scores"))) return s;
-    if ((s = run_score(ctx->cfg, p, B, qhat, scores, static_cast<hipStream_t>(stream)))) return s;
+    if ((s = run_score(ctx, p, B, qhat, scores, nullptr, static_cast<hipStream_t>(stream)))) return s;
     return ok();
 }
 
@@ -464,9 +510,9 @@ pkm_status pkm_flat_workspace_bytes(const pkm_config *cfg, int64_t B, size_t *by
 {
     if (pkm_status s = check_config(cfg)) return s;
     if (!bytes) return fail(PKM_E_ARG, "bytes is NULL");
-    size_t sizes[3];
+    size_t sizes[kFlatPieces];
     if (!flat_layout(*cfg, B, sizes)) return fail(PKM_E_ARG, "flat search B must be in [0, %lld]", (long long)kFlatMaxBatch);
-    *bytes = sizes[0] + sizes[1] + sizes[2];
+    *bytes = sizes[0] + sizes[1] + sizes[2] + sizes[3];
     return ok();
 }
 
@@ -476,22 +522,25 @@ pkm_status pkm_flat_search(pkm_ctx *ctx, const pkm_params *p, int64_t B, const f
     pkm_status s;
     if ((s = check_ctx(ctx))) return s;
     const pkm_config &c = ctx->cfg;
-    size_t sizes[3];
+    size_t sizes[kFlatPieces];
     if (!flat_layout(c, B, sizes)) return fail(PKM_E_ARG, "flat search B must be in [0, %lld]", (long long)kFlatMaxBatch);
     if (B == 0) return ok();
     if (!p) return fail(PKM_E_ARG, "params is NULL");
     if ((s = need(p->subkeys, "subkeys")) || (s = need(qhat, "qhat")) || (s = need(workspace, "workspace")) ||
         (s = need(idx, "idx")) || (s = need(top, "top")))
         return s;
-    if (workspace_bytes < sizes[0] + sizes[1] + sizes[2])
-        return fail(PKM_E_ARG, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes,
-                    sizes[0] + sizes[1] + sizes[2]);
+    const size_t need_bytes = sizes[0] + sizes[1] + sizes[2] + sizes[3];
+    if (workspace_bytes < need_bytes)
+        return fail(PKM_E_ARG, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, need_bytes);
     hipStream_t st = static_cast<hipStream_t>(stream);
     char *w = static_cast<char *>(workspace);
     float *scores = reinterpret_cast<float *>(w);
     uint64_t *buf0 = reinterpret_cast<uint64_t *>(w + sizes[0]);
     uint64_t *buf1 = reinterpret_cast<uint64_t *>(w + sizes[0] + sizes[1]);
-    if ((s = launched(pkm::launch_gemm_nt_f32_product(flat_args(c, p, B, qhat, scores), st), "flat key scoring")))
+    int32_t *exps = reinterpret_cast<int32_t *>(w + sizes[0] + sizes[1] + sizes[2]);
+    if ((s = launched(pkm::launch_gemm_nt_f32_product(
+                          flat_args(c, p, B, qhat, scores, exps, (int64_t)(sizes[3] / sizeof(int32_t))), st),
+                      "flat key scoring")))
         return s;
     if ((s = launched(pkm::launch_flat_topk(scores, B * c.heads, (int64_t)c.n_keys * c.n_keys, c.k, buf0, buf1, idx,
                                             top, st),
@@ -545,6 +594,8 @@ pkm_status run_backward(pkm_ctx *ctx, const pkm_params *p, int64_t B, const floa
     uint32_t *list = static_cast<uint32_t *>(piece[15]);
     float *partial = static_cast<float *>(piece[16]);
     const int64_t partial_floats = (int64_t)(sizes[16] / sizeof(float));
+    int32_t *exps = static_cast<int32_t *>(piece[17]);
+    const int64_t exp_ints = (int64_t)(sizes[17] / sizeof(int32_t));
 
     const int H = c.heads, D = c.dim, k = c.k, n = c.n_keys, HD = H * D, N = n * n;
     if (grads->dx &&
@@ -567,7 +618,7 @@ pkm_status run_backward(pkm_ctx *ctx, const pkm_params *p, int64_t B, const floa
             continue;
         }
         // q before BN
-        pkm::GemmArgs qa = query_args(c, p, nb, xc, Q);
+        pkm::GemmArgs qa = query_args(c, p, nb, xc, Q, exps, exp_ints);
         qa.bn_mean = qa.bn_var = qa.bn_gamma = qa.bn_beta = nullptr;
         if ((s = launched(pkm::launch_gemm_nt_f32(qa, st), "query recompute"))) return s;
         if ((s = launched(pkm::launch_value_backward(p->values, p->value_scale, c.value_type, D, N, nb, H, k, ic, wc,
@@ -616,6 +667,8 @@ pkm_status run_backward(pkm_ctx *ctx, const pkm_params *p, int64_t B, const floa
             a.accumulate = true;
             a.partial = partial;
             a.partial_floats = partial_floats;
+            a.exp_ws = exps;
+            a.exp_ws_ints = exp_ints;
             if ((s = launched(pkm::launch_gemm_nt_f32(a, st), "dWq"))) return s;
         }
         if (grads->dsubkeys &&
@@ -637,6 +690,8 @@ pkm_status run_backward(pkm_ctx *ctx, const pkm_params *p, int64_t B, const floa
             a.batch = 1;
             a.partial = partial;
             a.partial_floats = partial_floats;
+            a.exp_ws = exps;
+            a.exp_ws_ints = exp_ints;
             if ((s = launched(pkm::launch_gemm_nt_f32(a, st), "dx"))) return s;
         }
         if (grads->dvalues &&
@@ -737,7 +792,7 @@ pkm_status pkm_forward_batch_stats(pkm_ctx *ctx, const pkm_params *p, int64_t B,
     const int HD = c.heads * c.dim;
     int32_t *ci = idx ? idx : ctx->idx;
     float *cw = weights ? weights : ctx->weights;
-    pkm::GemmArgs qa = query_args(c, p, B, x, ctx->qhat);
+    pkm::GemmArgs qa = query_args(c, p, B, x, ctx->qhat, ctx->gemm_exp, ctx->gemm_exp_ints);
     qa.bn_mean = qa.bn_var = qa.bn_gamma = qa.bn_beta = nullptr;
     if ((s = launched(pkm::launch_gemm_nt_f32(qa, st), "query projection")) ||
         (s = launched(pkm::launch_batch_stats(ctx->qhat, B, HD, ctx->stat_part, batch_mean, batch_var, running_mean,
@@ -746,7 +801,7 @@ pkm_status pkm_forward_batch_stats(pkm_ctx *ctx, const pkm_params *p, int64_t B,
         (s = launched(pkm::launch_bn_apply(ctx->qhat, B, HD, batch_mean, batch_var, p->bn_gamma, p->bn_beta, c.bn_eps,
                                            st),
                       "batch normalisation")) ||
-        (s = run_score(c, p, B, ctx->qhat, ctx->scores, st)) ||
+        (s = run_score(ctx, p, B, ctx->qhat, ctx->scores, nullptr, st)) ||
         (s = launched(pkm::launch_select(ctx->scores, B, c.heads, c.n_keys, c.k, ctx->stair, ci, cw, st), "select")) ||
         (s = launched(pkm::launch_gather(p->values, p->value_scale, c.value_type, c.dim, c.n_keys * c.n_keys, B,
                                          c.heads * c.k, ci, cw, out, st),

@@ -9,7 +9,8 @@
 namespace pkm {
 
 // C[g][m][n] = sum_k A[g][m][k] * B[g][n][k]  (both operands K-contiguous),
-// for g < batch, m < M, n < N; K % 32 == 0.  With bn_* non-null the epilogue
+// for g < batch, m < M, n < N; K % 32 == 0; fp32 operands, fp32-accurate
+// result (fp16 pieces on the matrix cores, see gemm_f32.hip).  With bn_* non-null the epilogue
 // applies inference BatchNorm to column n:
 //   (c - mean[n]) / sqrt(var[n] + eps) * gamma[n] + beta[n].
 // stream_out: store C with non-temporal stores (for a result read once by a
@@ -42,9 +43,34 @@ struct GemmArgs {
     // capacity the contraction runs unsplit on smaller tiles.
     float *partial;
     int64_t partial_floats;
-    int k_chunk;  // set by the launcher: K per split (0: no split)
+    // Row-exponent workspace (required): the launcher writes one int32 per
+    // row of A and of B -- gemm_exp_ints(a) of them -- and the kernel scales
+    // each row by that power of two before splitting it into fp16 pieces,
+    // undoing both in the epilogue.
+    int32_t *exp_ws;
+    int64_t exp_ws_ints;
+    // Optional, with a staged (non-streamed) epilogue: record per output row
+    // and segment of seg_cols columns (seg_cols % 32 == 0, N % seg_cols ==
+    // 0) the largest |C| as float bits, by atomic max into
+    // row_seg_max[row * (N / seg_cols) + col / seg_cols]; the pre-pass first
+    // zeroes zero_n uint32s at zero_ptr (the caller's choice of what to clear).
+    uint32_t *row_seg_max;
+    int seg_cols;
+    uint32_t *zero_ptr;
+    int64_t zero_n;
+    // Optional: A's row maxima known beforehand (float bits): row m of batch
+    // entry g has largest magnitude a_rowmax[m * a_rowmax_ld + g]; the
+    // pre-pass then reads these instead of A.
+    const uint32_t *a_rowmax;
+    int a_rowmax_ld;
+    // set by the launcher
+    int k_chunk;  // K per split (0: no split)
+    const int32_t *a_exp, *b_exp, *b2_exp;
 };
 constexpr int kMaxKSplits = 4;
+// int32s of row exponents a contraction needs: batch * (M + N), or
+// batch * (M + 2 key_n) with a product-key B operand.
+int64_t gemm_exp_ints(const GemmArgs &a);
 hipError_t launch_gemm_nt_f32(const GemmArgs &a, hipStream_t stream);
 // The same contraction with a product-key B operand and a 32 x 256 tile
 // suited to a few dozen rows of A (the flat exact search over all keys).

@@ -84,14 +84,17 @@ def test_workspace_bytes():
     mb, H, D, n, k = 16384, 4, 1024, 1024, 32
     stair = 320 * 4  # staircase cells of the candidate grid
     stat_part = (mb // 64) * H * D * 4  # batch-statistics partial sums
-    assert pk.workspace_bytes(cfg) == 4 * mb * H * (D + 2 * n + 2 * k) + stair + stat_part
+    exps = max(mb + H * D, 2 * H * (mb + n)) * 4  # GEMM row exponents (query or scoring)
+    qmax = mb * 2 * H * 4  # largest |q^| per (token, half of a head)
+    assert pk.workspace_bytes(cfg) == 4 * mb * H * (D + 2 * n + 2 * k) + stair + stat_part + exps + qmax
     with pytest.raises(pk.PkmError):
         pk.workspace_bytes(pk.make_config(**{**GOOD, "k": 0}))
 
 
 def test_flat_workspace_bytes():
     """Key scores [B, H, n^2] fp32, then the merge buffers: ceil(n^2 / 4096) * k
-    packed keys per row and ceil(that / 2048) * k, each rounded to 256 bytes."""
+    packed keys per row and ceil(that / 2048) * k, then the GEMM's row
+    exponents (H (B + 2 n) int32), each rounded to 256 bytes."""
     lib = pk.load_library()
     cfg = pk.make_config(**GOOD)
     H, n, k = 4, 1024, 32
@@ -102,7 +105,8 @@ def test_flat_workspace_bytes():
     for B in (1, 16, 100):
         rows = B * H
         keys = (n * n + 4095) // 4096 * k
-        want = rnd(rows * n * n * 4) + rnd(rows * keys * 8) + rnd(rows * ((keys + 2047) // 2048) * k * 8)
+        want = (rnd(rows * n * n * 4) + rnd(rows * keys * 8) + rnd(rows * ((keys + 2047) // 2048) * k * 8)
+                + rnd(H * (B + 2 * n) * 4))
         got = ctypes.c_size_t()
         assert lib.pkm_flat_workspace_bytes(ctypes.byref(cfg), B, ctypes.byref(got)) == pk.PKM_OK
         assert got.value == want
@@ -115,7 +119,8 @@ def test_backward_workspace_bytes():
     """Chunks of max_batch tokens: q, dq^, dq [mb, H*D], dq^T [H*D, mb32],
     x^T [D, mb32], Wq^T, the half-score gradients [2H, n, mb32],
     the BN partial sums, per-row counts / cursors / offsets and the lists,
-    then up to four split-K partial products of the dWq / dx GEMMs."""
+    then up to four split-K partial products of the dWq / dx GEMMs and the
+    GEMMs' row exponents."""
     lib = pk.load_library()
     cfg = pk.make_config(**{**GOOD, "max_batch": 1000})
     mb, mb32, H, D, n, k = 1000, 1024, 4, 1024, 1024, 32
@@ -127,7 +132,7 @@ def test_backward_workspace_bytes():
     want = (3 * rnd(mb * HD * 4) + rnd(mb * H * k * 4) + rnd(HD * mb32 * 4) + rnd(D * mb32 * 4)
             + rnd(D * HD * 4) + rnd(2 * HD * 4) + rnd(2 * H * n * mb32 * 4) + 2 * rnd(((mb + 63) // 64) * HD * 4)
             + 3 * rnd(N * 4) + rnd(((N + 4095) // 4096) * 4) + rnd(mb * H * k * 4)
-            + rnd(4 * max(HD * D, mb * D) * 4))
+            + rnd(4 * max(HD * D, mb * D) * 4) + rnd(max(mb + HD, H * 2 * D, mb + D) * 4))
     got = ctypes.c_size_t()
     assert lib.pkm_backward_workspace_bytes(ctypes.byref(cfg), ctypes.byref(got)) == pk.PKM_OK
     assert got.value == want

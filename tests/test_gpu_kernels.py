@@ -207,6 +207,46 @@ def test_query_and_score_parity(torch, name):
             assert (np.abs(scores[:, h, p] - ref) <= 1e-5 * m + 1e-7).all()
 
 
+def test_query_and_score_wide_range(torch):
+    """The contractions scale every operand row by a power of two before
+    splitting it into fp16 pieces, so rows of any size keep fp32 accuracy:
+    token rows multiplied by 2^-30 .. 2^30, projection rows by 2^-20 ..
+    2^20 and subkey rows by 2^-25 .. 2^25 (far outside fp16's range either
+    way), checked element by element against fp64 as above (1e-5 of the L1
+    mass)."""
+    wl = synthetic.Workload("range", 96, 128, 2, 64, 8, "f32", "random")
+    params = synthetic.make_params(wl, with_values=False, seed=7)
+    params["values"] = np.zeros((wl.N, wl.D), np.float32)
+    params["scale"] = None
+    rng = np.random.default_rng(7)
+    x = synthetic.make_x(wl, seed=7) * np.exp2(rng.integers(-30, 31, (wl.B, 1))).astype(np.float32)
+    params["wq"] = params["wq"] * np.exp2(rng.integers(-20, 21, (wl.H, wl.D, 1))).astype(np.float32)
+    params["subkeys"] = params["subkeys"] * np.exp2(rng.integers(-25, 26, (wl.H, 2, wl.n, 1))).astype(np.float32)
+    x[5] = 0.0  # a row of zeros
+    mem = pk.Memory(wl.D, wl.H, wl.n, wl.k, "f32")
+    P = pk.params_to_device(params, "f32", support.device())
+    say("wide-range query/score")
+    qhat = mem.query(P, _to(torch, x)).cpu().numpy().astype(np.float64)
+    w64 = params["wq"].astype(np.float64)
+    inv = params["gamma"].astype(np.float64) / np.sqrt(params["var"].astype(np.float64) + 1e-5)
+    q = np.einsum("hfd,bd->bhf", w64, x.astype(np.float64))
+    ref = (q - params["mean"]) * inv + params["beta"]
+    mass = np.einsum("hfd,bd->bhf", np.abs(w64), np.abs(x).astype(np.float64)) * np.abs(inv)
+    assert np.isfinite(qhat).all()
+    assert (np.abs(qhat - ref) <= 1e-5 * mass + 1e-6 * np.abs(ref) + 1e-30).all()
+    q32 = (qhat * np.exp2(rng.integers(-30, 31, (wl.B, 1, 1)))).astype(np.float32)
+    scores = mem.score(P, _to(torch, q32)).cpu().numpy().astype(np.float64)
+    half = wl.D // 2
+    sub = params["subkeys"].astype(np.float64)
+    for h in range(wl.H):
+        for p in range(2):
+            qp = q32[:, h, p * half:(p + 1) * half].astype(np.float64)
+            r = qp @ sub[h, p].T
+            m = np.abs(qp) @ np.abs(sub[h, p]).T
+            assert np.isfinite(scores[:, h, p]).all()
+            assert (np.abs(scores[:, h, p] - r) <= 1e-5 * m + 1e-30).all()
+
+
 @pytest.mark.parametrize("name", ["mid", "default", "large_memory"])
 def test_score_error_guard(torch, name):
     """The index-parity rule needs tau to exceed twice the largest full-score
