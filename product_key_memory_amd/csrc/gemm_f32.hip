@@ -109,6 +109,19 @@ struct Tile {
     static_assert(EPI_ROWS * BN / 4 % THREADS == 0 && THREADS % (BN / 4) == 0, "epilogue work divides");
 };
 
+// The power of two that scales a row whose largest magnitude is m into
+// [2^14, 2^15); 0 for m = 0 or not finite.
+__device__ __forceinline__ int row_exponent(float m)
+{
+    int ex = 0;
+    if (m > 0.0f && m <= 3.402823466e38f) {
+        int p;
+        (void)__builtin_frexpf(m, &p);  // m = f 2^p, f in [0.5, 1)
+        ex = kRowTop + 1 - p;
+    }
+    return ex;
+}
+
 using BigTile = Tile<256, 256, 4, 2>;
 using SmallTile = Tile<128, 128, 2, 2>;
 using KeyTile = Tile<32, 256, 1, 4>;
@@ -220,7 +233,11 @@ __global__ __launch_bounds__(T::THREADS) void gemm_nt_f32_kernel(GemmArgs a)
     const float *A = a.A + (int64_t)g * a.strideA + kbeg;
     const float *Bmat = a.B + (int64_t)g * a.strideB + kbeg;
     float *C = a.C + (int64_t)g * a.strideC + (int64_t)blockIdx.z * a.batch * a.strideC;
-    const int32_t *a_exp = a.a_exp + (int64_t)g * a.M;
+    const int32_t *a_exp = a.a_rowmax ? nullptr : a.a_exp + (int64_t)g * a.M;
+    // exponent of A row m (its maxima given, or computed by the pre-pass)
+    const auto row_exp = [&](int m) {
+        return a.a_rowmax ? row_exponent(__uint_as_float(a.a_rowmax[(int64_t)m * a.a_rowmax_ld + g])) : a_exp[m];
+    };
     const int32_t *b_exp = a.b_exp + (int64_t)g * (PRODUCT_B ? a.key_n : a.N);
     const int32_t *b2_exp = PRODUCT_B ? a.b2_exp + (int64_t)g * a.key_n : nullptr;
     const int m0 = tm * T::BM, n0 = tn * T::BN;
@@ -244,7 +261,7 @@ __global__ __launch_bounds__(T::THREADS) void gemm_nt_f32_kernel(GemmArgs a)
             const int m = min(m0 + r, a.M - 1);
             st.src[u] = A + (int64_t)m * a.lda + kk * 8;
             if constexpr (PRODUCT_B) st.src2[u] = nullptr;
-            st.ex[u] = a_exp[m];
+            st.ex[u] = row_exp(m);
             st.lds[u] = r * kRowDw + kk * 4;
             st.stage_stride[u] = T::BM * kRowDw;
         } else {
@@ -313,7 +330,7 @@ __global__ __launch_bounds__(T::THREADS) void gemm_nt_f32_kernel(GemmArgs a)
     // wave is past its last fragment read).
     int32_t *ex_lds = reinterpret_cast<int32_t *>(smem) + T::EX_OFF;
     for (int t = tid; t < T::BM + T::BN; t += T::THREADS)
-        ex_lds[t] = t < T::BM ? a_exp[min(m0 + t, a.M - 1)] : col_exp(min(n0 + t - T::BM, a.N - 1));
+        ex_lds[t] = t < T::BM ? row_exp(min(m0 + t, a.M - 1)) : col_exp(min(n0 + t - T::BM, a.N - 1));
     __syncthreads();
 
     if constexpr (STREAM_OUT) {
@@ -481,17 +498,6 @@ __device__ __forceinline__ float wave_max(float x)
     return x;
 }
 
-__device__ __forceinline__ int row_exponent(float m)
-{
-    int ex = 0;
-    if (m > 0.0f && m <= 3.402823466e38f) {
-        int p;
-        (void)__builtin_frexpf(m, &p);  // m = f 2^p, f in [0.5, 1)
-        ex = kRowTop + 1 - p;
-    }
-    return ex;
-}
-
 __global__ __launch_bounds__(256) void row_exponent_kernel(ExpJobs jobs)
 {
     const int lane = threadIdx.x & 63;
@@ -506,9 +512,10 @@ __global__ __launch_bounds__(256) void row_exponent_kernel(ExpJobs jobs)
     const int j = wv >= jobs.first_wave[2] ? 2 : wv >= jobs.first_wave[1] ? 1 : 0;
     const ExpJob &jb = jobs.job[j];
     const uint32_t r0 = (uint32_t)(wv - jobs.first_wave[j]) * kExpRows;
-    if (jb.maxbits) {
-        if (lane < kExpRows && r0 + lane < jb.rows) {
-            const uint32_t r = r0 + lane, g = r / jb.per_batch;
+    if (jb.maxbits) {  // one row per lane
+        const uint32_t r = (uint32_t)(wv - jobs.first_wave[j]) * 64 + lane;
+        if (r < jb.rows) {
+            const uint32_t g = r / jb.per_batch;
             jb.out[r] = row_exponent(__uint_as_float(jb.maxbits[(int64_t)(r - g * jb.per_batch) * jb.ld + g]));
         }
         return;
@@ -525,18 +532,19 @@ __global__ __launch_bounds__(256) void row_exponent_kernel(ExpJobs jobs)
     const bool vec = jb.K % 4 == 0 && jb.ld % 4 == 0 && jb.stride % 4 == 0 &&
                      (reinterpret_cast<uintptr_t>(jb.base) & 15) == 0;
     if (vec) {
-        for (int c0 = 4 * lane; c0 < jb.K; c0 += 512) {
-            fx4 v[kExpRows][2];
+        // sixteen float4 loads in flight per lane
+        for (int c0 = 4 * lane; c0 < jb.K; c0 += 1024) {
+            fx4 v[kExpRows][4];
 #pragma unroll
             for (int i = 0; i < kExpRows; ++i)
 #pragma unroll
-                for (int q = 0; q < 2; ++q)
+                for (int q = 0; q < 4; ++q)
                     v[i][q] = c0 + 256 * q < jb.K ? *reinterpret_cast<const fx4 *>(row[i] + c0 + 256 * q)
                                                   : fx4{0, 0, 0, 0};
 #pragma unroll
             for (int i = 0; i < kExpRows; ++i)
 #pragma unroll
-                for (int q = 0; q < 2; ++q)
+                for (int q = 0; q < 4; ++q)
                     mx[i] = fmaxf(fmaxf(mx[i], fmaxf(fabsf(v[i][q][0]), fabsf(v[i][q][1]))),
                                   fmaxf(fabsf(v[i][q][2]), fabsf(v[i][q][3])));
         }
@@ -567,9 +575,10 @@ hipError_t launch_exponents(const ExpJob *jobs, int count, uint32_t *zero_ptr, i
         j.first_wave[i] = w;
         if (i < count) {
             j.job[i] = jobs[i];
-            w += ((int64_t)jobs[i].rows + kExpRows - 1) / kExpRows;
+            const int per_wave = jobs[i].maxbits ? 64 : kExpRows;
+            w += ((int64_t)jobs[i].rows + per_wave - 1) / per_wave;
         } else {
-            j.job[i] = jobs[0];
+            j.job[i] = count > 0 ? jobs[0] : ExpJob{};
         }
     }
     j.first_wave[3] = w;
@@ -581,32 +590,43 @@ hipError_t launch_exponents(const ExpJob *jobs, int count, uint32_t *zero_ptr, i
     return hipGetLastError();
 }
 
-// The row exponents of both operands into the workspace, in one launch;
-// sets a_exp, b_exp (and b2_exp for a product-key B operand).
+// The row exponents of both operands into the workspace, in one launch
+// (with the extra set, if asked); sets a_exp, b_exp (and b2_exp for a
+// product-key B operand).  Nothing to launch when both are known.
 hipError_t prepare_exponents(GemmArgs &a, bool product_b, hipStream_t stream)
 {
+    if (a.a_rowmax && a.b_exp_given && !product_b && !a.extra_exp.base) {
+        a.b_exp = a.b_exp_given;
+        return a.zero_ptr ? launch_exponents(nullptr, 0, a.zero_ptr, a.zero_n, stream) : hipSuccess;
+    }
     if (!a.exp_ws || a.exp_ws_ints < gemm_exp_ints(a)) return hipErrorInvalidValue;
     if (gemm_exp_ints(a) >= ((int64_t)1 << 31)) return hipErrorInvalidConfiguration;
     int32_t *w = a.exp_ws;
     ExpJob jobs[3];
-    a.a_exp = w;
-    jobs[0] = exp_job(a.A, a.M, a.batch, a.strideA, a.lda, a.K, w);
-    if (a.a_rowmax) {
-        jobs[0].maxbits = a.a_rowmax;
-        jobs[0].ld = a.a_rowmax_ld;
+    int n = 0;
+    if (!a.a_rowmax) {
+        a.a_exp = w;
+        jobs[n++] = exp_job(a.A, a.M, a.batch, a.strideA, a.lda, a.K, w);
     }
     w += (int64_t)a.batch * a.M;
     if (product_b) {
         a.b_exp = w;
-        jobs[1] = exp_job(a.B, a.key_n, a.batch, a.strideB, a.ldb, a.split_k, w);
+        jobs[n++] = exp_job(a.B, a.key_n, a.batch, a.strideB, a.ldb, a.split_k, w);
         w += (int64_t)a.batch * a.key_n;
         a.b2_exp = w;
-        jobs[2] = exp_job(a.B2, a.key_n, a.batch, a.strideB, a.ldb, a.K - a.split_k, w);
-        return launch_exponents(jobs, 3, a.zero_ptr, a.zero_n, stream);
+        jobs[n++] = exp_job(a.B2, a.key_n, a.batch, a.strideB, a.ldb, a.K - a.split_k, w);
+    } else if (a.b_exp_given) {
+        a.b_exp = a.b_exp_given;
+    } else {
+        a.b_exp = w;
+        jobs[n++] = exp_job(a.B, a.N, a.batch, a.strideB, a.ldb, a.K, w);
     }
-    a.b_exp = w;
-    jobs[1] = exp_job(a.B, a.N, a.batch, a.strideB, a.ldb, a.K, w);
-    return launch_exponents(jobs, 2, a.zero_ptr, a.zero_n, stream);
+    if (a.extra_exp.base) {
+        if (n >= 3) return hipErrorInvalidValue;
+        const auto &x = a.extra_exp;
+        jobs[n++] = exp_job(x.base, x.rows_per_batch, x.batch, x.stride, x.ld, x.K, x.out);
+    }
+    return launch_exponents(jobs, n, a.zero_ptr, a.zero_n, stream);
 }
 
 template <typename T>

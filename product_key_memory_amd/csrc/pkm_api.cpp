@@ -25,6 +25,7 @@ struct pkm_ctx {
     int32_t *gemm_exp; // row exponents of the GEMM operands
     int64_t gemm_exp_ints;
     uint32_t *qmax;    // largest |q^| per (token, half of a head) [max_batch, 2H], float bits
+    int32_t *sub_exp;  // row exponents of the subkeys [2H, n]
 };
 
 namespace {
@@ -73,7 +74,7 @@ int64_t forward_exp_ints(const pkm_config &c)
 }
 
 // Workspace pieces for one chunk of mb tokens; false on size overflow.
-constexpr int kPieces = 8;
+constexpr int kPieces = 9;
 bool workspace_layout(const pkm_config &c, size_t sizes[kPieces])
 {
     const double mb = (double)c.max_batch;
@@ -88,6 +89,7 @@ bool workspace_layout(const pkm_config &c, size_t sizes[kPieces])
     sizes[5] = round_up((size_t)pkm::stat_chunks(c.max_batch) * H * (size_t)c.dim * sizeof(float));
     sizes[6] = round_up((size_t)forward_exp_ints(c) * sizeof(int32_t));
     sizes[7] = round_up(m * 2 * H * sizeof(uint32_t));
+    sizes[8] = round_up(2 * H * (size_t)c.n_keys * sizeof(int32_t));
     return true;
 }
 
@@ -212,9 +214,10 @@ pkm::GemmArgs score_args(const pkm_config &c, const pkm_params *p, int64_t B, co
 }
 
 // In chunks of max_batch tokens: the context's row-exponent workspace is
-// sized for one.  With qmax (B <= max_batch), the projection also records
-// the largest |q^| of every (token, half of a head) there, and the scoring
-// takes its row exponents from it instead of reading q^ once more.
+// sized for one.  With qmax, the projection also records the largest |q^|
+// of every (token, half of a head) there and computes the subkeys' row
+// exponents in its pre-pass, and the scoring takes its row exponents from
+// both instead of reading q^ and the subkeys once more (no pre-pass).
 pkm_status run_query(const pkm_ctx *ctx, const pkm_params *p, int64_t B, const float *x, float *qhat,
                      uint32_t *qmax, hipStream_t st)
 {
@@ -228,6 +231,14 @@ pkm_status run_query(const pkm_ctx *ctx, const pkm_params *p, int64_t B, const f
             a.seg_cols = c.dim / 2;
             a.zero_ptr = qmax;
             a.zero_n = nb * 2 * c.heads;
+            // the subkeys' row exponents for the scoring, in the same pre-pass
+            a.extra_exp.base = p->subkeys;
+            a.extra_exp.rows_per_batch = c.n_keys;
+            a.extra_exp.batch = 2 * c.heads;
+            a.extra_exp.stride = (int64_t)c.n_keys * (c.dim / 2);
+            a.extra_exp.ld = c.dim / 2;
+            a.extra_exp.K = c.dim / 2;
+            a.extra_exp.out = ctx->sub_exp;
         }
         if (pkm_status s = launched(pkm::launch_gemm_nt_f32(a, st), "query projection")) return s;
     }
@@ -245,6 +256,7 @@ pkm_status run_score(const pkm_ctx *ctx, const pkm_params *p, int64_t B, const f
         if (qmax) {
             a.a_rowmax = qmax;
             a.a_rowmax_ld = 2 * c.heads;
+            a.b_exp_given = ctx->sub_exp;
         }
         if (pkm_status s = launched(pkm::launch_gemm_nt_f32(a, st), "subkey scoring")) return s;
     }
@@ -400,6 +412,7 @@ pkm_status pkm_create(const pkm_config *cfg, pkm_ctx **out)
     ctx->gemm_exp_ints = (int64_t)(sizes[6] / sizeof(int32_t));
     ctx->qmax = reinterpret_cast<uint32_t *>(w + sizes[0] + sizes[1] + sizes[2] + sizes[3] + sizes[4] + sizes[5] +
                                              sizes[6]);
+    ctx->sub_exp = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(ctx->qmax) + sizes[7]);
     uint32_t stair[pkm::kMaxStaircaseCells] = {};
     pkm::staircase_table(cfg->k, stair);
     e = hipMemcpy(ctx->stair, stair, sizeof stair, hipMemcpyHostToDevice);

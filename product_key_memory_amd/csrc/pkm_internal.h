@@ -59,10 +59,22 @@ struct GemmArgs {
     uint32_t *zero_ptr;
     int64_t zero_n;
     // Optional: A's row maxima known beforehand (float bits): row m of batch
-    // entry g has largest magnitude a_rowmax[m * a_rowmax_ld + g]; the
-    // pre-pass then reads these instead of A.
+    // entry g has largest magnitude a_rowmax[m * a_rowmax_ld + g], turned
+    // into exponents by the kernel itself.
     const uint32_t *a_rowmax;
     int a_rowmax_ld;
+    // Optional: B's row exponents computed beforehand ([batch][N]).  With
+    // both this and a_rowmax the contraction needs no pre-pass.
+    const int32_t *b_exp_given;
+    // Optional: one more set of row exponents for a later contraction,
+    // computed in this one's pre-pass (rows_per_batch * batch rows of K
+    // floats, row m of entry g at base + g * stride + m * ld).
+    struct {
+        const float *base;
+        int64_t rows_per_batch, stride, ld;
+        int batch, K;
+        int32_t *out;
+    } extra_exp;
     // set by the launcher
     int k_chunk;  // K per split (0: no split)
     const int32_t *a_exp, *b_exp, *b2_exp;

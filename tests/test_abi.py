@@ -86,7 +86,9 @@ def test_workspace_bytes():
     stat_part = (mb // 64) * H * D * 4  # batch-statistics partial sums
     exps = max(mb + H * D, 2 * H * (mb + n)) * 4  # GEMM row exponents (query or scoring)
     qmax = mb * 2 * H * 4  # largest |q^| per (token, half of a head)
-    assert pk.workspace_bytes(cfg) == 4 * mb * H * (D + 2 * n + 2 * k) + stair + stat_part + exps + qmax
+    sub_exp = 2 * H * n * 4  # the subkeys' row exponents
+    assert (pk.workspace_bytes(cfg) ==
+            4 * mb * H * (D + 2 * n + 2 * k) + stair + stat_part + exps + qmax + sub_exp)
     with pytest.raises(pk.PkmError):
         pk.workspace_bytes(pk.make_config(**{**GOOD, "k": 0}))
 
