@@ -142,11 +142,13 @@ pkm_status pkm_forward(pkm_ctx *ctx, const pkm_params *p, int64_t B, const float
                        float *weights, void *stream);
 
 /* Steps a1-a2 only: qhat [B, H, D] fp32 = BN_h(Wq[h] . x[b]).  Uses wq and
- * the four BN arrays of p.  No workspace is used. */
+ * the four BN arrays of p, and the context's workspace for the contraction's
+ * row exponents (so, like pkm_forward, one stream per context at a time);
+ * any B is done in chunks of max_batch. */
 pkm_status pkm_query(pkm_ctx *ctx, const pkm_params *p, int64_t B, const float *x, float *qhat, void *stream);
 
 /* Step a3 only: scores [B, H, 2, n] fp32 from qhat [B, H, D] and p->subkeys.
- * No workspace is used. */
+ * Uses the context's workspace for the contraction's row exponents. */
 pkm_status pkm_score(pkm_ctx *ctx, const pkm_params *p, int64_t B, const float *qhat, float *scores,
                      void *stream);
 
@@ -177,8 +179,8 @@ pkm_status pkm_gather(pkm_ctx *ctx, const pkm_params *p, int64_t B, int32_t rows
  *   top   [B, H, k] fp32 the scores of those keys
  * workspace is caller-owned device memory of at least
  * pkm_flat_workspace_bytes(cfg, B) bytes (16-byte aligned): it holds the
- * B * H * n^2 fp32 key scores and the top-k merge buffers, so the call
- * allocates nothing.  Work: 2 * B * H * n^2 * D flop.  B <= 65536; a
+ * B * H * n^2 fp32 key scores, the top-k merge buffers and the
+ * contraction's row exponents, so the call allocates nothing.  Work: 2 * B * H * n^2 * D flop.  B <= 65536; a
  * smaller workspace is PKM_E_ARG. */
 pkm_status pkm_flat_workspace_bytes(const pkm_config *cfg, int64_t B, size_t *bytes);
 pkm_status pkm_flat_search(pkm_ctx *ctx, const pkm_params *p, int64_t B, const float *qhat, void *workspace,
