@@ -59,8 +59,9 @@
 // scored by one full-length dot product).  The B operand is the virtual
 // key matrix: row j = (a, c) is [C0[a]; C1[c]], read from the two subkey
 // sets as K advances (a chunk never straddles the halves), with the smaller
-// of the two rows' exponents.  M is a few dozen tokens, so this uses 32 x 256
-// tiles: 4 waves of 32 x 64.
+// of the two rows' exponents.  M is a few dozen tokens: up to 32 use 32 x 256
+// tiles (4 waves of 32 x 64), more use 64 x 256 tiles (8 waves of 32 x 64,
+// ping-pong), which stage each key row once for twice the rows of A.
 #include "pkm_internal.h"
 #include "wave_ops.h"
 
@@ -100,8 +101,10 @@ struct Tile {
     // runs one phase behind the first, so on every SIMD one wave issues MFMAs
     // while the other reads fragments and splits, stores and loads chunks.
     static constexpr bool PING_PONG = WAVES == 8;
-    // rows of C staged through LDS per epilogue pass
-    static constexpr int EPI_ROWS = BM < 64 ? BM : 64;
+    // rows of C staged through LDS per epilogue pass: 64, or 32 where 64
+    // rows and the exponents would not fit in the stages' LDS
+    static constexpr int EPI_ROWS =
+        BM < 64 ? BM : ((size_t)(64 * (BN + 8) + BM + BN) * sizeof(float) <= LDS_BYTES ? 64 : 32);
     static_assert(BM % 32 == 0 && BN % 32 == 0 && BM % EPI_ROWS == 0, "tile shape");
     // epilogue LDS: the staged rows, then the tile's row and column exponents
     static constexpr int EX_OFF = EPI_ROWS * (BN + 8);
@@ -125,6 +128,7 @@ __device__ __forceinline__ int row_exponent(float m)
 using BigTile = Tile<256, 256, 4, 2>;
 using SmallTile = Tile<128, 128, 2, 2>;
 using KeyTile = Tile<32, 256, 1, 4>;
+using KeyTile64 = Tile<64, 256, 2, 4>;
 
 // The staging work of one thread: UNITS groups; for each, the global source
 // of its 8 k-values (product-key B rows keep both halves' rows), the row's
@@ -745,6 +749,7 @@ hipError_t launch_gemm_nt_f32_product(const GemmArgs &args, hipStream_t stream)
     GemmArgs a = args;
     hipError_t e = prepare_exponents(a, true, stream);
     if (e != hipSuccess) return e;
+    if (a.M > 32) return launch_variant<KeyTile64, false, false, true>(a, stream);
     return launch_variant<KeyTile, false, false, true>(a, stream);
 }
 

@@ -101,7 +101,9 @@ def test_flat_search_full_size(torch, name, tokens):
     dict(B=3, D=64, H=1, n=2048, k=64),    # 4M keys: two merge passes
     dict(B=2, D=64, H=1, n=4096, k=32),    # the largest n_keys: 16.7M keys
     dict(B=4, D=64, H=3, n=8, k=8),        # k = n_keys
-    dict(B=33, D=192, H=1, n=40, k=1),     # k = 1, a ragged 32-row tile
+    dict(B=33, D=192, H=1, n=40, k=1),     # k = 1, a ragged 64-row tile
+    dict(B=31, D=64, H=2, n=24, k=8),      # a ragged 32-row tile
+    dict(B=70, D=128, H=2, n=24, k=8),     # two 64-row tiles, the second ragged
 ])
 def test_flat_search_edge_shapes(torch, shape):
     wl = synthetic.Workload("flat_edge", shape["B"], shape["D"], shape["H"], shape["n"], shape["k"], "f32", "random")
@@ -111,7 +113,8 @@ def test_flat_search_edge_shapes(torch, shape):
     flat_vs_oracle(torch, wl, params, x)
 
 
-@pytest.mark.parametrize("B,D,H,n,k", [(6, 64, 2, 64, 32), (3, 64, 1, 100, 64), (2, 128, 1, 300, 17)])
+@pytest.mark.parametrize("B,D,H,n,k", [(6, 64, 2, 64, 32), (3, 64, 1, 100, 64), (2, 128, 1, 300, 17),
+                                       (40, 64, 1, 48, 16)])
 def test_flat_search_exact_ties(torch, B, D, H, n, k):
     """Small integer queries and subkeys: every score is exact in fp32, and
     many keys tie.  The oracle's steps a4-a6 on the exact half scores give
