@@ -61,7 +61,9 @@
 // sets as K advances (a chunk never straddles the halves), with the smaller
 // of the two rows' exponents.  M is a few dozen tokens: up to 32 use 32 x 256
 // tiles (4 waves of 32 x 64), more use 64 x 256 tiles (8 waves of 32 x 64,
-// ping-pong), which stage each key row once for twice the rows of A.
+// ping-pong), which stage each key row once for twice the rows of A.  The
+// epilogue can record each row's largest score per group of 64 keys, from
+// which the top-k derives a threshold.
 #include "pkm_internal.h"
 #include "wave_ops.h"
 
@@ -424,6 +426,22 @@ __global__ __launch_bounds__(T::THREADS) void gemm_nt_f32_kernel(GemmArgs a)
 #pragma unroll
             for (int e = 0; e < 4; ++e) x[e] = __builtin_ldexpf(x[e], -(erow + ecol[e]));
             if (BN_EPILOGUE) x = (x - bn_mean) * bn_mul + bn_beta;
+            if constexpr (PRODUCT_B) {
+                static_assert(T::BN % 64 == 0, "a group of 64 columns is 16 lanes of one row");
+                if (a.group_max) {
+                    uint32_t mk = 0;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (live && e < ncol) mk = max(mk, order_key(x[e]));
+                    mk = max(mk, xor_lane<1>(mk));
+                    mk = max(mk, xor_lane<2>(mk));
+                    mk = max(mk, xor_lane<4>(mk));
+                    mk = max(mk, xor_lane<8>(mk));
+                    if (live && lane % 16 == 0)
+                        a.group_max[(int64_t)row * a.group_ld + (int64_t)g * a.group_stride + col / 64] =
+                            key_score(mk);
+                }
+            }
             if (a.row_seg_max) {
                 // the row's largest |C| per segment: lanes of one row hold
                 // consecutive columns, 4 each; a segment spans whole groups

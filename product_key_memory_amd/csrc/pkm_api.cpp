@@ -263,21 +263,44 @@ pkm_status run_score(const pkm_ctx *ctx, const pkm_params *p, int64_t B, const f
     return PKM_OK;
 }
 
-// Flat search workspace for B tokens: key scores [B, H, n^2] fp32 and the two
-// top-k merge buffers of packed keys; false if B is out of range.
+// Flat search workspace for B tokens: key scores [B, H, n^2] fp32, the two
+// top-k merge buffers of packed keys, the contraction's row exponents, and
+// for rows of more than 4096 keys the threshold's pieces: group maxima
+// [B, H, G] (G = ceil(n^2 / 64)), theta's top-k [B, H, k] (indices, scores),
+// the list counts [B, H] and the lists [B, H, kFlatListCap] of packed keys.
+// The merge buffers serve the top-k over rows of G group maxima then, else
+// over the n^2 scores.  False if B is out of range.
 constexpr int64_t kFlatMaxBatch = 65536;
-constexpr int kFlatPieces = 4;
+constexpr int kFlatPieces = 9;
+constexpr int64_t kFlatDirectMax = 4096;  // longest row topped without a threshold
 bool flat_layout(const pkm_config &c, int64_t B, size_t sizes[kFlatPieces])
 {
     if (B < 0 || B > kFlatMaxBatch) return false;
     const int64_t rows = B * c.heads, N = (int64_t)c.n_keys * c.n_keys;
-    const int64_t keys = pkm::flat_topk_keys_per_row(N, c.k);
     if ((double)rows * (double)N * 4.0 > 1.0e15) return false;
+    const bool threshold = N > kFlatDirectMax;
+    const int64_t G = (N + 63) / 64;
+    const int64_t keys = pkm::flat_topk_keys_per_row(threshold ? G : N, c.k);
+    for (int i = 0; i < kFlatPieces; ++i) sizes[i] = 0;
     sizes[0] = round_up((size_t)(rows * N) * sizeof(float));
     sizes[1] = round_up((size_t)(rows * keys) * sizeof(uint64_t));
     sizes[2] = round_up((size_t)(rows * ((keys + 2047) / 2048) * c.k) * sizeof(uint64_t));
     sizes[3] = round_up((size_t)(c.heads * (B + 2 * (int64_t)c.n_keys)) * sizeof(int32_t));  // row exponents
+    if (threshold) {
+        sizes[4] = round_up((size_t)(rows * G) * sizeof(float));
+        sizes[5] = round_up((size_t)(rows * c.k) * sizeof(int32_t));
+        sizes[6] = round_up((size_t)(rows * c.k) * sizeof(float));
+        sizes[7] = round_up((size_t)rows * sizeof(uint32_t));
+        sizes[8] = round_up((size_t)(rows * pkm::kFlatListCap) * sizeof(uint64_t));
+    }
     return true;
+}
+
+size_t total_bytes(const size_t *sizes, int n)
+{
+    size_t t = 0;
+    for (int i = 0; i < n; ++i) t += sizes[i];
+    return t;
 }
 
 pkm::GemmArgs flat_args(const pkm_config &c, const pkm_params *p, int64_t B, const float *qhat, float *scores,
@@ -525,7 +548,7 @@ pkm_status pkm_flat_workspace_bytes(const pkm_config *cfg, int64_t B, size_t *by
     if (!bytes) return fail(PKM_E_ARG, "bytes is NULL");
     size_t sizes[kFlatPieces];
     if (!flat_layout(*cfg, B, sizes)) return fail(PKM_E_ARG, "flat search B must be in [0, %lld]", (long long)kFlatMaxBatch);
-    *bytes = sizes[0] + sizes[1] + sizes[2] + sizes[3];
+    *bytes = total_bytes(sizes, kFlatPieces);
     return ok();
 }
 
@@ -542,23 +565,38 @@ pkm_status pkm_flat_search(pkm_ctx *ctx, const pkm_params *p, int64_t B, const f
     if ((s = need(p->subkeys, "subkeys")) || (s = need(qhat, "qhat")) || (s = need(workspace, "workspace")) ||
         (s = need(idx, "idx")) || (s = need(top, "top")))
         return s;
-    const size_t need_bytes = sizes[0] + sizes[1] + sizes[2] + sizes[3];
+    const size_t need_bytes = total_bytes(sizes, kFlatPieces);
     if (workspace_bytes < need_bytes)
         return fail(PKM_E_ARG, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, need_bytes);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    char *w = static_cast<char *>(workspace);
-    float *scores = reinterpret_cast<float *>(w);
-    uint64_t *buf0 = reinterpret_cast<uint64_t *>(w + sizes[0]);
-    uint64_t *buf1 = reinterpret_cast<uint64_t *>(w + sizes[0] + sizes[1]);
-    int32_t *exps = reinterpret_cast<int32_t *>(w + sizes[0] + sizes[1] + sizes[2]);
-    if ((s = launched(pkm::launch_gemm_nt_f32_product(
-                          flat_args(c, p, B, qhat, scores, exps, (int64_t)(sizes[3] / sizeof(int32_t))), st),
-                      "flat key scoring")))
-        return s;
-    if ((s = launched(pkm::launch_flat_topk(scores, B * c.heads, (int64_t)c.n_keys * c.n_keys, c.k, buf0, buf1, idx,
-                                            top, st),
-                      "flat top-k")))
-        return s;
+    char *piece[kFlatPieces];
+    piece[0] = static_cast<char *>(workspace);
+    for (int i = 1; i < kFlatPieces; ++i) piece[i] = piece[i - 1] + sizes[i - 1];
+    float *scores = reinterpret_cast<float *>(piece[0]);
+    uint64_t *buf0 = reinterpret_cast<uint64_t *>(piece[1]);
+    uint64_t *buf1 = reinterpret_cast<uint64_t *>(piece[2]);
+    int32_t *exps = reinterpret_cast<int32_t *>(piece[3]);
+    const int64_t rows = B * c.heads, N = (int64_t)c.n_keys * c.n_keys;
+    const bool threshold = N > kFlatDirectMax;
+    pkm::GemmArgs a = flat_args(c, p, B, qhat, scores, exps, (int64_t)(sizes[3] / sizeof(int32_t)));
+    float *gmax = threshold ? reinterpret_cast<float *>(piece[4]) : nullptr;
+    if (gmax) {
+        const int64_t G = (N + 63) / 64;
+        a.group_max = gmax;  // [B][H][G], like the scores
+        a.group_ld = c.heads * G;
+        a.group_stride = G;
+    }
+    if ((s = launched(pkm::launch_gemm_nt_f32_product(a, st), "flat key scoring"))) return s;
+    if (threshold)
+        s = launched(pkm::launch_flat_topk_threshold(scores, gmax, rows, N, c.k, buf0, buf1,
+                                                     reinterpret_cast<int32_t *>(piece[5]),
+                                                     reinterpret_cast<float *>(piece[6]),
+                                                     reinterpret_cast<uint32_t *>(piece[7]),
+                                                     reinterpret_cast<uint64_t *>(piece[8]), idx, top, st),
+                     "flat top-k");
+    else
+        s = launched(pkm::launch_flat_topk(scores, rows, N, c.k, buf0, buf1, idx, top, st), "flat top-k");
+    if (s) return s;
     return ok();
 }
 

@@ -75,6 +75,11 @@ struct GemmArgs {
         int batch, K;
         int32_t *out;
     } extra_exp;
+    // Optional, product-key B operand only: per row of C and group of 64
+    // consecutive columns, the group's largest value (by order key) at
+    // group_max[m * group_ld + g * group_stride + n / 64].
+    float *group_max;
+    int64_t group_ld, group_stride;
     // set by the launcher
     int k_chunk;  // K per split (0: no split)
     const int32_t *a_exp, *b_exp, *b2_exp;
@@ -112,6 +117,17 @@ void staircase_table(int k, uint32_t *out);
 int64_t flat_topk_keys_per_row(int64_t len, int k);
 hipError_t launch_flat_topk(const float *scores, int64_t rows, int64_t len, int k, uint64_t *buf0, uint64_t *buf1,
                             int32_t *idx, float *top, hipStream_t stream);
+// The same top-k for rows longer than 4096 with group maxima: gmax [rows][G]
+// holds the largest score of each group of 64 (G = ceil(len / 64)).  The
+// k-th largest group maximum, theta, is found first (launch_flat_topk over
+// gmax, with buf0 / buf1 sized for rows of G and tidx / ttop [rows][k]);
+// then the scores >= theta go to list [rows][kFlatListCap] (count [rows]
+// counts them) and the list's top-k is the row's.  A row whose list
+// overflows is scanned in full by one wave.
+constexpr int kFlatListCap = 512;
+hipError_t launch_flat_topk_threshold(const float *scores, const float *gmax, int64_t rows, int64_t len, int k,
+                                      uint64_t *buf0, uint64_t *buf1, int32_t *tidx, float *ttop, uint32_t *count,
+                                      uint64_t *list, int32_t *idx, float *top, hipStream_t stream);
 
 hipError_t launch_gather(const void *values, const float *scale, int value_type, int D, int N, int64_t B, int R,
                          const int32_t *idx, const float *w, float *out, hipStream_t stream);

@@ -42,17 +42,6 @@ namespace {
 constexpr int WAVES = 4;        // (token, head) pairs per 256-thread workgroup
 constexpr int STAIR_SLOTS = 5;  // staircase cells per lane: 280 cells at k = 64
 
-__device__ __forceinline__ uint32_t order_key(float f)
-{
-    const uint32_t u = __float_as_uint(f + 0.0f);  // -0 -> +0: equal scores give equal keys
-    return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
-}
-
-__device__ __forceinline__ float key_score(uint32_t k)
-{
-    return __uint_as_float(k ^ ((uint32_t)((int32_t)~k >> 31) | 0x80000000u));
-}
-
 __device__ __forceinline__ uint64_t pack(uint32_t key, uint32_t id)
 {
     return ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - id);
@@ -169,10 +158,35 @@ __device__ __forceinline__ uint64_t sorted_survivors(int count, Stage &st, int l
     return v;
 }
 
+// Clustered scores (e.g. a few lanes holding most of the best) can leave
+// more than kSlots elements at or above a first threshold kth.  The slots
+// then hold kSlots of them, so the k-th best key among the slots is a
+// higher threshold that still keeps at least k elements; it is raised that
+// way while it rises and the survivors overflow.  Returns the new count
+// (still above kSlots only for heavy exact ties, left to exact_cut).
+template <int M, typename IdOf>
+__device__ __forceinline__ int raise_threshold(const uint32_t (&key)[M], IdOf id_of, int k, uint32_t &kth, int count,
+                                               Stage &st, int lane)
+{
+#pragma unroll 1
+    for (int it = 0; it < 3 && count > kSlots; ++it) {
+        const uint64_t s = sorted_survivors(kSlots, st, lane);
+        const uint32_t t2 = read_lane((uint32_t)(s >> 32), k - 1);
+        if (t2 <= kth) break;
+        kth = t2;
+        count = 0;
+#pragma unroll
+        for (int t = 0; t < M; ++t) append(key[t] >= kth, key[t], id_of(t), count, st, lane);
+    }
+    return count;
+}
+
 // Exact top-k (k <= 64) of the wave's elements, keys in registers key[M]
 // (0 = absent) and recomputed by slow_key for the rare heavy-tie path: lane
-// j < k receives the j-th best packed key.
-template <int M, typename SlowKey, typename IdOf>
+// j < k receives the j-th best packed key.  RAISE: try raise_threshold
+// before that path (the flat search's rows, whose scores cluster; the
+// lookup's subkey scores keep the smaller register footprint).
+template <int M, bool RAISE = false, typename SlowKey, typename IdOf>
 __device__ uint64_t wave_topk(const uint32_t (&key)[M], SlowKey slow_key, IdOf id_of, int m, int k, Stage &st,
                               int lane)
 {
@@ -184,6 +198,7 @@ __device__ uint64_t wave_topk(const uint32_t (&key)[M], SlowKey slow_key, IdOf i
     int count = 0;
 #pragma unroll
     for (int t = 0; t < M; ++t) append(kept(key[t], id_of(t), kth, last), key[t], id_of(t), count, st, lane);
+    if constexpr (RAISE) count = raise_threshold(key, id_of, k, kth, count, st, lane);
     if (count > kSlots) {
         exact_cut(slow_key, id_of, m, k, kth, last);
         count = compact_rolled(slow_key, id_of, m, kth, last, st, lane);
@@ -409,7 +424,7 @@ __global__ __launch_bounds__(64 * WAVES) void flat_topk_kernel(const void *__res
             const int e = slot_element<VEC4>(t, lane);
             return e < m ? order_key(seg_row[e]) : 0u;
         };
-        c = wave_topk(key, reread, id_of, VEC4 ? MH : (m + 63) >> 6, k, stage[wv], lane);
+        c = wave_topk<MH, true>(key, reread, id_of, VEC4 ? MH : (m + 63) >> 6, k, stage[wv], lane);
     } else {
         const uint64_t *seg_row = static_cast<const uint64_t *>(in) + row * len + base;
         uint64_t v[MH];
@@ -439,6 +454,7 @@ __global__ __launch_bounds__(64 * WAVES) void flat_topk_kernel(const void *__res
         int count = 0;
 #pragma unroll
         for (int t = 0; t < MH; ++t) append(kept(key[t], id[t], kth, last), key[t], id[t], count, stage[wv], lane);
+        count = raise_threshold(key, [&](int t) { return id[t]; }, k, kth, count, stage[wv], lane);
         if (count > kSlots) {
             exact_cut(reread, id_again, (m + 63) >> 6, k, kth, last);
             count = compact_rolled(reread, id_again, (m + 63) >> 6, kth, last, stage[wv], lane);
@@ -466,6 +482,121 @@ hipError_t launch_flat_pass(const void *in, int64_t rows, int64_t len, int k, ui
     hipLaunchKernelGGL((flat_topk_kernel<FROM_SCORES, VEC4>), dim3((unsigned)blocks), dim3(64 * WAVES), 0, stream, in,
                        rows, len, (int)segs, k, out_keys, idx, top);
     return hipGetLastError();
+}
+
+// Flat top-k with a threshold (rows longer than one 4096-score segment).
+// theta = the k-th largest of a row's group maxima (groups of 64 scores): k
+// distinct groups hold an element >= theta, so the row's k-th best score is
+// >= theta and every winner scores >= theta.  For untied scores only a few
+// more than k elements do.  A wave takes kFilterBlocks blocks of 4096 scores;
+// a block whose lanes cannot hold a score >= theta is dropped after one
+// integer maximum per element; otherwise its elements >= theta are appended
+// to the row's list at positions from an atomic add (the list's order varies
+// between runs; its top-k, over unique packed keys, does not).
+constexpr int kFilterBlocks = 4;
+
+template <bool VEC4>
+__global__ __launch_bounds__(64 * WAVES) void flat_filter_kernel(const float *__restrict__ scores, int64_t rows,
+                                                                 int64_t len, int segs, int k,
+                                                                 const float *__restrict__ ttop,
+                                                                 uint32_t *__restrict__ count,
+                                                                 uint64_t *__restrict__ list)
+{
+    constexpr int MH = kFlatScoreSeg / 64;
+    const int lane = threadIdx.x & 63;
+    const int64_t item = (int64_t)blockIdx.x * WAVES + (threadIdx.x >> 6);  // row * segs + segment
+    if (item >= rows * segs) return;
+    const int64_t row = item / segs;
+    const int seg = (int)(item - row * segs);
+    const uint32_t tkey = order_key(ttop[row * k + k - 1]);
+    const float *srow = scores + row * len;
+    uint64_t *lst = list + row * kFlatListCap;
+#pragma unroll 1
+    for (int blk = 0; blk < kFilterBlocks; ++blk) {
+        const int64_t base = ((int64_t)seg * kFilterBlocks + blk) * kFlatScoreSeg;
+        if (base >= len) break;
+        const int m = (int)min((int64_t)kFlatScoreSeg, len - base);
+        const float *brow = srow + base;
+        float v[MH];
+        if constexpr (VEC4) {
+#pragma unroll
+            for (int q = 0; q < MH / 4; ++q) {
+                const float4 f = *reinterpret_cast<const float4 *>(brow + min(q * 256 + lane * 4, m - 4));
+                v[4 * q] = f.x;
+                v[4 * q + 1] = f.y;
+                v[4 * q + 2] = f.z;
+                v[4 * q + 3] = f.w;
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < MH; ++t) v[t] = brow[min(t * 64 + lane, m - 1)];
+        }
+        // A bound on the lane's largest order key from the largest raw bit
+        // pattern as a signed integer (clamped loads repeat real elements):
+        // exact over the non-negative scores, which outrank every negative
+        // one; with none, no key exceeds +0's; infinities and NaNs are
+        // always examined.
+        int32_t mx = INT32_MIN;
+#pragma unroll
+        for (int t = 0; t < MH; ++t) mx = max(mx, (int32_t)__float_as_uint(v[t]));
+        const uint32_t bound = mx >= 0x7F800000 ? 0xFFFFFFFFu : mx >= 0 ? order_key(__int_as_float(mx)) : 0x80000000u;
+        if (__ballot(bound >= tkey) == 0) continue;
+        // survivors are rare: one atomic add per register slot that has any
+#pragma unroll
+        for (int t = 0; t < MH; ++t) {
+            const int e = slot_element<VEC4>(t, lane);
+            const uint32_t key = order_key(v[t]);
+            const bool keep = e < m && key >= tkey;
+            const uint64_t mask = __ballot(keep);
+            if (mask == 0) continue;
+            uint32_t pos = 0;
+            if (lane == 0) pos = atomicAdd(count + row, (uint32_t)__popcll(mask));
+            const uint32_t p = read_lane(pos, 0) + (uint32_t)below_me(mask);
+            if (keep && p < (uint32_t)kFlatListCap) lst[p] = pack(key, (uint32_t)(base + e));
+        }
+    }
+}
+
+// Rows whose list overflowed (more than kFlatListCap scores >= theta, i.e.
+// heavy ties at theta): one wave scans the whole row, one 4096-score block
+// at a time (wave_topk), merging each block's k best into the running k
+// best, and overwrites the row's result.  Other rows return at once.
+template <bool VEC4>
+__global__ __launch_bounds__(64 * WAVES) void flat_rescan_kernel(const float *__restrict__ scores, int64_t rows,
+                                                                 int64_t len, int k, const uint32_t *__restrict__ count,
+                                                                 int32_t *__restrict__ idx_out,
+                                                                 float *__restrict__ top_out)
+{
+    constexpr int MH = kFlatScoreSeg / 64;
+    __shared__ Stage stage[WAVES];
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    const int64_t row = (int64_t)blockIdx.x * WAVES + wv;
+    if (row >= rows || count[row] <= (uint32_t)kFlatListCap) return;
+    const float *srow = scores + row * len;
+    uint64_t best = 0;
+#pragma unroll 1
+    for (int64_t base = 0; base < len; base += kFlatScoreSeg) {
+        const int m = (int)min((int64_t)kFlatScoreSeg, len - base);
+        const float *brow = srow + base;
+        uint32_t key[MH];
+        load_keys<MH, VEC4>(brow, m, lane, key);
+        const auto id_of = [=](int t) { return (uint32_t)(base + slot_element<VEC4>(t, lane)); };
+        const auto reread = [=](int t) {
+            const int e = slot_element<VEC4>(t, lane);
+            return e < m ? order_key(brow[e]) : 0u;
+        };
+        const uint64_t c = wave_topk<MH, true>(key, reread, id_of, VEC4 ? MH : (m + 63) >> 6, k, stage[wv], lane);
+        if (lane < k) {
+            stage[wv].slot[lane] = best;
+            stage[wv].slot[k + lane] = c;
+        }
+        best = sorted_survivors(2 * k, stage[wv], lane);
+    }
+    if (lane < k) {
+        idx_out[row * k + lane] = (int32_t)unpack_id(best);
+        top_out[row * k + lane] = key_score((uint32_t)(best >> 32));
+    }
 }
 
 template <int MH>
@@ -512,6 +643,43 @@ hipError_t launch_flat_topk(const float *scores, int64_t rows, int64_t len, int 
         dst = t;
     }
     return e;
+}
+
+hipError_t launch_flat_topk_threshold(const float *scores, const float *gmax, int64_t rows, int64_t len, int k,
+                                      uint64_t *buf0, uint64_t *buf1, int32_t *tidx, float *ttop, uint32_t *count,
+                                      uint64_t *list, int32_t *idx, float *top, hipStream_t stream)
+{
+    if (rows <= 0) return hipSuccess;
+    if (k < 1 || k > 64 || len <= kFlatScoreSeg) return hipErrorInvalidValue;
+    const int64_t groups = (len + 63) / 64;  // >= 65 > k
+    hipError_t e = launch_flat_topk(gmax, rows, groups, k, buf0, buf1, tidx, ttop, stream);
+    if (e != hipSuccess) return e;
+    if ((e = launch_fill(count, rows, 0u, stream)) != hipSuccess) return e;
+    if ((e = launch_fill(reinterpret_cast<uint32_t *>(list), rows * kFlatListCap * 2, 0u, stream)) != hipSuccess)
+        return e;
+    const bool vec4 = len % 4 == 0;
+    const int64_t segs = (len + (int64_t)kFlatScoreSeg * kFilterBlocks - 1) / ((int64_t)kFlatScoreSeg * kFilterBlocks);
+    const int64_t blocks = (rows * segs + WAVES - 1) / WAVES;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    if (vec4)
+        hipLaunchKernelGGL((flat_filter_kernel<true>), dim3((unsigned)blocks), dim3(64 * WAVES), 0, stream, scores,
+                           rows, len, (int)segs, k, ttop, count, list);
+    else
+        hipLaunchKernelGGL((flat_filter_kernel<false>), dim3((unsigned)blocks), dim3(64 * WAVES), 0, stream, scores,
+                           rows, len, (int)segs, k, ttop, count, list);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // the lists' top-k (unused slots hold 0, the absent key), then the rows
+    // whose list overflowed
+    if ((e = launch_flat_pass<false, false>(list, rows, kFlatListCap, k, nullptr, idx, top, stream)) != hipSuccess)
+        return e;
+    const unsigned rblocks = (unsigned)((rows + WAVES - 1) / WAVES);
+    if (vec4)
+        hipLaunchKernelGGL((flat_rescan_kernel<true>), dim3(rblocks), dim3(64 * WAVES), 0, stream, scores, rows, len,
+                           k, count, idx, top);
+    else
+        hipLaunchKernelGGL((flat_rescan_kernel<false>), dim3(rblocks), dim3(64 * WAVES), 0, stream, scores, rows, len,
+                           k, count, idx, top);
+    return hipGetLastError();
 }
 
 int staircase_cells(int k)

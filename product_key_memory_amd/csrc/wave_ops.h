@@ -87,6 +87,19 @@ __device__ __forceinline__ T sort64_desc(T v)
     return v;
 }
 
+// A score's order key: an unsigned integer with the same order as the fp32
+// score (-0 folded onto +0, so equal scores give equal keys), and back.
+__device__ __forceinline__ uint32_t order_key(float f)
+{
+    const uint32_t u = __float_as_uint(f + 0.0f);
+    return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_score(uint32_t k)
+{
+    return __uint_as_float(k ^ ((uint32_t)((int32_t)~k >> 31) | 0x80000000u));
+}
+
 // Wave-wide sum; every lane receives the same value (pairwise xor tree, so
 // the association is identical in all lanes).
 __device__ __forceinline__ float wave_sum(float x)

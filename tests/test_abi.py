@@ -94,24 +94,35 @@ def test_workspace_bytes():
 
 
 def test_flat_workspace_bytes():
-    """Key scores [B, H, n^2] fp32, then the merge buffers: ceil(n^2 / 4096) * k
-    packed keys per row and ceil(that / 2048) * k, then the GEMM's row
-    exponents (H (B + 2 n) int32), each rounded to 256 bytes."""
+    """Key scores [B, H, n^2] fp32, the merge buffers, the GEMM's row
+    exponents (H (B + 2 n) int32), each rounded to 256 bytes.  Rows of at
+    most 4096 keys are topped directly: merge buffers for rows of n^2
+    scores, ceil(n^2 / 4096) * k packed keys per row and ceil(that / 2048) *
+    k.  Longer rows use a threshold: merge buffers for rows of G = ceil(n^2 /
+    64) group maxima, then the group maxima [B, H, G] f32, theta's indices
+    and scores [B, H, k], the list counts [B, H] u32 and the lists [B, H, 512]
+    of packed keys."""
     lib = pk.load_library()
-    cfg = pk.make_config(**GOOD)
-    H, n, k = 4, 1024, 32
 
     def rnd(x):
         return (x + 255) // 256 * 256
 
-    for B in (1, 16, 100):
-        rows = B * H
-        keys = (n * n + 4095) // 4096 * k
-        want = (rnd(rows * n * n * 4) + rnd(rows * keys * 8) + rnd(rows * ((keys + 2047) // 2048) * k * 8)
-                + rnd(H * (B + 2 * n) * 4))
-        got = ctypes.c_size_t()
-        assert lib.pkm_flat_workspace_bytes(ctypes.byref(cfg), B, ctypes.byref(got)) == pk.PKM_OK
-        assert got.value == want
+    for n, k in ((1024, 32), (64, 32), (65, 64), (16, 4)):
+        cfg = pk.make_config(**{**GOOD, "n_keys": n, "k": k})
+        H, N = 4, n * n
+        for B in (1, 16, 100):
+            rows = B * H
+            G = (N + 63) // 64
+            thr = N > 4096
+            keys = ((G if thr else N) + 4095) // 4096 * k
+            want = (rnd(rows * N * 4) + rnd(rows * keys * 8) + rnd(rows * ((keys + 2047) // 2048) * k * 8)
+                    + rnd(H * (B + 2 * n) * 4))
+            if thr:
+                want += rnd(rows * G * 4) + 2 * rnd(rows * k * 4) + rnd(rows * 4) + rnd(rows * 512 * 8)
+            got = ctypes.c_size_t()
+            assert lib.pkm_flat_workspace_bytes(ctypes.byref(cfg), B, ctypes.byref(got)) == pk.PKM_OK
+            assert got.value == want, (n, k, B)
+    cfg = pk.make_config(**GOOD)
     got = ctypes.c_size_t()
     assert lib.pkm_flat_workspace_bytes(ctypes.byref(cfg), 65537, ctypes.byref(got)) == pk.PKM_E_ARG
     assert lib.pkm_flat_workspace_bytes(ctypes.byref(cfg), -1, ctypes.byref(got)) == pk.PKM_E_ARG

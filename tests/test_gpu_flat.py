@@ -137,6 +137,55 @@ def test_flat_search_exact_ties(torch, B, D, H, n, k):
     np.testing.assert_array_equal(top.cpu().numpy().astype(np.float64), ref_top)
 
 
+def threshold_counts(s, k):
+    """For exact half scores s [B, H, 2, n]: per row of n^2 keys, how many
+    scores are >= theta, the k-th largest maximum over groups of 64
+    consecutive flat indices (the flat search keeps those in a list of 512
+    and rescans rows with more)."""
+    B, H, _, n = s.shape
+    N = n * n
+    flat = (s[:, :, 0, :, None] + s[:, :, 1, None, :]).reshape(B, H, N)
+    G = (N + 63) // 64
+    padded = np.full((B, H, G * 64), -np.inf)
+    padded[..., :N] = flat
+    gmax = padded.reshape(B, H, G, 64).max(-1)
+    theta = -np.sort(-gmax, axis=-1)[..., k - 1]
+    return (flat >= theta[..., None]).sum(-1)
+
+
+@pytest.mark.parametrize("B,D,H,n,k,lo,hi,overflow", [
+    (3, 64, 2, 128, 64, -1, 2, True),     # heavy ties at theta: rows rescanned
+    (2, 64, 1, 67, 64, -1, 2, True),      # 4489 keys (odd: scalar loads), rescanned
+    (3, 64, 2, 96, 16, -40, 41, False),   # wide integer range: every row from its list
+])
+def test_flat_search_threshold_paths(torch, B, D, H, n, k, lo, hi, overflow):
+    """Rows of more than 4096 keys are topped through a threshold: the
+    scores >= theta go to a list and a row with more than 512 of them is
+    scanned in full.  Integer inputs make every score exact, so the test
+    knows which rows take which path and the result must match the
+    canonical answer bit for bit either way."""
+    rng = np.random.default_rng(23)
+    q = rng.integers(lo, hi, size=(B, H, D)).astype(np.float32)
+    sub = rng.integers(lo, hi, size=(H, 2, n, D // 2)).astype(np.float32)
+    half = D // 2
+    s = np.stack([np.einsum("bhd,hnd->bhn", q[..., p * half:(p + 1) * half].astype(np.float64),
+                            sub[:, p].astype(np.float64)) for p in range(2)], axis=2)
+    assert np.abs(s).max() * 2 < 2 ** 24  # every score exact in fp32
+    counts = threshold_counts(s, k)
+    assert (counts >= k).all()
+    assert bool((counts > 512).any()) == overflow, counts
+    ref_idx, ref_top, _ = oracle.select(s, k)
+    mem = pk.Memory(D, H, n, k, "f32", max_batch=B)
+    dummy = np.zeros((H, D), np.float32)
+    P = pk.Params(_to(torch, np.zeros((H, D, D), np.float32)), *[_to(torch, dummy) for _ in range(4)],
+                  _to(torch, sub), None)
+    say("flat search threshold paths", B, D, H, n, k, "list counts", counts.ravel().tolist())
+    idx, top = mem.flat_search(P, _to(torch, q))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(idx.cpu().numpy(), ref_idx)
+    np.testing.assert_array_equal(top.cpu().numpy().astype(np.float64), ref_top)
+
+
 def test_flat_search_arguments(torch):
     wl = synthetic.Workload("flat_err", 4, 64, 1, 16, 4, "f32", "unit")
     params = synthetic.make_params(wl, with_values=False)
