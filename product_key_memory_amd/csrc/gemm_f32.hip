@@ -163,6 +163,10 @@ struct Stager {
     // the LDS row.
     __device__ __forceinline__ void store(uint32_t *smem, int s) const
     {
+        // a 1.0 the compiler cannot fold, so that a - hi (exact) is one mixed
+        // fp32/fp16 FMA per value rather than a conversion and a subtraction
+        float one = 1.0f;
+        asm volatile("" : "+v"(one));
 #pragma unroll
         for (int u = 0; u < T::UNITS; ++u) {
             if (!valid[u]) continue;
@@ -171,18 +175,17 @@ struct Stager {
             for (int q = 0; q < 4; ++q)
                 e[q] = fx2{__builtin_ldexpf(v[u][q >> 1][2 * (q & 1)], ex[u]),
                            __builtin_ldexpf(v[u][q >> 1][2 * (q & 1) + 1], ex[u])};
+            u4 w[kPieces];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const hx2 h = __builtin_convertvector(e[q], hx2);
+                const fx2 r = {__builtin_fmaf(e[q][0], one, -(float)h[0]), __builtin_fmaf(e[q][1], one, -(float)h[1])};
+                w[0][q] = __builtin_bit_cast(uint32_t, h);
+                w[1][q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, hx2));
+            }
             uint32_t *dst = smem + lds[u] + s * stage_stride[u];
 #pragma unroll
-            for (int p = 0; p < kPieces; ++p) {
-                u4 w;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const hx2 h = __builtin_convertvector(e[q], hx2);
-                    w[q] = __builtin_bit_cast(uint32_t, h);
-                    e[q] -= __builtin_convertvector(h, fx2);
-                }
-                *reinterpret_cast<u4 *>(dst + p * kPieceDw) = w;
-            }
+            for (int p = 0; p < kPieces; ++p) *reinterpret_cast<u4 *>(dst + p * kPieceDw) = w[p];
         }
     }
 };
