@@ -13,15 +13,16 @@
 // the whole lookup, and no two packed keys are equal.
 //
 // Per-half top-k (no sort of all n elements).  Lane l holds elements l,
-// l + 64, ... of the half in registers.  T = the k-th largest of the 64 lane maxima (one
-// bitonic sort of 64 words): at least k elements are >= T, so every winner
-// is.  The elements >= T (about 1.35 k for random scores) are compacted into
-// LDS with ballot + mbcnt and one 64-lane bitonic sort of packed keys orders
-// them (65 to 128 survivors: two sorts and one bitonic merge).  If more than
-// 128 survive (heavy exact ties), the exact k-th key is found by MSB-first
-// bisection with ballot counts, then the last index kept among the ties,
-// and exactly k are compacted.  The halves are selected one after
-// the other; every row load is issued before the first is consumed.
+// l + 64, ... of the half in registers.  T = the k-th largest of the 64 lane
+// maxima, its low bits cleared (a ballot bisection): at least k elements are
+// >= T, so every winner is.  The elements >= T (about 1.35 k for random
+// scores) are compacted into LDS with ballot + mbcnt and one 64-lane bitonic
+// sort of packed keys orders them (65 to 128 survivors: two sorts and one
+// bitonic merge).  If more than 128 survive (heavy exact ties), the exact
+// k-th key is found by MSB-first bisection with ballot counts, then the last
+// index kept among the ties, and exactly k are compacted.  The halves are
+// selected one after the other; every row load is issued before the first
+// is consumed.
 //
 // Candidates.  With both halves sorted, s0[i] + s1[j] can only be beaten by
 // the cells above and left of it, so a cell with (i+1)(j+1) > k has at
@@ -181,6 +182,23 @@ __device__ __forceinline__ int raise_threshold(const uint32_t (&key)[M], IdOf id
     return count;
 }
 
+// A first threshold from the lanes' largest keys v: the largest T whose low
+// 12 bits are clear such that at least k lanes hold v >= T, by MSB-first
+// bisection with ballot counts (one compare per step instead of sorting the
+// 64 maxima).  T is at most the k-th largest v, so at least k elements are
+// >= T, and within 2^-11 of it relative to the score, so hardly more survive.
+constexpr int kBisectLowBits = 12;
+__device__ __forceinline__ uint32_t kth_lane_bound(uint32_t v, int k)
+{
+    uint32_t t = 0;
+#pragma unroll
+    for (int bit = 31; bit >= kBisectLowBits; --bit) {
+        const uint32_t cand = t | (1u << bit);
+        if (__popcll(__ballot(v >= cand)) >= k) t = cand;
+    }
+    return t;
+}
+
 // Exact top-k (k <= 64) of the wave's elements, keys in registers key[M]
 // (0 = absent) and recomputed by slow_key for the rare heavy-tie path: lane
 // j < k receives the j-th best packed key.  RAISE: try raise_threshold
@@ -193,7 +211,7 @@ __device__ uint64_t wave_topk(const uint32_t (&key)[M], SlowKey slow_key, IdOf i
     uint32_t lane_max = 0;
 #pragma unroll
     for (int t = 0; t < M; ++t) lane_max = key[t] > lane_max ? key[t] : lane_max;
-    uint32_t kth = read_lane(sort64_desc(lane_max), k - 1);
+    uint32_t kth = kth_lane_bound(lane_max, k);
     uint32_t last = 0xFFFFFFFFu;
     int count = 0;
 #pragma unroll
@@ -217,7 +235,7 @@ __device__ uint64_t wave_topk_rolled(KeyOf key_of, IdOf id_of, int m, int k, Sta
         const uint32_t key = key_of(t);
         lane_max = key > lane_max ? key : lane_max;
     }
-    uint32_t kth = read_lane(sort64_desc(lane_max), k - 1);
+    uint32_t kth = kth_lane_bound(lane_max, k);
     uint32_t last = 0xFFFFFFFFu;
     int count = compact_rolled(key_of, id_of, m, kth, last, st, lane);
     if (count > kSlots) {
@@ -449,7 +467,7 @@ __global__ __launch_bounds__(64 * WAVES) void flat_topk_kernel(const void *__res
         uint32_t lane_max = 0;
 #pragma unroll
         for (int t = 0; t < MH; ++t) lane_max = key[t] > lane_max ? key[t] : lane_max;
-        uint32_t kth = read_lane(sort64_desc(lane_max), k - 1);
+        uint32_t kth = kth_lane_bound(lane_max, k);
         uint32_t last = 0xFFFFFFFFu;
         int count = 0;
 #pragma unroll
