@@ -179,10 +179,11 @@ pkm_status pkm_gather(pkm_ctx *ctx, const pkm_params *p, int64_t B, int32_t rows
  *   top   [B, H, k] fp32 the scores of those keys
  * workspace is caller-owned device memory of at least
  * pkm_flat_workspace_bytes(cfg, B) bytes (16-byte aligned): it holds the
- * B * H * n^2 fp32 key scores, the contraction's row exponents and the
- * top-k's buffers (for n^2 > 4096: the largest score of every group of 64
- * keys, the threshold derived from them and per-row lists of the scores at
- * or above it), so the call allocates nothing.  Work: 2 * B * H * n^2 * D
+ * B * H * n^2 fp32 key scores, the contraction's row exponents, the
+ * subkeys split into fp16 pieces, and the top-k's buffers (for n^2 > 4096:
+ * the largest score of every group of 64 keys, the threshold derived from
+ * them and per-row lists of the scores at or above it), so the call
+ * allocates nothing.  Work: 2 * B * H * n^2 * D
  * flop.  B <= 65536; a smaller workspace is PKM_E_ARG. */
 pkm_status pkm_flat_workspace_bytes(const pkm_config *cfg, int64_t B, size_t *bytes);
 pkm_status pkm_flat_search(pkm_ctx *ctx, const pkm_params *p, int64_t B, const float *qhat, void *workspace,

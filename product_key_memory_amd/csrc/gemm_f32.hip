@@ -57,13 +57,14 @@
 // Flat exact search (the comparator for the product search of
 // §Factorising the key space: every one of the n^2 concatenated keys
 // scored by one full-length dot product).  The B operand is the virtual
-// key matrix: row j = (a, c) is [C0[a]; C1[c]], read from the two subkey
-// sets as K advances (a chunk never straddles the halves), with the smaller
-// of the two rows' exponents.  M is a few dozen tokens: up to 32 use 32 x 256
-// tiles (4 waves of 32 x 64), more use 64 x 256 tiles (8 waves of 32 x 64,
-// ping-pong), which stage each key row once for twice the rows of A.  The
-// epilogue can record each row's largest score per group of 64 keys, from
-// which the top-k derives a threshold.
+// key matrix: row j = (a, c) is [C0[a]; C1[c]].  The subkey rows are split
+// into their fp16 pieces once per call (split_keys_kernel, each row with
+// its own power of two) in the order a staging lane copies them, so a tile
+// stages its 256 virtual rows by copying pieces; the two halves of K
+// accumulate separately (their key-row exponents differ) and are scaled
+// and summed in the epilogue.  M is a few dozen tokens: 32 x 256 tiles, 4
+// waves of 32 x 64.  The epilogue can record each row's largest score per
+// group of 64 keys, from which the top-k derives a threshold.
 #include "pkm_internal.h"
 #include "wave_ops.h"
 
@@ -130,29 +131,53 @@ __device__ __forceinline__ int row_exponent(float m)
 using BigTile = Tile<256, 256, 4, 2>;
 using SmallTile = Tile<128, 128, 2, 2>;
 using KeyTile = Tile<32, 256, 1, 4>;
-using KeyTile64 = Tile<64, 256, 2, 4>;
+
+// Eight consecutive k-values of one row, scaled by 2^ex and split into their
+// hi and lo fp16 pieces (a - hi is exact: one mixed fp32/fp16 FMA per value
+// with `one` a 1.0 the compiler cannot fold away).
+__device__ __forceinline__ void split8(const fx4 (&v)[2], int ex, float one, u4 &hi, u4 &lo)
+{
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const fx2 e = {__builtin_ldexpf(v[q >> 1][2 * (q & 1)], ex), __builtin_ldexpf(v[q >> 1][2 * (q & 1) + 1], ex)};
+        const hx2 h = __builtin_convertvector(e, hx2);
+        const fx2 r = {__builtin_fmaf(e[0], one, -(float)h[0]), __builtin_fmaf(e[1], one, -(float)h[1])};
+        hi[q] = __builtin_bit_cast(uint32_t, h);
+        lo[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, hx2));
+    }
+}
 
 // The staging work of one thread: UNITS groups; for each, the global source
-// of its 8 k-values (product-key B rows keep both halves' rows), the row's
-// exponent, and its LDS destination in stage 0 (dwords) with the stride
-// between stages.
+// of its 8 k-values, the row's exponent, and its LDS destination in stage 0
+// (dwords) with the stride between stages.  Product-key B rows come already
+// split (split_keys_kernel): a B unit copies its lane's two 16-byte pieces
+// of each chunk, from the first subkey set's row (src) and from chunk kch
+// on from the second set's (src2), both pointing at pieces.
 template <typename T, bool PRODUCT_B>
 struct Stager {
     const float *src[T::UNITS];
     const float *src2[PRODUCT_B ? T::UNITS : 1];
+    bool is_b[PRODUCT_B ? T::UNITS : 1];
+    int kch;
     int lds[T::UNITS], stage_stride[T::UNITS], ex[T::UNITS];
     bool valid[T::UNITS];
     fx4 v[T::UNITS][2];
 
-    __device__ __forceinline__ void load(int kt, int split)
+    __device__ __forceinline__ void load(int kt)
     {
 #pragma unroll
         for (int u = 0; u < T::UNITS; ++u) {
             if (!valid[u]) continue;
-            const int k = kt * kBK;
-            const float *q = src[u] + k;
-            if constexpr (PRODUCT_B)
-                if (src2[u] && k >= split) q = src2[u] + (k - split);
+            if constexpr (PRODUCT_B) {
+                if (is_b[u]) {
+                    const u4 *q = kt < kch ? reinterpret_cast<const u4 *>(src[u]) + (int64_t)kt * 128
+                                           : reinterpret_cast<const u4 *>(src2[u]) + (int64_t)(kt - kch) * 128;
+                    v[u][0] = __builtin_bit_cast(fx4, q[0]);
+                    v[u][1] = __builtin_bit_cast(fx4, q[64]);
+                    continue;
+                }
+            }
+            const float *q = src[u] + kt * kBK;
             v[u][0] = *reinterpret_cast<const fx4 *>(q);
             v[u][1] = *reinterpret_cast<const fx4 *>(q + 4);
         }
@@ -163,26 +188,22 @@ struct Stager {
     // the LDS row.
     __device__ __forceinline__ void store(uint32_t *smem, int s) const
     {
-        // a 1.0 the compiler cannot fold, so that a - hi (exact) is one mixed
-        // fp32/fp16 FMA per value rather than a conversion and a subtraction
         float one = 1.0f;
         asm volatile("" : "+v"(one));
 #pragma unroll
         for (int u = 0; u < T::UNITS; ++u) {
             if (!valid[u]) continue;
-            fx2 e[4];
+            if constexpr (PRODUCT_B) {
+                if (is_b[u]) {  // pieces as loaded
+                    uint32_t *dst = smem + lds[u] + s * stage_stride[u];
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                e[q] = fx2{__builtin_ldexpf(v[u][q >> 1][2 * (q & 1)], ex[u]),
-                           __builtin_ldexpf(v[u][q >> 1][2 * (q & 1) + 1], ex[u])};
-            u4 w[kPieces];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const hx2 h = __builtin_convertvector(e[q], hx2);
-                const fx2 r = {__builtin_fmaf(e[q][0], one, -(float)h[0]), __builtin_fmaf(e[q][1], one, -(float)h[1])};
-                w[0][q] = __builtin_bit_cast(uint32_t, h);
-                w[1][q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, hx2));
+                    for (int p = 0; p < kPieces; ++p)
+                        *reinterpret_cast<u4 *>(dst + p * kPieceDw) = __builtin_bit_cast(u4, v[u][p]);
+                    continue;
+                }
             }
+            u4 w[kPieces];
+            split8(v[u], ex[u], one, w[0], w[1]);
             uint32_t *dst = smem + lds[u] + s * stage_stride[u];
 #pragma unroll
             for (int p = 0; p < kPieces; ++p) *reinterpret_cast<u4 *>(dst + p * kPieceDw) = w[p];
@@ -228,6 +249,7 @@ __device__ __forceinline__ void mfma_frags(floatx16 (&acc)[T::TM][T::TN], const 
 template <typename T, bool BN_EPILOGUE, bool STREAM_OUT, bool PRODUCT_B = false, bool ACCUMULATE = false>
 __global__ __launch_bounds__(T::THREADS) void gemm_nt_f32_kernel(GemmArgs a)
 {
+    static_assert(!PRODUCT_B || (!STREAM_OUT && !BN_EPILOGUE && !ACCUMULATE), "product-key B: plain staged epilogue");
     extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
     uint32_t *As = smem;
     uint32_t *Bs = smem + T::STAGES * T::BM * kRowDw;
@@ -261,11 +283,18 @@ __global__ __launch_bounds__(T::THREADS) void gemm_nt_f32_kernel(GemmArgs a)
     // Rows past the matrix edge re-read the last row; their results are
     // never stored.
     Stager<T, PRODUCT_B> st;
+    st.kch = a.split_k / kBK;
+    // product-key B: the split rows of this batch entry's two subkey sets
+    const int kgroups = (a.key_n + 31) / 32;
+    const u4 *set0 =
+        PRODUCT_B ? reinterpret_cast<const u4 *>(a.b_split) + (int64_t)g * 2 * kgroups * st.kch * 128 : nullptr;
+    const u4 *set1 = PRODUCT_B ? set0 + (int64_t)kgroups * st.kch * 128 : nullptr;
 #pragma unroll
     for (int u = 0; u < T::UNITS; ++u) {
         const int grp = wave + T::WAVES * u;
         st.valid[u] = grp < T::GROUPS;
         const int r = min(grp, T::GROUPS - 1) * 32 + il;  // row of the A tile, then of the B tile
+        if constexpr (PRODUCT_B) st.is_b[u] = r >= T::BM;
         if (r < T::BM) {
             const int m = min(m0 + r, a.M - 1);
             st.src[u] = A + (int64_t)m * a.lda + kk * 8;
@@ -276,10 +305,11 @@ __global__ __launch_bounds__(T::THREADS) void gemm_nt_f32_kernel(GemmArgs a)
         } else {
             const int j = min(n0 + r - T::BM, a.N - 1);
             if constexpr (PRODUCT_B) {
+                // lane (kk, row % 32) of the subkey row's group, chunk 0
                 const int ka = j / a.key_n, kc = j - ka * a.key_n;
-                st.src[u] = Bmat + (int64_t)ka * a.ldb + kk * 8;
-                st.src2[u] = a.B2 + (int64_t)g * a.strideB + (int64_t)kc * a.ldb + kk * 8;
-                st.ex[u] = min(b_exp[ka], b2_exp[kc]);
+                st.src[u] = reinterpret_cast<const float *>(set0 + (int64_t)(ka / 32) * st.kch * 128 + kk * 32 + ka % 32);
+                st.src2[u] = reinterpret_cast<const float *>(set1 + (int64_t)(kc / 32) * st.kch * 128 + kk * 32 + kc % 32);
+                st.ex[u] = 0;
             } else {
                 st.src[u] = Bmat + (int64_t)j * a.ldb + kk * 8;
                 st.ex[u] = b_exp[j];
@@ -288,50 +318,62 @@ __global__ __launch_bounds__(T::THREADS) void gemm_nt_f32_kernel(GemmArgs a)
             st.stage_stride[u] = T::BN * kRowDw;
         }
     }
-    // exponent of output column n (its B row's)
-    const auto col_exp = [&](int n) {
-        if constexpr (PRODUCT_B) {
-            const int ka = n / a.key_n;
-            return min(b_exp[ka], b2_exp[n - ka * a.key_n]);
-        }
-        return b_exp[n];
-    };
+    // exponent of output column n (its B row's; product-key columns are
+    // scaled in the epilogue's combination below instead)
+    const auto col_exp = [&](int n) { return PRODUCT_B ? 0 : b_exp[n]; };
 
-    floatx16 acc[T::TM][T::TN];
+    // Product-key B: the two halves of K carry their own key-row exponents,
+    // so they accumulate separately (acc, then acc2) and meet in the epilogue
+    floatx16 acc[T::TM][T::TN], acc2[PRODUCT_B ? T::TM : 1][PRODUCT_B ? T::TN : 1];
 #pragma unroll
     for (int i = 0; i < T::TM; ++i)
 #pragma unroll
         for (int j = 0; j < T::TN; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+    if constexpr (PRODUCT_B)
+#pragma unroll
+        for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+            for (int j = 0; j < T::TN; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc2[i][j][v] = 0.0f;
 
     const int KT = klen / kBK;
-    st.load(0, a.split_k);
+    st.load(0);
     st.store(smem, 0);
-    if (KT > 1) st.load(1, a.split_k);
+    if (KT > 1) st.load(1);
     __syncthreads();
     const bool late = T::PING_PONG && wave >= T::WAVES / 2;
     if (late) __builtin_amdgcn_s_barrier();
-    for (int kt = 0; kt < KT; ++kt) {
-        const int s = kt & 1;
-        hx8 af[T::TM][kPieces], bf[T::TN][kPieces];
-        read_frags<T>(af, bf, As + s * T::BM * kRowDw, Bs + s * T::BN * kRowDw, wm, wn, il, kk);
-        // chunk kt + 1 into the other stage (last read in chunk kt - 1,
-        // before the barrier that closed it), then fetch chunk kt + 2
-        if (kt + 1 < KT) {
-            st.store(smem, s ^ 1);
-            if (kt + 2 < KT) st.load(kt + 2, a.split_k);
+    const auto run = [&](auto &accx, int kt0, int kt1) {
+        for (int kt = kt0; kt < kt1; ++kt) {
+            const int s = kt & 1;
+            hx8 af[T::TM][kPieces], bf[T::TN][kPieces];
+            read_frags<T>(af, bf, As + s * T::BM * kRowDw, Bs + s * T::BN * kRowDw, wm, wn, il, kk);
+            // chunk kt + 1 into the other stage (last read in chunk kt - 1,
+            // before the barrier that closed it), then fetch chunk kt + 2
+            if (kt + 1 < KT) {
+                st.store(smem, s ^ 1);
+                if (kt + 2 < KT) st.load(kt + 2);
+            }
+            if constexpr (T::PING_PONG) {
+                __syncthreads();
+                __builtin_amdgcn_s_setprio(1);
+                mfma_frags<T>(accx, af, bf);
+                __builtin_amdgcn_s_setprio(0);
+                __syncthreads();
+            } else {
+                mfma_frags<T>(accx, af, bf);
+                __syncthreads();
+            }
         }
-        if constexpr (T::PING_PONG) {
-            __syncthreads();
-            __builtin_amdgcn_s_setprio(1);
-            mfma_frags<T>(acc, af, bf);
-            __builtin_amdgcn_s_setprio(0);
-            __syncthreads();
-        } else {
-            mfma_frags<T>(acc, af, bf);
-            __syncthreads();
-        }
+    };
+    if constexpr (PRODUCT_B) {
+        run(acc, 0, st.kch);
+        run(acc2, st.kch, KT);
+    } else {
+        run(acc, 0, KT);
     }
     if (T::PING_PONG && !late) __builtin_amdgcn_s_barrier();
 
@@ -341,6 +383,27 @@ __global__ __launch_bounds__(T::THREADS) void gemm_nt_f32_kernel(GemmArgs a)
     for (int t = tid; t < T::BM + T::BN; t += T::THREADS)
         ex_lds[t] = t < T::BM ? row_exp(min(m0 + t, a.M - 1)) : col_exp(min(n0 + t - T::BM, a.N - 1));
     __syncthreads();
+    if constexpr (PRODUCT_B) {
+        // both halves to true scale and summed, into acc (32x32 layout:
+        // register v of lane l is row 8 (v / 4) + 4 (l / 32) + v % 4, column
+        // l % 32 of its block); the staged epilogue below then scales nothing
+#pragma unroll
+        for (int j = 0; j < T::TN; ++j) {
+            const int col = min(n0 + wn * T::TN * 32 + j * 32 + il, a.N - 1);
+            const int ka = col / a.key_n;
+            const int e0 = b_exp[ka], e1 = b2_exp[col - ka * a.key_n];
+#pragma unroll
+            for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+                for (int v4 = 0; v4 < 4; ++v4) {
+                    const i4 er = *reinterpret_cast<const i4 *>(&ex_lds[wm * T::TM * 32 + i * 32 + v4 * 8 + kk * 4]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        acc[i][j][v4 * 4 + e] = __builtin_ldexpf(acc[i][j][v4 * 4 + e], -(er[e] + e0)) +
+                                                __builtin_ldexpf(acc2[i][j][v4 * 4 + e], -(er[e] + e1));
+                }
+        }
+    }
 
     if constexpr (STREAM_OUT) {
         // A streamed result (read once by the next kernel) is stored straight
@@ -426,8 +489,9 @@ __global__ __launch_bounds__(T::THREADS) void gemm_nt_f32_kernel(GemmArgs a)
             const bool live = row < a.M && ncol > 0;
             fx4 x = *reinterpret_cast<const fx4 *>(&stage[r * CS + c0]);
             const int erow = ex_lds[pass * PR + r];
+            if constexpr (!PRODUCT_B)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = __builtin_ldexpf(x[e], -(erow + ecol[e]));
+                for (int e = 0; e < 4; ++e) x[e] = __builtin_ldexpf(x[e], -(erow + ecol[e]));
             if (BN_EPILOGUE) x = (x - bn_mean) * bn_mul + bn_beta;
             if constexpr (PRODUCT_B) {
                 static_assert(T::BN % 64 == 0, "a group of 64 columns is 16 lanes of one row");
@@ -654,6 +718,43 @@ hipError_t prepare_exponents(GemmArgs &a, bool product_b, hipStream_t stream)
     return launch_exponents(jobs, n, a.zero_ptr, a.zero_n, stream);
 }
 
+// The key rows of a product-key B operand split once per call, for the
+// flat search: every subkey row of both sets (batch entry g, set p = 0 at
+// B, 1 at B2) scaled by its own power of two (b_exp / b2_exp) and split as
+// split8 does, stored in the order a staging lane copies them: per set,
+// [group of 32 rows][chunk of 16 k][piece][lane][8 fp16] with lane l = 32 kh
+// + row % 32 holding k = 16 chunk + 8 kh .. + 7.  Rows past key_n are zero.
+// One thread per (set, group, chunk, lane).
+__global__ __launch_bounds__(256) void split_keys_kernel(const float *B, const float *B2, int64_t strideB, int64_t ldb,
+                                                         int key_n, int kch, const int32_t *b_exp,
+                                                         const int32_t *b2_exp, u4 *out)
+{
+    const int set = blockIdx.y;
+    const int g = set >> 1, half = set & 1;
+    const int64_t per_set = (int64_t)((key_n + 31) / 32) * kch * 64;
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= per_set) return;
+    const int lane = (int)(t & 63);
+    const int64_t blk = t >> 6;  // group * kch + chunk
+    const int grp = (int)(blk / kch), c = (int)(blk - (int64_t)grp * kch);
+    const int row = grp * 32 + (lane & 31);
+    fx4 v[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+    int ex = 0;
+    if (row < key_n) {
+        const float *src = (half ? B2 : B) + (int64_t)g * strideB + (int64_t)row * ldb + c * kBK + (lane >> 5) * 8;
+        v[0] = *reinterpret_cast<const fx4 *>(src);
+        v[1] = *reinterpret_cast<const fx4 *>(src + 4);
+        ex = (half ? b2_exp : b_exp)[(int64_t)g * key_n + row];
+    }
+    float one = 1.0f;
+    asm volatile("" : "+v"(one));
+    u4 hi, lo;
+    split8(v, ex, one, hi, lo);
+    u4 *dst = out + (int64_t)set * per_set * 2 + blk * 128 + lane;
+    dst[0] = hi;
+    dst[64] = lo;
+}
+
 template <typename T>
 int64_t tile_count(const GemmArgs &a)
 {
@@ -720,6 +821,11 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *P, int 
 
 }  // namespace
 
+int64_t gemm_split_bytes(const GemmArgs &a)
+{
+    return (int64_t)a.batch * 2 * ((a.key_n + 31) / 32) * 32 * (int64_t)a.split_k * 4;
+}
+
 int64_t gemm_exp_ints(const GemmArgs &a)
 {
     const int64_t b_rows = a.B2 ? 2 * (int64_t)a.key_n : (int64_t)a.N;
@@ -763,14 +869,20 @@ hipError_t launch_gemm_nt_f32(const GemmArgs &args, hipStream_t stream)
 hipError_t launch_gemm_nt_f32_product(const GemmArgs &args, hipStream_t stream)
 {
     if (args.M <= 0 || args.N <= 0 || args.batch <= 0) return hipSuccess;
-    if (args.K % 32 != 0 || args.split_k % 32 != 0 || args.split_k <= 0 || args.split_k >= args.K || !args.B2 ||
-        args.key_n <= 0 || (int64_t)args.key_n * args.key_n < args.N || args.bn_mean || args.k_chunk != 0)
+    if (args.K % 32 != 0 || args.split_k % 32 != 0 || 2 * args.split_k != args.K || !args.B2 || args.key_n <= 0 ||
+        (int64_t)args.key_n * args.key_n < args.N || args.bn_mean || args.k_chunk != 0 || !args.b_split ||
+        args.b_split_bytes < gemm_split_bytes(args) || (reinterpret_cast<uintptr_t>(args.b_split) & 15) != 0)
         return hipErrorInvalidValue;
-    if (tile_count<KeyTile>(args) > 0x7FFFFFFF || args.batch > 65535) return hipErrorInvalidConfiguration;
+    if (tile_count<KeyTile>(args) > 0x7FFFFFFF || args.batch > 32767) return hipErrorInvalidConfiguration;
     GemmArgs a = args;
     hipError_t e = prepare_exponents(a, true, stream);
     if (e != hipSuccess) return e;
-    if (a.M > 32) return launch_variant<KeyTile64, false, false, true>(a, stream);
+    const int kch = a.split_k / kBK;
+    const int64_t per_set = (int64_t)((a.key_n + 31) / 32) * kch * 64;
+    hipLaunchKernelGGL(split_keys_kernel, dim3((unsigned)((per_set + 255) / 256), 2 * a.batch), dim3(256), 0, stream,
+                       a.B, a.B2, a.strideB, a.ldb, a.key_n, kch, a.b_exp, a.b2_exp,
+                       reinterpret_cast<u4 *>(a.b_split));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     return launch_variant<KeyTile, false, false, true>(a, stream);
 }
 

@@ -269,9 +269,11 @@ pkm_status run_score(const pkm_ctx *ctx, const pkm_params *p, int64_t B, const f
 // [B, H, G] (G = ceil(n^2 / 64)), theta's top-k [B, H, k] (indices, scores),
 // the list counts [B, H] and the lists [B, H, kFlatListCap] of packed keys.
 // The merge buffers serve the top-k over rows of G group maxima then, else
-// over the n^2 scores.  False if B is out of range.
+// over the n^2 scores.  Last, the subkeys split into fp16 pieces for the
+// contraction (H * 2 sets of n rounded up to 32 rows, D/2 * 4 bytes each).
+// False if B is out of range.
 constexpr int64_t kFlatMaxBatch = 65536;
-constexpr int kFlatPieces = 9;
+constexpr int kFlatPieces = 10;
 constexpr int64_t kFlatDirectMax = 4096;  // longest row topped without a threshold
 bool flat_layout(const pkm_config &c, int64_t B, size_t sizes[kFlatPieces])
 {
@@ -293,6 +295,7 @@ bool flat_layout(const pkm_config &c, int64_t B, size_t sizes[kFlatPieces])
         sizes[7] = round_up((size_t)rows * sizeof(uint32_t));
         sizes[8] = round_up((size_t)(rows * pkm::kFlatListCap) * sizeof(uint64_t));
     }
+    sizes[9] = round_up((size_t)c.heads * 2 * ((c.n_keys + 31) / 32) * 32 * (size_t)(c.dim / 2) * 4);
     return true;
 }
 
@@ -579,6 +582,8 @@ pkm_status pkm_flat_search(pkm_ctx *ctx, const pkm_params *p, int64_t B, const f
     const int64_t rows = B * c.heads, N = (int64_t)c.n_keys * c.n_keys;
     const bool threshold = N > kFlatDirectMax;
     pkm::GemmArgs a = flat_args(c, p, B, qhat, scores, exps, (int64_t)(sizes[3] / sizeof(int32_t)));
+    a.b_split = piece[9];
+    a.b_split_bytes = (int64_t)sizes[9];
     float *gmax = threshold ? reinterpret_cast<float *>(piece[4]) : nullptr;
     if (gmax) {
         const int64_t G = (N + 63) / 64;

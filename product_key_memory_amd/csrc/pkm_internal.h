@@ -30,7 +30,8 @@ struct GemmArgs {
     bool stream_out;
     // Product-key B operand (B2 non-null): row j of B is the concatenation
     // [B[j / key_n][0, split_k), B2[j % key_n][0, K - split_k)], both with
-    // row stride ldb and batch stride strideB; split_k % 32 == 0.
+    // row stride ldb and batch stride strideB; split_k = K / 2, a multiple
+    // of 32; needs b_split.
     const float *B2;
     int split_k, key_n;
     // accumulate: C += A . B^T instead of C = A . B^T (no BN, no streaming).
@@ -80,6 +81,12 @@ struct GemmArgs {
     // group_max[m * group_ld + g * group_stride + n / 64].
     float *group_max;
     int64_t group_ld, group_stride;
+    // Product-key B operand only: a workspace of b_split_bytes >=
+    // gemm_split_bytes(a) bytes (16-byte aligned) into which the subkey rows
+    // are split into fp16 pieces once, so the contraction copies them
+    // instead of splitting every virtual key row in every tile.
+    void *b_split;
+    int64_t b_split_bytes;
     // set by the launcher
     int k_chunk;  // K per split (0: no split)
     const int32_t *a_exp, *b_exp, *b2_exp;
@@ -88,9 +95,13 @@ constexpr int kMaxKSplits = 4;
 // int32s of row exponents a contraction needs: batch * (M + N), or
 // batch * (M + 2 key_n) with a product-key B operand.
 int64_t gemm_exp_ints(const GemmArgs &a);
+// bytes of the pre-split key rows: batch * 2 sets * key_n rounded up to 32
+// rows * split_k * (two fp16 pieces)
+int64_t gemm_split_bytes(const GemmArgs &a);
 hipError_t launch_gemm_nt_f32(const GemmArgs &a, hipStream_t stream);
-// The same contraction with a product-key B operand and a 32 x 256 tile
-// suited to a few dozen rows of A (the flat exact search over all keys).
+// The same contraction with a product-key B operand (b_split required) and
+// 32 x 256 tiles, suited to a few dozen rows of A (the flat exact search
+// over all keys).
 hipError_t launch_gemm_nt_f32_product(const GemmArgs &a, hipStream_t stream);
 
 // Per (token, head): exact top-k of each half's n scores, the exact top-k of

@@ -101,7 +101,8 @@ def test_flat_workspace_bytes():
     k.  Longer rows use a threshold: merge buffers for rows of G = ceil(n^2 /
     64) group maxima, then the group maxima [B, H, G] f32, theta's indices
     and scores [B, H, k], the list counts [B, H] u32 and the lists [B, H, 512]
-    of packed keys."""
+    of packed keys.  Last, the subkeys split into two fp16 pieces (H * 2 sets
+    of n rounded up to 32 rows, D/2 values, 4 bytes each)."""
     lib = pk.load_library()
 
     def rnd(x):
@@ -119,6 +120,7 @@ def test_flat_workspace_bytes():
                     + rnd(H * (B + 2 * n) * 4))
             if thr:
                 want += rnd(rows * G * 4) + 2 * rnd(rows * k * 4) + rnd(rows * 4) + rnd(rows * 512 * 8)
+            want += rnd(H * 2 * ((n + 31) // 32) * 32 * (1024 // 2) * 4)  # the split subkeys
             got = ctypes.c_size_t()
             assert lib.pkm_flat_workspace_bytes(ctypes.byref(cfg), B, ctypes.byref(got)) == pk.PKM_OK
             assert got.value == want, (n, k, B)
