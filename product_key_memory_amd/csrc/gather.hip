@@ -13,7 +13,7 @@
 // token's (row, weight) pairs are read once into lanes and broadcast with
 // v_readlane, so every row address is a scalar base plus the lane offset.
 // Sixteen row loads are issued before any is consumed to keep enough bytes in
-// flight per wave.  Rows are summed in their given order, so results are
+// flight per wave; they are non-temporal (each row is read once).  Rows are summed in their given order, so results are
 // bitwise reproducible.  A row index outside [0, N) is clamped into range
 // (memory-safe; the result for such a row is meaningless).
 #include "pkm_internal.h"
@@ -63,6 +63,16 @@ __host__ __device__ __forceinline__ int64_t elem_bytes(int64_t c)
 }
 
 typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+
+// One lane's 16 bytes of a table row, loaded non-temporally: each row is
+// read once per lookup, so the load need not keep it in the caches (measured
+// ≈3 % faster for the whole step than plain loads, same results).
+__device__ __forceinline__ uint4 load_row_piece(const uint8_t *p)
+{
+    const u4v t = __builtin_nontemporal_load(reinterpret_cast<const u4v *>(p));
+    return make_uint4(t[0], t[1], t[2], t[3]);
+}
 
 template <int VT>
 __device__ __forceinline__ void accumulate(float (&acc)[Fmt<VT>::EPL], const uint4 &v, float wt)
@@ -141,7 +151,7 @@ __global__ __launch_bounds__(64 * WAVES) void gather_kernel(const uint8_t *__res
                 const int row = min(max(__builtin_amdgcn_readlane(my_row, r + u), 0), N - 1);
                 wt[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), r + u));
                 if constexpr (SCALED) wt[u] *= scale[row];
-                v[u] = active ? *reinterpret_cast<const uint4 *>(col + (int64_t)row * row_bytes) : make_uint4(0, 0, 0, 0);
+                v[u] = active ? load_row_piece(col + (int64_t)row * row_bytes) : make_uint4(0, 0, 0, 0);
             }
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u) accumulate<VT>(acc, v[u], wt[u]);
@@ -150,7 +160,7 @@ __global__ __launch_bounds__(64 * WAVES) void gather_kernel(const uint8_t *__res
             const int row = min(max(__builtin_amdgcn_readlane(my_row, r), 0), N - 1);
             float wt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), r));
             if constexpr (SCALED) wt *= scale[row];
-            const uint4 v = active ? *reinterpret_cast<const uint4 *>(col + (int64_t)row * row_bytes) : make_uint4(0, 0, 0, 0);
+            const uint4 v = active ? load_row_piece(col + (int64_t)row * row_bytes) : make_uint4(0, 0, 0, 0);
             accumulate<VT>(acc, v, wt);
         }
     }
@@ -217,8 +227,7 @@ __global__ __launch_bounds__(64 * WAVES) void gather_pair_kernel(const uint8_t *
                 const int row = min(max(half ? row_o : row_e, 0), N - 1);
                 wt[u] = ok ? (half ? w_o : w_e) : 0.0f;
                 if constexpr (SCALED) wt[u] *= scale[row];
-                v[u] = active && ok ? *reinterpret_cast<const uint4 *>(col + (int64_t)row * row_bytes)
-                                    : make_uint4(0, 0, 0, 0);
+                v[u] = active && ok ? load_row_piece(col + (int64_t)row * row_bytes) : make_uint4(0, 0, 0, 0);
             }
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u) accumulate<VT>(acc, v[u], wt[u]);
