@@ -62,6 +62,22 @@ __host__ __device__ __forceinline__ int64_t elem_bytes(int64_t c)
 }
 
 typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+typedef float f4v __attribute__((ext_vector_type(4)));
+
+// Loads of data read once per call (table rows, the old value-gradient
+// rows), non-temporal so they do not displace what the caches hold for the
+// rest of the pass (measured: the backward 1.81 -> 1.72 ms, same results).
+__device__ __forceinline__ uint4 load_once(const uint8_t *p)
+{
+    const u4v t = __builtin_nontemporal_load(reinterpret_cast<const u4v *>(p));
+    return make_uint4(t[0], t[1], t[2], t[3]);
+}
+__device__ __forceinline__ float4 load_once(const float *p)
+{
+    const f4v t = __builtin_nontemporal_load(reinterpret_cast<const f4v *>(p));
+    return make_float4(t[0], t[1], t[2], t[3]);
+}
 
 // dot of EPL decoded values with EPL fp32 values
 template <int VT>
@@ -189,8 +205,7 @@ __global__ __launch_bounds__(64 * WAVES) void value_backward_kernel(const uint8_
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int r = __builtin_amdgcn_readlane(my_row, min(j0 + u, k - 1));
-                v[u] = active ? *reinterpret_cast<const uint4 *>(values + (int64_t)r * row_bytes + elem_bytes<VT>(c0))
-                              : make_uint4(0, 0, 0, 0);
+                v[u] = active ? load_once(values + (int64_t)r * row_bytes + elem_bytes<VT>(c0)) : make_uint4(0, 0, 0, 0);
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) part[u] += dot_row<VT>(v[u], dv);
@@ -553,7 +568,7 @@ __global__ __launch_bounds__(64 * WAVES) void value_grad_kernel(const uint32_t *
                     const int c = c1 + 256 * q + 4 * lane;
                     act[q] = c < D;
                     col[q] = act[q] ? c : 0;
-                    old[q] = act[q] ? *reinterpret_cast<const float4 *>(out + col[q]) : make_float4(0, 0, 0, 0);
+                    old[q] = act[q] ? load_once(out + col[q]) : make_float4(0, 0, 0, 0);
                     acc[q] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
                 }
                 for (uint32_t t0 = 0; t0 < m; t0 += 2) {
@@ -585,7 +600,6 @@ __global__ __launch_bounds__(64 * WAVES) void value_grad_kernel(const uint32_t *
                         const float4 nv = make_float4(old[q].x + acc[q].x, old[q].y + acc[q].y, old[q].z + acc[q].z,
                                                       old[q].w + acc[q].w);
                         // written once per call: stream it out of the caches
-                        typedef float f4v __attribute__((ext_vector_type(4)));
                         const f4v nvv = {nv.x, nv.y, nv.z, nv.w};
                         __builtin_nontemporal_store(nvv, reinterpret_cast<f4v *>(out + col[q]));
                     }
