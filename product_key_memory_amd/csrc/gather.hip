@@ -13,7 +13,7 @@
 // token's (row, weight) pairs are read once into lanes and broadcast with
 // v_readlane, so every row address is a scalar base plus the lane offset.
 // Sixteen row loads are issued before any is consumed to keep enough bytes in
-// flight per wave; they are non-temporal (each row is read once).  Rows are summed in their given order, so results are
+// flight per wave (non-temporal when the launch seldom repeats a row).  Rows are summed in their given order, so results are
 // bitwise reproducible.  A row index outside [0, N) is clamped into range
 // (memory-safe; the result for such a row is meaningless).
 #include "pkm_internal.h"
@@ -23,9 +23,7 @@ namespace {
 
 constexpr int WAVES = 4;
 constexpr int UNROLL = 16;  // row loads in flight per wave
-#ifndef PAIR_SPLIT
-#define PAIR_SPLIT 2
-#endif
+constexpr int kPairSplit = 2;  // waves per token in gather_pair_kernel
 
 template <int VT>
 struct Fmt;
@@ -65,13 +63,20 @@ __host__ __device__ __forceinline__ int64_t elem_bytes(int64_t c)
 typedef float floatx2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u4v __attribute__((ext_vector_type(4)));
 
-// One lane's 16 bytes of a table row, loaded non-temporally: each row is
-// read once per lookup, so the load need not keep it in the caches (measured
-// ≈3 % faster for the whole step than plain loads, same results).
+// One lane's 16 bytes of a table row.  NT: a non-temporal load, for
+// launches that read fewer rows than the table holds (B R < N), where a row
+// is seldom read twice and keeping it would only displace the rest of the
+// step's data (the default shape: 2-3 % faster steps).  With more reads than
+// rows (e.g. 16,384 tokens of 128 rows over 1M rows) repeats are common and
+// plain loads let the caches serve them (2 % faster there).
+template <bool NT>
 __device__ __forceinline__ uint4 load_row_piece(const uint8_t *p)
 {
-    const u4v t = __builtin_nontemporal_load(reinterpret_cast<const u4v *>(p));
-    return make_uint4(t[0], t[1], t[2], t[3]);
+    if constexpr (NT) {
+        const u4v t = __builtin_nontemporal_load(reinterpret_cast<const u4v *>(p));
+        return make_uint4(t[0], t[1], t[2], t[3]);
+    }
+    return *reinterpret_cast<const uint4 *>(p);
 }
 
 template <int VT>
@@ -114,7 +119,7 @@ __device__ __forceinline__ void accumulate(float (&acc)[Fmt<VT>::EPL], const uin
     }
 }
 
-template <int VT>
+template <int VT, bool NT>
 __global__ __launch_bounds__(64 * WAVES) void gather_kernel(const uint8_t *__restrict__ values,
                                                             const float *__restrict__ scale, int D, int N, int64_t B, int R,
                                                             int slices, const int32_t *__restrict__ idx,
@@ -151,7 +156,7 @@ __global__ __launch_bounds__(64 * WAVES) void gather_kernel(const uint8_t *__res
                 const int row = min(max(__builtin_amdgcn_readlane(my_row, r + u), 0), N - 1);
                 wt[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), r + u));
                 if constexpr (SCALED) wt[u] *= scale[row];
-                v[u] = active ? load_row_piece(col + (int64_t)row * row_bytes) : make_uint4(0, 0, 0, 0);
+                v[u] = active ? load_row_piece<NT>(col + (int64_t)row * row_bytes) : make_uint4(0, 0, 0, 0);
             }
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u) accumulate<VT>(acc, v[u], wt[u]);
@@ -160,7 +165,7 @@ __global__ __launch_bounds__(64 * WAVES) void gather_kernel(const uint8_t *__res
             const int row = min(max(__builtin_amdgcn_readlane(my_row, r), 0), N - 1);
             float wt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), r));
             if constexpr (SCALED) wt *= scale[row];
-            const uint4 v = active ? load_row_piece(col + (int64_t)row * row_bytes) : make_uint4(0, 0, 0, 0);
+            const uint4 v = active ? load_row_piece<NT>(col + (int64_t)row * row_bytes) : make_uint4(0, 0, 0, 0);
             accumulate<VT>(acc, v, wt);
         }
     }
@@ -179,7 +184,7 @@ __global__ __launch_bounds__(64 * WAVES) void gather_kernel(const uint8_t *__res
 // fixed order: odd rows onto even rows within a wave, then the later waves
 // onto the first through LDS.  (Measured at D = 1024, int4: SPLIT 2 is the
 // fastest of 1, 2 and 4, all near 4 TB/s: 512-byte random rows.)
-template <int VT, int SPLIT>
+template <int VT, int SPLIT, bool NT>
 __global__ __launch_bounds__(64 * WAVES) void gather_pair_kernel(const uint8_t *__restrict__ values,
                                                                  const float *__restrict__ scale, int D, int N,
                                                                  int64_t B, int R, const int32_t *__restrict__ idx,
@@ -227,7 +232,7 @@ __global__ __launch_bounds__(64 * WAVES) void gather_pair_kernel(const uint8_t *
                 const int row = min(max(half ? row_o : row_e, 0), N - 1);
                 wt[u] = ok ? (half ? w_o : w_e) : 0.0f;
                 if constexpr (SCALED) wt[u] *= scale[row];
-                v[u] = active && ok ? load_row_piece(col + (int64_t)row * row_bytes) : make_uint4(0, 0, 0, 0);
+                v[u] = active && ok ? load_row_piece<NT>(col + (int64_t)row * row_bytes) : make_uint4(0, 0, 0, 0);
             }
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u) accumulate<VT>(acc, v[u], wt[u]);
@@ -257,20 +262,30 @@ template <int VT>
 hipError_t launch(const void *values, const float *scale, int D, int N, int64_t B, int R, const int32_t *idx,
                   const float *w, float *out, hipStream_t stream)
 {
+    const bool nt = B * R < N;
+    const uint8_t *v = static_cast<const uint8_t *>(values);
     if (elem_bytes<VT>(D) <= 512) {
-        constexpr int SPLIT = PAIR_SPLIT;
+        constexpr int SPLIT = kPairSplit;
         const int64_t blocks = (B + WAVES / SPLIT - 1) / (WAVES / SPLIT);
         if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL((gather_pair_kernel<VT, SPLIT>), dim3((unsigned)blocks), dim3(64 * WAVES), 0, stream,
-                           static_cast<const uint8_t *>(values), scale, D, N, B, R, idx, w, out);
+        if (nt)
+            hipLaunchKernelGGL((gather_pair_kernel<VT, SPLIT, true>), dim3((unsigned)blocks), dim3(64 * WAVES), 0,
+                               stream, v, scale, D, N, B, R, idx, w, out);
+        else
+            hipLaunchKernelGGL((gather_pair_kernel<VT, SPLIT, false>), dim3((unsigned)blocks), dim3(64 * WAVES), 0,
+                               stream, v, scale, D, N, B, R, idx, w, out);
         return hipGetLastError();
     }
     const int width = 64 * Fmt<VT>::EPL;  // columns per wave
     const int slices = (D + width - 1) / width;
     const int64_t waves = B * slices;
     const int64_t blocks = (waves + WAVES - 1) / WAVES;
-    hipLaunchKernelGGL(gather_kernel<VT>, dim3((unsigned)blocks), dim3(64 * WAVES), 0, stream,
-                       static_cast<const uint8_t *>(values), scale, D, N, B, R, slices, idx, w, out);
+    if (nt)
+        hipLaunchKernelGGL((gather_kernel<VT, true>), dim3((unsigned)blocks), dim3(64 * WAVES), 0, stream, v, scale,
+                           D, N, B, R, slices, idx, w, out);
+    else
+        hipLaunchKernelGGL((gather_kernel<VT, false>), dim3((unsigned)blocks), dim3(64 * WAVES), 0, stream, v, scale,
+                           D, N, B, R, slices, idx, w, out);
     return hipGetLastError();
 }
 
