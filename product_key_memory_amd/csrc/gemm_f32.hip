@@ -246,24 +246,19 @@ __device__ __forceinline__ void mfma_frags(floatx16 (&acc)[T::TM][T::TN], const 
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i][pa[t]], bf[j][pb[t]], acc[i][j], 0, 0, 0);
 }
 
-template <typename T, bool BN_EPILOGUE, bool STREAM_OUT, bool PRODUCT_B = false, bool ACCUMULATE = false>
-__global__ __launch_bounds__(T::THREADS) void gemm_nt_f32_kernel(GemmArgs a)
+// One BM x BN tile (tm, tn) of batch entry g and K range z.
+template <typename T, bool BN_EPILOGUE, bool STREAM_OUT, bool PRODUCT_B, bool ACCUMULATE>
+__device__ __forceinline__ void gemm_tile(const GemmArgs &a, int tm, int tn, int g, int z, uint32_t *smem)
 {
     static_assert(!PRODUCT_B || (!STREAM_OUT && !BN_EPILOGUE && !ACCUMULATE), "product-key B: plain staged epilogue");
-    extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
     uint32_t *As = smem;
     uint32_t *Bs = smem + T::STAGES * T::BM * kRowDw;
-
-    const int tiles_n = (a.N + T::BN - 1) / T::BN;
-    const int tm = blockIdx.x / tiles_n;
-    const int tn = blockIdx.x - tm * tiles_n;
-    const int g = blockIdx.y;
     // split-K: this block's range of K (the operands are K-contiguous)
-    const int kbeg = a.k_chunk ? (int)blockIdx.z * a.k_chunk : 0;
+    const int kbeg = a.k_chunk ? z * a.k_chunk : 0;
     const int klen = a.k_chunk ? min(a.k_chunk, a.K - kbeg) : a.K;
     const float *A = a.A + (int64_t)g * a.strideA + kbeg;
     const float *Bmat = a.B + (int64_t)g * a.strideB + kbeg;
-    float *C = a.C + (int64_t)g * a.strideC + (int64_t)blockIdx.z * a.batch * a.strideC;
+    float *C = a.C + (int64_t)g * a.strideC + (int64_t)z * a.batch * a.strideC;
     const int32_t *a_exp = a.a_rowmax ? nullptr : a.a_exp + (int64_t)g * a.M;
     // exponent of A row m (its maxima given, or computed by the pre-pass)
     const auto row_exp = [&](int m) {
@@ -552,6 +547,30 @@ __global__ __launch_bounds__(T::THREADS) void gemm_nt_f32_kernel(GemmArgs a)
     }
 }
 
+// PERSIST: a grid of at most one workgroup per CU walks all tiles (batch
+// entry major), a barrier between tiles; otherwise one tile per workgroup,
+// grid (tiles, batch, K ranges).
+template <typename T, bool BN_EPILOGUE, bool STREAM_OUT, bool PRODUCT_B = false, bool ACCUMULATE = false,
+          bool PERSIST = false>
+__global__ __launch_bounds__(T::THREADS) void gemm_nt_f32_kernel(GemmArgs a)
+{
+    extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
+    const int tiles_n = (a.N + T::BN - 1) / T::BN;
+    if constexpr (PERSIST) {
+        const int tiles = ((a.M + T::BM - 1) / T::BM) * tiles_n;
+        const int64_t total = (int64_t)tiles * a.batch;
+        for (int64_t t = blockIdx.x; t < total; t += gridDim.x) {
+            const int g = (int)(t / tiles);
+            const int r = (int)(t - (int64_t)g * tiles);
+            gemm_tile<T, BN_EPILOGUE, STREAM_OUT, PRODUCT_B, ACCUMULATE>(a, r / tiles_n, r % tiles_n, g, 0, smem);
+            __syncthreads();
+        }
+    } else {
+        gemm_tile<T, BN_EPILOGUE, STREAM_OUT, PRODUCT_B, ACCUMULATE>(a, blockIdx.x / tiles_n, blockIdx.x % tiles_n,
+                                                                     blockIdx.y, blockIdx.z, smem);
+    }
+}
+
 // Row exponents: for each row of a K-long fp32 matrix, the power of two that
 // scales the row's largest magnitude into [2^14, 2^15); 0 for a row of
 // zeros (or a non-finite largest magnitude, which no scaling helps).  One
@@ -761,10 +780,11 @@ int64_t tile_count(const GemmArgs &a)
     return (int64_t)((a.M + T::BM - 1) / T::BM) * ((a.N + T::BN - 1) / T::BN);
 }
 
-template <typename T, bool BN_EPILOGUE, bool STREAM_OUT, bool PRODUCT_B = false, bool ACCUMULATE = false>
+template <typename T, bool BN_EPILOGUE, bool STREAM_OUT, bool PRODUCT_B = false, bool ACCUMULATE = false,
+          bool PERSIST = false>
 hipError_t launch_variant(const GemmArgs &a, hipStream_t stream)
 {
-    const auto kernel = &gemm_nt_f32_kernel<T, BN_EPILOGUE, STREAM_OUT, PRODUCT_B, ACCUMULATE>;
+    const auto kernel = &gemm_nt_f32_kernel<T, BN_EPILOGUE, STREAM_OUT, PRODUCT_B, ACCUMULATE, PERSIST>;
     if (T::LDS_BYTES > 65536) {
         // Dynamic LDS above 64 KiB must be allowed per kernel (gfx950 has
         // 160 KiB per CU); done once per kernel and device.
@@ -780,7 +800,11 @@ hipError_t launch_variant(const GemmArgs &a, hipStream_t stream)
             allowed_on.fetch_or(bit, std::memory_order_acq_rel);
         }
     }
-    const dim3 grid((unsigned)tile_count<T>(a), a.batch, a.k_chunk ? (a.K + a.k_chunk - 1) / a.k_chunk : 1);
+    dim3 grid((unsigned)tile_count<T>(a), a.batch, a.k_chunk ? (a.K + a.k_chunk - 1) / a.k_chunk : 1);
+    if constexpr (PERSIST) {
+        const int64_t total = tile_count<T>(a) * a.batch;
+        grid = dim3((unsigned)(total < kCUs ? total : kCUs), 1, 1);
+    }
     hipLaunchKernelGGL(kernel, grid, dim3(T::THREADS), T::LDS_BYTES, stream, a);
     return hipGetLastError();
 }
@@ -793,11 +817,18 @@ hipError_t launch_tile(const GemmArgs &a, hipStream_t stream)
         if (a.bn_mean || a.stream_out) return hipErrorInvalidValue;
         return launch_variant<T, false, false, false, true>(a, stream);
     }
+    // More 256x256 tiles than CUs: one workgroup per CU walks its tiles, so
+    // the stores of one tile drain while the next one computes
+    const bool persist = T::PING_PONG && !a.k_chunk && tile_count<T>(a) * a.batch > kCUs;
     if (a.bn_mean) {
         if (a.stream_out) return launch_variant<T, true, true>(a, stream);
+        if (persist) return launch_variant<T, true, false, false, false, true>(a, stream);
         return launch_variant<T, true, false>(a, stream);
     }
-    if (a.stream_out) return launch_variant<T, false, true>(a, stream);
+    if (a.stream_out) {
+        if (persist) return launch_variant<T, false, true, false, false, true>(a, stream);
+        return launch_variant<T, false, true>(a, stream);
+    }
     return launch_variant<T, false, false>(a, stream);
 }
 
