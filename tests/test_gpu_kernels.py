@@ -207,6 +207,39 @@ def test_query_and_score_parity(torch, name):
             assert (np.abs(scores[:, h, p] - ref) <= 1e-5 * m + 1e-7).all()
 
 
+def test_query_and_score_persistent_ragged(torch):
+    """More 256x256 tiles than CUs (4,389 tokens: 288 projection tiles and
+    576 scoring tiles over 256 workgroups, the last tile row ragged) take
+    the path where each workgroup walks several tiles.  Sampled tokens,
+    including every row of the ragged tile, against fp64 as above."""
+    wl = synthetic.Workload("persist", 4389, 1024, 4, 1024, 32, "f32", "random")
+    params = synthetic.make_params(wl, with_values=False, seed=3)
+    params["values"] = np.zeros((1, wl.D), np.float32)
+    params["scale"] = None
+    x = synthetic.make_x(wl, seed=3)
+    mem = pk.Memory(wl.D, wl.H, wl.n, wl.k, "f32", max_batch=wl.B)
+    dev = [_to(torch, params[key]) for key in ("wq", "mean", "var", "gamma", "beta", "subkeys")]
+    P = pk.Params(*dev, None)
+    say("persistent query/score", wl.B, "tokens")
+    qhat = mem.query(P, _to(torch, x)).cpu().numpy()
+    tokens = np.array(sorted(set(range(0, wl.B, 97)) | set(range(4352, wl.B)) | {255, 256, 4095, 4096}))
+    w64 = params["wq"].astype(np.float64)
+    xs = x[tokens].astype(np.float64)
+    inv = params["gamma"].astype(np.float64) / np.sqrt(params["var"].astype(np.float64) + 1e-5)
+    ref = (np.einsum("hfd,bd->bhf", w64, xs) - params["mean"]) * inv + params["beta"]
+    mass = np.einsum("hfd,bd->bhf", np.abs(w64), np.abs(xs)) * np.abs(inv)
+    assert (np.abs(qhat[tokens] - ref) <= 1e-5 * mass + 1e-7).all()
+    scores = mem.score(P, _to(torch, qhat)).cpu().numpy()[tokens].astype(np.float64)
+    half = wl.D // 2
+    sub = params["subkeys"].astype(np.float64)
+    for h in range(wl.H):
+        for p in range(2):
+            qp = qhat[tokens, h, p * half:(p + 1) * half].astype(np.float64)
+            r = qp @ sub[h, p].T
+            m = np.abs(qp) @ np.abs(sub[h, p]).T
+            assert (np.abs(scores[:, h, p] - r) <= 1e-5 * m + 1e-7).all()
+
+
 def test_query_and_score_wide_range(torch):
     """The contractions scale every operand row by a power of two before
     splitting it into fp16 pieces, so rows of any size keep fp32 accuracy:
