@@ -21,7 +21,7 @@ struct pkm_ctx {
     int32_t *idx;    // [max_batch, H, k]
     float *weights;  // [max_batch, H, k]
     uint32_t *stair; // staircase cells of the candidate grid for this k
-    float *stat_part; // batch-statistics partial sums [chunks, H * D]
+    float *stat_part; // batch statistics: chunk means and squared deviations [2, chunks, H * D]
     int32_t *gemm_exp; // row exponents of the GEMM operands
     int64_t gemm_exp_ints;
     uint32_t *qmax;    // largest |q^| per (token, half of a head) [max_batch, 2H], float bits
@@ -86,7 +86,7 @@ bool workspace_layout(const pkm_config &c, size_t sizes[kPieces])
     sizes[2] = round_up(m * H * (size_t)c.k * sizeof(int32_t));
     sizes[3] = round_up(m * H * (size_t)c.k * sizeof(float));
     sizes[4] = round_up(pkm::kMaxStaircaseCells * sizeof(uint32_t));
-    sizes[5] = round_up((size_t)pkm::stat_chunks(c.max_batch) * H * (size_t)c.dim * sizeof(float));
+    sizes[5] = round_up((size_t)pkm::stat_part_floats(c.max_batch, H * c.dim) * sizeof(float));
     sizes[6] = round_up((size_t)forward_exp_ints(c) * sizeof(int32_t));
     sizes[7] = round_up(m * 2 * H * sizeof(uint32_t));
     sizes[8] = round_up(2 * H * (size_t)c.n_keys * sizeof(int32_t));
@@ -850,14 +850,30 @@ pkm_status pkm_forward_batch_stats(pkm_ctx *ctx, const pkm_params *p, int64_t B,
     float *cw = weights ? weights : ctx->weights;
     pkm::GemmArgs qa = query_args(c, p, B, x, ctx->qhat, ctx->gemm_exp, ctx->gemm_exp_ints);
     qa.bn_mean = qa.bn_var = qa.bn_gamma = qa.bn_beta = nullptr;
+    // With half-heads of whole 256-column groups the normalisation records
+    // q^'s per-half maxima and the projection's pre-pass the subkeys' row
+    // exponents, so the scoring needs no pre-pass of its own (as in
+    // pkm_forward); otherwise the scoring computes its exponents.
+    uint32_t *qmax = (c.dim / 2) % 256 == 0 ? ctx->qmax : nullptr;
+    if (qmax) {
+        qa.zero_ptr = qmax;
+        qa.zero_n = B * 2 * c.heads;
+        qa.extra_exp.base = p->subkeys;
+        qa.extra_exp.rows_per_batch = c.n_keys;
+        qa.extra_exp.batch = 2 * c.heads;
+        qa.extra_exp.stride = (int64_t)c.n_keys * (c.dim / 2);
+        qa.extra_exp.ld = c.dim / 2;
+        qa.extra_exp.K = c.dim / 2;
+        qa.extra_exp.out = ctx->sub_exp;
+    }
     if ((s = launched(pkm::launch_gemm_nt_f32(qa, st), "query projection")) ||
         (s = launched(pkm::launch_batch_stats(ctx->qhat, B, HD, ctx->stat_part, batch_mean, batch_var, running_mean,
                                               running_var, momentum, st),
                       "batch statistics")) ||
         (s = launched(pkm::launch_bn_apply(ctx->qhat, B, HD, batch_mean, batch_var, p->bn_gamma, p->bn_beta, c.bn_eps,
-                                           st),
+                                           qmax, c.dim / 2, st),
                       "batch normalisation")) ||
-        (s = run_score(ctx, p, B, ctx->qhat, ctx->scores, nullptr, st)) ||
+        (s = run_score(ctx, p, B, ctx->qhat, ctx->scores, qmax, st)) ||
         (s = launched(pkm::launch_select(ctx->scores, B, c.heads, c.n_keys, c.k, ctx->stair, ci, cw, st), "select")) ||
         (s = launched(pkm::launch_gather(p->values, p->value_scale, c.value_type, c.dim, c.n_keys * c.n_keys, B,
                                          c.heads * c.k, ci, cw, out, st),

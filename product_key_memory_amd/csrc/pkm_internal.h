@@ -166,13 +166,18 @@ hipError_t launch_dsub(const float *G, int64_t ldG, int64_t B, const float *q, i
                        hipStream_t st);
 // ---- batch statistics (batch_norm.hip)
 // mean, var [cols] of q [B][cols] (biased var; B >= 2); part holds
-// stat_chunks(B) * cols floats; running stats updated when non-NULL.
+// stat_part_floats(B, cols) floats; running stats updated when non-NULL.
 int stat_chunks(int64_t B);
+int64_t stat_part_floats(int64_t B, int cols);
 hipError_t launch_batch_stats(const float *q, int64_t B, int cols, float *part, float *mean, float *var,
                               float *running_mean, float *running_var, float momentum, hipStream_t st);
-// q = BN(q) in place with the given statistics (cols % 4 == 0)
+// q = BN(q) in place with the given statistics (cols % 4 == 0).  With
+// row_max non-NULL (cols and seg_cols multiples of 256): also each row's
+// largest |q| per segment of seg_cols columns, by atomic max of the float
+// bits into row_max[row * (cols / seg_cols) + col / seg_cols], which must
+// start at zero.
 hipError_t launch_bn_apply(float *q, int64_t B, int cols, const float *mean, const float *var, const float *gamma,
-                           const float *beta, float eps, hipStream_t st);
+                           const float *beta, float eps, uint32_t *row_max, int seg_cols, hipStream_t st);
 // BN backward with batch statistics: dq from dq^, q and the column sums
 // sum_g = sum dq^ xhat, sum_b = sum dq^ of the batch
 hipError_t launch_bn_batch_dq(const float *dqh, const float *q, int64_t B, int cols, const float *mean,

@@ -83,7 +83,7 @@ def test_workspace_bytes():
     cfg = pk.make_config(**GOOD)
     mb, H, D, n, k = 16384, 4, 1024, 1024, 32
     stair = 320 * 4  # staircase cells of the candidate grid
-    stat_part = (mb // 64) * H * D * 4  # batch-statistics partial sums
+    stat_part = 2 * (mb // 64) * H * D * 4  # batch statistics: each 64-row chunk's mean and squared deviations
     exps = max(mb + H * D, 2 * H * (mb + n)) * 4  # GEMM row exponents (query or scoring)
     qmax = mb * 2 * H * 4  # largest |q^| per (token, half of a head)
     sub_exp = 2 * H * n * 4  # the subkeys' row exponents
