@@ -399,14 +399,25 @@ __global__ __launch_bounds__(256) void colsum_partial_kernel(const float *__rest
 {
     const int col = blockIdx.x * 256 + threadIdx.x;
     if (col >= cols) return;
-    const int64_t t0 = (int64_t)blockIdx.y * kColChunk, t1 = min(B, t0 + kColChunk);
+    const int64_t t0 = (int64_t)blockIdx.y * kColChunk;
+    const int n = (int)min((int64_t)kColChunk, B - t0);
     const float mu = mean[col], inv = 1.0f / sqrtf(var[col] + eps);
-    float sg = 0.0f, sb = 0.0f;
-    for (int64_t t = t0; t < t1; ++t) {
-        const float g = dqhat[t * cols + col];
-        sg = fmaf(g, (q[t * cols + col] - mu) * inv, sg);
-        sb += g;
+    // the chunk's rows loaded together (rows past B repeat the last one and
+    // are not added), then summed in row order
+    float g[kColChunk], x[kColChunk];
+#pragma unroll
+    for (int i = 0; i < kColChunk; ++i) {
+        const int64_t t = t0 + min(i, n - 1);
+        g[i] = dqhat[t * cols + col];
+        x[i] = q[t * cols + col];
     }
+    float sg = 0.0f, sb = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kColChunk; ++i)
+        if (i < n) {
+            sg = fmaf(g[i], (x[i] - mu) * inv, sg);
+            sb += g[i];
+        }
     part_g[(int64_t)blockIdx.y * cols + col] = sg;
     part_b[(int64_t)blockIdx.y * cols + col] = sb;
 }
@@ -421,6 +432,7 @@ __global__ __launch_bounds__(256) void colsum_final_kernel(const float *__restri
     const int col = blockIdx.x * 256 + threadIdx.x;
     if (col >= cols) return;
     float sg = 0.0f, sb = 0.0f;
+#pragma unroll 8
     for (int c = 0; c < chunks; ++c) {
         sg += part_g[(int64_t)c * cols + col];
         sb += part_b[(int64_t)c * cols + col];
