@@ -97,6 +97,33 @@ def test_backward_against_oracle(torch, wl, gamma_beta):
     print(wl.name, {k: f"{v:.2g}" for k, v in errs.items()}, flush=True)
 
 
+def _random_backward_configs(count, seed):
+    """Seeded random small configurations (D a multiple of 64, every table
+    format, chunked and unchunked), with random BN affine parameters."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        D = int(rng.choice([64, 128, 192, 256]))
+        n = int(rng.integers(2, 80))
+        k = int(rng.integers(1, min(32, n) + 1))
+        H = int(rng.integers(1, 4))
+        B = int(rng.integers(2, 300))
+        table = str(rng.choice(["f32", "bf16", "e4m3", "int8", "int4"]))
+        max_batch = int(rng.choice([B, max(1, B // 2), 64]))
+        out.append(dict(B=B, D=D, H=H, n=n, k=k, table=table, max_batch=max_batch, seed=int(200 + i)))
+    return out
+
+
+@pytest.mark.parametrize("cfg", _random_backward_configs(8, 7),
+                         ids=lambda c: "B{B}-D{D}-H{H}-n{n}-k{k}-{table}-mb{max_batch}".format(**c))
+def test_backward_random_configs(torch, cfg):
+    wl = synthetic.Workload("rb", cfg["B"], cfg["D"], cfg["H"], cfg["n"], cfg["k"], cfg["table"], "random")
+    params, x, dout = case(wl, cfg["seed"], gamma_beta=True)
+    got, _ = gpu_backward(torch, wl, params, x, dout, max_batch=cfg["max_batch"])
+    ref = oracle.backward(support.model_for(wl, params), x, dout)
+    compare(got, ref)
+
+
 def test_backward_chunks_accumulate_and_repeat_bitwise(torch):
     """max_batch smaller than B: the chunks add into the parameter gradients;
     a second call adds the same again (to rounding: each chunk's sum is

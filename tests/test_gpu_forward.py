@@ -101,6 +101,37 @@ def test_forward_edge_shapes(torch, shape):
     compare(wl, params, x, out, idx, w)
 
 
+def _random_configs(count, seed):
+    """Seeded random small configurations over the supported ranges (D a
+    multiple of 64, 1 <= k <= min(64, n_keys), every table format, chunked
+    and unchunked)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        D = int(rng.choice([64, 128, 192, 256, 320, 512]))
+        n = int(rng.integers(2, 260))
+        k = int(rng.integers(1, min(64, n) + 1))
+        H = int(rng.integers(1, 5))
+        B = int(rng.integers(1, 700))
+        table = str(rng.choice(["f32", "bf16", "e4m3", "int8", "int4"]))
+        max_batch = int(rng.choice([B, max(1, B // 3), 64]))
+        out.append(dict(B=B, D=D, H=H, n=n, k=k, table=table, max_batch=max_batch, seed=int(100 + i)))
+    return out
+
+
+@pytest.mark.parametrize("cfg", _random_configs(12, 2026), ids=lambda c: "B{B}-D{D}-H{H}-n{n}-k{k}-{table}-mb{max_batch}".format(**c))
+def test_forward_random_configs(torch, cfg):
+    """The whole lookup on seeded random configurations against the oracle
+    (every token), with the invariants."""
+    wl = synthetic.Workload("rand", cfg["B"], cfg["D"], cfg["H"], cfg["n"], cfg["k"], cfg["table"], "random")
+    params = synthetic.make_params(wl, seed=cfg["seed"])
+    x = synthetic.make_x(wl, seed=cfg["seed"])
+    support.gap_clean(wl, params, x, seed=cfg["seed"])
+    out, idx, w = support.gpu_forward(wl, params, x, max_batch=cfg["max_batch"])
+    invariants(wl, idx, w)
+    compare(wl, params, x, out, idx, w)
+
+
 def test_forward_random_gamma_beta(torch):
     wl = synthetic.Workload("gb", 200, 256, 2, 128, 16, "f32", "random")
     params = synthetic.make_params(wl, seed=9)
