@@ -197,13 +197,23 @@ def flat_vs_product(torch, pk, wl, P, xt, kt, tokens=64, steps=5, warmup=2):
 
 def backward_step(torch, mem, wl, P, xt, idx, wts, fwd_ms, steps, warmup):
     """The gradients of a loss through the same batch (pkm_backward): every
-    parameter gradient, dx and the dense fp32 value-table gradient."""
+    parameter gradient, dx and the dense fp32 value-table gradient (and
+    again with the value gradient's sparse form)."""
     dout = torch.randn((wl.B, wl.D), dtype=torch.float32, device="cuda", generator=torch.Generator("cuda").manual_seed(1))
     grads = {"dx": (wl.B, wl.D), "dwq": (wl.H, wl.D, wl.D), "dbn_gamma": (wl.H, wl.D), "dbn_beta": (wl.H, wl.D),
              "dsubkeys": (wl.H, 2, wl.n, wl.D // 2), "dvalues": (wl.N, wl.D)}
     grads = {name: torch.zeros(shape, dtype=torch.float32, device="cuda") for name, shape in grads.items()}
     ws = torch.empty(mem.backward_workspace_bytes(), dtype=torch.uint8, device="cuda")
     ms = timed_steps(torch, lambda: mem.backward(P, xt, idx, wts, dout, grads, ws), steps, warmup)
+    # the same step with the value gradient in its sparse form (touched rows only, written once)
+    cap = min(wl.N, wl.B * wl.H * wl.k)
+    sparse = {name: t for name, t in grads.items() if name != "dvalues"}
+    sparse.update({"dvalues_rows": torch.empty(cap, dtype=torch.int32, device="cuda"),
+                   "dvalues_sparse": torch.empty((cap, wl.D), dtype=torch.float32, device="cuda"),
+                   "dvalues_count": torch.empty(1, dtype=torch.int64, device="cuda")})
+    sparse_ms = timed_steps(torch, lambda: mem.backward(P, xt, idx, wts, dout, sparse, ws), steps, warmup)
+    touched = int(sparse["dvalues_count"].item())
+    del sparse
     # the same step with training-mode BN (statistics of this batch, running statistics updated)
     out = torch.empty((wl.B, wl.D), dtype=torch.float32, device="cuda")
     running = (torch.zeros((wl.H, wl.D), device="cuda"), torch.ones((wl.H, wl.D), device="cuda"))
@@ -220,6 +230,7 @@ def backward_step(torch, mem, wl, P, xt, idx, wts, fwd_ms, steps, warmup):
     flop = 2.0 * wl.B * wl.H * wl.D * wl.D * 3
     return {"ms": round(ms, 4), "tokens_per_s": round(wl.B / (ms * 1e-3), 1),
             "forward_backward_tokens_per_s": round(wl.B / ((ms + fwd_ms) * 1e-3), 1),
+            "sparse_value_grad_ms": round(sparse_ms, 4), "rows_touched": touched,
             "batch_stats_forward_ms": round(fwd_bs_ms, 4), "batch_stats_backward_ms": round(bwd_bs_ms, 4),
             "batch_stats_forward_backward_tokens_per_s": round(wl.B / ((fwd_bs_ms + bwd_bs_ms) * 1e-3), 1),
             "gemm_flop": flop, "gemm_tflops_if_all_time": round(flop / (ms * 1e-3) / 1e12, 2),

@@ -192,7 +192,22 @@ pkm_status pkm_flat_search(pkm_ctx *ctx, const pkm_params *p, int64_t B, const f
 /* Gradients written by pkm_backward.  Parameter gradients are ADDED to what
  * the buffers hold (zero them for one batch's gradient); dx is overwritten.
  * Any member may be NULL to skip that gradient (dbn_gamma and dbn_beta go
- * together).  All are fp32 device buffers, 16-byte aligned. */
+ * together).  The float buffers are fp32 device memory, 16-byte aligned.
+ *
+ * The value gradient comes in one of two forms.  dvalues is the dense one.
+ * The sparse one (the last three members, all set or all NULL, dvalues then
+ * NULL) holds only the rows some winner selected: a batch touches at most
+ * B*H*k of the n_keys^2 rows, and those rows are the only ones that move
+ * ("Product-Key Memory", §Keeping the memory in use: unselected slots get
+ * no gradient).  With U the number of distinct rows in idx:
+ *   dvalues_rows    [U] int32, the rows in increasing order;
+ *   dvalues_sparse  [U, D]: row u holds the gradient of row dvalues_rows[u]
+ *                   (overwritten, not added to);
+ *   dvalues_count   one int64 in device memory, set to U (0 for B = 0;
+ *                   the other two may then be NULL).
+ * The caller sizes the first two for min(n_keys^2, B*H*k) rows; entries
+ * beyond U are left as they were.  The sparse form needs B <= max_batch.
+ * Scattered into zeros it equals the dense form bit for bit. */
 typedef struct {
     float *dx;        /* [B, D] */
     float *dwq;       /* [H, D, D] */
@@ -201,6 +216,9 @@ typedef struct {
     float *dsubkeys;  /* [H, 2, n_keys, D/2] */
     float *dvalues;   /* [n_keys^2, D]: w.r.t. the dequantised value rows
                          (scale[row] * stored value for E4M3 tables) */
+    int32_t *dvalues_rows;  /* sparse form, see above */
+    float *dvalues_sparse;
+    int64_t *dvalues_count;
 } pkm_grads;
 
 /* Bytes of caller-owned device workspace pkm_backward needs for cfg (it
@@ -229,7 +247,9 @@ pkm_status pkm_backward(pkm_ctx *ctx, const pkm_params *p, int64_t B, const floa
  * statistics of this batch ("Product-Key Memory", §Keeping the memory in
  * use: batch normalisation of the queries), the one step that couples the
  * tokens.  Per head h and feature f over the B tokens: mean and biased
- * variance of q = Wq[h] . x_b (two passes, fixed order), then
+ * variance of q = Wq[h] . x_b (one pass: per chunk of 64 tokens the mean
+ * and the sum of squared deviations, the chunks merged pairwise in a fixed
+ * order), then
  * q^ = (q - mean) / sqrt(var + eps) * gamma + beta; steps a3-a7 as in
  * pkm_forward.  2 <= B <= max_batch (one pass over the whole batch).
  *   batch_mean, batch_var  [H, D] fp32, written (biased variance)

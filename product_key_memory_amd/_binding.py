@@ -152,11 +152,13 @@ def _expect(t, name, shape, dtype, device=None):
         raise ValueError(f"{name} must be 16-byte aligned")
 
 
+GRAD_NAMES = ("dx", "dwq", "dbn_gamma", "dbn_beta", "dsubkeys", "dvalues", "dvalues_rows", "dvalues_sparse",
+              "dvalues_count")
+SPARSE_VALUE_GRADS = ("dvalues_rows", "dvalues_sparse", "dvalues_count")
+
+
 class GradsStruct(ctypes.Structure):
-    _fields_ = [(name, ctypes.c_void_p) for name in ("dx", "dwq", "dbn_gamma", "dbn_beta", "dsubkeys", "dvalues")]
-
-
-GRAD_NAMES = ("dx", "dwq", "dbn_gamma", "dbn_beta", "dsubkeys", "dvalues")
+    _fields_ = [(name, ctypes.c_void_p) for name in GRAD_NAMES]
 
 
 class Params:
@@ -346,14 +348,19 @@ class Memory:
                                                 float(momentum), _stream_handle(stream)))
         return out, idx, weights, mean, var
 
-    def backward(self, params, x, idx, weights, dout, grads=None, workspace=None, stream=None, batch_stats=None):
+    def backward(self, params, x, idx, weights, dout, grads=None, workspace=None, stream=None, batch_stats=None,
+                 sparse_values=False):
         """Gradients of a loss given dout = dL/dout [B, D] for the winners
-        (idx, weights) a forward call returned.  grads: dict name -> fp32
-        tensor (parameter gradients are added to, dx is overwritten; a
-        missing name is skipped), or None for freshly zeroed buffers of every
-        gradient.  batch_stats: (mean, var) from forward_batch_stats for the
-        training-mode BN backward, or None (running statistics).  Returns
-        the dict."""
+        (idx, weights) a forward call returned.  grads: dict name -> tensor
+        (parameter gradients are added to, dx is overwritten; a missing name
+        is skipped), or None for freshly zeroed buffers of every gradient.
+        sparse_values: with grads None, the value gradient in its sparse
+        form instead of dvalues -- dvalues_rows [cap] int32, dvalues_sparse
+        [cap, D] f32 and dvalues_count [1] int64 with cap = min(n^2, B*H*k);
+        the first dvalues_count entries hold the touched rows in increasing
+        order and their gradients.  batch_stats: (mean, var) from
+        forward_batch_stats for the training-mode BN backward, or None
+        (running statistics).  Returns the dict."""
         torch = _torch()
         B = x.shape[0]
         D, H, n, k = self.dim, self.heads, self.n_keys, self.k
@@ -363,14 +370,19 @@ class Memory:
         _expect(dout, "dout", (B, D), "float32", dev)
         _expect(idx, "idx", (B, H, k), "int32", dev)
         _expect(weights, "weights", (B, H, k), "float32", dev)
+        cap = min(n * n, B * H * k)
         shapes = {"dx": (B, D), "dwq": (H, D, D), "dbn_gamma": (H, D), "dbn_beta": (H, D),
-                  "dsubkeys": (H, 2, n, D // 2), "dvalues": (n * n, D)}
+                  "dsubkeys": (H, 2, n, D // 2), "dvalues": (n * n, D), "dvalues_rows": (cap,),
+                  "dvalues_sparse": (cap, D), "dvalues_count": (1,)}
+        dtypes = {"dvalues_rows": "int32", "dvalues_count": "int64"}
         if grads is None:
-            grads = {name: torch.zeros(shape, dtype=torch.float32, device=dev) for name, shape in shapes.items()}
+            skip = ("dvalues",) if sparse_values else SPARSE_VALUE_GRADS
+            grads = {name: torch.zeros(shape, dtype=getattr(torch, dtypes.get(name, "float32")), device=dev)
+                     for name, shape in shapes.items() if name not in skip}
         for name, t in grads.items():
             if name not in shapes:
                 raise ValueError(f"unknown gradient {name}")
-            _expect(t, name, shapes[name], "float32", dev)
+            _expect(t, name, shapes[name], dtypes.get(name, "float32"), dev)
         need = self.backward_workspace_bytes()
         if workspace is None:
             workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)

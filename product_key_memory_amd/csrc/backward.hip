@@ -477,6 +477,9 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *l
     return excl;
 }
 
+// FLAGS: scan (count > 0) instead of count (the positions of the touched
+// rows among themselves)
+template <bool FLAGS>
 __global__ __launch_bounds__(256) void scan_sums_kernel(const uint32_t *__restrict__ count, int N,
                                                         uint32_t *__restrict__ block_sum)
 {
@@ -484,14 +487,19 @@ __global__ __launch_bounds__(256) void scan_sums_kernel(const uint32_t *__restri
     const int64_t base = (int64_t)blockIdx.x * kScanBlock + threadIdx.x * 16;
     uint32_t s = 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) s += base + i < N ? count[base + i] : 0u;
+    for (int i = 0; i < 16; ++i) {
+        const uint32_t c = base + i < N ? count[base + i] : 0u;
+        s += FLAGS ? (c != 0u) : c;
+    }
     uint32_t total;
     block_exclusive_scan(s, lds, total);
     if (threadIdx.x == 0) block_sum[blockIdx.x] = total;
 }
 
-// One workgroup: exclusive scan of the block sums in place (nb <= 256 * 64).
-__global__ __launch_bounds__(256) void scan_top_kernel(uint32_t *__restrict__ block_sum, int nb)
+// One workgroup: exclusive scan of the block sums in place (nb <= 256 * 64);
+// the grand total to *total when given.
+__global__ __launch_bounds__(256) void scan_top_kernel(uint32_t *__restrict__ block_sum, int nb,
+                                                       int64_t *__restrict__ total_out)
 {
     __shared__ uint32_t lds[256];
     uint32_t carry = 0;
@@ -503,8 +511,10 @@ __global__ __launch_bounds__(256) void scan_top_kernel(uint32_t *__restrict__ bl
         if (i < nb) block_sum[i] = carry + excl;
         carry += total;
     }
+    if (total_out && threadIdx.x == 0) *total_out = (int64_t)carry;
 }
 
+template <bool FLAGS>
 __global__ __launch_bounds__(256) void scan_apply_kernel(const uint32_t *__restrict__ count, int N,
                                                          const uint32_t *__restrict__ block_off,
                                                          uint32_t *__restrict__ offs)
@@ -514,7 +524,8 @@ __global__ __launch_bounds__(256) void scan_apply_kernel(const uint32_t *__restr
     uint32_t v[16], s = 0;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        v[i] = base + i < N ? count[base + i] : 0u;
+        const uint32_t c = base + i < N ? count[base + i] : 0u;
+        v[i] = FLAGS ? (c != 0u) : c;
         s += v[i];
     }
     uint32_t total;
@@ -537,19 +548,24 @@ __global__ __launch_bounds__(256) void fill_lists_kernel(const int32_t *__restri
 }
 
 // dV[r] += sum over the occurrences o of r, in increasing o (token, head,
-// winner), of w[o] * dout[token(o)].  One wave per kGradRows (8) rows; the wave
+// winner), of w[o] * dout[token(o)].  SPARSE: the sum alone goes to row
+// pos[r] of a compact [U][D] array and r to rows[pos[r]] (no old row read).
+// One wave per kGradRows (8) rows; the wave
 // takes its non-empty rows in turn.  Up to 64 occurrences are put in order
 // by a 64-lane bitonic sort (lane t holds the t-th) and summed over passes
 // of 1024 columns (lane l: columns 4 l + 256 q, q < 4; the old row and two
 // occurrences' dout rows in flight), then added to the row; more are
 // walked by repeated minimum search, each added into the row in turn.
 constexpr int kGradRows = 8;
+template <bool SPARSE>
 __global__ __launch_bounds__(64 * WAVES) void value_grad_kernel(const uint32_t *__restrict__ count,
                                                                const uint32_t *__restrict__ offs,
                                                                const uint32_t *__restrict__ list, int N, int D,
                                                                int per_token, const float *__restrict__ w,
                                                                const float *__restrict__ dout,
-                                                               float *__restrict__ dval)
+                                                               float *__restrict__ dval,
+                                                               const uint32_t *__restrict__ pos,
+                                                               int32_t *__restrict__ rows)
 {
     const int lane = threadIdx.x & 63;
     const int64_t group = (int64_t)blockIdx.x * WAVES + (threadIdx.x >> 6);
@@ -565,7 +581,8 @@ __global__ __launch_bounds__(64 * WAVES) void value_grad_kernel(const uint32_t *
         const int64_t r = group * kGradRows + src;
         const uint32_t m = (uint32_t)__builtin_amdgcn_readlane((int)my_count, src);
         const uint32_t start = (uint32_t)__builtin_amdgcn_readlane((int)my_start, src);
-        float *out = dval + r * D;
+        float *out = dval + (SPARSE ? (int64_t)pos[r] : r) * D;
+        if (SPARSE && lane == 0) rows[pos[r]] = (int32_t)r;
         if (m <= 64) {
             const uint32_t id = lane < (int)m ? list[start + lane] : 0xFFFFFFFFu;
             const uint32_t asc = m == 1 ? id : ~sort64_desc(~id);  // lane t: the t-th smallest id
@@ -580,7 +597,7 @@ __global__ __launch_bounds__(64 * WAVES) void value_grad_kernel(const uint32_t *
                     const int c = c1 + 256 * q + 4 * lane;
                     act[q] = c < D;
                     col[q] = act[q] ? c : 0;
-                    old[q] = act[q] ? load_once(out + col[q]) : make_float4(0, 0, 0, 0);
+                    old[q] = act[q] && !SPARSE ? load_once(out + col[q]) : make_float4(0, 0, 0, 0);
                     acc[q] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
                 }
                 for (uint32_t t0 = 0; t0 < m; t0 += 2) {
@@ -619,6 +636,8 @@ __global__ __launch_bounds__(64 * WAVES) void value_grad_kernel(const uint32_t *
         } else {
             // more than 64: walk the occurrences in increasing id (one wave
             // minimum per step), adding each into the row
+            if (SPARSE)
+                for (int d = lane; d < D; d += 64) out[d] = 0.0f;
             int64_t last = -1;
             for (uint32_t t = 0; t < m; ++t) {
                 uint32_t best = 0xFFFFFFFFu;
@@ -739,7 +758,8 @@ hipError_t launch_usage(const int32_t *idx, int64_t M, int N, uint32_t *counts, 
 
 hipError_t launch_value_grad(const int32_t *idx, int64_t M, int N, int D, int per_token, const float *w,
                              const float *dout, uint32_t *count, uint32_t *cursor, uint32_t *offs,
-                             uint32_t *block_sum, uint32_t *list, float *dval, hipStream_t st)
+                             uint32_t *block_sum, uint32_t *list, float *dval, int32_t *rows, int64_t *row_count,
+                             hipStream_t st)
 {
     if (M <= 0) return hipSuccess;
     const int64_t nb = scan_blocks(N);
@@ -748,12 +768,24 @@ hipError_t launch_value_grad(const int32_t *idx, int64_t M, int N, int D, int pe
     if ((e = launch_fill(count, N, 0u, st)) != hipSuccess || (e = launch_fill(cursor, N, 0u, st)) != hipSuccess)
         return e;
     hipLaunchKernelGGL(count_rows_kernel, dim3(grid_of(M, 256)), dim3(256), 0, st, idx, M, N, count);
-    hipLaunchKernelGGL(scan_sums_kernel, dim3((unsigned)nb), dim3(256), 0, st, count, N, block_sum);
-    hipLaunchKernelGGL(scan_top_kernel, dim3(1), dim3(256), 0, st, block_sum, (int)nb);
-    hipLaunchKernelGGL(scan_apply_kernel, dim3((unsigned)nb), dim3(256), 0, st, count, N, block_sum, offs);
+    hipLaunchKernelGGL(scan_sums_kernel<false>, dim3((unsigned)nb), dim3(256), 0, st, count, N, block_sum);
+    hipLaunchKernelGGL(scan_top_kernel, dim3(1), dim3(256), 0, st, block_sum, (int)nb, nullptr);
+    hipLaunchKernelGGL(scan_apply_kernel<false>, dim3((unsigned)nb), dim3(256), 0, st, count, N, block_sum, offs);
     hipLaunchKernelGGL(fill_lists_kernel, dim3(grid_of(M, 256)), dim3(256), 0, st, idx, M, N, offs, cursor, list);
-    hipLaunchKernelGGL(value_grad_kernel, dim3(grid_of((N + kGradRows - 1) / kGradRows, WAVES)), dim3(64 * WAVES), 0,
-                       st, count, offs, list, N, D, per_token, w, dout, dval);
+    const dim3 grid(grid_of((N + kGradRows - 1) / kGradRows, WAVES)), block(64 * WAVES);
+    if (rows) {
+        // the touched rows' positions among themselves, into cursor (free
+        // once the lists are filled), and their number
+        hipLaunchKernelGGL(scan_sums_kernel<true>, dim3((unsigned)nb), dim3(256), 0, st, count, N, block_sum);
+        hipLaunchKernelGGL(scan_top_kernel, dim3(1), dim3(256), 0, st, block_sum, (int)nb, row_count);
+        hipLaunchKernelGGL(scan_apply_kernel<true>, dim3((unsigned)nb), dim3(256), 0, st, count, N, block_sum,
+                           cursor);
+        hipLaunchKernelGGL(value_grad_kernel<true>, grid, block, 0, st, count, offs, list, N, D, per_token, w, dout,
+                           dval, cursor, rows);
+    } else {
+        hipLaunchKernelGGL(value_grad_kernel<false>, grid, block, 0, st, count, offs, list, N, D, per_token, w, dout,
+                           dval, nullptr, nullptr);
+    }
     return hipGetLastError();
 }
 

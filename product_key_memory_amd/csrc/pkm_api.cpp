@@ -371,11 +371,17 @@ bool backward_layout(const pkm_config &c, size_t sizes[kBwdPieces])
 pkm_status check_grads(const pkm_grads *g)
 {
     if (!g) return fail(PKM_E_ARG, "grads is NULL");
-    const void *ptrs[] = {g->dx, g->dwq, g->dbn_gamma, g->dbn_beta, g->dsubkeys, g->dvalues};
+    const void *ptrs[] = {g->dx, g->dwq, g->dbn_gamma, g->dbn_beta, g->dsubkeys, g->dvalues, g->dvalues_sparse};
     for (const void *q : ptrs)
         if (q && !aligned16(q)) return fail(PKM_E_ARG, "gradient buffers must be 16-byte aligned");
     if ((g->dbn_gamma == nullptr) != (g->dbn_beta == nullptr))
         return fail(PKM_E_ARG, "dbn_gamma and dbn_beta go together");
+    const int sparse = (g->dvalues_rows != nullptr) + (g->dvalues_sparse != nullptr) + (g->dvalues_count != nullptr);
+    if (sparse != 0 && sparse != 3)
+        return fail(PKM_E_ARG, "dvalues_rows, dvalues_sparse and dvalues_count go together");
+    if (sparse && g->dvalues) return fail(PKM_E_ARG, "dvalues and the sparse value gradient exclude each other");
+    if (sparse && ((uintptr_t)g->dvalues_rows % 4 || (uintptr_t)g->dvalues_count % 8))
+        return fail(PKM_E_ARG, "dvalues_rows and dvalues_count must be aligned to their element size");
     return PKM_OK;
 }
 
@@ -654,6 +660,8 @@ pkm_status run_backward(pkm_ctx *ctx, const pkm_params *p, int64_t B, const floa
     const int64_t exp_ints = (int64_t)(sizes[17] / sizeof(int32_t));
 
     const int H = c.heads, D = c.dim, k = c.k, n = c.n_keys, HD = H * D, N = n * n;
+    // the dense value gradient or the sparse one (one chunk, checked)
+    float *dval = grads->dvalues_sparse ? grads->dvalues_sparse : grads->dvalues;
     if (grads->dx &&
         (s = launched(pkm::launch_transpose(p->wq, D, HD, D, wqT, HD, HD, nullptr, nullptr, nullptr, nullptr, 0.0f, st),
                       "Wq transpose")))
@@ -666,9 +674,10 @@ pkm_status run_backward(pkm_ctx *ctx, const pkm_params *p, int64_t B, const floa
         // everything but the value gradient flows through the scores
         const bool through_scores = grads->dx || grads->dwq || grads->dbn_gamma || grads->dsubkeys;
         if (!through_scores) {
-            if (grads->dvalues &&
+            if (dval &&
                 (s = launched(pkm::launch_value_grad(ic, nb * H * k, N, D, H * k, wc, doutc, count, cursor, offs,
-                                                     block_sum, list, grads->dvalues, st),
+                                                     block_sum, list, dval, grads->dvalues_rows,
+                                                     grads->dvalues_count, st),
                               "value gradient")))
                 return s;
             continue;
@@ -750,10 +759,10 @@ pkm_status run_backward(pkm_ctx *ctx, const pkm_params *p, int64_t B, const floa
             a.exp_ws_ints = exp_ints;
             if ((s = launched(pkm::launch_gemm_nt_f32(a, st), "dx"))) return s;
         }
-        if (grads->dvalues &&
-            (s = launched(pkm::launch_value_grad(ic, nb * H * k, N, D, H * k, wc, doutc, count, cursor, offs,
-                                                 block_sum, list, grads->dvalues, st),
-                          "value gradient")))
+        if (dval && (s = launched(pkm::launch_value_grad(ic, nb * H * k, N, D, H * k, wc, doutc, count, cursor, offs,
+                                                         block_sum, list, dval, grads->dvalues_rows,
+                                                         grads->dvalues_count, st),
+                                  "value gradient")))
             return s;
     }
     return ok();
@@ -786,7 +795,20 @@ pkm_status check_backward_args(pkm_ctx *ctx, const pkm_params *p, int64_t B, con
         return s;
     if (workspace_bytes < need_bytes)
         return fail(PKM_E_ARG, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, need_bytes);
+    if (grads->dvalues_sparse && B > c.max_batch)
+        return fail(PKM_E_ARG, "the sparse value gradient needs B <= max_batch (got B = %lld)", (long long)B);
     return PKM_OK;
+}
+
+// B = 0: the sparse value gradient's row count is still written (zero);
+// its row buffers have no entries then and may be NULL.
+pkm_status empty_backward(const pkm_grads *grads, void *stream)
+{
+    if (!grads || !grads->dvalues_count) return ok();
+    if ((uintptr_t)grads->dvalues_count % 8) return fail(PKM_E_ARG, "dvalues_count must be 8-byte aligned");
+    return launched(pkm::launch_fill(reinterpret_cast<uint32_t *>(grads->dvalues_count), 2, 0u,
+                                     static_cast<hipStream_t>(stream)),
+                    "clear");
 }
 
 }  // namespace
@@ -799,7 +821,7 @@ pkm_status pkm_backward(pkm_ctx *ctx, const pkm_params *p, int64_t B, const floa
 {
     if (pkm_status s = check_backward_args(ctx, p, B, x, idx, weights, dout, grads, workspace, workspace_bytes, false))
         return s;
-    if (B == 0) return ok();
+    if (B == 0) return empty_backward(grads, stream);
     return run_backward(ctx, p, B, x, idx, weights, dout, p->bn_mean, p->bn_var, false, grads, workspace,
                         workspace_bytes, stream);
 }
@@ -811,7 +833,7 @@ pkm_status pkm_backward_batch_stats(pkm_ctx *ctx, const pkm_params *p, int64_t B
 {
     if (pkm_status s = check_backward_args(ctx, p, B, x, idx, weights, dout, grads, workspace, workspace_bytes, true))
         return s;
-    if (B == 0) return ok();
+    if (B == 0) return empty_backward(grads, stream);
     if (B < 2 || B > ctx->cfg.max_batch)
         return fail(PKM_E_ARG, "batch statistics need 2 <= B <= max_batch (got B = %lld)", (long long)B);
     pkm_status s;

@@ -199,8 +199,12 @@ hipError_t launch_bn_grads(const float *dqhat, const float *q, const float *mean
 int64_t scan_blocks(int N);
 // counts [N] += occurrences of each row among idx [M] (clamped into [0, N))
 hipError_t launch_usage(const int32_t *idx, int64_t M, int N, uint32_t *counts, hipStream_t st);
+// rows non-NULL: the sparse form instead -- the U distinct rows among idx in
+// increasing order to rows [U], their sums to dval [U][D] (not added to),
+// U to *row_count (device int64).
 hipError_t launch_value_grad(const int32_t *idx, int64_t M, int N, int D, int per_token, const float *w,
                              const float *dout, uint32_t *count, uint32_t *cursor, uint32_t *offs,
-                             uint32_t *block_sum, uint32_t *list, float *dval, hipStream_t st);
+                             uint32_t *block_sum, uint32_t *list, float *dval, int32_t *rows, int64_t *row_count,
+                             hipStream_t st);
 
 }  // namespace pkm

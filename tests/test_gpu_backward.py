@@ -182,6 +182,78 @@ def test_backward_hot_rows(torch):
     compare(got, ref)
 
 
+def _sparse_grads(torch, wl, B, sentinel_rows=-7, sentinel=3.5):
+    cap = min(wl.N, B * wl.H * wl.k)
+    dev = support.device()
+    return {"dvalues_rows": torch.full((cap,), sentinel_rows, dtype=torch.int32, device=dev),
+            "dvalues_sparse": torch.full((cap, wl.D), sentinel, dtype=torch.float32, device=dev),
+            "dvalues_count": torch.full((1,), -1, dtype=torch.int64, device=dev)}
+
+
+@pytest.mark.parametrize("name,B,dim,heads,n,k,table,seed,others", [
+    ("bsp", 40, 64, 2, 16, 4, "f32", 8, True),      # most rows touched, some more than once
+    ("bsp1", 40, 64, 2, 16, 4, "int8", 9, False),   # the value gradient alone
+    ("bsp2", 33, 192, 3, 40, 8, "bf16", 10, True),  # ragged: 33 tokens, 1600 rows
+    ("bsp3", 100, 64, 2, 16, 4, "f32", 11, True),   # one token repeated: rows past 64 occurrences
+])
+def test_backward_sparse_values(torch, name, B, dim, heads, n, k, table, seed, others):
+    """The sparse value gradient: the distinct rows of idx in increasing
+    order, their count, and rows that scattered into zeros equal the dense
+    gradient bit for bit (and so the oracle's); entries past the count are
+    left as they were; the other gradients are unchanged."""
+    wl = synthetic.Workload(name, B, dim, heads, n, k, table, "random")
+    params, x, dout = case(wl, seed, True)
+    if name == "bsp3":
+        x = np.repeat(x[:1], B, axis=0)
+    dense, idx = gpu_backward(torch, wl, params, x, dout)
+    ref = oracle.backward(support.model_for(wl, params), x, dout)
+    compare(dense, ref)
+    grads = _sparse_grads(torch, wl, B)
+    if others:
+        grads.update({nm: torch.zeros(dense[nm].shape, dtype=torch.float32, device=support.device())
+                      for nm in ("dx", "dwq", "dbn_gamma", "dbn_beta", "dsubkeys")})
+    got, idx2 = gpu_backward(torch, wl, params, x, dout, grads=grads)
+    assert np.array_equal(idx, idx2)
+    rows = np.unique(idx)
+    U = int(got["dvalues_count"][0])
+    assert U == rows.size
+    assert np.array_equal(got["dvalues_rows"][:U], rows)
+    assert (got["dvalues_rows"][U:] == -7).all() and (got["dvalues_sparse"][U:] == 3.5).all()
+    assert np.array_equal(got["dvalues_sparse"][:U], dense["dvalues"][rows])
+    assert not np.delete(dense["dvalues"], rows, axis=0).any()
+    for nm in got:
+        if nm in dense:
+            assert np.array_equal(got[nm], dense[nm]), nm
+
+
+def test_backward_sparse_values_batch_stats_and_empty(torch):
+    """The sparse form under training-mode BN equals the dense one; B = 0
+    writes a count of zero."""
+    wl = synthetic.Workload("bsps", 48, 128, 2, 20, 6, "bf16", "random")
+    params, x, dout = case(wl, 12, True)
+    mem = pk.Memory(wl.D, wl.H, wl.n, wl.k, wl.table, max_batch=64)
+    P = pk.params_to_device(params, wl.table, support.device())
+    xt, dt = _to(torch, x), _to(torch, dout)
+    say("sparse value gradient, batch statistics", wl)
+    _, idx, w, mean, var = mem.forward_batch_stats(P, xt)
+    dense = mem.backward(P, xt, idx, w, dt, batch_stats=(mean, var))
+    sparse = mem.backward(P, xt, idx, w, dt, batch_stats=(mean, var), sparse_values=True)
+    torch.cuda.synchronize()
+    assert "dvalues" not in sparse and "dvalues" in dense
+    rows = torch.unique(idx.long()).to(torch.int32)
+    U = int(sparse["dvalues_count"].item())
+    assert U == rows.numel()
+    assert torch.equal(sparse["dvalues_rows"][:U], rows)
+    assert torch.equal(sparse["dvalues_sparse"][:U], dense["dvalues"][rows.long()])
+    for nm in ("dx", "dwq", "dbn_gamma", "dbn_beta", "dsubkeys"):
+        assert torch.equal(sparse[nm], dense[nm]), nm
+    say("sparse value gradient, B = 0")
+    grads = _sparse_grads(torch, wl, 0)
+    mem.backward(P, xt[:0], idx[:0], w[:0], dt[:0], grads=grads)
+    torch.cuda.synchronize()
+    assert int(grads["dvalues_count"].item()) == 0
+
+
 def test_backward_arguments(torch):
     wl = synthetic.Workload("berr", 4, 64, 1, 16, 4, "f32", "unit")
     params = synthetic.make_params(wl)
@@ -199,6 +271,19 @@ def test_backward_arguments(torch):
     g = mem.backward(P, x[:0], idx[:0], w[:0], x[:0])
     torch.cuda.synchronize()
     assert g["dx"].shape == (0, wl.D)
+    # the sparse value gradient: all three members or none, not with the
+    # dense one, and one chunk only
+    sp = _sparse_grads(torch, wl, 4)
+    for bad in ({"dvalues_rows": sp["dvalues_rows"]},
+                {**sp, "dvalues": torch.zeros((wl.N, wl.D), device=support.device())}):
+        with pytest.raises(pk.PkmError) as e:
+            mem.backward(P, x, idx, w, x, grads=bad)
+        assert e.value.status == pk.PKM_E_ARG
+    x16 = torch.zeros((16, wl.D), device=support.device())
+    _, idx16, w16 = mem.forward(P, x16)
+    with pytest.raises(pk.PkmError) as e:
+        mem.backward(P, x16, idx16, w16, x16, grads=_sparse_grads(torch, wl, 16))
+    assert e.value.status == pk.PKM_E_ARG and "max_batch" in pk.last_error()
 
 
 @pytest.mark.slow
