@@ -550,14 +550,14 @@ __global__ __launch_bounds__(256) void fill_lists_kernel(const int32_t *__restri
 // dV[r] += sum over the occurrences o of r, in increasing o (token, head,
 // winner), of w[o] * dout[token(o)].  SPARSE: the sum alone goes to row
 // pos[r] of a compact [U][D] array and r to rows[pos[r]] (no old row read).
-// One wave per kGradRows (8) rows; the wave
+// One wave per ROWS rows (8 dense, 2 sparse: measured best); the wave
 // takes its non-empty rows in turn.  Up to 64 occurrences are put in order
 // by a 64-lane bitonic sort (lane t holds the t-th) and summed over passes
 // of 1024 columns (lane l: columns 4 l + 256 q, q < 4; the old row and two
 // occurrences' dout rows in flight), then added to the row; more are
 // walked by repeated minimum search, each added into the row in turn.
-constexpr int kGradRows = 8;
-template <bool SPARSE>
+constexpr int kGradRowsDense = 8, kGradRowsSparse = 2;
+template <bool SPARSE, int ROWS>
 __global__ __launch_bounds__(64 * WAVES) void value_grad_kernel(const uint32_t *__restrict__ count,
                                                                const uint32_t *__restrict__ offs,
                                                                const uint32_t *__restrict__ list, int N, int D,
@@ -569,16 +569,16 @@ __global__ __launch_bounds__(64 * WAVES) void value_grad_kernel(const uint32_t *
 {
     const int lane = threadIdx.x & 63;
     const int64_t group = (int64_t)blockIdx.x * WAVES + (threadIdx.x >> 6);
-    if (group * kGradRows >= N) return;
-    const int64_t r_lane = group * kGradRows + lane;
-    const bool mine = lane < kGradRows && r_lane < N;
+    if (group * ROWS >= N) return;
+    const int64_t r_lane = group * ROWS + lane;
+    const bool mine = lane < ROWS && r_lane < N;
     const uint32_t my_count = mine ? count[r_lane] : 0u;
     const uint32_t my_start = mine ? offs[r_lane] : 0u;
     uint64_t pending = __ballot(my_count > 0);
     while (pending) {
         const int src = __builtin_ctzll(pending);
         pending &= pending - 1;
-        const int64_t r = group * kGradRows + src;
+        const int64_t r = group * ROWS + src;
         const uint32_t m = (uint32_t)__builtin_amdgcn_readlane((int)my_count, src);
         const uint32_t start = (uint32_t)__builtin_amdgcn_readlane((int)my_start, src);
         float *out = dval + (SPARSE ? (int64_t)pos[r] : r) * D;
@@ -772,7 +772,7 @@ hipError_t launch_value_grad(const int32_t *idx, int64_t M, int N, int D, int pe
     hipLaunchKernelGGL(scan_top_kernel, dim3(1), dim3(256), 0, st, block_sum, (int)nb, nullptr);
     hipLaunchKernelGGL(scan_apply_kernel<false>, dim3((unsigned)nb), dim3(256), 0, st, count, N, block_sum, offs);
     hipLaunchKernelGGL(fill_lists_kernel, dim3(grid_of(M, 256)), dim3(256), 0, st, idx, M, N, offs, cursor, list);
-    const dim3 grid(grid_of((N + kGradRows - 1) / kGradRows, WAVES)), block(64 * WAVES);
+    const dim3 block(64 * WAVES);
     if (rows) {
         // the touched rows' positions among themselves, into cursor (free
         // once the lists are filled), and their number
@@ -780,11 +780,13 @@ hipError_t launch_value_grad(const int32_t *idx, int64_t M, int N, int D, int pe
         hipLaunchKernelGGL(scan_top_kernel, dim3(1), dim3(256), 0, st, block_sum, (int)nb, row_count);
         hipLaunchKernelGGL(scan_apply_kernel<true>, dim3((unsigned)nb), dim3(256), 0, st, count, N, block_sum,
                            cursor);
-        hipLaunchKernelGGL(value_grad_kernel<true>, grid, block, 0, st, count, offs, list, N, D, per_token, w, dout,
-                           dval, cursor, rows);
+        const dim3 grid(grid_of((N + kGradRowsSparse - 1) / kGradRowsSparse, WAVES));
+        hipLaunchKernelGGL((value_grad_kernel<true, kGradRowsSparse>), grid, block, 0, st, count, offs, list, N, D,
+                           per_token, w, dout, dval, cursor, rows);
     } else {
-        hipLaunchKernelGGL(value_grad_kernel<false>, grid, block, 0, st, count, offs, list, N, D, per_token, w, dout,
-                           dval, nullptr, nullptr);
+        const dim3 grid(grid_of((N + kGradRowsDense - 1) / kGradRowsDense, WAVES));
+        hipLaunchKernelGGL((value_grad_kernel<false, kGradRowsDense>), grid, block, 0, st, count, offs, list, N, D,
+                           per_token, w, dout, dval, nullptr, nullptr);
     }
     return hipGetLastError();
 }
