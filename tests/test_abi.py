@@ -181,3 +181,33 @@ def test_binding_rejects_host_tensors():
         pk._binding._expect(torch.zeros(4, 4), "x", (4, 5), "float32")
     with pytest.raises(ValueError, match="expected one of"):
         pk._binding._expect(torch.zeros(4, 4, dtype=torch.float64), "x", (4, 4), "float32")
+
+
+def test_struct_layouts_match_the_header(tmp_path):
+    """The binding's ctypes structures have the header's member names,
+    offsets and sizes (a C program built against include/pkm.h prints
+    them)."""
+    structs = {"pkm_config": pk._binding.Config, "pkm_params": pk._binding.ParamsStruct,
+               "pkm_grads": pk._binding.GradsStruct}
+    lines = ['#include <stddef.h>', '#include <stdio.h>', '#include "pkm.h"', "int main(void) {"]
+    for cname, py in structs.items():
+        lines.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
+        for field, _ in py._fields_:
+            lines.append(f'printf("{cname} {field} %zu\\n", offsetof({cname}, {field}));')
+    lines += ["return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split("\n")
+    got = {tuple(line.split()[:2]): int(line.split()[2]) for line in out if line}
+    for cname, py in structs.items():
+        assert got[(cname, "size")] == ctypes.sizeof(py), cname
+        for field, _ in py._fields_:
+            assert got[(cname, field)] == getattr(py, field).offset, (cname, field)
+    # every member the header declares is in the binding
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    for cname, py in structs.items():
+        body = re.search(r"typedef struct \{([^{}]*)\}\s*" + cname + ";", text).group(1)
+        members = re.findall(r"(\w+)\s*;", body)
+        assert members == [f for f, _ in py._fields_], cname
