@@ -310,3 +310,11 @@ def test_backward_default_shape(torch):
     want = wl.H * dout.astype(np.float64).sum(0)
     assert np.abs(got["dvalues"].sum(0, dtype=np.float64) - want).max() <= 1e-4 * np.abs(want).max()
     print("default backward", {k: f"{v:.2g}" for k, v in errs.items()}, flush=True)
+    # the sparse value gradient (one chunk of all 1024 tokens): the same
+    # touched rows, in order, against the oracle's rows
+    sparse = _sparse_grads(torch, wl, x.shape[0])
+    got_s, idx_s = gpu_backward(torch, wl, params, x, dout, max_batch=1024, grads=sparse)
+    assert np.array_equal(idx_s, idx)
+    U = int(got_s["dvalues_count"][0])
+    assert U == rows.size and np.array_equal(got_s["dvalues_rows"][:U], rows)
+    compare({"dvalues": got_s["dvalues_sparse"][:U]}, {"dval": ref["dval"][rows]})
