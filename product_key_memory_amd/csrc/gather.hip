@@ -61,6 +61,7 @@ __host__ __device__ __forceinline__ int64_t elem_bytes(int64_t c)
 }
 
 typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef _Float16 halfx2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u4v __attribute__((ext_vector_type(4)));
 
 // One lane's 16 bytes of a table row.  NT: a non-temporal load, for
@@ -110,13 +111,36 @@ __device__ __forceinline__ void accumulate(float (&acc)[Fmt<VT>::EPL], const uin
             for (int j = 0; j < 4; ++j)
                 acc[4 * i + j] = fmaf(wt, (float)(int32_t)__builtin_amdgcn_sbfe((int)w[i], 8 * j, 8), acc[4 * i + j]);
     } else {
-        // nibble j of a word (element 8 i + j), sign-extended the same way
+        // Nibble j of word i is element 8 i + j.  Flipping bit 3 of every
+        // nibble turns the two's complement value v into v + 8 in [0, 15];
+        // nibbles j and j + 4 then sit in the low bits of the word's two
+        // fp16 halves after one shift and mask, each half the fp16
+        // subnormal (v + 8) 2^-24, which the mixed fp16/fp32 FMA widens
+        // exactly: acc += (wt 2^24) ((v + 8) 2^-24) = wt (v + 8), two
+        // instructions per element instead of extract, convert and FMA.
+        // The caller takes the 8 sum(wt) back off (int4_offset_sum).
+        const float wt24 = wt * 0x1p24f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t x = w[i] ^ 0x88888888u;
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                acc[8 * i + j] = fmaf(wt, (float)(int32_t)__builtin_amdgcn_sbfe((int)w[i], 4 * j, 4), acc[8 * i + j]);
+            for (int j = 0; j < 4; ++j) {
+                const halfx2 h = __builtin_bit_cast(halfx2, (x >> (4 * j)) & 0x000F000Fu);
+                acc[8 * i + j] = fmaf(wt24, (float)h.x, acc[8 * i + j]);
+                acc[8 * i + j + 4] = fmaf(wt24, (float)h.y, acc[8 * i + j + 4]);
+            }
+        }
     }
+}
+
+// int4 rows accumulate wt (v + 8) (see accumulate): subtract 8 times the sum
+// of the weights the lane applied, once, exactly scaled (one rounding).
+template <int VT>
+__device__ __forceinline__ void int4_offset_sum(float (&acc)[Fmt<VT>::EPL], float wsum)
+{
+    if constexpr (VT == 4)
+#pragma unroll
+        for (int e = 0; e < Fmt<VT>::EPL; ++e) acc[e] = fmaf(-8.0f, wsum, acc[e]);
 }
 
 template <int VT, bool NT>
@@ -137,7 +161,7 @@ __global__ __launch_bounds__(64 * WAVES) void gather_kernel(const uint8_t *__res
     const int64_t row_bytes = elem_bytes<VT>(D);
     const uint8_t *col = values + (active ? elem_bytes<VT>(c0) : 0);
 
-    float acc[EPL];
+    float acc[EPL], wsum = 0.0f;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
 
@@ -159,7 +183,10 @@ __global__ __launch_bounds__(64 * WAVES) void gather_kernel(const uint8_t *__res
                 v[u] = active ? load_row_piece<NT>(col + (int64_t)row * row_bytes) : make_uint4(0, 0, 0, 0);
             }
 #pragma unroll
-            for (int u = 0; u < UNROLL; ++u) accumulate<VT>(acc, v[u], wt[u]);
+            for (int u = 0; u < UNROLL; ++u) {
+                accumulate<VT>(acc, v[u], wt[u]);
+                if constexpr (VT == 4) wsum += wt[u];
+            }
         }
         for (; r < nr; ++r) {
             const int row = min(max(__builtin_amdgcn_readlane(my_row, r), 0), N - 1);
@@ -167,8 +194,10 @@ __global__ __launch_bounds__(64 * WAVES) void gather_kernel(const uint8_t *__res
             if constexpr (SCALED) wt *= scale[row];
             const uint4 v = active ? load_row_piece<NT>(col + (int64_t)row * row_bytes) : make_uint4(0, 0, 0, 0);
             accumulate<VT>(acc, v, wt);
+            if constexpr (VT == 4) wsum += wt;
         }
     }
+    int4_offset_sum<VT>(acc, wsum);
     if (active) {
         float4 *o = reinterpret_cast<float4 *>(out + b * D + c0);
 #pragma unroll
@@ -204,7 +233,7 @@ __global__ __launch_bounds__(64 * WAVES) void gather_pair_kernel(const uint8_t *
     const int64_t row_bytes = elem_bytes<VT>(D);
     const uint8_t *col = values + (active ? elem_bytes<VT>(c0) : 0);
 
-    float acc[EPL];
+    float acc[EPL], wsum = 0.0f;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
 
@@ -215,7 +244,9 @@ __global__ __launch_bounds__(64 * WAVES) void gather_pair_kernel(const uint8_t *
     for (int r0 = rb; r0 < re; r0 += 64) {
         const int nr = min(64, re - r0);
         const int my_row = lane < nr ? ib[r0 + lane] : 0;
-        const float my_w = lane < nr ? wb[r0 + lane] : 0.0f;
+        // the weights, times the row scales, for up to 64 rows at once
+        float my_w = lane < nr ? wb[r0 + lane] : 0.0f;
+        if constexpr (SCALED) my_w *= lane < nr ? scale[min(max(my_row, 0), N - 1)] : 0.0f;
         const int pairs = (nr + 1) >> 1;
         for (int t0 = 0; t0 < pairs; t0 += UNROLL) {
             uint4 v[UNROLL];
@@ -231,13 +262,16 @@ __global__ __launch_bounds__(64 * WAVES) void gather_pair_kernel(const uint8_t *
                 const bool ok = 2 * (t0 + u) + half < nr;
                 const int row = min(max(half ? row_o : row_e, 0), N - 1);
                 wt[u] = ok ? (half ? w_o : w_e) : 0.0f;
-                if constexpr (SCALED) wt[u] *= scale[row];
                 v[u] = active && ok ? load_row_piece<NT>(col + (int64_t)row * row_bytes) : make_uint4(0, 0, 0, 0);
             }
 #pragma unroll
-            for (int u = 0; u < UNROLL; ++u) accumulate<VT>(acc, v[u], wt[u]);
+            for (int u = 0; u < UNROLL; ++u) {
+                accumulate<VT>(acc, v[u], wt[u]);
+                if constexpr (VT == 4) wsum += wt[u];
+            }
         }
     }
+    int4_offset_sum<VT>(acc, wsum);
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[e] += __shfl_xor(acc[e], 32, 64);
     if constexpr (SPLIT > 1) {
