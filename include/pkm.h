@@ -16,15 +16,16 @@
  *   a6  w = softmax of the k winning scores (no temperature)
  *   a7  out[b,:] = sum_h sum_j w[b,h,j] * scale[row] * values[row,:],
  *       row = idx[b,h,j]                (EmbeddingBag "sum", per-sample
- *                                        weights; scale = 1 unless E4M3)
+ *                                        weights; scale = 1 for fp32 and
+ *                                        bf16 tables)
  *
  * The winners are the exact top-k over all n_keys^2 concatenated keys (the
  * exactness argument of §Factorising the key space); a5-a7 follow the top-k
  * then softmax read of "Memory Retrieval Mechanisms: From Soft to
  * Efficient" (top-k section).  Scores, softmax and the accumulation run in
- * fp32; the value table may be fp32, bf16 or OCP FP8 E4M3 (E4M3FN) with one
- * fp32 scale per row (the page's note that the table suits a lower
- * precision).
+ * fp32; the value table may be fp32, bf16, or OCP FP8 E4M3 (E4M3FN), int8 or
+ * int4 with one fp32 scale per row (the page's note that the table suits a
+ * lower precision).
  *
  * Conventions for every call:
  *   - Pointers to tensors are DEVICE pointers, owned by the caller, row-major
@@ -34,7 +35,10 @@
  *     only enqueue work: they return before it runs and never synchronise the
  *     device.  Inputs must stay alive and outputs untouched until the stream
  *     reaches that point.  Results are deterministic (bitwise) for identical
- *     inputs and configuration.
+ *     inputs and configuration.  Apart from pkm_create and pkm_destroy, no
+ *     call allocates, copies or clears memory with the runtime: each only
+ *     launches kernels on its stream, so a caller may capture the calls in a
+ *     HIP graph and replay them.
  *   - One context serves one stream at a time: the workspace is shared by
  *     every call on a context.  Use one context per concurrent stream.
  *   - Argument errors are detected on the host before anything is enqueued
