@@ -219,7 +219,8 @@ typedef struct {
     float *dbn_beta;  /* [H, D] */
     float *dsubkeys;  /* [H, 2, n_keys, D/2] */
     float *dvalues;   /* [n_keys^2, D]: w.r.t. the dequantised value rows
-                         (scale[row] * stored value for E4M3 tables) */
+                         (scale[row] * decoded value for the scaled
+                         tables: E4M3, int8, int4) */
     int32_t *dvalues_rows;  /* sparse form, see above */
     float *dvalues_sparse;
     int64_t *dvalues_count;
