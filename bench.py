@@ -248,17 +248,23 @@ def cpu_baseline(wl, params, x, seconds=10.0):
     oracle.run(model, x[:probe], want=("out",), nthreads=cores)
     rate = probe / max(time.perf_counter() - t0, 1e-9)
     sample = int(min(x.shape[0], max(cores, rate * seconds)))
-    t0 = time.perf_counter()
-    oracle.run(model, x[:sample], want=("out",), nthreads=cores)
-    dt = time.perf_counter() - t0
+    # when the whole batch takes less than the time budget, pass over it
+    # again until the budget is spent (a steadier figure)
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        oracle.run(model, x[:sample], want=("out",), nthreads=cores)
+        passes += 1
+        dt = time.perf_counter() - t0
+        if sample < x.shape[0] or dt >= 0.8 * seconds:
+            break
     # one core, on a sample a tenth of the time budget long
-    one = max(1, int(sample / dt / cores * seconds / 10))
+    one = max(1, min(x.shape[0], int(passes * sample / dt / cores * seconds / 10)))
     t0 = time.perf_counter()
     oracle.run(model, x[:one], want=("out",), nthreads=1)
     dt1 = time.perf_counter() - t0
-    return {"value": sample / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"first {sample} of the {wl.B} tokens of the {wl.name} workload, full lookup in fp64, "
-                      f"{dt:.1f} s wall on {cores} threads",
+    return {"value": passes * sample / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{passes} pass(es) over the first {sample} of the {wl.B} tokens of the {wl.name} workload, "
+                      f"full lookup in fp64, {dt:.1f} s wall on {cores} threads",
             "single_core_value": one / dt1,
             "single_core_sample": f"first {one} tokens on 1 thread, {dt1:.1f} s wall"}
 
