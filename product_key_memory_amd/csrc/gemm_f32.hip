@@ -60,11 +60,14 @@
 // key matrix: row j = (a, c) is [C0[a]; C1[c]].  The subkey rows are split
 // into their fp16 pieces once per call (split_keys_kernel, each row with
 // its own power of two) in the order a staging lane copies them, so a tile
-// stages its 256 virtual rows by copying pieces; the two halves of K
-// accumulate separately (their key-row exponents differ) and are scaled
-// and summed in the epilogue.  M is a few dozen tokens: 32 x 256 tiles, 4
-// waves of 32 x 64.  The epilogue can record each row's largest score per
-// group of 64 keys, from which the top-k derives a threshold.
+// stages its 256 virtual rows by copying pieces.  The two halves of K carry
+// different key-row exponents: after the first half the accumulators of
+// each key are multiplied by the power of two between them (exact) and the
+// second half adds on in the same registers.  M is a few dozen tokens:
+// 64 x 256 tiles of 4 waves of 64 x 64 (32 x 256, waves of 32 x 64, for at
+// most 32 tokens), so each staged key row serves up to 64 tokens.  The
+// epilogue can record each row's largest score per group of 64 keys, from
+// which the top-k derives a threshold.
 #include "pkm_internal.h"
 #include "wave_ops.h"
 
@@ -130,7 +133,8 @@ __device__ __forceinline__ int row_exponent(float m)
 
 using BigTile = Tile<256, 256, 4, 2>;
 using SmallTile = Tile<128, 128, 2, 2>;
-using KeyTile = Tile<32, 256, 1, 4>;
+using KeyTile = Tile<32, 256, 1, 4>;    // up to 32 rows of A
+using KeyTile64 = Tile<64, 256, 1, 4>;  // more: each staged key row serves 64
 
 // Eight consecutive k-values of one row, scaled by 2^ex and split into their
 // hi and lo fp16 pieces (a - hi is exact: one mixed fp32/fp16 FMA per value
@@ -317,22 +321,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, int tm, int tn, int
     // scaled in the epilogue's combination below instead)
     const auto col_exp = [&](int n) { return PRODUCT_B ? 0 : b_exp[n]; };
 
-    // Product-key B: the two halves of K carry their own key-row exponents,
-    // so they accumulate separately (acc, then acc2) and meet in the epilogue
-    floatx16 acc[T::TM][T::TN], acc2[PRODUCT_B ? T::TM : 1][PRODUCT_B ? T::TN : 1];
+    floatx16 acc[T::TM][T::TN];
 #pragma unroll
     for (int i = 0; i < T::TM; ++i)
 #pragma unroll
         for (int j = 0; j < T::TN; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-    if constexpr (PRODUCT_B)
-#pragma unroll
-        for (int i = 0; i < T::TM; ++i)
-#pragma unroll
-            for (int j = 0; j < T::TN; ++j)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) acc2[i][j][v] = 0.0f;
 
     const int KT = klen / kBK;
     st.load(0);
@@ -365,8 +360,24 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, int tm, int tn, int
         }
     };
     if constexpr (PRODUCT_B) {
+        // Product-key B: the two halves of K carry their own key-row
+        // exponents e0 (first subkey) and e1 (second).  After the first
+        // half the sums of column n are moved from scale 2^e0 to 2^e1
+        // (exact: a power of two), then the second half adds on in the same
+        // accumulators.  32x32 layout: lane l holds column l % 32 of each
+        // block.
         run(acc, 0, st.kch);
-        run(acc2, st.kch, KT);
+#pragma unroll
+        for (int j = 0; j < T::TN; ++j) {
+            const int col = min(n0 + wn * T::TN * 32 + j * 32 + il, a.N - 1);
+            const int ka = col / a.key_n;
+            const int shift = b2_exp[col - ka * a.key_n] - b_exp[ka];
+#pragma unroll
+            for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[i][j][v] = __builtin_ldexpf(acc[i][j][v], shift);
+        }
+        run(acc, st.kch, KT);
     } else {
         run(acc, 0, KT);
     }
@@ -379,14 +390,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, int tm, int tn, int
         ex_lds[t] = t < T::BM ? row_exp(min(m0 + t, a.M - 1)) : col_exp(min(n0 + t - T::BM, a.N - 1));
     __syncthreads();
     if constexpr (PRODUCT_B) {
-        // both halves to true scale and summed, into acc (32x32 layout:
-        // register v of lane l is row 8 (v / 4) + 4 (l / 32) + v % 4, column
-        // l % 32 of its block); the staged epilogue below then scales nothing
+        // to true scale, 2^-(e_row + e1) (32x32 layout: register v of lane l
+        // is row 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32 of its
+        // block); the staged epilogue below then scales nothing
 #pragma unroll
         for (int j = 0; j < T::TN; ++j) {
             const int col = min(n0 + wn * T::TN * 32 + j * 32 + il, a.N - 1);
             const int ka = col / a.key_n;
-            const int e0 = b_exp[ka], e1 = b2_exp[col - ka * a.key_n];
+            const int e1 = b2_exp[col - ka * a.key_n];
 #pragma unroll
             for (int i = 0; i < T::TM; ++i)
 #pragma unroll
@@ -394,8 +405,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, int tm, int tn, int
                     const i4 er = *reinterpret_cast<const i4 *>(&ex_lds[wm * T::TM * 32 + i * 32 + v4 * 8 + kk * 4]);
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        acc[i][j][v4 * 4 + e] = __builtin_ldexpf(acc[i][j][v4 * 4 + e], -(er[e] + e0)) +
-                                                __builtin_ldexpf(acc2[i][j][v4 * 4 + e], -(er[e] + e1));
+                        acc[i][j][v4 * 4 + e] = __builtin_ldexpf(acc[i][j][v4 * 4 + e], -(er[e] + e1));
                 }
         }
     }
@@ -905,6 +915,7 @@ hipError_t launch_gemm_nt_f32_product(const GemmArgs &args, hipStream_t stream)
         args.b_split_bytes < gemm_split_bytes(args) || (reinterpret_cast<uintptr_t>(args.b_split) & 15) != 0)
         return hipErrorInvalidValue;
     if (tile_count<KeyTile>(args) > 0x7FFFFFFF || args.batch > 32767) return hipErrorInvalidConfiguration;
+    const bool wide = args.M > 32;
     GemmArgs a = args;
     hipError_t e = prepare_exponents(a, true, stream);
     if (e != hipSuccess) return e;
@@ -914,6 +925,7 @@ hipError_t launch_gemm_nt_f32_product(const GemmArgs &args, hipStream_t stream)
                        a.B, a.B2, a.strideB, a.ldb, a.key_n, kch, a.b_exp, a.b2_exp,
                        reinterpret_cast<u4 *>(a.b_split));
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (wide) return launch_variant<KeyTile64, false, false, true>(a, stream);
     return launch_variant<KeyTile, false, false, true>(a, stream);
 }
 

@@ -101,9 +101,11 @@ def test_flat_search_full_size(torch, name, tokens):
     dict(B=3, D=64, H=1, n=2048, k=64),    # 4M keys: two merge passes
     dict(B=2, D=64, H=1, n=4096, k=32),    # the largest n_keys: 16.7M keys
     dict(B=4, D=64, H=3, n=8, k=8),        # k = n_keys
-    dict(B=33, D=192, H=1, n=40, k=1),     # k = 1, two 32-row tiles, the second ragged
+    dict(B=33, D=192, H=1, n=40, k=1),     # k = 1, one ragged 64-row tile
     dict(B=31, D=64, H=2, n=24, k=8),      # one ragged 32-row tile; n not a multiple of 32
-    dict(B=70, D=128, H=2, n=24, k=8),     # three 32-row tiles
+    dict(B=70, D=128, H=2, n=24, k=8),     # two 64-row tiles, the second ragged
+    dict(B=64, D=64, H=2, n=16, k=4),      # one full 64-row tile
+    dict(B=65, D=64, H=1, n=16, k=4),      # a second 64-row tile holding one row
 ])
 def test_flat_search_edge_shapes(torch, shape):
     wl = synthetic.Workload("flat_edge", shape["B"], shape["D"], shape["H"], shape["n"], shape["k"], "f32", "random")
