@@ -506,79 +506,62 @@ hipError_t launch_flat_pass(const void *in, int64_t rows, int64_t len, int k, ui
 // theta = the k-th largest of a row's group maxima (groups of 64 scores): k
 // distinct groups hold an element >= theta, so the row's k-th best score is
 // >= theta and every winner scores >= theta.  For untied scores only a few
-// more than k elements do.  A wave takes kFilterBlocks blocks of 4096 scores;
-// a block whose lanes cannot hold a score >= theta is dropped after one
-// integer maximum per element; otherwise its elements >= theta are appended
-// to the row's list at positions from an atomic add (the list's order varies
-// between runs; its top-k, over unique packed keys, does not).
-constexpr int kFilterBlocks = 4;
+// more than k elements do.  A group whose maximum is below theta holds no
+// such element, so only the groups whose maximum reaches theta (about k of
+// the row's n^2 / 64) are read: a wave scans kGroupSeg group maxima of its
+// row and, for each group that qualifies, reads its 64 scores and appends
+// those >= theta to the row's list at positions from an atomic add (the
+// list's order varies between runs; its top-k, over unique packed keys,
+// does not).  The maxima are the scores' own values (order-key maxima), so
+// the test is exact.
+constexpr int kGroupSeg = 1024;
 
-template <bool VEC4>
-__global__ __launch_bounds__(64 * WAVES) void flat_filter_kernel(const float *__restrict__ scores, int64_t rows,
-                                                                 int64_t len, int segs, int k,
+__global__ __launch_bounds__(64 * WAVES) void flat_filter_kernel(const float *__restrict__ scores,
+                                                                 const float *__restrict__ gmax, int64_t rows,
+                                                                 int64_t len, int64_t groups, int segs, int k,
                                                                  const float *__restrict__ ttop,
                                                                  uint32_t *__restrict__ count,
                                                                  uint64_t *__restrict__ list)
 {
-    constexpr int MH = kFlatScoreSeg / 64;
     const int lane = threadIdx.x & 63;
     const int64_t item = (int64_t)blockIdx.x * WAVES + (threadIdx.x >> 6);  // row * segs + segment
     if (item >= rows * segs) return;
     const int64_t row = item / segs;
     const int seg = (int)(item - row * segs);
     const uint32_t tkey = order_key(ttop[row * k + k - 1]);
+    const float *grow = gmax + row * groups;
     const float *srow = scores + row * len;
     uint64_t *lst = list + row * kFlatListCap;
-#pragma unroll 1
-    for (int blk = 0; blk < kFilterBlocks; ++blk) {
-        const int64_t base = ((int64_t)seg * kFilterBlocks + blk) * kFlatScoreSeg;
-        if (base >= len) break;
-        const int m = (int)min((int64_t)kFlatScoreSeg, len - base);
-        const float *brow = srow + base;
-        float v[MH];
-        if constexpr (VEC4) {
+    const int64_t g0 = (int64_t)seg * kGroupSeg;
+    float gm[kGroupSeg / 64];
 #pragma unroll
-            for (int q = 0; q < MH / 4; ++q) {
-                const float4 f = *reinterpret_cast<const float4 *>(brow + min(q * 256 + lane * 4, m - 4));
-                v[4 * q] = f.x;
-                v[4 * q + 1] = f.y;
-                v[4 * q + 2] = f.z;
-                v[4 * q + 3] = f.w;
-            }
-        } else {
+    for (int t = 0; t < kGroupSeg / 64; ++t) {
+        const int64_t g = g0 + t * 64 + lane;
+        gm[t] = g < groups ? grow[g] : 0.0f;
+    }
 #pragma unroll
-            for (int t = 0; t < MH; ++t) v[t] = brow[min(t * 64 + lane, m - 1)];
-        }
-        // A bound on the lane's largest order key from the largest raw bit
-        // pattern as a signed integer (clamped loads repeat real elements):
-        // exact over the non-negative scores, which outrank every negative
-        // one; with none, no key exceeds +0's; infinities and NaNs are
-        // always examined.
-        int32_t mx = INT32_MIN;
-#pragma unroll
-        for (int t = 0; t < MH; ++t) mx = max(mx, (int32_t)__float_as_uint(v[t]));
-        const uint32_t bound = mx >= 0x7F800000 ? 0xFFFFFFFFu : mx >= 0 ? order_key(__int_as_float(mx)) : 0x80000000u;
-        if (__ballot(bound >= tkey) == 0) continue;
-        // survivors are rare: one atomic add per register slot that has any
-#pragma unroll
-        for (int t = 0; t < MH; ++t) {
-            const int e = slot_element<VEC4>(t, lane);
-            const uint32_t key = order_key(v[t]);
-            const bool keep = e < m && key >= tkey;
+    for (int t = 0; t < kGroupSeg / 64; ++t) {
+        uint64_t hits = __ballot(g0 + t * 64 + lane < groups && order_key(gm[t]) >= tkey);
+        while (hits) {
+            const int l = __builtin_ctzll(hits);
+            hits &= hits - 1;
+            const int64_t base = (g0 + t * 64 + l) * 64;
+            const int m = (int)min((int64_t)64, len - base);
+            const float v = lane < m ? srow[base + lane] : 0.0f;
+            const uint32_t key = order_key(v);
+            const bool keep = lane < m && key >= tkey;
             const uint64_t mask = __ballot(keep);
             if (mask == 0) continue;
             uint32_t pos = 0;
             if (lane == 0) pos = atomicAdd(count + row, (uint32_t)__popcll(mask));
             const uint32_t p = read_lane(pos, 0) + (uint32_t)below_me(mask);
-            if (keep && p < (uint32_t)kFlatListCap) lst[p] = pack(key, (uint32_t)(base + e));
+            if (keep && p < (uint32_t)kFlatListCap) lst[p] = pack(key, (uint32_t)(base + lane));
         }
     }
 }
 
-// Rows whose list overflowed (more than kFlatListCap scores >= theta, i.e.
-// heavy ties at theta): one wave scans the whole row, one 4096-score block
-// at a time (wave_topk), merging each block's k best into the running k
-// best, and overwrites the row's result.  Other rows return at once.
+// A row whose list overflowed (more than kFlatListCap scores >= theta: heavy
+// exact ties) is ranked in full by one wave.
 template <bool VEC4>
 __global__ __launch_bounds__(64 * WAVES) void flat_rescan_kernel(const float *__restrict__ scores, int64_t rows,
                                                                  int64_t len, int k, const uint32_t *__restrict__ count,
@@ -676,15 +659,11 @@ hipError_t launch_flat_topk_threshold(const float *scores, const float *gmax, in
     if ((e = launch_fill(reinterpret_cast<uint32_t *>(list), rows * kFlatListCap * 2, 0u, stream)) != hipSuccess)
         return e;
     const bool vec4 = len % 4 == 0;
-    const int64_t segs = (len + (int64_t)kFlatScoreSeg * kFilterBlocks - 1) / ((int64_t)kFlatScoreSeg * kFilterBlocks);
+    const int64_t segs = (groups + kGroupSeg - 1) / kGroupSeg;
     const int64_t blocks = (rows * segs + WAVES - 1) / WAVES;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    if (vec4)
-        hipLaunchKernelGGL((flat_filter_kernel<true>), dim3((unsigned)blocks), dim3(64 * WAVES), 0, stream, scores,
-                           rows, len, (int)segs, k, ttop, count, list);
-    else
-        hipLaunchKernelGGL((flat_filter_kernel<false>), dim3((unsigned)blocks), dim3(64 * WAVES), 0, stream, scores,
-                           rows, len, (int)segs, k, ttop, count, list);
+    hipLaunchKernelGGL(flat_filter_kernel, dim3((unsigned)blocks), dim3(64 * WAVES), 0, stream, scores, gmax, rows,
+                       len, groups, (int)segs, k, ttop, count, list);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // the lists' top-k (unused slots hold 0, the absent key), then the rows
     // whose list overflowed
