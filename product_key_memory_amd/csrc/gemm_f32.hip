@@ -541,7 +541,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, int tm, int tn, int
                 float *dst = &C[(int64_t)row * a.ldc + col];
                 if (vec && ncol == 4) {
                     if (ACCUMULATE) x += *reinterpret_cast<const fx4 *>(dst);
-                    *reinterpret_cast<fx4 *>(dst) = x;
+                    // the flat search's key scores are read back only where
+                    // a group can hold a winner: stream them past the caches
+                    if constexpr (PRODUCT_B) __builtin_nontemporal_store(x, reinterpret_cast<fx4 *>(dst));
+                    else *reinterpret_cast<fx4 *>(dst) = x;
                 } else {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
