@@ -109,7 +109,9 @@ typedef struct {
     const float *subkeys;     /* [H, 2, n, D/2]: half p of head h */
     const void *values;       /* [N, D] of value_type ([N, D/2] bytes for int4), N = n*n */
     const float *value_scale; /* [N] for the E4M3, int8 and int4 tables, else ignored
-                                 (may be NULL) */
+                                 (may be NULL).  Finite; for int4 tables
+                                 |scale| < 2^100 (the decode scales the
+                                 weight by 2^24) */
 } pkm_params;
 
 typedef struct pkm_ctx pkm_ctx; /* opaque; owned by the library */
