@@ -226,6 +226,24 @@ def test_backward_sparse_values(torch, name, B, dim, heads, n, k, table, seed, o
             assert np.array_equal(got[nm], dense[nm]), nm
 
 
+@pytest.mark.parametrize("cfg", _random_backward_configs(6, 31),
+                         ids=lambda c: "B{B}-D{D}-H{H}-n{n}-k{k}-{table}".format(**c))
+def test_backward_sparse_values_random_configs(torch, cfg):
+    """Seeded random configurations (one chunk): the sparse value gradient's
+    rows are the distinct rows of idx in order, and its values equal the
+    dense gradient's rows bit for bit."""
+    wl = synthetic.Workload("rbs", cfg["B"], cfg["D"], cfg["H"], cfg["n"], cfg["k"], cfg["table"], "random")
+    params, x, dout = case(wl, cfg["seed"], gamma_beta=True)
+    dense, idx = gpu_backward(torch, wl, params, x, dout, max_batch=cfg["B"],
+                              grads={"dvalues": torch.zeros((wl.N, wl.D), device=support.device())})
+    got, idx2 = gpu_backward(torch, wl, params, x, dout, max_batch=cfg["B"], grads=_sparse_grads(torch, wl, wl.B))
+    assert np.array_equal(idx, idx2)
+    rows = np.unique(idx)
+    U = int(got["dvalues_count"][0])
+    assert U == rows.size and np.array_equal(got["dvalues_rows"][:U], rows)
+    assert np.array_equal(got["dvalues_sparse"][:U], dense["dvalues"][rows])
+
+
 def test_backward_sparse_values_batch_stats_and_empty(torch):
     """The sparse form under training-mode BN equals the dense one; B = 0
     writes a count of zero."""
