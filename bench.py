@@ -94,24 +94,65 @@ def end_to_end(wl, ms):
             "composite_frac": round(value * ideal / wl.B, 4), "composite_ideal_us": round(ideal * 1e6, 2)}
 
 
-def timed_steps(torch, fn, steps, warmup):
-    """Average ms per call of fn over `steps` calls after `warmup` calls,
-    bracketed by device synchronisation, timed with events on the current
-    stream (the stream the library launches on)."""
+WARM_SECONDS = 1.0   # least warm-up wall time before any timed call
+WARM_MAX_SECONDS = 10.0
+WARM_SETTLE = 0.02   # warm-up ends once two successive medians agree this well
+
+
+def warm_up(torch, fn, warmup):
+    """At least `warmup` calls and WARM_SECONDS of calls, then calls in
+    rounds of 10 until two successive rounds' median call times agree
+    within WARM_SETTLE (clocks and caches settled), at most WARM_MAX_SECONDS.
+    Returns the number of calls made."""
+    calls, t0 = 0, time.perf_counter()
     for _ in range(warmup):
         fn()
+        calls += 1
     torch.cuda.synchronize()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(steps):
+    while time.perf_counter() - t0 < WARM_SECONDS:
         fn()
-    stop.record()
+        calls += 1
+        torch.cuda.synchronize()
+    prev = None
+    while time.perf_counter() - t0 < WARM_MAX_SECONDS:
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(11)]
+        ev[0].record()
+        for i in range(10):
+            fn()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        calls += 10
+        med = float(np.median([ev[i].elapsed_time(ev[i + 1]) for i in range(10)]))
+        if prev is not None and abs(med - prev) <= WARM_SETTLE * prev:
+            break
+        prev = med
+    return calls
+
+
+def timed_steps(torch, fn, steps, warmup, stats=None):
+    """Median ms per call of fn over `steps` calls, each bracketed by its own
+    pair of events on the current stream (the stream the library launches
+    on), after warm_up(); the calls are enqueued back to back and the
+    device is synchronised before and after them.  With stats (a dict),
+    also records the mean, min, max and the warm-up call count."""
+    calls = warm_up(torch, fn, warmup)
     torch.cuda.synchronize()
-    return start.elapsed_time(stop) / steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
+    for i in range(steps):
+        fn()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    t = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
+    if stats is not None:
+        stats.update(mean_ms=round(float(t.mean()), 4), min_ms=round(float(t.min()), 4),
+                     max_ms=round(float(t.max()), 4), warmup_calls=calls,
+                     total_ms=round(float(ev[0].elapsed_time(ev[steps])), 4))
+    return float(np.median(t))
 
 
 def kernel_times(torch, mem, P, xt, steps, warmup):
-    """Average ms of each stage's kernel: events between consecutive stage
+    """Median ms of each stage's kernel: events between consecutive stage
     calls on one stream, every iteration enqueued before one final sync."""
     B = xt.shape[0]
     q = torch.empty((B, mem.heads, mem.dim), dtype=torch.float32, device=xt.device)
@@ -121,9 +162,12 @@ def kernel_times(torch, mem, P, xt, steps, warmup):
     out = torch.empty((B, mem.dim), dtype=torch.float32, device=xt.device)
     stages = [lambda: mem.query(P, xt, q), lambda: mem.score(P, q, s), lambda: mem.select(s, idx, w),
               lambda: mem.gather(P, idx, w, out)]
-    for _ in range(warmup):
+
+    def step():
         for f in stages:
             f()
+
+    warm_up(torch, step, warmup)
     torch.cuda.synchronize()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(steps)]
     for it in range(steps):
@@ -133,7 +177,7 @@ def kernel_times(torch, mem, P, xt, steps, warmup):
             ev[it][j + 1].record()
     torch.cuda.synchronize()
     names = ["query_gemm", "score_gemm", "select", "gather"]
-    return {nm: float(np.mean([ev[it][j].elapsed_time(ev[it][j + 1]) for it in range(steps)]))
+    return {nm: float(np.median([ev[it][j].elapsed_time(ev[it][j + 1]) for it in range(steps)]))
             for j, nm in enumerate(names)}
 
 
@@ -237,11 +281,45 @@ def backward_step(torch, mem, wl, P, xt, idx, wts, fwd_ms, steps, warmup):
             "workspace_bytes": mem.backward_workspace_bytes()}
 
 
+def _ranges(cpus):
+    """[0, 1, 2, 5] -> "0-2,5"."""
+    out, cpus = [], sorted(cpus)
+    i = 0
+    while i < len(cpus):
+        j = i
+        while j + 1 < len(cpus) and cpus[j + 1] == cpus[j] + 1:
+            j += 1
+        out.append(str(cpus[i]) if i == j else f"{cpus[i]}-{cpus[j]}")
+        i = j + 1
+    return ",".join(out)
+
+
+def host_cores():
+    """The host's logical CPUs, this process's affinity mask, and the CPU
+    time its cgroup allows (cpu.max), if any."""
+    aff = sorted(os.sched_getaffinity(0))
+    quota = None
+    try:
+        with open("/sys/fs/cgroup/cpu.max") as f:
+            q, period = f.read().split()
+        if q != "max":
+            quota = int(q) / int(period)
+    except (OSError, ValueError):
+        pass
+    return {"os_cpu_count": os.cpu_count(), "affinity_count": len(aff), "affinity_mask": _ranges(aff),
+            "cgroup_cpu_quota": quota}
+
+
 def cpu_baseline(wl, params, x, seconds=10.0):
-    """The fp64 oracle on host cores over a bounded sample of the tokens."""
+    """The fp64 oracle on every host core this process may use (its
+    affinity mask, or the whole CPUs its cgroup quota allows if fewer) over
+    a bounded sample of the tokens."""
     import oracle
 
-    cores = min(16, len(os.sched_getaffinity(0)))
+    hc = host_cores()
+    cores = hc["affinity_count"]
+    if hc["cgroup_cpu_quota"]:
+        cores = max(1, min(cores, int(hc["cgroup_cpu_quota"])))
     model = oracle.Model.from_params(params, wl.k, wl.table)
     probe = min(x.shape[0], 2 * cores)
     t0 = time.perf_counter()
@@ -262,7 +340,7 @@ def cpu_baseline(wl, params, x, seconds=10.0):
     t0 = time.perf_counter()
     oracle.run(model, x[:one], want=("out",), nthreads=1)
     dt1 = time.perf_counter() - t0
-    return {"value": passes * sample / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+    return {"value": passes * sample / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle", "host": hc,
             "sample": f"{passes} pass(es) over the first {sample} of the {wl.B} tokens of the {wl.name} workload, "
                       f"full lookup in fp64, {dt:.1f} s wall on {cores} threads",
             "single_core_value": one / dt1,
@@ -314,7 +392,8 @@ def main():
     idx = torch.empty((wl.B, wl.H, wl.k), dtype=torch.int32, device="cuda")
     wts = torch.empty((wl.B, wl.H, wl.k), dtype=torch.float32, device="cuda")
 
-    ms = timed_steps(torch, lambda: mem.forward(P, xt, out, idx, wts), args.steps, args.warmup)
+    step_stats = {}
+    ms = timed_steps(torch, lambda: mem.forward(P, xt, out, idx, wts), args.steps, args.warmup, step_stats)
     rows = idx.cpu().numpy().ravel()
     distinct = float(np.unique(rows).size) / rows.size
     kt = kernel_times(torch, mem, P, xt, args.steps, args.warmup)
@@ -350,7 +429,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp32",
+        "dtype": "fp32 (fp16x3 split)",
+        "timing": dict(step_stats, statistic="median of per-step event pairs"),
         "data": "synthetic",
         "config": {"workload": wl.name, "tokens_per_step": B, "dim": wl.D, "heads": wl.H, "n_keys": wl.n,
                    "rows": wl.N, "k": wl.k, "value_table": wl.table, "seed": 0, "max_batch": max_batch},

@@ -63,6 +63,10 @@ def load_library(path):
     lib.pkmo_int4_to_f64.argtypes = [ctypes.c_uint8]
     lib.pkmo_usage.restype = ctypes.c_int
     lib.pkmo_usage.argtypes = [ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.pkmo_scores.restype = ctypes.c_int
+    lib.pkmo_scores.argtypes = [ctypes.POINTER(_Model), ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    lib.pkmo_running_update.restype = ctypes.c_int
+    lib.pkmo_running_update.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_double] + [ctypes.c_void_p] * 4
     lib.pkmo_select.restype = ctypes.c_int
     lib.pkmo_select.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int] + [ctypes.c_void_p] * 4
     lib.pkmo_gather.restype = ctypes.c_int
@@ -183,6 +187,19 @@ def int4_to_f64(nibble, lib=None):
     return (lib or _load()).pkmo_int4_to_f64(int(nibble))
 
 
+def scores(model, x, lib=None):
+    """Steps 1-3: the half scores [B, H, 2, n] (fp64) of every token of
+    x [B, D] (f32), the numbers run() ranks."""
+    lib = lib or _load()
+    x = _c(x, np.float32)
+    B = x.shape[0]
+    assert x.shape == (B, model.D)
+    s = np.empty((B, model.H, 2, model.n), np.float64)
+    if lib.pkmo_scores(ctypes.byref(model._s), B, _ptr(x), _ptr(s)) != 0:
+        raise ValueError("oracle rejected its arguments")
+    return s
+
+
 def select(scores, k, lib=None):
     """Steps 4-6 from given half scores [..., 2, n] (any float dtype, read
     as fp64).  Returns idx, top, w, each [..., k]."""
@@ -199,9 +216,9 @@ def select(scores, k, lib=None):
     return idx, top, w
 
 
-def gather(model, rows, w, lib=None):
+def gather(model, rows, w, out=None, lib=None):
     """Step 7 from given rows [B, R] (int32) and weights [B, R] (read as
-    fp64).  Returns out [B, D] fp64."""
+    fp64).  Returns out [B, D] fp64 (overwritten when given)."""
     lib = lib or _load()
     rows = _c(np.asarray(rows, np.int32), np.int32)
     w = np.ascontiguousarray(w, dtype=np.float64)
@@ -209,7 +226,9 @@ def gather(model, rows, w, lib=None):
     assert w.shape == (B, R)
     if B and (rows.min() < 0 or rows.max() >= model.n * model.n):
         raise ValueError("row index out of range")
-    out = np.empty((B, model.D), np.float64)
+    if out is None:
+        out = np.empty((B, model.D), np.float64)
+    assert out.dtype == np.float64 and out.shape == (B, model.D) and out.flags.c_contiguous
     if lib.pkmo_gather(ctypes.byref(model._s), B, R, _ptr(rows), _ptr(w), _ptr(out)) != 0:
         raise ValueError("oracle rejected its arguments")
     return out
@@ -294,6 +313,20 @@ def backward_batch_stats(model, x, dout, mean, var, want=GRADS, lib=None):
     if rc != 0:
         raise ValueError("oracle rejected its arguments" if rc == -1 else "oracle ran out of memory")
     return res
+
+
+def running_update(rmean, rvar, mean, var, B, momentum=0.1, lib=None):
+    """BatchNorm's running statistics after a batch of B tokens with
+    statistics mean / var (biased): returns the updated (rmean, rvar), fp64
+    copies of the given arrays."""
+    lib = lib or _load()
+    rm = np.array(rmean, np.float64, copy=True, order="C")
+    rv = np.array(rvar, np.float64, copy=True, order="C")
+    mean, var = _c(np.asarray(mean, np.float64), np.float64), _c(np.asarray(var, np.float64), np.float64)
+    assert rm.shape == rv.shape == mean.shape == var.shape
+    if lib.pkmo_running_update(rm.size, int(B), float(momentum), _ptr(mean), _ptr(var), _ptr(rm), _ptr(rv)) != 0:
+        raise ValueError("oracle rejected its arguments")
+    return rm, rv
 
 
 def usage(rows, N, counts=None, lib=None):

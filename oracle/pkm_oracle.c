@@ -115,10 +115,11 @@ double pkmo_e4m3_to_f64(uint8_t bits)
     return sign ? -v : v;
 }
 
-/* Symmetric integer codes ("a good candidate for keeping in a lower
- * precision", the note after the code listing): int8 is an ordinary two's
- * complement byte; int4 is a two's complement nibble, two per byte, the
- * element with the even index in the low nibble. */
+/* Symmetric integer codes (the note after the code listing: the value
+ * table is the layer's whole memory cost, so it is the part worth storing
+ * in fewer bits): int8 is an ordinary two's complement byte; int4 is a two's
+ * complement nibble, two per byte, the element with the even index in the
+ * low nibble. */
 double pkmo_int8_to_f64(int8_t code) { return (double)code; }
 
 double pkmo_int4_to_f64(uint8_t nibble)
@@ -350,6 +351,25 @@ int pkmo_run(const pkmo_model *M, int64_t B, const float *x, int kk, double *out
         pthread_join(th[t], NULL);
     free(th);
     free(jobs);
+    return 0;
+}
+
+/*
+ * Steps 1-3 alone: scores [B][H][2][n] of each token's two query halves
+ * against their subkey sets, the same arithmetic pkmo_run ranks.
+ * Returns 0, or -1 on bad arguments.
+ */
+int pkmo_scores(const pkmo_model *M, int64_t B, const float *x, double *scores)
+{
+    if (!M || !x || !scores || B < 0 || (M->D & 1) || M->H < 1) return -1;
+    const int D = M->D, H = M->H, n = M->n;
+    double *q = (double *)malloc(sizeof(double) * (size_t)D);
+    for (int64_t b = 0; b < B; ++b)
+        for (int h = 0; h < H; ++h) {
+            pkmo_project_bn(M, h, x + b * D, q);
+            pkmo_half_scores(M, h, q, scores + (b * H + h) * 2 * (int64_t)n);
+        }
+    free(q);
     return 0;
 }
 
@@ -868,6 +888,31 @@ int pkmo_backward_batch_stats(const pkmo_model *M, int64_t B, const float *x, co
     }
     free(qhat); free(xhat); free(dqh); free(dtv); free(wv); free(rows); free(s); free(t0); free(t1);
     free(i0); free(i1); free(tp); free(g); free(m1); free(m2);
+    return 0;
+}
+
+/*
+ * The running statistics a training-mode BatchNorm1d keeps for inference
+ * (the module's running_mean / running_var buffers; "Product-Key Memory",
+ * §Keeping the memory in use, and the code listing's BatchNorm1d): after a
+ * batch of B >= 2 tokens with statistics mean / var (var biased, as the
+ * normalisation uses it), each running value moves a fraction `momentum`
+ * of the way to the batch's value; the variance it moves to is the
+ * unbiased estimate var * B / (B - 1).
+ *   rmean = (1 - momentum) rmean + momentum mean
+ *   rvar  = (1 - momentum) rvar  + momentum var B / (B - 1)
+ * count entries of each array, fp64, updated in place.  Returns 0, or -1
+ * on bad arguments.
+ */
+int pkmo_running_update(int64_t count, int64_t B, double momentum, const double *mean, const double *var,
+                        double *rmean, double *rvar)
+{
+    if (count < 0 || B < 2 || !(momentum >= 0.0 && momentum <= 1.0) || !mean || !var || !rmean || !rvar) return -1;
+    const double unbias = (double)B / (double)(B - 1);
+    for (int64_t i = 0; i < count; ++i) {
+        rmean[i] = (1.0 - momentum) * rmean[i] + momentum * mean[i];
+        rvar[i] = (1.0 - momentum) * rvar[i] + momentum * (var[i] * unbias);
+    }
     return 0;
 }
 

@@ -15,10 +15,21 @@ build, or a variant passed as ``lib``) disagrees with:
     operation counts (tests/golden/op_counts.json);
   - special cases: k = n_keys (every key is a candidate), k = 1 (argmax of
     each half), exact integer ties (lower index wins).
+The stand-alone steps are pinned on their own:
+  - select (steps 4-6 from given half scores) against a brute force over
+    the whole n x n grid of half-score sums (the score of key (a, b) is
+    s0[a] + s1[b], §Factorising the key space), ranked by (score desc,
+    flat index asc), and torch's softmax; and bit for bit against run() on
+    the oracle's own half scores;
+  - gather (step 7) against torch's embedding_bag(mode="sum",
+    per_sample_weights) on every table format, into a garbage-filled output;
+  - the running-statistics update against the buffers torch's
+    F.batch_norm(training=True, momentum=m) updates in place.
 The backward direction (gradients of sum(dout * out)) is pinned to:
-  - torch autograd in fp64 through the page's code listing composed per
-    head (Linear, BatchNorm1d in eval mode, chunk, the two subkey products,
-    topk of each half, the k x k grid, topk, softmax, embedding_bag);
+  - torch autograd in fp64 through the method written from its definition,
+    per head and summed over heads: Linear, BatchNorm1d, the score of
+    every one of the n^2 concatenated keys, the best k of them, softmax,
+    and the weighted sum of their value rows;
   - central finite differences of the oracle's own forward output, with
     steps that are exact in fp32 and small enough not to change the winners;
   - identities: the value gradient sums to H * sum_b dout_b (each head's
@@ -276,13 +287,119 @@ def pin_op_counts(lib=None):
     assert r["idx"].shape[-1] == k
 
 
+def _brute_force_select(s, k):
+    """Top-k of the full n x n grid of half-score sums for one (token,
+    head): s [2, n] fp64.  Returns flat indices, scores, softmax weights."""
+    n = s.shape[1]
+    grid = (s[0][:, None] + s[1][None, :]).reshape(-1)  # cell a*n + b holds s0[a] + s1[b]
+    flat = np.arange(n * n)
+    order = np.lexsort((flat, -grid))[:k]  # score desc, then flat index asc
+    top = grid[order]
+    return order.astype(np.int32), top, torch.softmax(torch.from_numpy(top), -1).numpy()
+
+
+def pin_select(lib=None):
+    """select() against the brute force over the whole grid: random fp64
+    scores (every k up to n at a small n, and a larger n), exact integer
+    ties; then bit for bit against run() on the oracle's own half scores."""
+    rng = np.random.default_rng(21)
+    cases = [(rng.standard_normal((30, 2, 9)), k) for k in range(1, 10)]
+    cases.append((rng.standard_normal((25, 2, 70)) * 3.0, 16))
+    cases.append((rng.integers(-2, 3, (40, 2, 12)).astype(np.float64), 5))  # heavy exact ties
+    cases.append((rng.integers(-1, 2, (20, 2, 6)).astype(np.float64), 6))
+    for s, k in cases:
+        idx, top, w = oracle.select(s, k, lib=lib)
+        for p in range(s.shape[0]):
+            ri, rt, rw = _brute_force_select(s[p], k)
+            assert (idx[p] == ri).all(), f"select winners differ (k={k}, row {p})"
+            assert (top[p] == rt).all(), "select scores differ"
+            np.testing.assert_allclose(w[p], rw, rtol=1e-13, atol=1e-300)
+    # the same function on the scores the lookup ranks: bit for bit
+    wl = synthetic.Workload("sel", 20, 64, 3, 24, 7, "f32", "random")
+    params = synthetic.make_params(wl, 11, with_values=False)
+    model = _model(params, wl.k, wl.table)
+    x = synthetic.make_x(wl, 11)
+    sc = oracle.scores(model, x, lib=lib)
+    idx, top, w = oracle.select(sc, wl.k, lib=lib)
+    r = oracle.run(model, x, want=("idx", "top", "w"), lib=lib)
+    assert (idx == r["idx"]).all() and (top == r["top"]).all() and (w == r["w"]).all(), "select differs from run"
+    # half scores against library products of the oracle's own q^
+    qh = oracle.run(model, x, want=("qhat",), lib=lib)["qhat"]
+    half = wl.D // 2
+    for h in range(wl.H):
+        for p in range(2):
+            ref = qh[:, h, p * half:(p + 1) * half] @ params["subkeys"][h, p].astype(np.float64).T
+            np.testing.assert_allclose(sc[:, h, p], ref, rtol=1e-12, atol=1e-12)
+
+
+def pin_gather(lib=None):
+    """gather() against torch's embedding_bag(mode="sum",
+    per_sample_weights) in fp64 on every table format: repeated rows inside
+    and across bags, one-row bags, an output buffer full of garbage (every
+    entry must be overwritten), and an empty batch."""
+    rng = np.random.default_rng(31)
+    for t, table in enumerate(("f32", "bf16", "e4m3", "int8", "int4")):
+        wl = synthetic.Workload("gat", 1, 64, 1, 8, 2, table, "unit")
+        params = synthetic.make_params(wl, 40 + t)
+        model = _model(params, wl.k, table)
+        vals = dequant_table(params["values"], params.get("scale"), table)
+        for B, R in ((17, 9), (5, 1), (0, 4)):
+            rows = rng.integers(0, wl.N, (B, R)).astype(np.int32)
+            if B and R > 2:
+                rows[0, 1] = rows[0, 0]  # a repeat inside a bag
+                rows[1, :] = rows[0, 0]  # a bag of one row R times
+            w = rng.standard_normal((B, R))
+            out = np.full((B, wl.D), np.nan)
+            got = oracle.gather(model, rows, w, out=out, lib=lib)
+            ref = F.embedding_bag(torch.from_numpy(rows.astype(np.int64)), vals, mode="sum",
+                                  per_sample_weights=torch.from_numpy(w)).numpy()
+            assert got.shape == (B, wl.D)
+            np.testing.assert_allclose(got, ref, rtol=1e-13, atol=1e-15)
+
+
+def pin_running_update(lib=None):
+    """The running statistics after a training-mode batch: the oracle's
+    update (from the oracle's own batch statistics, or from given ones)
+    against the buffers torch's F.batch_norm(training=True, momentum=m)
+    updates in place, for several batch sizes and momenta."""
+    rng = np.random.default_rng(51)
+    for B, m in ((2, 0.1), (7, 0.37), (100, 0.1), (33, 0.0), (5, 1.0)):
+        q = rng.standard_normal((B, 48)) * rng.uniform(0.2, 3.0, 48) + rng.normal(0, 2, 48)
+        rm0, rv0 = rng.normal(0, 1, 48), rng.uniform(0.5, 2.0, 48)
+        trm, trv = torch.from_numpy(rm0.copy()), torch.from_numpy(rv0.copy())
+        F.batch_norm(torch.from_numpy(q), trm, trv, training=True, momentum=m)
+        rm, rv = oracle.running_update(rm0, rv0, q.mean(0), q.var(0), B, m, lib=lib)
+        np.testing.assert_allclose(rm, trm.numpy(), rtol=1e-14, atol=1e-15)
+        np.testing.assert_allclose(rv, trv.numpy(), rtol=1e-14, atol=1e-15)
+    # chained with the oracle's batch statistics of a lookup's queries
+    wl = synthetic.Workload("run", 12, 32, 2, 8, 3, "f32", "random")
+    params = synthetic.make_params(wl, 52, with_values=False)
+    model = _model(params, wl.k, wl.table)
+    x = synthetic.make_x(wl, 52)
+    mean, var = oracle.batch_stats(model, x, lib=lib)
+    rm0 = rng.normal(0, 1, (wl.H, wl.D))
+    rv0 = rng.uniform(0.5, 2.0, (wl.H, wl.D))
+    rm, rv = oracle.running_update(rm0, rv0, mean, var, wl.B, 0.1, lib=lib)
+    xt = torch.from_numpy(x).double()
+    for h in range(wl.H):
+        trm, trv = torch.from_numpy(rm0[h].copy()), torch.from_numpy(rv0[h].copy())
+        F.batch_norm(F.linear(xt, torch.from_numpy(params["wq"][h]).double()), trm, trv, training=True, momentum=0.1)
+        np.testing.assert_allclose(rm[h], trm.numpy(), rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(rv[h], trv.numpy(), rtol=1e-12, atol=1e-12)
+
+
 # ------------------------------------------------------------------ backward
 
 def module_autograd(params, x, dout, k, table="f32", eps=1e-5, training=False):
     """Gradients of sum(dout * out) by torch autograd in fp64 through the
-    page's code listing, composed per head and summed over heads.  With
-    training=True BatchNorm1d normalises with the batch's statistics (and
-    the result holds "out", "mean" and "var" too)."""
+    method written from its definition, per head and summed over heads:
+    q^ = BatchNorm1d(Linear(x)); every key (a, b) is the concatenation
+    [c0_a; c1_b] ("Product-Key Memory", §Factorising the key space) and
+    gets the score q^ . key; the best k scores of all n^2 keys (score desc,
+    flat index a*n + b asc) are the winners; their softmax weights the sum
+    of their value rows.  Gradients reach the subkeys through the keys they
+    form.  With training=True BatchNorm1d normalises with the batch's
+    statistics (and the result holds "out", "mean" and "var" too)."""
     leaf = lambda a: torch.from_numpy(np.ascontiguousarray(a)).double().requires_grad_()  # noqa: E731
     wq, gamma, beta, sub = leaf(params["wq"]), leaf(params["gamma"]), leaf(params["beta"]), leaf(params["subkeys"])
     vals = dequant_table(params["values"], params.get("scale"), table).clone().requires_grad_()
@@ -301,14 +418,13 @@ def module_autograd(params, x, dout, k, table="f32", eps=1e-5, training=False):
             qh = F.batch_norm(q, None, None, gamma[h], beta[h], training=True, eps=eps)
         else:
             qh = F.batch_norm(q, mean[h], var[h], gamma[h], beta[h], training=False, eps=eps)
-        q1, q2 = qh.chunk(2, dim=1)
-        s1, i1 = (q1 @ sub[h, 0].T).topk(k, dim=1)
-        s2, i2 = (q2 @ sub[h, 1].T).topk(k, dim=1)
-        all_scores = (s1[:, :, None] + s2[:, None, :]).reshape(-1, k * k)
-        all_idx = (i1[:, :, None] * n + i2[:, None, :]).reshape(-1, k * k)
-        top, pos = all_scores.topk(k, dim=1)
-        w = top.softmax(dim=-1)
-        out = out + F.embedding_bag(all_idx.gather(1, pos), vals, per_sample_weights=w, mode="sum")
+        first = torch.arange(n).repeat_interleave(n)  # key a*n + b = [c0_a; c1_b]
+        second = torch.arange(n).repeat(n)
+        keys = torch.cat([sub[h, 0][first], sub[h, 1][second]], dim=1)
+        scores = qh @ keys.T
+        win = torch.sort(scores.detach(), dim=1, descending=True, stable=True).indices[:, :k]
+        w = torch.softmax(scores.gather(1, win), dim=-1)
+        out = out + (w[:, :, None] * vals[win]).sum(dim=1)
     (out * torch.from_numpy(dout).double()).sum().backward()
     res = {"dx": xt.grad.numpy(), "dwq": wq.grad.numpy(), "dgamma": gamma.grad.numpy(),
            "dbeta": beta.grad.numpy(), "dsub": sub.grad.numpy(), "dval": vals.grad.numpy()}
@@ -329,7 +445,7 @@ def backward_case(wl, seed=0, gamma_beta=False):
 
 
 def pin_backward_autograd(wl, seed=0, gamma_beta=False, lib=None):
-    """Oracle gradients == torch autograd through the page's module."""
+    """Oracle gradients == torch autograd through the method's definition."""
     params, x, dout = backward_case(wl, seed, gamma_beta)
     g = oracle.backward(_model(params, wl.k, wl.table), x, dout, lib=lib)
     ref = module_autograd(params, x, dout, wl.k, wl.table)
@@ -406,7 +522,7 @@ def pin_backward_identities(lib=None):
 def pin_batch_stats_autograd(wl, seed=0, lib=None):
     """Batch-statistics BN: the oracle's statistics, forward output and
     gradients == torch (F.batch_norm(training=True)) in fp64 through the
-    page's module."""
+    method's definition."""
     params, x, dout = backward_case(wl, seed, gamma_beta=True)
     model = _model(params, wl.k, wl.table)
     mean, var = oracle.batch_stats(model, x, lib=lib)

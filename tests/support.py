@@ -35,6 +35,19 @@ def key_l1_mass(wl, params, qhat, flat, h):
     return float(np.abs(qhat[:half]) @ np.abs(c0) + np.abs(qhat[half:]) @ np.abs(c1))
 
 
+def taus(wl, params, qhat, flat):
+    """tau for every (token, head) from q^ [B, H, D] and the flat row of
+    its k-th winner [B, H] (vectorised key_l1_mass)."""
+    half, n = wl.D // 2, wl.n
+    flat = np.asarray(flat, np.int64)
+    heads = np.arange(wl.H)[None, :]
+    c0 = np.abs(params["subkeys"][heads, 0, flat // n]).astype(np.float64)  # [B, H, D/2]
+    c1 = np.abs(params["subkeys"][heads, 1, flat % n]).astype(np.float64)
+    q = np.abs(qhat)
+    mass = np.einsum("bhd,bhd->bh", q[..., :half], c0) + np.einsum("bhd,bhd->bh", q[..., half:], c1)
+    return np.maximum(TAU_ABS, TAU_REL * mass)
+
+
 def gaps_and_tau(wl, params, x, model=None):
     """Per (token, head): fp64 gap between the k-th and (k+1)-th full scores,
     and the tau it must clear.  Both [B, H]."""
@@ -49,27 +62,31 @@ def gaps_and_tau(wl, params, x, model=None):
 
         r = pins.flat_search(params, x, k + 1, with_values=False)
     gap = r["top"][:, :, k - 1] - r["top"][:, :, k]
-    B = x.shape[0]
-    tau = np.empty((B, wl.H))
-    for b in range(B):
-        for h in range(wl.H):
-            tau[b, h] = max(TAU_ABS, TAU_REL * key_l1_mass(wl, params, r["qhat"][b, h], r["idx"][b, h, k - 1], h))
-    return gap, tau
+    return gap, taus(wl, params, r["qhat"], r["idx"][:, :, k - 1])
 
 
-def gap_clean(wl, params, x, tokens=None, seed=0, max_attempts=60):
+def gap_clean(wl, params, x, tokens=None, seed=0, max_attempts=60, want_tau=False, chunk=4096):
     """Re-draw rows of x (in place) until every listed token clears tau on
-    every head.  Returns the per-token attempt counts."""
+    every head.  Returns the per-token attempt counts (and, with want_tau,
+    the tau [B, H] of the final draw for the listed tokens; NaN elsewhere).
+    The oracle runs over at most `chunk` tokens at a time."""
     model = model_for(wl, params)
     todo = np.arange(x.shape[0]) if tokens is None else np.asarray(tokens)
     attempts = np.zeros(x.shape[0], dtype=np.int64)
-    if wl.k >= wl.N:
-        return attempts  # no (k+1)-th key: every key is a winner
+    tau_all = np.full((x.shape[0], wl.H), np.nan)
+    if wl.k >= wl.N:  # no (k+1)-th key: every key is a winner
+        tau_all[todo] = TAU_ABS
+        return (attempts, tau_all) if want_tau else attempts
     for _ in range(max_attempts):
-        gap, tau = gaps_and_tau(wl, params, x[todo], model)
-        bad = todo[(gap < tau).any(axis=1)]
+        bad = []
+        for c0 in range(0, todo.size, chunk):
+            part = todo[c0:c0 + chunk]
+            gap, tau = gaps_and_tau(wl, params, x[part], model)
+            tau_all[part] = tau
+            bad.append(part[(gap < tau).any(axis=1)])
+        bad = np.concatenate(bad) if bad else todo[:0]
         if bad.size == 0:
-            return attempts
+            return (attempts, tau_all) if want_tau else attempts
         for b in bad:
             attempts[b] += 1
             x[b] = synthetic.redraw_row(wl, seed, b, attempts[b])
@@ -89,10 +106,7 @@ def gap_clean_batch_stats(wl, params, x, seed=0, max_rounds=60):
         mean, var = oracle.batch_stats(model, x)
         r = oracle.run_batch_stats(model, x, mean, var, kk=k + 1, want=("top", "idx", "qhat"))
         gap = r["top"][:, :, k - 1] - r["top"][:, :, k]
-        tau = np.empty((x.shape[0], wl.H))
-        for b in range(x.shape[0]):
-            for h in range(wl.H):
-                tau[b, h] = max(TAU_ABS, TAU_REL * key_l1_mass(wl, params, r["qhat"][b, h], r["idx"][b, h, k - 1], h))
+        tau = taus(wl, params, r["qhat"], r["idx"][:, :, k - 1])
         bad = np.nonzero((gap < tau).any(axis=1))[0]
         if bad.size == 0:
             return mean, var, tau

@@ -7,7 +7,8 @@ Inputs are gap-clean for the batch-statistics lookup (tests/support.py:
 re-drawing a token moves every token's statistics, so the whole batch is
 measured again after each round).  Statistics: |mean - ref| within 1e-5 of
 the column's standard deviation, var within 1e-4 relative (fp32 sums of B
-values).  Indices, outputs and weights: the lookup's rules and tolerances.
+values); the running statistics within 1e-5 of the oracle's update (pinned
+to the buffers torch's F.batch_norm(training=True) updates).  Indices, outputs and weights: the lookup's rules and tolerances.
 Gradients: each tensor within 1e-4 of its largest entry, dx per token
 within 1e-4 of max(the token's largest entry, the batch median of that) --
 as for the running-statistics backward.
@@ -68,8 +69,7 @@ def run_case(torch, wl, seed, backward=True, running=True, max_batch=None):
     assert support.rel_rowmax_err(out, ref["out"]).max() <= tol
     if running:
         rm, rv = (t.cpu().numpy() for t in run)
-        want_m = 0.9 * rm0 + 0.1 * mean
-        want_v = 0.9 * rv0 + 0.1 * var * wl.B / (wl.B - 1)
+        want_m, want_v = oracle.running_update(rm0, rv0, mean, var, wl.B, 0.1)
         assert np.abs(rm - want_m).max() <= 1e-5 * (np.abs(want_m).max() + 1)
         assert np.abs(rv - want_v).max() <= 1e-5 * np.abs(want_v).max()
     if not backward:

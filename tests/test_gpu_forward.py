@@ -31,12 +31,14 @@ def torch():
     return t
 
 
-def compare(wl, params, x, out, idx, w, tokens=None):
-    """Oracle on the listed tokens (all by default) vs the GPU results."""
+def compare(wl, params, x, out, idx, w, tokens=None, tau=None):
+    """Oracle on the listed tokens (all by default) vs the GPU results; tau
+    [len(tokens), H] as the gap-clean draw measured it (else measured here)."""
     tokens = np.arange(x.shape[0]) if tokens is None else np.asarray(tokens)
     model = support.model_for(wl, params)
     r = oracle.run(model, x[tokens], want=("out", "idx", "top", "w"))
-    _, tau = support.gaps_and_tau(wl, params, x[tokens], model)
+    if tau is None:
+        _, tau = support.gaps_and_tau(wl, params, x[tokens], model)
     support.check_indices(idx[tokens], r["idx"], r["top"], tau)
     tol = TOL[wl.table]
     wm = support.weights_by_index(idx[tokens], w[tokens], r["idx"])
@@ -201,26 +203,48 @@ def test_empty_batch_and_argument_errors(torch):
         mem.forward(P, torch.zeros((4, wl.D + 64), device=support.device()))
 
 
-# Full-size workloads: the GPU runs every token; the oracle checks a sample
-# (the first and last tokens, chunk edges and a spread in between), each
-# re-drawn until gap-clean; every token is checked against the invariants.
-def _sample(B):
-    s = set([0, 1, B - 1, B // 2, 16383, 16384]) | set(np.linspace(0, B - 1, 26).astype(int).tolist())
-    return np.array(sorted(t for t in s if 0 <= t < B))
+# Full-size workloads: every token is re-drawn until gap-clean, the GPU
+# looks up the whole batch in one call (the configuration the benchmark
+# times), and every token is compared with the oracle, in parts of at most
+# 8192 tokens per test so that each test stays well inside a minute of
+# oracle time.
+FULL_PART = 8192
+_FULL = {}
+
+
+def _full_size(name):
+    """(wl, params, x, tau, out, idx, w) of a full-size workload, built once
+    per workload (the previous one is dropped)."""
+    if name not in _FULL:
+        _FULL.clear()
+        wl = synthetic.WORKLOADS[name]
+        print(f"[cpu] {name}: drawing inputs", flush=True)
+        params = synthetic.make_params(wl)
+        x = synthetic.make_x(wl)
+        print(f"[cpu] {name}: gap-clean draw of all {wl.B} tokens", flush=True)
+        attempts, tau = support.gap_clean(wl, params, x, want_tau=True)
+        print(f"[cpu] {name}: {(attempts > 0).sum()} tokens re-drawn", flush=True)
+        out, idx, w = support.gpu_forward(wl, params, x, max_batch=wl.B)
+        invariants(wl, idx, w)
+        _FULL[name] = (wl, params, x, tau, out, idx, w)
+    return _FULL[name]
+
+
+def _full_size_parts():
+    for name in ("default", "default_int8", "default_int4", "large_memory", "large_batch"):
+        B = synthetic.WORKLOADS[name].B
+        for t0 in range(0, B, FULL_PART):
+            yield name, t0, min(B, t0 + FULL_PART)
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("name", ["default", "large_batch", "large_memory", "default_int8", "default_int4"])
-def test_forward_full_size_sampled(torch, name):
-    wl = synthetic.WORKLOADS[name]
-    params = synthetic.make_params(wl)
-    x = synthetic.make_x(wl)
-    tokens = _sample(wl.B)
-    support.gap_clean(wl, params, x, tokens=tokens)
-    out, idx, w = support.gpu_forward(wl, params, x)
-    invariants(wl, idx, w)
-    err = compare(wl, params, x, out, idx, w, tokens=tokens)
-    print(f"{name}: max row error {err.max():.3g} over {len(tokens)} sampled tokens", flush=True)
+@pytest.mark.parametrize("name,t0,t1", list(_full_size_parts()), ids=lambda v: str(v))
+def test_forward_full_size_every_token(torch, name, t0, t1):
+    wl, params, x, tau, out, idx, w = _full_size(name)
+    tokens = np.arange(t0, t1)
+    print(f"[cpu] {name}: oracle on tokens {t0}..{t1 - 1}", flush=True)
+    err = compare(wl, params, x, out, idx, w, tokens=tokens, tau=tau[tokens])
+    print(f"{name} tokens {t0}..{t1 - 1}: max row error {err.max():.3g}", flush=True)
 
 
 def test_usage_counts(torch):

@@ -38,6 +38,18 @@ def test_flat_search_quantised_tables(table):
     pins.pin_against_flat_search(wl, seed=2)
 
 
+def test_select_against_brute_force_grid():
+    pins.pin_select()
+
+
+def test_gather_against_embedding_bag():
+    pins.pin_gather()
+
+
+def test_running_update_against_torch():
+    pins.pin_running_update()
+
+
 def test_integer_ties_every_k():
     pins.pin_integer_ties()
 

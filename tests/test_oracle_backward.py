@@ -1,5 +1,6 @@
 """CPU: the oracle's backward direction against its pins (tests/pins.py):
-torch autograd through the page's module, finite differences, identities."""
+torch autograd through the method's definition, finite differences,
+identities."""
 import pytest
 
 import synthetic

@@ -33,6 +33,18 @@ MUTATIONS = {
     "int4_nibble_order": ("(uint8_t)(d & 1 ? byte >> 4 : byte)", "(uint8_t)(d & 1 ? byte : byte >> 4)"),
     "candidate_count": ("    return c;\n}", "    return c - 1;\n}"),
     "half_topk_from_wrong_row": ("pkmo_topk_sorted(n, s + n, kk, t1, i1);", "pkmo_topk_sorted(n, s, kk, t1, i1);"),
+    # stand-alone steps
+    "select_half1_from_half0": ("        pkmo_topk_sorted(n, s + n, k, t1, i1);\n        pkmo_candidates_topk(n, k, t0, i0, t1, i1, k, tp, fl);",
+                                "        pkmo_topk_sorted(n, s, k, t1, i1);\n        pkmo_candidates_topk(n, k, t0, i0, t1, i1, k, tp, fl);"),
+    "select_softmax_of_half0": ("if (w) pkmo_softmax(k, tp, w + p * k);", "if (w) pkmo_softmax(k, t0, w + p * k);"),
+    "gather_out_not_cleared": ("            out[b * M->D + d] = 0.0;\n        pkmo_gather_add", "        pkmo_gather_add"),
+    "gather_rows_of_first_bag": ("pkmo_gather_add(M, R, rows + b * R, w + b * R, out + b * M->D);",
+                                 "pkmo_gather_add(M, R, rows, w + b * R, out + b * M->D);"),
+    "scores_second_half_from_first_set": ("const float *c = M->subkeys + (((int64_t)h * 2 + p) * n + j) * half;",
+                                          "const float *c = M->subkeys + (((int64_t)h * 2 + 0) * n + j) * half;"),
+    "running_var_biased": ("momentum * (var[i] * unbias);", "momentum * var[i];"),
+    "running_momentum_reversed": ("rmean[i] = (1.0 - momentum) * rmean[i] + momentum * mean[i];",
+                                  "rmean[i] = momentum * rmean[i] + (1.0 - momentum) * mean[i];"),
     # backward direction
     "bwd_softmax_no_centering": ("dtj[j] = wj[j] * (g[j] - wg);", "dtj[j] = wj[j] * g[j];"),
     "bwd_dqhat_halves_swapped": ("dqh[half + d] += dtj[j] * (double)c1[d];", "dqh[half + d] += dtj[j] * (double)c0[d];"),
@@ -54,6 +66,9 @@ MUTATIONS = {
 }
 
 PINS = [
+    pins.pin_select,
+    pins.pin_gather,
+    pins.pin_running_update,
     pins.pin_hand_example,
     pins.pin_codecs,
     pins.pin_integer_ties,
