@@ -147,6 +147,27 @@ void pkm_destroy(pkm_ctx *ctx);
 pkm_status pkm_forward(pkm_ctx *ctx, const pkm_params *p, int64_t B, const float *x, float *out, int32_t *idx,
                        float *weights, void *stream);
 
+/* The whole lookup (a1-a7) without a context and without allocating: for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * serving loops that must not call hipMalloc, harnesses that forbid it).
+ * Same arguments, results and errors as pkm_forward, with cfg in place of a
+ * context.  The workspace is a static device array of 128 MiB inside the
+ * library, one per GPU, held from the first call on that GPU until the
+ * process ends; nothing is allocated or freed by this call, by the runtime
+ * or by any library.
+ *   cfg->max_batch  the most tokens per chunk; the call works in the largest
+ *                   chunk (at most this) whose workspace fits the array (a
+ *                   multiple of 256 tokens from 256 on; about 2560 tokens
+ *                   at D = 1024, H = 4, n_keys = 1024)
+ * PKM_E_UNSUPPORTED if the workspace of a single token does not fit the
+ * array, or if the device is not gfx950 (checked on the first call on each
+ * device).  Every call on one GPU uses that GPU's single array, which keeps
+ * the last call's contents (each call rewrites what it reads): calls that
+ * overlap on one GPU, on different streams or from different threads,
+ * race and give undefined results; serialise them. */
+pkm_status pkm_forward_noalloc(const pkm_config *cfg, const pkm_params *p, int64_t B, const float *x, float *out,
+                               int32_t *idx, float *weights, void *stream);
+
 /* Steps a1-a2 only: qhat [B, H, D] fp32 = BN_h(Wq[h] . x[b]).  Uses wq and
  * the four BN arrays of p, and the context's workspace for the contraction's
  * row exponents (so, like pkm_forward, one stream per context at a time);

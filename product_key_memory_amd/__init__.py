@@ -10,7 +10,8 @@ streams, nothing else.
 """
 from ._binding import (  # noqa: F401
     EXPORTS, LIB_PATH, PKM_E_ARG, PKM_E_DEVICE, PKM_E_NOMEM, PKM_E_UNSUPPORTED, PKM_OK, SCALED, VALUE_TYPES, Config,
-    Memory, Params, PkmError, config_check, last_error, load_library, make_config, status_str, workspace_bytes,
+    Memory, Params, PkmError, config_check, forward_noalloc, last_error, load_library, make_config, status_str,
+    workspace_bytes,
 )
 
 

@@ -19,7 +19,7 @@ EXPORTS = (
     "pkm_config_check", "pkm_workspace_bytes", "pkm_create", "pkm_destroy", "pkm_forward", "pkm_query",
     "pkm_score", "pkm_select", "pkm_gather", "pkm_flat_workspace_bytes", "pkm_flat_search",
     "pkm_backward_workspace_bytes", "pkm_backward", "pkm_forward_batch_stats", "pkm_backward_batch_stats",
-    "pkm_usage", "pkm_status_str", "pkm_last_error",
+    "pkm_usage", "pkm_status_str", "pkm_last_error", "pkm_forward_noalloc",
 )
 
 
@@ -61,6 +61,7 @@ def load_library(path=LIB_PATH):
         "pkm_create": (ctypes.c_int, [cfg_p, ctypes.POINTER(vp)]),
         "pkm_destroy": (None, [vp]),
         "pkm_forward": (ctypes.c_int, [vp, par_p, i64, vp, vp, vp, vp, vp]),
+        "pkm_forward_noalloc": (ctypes.c_int, [cfg_p, par_p, i64, vp, vp, vp, vp, vp]),
         "pkm_query": (ctypes.c_int, [vp, par_p, i64, vp, vp, vp]),
         "pkm_score": (ctypes.c_int, [vp, par_p, i64, vp, vp, vp]),
         "pkm_select": (ctypes.c_int, [vp, i64, vp, vp, vp, vp]),
@@ -176,6 +177,24 @@ class Params:
 
     def __getitem__(self, name):
         return self.tensors[name]
+
+
+def forward_noalloc(cfg, params, x, out, idx=None, weights=None, stream=None):
+    """The whole lookup through pkm_forward_noalloc: no context, and nothing
+    allocated by the library or here -- out (and idx / weights, if wanted)
+    are the caller's tensors.  cfg: a Config (its max_batch caps the chunk).
+    Calls on one GPU share the library's scratch array: do not overlap them."""
+    B = x.shape[0]
+    H, D, k = cfg.heads, cfg.dim, cfg.k
+    dev = params["wq"].device
+    _expect(x, "x", (B, D), "float32", dev)
+    _expect(out, "out", (B, D), "float32", dev)
+    for t, name, dt in ((idx, "idx", "int32"), (weights, "weights", "float32")):
+        if t is not None:
+            _expect(t, name, (B, H, k), dt, dev)
+    _check(load_library().pkm_forward_noalloc(ctypes.byref(cfg), ctypes.byref(params.struct), B, _ptr(x), _ptr(out),
+                                              _ptr(idx), _ptr(weights), _stream_handle(stream)))
+    return out, idx, weights
 
 
 class Memory:

@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "pkm_internal.h"
@@ -20,7 +21,6 @@ struct pkm_ctx {
     float *scores;   // [max_batch, H, 2, n]
     int32_t *idx;    // [max_batch, H, k]
     float *weights;  // [max_batch, H, k]
-    uint32_t *stair; // staircase cells of the candidate grid for this k
     float *stat_part; // batch statistics: chunk means and squared deviations [2, chunks, H * D]
     int32_t *gemm_exp; // row exponents of the GEMM operands
     int64_t gemm_exp_ints;
@@ -73,9 +73,12 @@ int64_t forward_exp_ints(const pkm_config &c)
     return q > sc ? q : sc;
 }
 
-// Workspace pieces for one chunk of mb tokens; false on size overflow.
-constexpr int kPieces = 9;
-bool workspace_layout(const pkm_config &c, size_t sizes[kPieces])
+// Workspace pieces for one chunk of c.max_batch tokens: q^, scores, idx,
+// weights, the batch statistics' partial sums (only with batch_stats), the
+// GEMM row exponents, q^'s per-half maxima and the subkeys' row exponents.
+// False on size overflow.
+constexpr int kPieces = 8;
+bool workspace_layout(const pkm_config &c, size_t sizes[kPieces], bool batch_stats = true)
 {
     const double mb = (double)c.max_batch;
     const double total = mb * c.heads * ((double)c.dim + 2.0 * c.n_keys + 2.0 * c.k) * 4.0;
@@ -85,12 +88,30 @@ bool workspace_layout(const pkm_config &c, size_t sizes[kPieces])
     sizes[1] = round_up(m * H * 2 * (size_t)c.n_keys * sizeof(float));
     sizes[2] = round_up(m * H * (size_t)c.k * sizeof(int32_t));
     sizes[3] = round_up(m * H * (size_t)c.k * sizeof(float));
-    sizes[4] = round_up(pkm::kMaxStaircaseCells * sizeof(uint32_t));
-    sizes[5] = round_up((size_t)pkm::stat_part_floats(c.max_batch, H * c.dim) * sizeof(float));
-    sizes[6] = round_up((size_t)forward_exp_ints(c) * sizeof(int32_t));
-    sizes[7] = round_up(m * 2 * H * sizeof(uint32_t));
-    sizes[8] = round_up(2 * H * (size_t)c.n_keys * sizeof(int32_t));
+    sizes[4] = batch_stats ? round_up((size_t)pkm::stat_part_floats(c.max_batch, H * c.dim) * sizeof(float)) : 0;
+    sizes[5] = round_up((size_t)forward_exp_ints(c) * sizeof(int32_t));
+    sizes[6] = round_up(m * 2 * H * sizeof(uint32_t));
+    sizes[7] = round_up(2 * H * (size_t)c.n_keys * sizeof(int32_t));
     return true;
+}
+
+// Points the context's workspace pieces into w (laid out by
+// workspace_layout).
+void assign_workspace(pkm_ctx *ctx, char *w, const size_t sizes[kPieces])
+{
+    char *piece[kPieces];
+    piece[0] = w;
+    for (int i = 1; i < kPieces; ++i) piece[i] = piece[i - 1] + sizes[i - 1];
+    ctx->workspace = w;
+    ctx->qhat = reinterpret_cast<float *>(piece[0]);
+    ctx->scores = reinterpret_cast<float *>(piece[1]);
+    ctx->idx = reinterpret_cast<int32_t *>(piece[2]);
+    ctx->weights = reinterpret_cast<float *>(piece[3]);
+    ctx->stat_part = sizes[4] ? reinterpret_cast<float *>(piece[4]) : nullptr;
+    ctx->gemm_exp = reinterpret_cast<int32_t *>(piece[5]);
+    ctx->gemm_exp_ints = (int64_t)(sizes[5] / sizeof(int32_t));
+    ctx->qmax = reinterpret_cast<uint32_t *>(piece[6]);
+    ctx->sub_exp = reinterpret_cast<int32_t *>(piece[7]);
 }
 
 pkm_status check_config(const pkm_config *c)
@@ -385,6 +406,109 @@ pkm_status check_grads(const pkm_grads *g)
     return PKM_OK;
 }
 
+pkm_status check_forward_args(const pkm_config &c, const pkm_params *p, const float *x, const float *out,
+                              const int32_t *idx, const float *weights)
+{
+    pkm_status s;
+    if ((s = check_query_params(p)) || (s = need(p->subkeys, "subkeys")) || (s = check_value_params(c, p))) return s;
+    if ((s = need(x, "x")) || (s = need(out, "out"))) return s;
+    if ((idx && !aligned16(idx)) || (weights && !aligned16(weights)))
+        return fail(PKM_E_ARG, "idx / weights must be 16-byte aligned");
+    return PKM_OK;
+}
+
+// a1-a7 over B tokens in chunks of the context's max_batch, every chunk
+// through the context's workspace; launches only.
+pkm_status forward_chunks(const pkm_ctx *ctx, const pkm_params *p, int64_t B, const float *x, float *out,
+                          int32_t *idx, float *weights, hipStream_t st)
+{
+    pkm_status s;
+    const pkm_config &c = ctx->cfg;
+    const int64_t H = c.heads, D = c.dim, k = c.k;
+    for (int64_t b0 = 0; b0 < B; b0 += c.max_batch) {
+        const int64_t nb = B - b0 < c.max_batch ? B - b0 : c.max_batch;
+        int32_t *ci = idx ? idx + b0 * H * k : ctx->idx;
+        float *cw = weights ? weights + b0 * H * k : ctx->weights;
+        if ((s = run_query(ctx, p, nb, x + b0 * D, ctx->qhat, ctx->qmax, st))) return s;
+        if ((s = run_score(ctx, p, nb, ctx->qhat, ctx->scores, ctx->qmax, st))) return s;
+        if ((s = launched(pkm::launch_select(ctx->scores, nb, c.heads, c.n_keys, c.k, ci, cw, st), "select")))
+            return s;
+        if ((s = launched(pkm::launch_gather(p->values, p->value_scale, c.value_type, c.dim, c.n_keys * c.n_keys, nb,
+                                             (int)(H * k), ci, cw, out + b0 * D, st),
+                          "gather")))
+            return s;
+    }
+    return PKM_OK;
+}
+
+// ------------------------------------------------------------------ scratch
+//
+// The allocation-free forward (pkm_forward_noalloc) keeps its workspace in
+// this file-scope device array: every GPU the library runs on holds its own
+// copy for the life of the process.  In host code the array's name is not a
+// device address; its address on each device comes from hipGetSymbolAddress,
+// taken once per device with that device current, and only that address is
+// used afterwards.
+constexpr size_t kScratchBytes = (size_t)128 << 20;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mutex;
+char *g_scratch_ptr[kMaxDevices];  // scratch's address on each device, once taken
+
+pkm_status scratch_on_current_device(int *device, char **out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(PKM_E_DEVICE, "no HIP device: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(PKM_E_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess) return fail(PKM_E_DEVICE, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+        if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+            return fail(PKM_E_UNSUPPORTED, "device %d is %s; the kernels are built for gfx950", dev, prop.gcnArchName);
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            return fail(PKM_E_DEVICE, "address of the scratch array on device %d: %s", dev, hipGetErrorString(e));
+        }
+        g_scratch_ptr[dev] = static_cast<char *>(ptr);
+    }
+    *device = dev;
+    *out = g_scratch_ptr[dev];
+    return PKM_OK;
+}
+
+size_t noalloc_bytes(pkm_config c, int64_t mb)
+{
+    c.max_batch = mb;
+    size_t sizes[kPieces];
+    if (!workspace_layout(c, sizes, false)) return SIZE_MAX;
+    return total_bytes(sizes, kPieces);
+}
+
+// The chunk the allocation-free forward works in: the most tokens, at most
+// c.max_batch, whose workspace fits the scratch array (a multiple of 256
+// from 256 tokens on, the contractions' tile height).  Sets c.max_batch.
+pkm_status noalloc_chunk(pkm_config &c)
+{
+    const size_t one = noalloc_bytes(c, 1);
+    if (one > kScratchBytes)
+        return fail(PKM_E_UNSUPPORTED, "one token's workspace (%zu bytes) exceeds the %zu-byte scratch array", one,
+                    kScratchBytes);
+    int64_t lo = 1, hi = c.max_batch;  // the workspace grows with the chunk
+    while (lo < hi) {
+        const int64_t mid = lo + (hi - lo + 1) / 2;
+        if (noalloc_bytes(c, mid) <= kScratchBytes) lo = mid;
+        else hi = mid - 1;
+    }
+    c.max_batch = lo >= 256 ? lo / 256 * 256 : lo;
+    return PKM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -432,27 +556,7 @@ pkm_status pkm_create(const pkm_config *cfg, pkm_ctx **out)
     }
     ctx->cfg = *cfg;
     ctx->device = dev;
-    ctx->workspace = ws;
-    char *w = static_cast<char *>(ws);
-    ctx->qhat = reinterpret_cast<float *>(w);
-    ctx->scores = reinterpret_cast<float *>(w + sizes[0]);
-    ctx->idx = reinterpret_cast<int32_t *>(w + sizes[0] + sizes[1]);
-    ctx->weights = reinterpret_cast<float *>(w + sizes[0] + sizes[1] + sizes[2]);
-    ctx->stair = reinterpret_cast<uint32_t *>(w + sizes[0] + sizes[1] + sizes[2] + sizes[3]);
-    ctx->stat_part = reinterpret_cast<float *>(w + sizes[0] + sizes[1] + sizes[2] + sizes[3] + sizes[4]);
-    ctx->gemm_exp = reinterpret_cast<int32_t *>(w + sizes[0] + sizes[1] + sizes[2] + sizes[3] + sizes[4] + sizes[5]);
-    ctx->gemm_exp_ints = (int64_t)(sizes[6] / sizeof(int32_t));
-    ctx->qmax = reinterpret_cast<uint32_t *>(w + sizes[0] + sizes[1] + sizes[2] + sizes[3] + sizes[4] + sizes[5] +
-                                             sizes[6]);
-    ctx->sub_exp = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(ctx->qmax) + sizes[7]);
-    uint32_t stair[pkm::kMaxStaircaseCells] = {};
-    pkm::staircase_table(cfg->k, stair);
-    e = hipMemcpy(ctx->stair, stair, sizeof stair, hipMemcpyHostToDevice);
-    if (e != hipSuccess) {
-        (void)hipFree(ws);
-        delete ctx;
-        return fail(PKM_E_DEVICE, "uploading the candidate staircase: %s", hipGetErrorString(e));
-    }
+    assign_workspace(ctx, static_cast<char *>(ws), sizes);
     if (log_on())
         fprintf(stderr, "pkm: context on device %d (%s): D=%d H=%d n=%d k=%d values=%d max_batch=%lld workspace=%zu\n",
                 dev, prop.gcnArchName, cfg->dim, cfg->heads, cfg->n_keys, cfg->k, cfg->value_type,
@@ -474,26 +578,27 @@ pkm_status pkm_forward(pkm_ctx *ctx, const pkm_params *p, int64_t B, const float
     pkm_status s;
     if ((s = check_ctx(ctx)) || (s = check_batch(ctx->cfg, B))) return s;
     if (B == 0) return ok();
-    const pkm_config &c = ctx->cfg;
-    if ((s = check_query_params(p)) || (s = need(p->subkeys, "subkeys")) || (s = check_value_params(c, p))) return s;
-    if ((s = need(x, "x")) || (s = need(out, "out"))) return s;
-    if ((idx && !aligned16(idx)) || (weights && !aligned16(weights)))
-        return fail(PKM_E_ARG, "idx / weights must be 16-byte aligned");
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    const int64_t H = c.heads, D = c.dim, k = c.k;
-    for (int64_t b0 = 0; b0 < B; b0 += c.max_batch) {
-        const int64_t nb = B - b0 < c.max_batch ? B - b0 : c.max_batch;
-        int32_t *ci = idx ? idx + b0 * H * k : ctx->idx;
-        float *cw = weights ? weights + b0 * H * k : ctx->weights;
-        if ((s = run_query(ctx, p, nb, x + b0 * D, ctx->qhat, ctx->qmax, st))) return s;
-        if ((s = run_score(ctx, p, nb, ctx->qhat, ctx->scores, ctx->qmax, st))) return s;
-        if ((s = launched(pkm::launch_select(ctx->scores, nb, c.heads, c.n_keys, c.k, ctx->stair, ci, cw, st), "select")))
-            return s;
-        if ((s = launched(pkm::launch_gather(p->values, p->value_scale, c.value_type, c.dim, c.n_keys * c.n_keys, nb, (int)(H * k), ci, cw,
-                                             out + b0 * D, st),
-                          "gather")))
-            return s;
-    }
+    if ((s = check_forward_args(ctx->cfg, p, x, out, idx, weights))) return s;
+    if ((s = forward_chunks(ctx, p, B, x, out, idx, weights, static_cast<hipStream_t>(stream)))) return s;
+    return ok();
+}
+
+pkm_status pkm_forward_noalloc(const pkm_config *cfg, const pkm_params *p, int64_t B, const float *x, float *out,
+                               int32_t *idx, float *weights, void *stream)
+{
+    pkm_status s;
+    if ((s = check_config(cfg)) || (s = check_batch(*cfg, B))) return s;
+    pkm_ctx ctx{};
+    ctx.cfg = *cfg;
+    if ((s = noalloc_chunk(ctx.cfg))) return s;
+    if (B == 0) return ok();
+    if ((s = check_forward_args(ctx.cfg, p, x, out, idx, weights))) return s;
+    char *base = nullptr;
+    if ((s = scratch_on_current_device(&ctx.device, &base))) return s;
+    size_t sizes[kPieces];
+    workspace_layout(ctx.cfg, sizes, false);
+    assign_workspace(&ctx, base, sizes);
+    if ((s = forward_chunks(&ctx, p, B, x, out, idx, weights, static_cast<hipStream_t>(stream)))) return s;
     return ok();
 }
 
@@ -526,7 +631,7 @@ pkm_status pkm_select(pkm_ctx *ctx, int64_t B, const float *scores, int32_t *idx
     if (B == 0) return ok();
     if ((s = need(scores, "scores")) || (s = need(idx, "idx")) || (s = need(weights, "weights"))) return s;
     const pkm_config &c = ctx->cfg;
-    if ((s = launched(pkm::launch_select(scores, B, c.heads, c.n_keys, c.k, ctx->stair, idx, weights,
+    if ((s = launched(pkm::launch_select(scores, B, c.heads, c.n_keys, c.k, idx, weights,
                                          static_cast<hipStream_t>(stream)),
                       "select")))
         return s;
@@ -896,7 +1001,7 @@ pkm_status pkm_forward_batch_stats(pkm_ctx *ctx, const pkm_params *p, int64_t B,
                                            qmax, c.dim / 2, st),
                       "batch normalisation")) ||
         (s = run_score(ctx, p, B, ctx->qhat, ctx->scores, qmax, st)) ||
-        (s = launched(pkm::launch_select(ctx->scores, B, c.heads, c.n_keys, c.k, ctx->stair, ci, cw, st), "select")) ||
+        (s = launched(pkm::launch_select(ctx->scores, B, c.heads, c.n_keys, c.k, ci, cw, st), "select")) ||
         (s = launched(pkm::launch_gather(p->values, p->value_scale, c.value_type, c.dim, c.n_keys * c.n_keys, B,
                                          c.heads * c.k, ci, cw, out, st),
                       "gather")))

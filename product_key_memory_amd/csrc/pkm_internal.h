@@ -106,17 +106,16 @@ hipError_t launch_gemm_nt_f32_product(const GemmArgs &a, hipStream_t stream);
 
 // Per (token, head): exact top-k of each half's n scores, the exact top-k of
 // the k*k candidates and the softmax.  scores [B][H][2][n] -> idx, w
-// [B][H][k].  k <= 64, n <= 4096.  stair: the staircase_table(k) cells in
-// device memory.
-hipError_t launch_select(const float *scores, int64_t B, int H, int n, int k, const uint32_t *stair,
-                         int32_t *idx, float *w, hipStream_t stream);
+// [B][H][k].  k <= 64, n <= 4096.  The staircase of candidate cells the
+// kernel ranks first is a table in the library's device code (one row per
+// k), so the call needs no workspace.
+hipError_t launch_select(const float *scores, int64_t B, int H, int n, int k, int32_t *idx, float *w,
+                         hipStream_t stream);
 
-// The candidate cells (i, j) with (i+1)(j+1) <= k, packed (i << 16) | j in
-// row-major order: staircase_cells(k) entries (at most 280 for k <= 64),
-// then 0xFFFFFFFF up to kMaxStaircaseCells.
+// The candidate cells (i, j) with (i+1)(j+1) <= k: staircase_cells(k) of
+// them (at most 280 for k <= 64), padded to kMaxStaircaseCells per k.
 constexpr int kMaxStaircaseCells = 320;
 int staircase_cells(int k);
-void staircase_table(int k, uint32_t *out);
 
 // out[b][:] = sum_r w[b][r] * scale[row] * values[row][:], row = idx[b][r],
 // r < R, N table rows (rows are clamped into [0, N)).  value_type: 0 f32,

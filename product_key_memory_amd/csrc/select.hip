@@ -345,10 +345,30 @@ __device__ uint64_t full_grid_topk(int n, int k, float (*hs)[64], uint32_t (*hi)
     return wave_topk_rolled(key_of, id_of, slots, k, st, lane);
 }
 
+// The staircase cells of every k <= 64, fixed at compile time: row k - 1
+// holds the cells (i, j) with (i+1)(j+1) <= k, packed (i << 16) | j in
+// row-major order, then 0xFFFFFFFF up to kMaxStaircaseCells.
+struct StairTables {
+    uint32_t cell[64][kMaxStaircaseCells];
+};
+
+constexpr StairTables make_stair_tables()
+{
+    StairTables t{};
+    for (int k = 1; k <= 64; ++k) {
+        for (int c = 0; c < kMaxStaircaseCells; ++c) t.cell[k - 1][c] = 0xFFFFFFFFu;
+        int c = 0;
+        for (int i = 0; i < k; ++i)
+            for (int j = 0; (i + 1) * (j + 1) <= k; ++j) t.cell[k - 1][c++] = ((uint32_t)i << 16) | (uint32_t)j;
+    }
+    return t;
+}
+
+__device__ const StairTables kStairTables = make_stair_tables();
+
 template <int MH, bool VEC4>
 __global__ __launch_bounds__(64 * WAVES) void select_kernel(const float *__restrict__ scores, int64_t pairs, int n,
-                                                            int k, const uint32_t *__restrict__ stair,
-                                                            int stair_cells, int32_t *__restrict__ idx_out,
+                                                            int k, int32_t *__restrict__ idx_out,
                                                             float *__restrict__ w_out)
 {
     __shared__ Stage stage[WAVES];
@@ -366,8 +386,9 @@ __global__ __launch_bounds__(64 * WAVES) void select_kernel(const float *__restr
     half_topk<MH, VEC4>(scores + pair * 2 * (int64_t)n, n, k, stage[wv], hs, hi, lane);
     wave_sync_lds();
 
-    // a5 on the staircase: stair[c] = (i << 16) | j for c < stair_cells,
-    // 0xFFFFFFFF up to STAIR_SLOTS * 64 (loaded unconditionally)
+    // a5 on the staircase: stair[c] = (i << 16) | j for the staircase's
+    // cells, 0xFFFFFFFF up to STAIR_SLOTS * 64 (loaded unconditionally)
+    const uint32_t *stair = kStairTables.cell[k - 1];
     const auto cell_of = [=](int t) { return stair[t * 64 + lane]; };
     uint32_t cell[STAIR_SLOTS], key[STAIR_SLOTS], id[STAIR_SLOTS];
 #pragma unroll
@@ -601,17 +622,14 @@ __global__ __launch_bounds__(64 * WAVES) void flat_rescan_kernel(const float *__
 }
 
 template <int MH>
-hipError_t launch(const float *scores, int64_t pairs, int n, int k, const uint32_t *stair, int cells, int32_t *idx,
-                  float *w, hipStream_t stream)
+hipError_t launch(const float *scores, int64_t pairs, int n, int k, int32_t *idx, float *w, hipStream_t stream)
 {
     const int64_t blocks = (pairs + WAVES - 1) / WAVES;
     const dim3 grid((unsigned)blocks), block(64 * WAVES);
     if (n % 256 == 0 && n == MH * 64)
-        hipLaunchKernelGGL((select_kernel<MH, true>), grid, block, 0, stream, scores, pairs, n, k, stair, cells, idx,
-                           w);
+        hipLaunchKernelGGL((select_kernel<MH, true>), grid, block, 0, stream, scores, pairs, n, k, idx, w);
     else
-        hipLaunchKernelGGL((select_kernel<MH, false>), grid, block, 0, stream, scores, pairs, n, k, stair, cells, idx,
-                           w);
+        hipLaunchKernelGGL((select_kernel<MH, false>), grid, block, 0, stream, scores, pairs, n, k, idx, w);
     return hipGetLastError();
 }
 
@@ -686,28 +704,19 @@ int staircase_cells(int k)
     return c;
 }
 
-void staircase_table(int k, uint32_t *out)
-{
-    for (int c = 0; c < kMaxStaircaseCells; ++c) out[c] = 0xFFFFFFFFu;
-    int c = 0;
-    for (int i = 0; i < k; ++i)
-        for (int j = 0; j < k; ++j)
-            if ((i + 1) * (j + 1) <= k) out[c++] = ((uint32_t)i << 16) | (uint32_t)j;
-}
-
-hipError_t launch_select(const float *scores, int64_t B, int H, int n, int k, const uint32_t *stair,
-                         int32_t *idx, float *w, hipStream_t stream)
+hipError_t launch_select(const float *scores, int64_t B, int H, int n, int k, int32_t *idx, float *w,
+                         hipStream_t stream)
 {
     const int64_t pairs = B * H;
     if (pairs <= 0) return hipSuccess;
-    const int cells = staircase_cells(k);
+    if (k < 1 || k > 64 || k > n) return hipErrorInvalidValue;
     static_assert(STAIR_SLOTS * 64 <= kMaxStaircaseCells, "the kernel reads the whole padded table");
-    if (cells > STAIR_SLOTS * 64) return hipErrorInvalidValue;
+    if (staircase_cells(k) > STAIR_SLOTS * 64) return hipErrorInvalidValue;
     const int mh = (n + 63) / 64;
-    if (mh <= 4) return launch<4>(scores, pairs, n, k, stair, cells, idx, w, stream);
-    if (mh <= 16) return launch<16>(scores, pairs, n, k, stair, cells, idx, w, stream);
-    if (mh <= 32) return launch<32>(scores, pairs, n, k, stair, cells, idx, w, stream);
-    return launch<64>(scores, pairs, n, k, stair, cells, idx, w, stream);
+    if (mh <= 4) return launch<4>(scores, pairs, n, k, idx, w, stream);
+    if (mh <= 16) return launch<16>(scores, pairs, n, k, idx, w, stream);
+    if (mh <= 32) return launch<32>(scores, pairs, n, k, idx, w, stream);
+    return launch<64>(scores, pairs, n, k, idx, w, stream);
 }
 
 }  // namespace pkm

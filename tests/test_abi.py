@@ -82,13 +82,12 @@ def test_config_check(change, status):
 def test_workspace_bytes():
     cfg = pk.make_config(**GOOD)
     mb, H, D, n, k = 16384, 4, 1024, 1024, 32
-    stair = 320 * 4  # staircase cells of the candidate grid
     stat_part = 2 * (mb // 64) * H * D * 4  # batch statistics: each 64-row chunk's mean and squared deviations
     exps = max(mb + H * D, 2 * H * (mb + n)) * 4  # GEMM row exponents (query or scoring)
     qmax = mb * 2 * H * 4  # largest |q^| per (token, half of a head)
     sub_exp = 2 * H * n * 4  # the subkeys' row exponents
     assert (pk.workspace_bytes(cfg) ==
-            4 * mb * H * (D + 2 * n + 2 * k) + stair + stat_part + exps + qmax + sub_exp)
+            4 * mb * H * (D + 2 * n + 2 * k) + stat_part + exps + qmax + sub_exp)
     with pytest.raises(pk.PkmError):
         pk.workspace_bytes(pk.make_config(**{**GOOD, "k": 0}))
 
@@ -166,6 +165,18 @@ def test_null_arguments_rejected_before_any_launch():
     grads = pk._binding.GradsStruct()
     assert lib.pkm_backward(null, ctypes.byref(params), 1, null, null, null, null, ctypes.byref(grads), null, 0,
                             null) == pk.PKM_E_ARG
+    good = pk.make_config(**GOOD)
+    assert lib.pkm_forward_noalloc(None, ctypes.byref(params), 1, null, null, null, null, null) == pk.PKM_E_ARG
+    assert lib.pkm_forward_noalloc(ctypes.byref(good), ctypes.byref(params), 1, null, null, null, null,
+                                   null) == pk.PKM_E_ARG
+    assert lib.pkm_forward_noalloc(ctypes.byref(good), ctypes.byref(params), -1, null, null, null, null,
+                                   null) == pk.PKM_E_ARG
+    # one token's workspace larger than the library's scratch array
+    huge = pk.make_config(**{**GOOD, "dim": 65536, "heads": 512, "n_keys": 4096})
+    assert lib.pkm_config_check(ctypes.byref(huge)) == pk.PKM_OK
+    assert lib.pkm_forward_noalloc(ctypes.byref(huge), ctypes.byref(params), 1, null, null, null, null,
+                                   null) == pk.PKM_E_UNSUPPORTED
+    assert "scratch" in pk.last_error()
     assert lib.pkm_create(None, ctypes.byref(ctypes.c_void_p())) == pk.PKM_E_ARG
     assert lib.pkm_create(ctypes.byref(pk.make_config(**GOOD)), None) == pk.PKM_E_ARG
     assert "NULL" in pk.last_error()
