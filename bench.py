@@ -33,7 +33,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 # Sources of each kernel: measured HBM traffic is only reported while they
 # are unchanged since the counters were taken.
 KERNEL_SOURCES = {"query_gemm": ["gemm_f32.hip"], "score_gemm": ["gemm_f32.hip"],
-                  "select": ["select.hip", "wave_ops.h"], "gather": ["gather.hip"]}
+                  "select": ["select.hip", "wave_ops.h"], "gather": ["gather.hip", "gather_dev.h"],
+                  "select_gather": ["select.hip", "wave_ops.h", "gather_dev.h"]}
 
 
 def measured_traffic(workload, kernel):
@@ -65,6 +66,12 @@ def per_token_work(wl):
     }
 
 
+def fused(wl):
+    """Whether the forward runs a4-a7 as one kernel (n_keys 1024 or 2048,
+    H k <= 512)."""
+    return wl.n in (1024, 2048) and wl.H * wl.k <= 512
+
+
 def stage_bytes(wl):
     """Algorithmic HBM bytes of each stage for the whole batch: operands read
     once, results written once."""
@@ -75,6 +82,8 @@ def stage_bytes(wl):
         "score_gemm": 4 * (B * H * D + H * n * D + B * H * 2 * n),
         "select": work["select_bytes"] * B,
         "gather": work["gather_bytes"] * B + B * H * k * 8 + B * D * 4,
+        # fused: read the scores, write the selection, read the rows, write out
+        "select_gather": (work["select_bytes"] + work["gather_bytes"]) * B + B * D * 4,
     }
 
 
@@ -84,8 +93,8 @@ def end_to_end(wl, ms):
     bytes / HBM peak)."""
     work = per_token_work(wl)
     nbytes = stage_bytes(wl)
-    flops = {"query_gemm": work["query_flop"] * wl.B, "score_gemm": work["score_flop"] * wl.B,
-             "select": 0.0, "gather": 0.0}
+    flops = {"query_gemm": work["query_flop"] * wl.B, "score_gemm": work["score_flop"] * wl.B}
+    flops.update({"select_gather": 0.0} if fused(wl) else {"select": 0.0, "gather": 0.0})
     ideal = sum(max(flops[s] / (GEMM_PEAK_TFLOPS * 1e12), nbytes[s] / (HBM_PEAK_GBS * 1e9)) for s in flops)
     hbm_only = work["gather_bytes"] * wl.B / (HBM_PEAK_GBS * 1e9)
     value = wl.B / (ms * 1e-3)
@@ -151,9 +160,10 @@ def timed_steps(torch, fn, steps, warmup, stats=None):
     return float(np.median(t))
 
 
-def kernel_times(torch, mem, P, xt, steps, warmup):
-    """Median ms of each stage's kernel: events between consecutive stage
-    calls on one stream, every iteration enqueued before one final sync."""
+def kernel_times(torch, mem, P, xt, steps, warmup, wl):
+    """Median ms of each of the forward's kernels, and of the stand-alone
+    select and gather: events between consecutive stage calls on one
+    stream, every iteration enqueued before one final sync."""
     B = xt.shape[0]
     q = torch.empty((B, mem.heads, mem.dim), dtype=torch.float32, device=xt.device)
     s = torch.empty((B, mem.heads, 2, mem.n_keys), dtype=torch.float32, device=xt.device)
@@ -162,6 +172,10 @@ def kernel_times(torch, mem, P, xt, steps, warmup):
     out = torch.empty((B, mem.dim), dtype=torch.float32, device=xt.device)
     stages = [lambda: mem.query(P, xt, q), lambda: mem.score(P, q, s), lambda: mem.select(s, idx, w),
               lambda: mem.gather(P, idx, w, out)]
+    names = ["query_gemm", "score_gemm", "select", "gather"]
+    if fused(wl):
+        stages.append(lambda: mem.select_gather(P, s, out, idx, w))
+        names.append("select_gather")
 
     def step():
         for f in stages:
@@ -176,7 +190,6 @@ def kernel_times(torch, mem, P, xt, steps, warmup):
             f()
             ev[it][j + 1].record()
     torch.cuda.synchronize()
-    names = ["query_gemm", "score_gemm", "select", "gather"]
     return {nm: float(np.median([ev[it][j].elapsed_time(ev[it][j + 1]) for it in range(steps)]))
             for j, nm in enumerate(names)}
 
@@ -396,7 +409,7 @@ def main():
     ms = timed_steps(torch, lambda: mem.forward(P, xt, out, idx, wts), args.steps, args.warmup, step_stats)
     rows = idx.cpu().numpy().ravel()
     distinct = float(np.unique(rows).size) / rows.size
-    kt = kernel_times(torch, mem, P, xt, args.steps, args.warmup)
+    kt = kernel_times(torch, mem, P, xt, args.steps, args.warmup, wl)
     g_uniform_ms = gather_uniform_ms(torch, mem, P, wl, args.steps, args.warmup)
     hbm = hbm_measured(torch, mem, P, wl, args.steps, args.warmup)
 
@@ -410,13 +423,18 @@ def main():
         "select": ("hbm", work["select_bytes"] * B / (kt["select"] * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"),
         "gather": ("hbm", work["gather_bytes"] * B / (kt["gather"] * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"),
     }
-    dominant = max(kt, key=kt.get)
+    if fused(wl):
+        rl["select_gather"] = ("hbm", (work["select_bytes"] + work["gather_bytes"]) * B /
+                               (kt["select_gather"] * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s")
+    # the forward's own kernels; the dominant one is the headline roofline
+    forward_kernels = ["query_gemm", "score_gemm"] + (["select_gather"] if fused(wl) else ["select", "gather"])
+    dominant = max(forward_kernels, key=kt.get)
 
     def roof(name):
         bound, achieved, peak, unit = rl[name]
         return {"kernel": name, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                 "frac": round(achieved / peak, 4), "traffic": measured_traffic(wl.name, name),
-                "avg_ms": round(kt[name], 4)}
+                "median_ms": round(kt[name], 4)}
 
     line = {
         "metric": METRIC,
@@ -442,6 +460,7 @@ def main():
         "gathered_rows_distinct_frac": round(distinct, 4),
         "end_to_end": end_to_end(wl, ms),
         "kernels_ms": {nm: round(v, 4) for nm, v in kt.items()},
+        "forward_kernels": forward_kernels,
         "kernel_rooflines": {nm: {"achieved": round(rl[nm][1], 2), "unit": rl[nm][3],
                                   "frac": round(rl[nm][1] / rl[nm][2], 4)} for nm in rl},
     }

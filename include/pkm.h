@@ -193,6 +193,18 @@ pkm_status pkm_select(pkm_ctx *ctx, int64_t B, const float *scores, int32_t *idx
 pkm_status pkm_gather(pkm_ctx *ctx, const pkm_params *p, int64_t B, int32_t rows_per_token, const int32_t *idx,
                       const float *weights, float *out, void *stream);
 
+/* Steps a4-a7 from scores [B, H, 2, n] fp32: the selection and the gather
+ * ("Product-Key Memory", §Factorising the key space and the code listing's
+ * forward, from the subkey scores on), out [B, D] fp32 overwritten; idx and
+ * weights [B, H, k] written as pkm_select writes them, or both NULL.  The
+ * same results, bit for bit, as pkm_select followed by pkm_gather, and what
+ * pkm_forward runs after the scoring: for n_keys 1024 or 2048 with H * k <=
+ * 512 one fused kernel (a workgroup per token selects every head, then
+ * gathers the token's rows); otherwise the two kernels (idx / weights NULL
+ * then use the context's workspace).  Uses p->values and p->value_scale. */
+pkm_status pkm_select_gather(pkm_ctx *ctx, const pkm_params *p, int64_t B, const float *scores, int32_t *idx,
+                             float *weights, float *out, void *stream);
+
 /* Flat exact search: the brute-force search the product search replaces
  * ("Product-Key Memory", §Factorising the key space: the product search
  * returns exactly the k best of all N = n^2 concatenated keys, with 2n

@@ -19,7 +19,7 @@ EXPORTS = (
     "pkm_config_check", "pkm_workspace_bytes", "pkm_create", "pkm_destroy", "pkm_forward", "pkm_query",
     "pkm_score", "pkm_select", "pkm_gather", "pkm_flat_workspace_bytes", "pkm_flat_search",
     "pkm_backward_workspace_bytes", "pkm_backward", "pkm_forward_batch_stats", "pkm_backward_batch_stats",
-    "pkm_usage", "pkm_status_str", "pkm_last_error", "pkm_forward_noalloc",
+    "pkm_usage", "pkm_status_str", "pkm_last_error", "pkm_forward_noalloc", "pkm_select_gather",
 )
 
 
@@ -66,6 +66,7 @@ def load_library(path=LIB_PATH):
         "pkm_score": (ctypes.c_int, [vp, par_p, i64, vp, vp, vp]),
         "pkm_select": (ctypes.c_int, [vp, i64, vp, vp, vp, vp]),
         "pkm_gather": (ctypes.c_int, [vp, par_p, i64, i32, vp, vp, vp, vp]),
+        "pkm_select_gather": (ctypes.c_int, [vp, par_p, i64, vp, vp, vp, vp, vp]),
         "pkm_flat_workspace_bytes": (ctypes.c_int, [cfg_p, i64, ctypes.POINTER(ctypes.c_size_t)]),
         "pkm_flat_search": (ctypes.c_int, [vp, par_p, i64, vp, vp, ctypes.c_size_t, vp, vp, vp]),
         "pkm_backward_workspace_bytes": (ctypes.c_int, [cfg_p, ctypes.POINTER(ctypes.c_size_t)]),
@@ -319,6 +320,25 @@ class Memory:
         _check(self.lib.pkm_gather(self._ctx, ctypes.byref(params.struct), B, R, _ptr(idx), _ptr(weights),
                                    _ptr(out), _stream_handle(stream)))
         return out
+
+    def select_gather(self, params, scores, out=None, idx=None, weights=None, stream=None):
+        """a4-a7 from scores [B, H, 2, n]: returns (out [B, D] f32, idx,
+        weights); idx / weights ([B, H, k]) are filled when given (both or
+        neither), else None."""
+        torch = _torch()
+        B = scores.shape[0]
+        self.check_params(params, ("values",))
+        _expect(scores, "scores", (B, self.heads, 2, self.n_keys), "float32", params["values"].device)
+        out = self._new((B, self.dim), torch.float32, scores) if out is None else out
+        _expect(out, "out", (B, self.dim), "float32", scores.device)
+        if (idx is None) != (weights is None):
+            raise ValueError("idx and weights go together")
+        if idx is not None:
+            _expect(idx, "idx", (B, self.heads, self.k), "int32", scores.device)
+            _expect(weights, "weights", (B, self.heads, self.k), "float32", scores.device)
+        _check(self.lib.pkm_select_gather(self._ctx, ctypes.byref(params.struct), B, _ptr(scores), _ptr(idx),
+                                          _ptr(weights), _ptr(out), _stream_handle(stream)))
+        return out, idx, weights
 
     def usage(self, idx, counts=None, stream=None):
         """Slot usage: counts [n_keys^2] uint32 (int32 accepted) += how often

@@ -431,6 +431,16 @@ pkm_status forward_chunks(const pkm_ctx *ctx, const pkm_params *p, int64_t B, co
         float *cw = weights ? weights + b0 * H * k : ctx->weights;
         if ((s = run_query(ctx, p, nb, x + b0 * D, ctx->qhat, ctx->qmax, st))) return s;
         if ((s = run_score(ctx, p, nb, ctx->qhat, ctx->scores, ctx->qmax, st))) return s;
+        if (pkm::select_gather_fusable(c.heads, c.n_keys, c.k)) {
+            // a4-a7 in one kernel; the selection is written out only if asked for
+            const bool keep = idx || weights;
+            if ((s = launched(pkm::launch_select_gather(ctx->scores, nb, c.heads, c.n_keys, c.k, p->values,
+                                                        p->value_scale, c.value_type, c.dim, c.n_keys * c.n_keys,
+                                                        keep ? ci : nullptr, keep ? cw : nullptr, out + b0 * D, st),
+                              "select and gather")))
+                return s;
+            continue;
+        }
         if ((s = launched(pkm::launch_select(ctx->scores, nb, c.heads, c.n_keys, c.k, ci, cw, st), "select")))
             return s;
         if ((s = launched(pkm::launch_gather(p->values, p->value_scale, c.value_type, c.dim, c.n_keys * c.n_keys, nb,
@@ -653,6 +663,41 @@ pkm_status pkm_gather(pkm_ctx *ctx, const pkm_params *p, int64_t B, int32_t rows
                                          weights, out, static_cast<hipStream_t>(stream)),
                       "gather")))
         return s;
+    return ok();
+}
+
+pkm_status pkm_select_gather(pkm_ctx *ctx, const pkm_params *p, int64_t B, const float *scores, int32_t *idx,
+                             float *weights, float *out, void *stream)
+{
+    pkm_status s;
+    if ((s = check_ctx(ctx)) || (s = check_batch(ctx->cfg, B))) return s;
+    if (B == 0) return ok();
+    const pkm_config &c = ctx->cfg;
+    if ((s = check_value_params(c, p))) return s;
+    if ((s = need(scores, "scores")) || (s = need(out, "out"))) return s;
+    if ((idx == nullptr) != (weights == nullptr)) return fail(PKM_E_ARG, "idx and weights go together (both or neither)");
+    if (idx && ((s = need(idx, "idx")) || (s = need(weights, "weights")))) return s;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int64_t H = c.heads, k = c.k, N = (int64_t)c.n_keys * c.n_keys;
+    if (pkm::select_gather_fusable(c.heads, c.n_keys, c.k)) {
+        if ((s = launched(pkm::launch_select_gather(scores, B, c.heads, c.n_keys, c.k, p->values, p->value_scale,
+                                                    c.value_type, c.dim, (int)N, idx, weights, out, st),
+                          "select and gather")))
+            return s;
+        return ok();
+    }
+    // the two kernels, in chunks of max_batch when the selection goes to the workspace
+    for (int64_t b0 = 0; b0 < B; b0 += idx ? B : c.max_batch) {
+        const int64_t nb = idx ? B : (B - b0 < c.max_batch ? B - b0 : c.max_batch);
+        int32_t *ci = idx ? idx : ctx->idx;
+        float *cw = idx ? weights : ctx->weights;
+        if ((s = launched(pkm::launch_select(scores + b0 * H * 2 * c.n_keys, nb, c.heads, c.n_keys, c.k, ci, cw, st),
+                          "select")) ||
+            (s = launched(pkm::launch_gather(p->values, p->value_scale, c.value_type, c.dim, (int)N, nb, (int)(H * k),
+                                             ci, cw, out + b0 * c.dim, st),
+                          "gather")))
+            return s;
+    }
     return ok();
 }
 

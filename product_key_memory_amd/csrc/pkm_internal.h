@@ -112,6 +112,17 @@ hipError_t launch_gemm_nt_f32_product(const GemmArgs &a, hipStream_t stream);
 hipError_t launch_select(const float *scores, int64_t B, int H, int n, int k, int32_t *idx, float *w,
                          hipStream_t stream);
 
+// a4-a7 in one kernel, one workgroup per token: the selection of every
+// head, then the gather of the token's H k rows (value_type as
+// launch_gather), bitwise the same as launch_select followed by
+// launch_gather.  idx / w [B][H][k] are written when non-NULL (both or
+// neither).  Only for the shapes select_gather_fusable accepts (n_keys 1024
+// or 2048, H k <= 512).
+bool select_gather_fusable(int H, int n, int k);
+hipError_t launch_select_gather(const float *scores, int64_t B, int H, int n, int k, const void *values,
+                                const float *scale, int value_type, int D, int N, int32_t *idx, float *w, float *out,
+                                hipStream_t stream);
+
 // The candidate cells (i, j) with (i+1)(j+1) <= k: staircase_cells(k) of
 // them (at most 280 for k <= 64), padded to kMaxStaircaseCells per k.
 constexpr int kMaxStaircaseCells = 320;

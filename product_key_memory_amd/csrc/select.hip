@@ -34,6 +34,7 @@
 // one comparison per column certifies the result.  Otherwise (ties) the full
 // k*k grid is ranked.  All scores stay fp32; the candidate sums are the same
 // fp32 additions whichever path runs.
+#include "gather_dev.h"
 #include "pkm_internal.h"
 #include "wave_ops.h"
 
@@ -366,24 +367,16 @@ constexpr StairTables make_stair_tables()
 
 __device__ const StairTables kStairTables = make_stair_tables();
 
+// a4-a6 for one (token, head) whose half scores start at row0 (half 1 at
+// row0 + n): lane j < k receives the j-th winner's flat row and softmax
+// weight (winners by score desc, flat row asc).  hs / hi: the wave's LDS
+// lists of the two halves' top-k.
 template <int MH, bool VEC4>
-__global__ __launch_bounds__(64 * WAVES) void select_kernel(const float *__restrict__ scores, int64_t pairs, int n,
-                                                            int k, int32_t *__restrict__ idx_out,
-                                                            float *__restrict__ w_out)
+__device__ __forceinline__ void select_pair(const float *row0, int n, int k, Stage &st, float (*hs)[64],
+                                            uint32_t (*hi)[64], int lane, int32_t &id_out, float &w_out)
 {
-    __shared__ Stage stage[WAVES];
-    __shared__ float half_score[WAVES][2][64];
-    __shared__ uint32_t half_index[WAVES][2][64];
-
-    const int lane = threadIdx.x & 63;
-    const int wv = threadIdx.x >> 6;
-    const int64_t pair = (int64_t)blockIdx.x * WAVES + wv;  // b * H + h
-    if (pair >= pairs) return;
-    float(*hs)[64] = half_score[wv];
-    uint32_t(*hi)[64] = half_index[wv];
-
     // a4
-    half_topk<MH, VEC4>(scores + pair * 2 * (int64_t)n, n, k, stage[wv], hs, hi, lane);
+    half_topk<MH, VEC4>(row0, n, k, st, hs, hi, lane);
     wave_sync_lds();
 
     // a5 on the staircase: stair[c] = (i << 16) | j for the staircase's
@@ -404,7 +397,7 @@ __global__ __launch_bounds__(64 * WAVES) void select_kernel(const float *__restr
         const uint32_t ij = cell_of(t);
         return ij != 0xFFFFFFFFu ? order_key(hs[0][ij >> 16] + hs[1][ij & 0xFFFFu]) : 0u;
     };
-    uint64_t c = wave_topk(key, stair_key, [&](int t) { return id[t]; }, STAIR_SLOTS, k, stage[wv], lane);
+    uint64_t c = wave_topk(key, stair_key, [&](int t) { return id[t]; }, STAIR_SLOTS, k, st, lane);
 
     // certificate: no cell outside the staircase reaches the k-th score
     const uint32_t vk = read_lane((uint32_t)(c >> 32), k - 1);
@@ -413,16 +406,108 @@ __global__ __launch_bounds__(64 * WAVES) void select_kernel(const float *__restr
         const int i_out = k / (lane + 1);  // first row of column `lane` outside the staircase
         if (i_out < k) reach = order_key(hs[0][i_out] + hs[1][lane]) >= vk;
     }
-    if (__ballot(reach) != 0ull) c = full_grid_topk(n, k, hs, hi, stage[wv], lane);
+    if (__ballot(reach) != 0ull) c = full_grid_topk(n, k, hs, hi, st, lane);
 
     // a6: softmax over the k winners; lane 0 holds the largest score.
     const float top = key_score((uint32_t)(c >> 32));
     const float mx = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(top), 0));
     const float e = lane < k ? expf(top - mx) : 0.0f;
     const float sum = wave_sum(e);
+    id_out = (int32_t)unpack_id(c);
+    w_out = e / sum;
+}
+
+template <int MH, bool VEC4>
+__global__ __launch_bounds__(64 * WAVES) void select_kernel(const float *__restrict__ scores, int64_t pairs, int n,
+                                                            int k, int32_t *__restrict__ idx_out,
+                                                            float *__restrict__ w_out)
+{
+    __shared__ Stage stage[WAVES];
+    __shared__ float half_score[WAVES][2][64];
+    __shared__ uint32_t half_index[WAVES][2][64];
+
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    const int64_t pair = (int64_t)blockIdx.x * WAVES + wv;  // b * H + h
+    if (pair >= pairs) return;
+    int32_t id;
+    float wt;
+    select_pair<MH, VEC4>(scores + pair * 2 * (int64_t)n, n, k, stage[wv], half_score[wv], half_index[wv], lane, id,
+                          wt);
     if (lane < k) {
-        idx_out[pair * k + lane] = (int32_t)unpack_id(c);
-        w_out[pair * k + lane] = e / sum;
+        idx_out[pair * k + lane] = id;
+        w_out[pair * k + lane] = wt;
+    }
+}
+
+// a4-a7 fused: one workgroup per token.  Its waves first select the
+// token's heads (wave w takes heads w, w + WAVES, ...), keeping the H k
+// (row, weight) pairs in LDS (and writing them out when idx_out is given),
+// then gather the token's output from those pairs with exactly the shares
+// and order of the stand-alone gather (a column slice per wave, or PAIR:
+// two waves splitting the rows of short rows), so the result is bitwise the
+// same as select followed by gather.  The selection is ALU-bound and the
+// gather HBM-bound; with several tokens' workgroups on a CU, one token's
+// selection runs while another token's row loads are in flight.
+constexpr int kFusedMaxRows = 512;  // H * k held in LDS
+
+template <int MH, int VT, bool NT, bool PAIR>
+__global__ __launch_bounds__(64 * WAVES) void select_gather_kernel(const float *__restrict__ scores, int H, int n,
+                                                                   int k, const uint8_t *__restrict__ values,
+                                                                   const float *__restrict__ scale, int D, int N,
+                                                                   int32_t *__restrict__ idx_out,
+                                                                   float *__restrict__ w_out, float *__restrict__ out)
+{
+    constexpr int EPL = gdev::Fmt<VT>::EPL;
+    __shared__ Stage stage[WAVES];
+    __shared__ float half_score[WAVES][2][64];
+    __shared__ uint32_t half_index[WAVES][2][64];
+    __shared__ int32_t sel_row[kFusedMaxRows];
+    __shared__ float sel_w[kFusedMaxRows];
+    __shared__ float part[PAIR ? EPL : 1][32];
+
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    const int64_t b = blockIdx.x;
+    for (int h = wv; h < H; h += WAVES) {
+        const int64_t pair = b * H + h;
+        int32_t id;
+        float wt;
+        select_pair<MH, true>(scores + pair * 2 * (int64_t)n, n, k, stage[wv], half_score[wv], half_index[wv], lane,
+                              id, wt);
+        if (lane < k) {
+            sel_row[h * k + lane] = id;
+            sel_w[h * k + lane] = wt;
+            if (idx_out) {
+                idx_out[pair * k + lane] = id;
+                w_out[pair * k + lane] = wt;
+            }
+        }
+    }
+    __syncthreads();
+    const int R = H * k;
+    if constexpr (PAIR) {
+        // two waves per token as the stand-alone pair gather
+        float acc[EPL];
+        if (wv < 2) gdev::gather_pair_share<VT, 2, NT>(values, scale, D, N, R, wv, true, sel_row, sel_w, acc, lane);
+        const int half = lane >> 5;
+        if (wv == 1 && half == 0) {
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) part[e][lane] = acc[e];
+        }
+        __syncthreads();
+        if (wv == 0 && half == 0 && (lane & 31) * EPL < D) {
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[e] += part[e][lane];
+            float4 *o = reinterpret_cast<float4 *>(out + b * D + (lane & 31) * EPL);
+#pragma unroll
+            for (int e = 0; e < EPL / 4; ++e)
+                o[e] = make_float4(acc[4 * e], acc[4 * e + 1], acc[4 * e + 2], acc[4 * e + 3]);
+        }
+    } else {
+        const int slices = (D + 64 * EPL - 1) / (64 * EPL);
+        for (int sl = wv; sl < slices; sl += WAVES)
+            gdev::gather_slice<VT, NT>(values, scale, D, N, R, sl, sel_row, sel_w, out + b * D, lane);
     }
 }
 
@@ -702,6 +787,60 @@ int staircase_cells(int k)
     int c = 0;
     for (int j = 0; j < k; ++j) c += k / (j + 1);
     return c;
+}
+
+namespace {
+
+template <int MH, int VT>
+hipError_t launch_fused(const float *scores, int64_t B, int H, int n, int k, const void *values, const float *scale,
+                        int D, int N, int32_t *idx, float *w, float *out, hipStream_t stream)
+{
+    const bool nt = B * H * k < N;  // as the stand-alone gather: rows seldom repeat
+    const bool pair = gdev::elem_bytes<VT>(D) <= 512;
+    const uint8_t *v = static_cast<const uint8_t *>(values);
+    const dim3 grid((unsigned)B), block(64 * WAVES);
+#define PKM_FUSED(NT_, PAIR_)                                                                                  \
+    hipLaunchKernelGGL((select_gather_kernel<MH, VT, NT_, PAIR_>), grid, block, 0, stream, scores, H, n, k, v, \
+                       scale, D, N, idx, w, out)
+    if (nt) {
+        if (pair) PKM_FUSED(true, true);
+        else PKM_FUSED(true, false);
+    } else {
+        if (pair) PKM_FUSED(false, true);
+        else PKM_FUSED(false, false);
+    }
+#undef PKM_FUSED
+    return hipGetLastError();
+}
+
+template <int MH>
+hipError_t launch_fused_vt(const float *scores, int64_t B, int H, int n, int k, const void *values,
+                           const float *scale, int value_type, int D, int N, int32_t *idx, float *w, float *out,
+                           hipStream_t stream)
+{
+    switch (value_type) {
+    case 0: return launch_fused<MH, 0>(scores, B, H, n, k, values, scale, D, N, idx, w, out, stream);
+    case 1: return launch_fused<MH, 1>(scores, B, H, n, k, values, scale, D, N, idx, w, out, stream);
+    case 2: return launch_fused<MH, 2>(scores, B, H, n, k, values, scale, D, N, idx, w, out, stream);
+    case 3: return launch_fused<MH, 3>(scores, B, H, n, k, values, scale, D, N, idx, w, out, stream);
+    default: return launch_fused<MH, 4>(scores, B, H, n, k, values, scale, D, N, idx, w, out, stream);
+    }
+}
+
+}  // namespace
+
+bool select_gather_fusable(int H, int n, int k) { return (n == 1024 || n == 2048) && H * k <= kFusedMaxRows; }
+
+hipError_t launch_select_gather(const float *scores, int64_t B, int H, int n, int k, const void *values,
+                                const float *scale, int value_type, int D, int N, int32_t *idx, float *w, float *out,
+                                hipStream_t stream)
+{
+    if (B <= 0) return hipSuccess;
+    if (k < 1 || k > 64 || k > n || !select_gather_fusable(H, n, k) || (idx == nullptr) != (w == nullptr) ||
+        B > 0x7FFFFFFF)
+        return hipErrorInvalidValue;
+    if (n == 1024) return launch_fused_vt<16>(scores, B, H, n, k, values, scale, value_type, D, N, idx, w, out, stream);
+    return launch_fused_vt<32>(scores, B, H, n, k, values, scale, value_type, D, N, idx, w, out, stream);
 }
 
 hipError_t launch_select(const float *scores, int64_t B, int H, int n, int k, int32_t *idx, float *w,

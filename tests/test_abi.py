@@ -160,6 +160,7 @@ def test_null_arguments_rejected_before_any_launch():
     assert lib.pkm_query(null, ctypes.byref(params), 1, null, null, null) == pk.PKM_E_ARG
     assert lib.pkm_score(null, ctypes.byref(params), 1, null, null, null) == pk.PKM_E_ARG
     assert lib.pkm_select(null, 1, null, null, null, null) == pk.PKM_E_ARG
+    assert lib.pkm_select_gather(null, ctypes.byref(params), 1, null, null, null, null, null) == pk.PKM_E_ARG
     assert lib.pkm_gather(null, ctypes.byref(params), 1, 1, null, null, null, null) == pk.PKM_E_ARG
     assert lib.pkm_flat_search(null, ctypes.byref(params), 1, null, null, 0, null, null, null) == pk.PKM_E_ARG
     grads = pk._binding.GradsStruct()
