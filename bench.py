@@ -68,8 +68,8 @@ def per_token_work(wl):
 
 def fused(wl):
     """Whether the forward runs a4-a7 as one kernel (n_keys 1024 or 2048,
-    H k <= 512)."""
-    return wl.n in (1024, 2048) and wl.H * wl.k <= 512
+    H k <= 512, table rows longer than 512 bytes)."""
+    return wl.n in (1024, 2048) and wl.H * wl.k <= 512 and wl.D * ELT_BYTES[wl.table] > 512
 
 
 def stage_bytes(wl):

@@ -199,9 +199,9 @@ pkm_status pkm_gather(pkm_ctx *ctx, const pkm_params *p, int64_t B, int32_t rows
  * weights [B, H, k] written as pkm_select writes them, or both NULL.  The
  * same results, bit for bit, as pkm_select followed by pkm_gather, and what
  * pkm_forward runs after the scoring: for n_keys 1024 or 2048 with H * k <=
- * 512 one fused kernel (a workgroup per token selects every head, then
- * gathers the token's rows); otherwise the two kernels (idx / weights NULL
- * then use the context's workspace).  Uses p->values and p->value_scale. */
+ * 512 and table rows longer than 512 bytes one fused kernel (a workgroup
+ * per token selects every head, then gathers the token's rows); otherwise
+ * the two kernels (idx / weights NULL then use the context's workspace).  Uses p->values and p->value_scale. */
 pkm_status pkm_select_gather(pkm_ctx *ctx, const pkm_params *p, int64_t B, const float *scores, int32_t *idx,
                              float *weights, float *out, void *stream);
 

@@ -155,7 +155,10 @@ __device__ __forceinline__ void gather_slice(const uint8_t *__restrict__ values,
     for (int r0 = 0; r0 < R; r0 += 64) {
         const int nr = min(64, R - r0);
         const int my_row = lane < nr ? ib[r0 + lane] : 0;
-        const float my_w = lane < nr ? wb[r0 + lane] : 0.0f;
+        // the weights, times the row scales, for up to 64 rows at once (one
+        // load per lane rather than one per row)
+        float my_w = lane < nr ? wb[r0 + lane] : 0.0f;
+        if constexpr (SCALED) my_w *= lane < nr ? scale[min(max(my_row, 0), N - 1)] : 0.0f;
         int r = 0;
         for (; r + UN <= nr; r += UN) {
             uint4 v[UN];
@@ -164,7 +167,6 @@ __device__ __forceinline__ void gather_slice(const uint8_t *__restrict__ values,
             for (int u = 0; u < UN; ++u) {
                 const int row = min(max(__builtin_amdgcn_readlane(my_row, r + u), 0), N - 1);
                 wt[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), r + u));
-                if constexpr (SCALED) wt[u] *= scale[row];
                 v[u] = active ? load_row_piece<NT>(col + (int64_t)row * row_bytes) : make_uint4(0, 0, 0, 0);
             }
 #pragma unroll
@@ -175,8 +177,7 @@ __device__ __forceinline__ void gather_slice(const uint8_t *__restrict__ values,
         }
         for (; r < nr; ++r) {
             const int row = min(max(__builtin_amdgcn_readlane(my_row, r), 0), N - 1);
-            float wt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), r));
-            if constexpr (SCALED) wt *= scale[row];
+            const float wt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), r));
             const uint4 v = active ? load_row_piece<NT>(col + (int64_t)row * row_bytes) : make_uint4(0, 0, 0, 0);
             accumulate<VT>(acc, v, wt);
             if constexpr (VT == 4) wsum += wt;

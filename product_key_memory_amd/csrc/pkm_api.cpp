@@ -431,7 +431,7 @@ pkm_status forward_chunks(const pkm_ctx *ctx, const pkm_params *p, int64_t B, co
         float *cw = weights ? weights + b0 * H * k : ctx->weights;
         if ((s = run_query(ctx, p, nb, x + b0 * D, ctx->qhat, ctx->qmax, st))) return s;
         if ((s = run_score(ctx, p, nb, ctx->qhat, ctx->scores, ctx->qmax, st))) return s;
-        if (pkm::select_gather_fusable(c.heads, c.n_keys, c.k)) {
+        if (pkm::select_gather_fusable(c.heads, c.n_keys, c.k, c.value_type, c.dim)) {
             // a4-a7 in one kernel; the selection is written out only if asked for
             const bool keep = idx || weights;
             if ((s = launched(pkm::launch_select_gather(ctx->scores, nb, c.heads, c.n_keys, c.k, p->values,
@@ -679,7 +679,7 @@ pkm_status pkm_select_gather(pkm_ctx *ctx, const pkm_params *p, int64_t B, const
     if (idx && ((s = need(idx, "idx")) || (s = need(weights, "weights")))) return s;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int64_t H = c.heads, k = c.k, N = (int64_t)c.n_keys * c.n_keys;
-    if (pkm::select_gather_fusable(c.heads, c.n_keys, c.k)) {
+    if (pkm::select_gather_fusable(c.heads, c.n_keys, c.k, c.value_type, c.dim)) {
         if ((s = launched(pkm::launch_select_gather(scores, B, c.heads, c.n_keys, c.k, p->values, p->value_scale,
                                                     c.value_type, c.dim, (int)N, idx, weights, out, st),
                           "select and gather")))

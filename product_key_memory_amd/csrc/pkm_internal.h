@@ -117,8 +117,8 @@ hipError_t launch_select(const float *scores, int64_t B, int H, int n, int k, in
 // launch_gather), bitwise the same as launch_select followed by
 // launch_gather.  idx / w [B][H][k] are written when non-NULL (both or
 // neither).  Only for the shapes select_gather_fusable accepts (n_keys 1024
-// or 2048, H k <= 512).
-bool select_gather_fusable(int H, int n, int k);
+// or 2048, H k <= 512, table rows longer than 512 bytes).
+bool select_gather_fusable(int H, int n, int k, int value_type, int D);
 hipError_t launch_select_gather(const float *scores, int64_t B, int H, int n, int k, const void *values,
                                 const float *scale, int value_type, int D, int N, int32_t *idx, float *w, float *out,
                                 hipStream_t stream);

@@ -443,15 +443,17 @@ __global__ __launch_bounds__(64 * WAVES) void select_kernel(const float *__restr
 // a4-a7 fused: one workgroup per token.  Its waves first select the
 // token's heads (wave w takes heads w, w + WAVES, ...), keeping the H k
 // (row, weight) pairs in LDS (and writing them out when idx_out is given),
-// then gather the token's output from those pairs with exactly the shares
-// and order of the stand-alone gather (a column slice per wave, or PAIR:
-// two waves splitting the rows of short rows), so the result is bitwise the
-// same as select followed by gather.  The selection is ALU-bound and the
-// gather HBM-bound; with several tokens' workgroups on a CU, one token's
-// selection runs while another token's row loads are in flight.
+// then gather the token's output from those pairs with exactly the share
+// and order of the stand-alone gather (a 1 KiB column slice per wave, every
+// row in order), so the result is bitwise the same as select followed by
+// gather.  The selection is ALU-bound and the gather HBM-bound; with
+// several tokens' workgroups on a CU, one token's selection runs while
+// another token's row loads are in flight.  Rows of at most 512 bytes are
+// not fused: their gather takes two waves per token, and the fused kernel's
+// occupancy would leave half the stand-alone kernel's loads in flight.
 constexpr int kFusedMaxRows = 512;  // H * k held in LDS
 
-template <int MH, int VT, bool NT, bool PAIR>
+template <int MH, int VT, bool NT>
 __global__ __launch_bounds__(64 * WAVES) void select_gather_kernel(const float *__restrict__ scores, int H, int n,
                                                                    int k, const uint8_t *__restrict__ values,
                                                                    const float *__restrict__ scale, int D, int N,
@@ -464,7 +466,6 @@ __global__ __launch_bounds__(64 * WAVES) void select_gather_kernel(const float *
     __shared__ uint32_t half_index[WAVES][2][64];
     __shared__ int32_t sel_row[kFusedMaxRows];
     __shared__ float sel_w[kFusedMaxRows];
-    __shared__ float part[PAIR ? EPL : 1][32];
 
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
@@ -485,30 +486,9 @@ __global__ __launch_bounds__(64 * WAVES) void select_gather_kernel(const float *
         }
     }
     __syncthreads();
-    const int R = H * k;
-    if constexpr (PAIR) {
-        // two waves per token as the stand-alone pair gather
-        float acc[EPL];
-        if (wv < 2) gdev::gather_pair_share<VT, 2, NT>(values, scale, D, N, R, wv, true, sel_row, sel_w, acc, lane);
-        const int half = lane >> 5;
-        if (wv == 1 && half == 0) {
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) part[e][lane] = acc[e];
-        }
-        __syncthreads();
-        if (wv == 0 && half == 0 && (lane & 31) * EPL < D) {
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) acc[e] += part[e][lane];
-            float4 *o = reinterpret_cast<float4 *>(out + b * D + (lane & 31) * EPL);
-#pragma unroll
-            for (int e = 0; e < EPL / 4; ++e)
-                o[e] = make_float4(acc[4 * e], acc[4 * e + 1], acc[4 * e + 2], acc[4 * e + 3]);
-        }
-    } else {
-        const int slices = (D + 64 * EPL - 1) / (64 * EPL);
-        for (int sl = wv; sl < slices; sl += WAVES)
-            gdev::gather_slice<VT, NT>(values, scale, D, N, R, sl, sel_row, sel_w, out + b * D, lane);
-    }
+    const int slices = (D + 64 * EPL - 1) / (64 * EPL);
+    for (int sl = wv; sl < slices; sl += WAVES)
+        gdev::gather_slice<VT, NT>(values, scale, D, N, H * k, sl, sel_row, sel_w, out + b * D, lane);
 }
 
 // Flat exact search: top-k over rows of up to n^2 scores, in passes.  Pass 1
@@ -796,20 +776,14 @@ hipError_t launch_fused(const float *scores, int64_t B, int H, int n, int k, con
                         int D, int N, int32_t *idx, float *w, float *out, hipStream_t stream)
 {
     const bool nt = B * H * k < N;  // as the stand-alone gather: rows seldom repeat
-    const bool pair = gdev::elem_bytes<VT>(D) <= 512;
     const uint8_t *v = static_cast<const uint8_t *>(values);
     const dim3 grid((unsigned)B), block(64 * WAVES);
-#define PKM_FUSED(NT_, PAIR_)                                                                                  \
-    hipLaunchKernelGGL((select_gather_kernel<MH, VT, NT_, PAIR_>), grid, block, 0, stream, scores, H, n, k, v, \
-                       scale, D, N, idx, w, out)
-    if (nt) {
-        if (pair) PKM_FUSED(true, true);
-        else PKM_FUSED(true, false);
-    } else {
-        if (pair) PKM_FUSED(false, true);
-        else PKM_FUSED(false, false);
-    }
-#undef PKM_FUSED
+    if (nt)
+        hipLaunchKernelGGL((select_gather_kernel<MH, VT, true>), grid, block, 0, stream, scores, H, n, k, v, scale, D,
+                           N, idx, w, out);
+    else
+        hipLaunchKernelGGL((select_gather_kernel<MH, VT, false>), grid, block, 0, stream, scores, H, n, k, v, scale, D,
+                           N, idx, w, out);
     return hipGetLastError();
 }
 
@@ -829,14 +803,19 @@ hipError_t launch_fused_vt(const float *scores, int64_t B, int H, int n, int k, 
 
 }  // namespace
 
-bool select_gather_fusable(int H, int n, int k) { return (n == 1024 || n == 2048) && H * k <= kFusedMaxRows; }
+bool select_gather_fusable(int H, int n, int k, int value_type, int D)
+{
+    const int64_t row_bytes = value_type == 0 ? 4 * (int64_t)D : value_type == 1 ? 2 * (int64_t)D
+                            : value_type == 4 ? D / 2 : D;
+    return (n == 1024 || n == 2048) && H * k <= kFusedMaxRows && row_bytes > 512;
+}
 
 hipError_t launch_select_gather(const float *scores, int64_t B, int H, int n, int k, const void *values,
                                 const float *scale, int value_type, int D, int N, int32_t *idx, float *w, float *out,
                                 hipStream_t stream)
 {
     if (B <= 0) return hipSuccess;
-    if (k < 1 || k > 64 || k > n || !select_gather_fusable(H, n, k) || (idx == nullptr) != (w == nullptr) ||
+    if (k < 1 || k > 64 || k > n || !select_gather_fusable(H, n, k, value_type, D) || (idx == nullptr) != (w == nullptr) ||
         B > 0x7FFFFFFF)
         return hipErrorInvalidValue;
     if (n == 1024) return launch_fused_vt<16>(scores, B, H, n, k, values, scale, value_type, D, N, idx, w, out, stream);

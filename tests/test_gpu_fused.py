@@ -1,10 +1,10 @@
 """GPU: the fused selection and gather (pkm_select_gather; what pkm_forward
-runs after the scoring when n_keys is 1024 or 2048 and H k <= 512).
+runs after the scoring when n_keys is 1024 or 2048, H k <= 512 and table
+rows are longer than 512 bytes; shorter rows take the two kernels).
 
 It must equal pkm_select followed by pkm_gather bit for bit -- the same
 selection, and each output column summed by the same rows in the same
-order -- for every table format and for both gather layouts (a column slice
-per wave, and two waves splitting the rows of rows of at most 512 bytes).
+order -- for every table format, fused or not.
 The whole lookup through it is checked against the fp64 oracle with the
 lookup's rules (indices exact, outputs within 1e-4 for fp32 tables and 2e-2
 for the others).
@@ -31,16 +31,16 @@ def torch():
 
 
 CASES = [
-    # (B, D, H, n, k, table): row bytes > 512 -> column slices; <= 512 -> paired waves
+    # (B, D, H, n, k, table): rows > 512 bytes are fused; <= 512 bytes take the two kernels
     (300, 1024, 4, 1024, 32, "bf16"),   # two 1 KiB slices
-    (200, 256, 3, 1024, 20, "bf16"),    # 512-byte rows: paired waves
+    (200, 256, 3, 1024, 20, "bf16"),    # 512-byte rows: not fused
     (150, 1024, 2, 1024, 16, "f32"),    # four slices
     (100, 128, 4, 1024, 32, "f32"),     # 512-byte rows
     (120, 1024, 4, 2048, 32, "e4m3"),   # n_keys 2048, one slice
     (90, 512, 2, 2048, 8, "e4m3"),      # 512-byte rows
     (160, 1024, 4, 1024, 32, "int8"),
-    (160, 1024, 4, 1024, 32, "int4"),   # 512-byte rows
-    (64, 2048, 2, 1024, 64, "int4"),    # 1 KiB rows, k = 64
+    (160, 1024, 4, 1024, 32, "int4"),   # 512-byte rows: not fused
+    (64, 2048, 2, 1024, 64, "int4"),    # 1 KiB rows: fused, k = 64
     (70, 320, 5, 1024, 7, "e4m3"),      # D not a power of two, H > 4 waves
 ]
 
