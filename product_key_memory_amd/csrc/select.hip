@@ -255,10 +255,13 @@ __device__ __forceinline__ int slot_element(int t, int lane)
     return VEC4 ? ((t >> 2) << 8) + (lane << 2) + (t & 3) : t * 64 + lane;
 }
 
+typedef float fx4v __attribute__((ext_vector_type(4)));
+
 // Loads the order keys of one half row (0 past the end of the row).  The
 // loads are unconditional (clamped index), so all of them are in flight
-// together instead of one exec-masked load at a time.
-template <int MH, bool VEC4>
+// together instead of one exec-masked load at a time.  NTS: non-temporal
+// loads (VEC4 rows), for a kernel whose later row reads rely on the caches.
+template <int MH, bool VEC4, bool NTS = false>
 __device__ __forceinline__ void load_keys(const float *row, int n, int lane, uint32_t (&key)[MH])
 {
     float v[MH];
@@ -266,11 +269,12 @@ __device__ __forceinline__ void load_keys(const float *row, int n, int lane, uin
         static_assert(MH % 4 == 0, "whole float4s");
 #pragma unroll
         for (int q = 0; q < MH / 4; ++q) {
-            const float4 f = *reinterpret_cast<const float4 *>(row + min(q * 256 + lane * 4, n - 4));
-            v[4 * q] = f.x;
-            v[4 * q + 1] = f.y;
-            v[4 * q + 2] = f.z;
-            v[4 * q + 3] = f.w;
+            const fx4v *src = reinterpret_cast<const fx4v *>(row + min(q * 256 + lane * 4, n - 4));
+            const fx4v f = NTS ? __builtin_nontemporal_load(src) : *src;
+            v[4 * q] = f[0];
+            v[4 * q + 1] = f[1];
+            v[4 * q + 2] = f[2];
+            v[4 * q + 3] = f[3];
         }
     } else {
 #pragma unroll
@@ -302,14 +306,14 @@ __device__ __forceinline__ void half_select(const uint32_t (&key)[MH], const flo
 // (MH <= 16 slots) load both halves before selecting, so the second row's
 // loads overlap the first selection; longer rows load each half in turn to
 // bound the live registers.
-template <int MH, bool VEC4>
+template <int MH, bool VEC4, bool NTS = false>
 __device__ void half_topk(const float *row0, int n, int k, Stage &st, float (*hs)[64], uint32_t (*hi)[64], int lane)
 {
     const float *row1 = row0 + n;
     if constexpr (MH <= 16) {
         uint32_t key0[MH], key1[MH];
-        load_keys<MH, VEC4>(row0, n, lane, key0);
-        load_keys<MH, VEC4>(row1, n, lane, key1);
+        load_keys<MH, VEC4, NTS>(row0, n, lane, key0);
+        load_keys<MH, VEC4, NTS>(row1, n, lane, key1);
         half_select<MH, VEC4>(key0, row0, 0, n, k, st, hs, hi, lane);
         half_select<MH, VEC4>(key1, row1, 1, n, k, st, hs, hi, lane);
     } else {
@@ -317,7 +321,7 @@ __device__ void half_topk(const float *row0, int n, int k, Stage &st, float (*hs
         for (int p = 0; p < 2; ++p) {
             uint32_t key[MH];
             const float *row = p ? row1 : row0;
-            load_keys<MH, VEC4>(row, n, lane, key);
+            load_keys<MH, VEC4, NTS>(row, n, lane, key);
             half_select<MH, VEC4>(key, row, p, n, k, st, hs, hi, lane);
         }
     }
@@ -371,12 +375,12 @@ __device__ const StairTables kStairTables = make_stair_tables();
 // row0 + n): lane j < k receives the j-th winner's flat row and softmax
 // weight (winners by score desc, flat row asc).  hs / hi: the wave's LDS
 // lists of the two halves' top-k.
-template <int MH, bool VEC4>
+template <int MH, bool VEC4, bool NTS = false>
 __device__ __forceinline__ void select_pair(const float *row0, int n, int k, Stage &st, float (*hs)[64],
                                             uint32_t (*hi)[64], int lane, int32_t &id_out, float &w_out)
 {
     // a4
-    half_topk<MH, VEC4>(row0, n, k, st, hs, hi, lane);
+    half_topk<MH, VEC4, NTS>(row0, n, k, st, hs, hi, lane);
     wave_sync_lds();
 
     // a5 on the staircase: stair[c] = (i << 16) | j for the staircase's
@@ -441,7 +445,7 @@ __global__ __launch_bounds__(64 * WAVES) void select_kernel(const float *__restr
 }
 
 // a4-a7 fused: one workgroup per token.  Its waves first select the
-// token's heads (wave w takes heads w, w + WAVES, ...), keeping the H k
+// token's heads (wave w takes heads w, w + kFusedWaves, ...), keeping the H k
 // (row, weight) pairs in LDS (and writing them out when idx_out is given),
 // then gather the token's output from those pairs with exactly the share
 // and order of the stand-alone gather (a 1 KiB column slice per wave, every
@@ -452,30 +456,33 @@ __global__ __launch_bounds__(64 * WAVES) void select_kernel(const float *__restr
 // not fused: their gather takes two waves per token, and the fused kernel's
 // occupancy would leave half the stand-alone kernel's loads in flight.
 constexpr int kFusedMaxRows = 512;  // H * k held in LDS
+constexpr int kFusedWaves = 4;      // waves per token
 
 template <int MH, int VT, bool NT>
-__global__ __launch_bounds__(64 * WAVES) void select_gather_kernel(const float *__restrict__ scores, int H, int n,
+__global__ __launch_bounds__(64 * kFusedWaves) void select_gather_kernel(const float *__restrict__ scores, int H, int n,
                                                                    int k, const uint8_t *__restrict__ values,
                                                                    const float *__restrict__ scale, int D, int N,
                                                                    int32_t *__restrict__ idx_out,
                                                                    float *__restrict__ w_out, float *__restrict__ out)
 {
     constexpr int EPL = gdev::Fmt<VT>::EPL;
-    __shared__ Stage stage[WAVES];
-    __shared__ float half_score[WAVES][2][64];
-    __shared__ uint32_t half_index[WAVES][2][64];
+    __shared__ Stage stage[kFusedWaves];
+    __shared__ float half_score[kFusedWaves][2][64];
+    __shared__ uint32_t half_index[kFusedWaves][2][64];
     __shared__ int32_t sel_row[kFusedMaxRows];
     __shared__ float sel_w[kFusedMaxRows];
 
     const int lane = threadIdx.x & 63;
     const int wv = threadIdx.x >> 6;
     const int64_t b = blockIdx.x;
-    for (int h = wv; h < H; h += WAVES) {
+    for (int h = wv; h < H; h += kFusedWaves) {
         const int64_t pair = b * H + h;
         int32_t id;
         float wt;
-        select_pair<MH, true>(scores + pair * 2 * (int64_t)n, n, k, stage[wv], half_score[wv], half_index[wv], lane,
-                              id, wt);
+        // scores read non-temporally when the gather's row reads go through
+        // the caches (rows repeat), so the scores do not displace them
+        select_pair<MH, true, !NT>(scores + pair * 2 * (int64_t)n, n, k, stage[wv], half_score[wv], half_index[wv],
+                                   lane, id, wt);
         if (lane < k) {
             sel_row[h * k + lane] = id;
             sel_w[h * k + lane] = wt;
@@ -487,7 +494,7 @@ __global__ __launch_bounds__(64 * WAVES) void select_gather_kernel(const float *
     }
     __syncthreads();
     const int slices = (D + 64 * EPL - 1) / (64 * EPL);
-    for (int sl = wv; sl < slices; sl += WAVES)
+    for (int sl = wv; sl < slices; sl += kFusedWaves)
         gdev::gather_slice<VT, NT>(values, scale, D, N, H * k, sl, sel_row, sel_w, out + b * D, lane);
 }
 
@@ -777,7 +784,7 @@ hipError_t launch_fused(const float *scores, int64_t B, int H, int n, int k, con
 {
     const bool nt = B * H * k < N;  // as the stand-alone gather: rows seldom repeat
     const uint8_t *v = static_cast<const uint8_t *>(values);
-    const dim3 grid((unsigned)B), block(64 * WAVES);
+    const dim3 grid((unsigned)B), block(64 * kFusedWaves);
     if (nt)
         hipLaunchKernelGGL((select_gather_kernel<MH, VT, true>), grid, block, 0, stream, scores, H, n, k, v, scale, D,
                            N, idx, w, out);
