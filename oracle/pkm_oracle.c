@@ -42,8 +42,12 @@
  *     wins in the candidate grid;
  *   - non-finite inputs are undefined (never generated).
  *
- * The backward direction (gradients of a loss through steps 7 -> 1 for
- * the winners the forward selected) is at the end of the file.
+ * Steps 1-3 (pkmo_scores), 4-6 (pkmo_select) and 7 (pkmo_gather) can also
+ * be run on their own, to check the GPU's stages one at a time.  The
+ * backward direction (gradients of a loss through steps 7 -> 1 for the
+ * winners the forward selected), the training-mode batch statistics and
+ * the running statistics BatchNorm1d keeps from them are at the end of the
+ * file.
  *
  * Every floating-point step is fp64; a product of two fp32 inputs is exact
  * in fp64.  Tokens are independent (running-statistics BN), so tokens may be
