@@ -26,10 +26,11 @@ def torch():
     return t
 
 
-@pytest.mark.parametrize("table", ["bf16", "int4"])
-def test_forward_and_backward_graph_replays(torch, table):
+@pytest.mark.parametrize("table,n,D", [("bf16", 64, 256), ("int4", 64, 256),
+                                       ("bf16", 1024, 512)])  # the last: fused select-gather
+def test_forward_and_backward_graph_replays(torch, table, n, D):
     dev = support.device()
-    wl = synthetic.Workload("graph", 300, 256, 2, 64, 16, table, "random")
+    wl = synthetic.Workload("graph", 300, D, 2, n, 16, table, "random")
     params = synthetic.make_params(wl, 3)
     P = pk.params_to_device(params, wl.table, dev)
     mem = pk.Memory(wl.D, wl.H, wl.n, wl.k, wl.table, max_batch=128)  # three chunks

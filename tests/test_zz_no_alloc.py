@@ -87,3 +87,44 @@ def test_noalloc_small_chunks_and_no_selection(torch):
     empty = torch.zeros((0, wl.D), device=support.device())
     pk.forward_noalloc(cfg, P, empty, torch.zeros((0, wl.D), device=support.device()))
     torch.cuda.synchronize()
+
+
+def test_noalloc_graph_replays(torch):
+    """Captured in a HIP graph (what the entry point is for): every replay,
+    with other eager calls that reuse the array between replays, gives the
+    eager call's bits."""
+    wl = synthetic.Workload("nag", 700, 1024, 4, 1024, 32, "bf16", "random")
+    params = synthetic.make_params(wl, seed=6)
+    x = synthetic.make_x(wl, seed=6)
+    dev = support.device()
+    P = pk.params_to_device(params, wl.table, dev)
+    cfg = pk.make_config(wl.D, wl.H, wl.n, wl.k, wl.table, max_batch=256)  # three chunks
+    xt = torch.from_numpy(x).to(dev)
+    say("no-alloc graph: eager reference")
+    ref = [torch.empty((wl.B, wl.D), device=dev), torch.empty((wl.B, wl.H, wl.k), dtype=torch.int32, device=dev),
+           torch.empty((wl.B, wl.H, wl.k), device=dev)]
+    pk.forward_noalloc(cfg, P, xt, *ref)
+    out, idx, w = (torch.empty_like(t) for t in ref)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up off the default stream before capture
+        pk.forward_noalloc(cfg, P, xt, out, idx, w, stream=side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    say("no-alloc graph: capture")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pk.forward_noalloc(cfg, P, xt, out, idx, w)
+    torch.cuda.synchronize()
+    other = torch.empty((300, wl.D), device=dev)
+    for rep in range(3):
+        say("no-alloc graph: replay", rep)
+        out.fill_(float("nan"))
+        idx.fill_(-1)
+        w.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref[0]) and torch.equal(idx, ref[1]) and torch.equal(w, ref[2]), rep
+        pk.forward_noalloc(cfg, P, xt[:300].contiguous(), other)  # eager work on the same array
+        torch.cuda.synchronize()
