@@ -84,6 +84,8 @@ def stage_bytes(wl):
         "gather": work["gather_bytes"] * B + B * H * k * 8 + B * D * 4,
         # fused: read the scores, write the selection, read the rows, write out
         "select_gather": (work["select_bytes"] + work["gather_bytes"]) * B + B * D * 4,
+        # the row exponents: read x, Wq and the subkeys once
+        "exponents": 4 * (B * D + H * D * D + H * n * D),
     }
 
 
@@ -161,21 +163,31 @@ def timed_steps(torch, fn, steps, warmup, stats=None):
 
 
 def kernel_times(torch, mem, P, xt, steps, warmup, wl):
-    """Median ms of each of the forward's kernels, and of the stand-alone
-    select and gather: events between consecutive stage calls on one
-    stream, every iteration enqueued before one final sync."""
+    """Median ms of each of the forward's own launches (pkm_forward_stage:
+    the row exponents, the projection, the scoring, the selection with the
+    gather), and of the stand-alone select and gather on the same scores:
+    events between consecutive calls on one stream, every iteration
+    enqueued before one final sync.  (With a chunked forward the stages
+    are timed through the single-step calls instead, which each compute
+    their own row exponents.)"""
     B = xt.shape[0]
     q = torch.empty((B, mem.heads, mem.dim), dtype=torch.float32, device=xt.device)
     s = torch.empty((B, mem.heads, 2, mem.n_keys), dtype=torch.float32, device=xt.device)
     idx = torch.empty((B, mem.heads, mem.k), dtype=torch.int32, device=xt.device)
     w = torch.empty((B, mem.heads, mem.k), dtype=torch.float32, device=xt.device)
+    idx2, w2 = torch.empty_like(idx), torch.empty_like(w)
     out = torch.empty((B, mem.dim), dtype=torch.float32, device=xt.device)
-    stages = [lambda: mem.query(P, xt, q), lambda: mem.score(P, q, s), lambda: mem.select(s, idx, w),
-              lambda: mem.gather(P, idx, w, out)]
-    names = ["query_gemm", "score_gemm", "select", "gather"]
-    if fused(wl):
-        stages.append(lambda: mem.select_gather(P, s, out, idx, w))
-        names.append("select_gather")
+    out2 = torch.empty_like(out)
+    mem.score(P, mem.query(P, xt, q), s)
+    mem.select(s, idx2, w2)
+    if mem.cfg.max_batch >= B:
+        stages = [lambda st=st: mem.forward_stage(P, xt, st, out, idx, w) for st in range(4)]
+        names = ["exponents", "query_gemm", "score_gemm", "select_gather" if fused(wl) else "select_and_gather"]
+    else:
+        stages = [lambda: mem.query(P, xt, q), lambda: mem.score(P, q, s)]
+        names = ["query_gemm", "score_gemm"]
+    stages += [lambda: mem.select(s, idx2, w2), lambda: mem.gather(P, idx2, w2, out2)]
+    names += ["select", "gather"]
 
     def step():
         for f in stages:
@@ -423,11 +435,13 @@ def main():
         "select": ("hbm", work["select_bytes"] * B / (kt["select"] * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"),
         "gather": ("hbm", work["gather_bytes"] * B / (kt["gather"] * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"),
     }
-    if fused(wl):
+    if "select_gather" in kt:
         rl["select_gather"] = ("hbm", (work["select_bytes"] + work["gather_bytes"]) * B /
                                (kt["select_gather"] * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s")
+    if "exponents" in kt:
+        rl["exponents"] = ("hbm", stage_bytes(wl)["exponents"] / (kt["exponents"] * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s")
     # the forward's own kernels; the dominant one is the headline roofline
-    forward_kernels = ["query_gemm", "score_gemm"] + (["select_gather"] if fused(wl) else ["select", "gather"])
+    forward_kernels = ["query_gemm", "score_gemm"] + (["select_gather"] if "select_gather" in kt else ["select", "gather"])
     dominant = max(forward_kernels, key=kt.get)
 
     def roof(name):

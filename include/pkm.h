@@ -168,6 +168,23 @@ pkm_status pkm_forward(pkm_ctx *ctx, const pkm_params *p, int64_t B, const float
 pkm_status pkm_forward_noalloc(const pkm_config *cfg, const pkm_params *p, int64_t B, const float *x, float *out,
                                int32_t *idx, float *weights, void *stream);
 
+/* For profiling and for callers that interleave other work: one stage of
+ * pkm_forward's own launches, for B <= max_batch tokens (one chunk), the
+ * intermediate results kept in the context's workspace between stages.
+ *   stage 0  the row exponents of x, Wq and the subkeys (the powers of two
+ *            the contractions scale rows by) and clearing q^'s per-half
+ *            maxima
+ *   stage 1  a1-a2, the projection with BN (recording q^'s maxima)
+ *   stage 2  a3, the subkey scoring
+ *   stage 3  a4-a7, the selection and the gather (as pkm_select_gather)
+ * Stages 0, 1, 2, 3 in order on one stream, with the same arguments and no
+ * other call on the context in between, do exactly what pkm_forward does
+ * for those tokens, with the same results.  Arguments as pkm_forward; a
+ * stage reads only those it needs (x: stages 0-1; out, idx, weights:
+ * stage 3).  PKM_E_ARG for a stage outside 0-3 or B > max_batch. */
+pkm_status pkm_forward_stage(pkm_ctx *ctx, const pkm_params *p, int64_t B, const float *x, float *out, int32_t *idx,
+                             float *weights, int stage, void *stream);
+
 /* Steps a1-a2 only: qhat [B, H, D] fp32 = BN_h(Wq[h] . x[b]).  Uses wq and
  * the four BN arrays of p, and the context's workspace for the contraction's
  * row exponents (so, like pkm_forward, one stream per context at a time);

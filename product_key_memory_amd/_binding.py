@@ -20,6 +20,7 @@ EXPORTS = (
     "pkm_score", "pkm_select", "pkm_gather", "pkm_flat_workspace_bytes", "pkm_flat_search",
     "pkm_backward_workspace_bytes", "pkm_backward", "pkm_forward_batch_stats", "pkm_backward_batch_stats",
     "pkm_usage", "pkm_status_str", "pkm_last_error", "pkm_forward_noalloc", "pkm_select_gather",
+    "pkm_forward_stage",
 )
 
 
@@ -62,6 +63,7 @@ def load_library(path=LIB_PATH):
         "pkm_destroy": (None, [vp]),
         "pkm_forward": (ctypes.c_int, [vp, par_p, i64, vp, vp, vp, vp, vp]),
         "pkm_forward_noalloc": (ctypes.c_int, [cfg_p, par_p, i64, vp, vp, vp, vp, vp]),
+        "pkm_forward_stage": (ctypes.c_int, [vp, par_p, i64, vp, vp, vp, vp, ctypes.c_int, vp]),
         "pkm_query": (ctypes.c_int, [vp, par_p, i64, vp, vp, vp]),
         "pkm_score": (ctypes.c_int, [vp, par_p, i64, vp, vp, vp]),
         "pkm_select": (ctypes.c_int, [vp, i64, vp, vp, vp, vp]),
@@ -272,6 +274,21 @@ class Memory:
         _check(self.lib.pkm_forward(self._ctx, ctypes.byref(params.struct), B, _ptr(x), _ptr(out), _ptr(idx),
                                     _ptr(weights), _stream_handle(stream)))
         return out, idx, weights
+
+    def forward_stage(self, params, x, stage, out, idx=None, weights=None, stream=None):
+        """One stage (0-3) of the forward's launches for B <= max_batch
+        tokens; stages 0..3 in order equal forward().  out / idx / weights
+        as forward() takes them (the caller's tensors)."""
+        B = x.shape[0]
+        self.check_params(params)
+        _expect(x, "x", (B, self.dim), "float32", params["wq"].device)
+        _expect(out, "out", (B, self.dim), "float32", x.device)
+        for t, name, dt in ((idx, "idx", "int32"), (weights, "weights", "float32")):
+            if t is not None:
+                _expect(t, name, (B, self.heads, self.k), dt, x.device)
+        _check(self.lib.pkm_forward_stage(self._ctx, ctypes.byref(params.struct), B, _ptr(x), _ptr(out), _ptr(idx),
+                                          _ptr(weights), int(stage), _stream_handle(stream)))
+        return out
 
     def query(self, params, x, qhat=None, stream=None):
         torch = _torch()

@@ -718,7 +718,8 @@ hipError_t prepare_exponents(GemmArgs &a, bool product_b, hipStream_t stream)
 {
     if (a.a_rowmax && a.b_exp_given && !product_b && !a.extra_exp.base) {
         a.b_exp = a.b_exp_given;
-        return a.zero_ptr ? launch_exponents(nullptr, 0, a.zero_ptr, a.zero_n, stream) : hipSuccess;
+        return a.zero_ptr && a.exp_phase != 2 ? launch_exponents(nullptr, 0, a.zero_ptr, a.zero_n, stream)
+                                              : hipSuccess;
     }
     if (!a.exp_ws || a.exp_ws_ints < gemm_exp_ints(a)) return hipErrorInvalidValue;
     if (gemm_exp_ints(a) >= ((int64_t)1 << 31)) return hipErrorInvalidConfiguration;
@@ -747,6 +748,7 @@ hipError_t prepare_exponents(GemmArgs &a, bool product_b, hipStream_t stream)
         const auto &x = a.extra_exp;
         jobs[n++] = exp_job(x.base, x.rows_per_batch, x.batch, x.stride, x.ld, x.K, x.out);
     }
+    if (a.exp_phase == 2) return hipSuccess;  // computed by an earlier launch with these arguments
     return launch_exponents(jobs, n, a.zero_ptr, a.zero_n, stream);
 }
 
@@ -882,7 +884,7 @@ hipError_t launch_gemm_nt_f32(const GemmArgs &args, hipStream_t stream)
     if (args.K % 32 != 0 || args.k_chunk != 0 || args.B2) return hipErrorInvalidValue;
     GemmArgs a = args;
     hipError_t e = prepare_exponents(a, false, stream);
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || a.exp_phase == 1) return e;
     const int64_t tiles = tile_count<BigTile>(a) * a.batch;
     if (tiles >= kCUs) return launch_tile<BigTile>(a, stream);
     // Split K when the contraction is long enough (at least 512 per split)
@@ -921,7 +923,7 @@ hipError_t launch_gemm_nt_f32_product(const GemmArgs &args, hipStream_t stream)
     const bool wide = args.M > 32;
     GemmArgs a = args;
     hipError_t e = prepare_exponents(a, true, stream);
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || a.exp_phase == 1) return e;
     const int kch = a.split_k / kBK;
     const int64_t per_set = (int64_t)((a.key_n + 31) / 32) * kch * 64;
     hipLaunchKernelGGL(split_keys_kernel, dim3((unsigned)((per_set + 255) / 256), 2 * a.batch), dim3(256), 0, stream,

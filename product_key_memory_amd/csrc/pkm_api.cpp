@@ -417,36 +417,67 @@ pkm_status check_forward_args(const pkm_config &c, const pkm_params *p, const fl
     return PKM_OK;
 }
 
+// One stage of the forward for nb <= max_batch tokens, intermediates in the
+// context's workspace: 0 the row exponents of x, Wq and the subkeys (and
+// clearing q^'s maxima), 1 the projection with BN (recording q^'s maxima),
+// 2 the subkey scoring, 3 the selection and the gather (one fused kernel
+// where select_gather_fusable, else two).  keep: write idx / w out.
+pkm_status forward_stage(const pkm_ctx *ctx, const pkm_params *p, int64_t nb, const float *x, float *out,
+                         int32_t *ci, float *cw, bool keep, int stage, hipStream_t st)
+{
+    const pkm_config &c = ctx->cfg;
+    const int64_t H = c.heads, k = c.k;
+    if (stage <= 1) {
+        pkm::GemmArgs a = query_args(c, p, nb, x, ctx->qhat, ctx->gemm_exp, ctx->gemm_exp_ints);
+        a.row_seg_max = ctx->qmax;
+        a.seg_cols = c.dim / 2;
+        a.zero_ptr = ctx->qmax;
+        a.zero_n = nb * 2 * c.heads;
+        // the subkeys' row exponents for the scoring, in the same pre-pass
+        a.extra_exp.base = p->subkeys;
+        a.extra_exp.rows_per_batch = c.n_keys;
+        a.extra_exp.batch = 2 * c.heads;
+        a.extra_exp.stride = (int64_t)c.n_keys * (c.dim / 2);
+        a.extra_exp.ld = c.dim / 2;
+        a.extra_exp.K = c.dim / 2;
+        a.extra_exp.out = ctx->sub_exp;
+        a.exp_phase = stage == 0 ? 1 : 2;
+        return launched(pkm::launch_gemm_nt_f32(a, st), stage == 0 ? "row exponents" : "query projection");
+    }
+    if (stage == 2) {
+        pkm::GemmArgs a = score_args(c, p, nb, ctx->qhat, ctx->scores, ctx->gemm_exp, ctx->gemm_exp_ints);
+        a.a_rowmax = ctx->qmax;
+        a.a_rowmax_ld = 2 * c.heads;
+        a.b_exp_given = ctx->sub_exp;
+        return launched(pkm::launch_gemm_nt_f32(a, st), "subkey scoring");
+    }
+    if (pkm::select_gather_fusable(c.heads, c.n_keys, c.k, c.value_type, c.dim))
+        return launched(pkm::launch_select_gather(ctx->scores, nb, c.heads, c.n_keys, c.k, p->values, p->value_scale,
+                                                  c.value_type, c.dim, c.n_keys * c.n_keys, keep ? ci : nullptr,
+                                                  keep ? cw : nullptr, out, st),
+                        "select and gather");
+    pkm_status s;
+    if ((s = launched(pkm::launch_select(ctx->scores, nb, c.heads, c.n_keys, c.k, ci, cw, st), "select"))) return s;
+    return launched(pkm::launch_gather(p->values, p->value_scale, c.value_type, c.dim, c.n_keys * c.n_keys, nb,
+                                       (int)(H * k), ci, cw, out, st),
+                    "gather");
+}
+
 // a1-a7 over B tokens in chunks of the context's max_batch, every chunk
-// through the context's workspace; launches only.
+// through the context's workspace, its four stages in order; launches only.
 pkm_status forward_chunks(const pkm_ctx *ctx, const pkm_params *p, int64_t B, const float *x, float *out,
                           int32_t *idx, float *weights, hipStream_t st)
 {
     pkm_status s;
     const pkm_config &c = ctx->cfg;
     const int64_t H = c.heads, D = c.dim, k = c.k;
+    const bool keep = idx || weights;
     for (int64_t b0 = 0; b0 < B; b0 += c.max_batch) {
         const int64_t nb = B - b0 < c.max_batch ? B - b0 : c.max_batch;
         int32_t *ci = idx ? idx + b0 * H * k : ctx->idx;
         float *cw = weights ? weights + b0 * H * k : ctx->weights;
-        if ((s = run_query(ctx, p, nb, x + b0 * D, ctx->qhat, ctx->qmax, st))) return s;
-        if ((s = run_score(ctx, p, nb, ctx->qhat, ctx->scores, ctx->qmax, st))) return s;
-        if (pkm::select_gather_fusable(c.heads, c.n_keys, c.k, c.value_type, c.dim)) {
-            // a4-a7 in one kernel; the selection is written out only if asked for
-            const bool keep = idx || weights;
-            if ((s = launched(pkm::launch_select_gather(ctx->scores, nb, c.heads, c.n_keys, c.k, p->values,
-                                                        p->value_scale, c.value_type, c.dim, c.n_keys * c.n_keys,
-                                                        keep ? ci : nullptr, keep ? cw : nullptr, out + b0 * D, st),
-                              "select and gather")))
-                return s;
-            continue;
-        }
-        if ((s = launched(pkm::launch_select(ctx->scores, nb, c.heads, c.n_keys, c.k, ci, cw, st), "select")))
-            return s;
-        if ((s = launched(pkm::launch_gather(p->values, p->value_scale, c.value_type, c.dim, c.n_keys * c.n_keys, nb,
-                                             (int)(H * k), ci, cw, out + b0 * D, st),
-                          "gather")))
-            return s;
+        for (int stage = 0; stage < 4; ++stage)
+            if ((s = forward_stage(ctx, p, nb, x + b0 * D, out + b0 * D, ci, cw, keep, stage, st))) return s;
     }
     return PKM_OK;
 }
@@ -609,6 +640,24 @@ pkm_status pkm_forward_noalloc(const pkm_config *cfg, const pkm_params *p, int64
     workspace_layout(ctx.cfg, sizes, false);
     assign_workspace(&ctx, base, sizes);
     if ((s = forward_chunks(&ctx, p, B, x, out, idx, weights, static_cast<hipStream_t>(stream)))) return s;
+    return ok();
+}
+
+pkm_status pkm_forward_stage(pkm_ctx *ctx, const pkm_params *p, int64_t B, const float *x, float *out, int32_t *idx,
+                             float *weights, int stage, void *stream)
+{
+    pkm_status s;
+    if ((s = check_ctx(ctx)) || (s = check_batch(ctx->cfg, B))) return s;
+    if (stage < 0 || stage > 3) return fail(PKM_E_ARG, "stage must be 0, 1, 2 or 3 (got %d)", stage);
+    if (B > ctx->cfg.max_batch)
+        return fail(PKM_E_ARG, "B = %lld is larger than max_batch = %lld: the stages work on one chunk",
+                    (long long)B, (long long)ctx->cfg.max_batch);
+    if (B == 0) return ok();
+    if ((s = check_forward_args(ctx->cfg, p, x, out, idx, weights))) return s;
+    const bool keep = idx || weights;
+    if ((s = forward_stage(ctx, p, B, x, out, idx ? idx : ctx->idx, weights ? weights : ctx->weights, keep, stage,
+                           static_cast<hipStream_t>(stream))))
+        return s;
     return ok();
 }
 

@@ -87,6 +87,11 @@ struct GemmArgs {
     // instead of splitting every virtual key row in every tile.
     void *b_split;
     int64_t b_split_bytes;
+    // Which part of the work a launch does: 0 the row-exponent pre-pass
+    // (when one is needed) then the contraction; 1 the pre-pass only; 2 the
+    // contraction only, its exponents computed by an earlier phase-1 launch
+    // with the same arguments and workspace.
+    int exp_phase;
     // set by the launcher
     int k_chunk;  // K per split (0: no split)
     const int32_t *a_exp, *b_exp, *b2_exp;

@@ -161,6 +161,7 @@ def test_null_arguments_rejected_before_any_launch():
     assert lib.pkm_score(null, ctypes.byref(params), 1, null, null, null) == pk.PKM_E_ARG
     assert lib.pkm_select(null, 1, null, null, null, null) == pk.PKM_E_ARG
     assert lib.pkm_select_gather(null, ctypes.byref(params), 1, null, null, null, null, null) == pk.PKM_E_ARG
+    assert lib.pkm_forward_stage(null, ctypes.byref(params), 1, null, null, null, null, 0, null) == pk.PKM_E_ARG
     assert lib.pkm_gather(null, ctypes.byref(params), 1, 1, null, null, null, null) == pk.PKM_E_ARG
     assert lib.pkm_flat_search(null, ctypes.byref(params), 1, null, null, 0, null, null, null) == pk.PKM_E_ARG
     grads = pk._binding.GradsStruct()

@@ -100,3 +100,30 @@ def test_unfusable_shape_takes_two_kernels(torch):
     out, _, _ = mem.select_gather(P, s)
     torch.cuda.synchronize()
     assert torch.equal(out, ref)
+
+
+@pytest.mark.parametrize("case", [CASES[0], CASES[1], CASES[4]], ids=_ids)
+def test_forward_stages_compose_to_forward(torch, case):
+    """pkm_forward_stage 0, 1, 2, 3 in order give pkm_forward's bits;
+    a stage outside 0-3 and a batch above max_batch are refused."""
+    B, D, H, n, k, table = case
+    wl = synthetic.Workload("stages", B, D, H, n, k, table, "random")
+    params = synthetic.make_params(wl, seed=24)
+    x = synthetic.make_x(wl, seed=24)
+    P = pk.params_to_device(params, table, support.device())
+    mem = pk.Memory(D, H, n, k, table, max_batch=B)
+    xt = torch.from_numpy(x).to(support.device())
+    say("forward stages", _ids(case))
+    ref = mem.forward(P, xt)
+    out = torch.full_like(ref[0], float("nan"))
+    idx = torch.full_like(ref[1], -1)
+    w = torch.full_like(ref[2], float("nan"))
+    for stage in range(4):
+        mem.forward_stage(P, xt, stage, out, idx, w)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref[0]) and torch.equal(idx, ref[1]) and torch.equal(w, ref[2])
+    with pytest.raises(pk.PkmError):
+        mem.forward_stage(P, xt, 4, out)
+    small = pk.Memory(D, H, n, k, table, max_batch=B - 1)
+    with pytest.raises(pk.PkmError):
+        small.forward_stage(P, xt, 0, out)
