@@ -32,7 +32,7 @@ SCALED = ("e4m3", "int8", "int4")  # tables with a per-row fp32 scale
 ROOT = os.path.dirname(os.path.abspath(__file__))
 # Sources of each kernel: measured HBM traffic is only reported while they
 # are unchanged since the counters were taken.
-KERNEL_SOURCES = {"query_gemm": ["gemm_f32.hip"], "score_gemm": ["gemm_f32.hip"],
+KERNEL_SOURCES = {"exponents": ["gemm_f32.hip"], "query_gemm": ["gemm_f32.hip"], "score_gemm": ["gemm_f32.hip"],
                   "select": ["select.hip", "wave_ops.h"], "gather": ["gather.hip", "gather_dev.h"],
                   "select_gather": ["select.hip", "wave_ops.h", "gather_dev.h"]}
 
@@ -165,11 +165,17 @@ def timed_steps(torch, fn, steps, warmup, stats=None):
 def kernel_times(torch, mem, P, xt, steps, warmup, wl):
     """Median ms of each of the forward's own launches (pkm_forward_stage:
     the row exponents, the projection, the scoring, the selection with the
-    gather), and of the stand-alone select and gather on the same scores:
-    events between consecutive calls on one stream, every iteration
-    enqueued before one final sync.  (With a chunked forward the stages
-    are timed through the single-step calls instead, which each compute
-    their own row exponents.)"""
+    gather), and of the stand-alone select and gather on the same scores.
+
+    Each launch is timed by difference: an event pair brackets a block of
+    launches (the forward's stages 0..s, or nothing, select, select then
+    gather), every block runs once per iteration, and a launch's time is
+    its block's time minus that of the block without it, taken within the
+    iteration and then the median over iterations.  The events' own cost
+    cancels, and each forward stage runs right after the one it follows in
+    the forward.  (With a chunked forward the projection and scoring are
+    timed through the single-step calls instead, which each compute their
+    own row exponents.)"""
     B = xt.shape[0]
     q = torch.empty((B, mem.heads, mem.dim), dtype=torch.float32, device=xt.device)
     s = torch.empty((B, mem.heads, 2, mem.n_keys), dtype=torch.float32, device=xt.device)
@@ -181,29 +187,36 @@ def kernel_times(torch, mem, P, xt, steps, warmup, wl):
     mem.score(P, mem.query(P, xt, q), s)
     mem.select(s, idx2, w2)
     if mem.cfg.max_batch >= B:
-        stages = [lambda st=st: mem.forward_stage(P, xt, st, out, idx, w) for st in range(4)]
-        names = ["exponents", "query_gemm", "score_gemm", "select_gather" if fused(wl) else "select_and_gather"]
+        fwd = [lambda st=st: mem.forward_stage(P, xt, st, out, idx, w) for st in range(4)]
+        fwd_names = ["exponents", "query_gemm", "score_gemm", "select_gather" if fused(wl) else "select_and_gather"]
     else:
-        stages = [lambda: mem.query(P, xt, q), lambda: mem.score(P, q, s)]
-        names = ["query_gemm", "score_gemm"]
-    stages += [lambda: mem.select(s, idx2, w2), lambda: mem.gather(P, idx2, w2, out2)]
-    names += ["select", "gather"]
+        fwd = [lambda: mem.query(P, xt, q), lambda: mem.score(P, q, s)]
+        fwd_names = ["query_gemm", "score_gemm"]
+    single = [lambda: mem.select(s, idx2, w2), lambda: mem.gather(P, idx2, w2, out2)]
+    # blocks[0] is empty; forward stage j is blocks[j + 1] minus blocks[j];
+    # select is the block after the forward's minus the empty one, gather
+    # the next minus that
+    blocks = [[]] + [fwd[:j + 1] for j in range(len(fwd))] + [single[:1], single]
+    pairs = [(j + 1, j) for j in range(len(fwd))] + [(len(fwd) + 1, 0), (len(fwd) + 2, len(fwd) + 1)]
+    names = fwd_names + ["select", "gather"]
 
-    def step():
-        for f in stages:
+    def run(block):
+        for f in block:
             f()
 
-    warm_up(torch, step, warmup)
+    warm_up(torch, lambda: [run(b) for b in blocks], warmup)
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(steps)]
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in blocks]
+          for _ in range(steps)]
     for it in range(steps):
-        ev[it][0].record()
-        for j, f in enumerate(stages):
-            f()
-            ev[it][j + 1].record()
+        for b, (e0, e1) in zip(blocks, ev[it]):
+            e0.record()
+            run(b)
+            e1.record()
     torch.cuda.synchronize()
-    return {nm: float(np.median([ev[it][j].elapsed_time(ev[it][j + 1]) for it in range(steps)]))
-            for j, nm in enumerate(names)}
+    t = [[e0.elapsed_time(e1) for e0, e1 in ev[it]] for it in range(steps)]
+    return {nm: float(np.median([t[it][hi] - t[it][lo] for it in range(steps)]))
+            for nm, (hi, lo) in zip(names, pairs)}
 
 
 def gather_uniform_ms(torch, mem, P, wl, steps, warmup):
@@ -441,7 +454,8 @@ def main():
     if "exponents" in kt:
         rl["exponents"] = ("hbm", stage_bytes(wl)["exponents"] / (kt["exponents"] * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s")
     # the forward's own kernels; the dominant one is the headline roofline
-    forward_kernels = ["query_gemm", "score_gemm"] + (["select_gather"] if "select_gather" in kt else ["select", "gather"])
+    forward_kernels = ((["exponents"] if "exponents" in kt else []) + ["query_gemm", "score_gemm"] +
+                       (["select_gather"] if "select_gather" in kt else ["select", "gather"]))
     dominant = max(forward_kernels, key=kt.get)
 
     def roof(name):
