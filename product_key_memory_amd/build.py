@@ -31,8 +31,28 @@ def _compile(src):
     return obj, r.stderr
 
 
+C_DRIVER_SRC = os.path.join(ROOT, "tests", "c_driver", "pkm_forward_main.c")
+C_DRIVER = os.path.join(ROOT, "tests", "c_driver", "pkm_forward_main")
+
+
+def build_c_driver():
+    """The plain-C test caller of the library (no torch in its process),
+    linked against the in-tree libpkm.so and the HIP runtime."""
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(HIPCC)))
+    cmd = ["gcc", "-std=c11", "-O2", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(rocm, "include"), "-I", os.path.join(ROOT, "include"),
+           C_DRIVER_SRC, "-o", C_DRIVER + ".tmp", "-L", PKG, "-lpkm", "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN/../../product_key_memory_amd", "-Wl,-rpath," + os.path.join(rocm, "lib")]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"gcc failed on {C_DRIVER_SRC}:\n{r.stdout}\n{r.stderr}")
+    os.replace(C_DRIVER + ".tmp", C_DRIVER)
+    return C_DRIVER
+
+
 def build(verbose=False):
-    """Compile every source and link libpkm.so; always rebuilds."""
+    """Compile every source and link libpkm.so, then the plain-C test
+    caller; always rebuilds."""
     os.makedirs(BUILD, exist_ok=True)
     with ThreadPoolExecutor(len(SOURCES)) as ex:
         results = list(ex.map(_compile, SOURCES))
@@ -44,6 +64,7 @@ def build(verbose=False):
     tmp = LIB + ".tmp"
     subprocess.check_call([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs)
     os.replace(tmp, LIB)
+    build_c_driver()
     return LIB
 
 

@@ -224,3 +224,25 @@ def test_struct_layouts_match_the_header(tmp_path):
         body = re.search(r"typedef struct \{([^{}]*)\}\s*" + cname + ";", text).group(1)
         members = re.findall(r"(\w+)\s*;", body)
         assert members == [f for f, _ in py._fields_], cname
+
+
+def test_c_program_rejects_bad_inputs_without_a_device(tmp_path):
+    """The plain-C caller (tests/c_driver) is built and linked, and turns a
+    malformed file or an unsupported configuration into an error before
+    any device call."""
+    import numpy as np
+
+    from product_key_memory_amd import build as pkm_build
+
+    assert os.path.exists(pkm_build.C_DRIVER)
+    bad = tmp_path / "bad.bin"
+    bad.write_bytes(b"NOTPKM00")
+    r = subprocess.run([pkm_build.C_DRIVER, str(bad), str(tmp_path / "o.bin")], capture_output=True, text=True,
+                       timeout=60)
+    assert r.returncode == 1 and "bad magic" in r.stderr
+    odd = tmp_path / "odd.bin"   # D = 63 is not a multiple of 64
+    odd.write_bytes(b"PKMIN1\0\0" + np.array([63, 1, 16, 4, 0, 0], np.int32).tobytes() +
+                    np.array([8, 8], np.int64).tobytes())
+    r = subprocess.run([pkm_build.C_DRIVER, str(odd), str(tmp_path / "o.bin")], capture_output=True, text=True,
+                       timeout=60)
+    assert r.returncode == 1 and "config" in r.stderr, r.stderr

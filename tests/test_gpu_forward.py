@@ -87,6 +87,7 @@ def test_tiny_product_search_equals_flat_search(torch):
     dict(B=129, D=128, H=3, n=64, k=64, table="bf16"),     # k = n_keys: every key is a candidate
     dict(B=77, D=192, H=1, n=300, k=1, table="e4m3"),      # k = 1: argmax of each half
     dict(B=64, D=64, H=2, n=2048, k=64, table="bf16"),     # large n with the largest k
+    dict(B=48, D=64, H=1, n=4096, k=64, table="int4"),     # the largest n_keys (16.8 M rows) and k
     dict(B=1, D=64, H=1, n=2, k=2, table="f32"),           # smallest memory
     dict(B=300, D=320, H=5, n=33, k=33, table="e4m3"),     # k = n, odd sizes, random BN
     dict(B=200, D=256, H=2, n=50, k=10, table="int8"),     # int8 table + row scales
