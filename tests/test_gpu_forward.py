@@ -147,17 +147,27 @@ def test_forward_random_gamma_beta(torch):
     compare(wl, params, x, out, idx, w)
 
 
-def test_chunking_stages_and_determinism(torch):
+@pytest.mark.parametrize("shape", [
+    (1000, 256, 2, 128, 16, "bf16"),
+    (333, 1024, 4, 1024, 32, "bf16"),   # the default widths, a ragged batch (fused select-gather)
+    (70, 64, 3, 40, 8, "f32"),          # subkey rows of 32 floats: two chunks
+    (257, 192, 1, 100, 12, "e4m3"),     # 12- and 6-chunk rows, a ragged 32-row group
+    (40, 2048, 1, 64, 4, "bf16"),       # a wide model, few tokens (small tiles)
+], ids=lambda s: "B{}-D{}-H{}-n{}-k{}-{}".format(*s))
+def test_chunking_stages_and_determinism(torch, shape):
     """Chunked (max_batch < B) and unchunked runs, a second identical run and
-    the four stage calls composed by hand all give bitwise identical
-    results."""
-    wl = synthetic.Workload("chunk", 1000, 256, 2, 128, 16, "bf16", "random")
+    the four single-step calls composed by hand all give bitwise identical
+    results (the forward takes the scoring's row exponents from the
+    projection's recorded maxima and one pre-pass; the single steps compute
+    their own)."""
+    B, D, H, n, k, table = shape
+    wl = synthetic.Workload("chunk", B, D, H, n, k, table, "random")
     params = synthetic.make_params(wl, seed=5)
     x = synthetic.make_x(wl, seed=5)
     P = pk.params_to_device(params, wl.table, support.device())
     a = support.gpu_forward(wl, params, x, max_batch=16384, dev_params=P)
     b = support.gpu_forward(wl, params, x, max_batch=16384, dev_params=P)
-    c = support.gpu_forward(wl, params, x, max_batch=96, dev_params=P)
+    c = support.gpu_forward(wl, params, x, max_batch=min(96, B - 1), dev_params=P)
     for u, v in zip(a, b):
         assert (u == v).all()
     for u, v in zip(a, c):
