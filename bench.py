@@ -273,15 +273,17 @@ def flat_vs_product(torch, pk, wl, P, xt, kt, tokens=64, steps=5, warmup=2):
             "product_us_per_token_full_batch": round(full_batch_us, 5),
             "speedup_per_token": round(flat_ms * 1e3 / tokens / full_batch_us, 1),
             "flat_gemm_tflops": round(flat_flop / (flat_ms * 1e-3) / 1e12, 2),
+            "flat_gemm_frac": round(flat_flop / (flat_ms * 1e-3) / 1e12 / GEMM_PEAK_TFLOPS, 4),
             "same_winner_sets": same,
             "key_scores_per_token_head": {"flat": wl.N, "product": 2 * wl.n}, "candidates_per_token_head": wl.k ** 2}
 
 
-def backward_step(torch, mem, wl, P, xt, idx, wts, fwd_ms, steps, warmup):
+def backward_step(torch, mem, wl, P, xt, idx, wts, dout, fwd_ms, steps, warmup):
     """The gradients of a loss through the same batch (pkm_backward): every
     parameter gradient, dx and the dense fp32 value-table gradient (and
-    again with the value gradient's sparse form)."""
-    dout = torch.randn((wl.B, wl.D), dtype=torch.float32, device="cuda", generator=torch.Generator("cuda").manual_seed(1))
+    again with the value gradient's sparse form).  Against a composite
+    ideal: the three contractions at the MFMA ceiling plus the step's
+    algorithmic HBM bytes at 8 TB/s."""
     grads = {"dx": (wl.B, wl.D), "dwq": (wl.H, wl.D, wl.D), "dbn_gamma": (wl.H, wl.D), "dbn_beta": (wl.H, wl.D),
              "dsubkeys": (wl.H, 2, wl.n, wl.D // 2), "dvalues": (wl.N, wl.D)}
     grads = {name: torch.zeros(shape, dtype=torch.float32, device="cuda") for name, shape in grads.items()}
@@ -310,7 +312,17 @@ def backward_step(torch, mem, wl, P, xt, idx, wts, fwd_ms, steps, warmup):
                             steps, warmup)
     # GEMM work of the backward: the recomputed q, dWq and dx (2 B H D^2 each)
     flop = 2.0 * wl.B * wl.H * wl.D * wl.D * 3
+    B, H, D, n = wl.B, wl.H, wl.D, wl.n
+    hbm = (per_token_work(wl)["gather_bytes"] * B  # the selected value rows, for dout . V[row]
+           + 2 * touched * D * 4                   # the dense value gradient's touched rows, read and written
+           + 2 * H * n * D * 4                     # the subkey gradient, read and written
+           + 2 * H * D * D * 4                     # dWq, read and written
+           + 2 * B * H * D * 4                     # q recomputed: written, read back
+           + 3 * B * D * 4)                        # x and dout read, dx written
+    ideal_us = (flop / (GEMM_PEAK_TFLOPS * 1e12) + hbm / (HBM_PEAK_GBS * 1e9)) * 1e6
     return {"ms": round(ms, 4), "tokens_per_s": round(wl.B / (ms * 1e-3), 1),
+            "composite_ideal_us": round(ideal_us, 1), "composite_frac": round(ideal_us * 1e-3 / ms, 4),
+            "hbm_bytes": int(hbm), "gemm_us_at_mfma_ceiling": round(flop / (GEMM_PEAK_TFLOPS * 1e12) * 1e6, 1),
             "forward_backward_tokens_per_s": round(wl.B / ((ms + fwd_ms) * 1e-3), 1),
             "sparse_value_grad_ms": round(sparse_ms, 4), "rows_touched": touched,
             "batch_stats_forward_ms": round(fwd_bs_ms, 4), "batch_stats_backward_ms": round(bwd_bs_ms, 4),
@@ -383,6 +395,37 @@ def cpu_baseline(wl, params, x, seconds=10.0):
                       f"full lookup in fp64, {dt:.1f} s wall on {cores} threads",
             "single_core_value": one / dt1,
             "single_core_sample": f"first {one} tokens on 1 thread, {dt1:.1f} s wall"}
+
+
+def cpu_backward_baseline(wl, params, x, dout, seconds=10.0):
+    """The fp64 oracle's backward (every gradient, the dense value gradient
+    over all N rows included) on the same cores as cpu_baseline, over the
+    first tokens of the batch: a one-token call measures the part that does
+    not grow with the tokens (the value gradient's N x D fp64 array, zeroed
+    per call), a small one the rate per token, and the sample is sized to
+    the time budget from the two."""
+    import oracle
+
+    hc = host_cores()
+    cores = hc["affinity_count"]
+    if hc["cgroup_cpu_quota"]:
+        cores = max(1, min(cores, int(hc["cgroup_cpu_quota"])))
+    model = oracle.Model.from_params(params, wl.k, wl.table)
+    t0 = time.perf_counter()
+    oracle.backward(model, x[:1], dout[:1], nthreads=cores)
+    fixed = time.perf_counter() - t0
+    probe = min(x.shape[0], 2 * cores)
+    t0 = time.perf_counter()
+    oracle.backward(model, x[:probe], dout[:probe], nthreads=cores)
+    per_token = max(time.perf_counter() - t0 - fixed, 1e-6) / probe
+    sample = int(min(x.shape[0], max(probe, (seconds - fixed) / per_token)))
+    t0 = time.perf_counter()
+    oracle.backward(model, x[:sample], dout[:sample], nthreads=cores)
+    dt = time.perf_counter() - t0
+    return {"value": sample / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"the first {sample} of the {wl.B} tokens of the {wl.name} workload, every gradient in fp64 "
+                      f"(the dense value gradient over all {wl.N} rows, {wl.N * wl.D * 8 / 2**30:.1f} GiB, "
+                      f"{fixed:.1f} s of each call), {dt:.1f} s wall on {cores} threads"}
 
 
 def main():
@@ -495,8 +538,13 @@ def main():
     if not args.no_flat:
         line["flat_vs_product"] = flat_vs_product(torch, pk, wl, P, xt, kt)
     if not args.no_backward:
-        line["backward"] = backward_step(torch, mem, wl, P, xt, idx, wts, ms, max(5, args.steps // 5),
+        dout = torch.randn((wl.B, wl.D), dtype=torch.float32, device="cuda",
+                           generator=torch.Generator("cuda").manual_seed(1))
+        line["backward"] = backward_step(torch, mem, wl, P, xt, idx, wts, dout, ms, max(5, args.steps // 5),
                                          max(2, args.warmup // 5))
+        if not args.no_cpu_baseline:
+            line["backward"]["cpu_baseline"] = cpu_backward_baseline(wl, params, x, dout.cpu().numpy(),
+                                                                     args.cpu_seconds)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, params, x, args.cpu_seconds)
     print(json.dumps(line), flush=True)
