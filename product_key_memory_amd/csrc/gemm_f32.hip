@@ -85,6 +85,7 @@ typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 typedef int32_t i4 __attribute__((ext_vector_type(4)));
 
 constexpr int kCUs = 256;     // MI355X compute units
+constexpr int kXcds = 8;      // its accelerator dies, each with its own L2
 constexpr int kBK = 16;       // k per chunk: one v_mfma_f32_32x32x16_f16 step
 constexpr int kPieces = 2;    // fp16 pieces per fp32 operand
 constexpr int kPieceDw = 8;   // dwords per piece in an LDS row (16 fp16)
@@ -570,12 +571,21 @@ __global__ __launch_bounds__(T::THREADS) void gemm_nt_f32_kernel(GemmArgs a)
     extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
     const int tiles_n = (a.N + T::BN - 1) / T::BN;
     if constexpr (PERSIST) {
-        const int tiles = ((a.M + T::BM - 1) / T::BM) * tiles_n;
-        const int64_t total = (int64_t)tiles * a.batch;
-        for (int64_t t = blockIdx.x; t < total; t += gridDim.x) {
-            const int g = (int)(t / tiles);
-            const int r = (int)(t - (int64_t)g * tiles);
-            gemm_tile<T, BN_EPILOGUE, STREAM_OUT, PRODUCT_B, ACCUMULATE>(a, r / tiles_n, r % tiles_n, g, 0, smem);
+        // Workgroups are dealt to the XCDs in turn (workgroup w on XCD w %
+        // kXcds, each XCD with its own L2).  Each XCD takes whole rows of
+        // tiles -- (batch entry, row tile) pairs r with r % kXcds its own --
+        // so a block of A rows is fetched into one L2 for all its column
+        // tiles instead of into every XCD's.  Every tile is computed once,
+        // the same way, whichever workgroup takes it.
+        const int tiles_m = (a.M + T::BM - 1) / T::BM;
+        const int rows = tiles_m * a.batch;
+        const int xcd = blockIdx.x % kXcds, per_xcd = gridDim.x / kXcds;
+        const int64_t mine = (int64_t)((rows - xcd + kXcds - 1) / kXcds) * tiles_n;
+        for (int64_t e = blockIdx.x / kXcds; e < mine; e += per_xcd) {
+            const int j = (int)(e / tiles_n), tn = (int)(e - (int64_t)j * tiles_n);
+            const int r = xcd + kXcds * j;
+            const int g = r / tiles_m;
+            gemm_tile<T, BN_EPILOGUE, STREAM_OUT, PRODUCT_B, ACCUMULATE>(a, r - g * tiles_m, tn, g, 0, smem);
             __syncthreads();
         }
     } else {
@@ -817,8 +827,13 @@ hipError_t launch_variant(const GemmArgs &a, hipStream_t stream)
     }
     dim3 grid((unsigned)tile_count<T>(a), a.batch, a.k_chunk ? (a.K + a.k_chunk - 1) / a.k_chunk : 1);
     if constexpr (PERSIST) {
+        // kCUs workgroups, kCUs / kXcds per XCD (the kernel's tile order
+        // needs a whole number per XCD; launch_tile persists only with more
+        // tiles than kCUs)
+        static_assert(kCUs % kXcds == 0, "workgroups per XCD");
         const int64_t total = tile_count<T>(a) * a.batch;
-        grid = dim3((unsigned)(total < kCUs ? total : kCUs), 1, 1);
+        if (total <= kCUs) return hipErrorInvalidConfiguration;
+        grid = dim3((unsigned)kCUs, 1, 1);
     }
     hipLaunchKernelGGL(kernel, grid, dim3(T::THREADS), T::LDS_BYTES, stream, a);
     return hipGetLastError();
