@@ -828,11 +828,11 @@ hipError_t launch_variant(const GemmArgs &a, hipStream_t stream)
     dim3 grid((unsigned)tile_count<T>(a), a.batch, a.k_chunk ? (a.K + a.k_chunk - 1) / a.k_chunk : 1);
     if constexpr (PERSIST) {
         // kCUs workgroups, kCUs / kXcds per XCD (the kernel's tile order
-        // needs a whole number per XCD; launch_tile persists only with more
-        // tiles than kCUs)
+        // needs a whole number per XCD; launch_tile persists only with at
+        // least kCUs tiles)
         static_assert(kCUs % kXcds == 0, "workgroups per XCD");
         const int64_t total = tile_count<T>(a) * a.batch;
-        if (total <= kCUs) return hipErrorInvalidConfiguration;
+        if (total < kCUs) return hipErrorInvalidConfiguration;
         grid = dim3((unsigned)kCUs, 1, 1);
     }
     hipLaunchKernelGGL(kernel, grid, dim3(T::THREADS), T::LDS_BYTES, stream, a);
@@ -847,9 +847,10 @@ hipError_t launch_tile(const GemmArgs &a, hipStream_t stream)
         if (a.bn_mean || a.stream_out) return hipErrorInvalidValue;
         return launch_variant<T, false, false, false, true>(a, stream);
     }
-    // More 256x256 tiles than CUs: one workgroup per CU walks its tiles, so
-    // the stores of one tile drain while the next one computes
-    const bool persist = T::PING_PONG && !a.k_chunk && tile_count<T>(a) * a.batch > kCUs;
+    // At least as many 256x256 tiles as CUs: one workgroup per CU walks its
+    // tiles in the XCD-aware order, and the stores of one tile drain while
+    // the next one computes
+    const bool persist = T::PING_PONG && !a.k_chunk && tile_count<T>(a) * a.batch >= kCUs;
     if (a.bn_mean) {
         if (a.stream_out) return launch_variant<T, true, true>(a, stream);
         if (persist) return launch_variant<T, true, false, false, false, true>(a, stream);
