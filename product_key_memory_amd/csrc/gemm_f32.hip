@@ -575,15 +575,21 @@ __global__ __launch_bounds__(T::THREADS) void gemm_nt_f32_kernel(GemmArgs a)
         // kXcds, each XCD with its own L2).  Each XCD takes whole rows of
         // tiles -- (batch entry, row tile) pairs r with r % kXcds its own --
         // so a block of A rows is fetched into one L2 for all its column
-        // tiles instead of into every XCD's.  Every tile is computed once,
-        // the same way, whichever workgroup takes it.
+        // tiles instead of into every XCD's.  Where that would leave XCDs
+        // short of rows (fewer rounds of tiles in plain order), the tiles go
+        // round-robin instead.  Every tile is computed once, the same way,
+        // whichever workgroup takes it.
         const int tiles_m = (a.M + T::BM - 1) / T::BM;
         const int rows = tiles_m * a.batch;
+        const int64_t total = (int64_t)rows * tiles_n;
         const int xcd = blockIdx.x % kXcds, per_xcd = gridDim.x / kXcds;
-        const int64_t mine = (int64_t)((rows - xcd + kXcds - 1) / kXcds) * tiles_n;
-        for (int64_t e = blockIdx.x / kXcds; e < mine; e += per_xcd) {
+        const int64_t rows_rounds = ((int64_t)((rows + kXcds - 1) / kXcds) * tiles_n + per_xcd - 1) / per_xcd;
+        const bool by_rows = rows_rounds <= (total + gridDim.x - 1) / gridDim.x;
+        const int64_t count = by_rows ? (int64_t)((rows - xcd + kXcds - 1) / kXcds) * tiles_n : total;
+        const int64_t step = by_rows ? per_xcd : gridDim.x;
+        for (int64_t e = by_rows ? blockIdx.x / kXcds : blockIdx.x; e < count; e += step) {
             const int j = (int)(e / tiles_n), tn = (int)(e - (int64_t)j * tiles_n);
-            const int r = xcd + kXcds * j;
+            const int r = by_rows ? xcd + kXcds * j : j;  // (batch entry, row tile) pair
             const int g = r / tiles_m;
             gemm_tile<T, BN_EPILOGUE, STREAM_OUT, PRODUCT_B, ACCUMULATE>(a, r - g * tiles_m, tn, g, 0, smem);
             __syncthreads();

@@ -151,6 +151,7 @@ def test_forward_random_gamma_beta(torch):
     (1000, 256, 2, 128, 16, "bf16"),
     (333, 1024, 4, 1024, 32, "bf16"),   # the default widths, a ragged batch (fused select-gather)
     (4500, 1024, 4, 1024, 32, "bf16"),  # more tiles than CUs in both contractions (one workgroup per CU walks them)
+    (300, 1024, 32, 64, 8, "bf16"),     # a wide projection over few tokens: 256 tiles in 2 rows (plain order)
     (70, 64, 3, 40, 8, "f32"),          # subkey rows of 32 floats: two chunks
     (257, 192, 1, 100, 12, "e4m3"),     # 12- and 6-chunk rows, a ragged 32-row group
     (40, 2048, 1, 64, 4, "bf16"),       # a wide model, few tokens (small tiles)
