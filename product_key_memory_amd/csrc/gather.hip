@@ -24,7 +24,11 @@ namespace {
 
 using namespace gdev;
 
-constexpr int WAVES = 4;
+// Waves per workgroup: eight for the slice kernel (measured 4 / 8 / 16 at
+// the default shape and large_memory: 8 the fastest for the bf16, E4M3 and
+// int8 tables), four for the paired kernel (int4 rows: 8 was 12 % slower).
+constexpr int WAVES = 8;
+constexpr int PAIR_WAVES = 4;
 constexpr int kPairSplit = 2;  // waves per token in gather_pair_kernel
 
 template <int VT, bool NT>
@@ -48,17 +52,17 @@ __global__ __launch_bounds__(64 * WAVES) void gather_kernel(const uint8_t *__res
 // SPLIT 2 is the fastest of 1, 2 and 4, all near 4 TB/s: 512-byte random
 // rows.)
 template <int VT, int SPLIT, bool NT>
-__global__ __launch_bounds__(64 * WAVES) void gather_pair_kernel(const uint8_t *__restrict__ values,
+__global__ __launch_bounds__(64 * PAIR_WAVES) void gather_pair_kernel(const uint8_t *__restrict__ values,
                                                                  const float *__restrict__ scale, int D, int N,
                                                                  int64_t B, int R, const int32_t *__restrict__ idx,
                                                                  const float *__restrict__ w,
                                                                  float *__restrict__ out)
 {
     constexpr int EPL = Fmt<VT>::EPL;
-    __shared__ float part[SPLIT > 1 ? SPLIT - 1 : 1][WAVES / SPLIT][EPL][32];
+    __shared__ float part[SPLIT > 1 ? SPLIT - 1 : 1][PAIR_WAVES / SPLIT][EPL][32];
     const int lane = threadIdx.x & 63, wave = (threadIdx.x >> 6) % SPLIT, slot = (threadIdx.x >> 6) / SPLIT;
-    const int64_t b = (int64_t)blockIdx.x * (WAVES / SPLIT) + slot;
-    if ((int64_t)blockIdx.x * (WAVES / SPLIT) >= B) return;  // whole workgroup past the end
+    const int64_t b = (int64_t)blockIdx.x * (PAIR_WAVES / SPLIT) + slot;
+    if ((int64_t)blockIdx.x * (PAIR_WAVES / SPLIT) >= B) return;  // whole workgroup past the end
     const bool live = b < B;
     const int64_t bb = live ? b : 0;
     float acc[EPL];
@@ -90,14 +94,14 @@ hipError_t launch(const void *values, const float *scale, int D, int N, int64_t 
     const uint8_t *v = static_cast<const uint8_t *>(values);
     if (elem_bytes<VT>(D) <= 512) {
         constexpr int SPLIT = kPairSplit;
-        const int64_t blocks = (B + WAVES / SPLIT - 1) / (WAVES / SPLIT);
+        const int64_t blocks = (B + PAIR_WAVES / SPLIT - 1) / (PAIR_WAVES / SPLIT);
         if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
         if (nt)
-            hipLaunchKernelGGL((gather_pair_kernel<VT, SPLIT, true>), dim3((unsigned)blocks), dim3(64 * WAVES), 0,
-                               stream, v, scale, D, N, B, R, idx, w, out);
+            hipLaunchKernelGGL((gather_pair_kernel<VT, SPLIT, true>), dim3((unsigned)blocks), dim3(64 * PAIR_WAVES),
+                               0, stream, v, scale, D, N, B, R, idx, w, out);
         else
-            hipLaunchKernelGGL((gather_pair_kernel<VT, SPLIT, false>), dim3((unsigned)blocks), dim3(64 * WAVES), 0,
-                               stream, v, scale, D, N, B, R, idx, w, out);
+            hipLaunchKernelGGL((gather_pair_kernel<VT, SPLIT, false>), dim3((unsigned)blocks), dim3(64 * PAIR_WAVES),
+                               0, stream, v, scale, D, N, B, R, idx, w, out);
         return hipGetLastError();
     }
     const int width = 64 * Fmt<VT>::EPL;  // columns per wave
