@@ -5,7 +5,8 @@
 // rows are read).
 //
 // This is the HBM-bound step: every selected row is a random 0.5-4 KiB read.
-// A wave64 owns one (token, column slice): each lane reads 16 contiguous bytes
+// A wave64 owns one (token, column slice) -- or a whole token when its rows
+// are exactly two slices long (gather_two_slices): each lane reads 16 contiguous bytes
 // of a row (4 fp32, 8 bf16, 16 E4M3 or int8, or 32 int4 values), so one
 // row-slice is one fully coalesced 1 KiB request, and keeps its fp32 partial
 // sums in registers.  Scaled formats (E4M3, int8, int4) fold the row's scale
@@ -39,6 +40,10 @@ __global__ __launch_bounds__(64 * WAVES) void gather_kernel(const uint8_t *__res
 {
     const int lane = threadIdx.x & 63;
     const int64_t wid = (int64_t)blockIdx.x * WAVES + (threadIdx.x >> 6);
+    if (slices == 2) {  // one wave per token reads its rows whole
+        if (wid < B) gather_two_slices<VT, NT>(values, scale, D, N, R, idx + wid * R, w + wid * R, out + wid * D, lane);
+        return;
+    }
     if (wid >= B * slices) return;
     const int64_t b = wid / slices;
     const int s = (int)(wid - b * slices);
@@ -106,7 +111,7 @@ hipError_t launch(const void *values, const float *scale, int D, int N, int64_t 
     }
     const int width = 64 * Fmt<VT>::EPL;  // columns per wave
     const int slices = (D + width - 1) / width;
-    const int64_t waves = B * slices;
+    const int64_t waves = B * (slices == 2 ? 1 : slices);  // two slices: one wave per token
     const int64_t blocks = (waves + WAVES - 1) / WAVES;
     if (nt)
         hipLaunchKernelGGL((gather_kernel<VT, true>), dim3((unsigned)blocks), dim3(64 * WAVES), 0, stream, v, scale,

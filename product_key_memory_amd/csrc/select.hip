@@ -448,9 +448,9 @@ __global__ __launch_bounds__(64 * WAVES) void select_kernel(const float *__restr
 // token's heads (wave w takes heads w, w + kFusedWaves, ...), keeping the H k
 // (row, weight) pairs in LDS (and writing them out when idx_out is given),
 // then gather the token's output from those pairs with exactly the share
-// and order of the stand-alone gather (a 1 KiB column slice per wave, every
-// row in order), so the result is bitwise the same as select followed by
-// gather.  The selection is ALU-bound and the gather HBM-bound; with
+// and order of the stand-alone gather (a 1 KiB column slice per wave, or
+// whole rows in wave 0 when they are two slices long; every row in order),
+// so the result is bitwise the same as select followed by gather.  The selection is ALU-bound and the gather HBM-bound; with
 // several tokens' workgroups on a CU, one token's selection runs while
 // another token's row loads are in flight.  Rows of at most 512 bytes are
 // not fused: their gather takes two waves per token, and the fused kernel's
@@ -494,6 +494,10 @@ __global__ __launch_bounds__(64 * kFusedWaves) void select_gather_kernel(const f
     }
     __syncthreads();
     const int slices = (D + 64 * EPL - 1) / (64 * EPL);
+    if (slices == 2) {  // as the stand-alone gather: one wave reads the rows whole
+        if (wv == 0) gdev::gather_two_slices<VT, NT>(values, scale, D, N, H * k, sel_row, sel_w, out + b * D, lane);
+        return;
+    }
     for (int sl = wv; sl < slices; sl += kFusedWaves)
         gdev::gather_slice<VT, NT>(values, scale, D, N, H * k, sl, sel_row, sel_w, out + b * D, lane);
 }

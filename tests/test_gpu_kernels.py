@@ -110,7 +110,10 @@ def test_bf16_decode_every_code(torch):
 
 @pytest.mark.parametrize("table", ["f32", "bf16", "e4m3", "int8", "int4"])
 @pytest.mark.parametrize("D,n,B,R", [(64, 16, 5, 4), (512, 64, 33, 16), (1024, 32, 17, 128), (1024, 32, 9, 130),
-                                     (192, 8, 7, 1), (2048, 16, 3, 67)])
+                                     (192, 8, 7, 1), (2048, 16, 3, 67),
+                                     # rows of two column slices, the second one partial (fp32 at 384, bf16 at
+                                     # 768) or full (int4 at 4096): one wave reads them whole
+                                     (384, 16, 9, 33), (768, 32, 11, 20), (4096, 8, 3, 9)])
 def test_gather_parity(torch, table, D, n, B, R):
     """Gather fed the same rows and fp32 weights as the oracle.  Both decode
     the same stored bits exactly; the only difference is fp32 vs fp64
