@@ -310,6 +310,12 @@ def backward_step(torch, mem, wl, P, xt, idx, wts, dout, fwd_ms, steps, warmup):
     bm, bv = stats["r"][3], stats["r"][4]
     bwd_bs_ms = timed_steps(torch, lambda: mem.backward(P, xt, idx, wts, dout, grads, ws, batch_stats=(bm, bv)),
                             steps, warmup)
+    # training with running statistics: the forward that also keeps the
+    # projection before BN, and the backward that takes it instead of
+    # computing it again
+    q = torch.empty((wl.B, wl.H, wl.D), dtype=torch.float32, device="cuda")
+    fwd_q_ms = timed_steps(torch, lambda: mem.forward_train(P, xt, out, idx, wts, q), steps, warmup)
+    bwd_q_ms = timed_steps(torch, lambda: mem.backward(P, xt, idx, wts, dout, grads, ws, q=q), steps, warmup)
     # GEMM work of the backward: the recomputed q, dWq and dx (2 B H D^2 each)
     flop = 2.0 * wl.B * wl.H * wl.D * wl.D * 3
     B, H, D, n = wl.B, wl.H, wl.D, wl.n
@@ -320,6 +326,8 @@ def backward_step(torch, mem, wl, P, xt, idx, wts, dout, fwd_ms, steps, warmup):
            + 2 * B * H * D * 4                     # q recomputed: written, read back
            + 3 * B * D * 4)                        # x and dout read, dx written
     ideal_us = (flop / (GEMM_PEAK_TFLOPS * 1e12) + hbm / (HBM_PEAK_GBS * 1e9)) * 1e6
+    # with q given: two contractions, q read once instead of written and read
+    ideal_q_us = (flop * 2 / 3 / (GEMM_PEAK_TFLOPS * 1e12) + (hbm - B * H * D * 4) / (HBM_PEAK_GBS * 1e9)) * 1e6
     return {"ms": round(ms, 4), "tokens_per_s": round(wl.B / (ms * 1e-3), 1),
             "composite_ideal_us": round(ideal_us, 1), "composite_frac": round(ideal_us * 1e-3 / ms, 4),
             "hbm_bytes": int(hbm), "gemm_us_at_mfma_ceiling": round(flop / (GEMM_PEAK_TFLOPS * 1e12) * 1e6, 1),
@@ -327,6 +335,9 @@ def backward_step(torch, mem, wl, P, xt, idx, wts, dout, fwd_ms, steps, warmup):
             "sparse_value_grad_ms": round(sparse_ms, 4), "rows_touched": touched,
             "batch_stats_forward_ms": round(fwd_bs_ms, 4), "batch_stats_backward_ms": round(bwd_bs_ms, 4),
             "batch_stats_forward_backward_tokens_per_s": round(wl.B / ((fwd_bs_ms + bwd_bs_ms) * 1e-3), 1),
+            "forward_train_ms": round(fwd_q_ms, 4), "with_saved_q_ms": round(bwd_q_ms, 4),
+            "with_saved_q_composite_frac": round(ideal_q_us * 1e-3 / bwd_q_ms, 4),
+            "forward_backward_saved_q_tokens_per_s": round(wl.B / ((fwd_q_ms + bwd_q_ms) * 1e-3), 1),
             "gemm_flop": flop, "gemm_tflops_if_all_time": round(flop / (ms * 1e-3) / 1e12, 2),
             "workspace_bytes": mem.backward_workspace_bytes()}
 

@@ -20,7 +20,7 @@ EXPORTS = (
     "pkm_score", "pkm_select", "pkm_gather", "pkm_flat_workspace_bytes", "pkm_flat_search",
     "pkm_backward_workspace_bytes", "pkm_backward", "pkm_forward_batch_stats", "pkm_backward_batch_stats",
     "pkm_usage", "pkm_status_str", "pkm_last_error", "pkm_forward_noalloc", "pkm_select_gather",
-    "pkm_forward_stage",
+    "pkm_forward_stage", "pkm_forward_train", "pkm_backward_with_q",
 )
 
 
@@ -78,6 +78,9 @@ def load_library(path=LIB_PATH):
                                                     ctypes.POINTER(GradsStruct), vp, ctypes.c_size_t, vp]),
         "pkm_backward": (ctypes.c_int, [vp, par_p, i64, vp, vp, vp, vp, ctypes.POINTER(GradsStruct), vp,
                                         ctypes.c_size_t, vp]),
+        "pkm_forward_train": (ctypes.c_int, [vp, par_p, i64, vp, vp, vp, vp, vp, vp]),
+        "pkm_backward_with_q": (ctypes.c_int, [vp, par_p, i64, vp, vp, vp, vp, vp, ctypes.POINTER(GradsStruct), vp,
+                                               ctypes.c_size_t, vp]),
         "pkm_status_str": (ctypes.c_char_p, [ctypes.c_int]),
         "pkm_last_error": (ctypes.c_char_p, []),
     }
@@ -275,6 +278,25 @@ class Memory:
                                     _ptr(weights), _stream_handle(stream)))
         return out, idx, weights
 
+    def forward_train(self, params, x, out=None, idx=None, weights=None, q=None, stream=None):
+        """forward() that also writes the projection before BN, q [B,H,D]
+        f32, for backward(..., q=q).  Returns (out, idx, weights, q)."""
+        torch = _torch()
+        B = x.shape[0]
+        self.check_params(params)
+        _expect(x, "x", (B, self.dim), "float32", params["wq"].device)
+        out = self._new((B, self.dim), torch.float32, x) if out is None else out
+        idx = self._new((B, self.heads, self.k), torch.int32, x) if idx is None else idx
+        weights = self._new((B, self.heads, self.k), torch.float32, x) if weights is None else weights
+        q = self._new((B, self.heads, self.dim), torch.float32, x) if q is None else q
+        _expect(out, "out", (B, self.dim), "float32", x.device)
+        _expect(idx, "idx", (B, self.heads, self.k), "int32", x.device)
+        _expect(weights, "weights", (B, self.heads, self.k), "float32", x.device)
+        _expect(q, "q", (B, self.heads, self.dim), "float32", x.device)
+        _check(self.lib.pkm_forward_train(self._ctx, ctypes.byref(params.struct), B, _ptr(x), _ptr(out), _ptr(idx),
+                                          _ptr(weights), _ptr(q), _stream_handle(stream)))
+        return out, idx, weights, q
+
     def forward_stage(self, params, x, stage, out, idx=None, weights=None, stream=None):
         """One stage (0-3) of the forward's launches for B <= max_batch
         tokens; stages 0..3 in order equal forward().  out / idx / weights
@@ -405,7 +427,7 @@ class Memory:
         return out, idx, weights, mean, var
 
     def backward(self, params, x, idx, weights, dout, grads=None, workspace=None, stream=None, batch_stats=None,
-                 sparse_values=False):
+                 sparse_values=False, q=None):
         """Gradients of a loss given dout = dL/dout [B, D] for the winners
         (idx, weights) a forward call returned.  grads: dict name -> tensor
         (parameter gradients are added to, dx is overwritten; a missing name
@@ -416,7 +438,9 @@ class Memory:
         the first dvalues_count entries hold the touched rows in increasing
         order and their gradients.  batch_stats: (mean, var) from
         forward_batch_stats for the training-mode BN backward, or None
-        (running statistics).  Returns the dict."""
+        (running statistics).  q: the projection before BN from
+        forward_train, used instead of computing it again (running
+        statistics only).  Returns the dict."""
         torch = _torch()
         B = x.shape[0]
         D, H, n, k = self.dim, self.heads, self.n_keys, self.k
@@ -444,7 +468,14 @@ class Memory:
             workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
         _expect(workspace, "workspace", (workspace.numel(),), "uint8", dev)
         gs = GradsStruct(*[None if grads.get(nm) is None else grads[nm].data_ptr() for nm in GRAD_NAMES])
-        if batch_stats is None:
+        if q is not None:
+            if batch_stats is not None:
+                raise ValueError("q (from forward_train) goes with running statistics only")
+            _expect(q, "q", (B, H, D), "float32", dev)
+            _check(self.lib.pkm_backward_with_q(self._ctx, ctypes.byref(params.struct), B, _ptr(x), _ptr(q),
+                                                _ptr(idx), _ptr(weights), _ptr(dout), ctypes.byref(gs),
+                                                _ptr(workspace), workspace.numel(), _stream_handle(stream)))
+        elif batch_stats is None:
             _check(self.lib.pkm_backward(self._ctx, ctypes.byref(params.struct), B, _ptr(x), _ptr(idx),
                                          _ptr(weights), _ptr(dout), ctypes.byref(gs), _ptr(workspace),
                                          workspace.numel(), _stream_handle(stream)))

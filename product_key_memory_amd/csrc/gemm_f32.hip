@@ -498,7 +498,17 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, int tm, int tn, int
             if constexpr (!PRODUCT_B)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) x[e] = __builtin_ldexpf(x[e], -(erow + ecol[e]));
-            if (BN_EPILOGUE) x = (x - bn_mean) * bn_mul + bn_beta;
+            if constexpr (BN_EPILOGUE) {
+                if (a.C_pre && live) {  // the values before BN as well
+                    float *pre = &a.C_pre[(int64_t)g * a.strideC + (int64_t)row * a.ldc + col];
+                    if (vec && ncol == 4) *reinterpret_cast<fx4 *>(pre) = x;
+                    else
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (e < ncol) pre[e] = x[e];
+                }
+                x = (x - bn_mean) * bn_mul + bn_beta;
+            }
             if constexpr (PRODUCT_B) {
                 static_assert(T::BN % 64 == 0, "a group of 64 columns is 16 lanes of one row");
                 if (a.group_max) {
@@ -849,6 +859,9 @@ template <typename T>
 hipError_t launch_tile(const GemmArgs &a, hipStream_t stream)
 {
     if (tile_count<T>(a) > 0x7FFFFFFF || a.batch > 65535) return hipErrorInvalidConfiguration;
+    if (a.C_pre && (!a.bn_mean || a.stream_out || a.accumulate || a.k_chunk ||
+                    (reinterpret_cast<uintptr_t>(a.C_pre) & 15) != 0 || (reinterpret_cast<uintptr_t>(a.C) & 15) != 0))
+        return hipErrorInvalidValue;
     if (a.accumulate) {
         if (a.bn_mean || a.stream_out) return hipErrorInvalidValue;
         return launch_variant<T, false, false, false, true>(a, stream);

@@ -423,7 +423,7 @@ pkm_status check_forward_args(const pkm_config &c, const pkm_params *p, const fl
 // 2 the subkey scoring, 3 the selection and the gather (one fused kernel
 // where select_gather_fusable, else two).  keep: write idx / w out.
 pkm_status forward_stage(const pkm_ctx *ctx, const pkm_params *p, int64_t nb, const float *x, float *out,
-                         int32_t *ci, float *cw, bool keep, int stage, hipStream_t st)
+                         int32_t *ci, float *cw, bool keep, int stage, hipStream_t st, float *q_pre = nullptr)
 {
     const pkm_config &c = ctx->cfg;
     const int64_t H = c.heads, k = c.k;
@@ -431,6 +431,7 @@ pkm_status forward_stage(const pkm_ctx *ctx, const pkm_params *p, int64_t nb, co
         pkm::GemmArgs a = query_args(c, p, nb, x, ctx->qhat, ctx->gemm_exp, ctx->gemm_exp_ints);
         a.row_seg_max = ctx->qmax;
         a.seg_cols = c.dim / 2;
+        a.C_pre = q_pre;  // the projection before BN as well, when asked for
         a.zero_ptr = ctx->qmax;
         a.zero_n = nb * 2 * c.heads;
         // the subkeys' row exponents for the scoring, in the same pre-pass
@@ -466,7 +467,7 @@ pkm_status forward_stage(const pkm_ctx *ctx, const pkm_params *p, int64_t nb, co
 // a1-a7 over B tokens in chunks of the context's max_batch, every chunk
 // through the context's workspace, its four stages in order; launches only.
 pkm_status forward_chunks(const pkm_ctx *ctx, const pkm_params *p, int64_t B, const float *x, float *out,
-                          int32_t *idx, float *weights, hipStream_t st)
+                          int32_t *idx, float *weights, hipStream_t st, float *q_pre = nullptr)
 {
     pkm_status s;
     const pkm_config &c = ctx->cfg;
@@ -477,7 +478,9 @@ pkm_status forward_chunks(const pkm_ctx *ctx, const pkm_params *p, int64_t B, co
         int32_t *ci = idx ? idx + b0 * H * k : ctx->idx;
         float *cw = weights ? weights + b0 * H * k : ctx->weights;
         for (int stage = 0; stage < 4; ++stage)
-            if ((s = forward_stage(ctx, p, nb, x + b0 * D, out + b0 * D, ci, cw, keep, stage, st))) return s;
+            if ((s = forward_stage(ctx, p, nb, x + b0 * D, out + b0 * D, ci, cw, keep, stage, st,
+                                   q_pre ? q_pre + b0 * H * D : nullptr)))
+                return s;
     }
     return PKM_OK;
 }
@@ -621,6 +624,17 @@ pkm_status pkm_forward(pkm_ctx *ctx, const pkm_params *p, int64_t B, const float
     if (B == 0) return ok();
     if ((s = check_forward_args(ctx->cfg, p, x, out, idx, weights))) return s;
     if ((s = forward_chunks(ctx, p, B, x, out, idx, weights, static_cast<hipStream_t>(stream)))) return s;
+    return ok();
+}
+
+pkm_status pkm_forward_train(pkm_ctx *ctx, const pkm_params *p, int64_t B, const float *x, float *out, int32_t *idx,
+                             float *weights, float *q, void *stream)
+{
+    pkm_status s;
+    if ((s = check_ctx(ctx)) || (s = check_batch(ctx->cfg, B))) return s;
+    if (B == 0) return ok();
+    if ((s = check_forward_args(ctx->cfg, p, x, out, idx, weights)) || (s = need(q, "q"))) return s;
+    if ((s = forward_chunks(ctx, p, B, x, out, idx, weights, static_cast<hipStream_t>(stream), q))) return s;
     return ok();
 }
 
@@ -829,7 +843,8 @@ namespace {
 // true, for the statistics of this batch (mean, var given; one chunk).
 pkm_status run_backward(pkm_ctx *ctx, const pkm_params *p, int64_t B, const float *x, const int32_t *idx,
                         const float *weights, const float *dout, const float *mean, const float *var, bool batch,
-                        const pkm_grads *grads, void *workspace, size_t workspace_bytes, void *stream)
+                        const pkm_grads *grads, void *workspace, size_t workspace_bytes, void *stream,
+                        const float *q_given = nullptr)
 {
     pkm_status s;
     const pkm_config &c = ctx->cfg;
@@ -881,10 +896,13 @@ pkm_status run_backward(pkm_ctx *ctx, const pkm_params *p, int64_t B, const floa
                 return s;
             continue;
         }
-        // q before BN
-        pkm::GemmArgs qa = query_args(c, p, nb, xc, Q, exps, exp_ints);
-        qa.bn_mean = qa.bn_var = qa.bn_gamma = qa.bn_beta = nullptr;
-        if ((s = launched(pkm::launch_gemm_nt_f32(qa, st), "query recompute"))) return s;
+        // q before BN: the forward's (pkm_forward_train), or computed again
+        const float *Qc = q_given ? q_given + b0 * HD : Q;
+        if (!q_given) {
+            pkm::GemmArgs qa = query_args(c, p, nb, xc, Q, exps, exp_ints);
+            qa.bn_mean = qa.bn_var = qa.bn_gamma = qa.bn_beta = nullptr;
+            if ((s = launched(pkm::launch_gemm_nt_f32(qa, st), "query recompute"))) return s;
+        }
         if ((s = launched(pkm::launch_value_backward(p->values, p->value_scale, c.value_type, D, N, nb, H, k, ic, wc,
                                                      doutc, dt, st),
                           "value backward")))
@@ -898,11 +916,11 @@ pkm_status run_backward(pkm_ctx *ctx, const pkm_params *p, int64_t B, const floa
                           "query gradient")))
             return s;
         if ((grads->dbn_gamma || batch) &&
-            (s = launched(pkm::launch_bn_grads(dqh, Q, mean, var, c.bn_eps, nb, HD, part_g, part_b, grads->dbn_gamma,
+            (s = launched(pkm::launch_bn_grads(dqh, Qc, mean, var, c.bn_eps, nb, HD, part_g, part_b, grads->dbn_gamma,
                                                grads->dbn_beta, batch ? sum_g : nullptr, batch ? sum_b : nullptr, st),
                           "BN gradients")))
             return s;
-        if (batch && (s = launched(pkm::launch_bn_batch_dq(dqh, Q, nb, HD, mean, var, p->bn_gamma, c.bn_eps, sum_g,
+        if (batch && (s = launched(pkm::launch_bn_batch_dq(dqh, Qc, nb, HD, mean, var, p->bn_gamma, c.bn_eps, sum_g,
                                                            sum_b, dq, st),
                                    "batch BN backward")))
             return s;
@@ -936,7 +954,7 @@ pkm_status run_backward(pkm_ctx *ctx, const pkm_params *p, int64_t B, const floa
             if ((s = launched(pkm::launch_gemm_nt_f32(a, st), "dWq"))) return s;
         }
         if (grads->dsubkeys &&
-            (s = launched(pkm::launch_dsub(G, nb32, nb, Q, H, D, n, mean, var, p->bn_gamma, p->bn_beta, c.bn_eps,
+            (s = launched(pkm::launch_dsub(G, nb32, nb, Qc, H, D, n, mean, var, p->bn_gamma, p->bn_beta, c.bn_eps,
                                            grads->dsubkeys, st),
                           "subkey gradient")))
             return s;
@@ -1023,6 +1041,18 @@ pkm_status pkm_backward(pkm_ctx *ctx, const pkm_params *p, int64_t B, const floa
     if (B == 0) return empty_backward(grads, stream);
     return run_backward(ctx, p, B, x, idx, weights, dout, p->bn_mean, p->bn_var, false, grads, workspace,
                         workspace_bytes, stream);
+}
+
+pkm_status pkm_backward_with_q(pkm_ctx *ctx, const pkm_params *p, int64_t B, const float *x, const float *q,
+                               const int32_t *idx, const float *weights, const float *dout, const pkm_grads *grads,
+                               void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (pkm_status s = check_backward_args(ctx, p, B, x, idx, weights, dout, grads, workspace, workspace_bytes, false))
+        return s;
+    if (B == 0) return empty_backward(grads, stream);
+    if (pkm_status s = need(q, "q")) return s;
+    return run_backward(ctx, p, B, x, idx, weights, dout, p->bn_mean, p->bn_var, false, grads, workspace,
+                        workspace_bytes, stream, q);
 }
 
 pkm_status pkm_backward_batch_stats(pkm_ctx *ctx, const pkm_params *p, int64_t B, const float *x,

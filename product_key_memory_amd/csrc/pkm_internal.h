@@ -24,6 +24,10 @@ struct GemmArgs {
     int64_t ldb, strideB;
     float *C;
     int64_t ldc, strideC;
+    // Optional, with the BN epilogue (staged, not streamed): the values
+    // before BN as well, same layout as C (the projection a training
+    // backward needs again).
+    float *C_pre;
     int M, N, K, batch;
     const float *bn_mean, *bn_var, *bn_gamma, *bn_beta;
     float bn_eps;

@@ -167,6 +167,9 @@ def test_null_arguments_rejected_before_any_launch():
     grads = pk._binding.GradsStruct()
     assert lib.pkm_backward(null, ctypes.byref(params), 1, null, null, null, null, ctypes.byref(grads), null, 0,
                             null) == pk.PKM_E_ARG
+    assert lib.pkm_forward_train(null, ctypes.byref(params), 1, null, null, null, null, null, null) == pk.PKM_E_ARG
+    assert lib.pkm_backward_with_q(null, ctypes.byref(params), 1, null, null, null, null, null, ctypes.byref(grads),
+                                   null, 0, null) == pk.PKM_E_ARG
     good = pk.make_config(**GOOD)
     assert lib.pkm_forward_noalloc(None, ctypes.byref(params), 1, null, null, null, null, null) == pk.PKM_E_ARG
     assert lib.pkm_forward_noalloc(ctypes.byref(good), ctypes.byref(params), 1, null, null, null, null,

@@ -154,6 +154,39 @@ def test_backward_chunks_accumulate_and_repeat_bitwise(torch):
             assert np.abs(t - want).max() <= 1e-6 * max(np.abs(want).max(), 1e-30), name
 
 
+@pytest.mark.parametrize("wl,max_batch,sample", [
+    (synthetic.Workload("bsq", 300, 256, 2, 40, 8, "bf16", "random"), 128, 1),    # chunked: q per chunk
+    (synthetic.Workload("bsq3", 200, 192, 3, 30, 6, "e4m3", "random"), 16384, 1),  # half-heads of 96 columns
+    (synthetic.WORKLOADS["default"], 4096, 37),                                   # the default shape
+], ids=lambda v: v.name if hasattr(v, "name") else str(v))
+def test_forward_train_and_backward_with_q(torch, wl, max_batch, sample):
+    """pkm_forward_train: out / idx / weights bitwise those of pkm_forward,
+    and q the projection before BN (Wq x against fp64, within fp32-level
+    rounding, on every `sample`-th token); pkm_backward_with_q on that q:
+    every gradient -- the dense and the sparse value gradient too --
+    bitwise that of pkm_backward, which computes q again."""
+    params, x, dout = case(wl, 7, True)
+    mem = pk.Memory(wl.D, wl.H, wl.n, wl.k, wl.table, max_batch=max_batch)
+    P = pk.params_to_device(params, wl.table, support.device())
+    xt, dt = _to(torch, x), _to(torch, dout)
+    say("forward_train / backward_with_q", wl, "max_batch =", max_batch)
+    out0, idx0, w0 = mem.forward(P, xt)
+    out1, idx1, w1, q = mem.forward_train(P, xt)
+    torch.cuda.synchronize()
+    assert torch.equal(out0, out1) and torch.equal(idx0, idx1) and torch.equal(w0, w1)
+    rows = np.arange(0, wl.B, sample)
+    ref_q = np.einsum("bd,hfd->bhf", x[rows].astype(np.float64), params["wq"].astype(np.float64))
+    got_q = q.cpu().numpy()[rows].astype(np.float64)
+    assert np.abs(got_q - ref_q).max() <= 1e-5 * np.abs(ref_q).max()
+    for sparse in (False, True) if wl.B <= max_batch else (False,):  # the sparse form takes one chunk
+        g0 = mem.backward(P, xt, idx0, w0, dt, sparse_values=sparse)
+        g1 = mem.backward(P, xt, idx1, w1, dt, sparse_values=sparse, q=q)
+        torch.cuda.synchronize()
+        for name in g0:
+            assert torch.equal(g0[name], g1[name]), (sparse, name)
+        del g0, g1
+
+
 def test_backward_subset_of_gradients(torch):
     """Skipped gradients leave no trace; the computed ones are unchanged."""
     wl = synthetic.Workload("bsub", 40, 64, 2, 16, 4, "f32", "random")
