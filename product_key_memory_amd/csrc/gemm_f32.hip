@@ -251,10 +251,12 @@ __device__ __forceinline__ void mfma_frags(floatx16 (&acc)[T::TM][T::TN], const 
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i][pa[t]], bf[j][pb[t]], acc[i][j], 0, 0, 0);
 }
 
-// One BM x BN tile (tm, tn) of batch entry g and K range z.
-template <typename T, bool BN_EPILOGUE, bool STREAM_OUT, bool PRODUCT_B, bool ACCUMULATE>
+// One BM x BN tile (tm, tn) of batch entry g and K range z.  KEEP_PRE: the
+// BN epilogue also stores the values before BN (a.C_pre).
+template <typename T, bool BN_EPILOGUE, bool STREAM_OUT, bool PRODUCT_B, bool ACCUMULATE, bool KEEP_PRE = false>
 __device__ __forceinline__ void gemm_tile(const GemmArgs &a, int tm, int tn, int g, int z, uint32_t *smem)
 {
+    static_assert(!KEEP_PRE || (BN_EPILOGUE && !STREAM_OUT), "values before BN: the staged BN epilogue");
     static_assert(!PRODUCT_B || (!STREAM_OUT && !BN_EPILOGUE && !ACCUMULATE), "product-key B: plain staged epilogue");
     uint32_t *As = smem;
     uint32_t *Bs = smem + T::STAGES * T::BM * kRowDw;
@@ -499,7 +501,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, int tm, int tn, int
 #pragma unroll
                 for (int e = 0; e < 4; ++e) x[e] = __builtin_ldexpf(x[e], -(erow + ecol[e]));
             if constexpr (BN_EPILOGUE) {
-                if (a.C_pre && live) {  // the values before BN as well
+                if (KEEP_PRE && live) {  // the values before BN as well
                     float *pre = &a.C_pre[(int64_t)g * a.strideC + (int64_t)row * a.ldc + col];
                     if (vec && ncol == 4) *reinterpret_cast<fx4 *>(pre) = x;
                     else
@@ -575,7 +577,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, int tm, int tn, int
 // entry major), a barrier between tiles; otherwise one tile per workgroup,
 // grid (tiles, batch, K ranges).
 template <typename T, bool BN_EPILOGUE, bool STREAM_OUT, bool PRODUCT_B = false, bool ACCUMULATE = false,
-          bool PERSIST = false>
+          bool PERSIST = false, bool KEEP_PRE = false>
 __global__ __launch_bounds__(T::THREADS) void gemm_nt_f32_kernel(GemmArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
@@ -601,12 +603,14 @@ __global__ __launch_bounds__(T::THREADS) void gemm_nt_f32_kernel(GemmArgs a)
             const int j = (int)(e / tiles_n), tn = (int)(e - (int64_t)j * tiles_n);
             const int r = by_rows ? xcd + kXcds * j : j;  // (batch entry, row tile) pair
             const int g = r / tiles_m;
-            gemm_tile<T, BN_EPILOGUE, STREAM_OUT, PRODUCT_B, ACCUMULATE>(a, r - g * tiles_m, tn, g, 0, smem);
+            gemm_tile<T, BN_EPILOGUE, STREAM_OUT, PRODUCT_B, ACCUMULATE, KEEP_PRE>(a, r - g * tiles_m, tn, g, 0,
+                                                                                   smem);
             __syncthreads();
         }
     } else {
-        gemm_tile<T, BN_EPILOGUE, STREAM_OUT, PRODUCT_B, ACCUMULATE>(a, blockIdx.x / tiles_n, blockIdx.x % tiles_n,
-                                                                     blockIdx.y, blockIdx.z, smem);
+        gemm_tile<T, BN_EPILOGUE, STREAM_OUT, PRODUCT_B, ACCUMULATE, KEEP_PRE>(a, blockIdx.x / tiles_n,
+                                                                               blockIdx.x % tiles_n, blockIdx.y,
+                                                                               blockIdx.z, smem);
     }
 }
 
@@ -822,10 +826,10 @@ int64_t tile_count(const GemmArgs &a)
 }
 
 template <typename T, bool BN_EPILOGUE, bool STREAM_OUT, bool PRODUCT_B = false, bool ACCUMULATE = false,
-          bool PERSIST = false>
+          bool PERSIST = false, bool KEEP_PRE = false>
 hipError_t launch_variant(const GemmArgs &a, hipStream_t stream)
 {
-    const auto kernel = &gemm_nt_f32_kernel<T, BN_EPILOGUE, STREAM_OUT, PRODUCT_B, ACCUMULATE, PERSIST>;
+    const auto kernel = &gemm_nt_f32_kernel<T, BN_EPILOGUE, STREAM_OUT, PRODUCT_B, ACCUMULATE, PERSIST, KEEP_PRE>;
     if (T::LDS_BYTES > 65536) {
         // Dynamic LDS above 64 KiB must be allowed per kernel (gfx950 has
         // 160 KiB per CU); done once per kernel and device.
@@ -870,6 +874,10 @@ hipError_t launch_tile(const GemmArgs &a, hipStream_t stream)
     // tiles in the XCD-aware order, and the stores of one tile drain while
     // the next one computes
     const bool persist = T::PING_PONG && !a.k_chunk && tile_count<T>(a) * a.batch >= kCUs;
+    if (a.C_pre) {  // the BN epilogue keeping the values before BN (checked above)
+        if (persist) return launch_variant<T, true, false, false, false, true, true>(a, stream);
+        return launch_variant<T, true, false, false, false, false, true>(a, stream);
+    }
     if (a.bn_mean) {
         if (a.stream_out) return launch_variant<T, true, true>(a, stream);
         if (persist) return launch_variant<T, true, false, false, false, true>(a, stream);
