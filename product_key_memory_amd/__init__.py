@@ -43,3 +43,12 @@ def params_to_device(p, table, device="cuda"):
     scale = dev(p["scale"]) if table in SCALED else None
     return Params(dev(p["wq"]), dev(p["mean"]), dev(p["var"]), dev(p["gamma"]), dev(p["beta"]), dev(p["subkeys"]), v,
                   scale)
+
+
+def __getattr__(name):
+    # the torch layer is imported on first use (it imports torch itself)
+    if name == "ProductKeyMemory":
+        from .layer import ProductKeyMemory
+
+        return ProductKeyMemory
+    raise AttributeError(f"module {__name__!r} has no attribute {name!r}")
