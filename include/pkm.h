@@ -127,9 +127,10 @@ pkm_status pkm_workspace_bytes(const pkm_config *cfg, size_t *bytes);
 /* Creates a context on the current HIP device: checks that the device is
  * gfx950 (PKM_E_UNSUPPORTED otherwise) and allocates the workspace
  * (PKM_E_NOMEM on failure): the normalised queries [max_batch, H, D] fp32,
- * the half scores [max_batch, H, 2, n] fp32 and idx/weight buffers
- * [max_batch, H, k] for pkm_forward calls that pass NULL for them.
- * *out receives the context, or NULL on error. */
+ * the half scores [max_batch, H, 2, n] fp32, idx/weight buffers
+ * [max_batch, H, k] for pkm_forward calls that pass NULL for them, and room
+ * for one prepared copy of Wq and the subkeys (pkm_prepare; as many bytes
+ * as the two arrays).  *out receives the context, or NULL on error. */
 pkm_status pkm_create(const pkm_config *cfg, pkm_ctx **out);
 
 /* Releases the workspace and the context.  NULL is a no-op.  The caller must
@@ -146,6 +147,24 @@ void pkm_destroy(pkm_ctx *ctx);
  * B == 0 enqueues nothing.  out must not alias any input. */
 pkm_status pkm_forward(pkm_ctx *ctx, const pkm_params *p, int64_t B, const float *x, float *out, int32_t *idx,
                        float *weights, void *stream);
+
+/* Prepares the parameters that are the same for every call: Wq (a1) and
+ * the subkeys (a3) are converted once into the form the two contractions
+ * read -- each row scaled by a power of two and split into two fp16 pieces,
+ * in the contractions' staging order (see gemm_f32.hip) -- and kept in the
+ * context.  From then on pkm_forward, pkm_forward_stage and
+ * pkm_forward_train on this context read that copy instead of p->wq and
+ * p->subkeys whenever they are given these same two pointers, which saves
+ * the per-call exponent pass over the weights and the splitting of B in
+ * every tile.  The results are bit for bit those of the unprepared calls as
+ * long as the two arrays hold what they held here: a caller that changes
+ * either array (an optimiser step) must call pkm_prepare again, or
+ * pkm_prepare(ctx, NULL, stream) to drop the copy.  Calls with other
+ * pointers are unaffected.  Uses p->wq and p->subkeys only.  Like every
+ * call, it enqueues on `stream`; forward calls on another stream must wait
+ * for it.  PKM_E_ARG for a NULL or misaligned array; on any error nothing
+ * stays prepared. */
+pkm_status pkm_prepare(pkm_ctx *ctx, const pkm_params *p, void *stream);
 
 /* The whole lookup (a1-a7) without a context and without allocating: for
  * callers that cannot allocate device memory (code under HIP graph capture,

@@ -20,7 +20,7 @@ EXPORTS = (
     "pkm_score", "pkm_select", "pkm_gather", "pkm_flat_workspace_bytes", "pkm_flat_search",
     "pkm_backward_workspace_bytes", "pkm_backward", "pkm_forward_batch_stats", "pkm_backward_batch_stats",
     "pkm_usage", "pkm_status_str", "pkm_last_error", "pkm_forward_noalloc", "pkm_select_gather",
-    "pkm_forward_stage", "pkm_forward_train", "pkm_backward_with_q",
+    "pkm_forward_stage", "pkm_forward_train", "pkm_backward_with_q", "pkm_prepare",
 )
 
 
@@ -79,6 +79,7 @@ def load_library(path=LIB_PATH):
         "pkm_backward": (ctypes.c_int, [vp, par_p, i64, vp, vp, vp, vp, ctypes.POINTER(GradsStruct), vp,
                                         ctypes.c_size_t, vp]),
         "pkm_forward_train": (ctypes.c_int, [vp, par_p, i64, vp, vp, vp, vp, vp, vp]),
+        "pkm_prepare": (ctypes.c_int, [vp, par_p, vp]),
         "pkm_backward_with_q": (ctypes.c_int, [vp, par_p, i64, vp, vp, vp, vp, vp, ctypes.POINTER(GradsStruct), vp,
                                                ctypes.c_size_t, vp]),
         "pkm_status_str": (ctypes.c_char_p, [ctypes.c_int]),
@@ -257,6 +258,17 @@ class Memory:
             _expect(t["values"], "values", (n * n, D // 2 if vt == "int4" else D), _DT[vt], dev)
             if vt in SCALED:
                 _expect(t["value_scale"], "value_scale", (n * n,), "float32", t["values"].device)
+
+    def prepare(self, params, stream=None):
+        """pkm_prepare: keep Wq and the subkeys of `params` in the form the
+        contractions read, for forward calls with these same arrays (their
+        contents must not change until prepare is called again).  None drops
+        the prepared form."""
+        if params is None:
+            _check(self.lib.pkm_prepare(self._ctx, None, _stream_handle(stream)))
+            return
+        self.check_params(params, parts=("query", "subkeys"))
+        _check(self.lib.pkm_prepare(self._ctx, ctypes.byref(params.struct), _stream_handle(stream)))
 
     def forward(self, params, x, out=None, idx=None, weights=None, stream=None, keep_selection=True):
         """The whole lookup.  Returns (out [B,D] f32, idx [B,H,k] i32,

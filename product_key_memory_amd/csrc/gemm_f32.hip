@@ -58,7 +58,7 @@
 // §Factorising the key space: every one of the n^2 concatenated keys
 // scored by one full-length dot product).  The B operand is the virtual
 // key matrix: row j = (a, c) is [C0[a]; C1[c]].  The subkey rows are split
-// into their fp16 pieces once per call (split_keys_kernel, each row with
+// into their fp16 pieces once per call (split_rows_kernel, each row with
 // its own power of two) in the order a staging lane copies them, so a tile
 // stages its 256 virtual rows by copying pieces.  The two halves of K carry
 // different key-row exponents: after the first half the accumulators of
@@ -155,28 +155,51 @@ __device__ __forceinline__ void split8(const fx4 (&v)[2], int ex, float one, u4 
 // The staging work of one thread: UNITS groups; for each, the global source
 // of its 8 k-values, the row's exponent, and its LDS destination in stage 0
 // (dwords) with the stride between stages.  Product-key B rows come already
-// split (split_keys_kernel): a B unit copies its lane's two 16-byte pieces
+// split (split_rows_kernel): a B unit copies its lane's two 16-byte pieces
 // of each chunk, from the first subkey set's row (src) and from chunk kch
-// on from the second set's (src2), both pointing at pieces.
-template <typename T, bool PRODUCT_B>
+// on from the second set's (src2), both pointing at pieces.  SPLIT_B: a
+// plain B operand split ahead of the call (weights split once, when they are
+// prepared), copied the same way from src alone.
+template <typename T, bool PRODUCT_B, bool SPLIT_B = false>
 struct Stager {
+    static constexpr bool PIECES_B = PRODUCT_B || SPLIT_B;
+    // When the A rows and the B rows each fill whole rounds of the waves'
+    // groups (both 256x256 and 128x128 tiles), unit u of every wave is an
+    // A group for u < BM / 32 / WAVES and a B group after, and every unit
+    // is in range: known at compile time, no flags in registers.
+    static constexpr bool STATIC_UNITS = (T::BM / 32) % T::WAVES == 0 && (T::BN / 32) % T::WAVES == 0;
     const float *src[T::UNITS];
     const float *src2[PRODUCT_B ? T::UNITS : 1];
-    bool is_b[PRODUCT_B ? T::UNITS : 1];
+    bool is_b[PIECES_B && !STATIC_UNITS ? T::UNITS : 1];
     int kch;
     int lds[T::UNITS], stage_stride[T::UNITS], ex[T::UNITS];
-    bool valid[T::UNITS];
+    bool valid[STATIC_UNITS ? 1 : T::UNITS];
     fx4 v[T::UNITS][2];
+
+    __device__ __forceinline__ bool b_unit(int u) const
+    {
+        if constexpr (STATIC_UNITS) return u >= T::BM / 32 / T::WAVES;
+        else return is_b[u];
+    }
+    __device__ __forceinline__ bool in_range(int u) const
+    {
+        if constexpr (STATIC_UNITS) return true;
+        else return valid[u];
+    }
 
     __device__ __forceinline__ void load(int kt)
     {
 #pragma unroll
         for (int u = 0; u < T::UNITS; ++u) {
-            if (!valid[u]) continue;
-            if constexpr (PRODUCT_B) {
-                if (is_b[u]) {
-                    const u4 *q = kt < kch ? reinterpret_cast<const u4 *>(src[u]) + (int64_t)kt * 128
-                                           : reinterpret_cast<const u4 *>(src2[u]) + (int64_t)(kt - kch) * 128;
+            if (!in_range(u)) continue;
+            if constexpr (PIECES_B) {
+                if (b_unit(u)) {
+                    const u4 *q;
+                    if constexpr (PRODUCT_B)
+                        q = kt < kch ? reinterpret_cast<const u4 *>(src[u]) + (int64_t)kt * 128
+                                     : reinterpret_cast<const u4 *>(src2[u]) + (int64_t)(kt - kch) * 128;
+                    else
+                        q = reinterpret_cast<const u4 *>(src[u]) + (int64_t)kt * 128;
                     v[u][0] = __builtin_bit_cast(fx4, q[0]);
                     v[u][1] = __builtin_bit_cast(fx4, q[64]);
                     continue;
@@ -197,9 +220,9 @@ struct Stager {
         asm volatile("" : "+v"(one));
 #pragma unroll
         for (int u = 0; u < T::UNITS; ++u) {
-            if (!valid[u]) continue;
-            if constexpr (PRODUCT_B) {
-                if (is_b[u]) {  // pieces as loaded
+            if (!in_range(u)) continue;
+            if constexpr (PIECES_B) {
+                if (b_unit(u)) {  // pieces as loaded
                     uint32_t *dst = smem + lds[u] + s * stage_stride[u];
 #pragma unroll
                     for (int p = 0; p < kPieces; ++p)
@@ -253,11 +276,15 @@ __device__ __forceinline__ void mfma_frags(floatx16 (&acc)[T::TM][T::TN], const 
 
 // One BM x BN tile (tm, tn) of batch entry g and K range z.  KEEP_PRE: the
 // BN epilogue also stores the values before BN (a.C_pre).
-template <typename T, bool BN_EPILOGUE, bool STREAM_OUT, bool PRODUCT_B, bool ACCUMULATE, bool KEEP_PRE = false>
+// SPLIT_B: B's rows come split into fp16 pieces (a.b_presplit, scaled by
+// a.b_exp_given), and the tile copies them.
+template <typename T, bool BN_EPILOGUE, bool STREAM_OUT, bool PRODUCT_B, bool ACCUMULATE, bool KEEP_PRE = false,
+          bool SPLIT_B = false>
 __device__ __forceinline__ void gemm_tile(const GemmArgs &a, int tm, int tn, int g, int z, uint32_t *smem)
 {
     static_assert(!KEEP_PRE || (BN_EPILOGUE && !STREAM_OUT), "values before BN: the staged BN epilogue");
     static_assert(!PRODUCT_B || (!STREAM_OUT && !BN_EPILOGUE && !ACCUMULATE), "product-key B: plain staged epilogue");
+    static_assert(!(PRODUCT_B && SPLIT_B), "one form of pre-split B");
     uint32_t *As = smem;
     uint32_t *Bs = smem + T::STAGES * T::BM * kRowDw;
     // split-K: this block's range of K (the operands are K-contiguous)
@@ -284,8 +311,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, int tm, int tn, int
 
     // Rows past the matrix edge re-read the last row; their results are
     // never stored.
-    Stager<T, PRODUCT_B> st;
+    Stager<T, PRODUCT_B, SPLIT_B> st;
     st.kch = a.split_k / kBK;
+    // pre-split plain B: this batch entry's rows, from this K range's first
+    // chunk (pieces of rows past N are zero)
+    const int kt_all = a.K / kBK;
+    const u4 *bsplit = SPLIT_B ? reinterpret_cast<const u4 *>(a.b_presplit) +
+                                     ((int64_t)g * ((a.N + 31) / 32) * kt_all + kbeg / kBK) * 128
+                               : nullptr;
     // product-key B: the split rows of this batch entry's two subkey sets
     const int kgroups = (a.key_n + 31) / 32;
     const u4 *set0 =
@@ -294,10 +327,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, int tm, int tn, int
 #pragma unroll
     for (int u = 0; u < T::UNITS; ++u) {
         const int grp = wave + T::WAVES * u;
-        st.valid[u] = grp < T::GROUPS;
+        if constexpr (!decltype(st)::STATIC_UNITS) st.valid[u] = grp < T::GROUPS;
         const int r = min(grp, T::GROUPS - 1) * 32 + il;  // row of the A tile, then of the B tile
-        if constexpr (PRODUCT_B) st.is_b[u] = r >= T::BM;
-        if (r < T::BM) {
+        if constexpr ((PRODUCT_B || SPLIT_B) && !decltype(st)::STATIC_UNITS) st.is_b[u] = r >= T::BM;
+        if (decltype(st)::STATIC_UNITS ? !st.b_unit(u) : r < T::BM) {
             const int m = min(m0 + r, a.M - 1);
             st.src[u] = A + (int64_t)m * a.lda + kk * 8;
             if constexpr (PRODUCT_B) st.src2[u] = nullptr;
@@ -311,6 +344,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, int tm, int tn, int
                 const int ka = j / a.key_n, kc = j - ka * a.key_n;
                 st.src[u] = reinterpret_cast<const float *>(set0 + (int64_t)(ka / 32) * st.kch * 128 + kk * 32 + ka % 32);
                 st.src2[u] = reinterpret_cast<const float *>(set1 + (int64_t)(kc / 32) * st.kch * 128 + kk * 32 + kc % 32);
+                st.ex[u] = 0;
+            } else if constexpr (SPLIT_B) {
+                // lane (kk, j % 32) of row j's group
+                st.src[u] = reinterpret_cast<const float *>(bsplit + (int64_t)(j / 32) * kt_all * 128 + kk * 32 + j % 32);
                 st.ex[u] = 0;
             } else {
                 st.src[u] = Bmat + (int64_t)j * a.ldb + kk * 8;
@@ -577,7 +614,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, int tm, int tn, int
 // entry major), a barrier between tiles; otherwise one tile per workgroup,
 // grid (tiles, batch, K ranges).
 template <typename T, bool BN_EPILOGUE, bool STREAM_OUT, bool PRODUCT_B = false, bool ACCUMULATE = false,
-          bool PERSIST = false, bool KEEP_PRE = false>
+          bool PERSIST = false, bool KEEP_PRE = false, bool SPLIT_B = false>
 __global__ __launch_bounds__(T::THREADS) void gemm_nt_f32_kernel(GemmArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
@@ -603,14 +640,13 @@ __global__ __launch_bounds__(T::THREADS) void gemm_nt_f32_kernel(GemmArgs a)
             const int j = (int)(e / tiles_n), tn = (int)(e - (int64_t)j * tiles_n);
             const int r = by_rows ? xcd + kXcds * j : j;  // (batch entry, row tile) pair
             const int g = r / tiles_m;
-            gemm_tile<T, BN_EPILOGUE, STREAM_OUT, PRODUCT_B, ACCUMULATE, KEEP_PRE>(a, r - g * tiles_m, tn, g, 0,
-                                                                                   smem);
+            gemm_tile<T, BN_EPILOGUE, STREAM_OUT, PRODUCT_B, ACCUMULATE, KEEP_PRE, SPLIT_B>(a, r - g * tiles_m, tn, g,
+                                                                                            0, smem);
             __syncthreads();
         }
     } else {
-        gemm_tile<T, BN_EPILOGUE, STREAM_OUT, PRODUCT_B, ACCUMULATE, KEEP_PRE>(a, blockIdx.x / tiles_n,
-                                                                               blockIdx.x % tiles_n, blockIdx.y,
-                                                                               blockIdx.z, smem);
+        gemm_tile<T, BN_EPILOGUE, STREAM_OUT, PRODUCT_B, ACCUMULATE, KEEP_PRE, SPLIT_B>(
+            a, blockIdx.x / tiles_n, blockIdx.x % tiles_n, blockIdx.y, blockIdx.z, smem);
     }
 }
 
@@ -782,20 +818,23 @@ hipError_t prepare_exponents(GemmArgs &a, bool product_b, hipStream_t stream)
     return launch_exponents(jobs, n, a.zero_ptr, a.zero_n, stream);
 }
 
-// The key rows of a product-key B operand split once per call, for the
-// flat search: every subkey row of both sets (batch entry g, set p = 0 at
-// B, 1 at B2) scaled by its own power of two (b_exp / b2_exp) and split as
-// split8 does, stored in the order a staging lane copies them: per set,
-// [group of 32 rows][chunk of 16 k][piece][lane][8 fp16] with lane l = 32 kh
-// + row % 32 holding k = 16 chunk + 8 kh .. + 7.  Rows past key_n are zero.
-// One thread per (set, group, chunk, lane).
-__global__ __launch_bounds__(256) void split_keys_kernel(const float *B, const float *B2, int64_t strideB, int64_t ldb,
-                                                         int key_n, int kch, const int32_t *b_exp,
+// Rows of a B operand split into fp16 pieces once: every row scaled by its
+// own power of two and split as split8 does, stored in the order a staging
+// lane copies them: per set of rows, [group of 32 rows][chunk of 16 k]
+// [piece][lane][8 fp16] with lane l = 32 kh + row % 32 holding k = 16 chunk
+// + 8 kh .. + 7.  Rows past `rows` are zero.  Product-key operand (B2
+// non-null, the flat search, split per call): set s = 2 g + p is batch entry
+// g's first (p = 0, at B, exponents b_exp) or second (at B2, b2_exp) subkey
+// set.  Plain operand (B2 null, prepared weights): set s is batch entry s
+// (b_exp).  One thread per (set, group, chunk, lane).
+__global__ __launch_bounds__(256) void split_rows_kernel(const float *B, const float *B2, int64_t strideB, int64_t ldb,
+                                                         int rows, int kch, const int32_t *b_exp,
                                                          const int32_t *b2_exp, u4 *out)
 {
     const int set = blockIdx.y;
-    const int g = set >> 1, half = set & 1;
-    const int64_t per_set = (int64_t)((key_n + 31) / 32) * kch * 64;
+    const bool pairs = B2 != nullptr;
+    const int g = pairs ? set >> 1 : set, half = pairs ? set & 1 : 0;
+    const int64_t per_set = (int64_t)((rows + 31) / 32) * kch * 64;
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (t >= per_set) return;
     const int lane = (int)(t & 63);
@@ -804,11 +843,11 @@ __global__ __launch_bounds__(256) void split_keys_kernel(const float *B, const f
     const int row = grp * 32 + (lane & 31);
     fx4 v[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
     int ex = 0;
-    if (row < key_n) {
+    if (row < rows) {
         const float *src = (half ? B2 : B) + (int64_t)g * strideB + (int64_t)row * ldb + c * kBK + (lane >> 5) * 8;
         v[0] = *reinterpret_cast<const fx4 *>(src);
         v[1] = *reinterpret_cast<const fx4 *>(src + 4);
-        ex = (half ? b2_exp : b_exp)[(int64_t)g * key_n + row];
+        ex = (half ? b2_exp : b_exp)[(int64_t)g * rows + row];
     }
     float one = 1.0f;
     asm volatile("" : "+v"(one));
@@ -826,10 +865,11 @@ int64_t tile_count(const GemmArgs &a)
 }
 
 template <typename T, bool BN_EPILOGUE, bool STREAM_OUT, bool PRODUCT_B = false, bool ACCUMULATE = false,
-          bool PERSIST = false, bool KEEP_PRE = false>
+          bool PERSIST = false, bool KEEP_PRE = false, bool SPLIT_B = false>
 hipError_t launch_variant(const GemmArgs &a, hipStream_t stream)
 {
-    const auto kernel = &gemm_nt_f32_kernel<T, BN_EPILOGUE, STREAM_OUT, PRODUCT_B, ACCUMULATE, PERSIST, KEEP_PRE>;
+    const auto kernel =
+        &gemm_nt_f32_kernel<T, BN_EPILOGUE, STREAM_OUT, PRODUCT_B, ACCUMULATE, PERSIST, KEEP_PRE, SPLIT_B>;
     if (T::LDS_BYTES > 65536) {
         // Dynamic LDS above 64 KiB must be allowed per kernel (gfx950 has
         // 160 KiB per CU); done once per kernel and device.
@@ -859,35 +899,43 @@ hipError_t launch_variant(const GemmArgs &a, hipStream_t stream)
     return hipGetLastError();
 }
 
-template <typename T>
-hipError_t launch_tile(const GemmArgs &a, hipStream_t stream)
+template <typename T, bool SPLIT_B>
+hipError_t launch_tile_form(const GemmArgs &a, hipStream_t stream)
 {
     if (tile_count<T>(a) > 0x7FFFFFFF || a.batch > 65535) return hipErrorInvalidConfiguration;
     if (a.C_pre && (!a.bn_mean || a.stream_out || a.accumulate || a.k_chunk ||
                     (reinterpret_cast<uintptr_t>(a.C_pre) & 15) != 0 || (reinterpret_cast<uintptr_t>(a.C) & 15) != 0))
         return hipErrorInvalidValue;
     if (a.accumulate) {
-        if (a.bn_mean || a.stream_out) return hipErrorInvalidValue;
-        return launch_variant<T, false, false, false, true>(a, stream);
+        if (a.bn_mean || a.stream_out || SPLIT_B) return hipErrorInvalidValue;
+        if constexpr (!SPLIT_B) return launch_variant<T, false, false, false, true>(a, stream);
     }
     // At least as many 256x256 tiles as CUs: one workgroup per CU walks its
     // tiles in the XCD-aware order, and the stores of one tile drain while
     // the next one computes
     const bool persist = T::PING_PONG && !a.k_chunk && tile_count<T>(a) * a.batch >= kCUs;
     if (a.C_pre) {  // the BN epilogue keeping the values before BN (checked above)
-        if (persist) return launch_variant<T, true, false, false, false, true, true>(a, stream);
-        return launch_variant<T, true, false, false, false, false, true>(a, stream);
+        if (persist) return launch_variant<T, true, false, false, false, true, true, SPLIT_B>(a, stream);
+        return launch_variant<T, true, false, false, false, false, true, SPLIT_B>(a, stream);
     }
     if (a.bn_mean) {
-        if (a.stream_out) return launch_variant<T, true, true>(a, stream);
-        if (persist) return launch_variant<T, true, false, false, false, true>(a, stream);
-        return launch_variant<T, true, false>(a, stream);
+        if (a.stream_out) return launch_variant<T, true, true, false, false, false, false, SPLIT_B>(a, stream);
+        if (persist) return launch_variant<T, true, false, false, false, true, false, SPLIT_B>(a, stream);
+        return launch_variant<T, true, false, false, false, false, false, SPLIT_B>(a, stream);
     }
     if (a.stream_out) {
-        if (persist) return launch_variant<T, false, true, false, false, true>(a, stream);
-        return launch_variant<T, false, true>(a, stream);
+        if (persist) return launch_variant<T, false, true, false, false, true, false, SPLIT_B>(a, stream);
+        return launch_variant<T, false, true, false, false, false, false, SPLIT_B>(a, stream);
     }
-    return launch_variant<T, false, false>(a, stream);
+    return launch_variant<T, false, false, false, false, false, false, SPLIT_B>(a, stream);
+}
+
+// B split ahead of the call (b_presplit) or in every tile
+template <typename T>
+hipError_t launch_tile(const GemmArgs &a, hipStream_t stream)
+{
+    if (a.b_presplit) return launch_tile_form<T, true>(a, stream);
+    return launch_tile_form<T, false>(a, stream);
 }
 
 // C[g][m][n] (+)= sum over s of P[s][g][m][n], s in order: the split-K
@@ -921,10 +969,32 @@ int64_t gemm_exp_ints(const GemmArgs &a)
     return (int64_t)a.batch * ((int64_t)a.M + b_rows);
 }
 
+int64_t gemm_presplit_bytes(int rows, int K, int batch)
+{
+    return (int64_t)batch * ((rows + 31) / 32) * 32 * (int64_t)K * 4;
+}
+
+hipError_t launch_presplit(const float *B, int64_t stride, int64_t ld, int rows, int K, int batch, int32_t *exp,
+                           void *out, hipStream_t stream)
+{
+    if (rows <= 0 || batch <= 0) return hipSuccess;
+    if (K % 32 != 0 || batch > 65535 || (reinterpret_cast<uintptr_t>(out) & 15) != 0) return hipErrorInvalidValue;
+    const ExpJob job = exp_job(B, rows, batch, stride, ld, K, exp);
+    hipError_t e = launch_exponents(&job, 1, nullptr, 0, stream);
+    if (e != hipSuccess) return e;
+    const int kch = K / kBK;
+    const int64_t per_set = (int64_t)((rows + 31) / 32) * kch * 64;
+    hipLaunchKernelGGL(split_rows_kernel, dim3((unsigned)((per_set + 255) / 256), batch), dim3(256), 0, stream, B,
+                       nullptr, stride, ld, rows, kch, exp, nullptr, reinterpret_cast<u4 *>(out));
+    return hipGetLastError();
+}
+
 hipError_t launch_gemm_nt_f32(const GemmArgs &args, hipStream_t stream)
 {
     if (args.M <= 0 || args.N <= 0 || args.batch <= 0) return hipSuccess;
     if (args.K % 32 != 0 || args.k_chunk != 0 || args.B2) return hipErrorInvalidValue;
+    if (args.b_presplit && (!args.b_exp_given || args.accumulate || (reinterpret_cast<uintptr_t>(args.b_presplit) & 15)))
+        return hipErrorInvalidValue;
     GemmArgs a = args;
     hipError_t e = prepare_exponents(a, false, stream);
     if (e != hipSuccess || a.exp_phase == 1) return e;
@@ -969,7 +1039,7 @@ hipError_t launch_gemm_nt_f32_product(const GemmArgs &args, hipStream_t stream)
     if (e != hipSuccess || a.exp_phase == 1) return e;
     const int kch = a.split_k / kBK;
     const int64_t per_set = (int64_t)((a.key_n + 31) / 32) * kch * 64;
-    hipLaunchKernelGGL(split_keys_kernel, dim3((unsigned)((per_set + 255) / 256), 2 * a.batch), dim3(256), 0, stream,
+    hipLaunchKernelGGL(split_rows_kernel, dim3((unsigned)((per_set + 255) / 256), 2 * a.batch), dim3(256), 0, stream,
                        a.B, a.B2, a.strideB, a.ldb, a.key_n, kch, a.b_exp, a.b2_exp,
                        reinterpret_cast<u4 *>(a.b_split));
     if ((e = hipGetLastError()) != hipSuccess) return e;

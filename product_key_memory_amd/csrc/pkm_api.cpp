@@ -26,6 +26,14 @@ struct pkm_ctx {
     int64_t gemm_exp_ints;
     uint32_t *qmax;    // largest |q^| per (token, half of a head) [max_batch, 2H], float bits
     int32_t *sub_exp;  // row exponents of the subkeys [2H, n]
+    // Prepared weights (pkm_prepare): the row exponents and fp16 pieces of
+    // Wq and of the subkeys, and the arrays they were made from (NULL:
+    // nothing prepared).
+    int32_t *prep_wq_exp;   // [H * D]
+    int32_t *prep_sub_exp;  // [2H * n]
+    void *prep_wq;
+    void *prep_sub;
+    const float *prep_wq_src, *prep_sub_src;
 };
 
 namespace {
@@ -75,10 +83,11 @@ int64_t forward_exp_ints(const pkm_config &c)
 
 // Workspace pieces for one chunk of c.max_batch tokens: q^, scores, idx,
 // weights, the batch statistics' partial sums (only with batch_stats), the
-// GEMM row exponents, q^'s per-half maxima and the subkeys' row exponents.
-// False on size overflow.
-constexpr int kPieces = 8;
-bool workspace_layout(const pkm_config &c, size_t sizes[kPieces], bool batch_stats = true)
+// GEMM row exponents, q^'s per-half maxima and the subkeys' row exponents;
+// then (only with prepared) the prepared weights: Wq's and the subkeys' row
+// exponents and fp16 pieces.  False on size overflow.
+constexpr int kPieces = 12;
+bool workspace_layout(const pkm_config &c, size_t sizes[kPieces], bool batch_stats = true, bool prepared = true)
 {
     const double mb = (double)c.max_batch;
     const double total = mb * c.heads * ((double)c.dim + 2.0 * c.n_keys + 2.0 * c.k) * 4.0;
@@ -92,6 +101,10 @@ bool workspace_layout(const pkm_config &c, size_t sizes[kPieces], bool batch_sta
     sizes[5] = round_up((size_t)forward_exp_ints(c) * sizeof(int32_t));
     sizes[6] = round_up(m * 2 * H * sizeof(uint32_t));
     sizes[7] = round_up(2 * H * (size_t)c.n_keys * sizeof(int32_t));
+    sizes[8] = prepared ? round_up(H * (size_t)c.dim * sizeof(int32_t)) : 0;
+    sizes[9] = prepared ? sizes[7] : 0;
+    sizes[10] = prepared ? round_up((size_t)pkm::gemm_presplit_bytes(c.heads * c.dim, c.dim, 1)) : 0;
+    sizes[11] = prepared ? round_up((size_t)pkm::gemm_presplit_bytes(c.n_keys, c.dim / 2, 2 * c.heads)) : 0;
     return true;
 }
 
@@ -112,6 +125,11 @@ void assign_workspace(pkm_ctx *ctx, char *w, const size_t sizes[kPieces])
     ctx->gemm_exp_ints = (int64_t)(sizes[5] / sizeof(int32_t));
     ctx->qmax = reinterpret_cast<uint32_t *>(piece[6]);
     ctx->sub_exp = reinterpret_cast<int32_t *>(piece[7]);
+    ctx->prep_wq_exp = reinterpret_cast<int32_t *>(piece[8]);
+    ctx->prep_sub_exp = reinterpret_cast<int32_t *>(piece[9]);
+    ctx->prep_wq = piece[10];
+    ctx->prep_sub = piece[11];
+    ctx->prep_wq_src = ctx->prep_sub_src = nullptr;
 }
 
 pkm_status check_config(const pkm_config *c)
@@ -427,6 +445,10 @@ pkm_status forward_stage(const pkm_ctx *ctx, const pkm_params *p, int64_t nb, co
 {
     const pkm_config &c = ctx->cfg;
     const int64_t H = c.heads, k = c.k;
+    // Wq and the subkeys from their prepared form when p names the arrays
+    // pkm_prepare took them from (the same pieces and exponents the tiles
+    // would compute, so the same results)
+    const bool prep = ctx->prep_wq_src && ctx->prep_wq_src == p->wq && ctx->prep_sub_src == p->subkeys;
     if (stage <= 1) {
         pkm::GemmArgs a = query_args(c, p, nb, x, ctx->qhat, ctx->gemm_exp, ctx->gemm_exp_ints);
         a.row_seg_max = ctx->qmax;
@@ -434,14 +456,19 @@ pkm_status forward_stage(const pkm_ctx *ctx, const pkm_params *p, int64_t nb, co
         a.C_pre = q_pre;  // the projection before BN as well, when asked for
         a.zero_ptr = ctx->qmax;
         a.zero_n = nb * 2 * c.heads;
-        // the subkeys' row exponents for the scoring, in the same pre-pass
-        a.extra_exp.base = p->subkeys;
-        a.extra_exp.rows_per_batch = c.n_keys;
-        a.extra_exp.batch = 2 * c.heads;
-        a.extra_exp.stride = (int64_t)c.n_keys * (c.dim / 2);
-        a.extra_exp.ld = c.dim / 2;
-        a.extra_exp.K = c.dim / 2;
-        a.extra_exp.out = ctx->sub_exp;
+        if (prep) {  // the pre-pass does x alone
+            a.b_exp_given = ctx->prep_wq_exp;
+            a.b_presplit = ctx->prep_wq;
+        } else {
+            // the subkeys' row exponents for the scoring, in the same pre-pass
+            a.extra_exp.base = p->subkeys;
+            a.extra_exp.rows_per_batch = c.n_keys;
+            a.extra_exp.batch = 2 * c.heads;
+            a.extra_exp.stride = (int64_t)c.n_keys * (c.dim / 2);
+            a.extra_exp.ld = c.dim / 2;
+            a.extra_exp.K = c.dim / 2;
+            a.extra_exp.out = ctx->sub_exp;
+        }
         a.exp_phase = stage == 0 ? 1 : 2;
         return launched(pkm::launch_gemm_nt_f32(a, st), stage == 0 ? "row exponents" : "query projection");
     }
@@ -449,7 +476,8 @@ pkm_status forward_stage(const pkm_ctx *ctx, const pkm_params *p, int64_t nb, co
         pkm::GemmArgs a = score_args(c, p, nb, ctx->qhat, ctx->scores, ctx->gemm_exp, ctx->gemm_exp_ints);
         a.a_rowmax = ctx->qmax;
         a.a_rowmax_ld = 2 * c.heads;
-        a.b_exp_given = ctx->sub_exp;
+        a.b_exp_given = prep ? ctx->prep_sub_exp : ctx->sub_exp;
+        if (prep) a.b_presplit = ctx->prep_sub;
         return launched(pkm::launch_gemm_nt_f32(a, st), "subkey scoring");
     }
     if (pkm::select_gather_fusable(c.heads, c.n_keys, c.k, c.value_type, c.dim))
@@ -530,7 +558,7 @@ size_t noalloc_bytes(pkm_config c, int64_t mb)
 {
     c.max_batch = mb;
     size_t sizes[kPieces];
-    if (!workspace_layout(c, sizes, false)) return SIZE_MAX;
+    if (!workspace_layout(c, sizes, false, false)) return SIZE_MAX;
     return total_bytes(sizes, kPieces);
 }
 
@@ -627,6 +655,27 @@ pkm_status pkm_forward(pkm_ctx *ctx, const pkm_params *p, int64_t B, const float
     return ok();
 }
 
+pkm_status pkm_prepare(pkm_ctx *ctx, const pkm_params *p, void *stream)
+{
+    pkm_status s;
+    if ((s = check_ctx(ctx))) return s;
+    ctx->prep_wq_src = ctx->prep_sub_src = nullptr;
+    if (!p) return ok();  // only dropped
+    if ((s = need(p->wq, "wq")) || (s = need(p->subkeys, "subkeys"))) return s;
+    const pkm_config &c = ctx->cfg;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if ((s = launched(pkm::launch_presplit(p->wq, 0, c.dim, c.heads * c.dim, c.dim, 1, ctx->prep_wq_exp, ctx->prep_wq,
+                                           st),
+                      "Wq split")) ||
+        (s = launched(pkm::launch_presplit(p->subkeys, (int64_t)c.n_keys * (c.dim / 2), c.dim / 2, c.n_keys,
+                                           c.dim / 2, 2 * c.heads, ctx->prep_sub_exp, ctx->prep_sub, st),
+                      "subkey split")))
+        return s;
+    ctx->prep_wq_src = p->wq;
+    ctx->prep_sub_src = p->subkeys;
+    return ok();
+}
+
 pkm_status pkm_forward_train(pkm_ctx *ctx, const pkm_params *p, int64_t B, const float *x, float *out, int32_t *idx,
                              float *weights, float *q, void *stream)
 {
@@ -651,7 +700,7 @@ pkm_status pkm_forward_noalloc(const pkm_config *cfg, const pkm_params *p, int64
     char *base = nullptr;
     if ((s = scratch_on_current_device(&ctx.device, &base))) return s;
     size_t sizes[kPieces];
-    workspace_layout(ctx.cfg, sizes, false);
+    workspace_layout(ctx.cfg, sizes, false, false);  // as noalloc_bytes sized it
     assign_workspace(&ctx, base, sizes);
     if ((s = forward_chunks(&ctx, p, B, x, out, idx, weights, static_cast<hipStream_t>(stream)))) return s;
     return ok();

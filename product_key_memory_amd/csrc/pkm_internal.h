@@ -71,6 +71,11 @@ struct GemmArgs {
     // Optional: B's row exponents computed beforehand ([batch][N]).  With
     // both this and a_rowmax the contraction needs no pre-pass.
     const int32_t *b_exp_given;
+    // Optional, with b_exp_given (not with accumulate): B's rows already
+    // scaled by those exponents and split into fp16 pieces by
+    // launch_presplit (16-byte aligned), so the tiles copy them instead of
+    // splitting B.  Bitwise the same results as splitting in the tiles.
+    const void *b_presplit;
     // Optional: one more set of row exponents for a later contraction,
     // computed in this one's pre-pass (rows_per_batch * batch rows of K
     // floats, row m of entry g at base + g * stride + m * ld).
@@ -108,6 +113,14 @@ int64_t gemm_exp_ints(const GemmArgs &a);
 // rows * split_k * (two fp16 pieces)
 int64_t gemm_split_bytes(const GemmArgs &a);
 hipError_t launch_gemm_nt_f32(const GemmArgs &a, hipStream_t stream);
+// A B operand of launch_gemm_nt_f32 prepared once for many contractions
+// (weights): rows [batch][rows][K] fp32 (row m of entry g at B + g * stride
+// + m * ld, K % 32 == 0) -> their row exponents exp [batch * rows] int32 and
+// their fp16 pieces at out (gemm_presplit_bytes(rows, K, batch) bytes,
+// 16-byte aligned), for GemmArgs::b_exp_given and b_presplit.
+int64_t gemm_presplit_bytes(int rows, int K, int batch);
+hipError_t launch_presplit(const float *B, int64_t stride, int64_t ld, int rows, int K, int batch, int32_t *exp,
+                           void *out, hipStream_t stream);
 // The same contraction with a product-key B operand (b_split required) and
 // 32 x 256 tiles, suited to a few dozen rows of A (the flat exact search
 // over all keys).

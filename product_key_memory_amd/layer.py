@@ -21,6 +21,14 @@ this module only allocates the gradient buffers and hands them to autograd.
   gradient), for optimisers that take sparse gradients.  E4M3, int8 and
   int4 tables (with their row scales) are buffers: looked up, not trained.
 
+- prepare_weights=True: the library keeps wq and the subkeys in the form
+  its contractions read (pkm_prepare), so each eval-mode forward skips
+  converting them; the copy is made again whenever either parameter has
+  changed in place since (torch's version counters: optimiser steps,
+  load_state_dict, copy_ under no_grad).  Changes that bypass the counters
+  (writing through .data) need refresh_prepared().  Same results bit for
+  bit.
+
 There is no CPU path: the module lives on a GPU, and every call raises if
 libpkm.so cannot be loaded.  Calls of one module must not overlap on
 different streams (they share the backward's workspace).
@@ -47,6 +55,7 @@ class _Lookup(torch.autograd.Function):
                 P, x, running=(layer.running_mean, layer.running_var), momentum=layer.momentum)
             ctx.save_for_backward(x, idx, w, mean, var)
         else:
+            layer._sync_prepared(P)
             out, idx, w, q = mem.forward_train(P, x)
             ctx.save_for_backward(x, idx, w, q)
         ctx.layer, ctx.batch_stats = layer, layer.training
@@ -124,7 +133,7 @@ class ProductKeyMemory(torch.nn.Module):
     """
 
     def __init__(self, dim, heads=4, n_keys=1024, k=32, value_type="bf16", bn_eps=1e-5, momentum=0.1,
-                 max_batch=16384, sparse_values=False, device="cuda"):
+                 max_batch=16384, sparse_values=False, prepare_weights=False, device="cuda"):
         super().__init__()
         device = torch.device(device)
         if device.type != "cuda":
@@ -134,6 +143,7 @@ class ProductKeyMemory(torch.nn.Module):
         self.dim, self.heads, self.n_keys, self.k = int(dim), int(heads), int(n_keys), int(k)
         self.value_type, self.bn_eps, self.momentum = value_type, float(bn_eps), float(momentum)
         self.max_batch, self.sparse_values = int(max_batch), bool(sparse_values)
+        self.prepare_weights, self._prep_key = bool(prepare_weights), None
         D, H, n = self.dim, self.heads, self.n_keys
         f32 = dict(dtype=torch.float32, device=device)
         self.wq = torch.nn.Parameter(torch.empty(H, D, D, **f32))
@@ -186,8 +196,24 @@ class ProductKeyMemory(torch.nn.Module):
             with torch.cuda.device(dev):
                 self._mem = Memory(self.dim, self.heads, self.n_keys, self.k, self.value_type, self.bn_eps,
                                    self.max_batch)
-            self._mem_device, self._ws = dev, None
+            self._mem_device, self._ws, self._prep_key = dev, None, None
         return self._mem
+
+    def _sync_prepared(self, P):
+        """With prepare_weights: prepares wq and the subkeys again when
+        either changed since the last time (pointer or version counter)."""
+        if not self.prepare_weights:
+            return
+        key = (self.wq.data_ptr(), self.wq._version, self.subkeys.data_ptr(), self.subkeys._version)
+        if key != self._prep_key:
+            self._memory().prepare(P)
+            self._prep_key = key
+
+    def refresh_prepared(self):
+        """Prepares wq and the subkeys again now (after changes that torch's
+        version counters do not see, such as writes through .data)."""
+        self._prep_key = None
+        self._sync_prepared(self._params())
 
     def _workspace(self):
         if self._ws is None:
@@ -213,7 +239,9 @@ class ProductKeyMemory(torch.nn.Module):
             values = self.values if isinstance(self.values, torch.nn.Parameter) else self.values.detach()
             out, idx, w = _Lookup.apply(self, x2, self.wq, self.bn_gamma, self.bn_beta, self.subkeys, values)
         else:
-            out, idx, w = self._memory().forward(self._params(), x2)
+            P = self._params()
+            self._sync_prepared(P)
+            out, idx, w = self._memory().forward(P, x2)
         out = out.reshape(*lead, self.dim)
         if return_selection:
             return out, idx.reshape(*lead, self.heads, self.k), w.reshape(*lead, self.heads, self.k)
@@ -221,4 +249,5 @@ class ProductKeyMemory(torch.nn.Module):
 
     def extra_repr(self):
         return (f"dim={self.dim}, heads={self.heads}, n_keys={self.n_keys}, k={self.k}, "
-                f"value_type={self.value_type}, max_batch={self.max_batch}, sparse_values={self.sparse_values}")
+                f"value_type={self.value_type}, max_batch={self.max_batch}, sparse_values={self.sparse_values}, "
+                f"prepare_weights={self.prepare_weights}")

@@ -86,8 +86,11 @@ def test_workspace_bytes():
     exps = max(mb + H * D, 2 * H * (mb + n)) * 4  # GEMM row exponents (query or scoring)
     qmax = mb * 2 * H * 4  # largest |q^| per (token, half of a head)
     sub_exp = 2 * H * n * 4  # the subkeys' row exponents
+    # prepared weights: Wq's and the subkeys' row exponents, and both split
+    # into two fp16 pieces (as many bytes as the fp32 arrays)
+    prepared = H * D * 4 + sub_exp + H * D * D * 4 + H * 2 * n * (D // 2) * 4
     assert (pk.workspace_bytes(cfg) ==
-            4 * mb * H * (D + 2 * n + 2 * k) + stat_part + exps + qmax + sub_exp)
+            4 * mb * H * (D + 2 * n + 2 * k) + stat_part + exps + qmax + sub_exp + prepared)
     with pytest.raises(pk.PkmError):
         pk.workspace_bytes(pk.make_config(**{**GOOD, "k": 0}))
 
@@ -168,6 +171,7 @@ def test_null_arguments_rejected_before_any_launch():
     assert lib.pkm_backward(null, ctypes.byref(params), 1, null, null, null, null, ctypes.byref(grads), null, 0,
                             null) == pk.PKM_E_ARG
     assert lib.pkm_forward_train(null, ctypes.byref(params), 1, null, null, null, null, null, null) == pk.PKM_E_ARG
+    assert lib.pkm_prepare(null, ctypes.byref(params), null) == pk.PKM_E_ARG
     assert lib.pkm_backward_with_q(null, ctypes.byref(params), 1, null, null, null, null, null, ctypes.byref(grads),
                                    null, 0, null) == pk.PKM_E_ARG
     good = pk.make_config(**GOOD)

@@ -183,3 +183,34 @@ def test_gradients_against_oracle(torch):
         g, r = t.cpu().numpy().astype(np.float64), ref[name]
         err = np.abs(g - r).max() / max(np.abs(r).max(), 1e-30)
         assert err <= 1e-4, (name, err)
+
+
+def test_prepared_weights_follow_the_parameters(torch):
+    """prepare_weights=True gives the unprepared layer's bits in eval mode,
+    with and without gradients, and stays right after an optimiser step
+    (the parameters change in place: the prepared copy is made again)."""
+    D, H, n, k, B = 256, 2, 64, 8, 300
+    ref_layer = make_layer(torch, D, H, n, k, "bf16", seed=31, max_batch=128).eval()
+    layer = make_layer(torch, D, H, n, k, "bf16", seed=31, max_batch=128, prepare_weights=True).eval()
+    x, dout = inputs(torch, B, D, 32)
+    say("layer prepared weights: eval, no grad")
+    with torch.no_grad():
+        assert torch.equal(layer(x), ref_layer(x))
+    opt = torch.optim.SGD(layer.parameters(), lr=0.5)
+    ref_opt = torch.optim.SGD(ref_layer.parameters(), lr=0.5)
+    for step in range(2):
+        say("layer prepared weights: gradient step", step)
+        for lay, o in ((layer, opt), (ref_layer, ref_opt)):
+            o.zero_grad()
+            (lay(x) * dout).sum().backward()
+            o.step()
+        torch.cuda.synchronize()
+        assert torch.equal(layer.wq, ref_layer.wq) and torch.equal(layer.subkeys, ref_layer.subkeys)
+        with torch.no_grad():
+            assert torch.equal(layer(x), ref_layer(x))
+    # a change the version counters do not see, then an explicit refresh
+    layer.wq.data.mul_(0.5)
+    ref_layer.wq.data.mul_(0.5)
+    layer.refresh_prepared()
+    with torch.no_grad():
+        assert torch.equal(layer(x), ref_layer(x))
