@@ -33,6 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 # Sources of each kernel: measured HBM traffic is only reported while they
 # are unchanged since the counters were taken.
 KERNEL_SOURCES = {"exponents": ["gemm_f32.hip"], "query_gemm": ["gemm_f32.hip"], "score_gemm": ["gemm_f32.hip"],
+                  "folded_gemm": ["gemm_f32.hip"],
                   "select": ["select.hip", "wave_ops.h"], "gather": ["gather.hip", "gather_dev.h"],
                   "select_gather": ["select.hip", "wave_ops.h", "gather_dev.h"]}
 
@@ -60,6 +61,7 @@ def per_token_work(wl):
     return {
         "query_flop": 2.0 * wl.H * wl.D * wl.D,              # a1: Wq[h] . x for every head
         "score_flop": 2.0 * wl.H * wl.n * wl.D,              # a3: 2 halves x n subkeys x D/2
+        "folded_flop": 2.0 * wl.D * 2 * wl.H * wl.n,         # a1-a3 folded: x . M for 2H n folded keys
         "select_bytes": wl.H * (2 * wl.n * 4 + wl.k * 8),    # a4-a6: read half scores, write idx + w
         # a7: the gathered rows (+ one fp32 scale per row for the scaled tables)
         "gather_bytes": wl.H * wl.k * (wl.D * ELT_BYTES[wl.table] + (4 if wl.table in SCALED else 0)),
@@ -81,6 +83,8 @@ def stage_bytes(wl, prepared=True):
     return {
         "query_gemm": 4 * (B * D + H * D * D + 4 * H * D + B * H * D),
         "score_gemm": 4 * (B * H * D + H * n * D + B * H * 2 * n),
+        # folded: x and the folded matrix (as pieces) read, the scores written
+        "folded_gemm": 4 * (B * D + 2 * H * n * D + 2 * H * n + B * H * 2 * n),
         "select": work["select_bytes"] * B,
         "gather": work["gather_bytes"] * B + B * H * k * 8 + B * D * 4,
         # fused: read the scores, write the selection, read the rows, write out
@@ -93,7 +97,8 @@ def stage_bytes(wl, prepared=True):
 def end_to_end(wl, ms):
     """Whole-step tokens/s against two bounds: the value gather alone at HBM
     peak, and the composite roofline sum over stages of max(flop / MFMA peak,
-    bytes / HBM peak)."""
+    bytes / HBM peak), with the method's own stages (projection, scoring,
+    selection and gather), whichever form the step runs them in."""
     work = per_token_work(wl)
     nbytes = stage_bytes(wl)
     flops = {"query_gemm": work["query_flop"] * wl.B, "score_gemm": work["score_flop"] * wl.B}
@@ -163,7 +168,7 @@ def timed_steps(torch, fn, steps, warmup, stats=None):
     return float(np.median(t))
 
 
-def kernel_times(torch, mem, P, xt, steps, warmup, wl):
+def kernel_times(torch, mem, P, xt, steps, warmup, wl, folded=False):
     """Median ms of each of the forward's own launches (pkm_forward_stage:
     the row exponents, the projection, the scoring, the selection with the
     gather), and of the stand-alone select and gather on the same scores.
@@ -187,9 +192,14 @@ def kernel_times(torch, mem, P, xt, steps, warmup, wl):
     out2 = torch.empty_like(out)
     mem.score(P, mem.query(P, xt, q), s)
     mem.select(s, idx2, w2)
-    if mem.cfg.max_batch >= B:
+    last = "select_gather" if fused(wl) else "select_and_gather"
+    if mem.cfg.max_batch >= B and folded:
+        # folded: stage 1 is a1-a3 as one contraction, stage 2 launches nothing
+        fwd = [lambda st=st: mem.forward_stage(P, xt, st, out, idx, w) for st in (0, 1, 3)]
+        fwd_names = ["exponents", "folded_gemm", last]
+    elif mem.cfg.max_batch >= B:
         fwd = [lambda st=st: mem.forward_stage(P, xt, st, out, idx, w) for st in range(4)]
-        fwd_names = ["exponents", "query_gemm", "score_gemm", "select_gather" if fused(wl) else "select_and_gather"]
+        fwd_names = ["exponents", "query_gemm", "score_gemm", last]
     else:
         fwd = [lambda: mem.query(P, xt, q), lambda: mem.score(P, q, s)]
         fwd_names = ["query_gemm", "score_gemm"]
@@ -200,6 +210,12 @@ def kernel_times(torch, mem, P, xt, steps, warmup, wl):
     blocks = [[]] + [fwd[:j + 1] for j in range(len(fwd))] + [single[:1], single]
     pairs = [(j + 1, j) for j in range(len(fwd))] + [(len(fwd) + 1, 0), (len(fwd) + 2, len(fwd) + 1)]
     names = fwd_names + ["select", "gather"]
+    if folded:
+        # the unfolded scoring from q^ on its own (its own exponent pass
+        # included), for the comparison with the flat search
+        blocks.append([lambda: mem.score(P, q, s)])
+        pairs.append((len(blocks) - 1, 0))
+        names.append("score_gemm_unfolded")
 
     def run(block):
         for f in block:
@@ -267,7 +283,7 @@ def flat_vs_product(torch, pk, wl, P, xt, kt, tokens=64, steps=5, warmup=2):
     prod_ms = timed_steps(torch, lambda: (mem.score(P, q, s), mem.select(s, pidx, pw)), 50, 10)
     same = bool((torch.sort(fidx, -1).values == torch.sort(pidx, -1).values).all().item())
     flat_flop = 2.0 * tokens * wl.H * wl.N * wl.D
-    full_batch_us = (kt["score_gemm"] + kt["select"]) * 1e3 / wl.B
+    full_batch_us = (kt.get("score_gemm", kt.get("score_gemm_unfolded")) + kt["select"]) * 1e3 / wl.B
     return {"tokens": tokens, "flat_ms": round(flat_ms, 4), "product_ms": round(prod_ms, 4),
             "speedup_same_tokens": round(flat_ms / prod_ms, 1),
             "flat_us_per_token": round(flat_ms * 1e3 / tokens, 3),
@@ -489,35 +505,47 @@ def main():
     # (pkm_prepare: Wq and the subkeys kept as the contractions read them, as
     # a server does once when it loads the layer); the step is timed with the
     # prepared weights, the same bits either way.
-    unprep_stats = {}
+    # The weights as they come (split in every call); prepared once as fp16
+    # pieces (bit for bit the same step); then, where n_keys <= D, folded
+    # (projection, batch-norm with its running statistics and subkeys as one
+    # matrix per half of a head), which is what a server does once when it
+    # loads the layer and what the step is timed with.
+    folded = wl.n <= wl.D
+    unprep_stats, split_stats = {}, {}
     unprep_ms = timed_steps(torch, lambda: mem.forward(P, xt, out, idx, wts), args.steps, args.warmup, unprep_stats)
-    prep_ms = timed_steps(torch, lambda: mem.prepare(P), 20, 5)
-    mem.prepare(P)
+    split_prep_ms = timed_steps(torch, lambda: mem.prepare(P, "split"), 20, 5)
+    mem.prepare(P, "split")
+    split_ms = timed_steps(torch, lambda: mem.forward(P, xt, out, idx, wts), args.steps, args.warmup, split_stats)
+    form = "fold" if folded else "split"
+    prep_ms = timed_steps(torch, lambda: mem.prepare(P, form), 5, 2)
+    mem.prepare(P, form)
     step_stats = {}
     ms = timed_steps(torch, lambda: mem.forward(P, xt, out, idx, wts), args.steps, args.warmup, step_stats)
     rows = idx.cpu().numpy().ravel()
     distinct = float(np.unique(rows).size) / rows.size
-    kt = kernel_times(torch, mem, P, xt, args.steps, args.warmup, wl)
+    kt = kernel_times(torch, mem, P, xt, args.steps, args.warmup, wl, folded)
     g_uniform_ms = gather_uniform_ms(torch, mem, P, wl, args.steps, args.warmup)
     hbm = hbm_measured(torch, mem, P, wl, args.steps, args.warmup)
 
     work = per_token_work(wl)
     B = wl.B
     rl = {
-        "query_gemm": ("mfma", work["query_flop"] * B / (kt["query_gemm"] * 1e-3) / 1e12, GEMM_PEAK_TFLOPS,
-                       "TFLOP/s"),
-        "score_gemm": ("mfma", work["score_flop"] * B / (kt["score_gemm"] * 1e-3) / 1e12, GEMM_PEAK_TFLOPS,
-                       "TFLOP/s"),
+        name: ("mfma", work[flop] * B / (kt[name] * 1e-3) / 1e12, GEMM_PEAK_TFLOPS, "TFLOP/s")
+        for name, flop in (("query_gemm", "query_flop"), ("score_gemm", "score_flop"), ("folded_gemm", "folded_flop"))
+        if name in kt
+    }
+    rl.update({
         "select": ("hbm", work["select_bytes"] * B / (kt["select"] * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"),
         "gather": ("hbm", work["gather_bytes"] * B / (kt["gather"] * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"),
-    }
+    })
     if "select_gather" in kt:
         rl["select_gather"] = ("hbm", (work["select_bytes"] + work["gather_bytes"]) * B /
                                (kt["select_gather"] * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s")
     if "exponents" in kt:
         rl["exponents"] = ("hbm", stage_bytes(wl)["exponents"] / (kt["exponents"] * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s")
     # the forward's own kernels; the dominant one is the headline roofline
-    forward_kernels = ((["exponents"] if "exponents" in kt else []) + ["query_gemm", "score_gemm"] +
+    forward_kernels = ((["exponents"] if "exponents" in kt else []) +
+                       (["folded_gemm"] if "folded_gemm" in kt else ["query_gemm", "score_gemm"]) +
                        (["select_gather"] if "select_gather" in kt else ["select", "gather"]))
     dominant = max(forward_kernels, key=kt.get)
 
@@ -550,11 +578,16 @@ def main():
         "gather_uniform_rows_gbs": round(work["gather_bytes"] * B / (g_uniform_ms * 1e-3) / 1e9, 1),
         "gathered_rows_distinct_frac": round(distinct, 4),
         "end_to_end": end_to_end(wl, ms),
-        "prepared_weights": {"prepare_ms": round(prep_ms, 4), "unprepared_ms_per_step": round(unprep_ms, 4),
+        "prepared_weights": {"form": form, "prepare_ms": round(prep_ms, 4),
+                             "unprepared_ms_per_step": round(unprep_ms, 4),
                              "unprepared_tokens_per_s": round(B / (unprep_ms * 1e-3), 1),
                              "unprepared_timing": unprep_stats,
-                             "note": "value is timed after pkm_prepare (Wq and the subkeys split into fp16 pieces "
-                                     "once); unprepared calls split them in every call, same results bit for bit"},
+                             "split_prepare_ms": round(split_prep_ms, 4), "split_ms_per_step": round(split_ms, 4),
+                             "split_tokens_per_s": round(B / (split_ms * 1e-3), 1), "split_timing": split_stats,
+                             "note": "value is timed after pkm_prepare once: 'fold' (n_keys <= D) runs a1-a3 as one "
+                                     "contraction of x with the folded projection, running-statistics batch-norm "
+                                     "and subkeys (fp32-accurate, checked against the oracle); 'split' keeps Wq and "
+                                     "the subkeys as fp16 pieces (bit for bit the unprepared step)"},
         "kernels_ms": {nm: round(v, 4) for nm, v in kt.items()},
         "forward_kernels": forward_kernels,
         "kernel_rooflines": {nm: {"achieved": round(rl[nm][1], 2), "unit": rl[nm][3],

@@ -148,23 +148,57 @@ void pkm_destroy(pkm_ctx *ctx);
 pkm_status pkm_forward(pkm_ctx *ctx, const pkm_params *p, int64_t B, const float *x, float *out, int32_t *idx,
                        float *weights, void *stream);
 
-/* Prepares the parameters that are the same for every call: Wq (a1) and
- * the subkeys (a3) are converted once into the form the two contractions
- * read -- each row scaled by a power of two and split into two fp16 pieces,
- * in the contractions' staging order (see gemm_f32.hip) -- and kept in the
- * context.  From then on pkm_forward, pkm_forward_stage and
- * pkm_forward_train on this context read that copy instead of p->wq and
- * p->subkeys whenever they are given these same two pointers, which saves
- * the per-call exponent pass over the weights and the splitting of B in
- * every tile.  The results are bit for bit those of the unprepared calls as
- * long as the two arrays hold what they held here: a caller that changes
- * either array (an optimiser step) must call pkm_prepare again, or
- * pkm_prepare(ctx, NULL, stream) to drop the copy.  Calls with other
- * pointers are unaffected.  Uses p->wq and p->subkeys only.  Like every
- * call, it enqueues on `stream`; forward calls on another stream must wait
- * for it.  PKM_E_ARG for a NULL or misaligned array; on any error nothing
- * stays prepared. */
-pkm_status pkm_prepare(pkm_ctx *ctx, const pkm_params *p, void *stream);
+/* Forms of prepared parameters (pkm_prepare). */
+typedef enum {
+    /* Wq and the subkeys split into fp16 pieces: bit for bit the unprepared
+     * results. */
+    PKM_PREPARE_SPLIT = 0,
+    /* Steps a1-a3 folded into one matrix per half of a head, for lookups
+     * with fixed batch-norm statistics (all three steps are linear maps):
+     * for head h, half p and subkey j,
+     *   s[h,p,j] = x . M[h,p,j,:] + bias[h,p,j],
+     *   M[h,p,j,i] = sum_f subkeys[h,p,j,f] m[f] Wq[h][f0+f, i],
+     *   bias[h,p,j] = sum_f subkeys[h,p,j,f] (beta[f0+f] - mean[f0+f] m[f]),
+     * m[f] = gamma[f0+f] / sqrt(var[f0+f] + eps), f0 = p D/2, f < D/2; the
+     * sums in fp64, rounded once to fp32.  The lookup then runs one
+     * contraction of x (2 B D 2H n flop) in place of the projection and the
+     * scoring (2 B H D (D + n)), with no q^ between them.  The scores agree
+     * with the unfolded ones to fp32 accuracy, not bit for bit.  Applies
+     * when n_keys <= D (otherwise folding adds work and PKM_PREPARE_SPLIT's
+     * form is prepared instead). */
+    PKM_PREPARE_FOLD = 1
+} pkm_prepare_form;
+
+/* Prepares the parameters that are the same for every call, once, in the
+ * form the contractions read, and keeps them in the context:
+ *   PKM_PREPARE_SPLIT: Wq (a1) and the subkeys (a3), each row scaled by a
+ *     power of two and split into two fp16 pieces in the contractions'
+ *     staging order (see gemm_f32.hip).  pkm_forward, pkm_forward_stage,
+ *     pkm_forward_train and pkm_half_scores on this context then read that
+ *     copy instead of p->wq and p->subkeys whenever they are given these
+ *     same two pointers (no per-call exponent pass over the weights, no
+ *     splitting of B in the tiles), with bit for bit the unprepared
+ *     results.  Uses p->wq and p->subkeys.
+ *   PKM_PREPARE_FOLD: the folded matrix and shift (see pkm_prepare_form),
+ *     used by pkm_forward, pkm_forward_stage and pkm_half_scores whenever
+ *     they are given the same wq, subkeys, bn_mean, bn_var, bn_gamma and
+ *     bn_beta pointers.  pkm_forward_train needs the projection itself and
+ *     reads p as given.  Uses those six arrays.
+ * The copy stands for the arrays' contents at this call: a caller that
+ * changes any of them (an optimiser step, new running statistics) must call
+ * pkm_prepare again, or pkm_prepare(ctx, NULL, 0, stream) to drop the copy.
+ * Calls with other pointers are unaffected.  Like every call it only
+ * enqueues on `stream`; forward calls on another stream must wait for it.
+ * PKM_E_ARG for a NULL or misaligned array or an unknown form; on any error
+ * nothing stays prepared. */
+pkm_status pkm_prepare(pkm_ctx *ctx, const pkm_params *p, int form, void *stream);
+
+/* Steps a1-a3 only, straight from the tokens: scores [B, H, 2, n] fp32 (the
+ * half scores the selection ranks), from x [B, D] and p (Wq, the batch-norm
+ * arrays and the subkeys; the folded form where pkm_prepare made one for
+ * them), in chunks of max_batch through the context's workspace. */
+pkm_status pkm_half_scores(pkm_ctx *ctx, const pkm_params *p, int64_t B, const float *x, float *scores,
+                           void *stream);
 
 /* The whole lookup (a1-a7) without a context and without allocating: for
  * callers that cannot allocate device memory (code under HIP graph capture,
@@ -196,6 +230,8 @@ pkm_status pkm_forward_noalloc(const pkm_config *cfg, const pkm_params *p, int64
  *   stage 1  a1-a2, the projection with BN (recording q^'s maxima)
  *   stage 2  a3, the subkey scoring
  *   stage 3  a4-a7, the selection and the gather (as pkm_select_gather)
+ * With a folded form prepared for p (PKM_PREPARE_FOLD): stage 0 the row
+ * exponents of x, stage 1 a1-a3 as one contraction, stage 2 nothing.
  * Stages 0, 1, 2, 3 in order on one stream, with the same arguments and no
  * other call on the context in between, do exactly what pkm_forward does
  * for those tokens, with the same results.  Arguments as pkm_forward; a

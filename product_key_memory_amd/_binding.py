@@ -20,8 +20,9 @@ EXPORTS = (
     "pkm_score", "pkm_select", "pkm_gather", "pkm_flat_workspace_bytes", "pkm_flat_search",
     "pkm_backward_workspace_bytes", "pkm_backward", "pkm_forward_batch_stats", "pkm_backward_batch_stats",
     "pkm_usage", "pkm_status_str", "pkm_last_error", "pkm_forward_noalloc", "pkm_select_gather",
-    "pkm_forward_stage", "pkm_forward_train", "pkm_backward_with_q", "pkm_prepare",
+    "pkm_forward_stage", "pkm_forward_train", "pkm_backward_with_q", "pkm_prepare", "pkm_half_scores",
 )
+PREPARE_FORMS = {"split": 0, "fold": 1}
 
 
 class PkmError(RuntimeError):
@@ -79,7 +80,8 @@ def load_library(path=LIB_PATH):
         "pkm_backward": (ctypes.c_int, [vp, par_p, i64, vp, vp, vp, vp, ctypes.POINTER(GradsStruct), vp,
                                         ctypes.c_size_t, vp]),
         "pkm_forward_train": (ctypes.c_int, [vp, par_p, i64, vp, vp, vp, vp, vp, vp]),
-        "pkm_prepare": (ctypes.c_int, [vp, par_p, vp]),
+        "pkm_prepare": (ctypes.c_int, [vp, par_p, ctypes.c_int, vp]),
+        "pkm_half_scores": (ctypes.c_int, [vp, par_p, i64, vp, vp, vp]),
         "pkm_backward_with_q": (ctypes.c_int, [vp, par_p, i64, vp, vp, vp, vp, vp, ctypes.POINTER(GradsStruct), vp,
                                                ctypes.c_size_t, vp]),
         "pkm_status_str": (ctypes.c_char_p, [ctypes.c_int]),
@@ -259,16 +261,34 @@ class Memory:
             if vt in SCALED:
                 _expect(t["value_scale"], "value_scale", (n * n,), "float32", t["values"].device)
 
-    def prepare(self, params, stream=None):
-        """pkm_prepare: keep Wq and the subkeys of `params` in the form the
-        contractions read, for forward calls with these same arrays (their
-        contents must not change until prepare is called again).  None drops
-        the prepared form."""
+    def prepare(self, params, form="split", stream=None):
+        """pkm_prepare: keep the parameters that are the same for every call
+        in the form the contractions read, for forward calls with these same
+        arrays (their contents must not change until prepare is called
+        again).  form "split": Wq and the subkeys as fp16 pieces (bit for bit
+        the unprepared results); "fold": projection, batch-norm and subkeys
+        folded into one matrix per half of a head (n_keys <= D; fp32-accurate,
+        not bitwise).  None drops the prepared form."""
         if params is None:
-            _check(self.lib.pkm_prepare(self._ctx, None, _stream_handle(stream)))
+            _check(self.lib.pkm_prepare(self._ctx, None, 0, _stream_handle(stream)))
             return
         self.check_params(params, parts=("query", "subkeys"))
-        _check(self.lib.pkm_prepare(self._ctx, ctypes.byref(params.struct), _stream_handle(stream)))
+        _check(self.lib.pkm_prepare(self._ctx, ctypes.byref(params.struct), PREPARE_FORMS[form],
+                                    _stream_handle(stream)))
+
+    def half_scores(self, params, x, scores=None, stream=None):
+        """pkm_half_scores: steps a1-a3 from x, scores [B, H, 2, n] f32 (through
+        the folded form when one was prepared for these arrays)."""
+        torch = _torch()
+        B = x.shape[0]
+        self.check_params(params, ("query", "subkeys"))
+        _expect(x, "x", (B, self.dim), "float32", params["wq"].device)
+        shape = (B, self.heads, 2, self.n_keys)
+        scores = self._new(shape, torch.float32, x) if scores is None else scores
+        _expect(scores, "scores", shape, "float32", x.device)
+        _check(self.lib.pkm_half_scores(self._ctx, ctypes.byref(params.struct), B, _ptr(x), _ptr(scores),
+                                        _stream_handle(stream)))
+        return scores
 
     def forward(self, params, x, out=None, idx=None, weights=None, stream=None, keep_selection=True):
         """The whole lookup.  Returns (out [B,D] f32, idx [B,H,k] i32,

@@ -466,6 +466,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, int tm, int tn, int
                 mul = a.bn_gamma[col] / sqrtf(a.bn_var[col] + a.bn_eps);
                 beta = a.bn_beta[col];
             }
+            const float bias = a.col_bias ? a.col_bias[(int64_t)g * a.N + col] : 0.0f;
 #pragma unroll
             for (int i = 0; i < T::TM; ++i) {
 #pragma unroll
@@ -479,6 +480,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, int tm, int tn, int
                         if (row < a.M) {
                             float c = __builtin_ldexpf(acc[i][j][v4 * 4 + e], -(er[e] + ecol));
                             if (BN_EPILOGUE) c = (c - mean) * mul + beta;
+                            if (a.col_bias) c += bias;
                             __builtin_nontemporal_store(c, &C[(int64_t)row * a.ldc + col]);
                         }
                     }
@@ -858,6 +860,80 @@ __global__ __launch_bounds__(256) void split_rows_kernel(const float *B, const f
     dst[64] = lo;
 }
 
+// The query projection, inference batch-norm and one subkey set folded
+// into one matrix (all three are linear maps, the batch-norm's statistics
+// fixed): for head h, half p and subkey j,
+//   s[f] . qhat[f] summed over the half's features f = x . M[g][j] + bias[g][j]
+// with g = 2h + p, m_f = gamma_f / sqrt(var_f + eps),
+//   M[g][j][i] = sum_f C[g][j][f] m_f Wq[h][f][i],
+//   bias[g][j] = sum_f C[g][j][f] (beta_f - mean_f m_f),
+// f over the half's D/2 features (C = the half's subkeys).  Accumulated in
+// fp64 from the fp32 parameters and rounded once to fp32.  64 x 64 tiles of
+// (j, i), 256 threads of 4 x 4 outputs, f in steps of 16 through LDS.
+__global__ __launch_bounds__(256) void fold_kernel(const float *wq, const float *mean, const float *var,
+                                                   const float *gamma, const float *beta, double eps,
+                                                   const float *sub, int D, int n, float *M, float *bias)
+{
+    const int g = blockIdx.z, h = g >> 1, p = g & 1, half = D / 2;
+    const int j0 = blockIdx.y * 64, i0 = blockIdx.x * 64;
+    const int f_base = h * D + p * half;  // the half's first feature in [H][D]
+    const float *C = sub + (int64_t)g * n * half;
+    __shared__ double As[16][65];  // [f][j]: C[j][f] m_f
+    __shared__ double Bs[16][65];  // [f][i]: Wq[h][f][i]
+    const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
+    double acc[4][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[r][c] = 0.0;
+    for (int f0 = 0; f0 < half; f0 += 16) {
+        for (int e = threadIdx.x; e < 1024; e += 256) {
+            const int jj = e / 16, ff = e % 16;  // C rows run along f
+            const int j = j0 + jj, f = f0 + ff;
+            double v = 0.0;
+            if (j < n) {
+                const int hf = f_base + f;
+                const double m = (double)gamma[hf] / sqrt((double)var[hf] + eps);
+                v = (double)C[(int64_t)j * half + f] * m;
+            }
+            As[ff][jj] = v;
+            const int ff2 = e / 64, ii = e % 64;  // Wq rows run along i
+            Bs[ff2][ii] = (double)wq[((int64_t)f_base + f0 + ff2) * D + i0 + ii];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int ff = 0; ff < 16; ++ff) {
+            double a[4], b[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) a[r] = As[ff][ty * 4 + r];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) b[c] = Bs[ff][tx * 4 + c];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) acc[r][c] = fma(a[r], b[c], acc[r][c]);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int j = j0 + ty * 4 + r;
+        if (j >= n) continue;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) M[((int64_t)g * n + j) * D + i0 + tx * 4 + c] = (float)acc[r][c];
+    }
+    if (blockIdx.x == 0 && threadIdx.x < 64 && j0 + (int)threadIdx.x < n) {
+        const int j = j0 + threadIdx.x;
+        double b = 0.0;
+        for (int f = 0; f < half; ++f) {
+            const int hf = f_base + f;
+            const double m = (double)gamma[hf] / sqrt((double)var[hf] + eps);
+            b = fma((double)C[(int64_t)j * half + f], (double)beta[hf] - (double)mean[hf] * m, b);
+        }
+        bias[(int64_t)g * n + j] = (float)b;
+    }
+}
+
 template <typename T>
 int64_t tile_count(const GemmArgs &a)
 {
@@ -986,6 +1062,15 @@ hipError_t launch_presplit(const float *B, int64_t stride, int64_t ld, int rows,
     const int64_t per_set = (int64_t)((rows + 31) / 32) * kch * 64;
     hipLaunchKernelGGL(split_rows_kernel, dim3((unsigned)((per_set + 255) / 256), batch), dim3(256), 0, stream, B,
                        nullptr, stride, ld, rows, kch, exp, nullptr, reinterpret_cast<u4 *>(out));
+    return hipGetLastError();
+}
+
+hipError_t launch_fold(const float *wq, const float *mean, const float *var, const float *gamma, const float *beta,
+                       float eps, const float *subkeys, int D, int H, int n, float *M, float *bias, hipStream_t stream)
+{
+    if (D % 64 != 0 || D / 2 % 16 != 0 || H < 1 || n < 1 || 2 * H > 65535) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(fold_kernel, dim3(D / 64, (n + 63) / 64, 2 * H), dim3(256), 0, stream, wq, mean, var, gamma,
+                       beta, (double)eps, subkeys, D, n, M, bias);
     return hipGetLastError();
 }
 

@@ -34,6 +34,15 @@ struct pkm_ctx {
     void *prep_wq;
     void *prep_sub;
     const float *prep_wq_src, *prep_sub_src;
+    // Folded form (pkm_prepare with PKM_PREPARE_FOLD, n_keys <= D): the
+    // matrix of the folded projection, batch-norm and subkeys as fp16 pieces
+    // with its row exponents, the per-key shift, and the batch-norm arrays
+    // it was made from.
+    int prep_mode;  // 0 nothing, 1 split, 2 folded
+    int32_t *fold_exp;  // [2H * n]
+    float *fold_bias;   // [2H * n]
+    void *fold_pieces;
+    const float *prep_bn_src[4];  // mean, var, gamma, beta
 };
 
 namespace {
@@ -86,7 +95,7 @@ int64_t forward_exp_ints(const pkm_config &c)
 // GEMM row exponents, q^'s per-half maxima and the subkeys' row exponents;
 // then (only with prepared) the prepared weights: Wq's and the subkeys' row
 // exponents and fp16 pieces.  False on size overflow.
-constexpr int kPieces = 12;
+constexpr int kPieces = 15;
 bool workspace_layout(const pkm_config &c, size_t sizes[kPieces], bool batch_stats = true, bool prepared = true)
 {
     const double mb = (double)c.max_batch;
@@ -105,6 +114,12 @@ bool workspace_layout(const pkm_config &c, size_t sizes[kPieces], bool batch_sta
     sizes[9] = prepared ? sizes[7] : 0;
     sizes[10] = prepared ? round_up((size_t)pkm::gemm_presplit_bytes(c.heads * c.dim, c.dim, 1)) : 0;
     sizes[11] = prepared ? round_up((size_t)pkm::gemm_presplit_bytes(c.n_keys, c.dim / 2, 2 * c.heads)) : 0;
+    // the folded form, where it applies (n_keys <= D); pkm_prepare builds
+    // its fp32 matrix in pieces 10-11 first (as large: n_keys <= D)
+    const bool fold = prepared && c.n_keys <= c.dim;
+    sizes[12] = fold ? round_up(2 * H * (size_t)c.n_keys * sizeof(int32_t)) : 0;
+    sizes[13] = fold ? round_up(2 * H * (size_t)c.n_keys * sizeof(float)) : 0;
+    sizes[14] = fold ? round_up((size_t)pkm::gemm_presplit_bytes(2 * c.heads * c.n_keys, c.dim, 1)) : 0;
     return true;
 }
 
@@ -130,6 +145,11 @@ void assign_workspace(pkm_ctx *ctx, char *w, const size_t sizes[kPieces])
     ctx->prep_wq = piece[10];
     ctx->prep_sub = piece[11];
     ctx->prep_wq_src = ctx->prep_sub_src = nullptr;
+    ctx->prep_mode = 0;
+    ctx->fold_exp = sizes[12] ? reinterpret_cast<int32_t *>(piece[12]) : nullptr;
+    ctx->fold_bias = sizes[13] ? reinterpret_cast<float *>(piece[13]) : nullptr;
+    ctx->fold_pieces = sizes[14] ? piece[14] : nullptr;
+    for (auto &b : ctx->prep_bn_src) b = nullptr;
 }
 
 pkm_status check_config(const pkm_config *c)
@@ -440,15 +460,49 @@ pkm_status check_forward_args(const pkm_config &c, const pkm_params *p, const fl
 // clearing q^'s maxima), 1 the projection with BN (recording q^'s maxima),
 // 2 the subkey scoring, 3 the selection and the gather (one fused kernel
 // where select_gather_fusable, else two).  keep: write idx / w out.
+// Whether p names the arrays the context's folded form was made from.
+bool folded_for(const pkm_ctx *ctx, const pkm_params *p)
+{
+    return ctx->prep_mode == 2 && ctx->prep_wq_src == p->wq && ctx->prep_sub_src == p->subkeys &&
+           ctx->prep_bn_src[0] == p->bn_mean && ctx->prep_bn_src[1] == p->bn_var &&
+           ctx->prep_bn_src[2] == p->bn_gamma && ctx->prep_bn_src[3] == p->bn_beta;
+}
+
 pkm_status forward_stage(const pkm_ctx *ctx, const pkm_params *p, int64_t nb, const float *x, float *out,
-                         int32_t *ci, float *cw, bool keep, int stage, hipStream_t st, float *q_pre = nullptr)
+                         int32_t *ci, float *cw, bool keep, int stage, hipStream_t st, float *q_pre = nullptr,
+                         float *scores_out = nullptr)
 {
     const pkm_config &c = ctx->cfg;
     const int64_t H = c.heads, k = c.k;
+    float *scores = scores_out ? scores_out : ctx->scores;
+    // Folded (and no projection wanted): the half scores in one contraction
+    // of x with the folded matrix, stage 0 x's row exponents, stage 1 the
+    // contraction, stage 2 nothing.
+    if (!q_pre && folded_for(ctx, p) && stage <= 2) {
+        if (stage == 2) return PKM_OK;
+        pkm::GemmArgs a{};
+        a.exp_ws = ctx->gemm_exp;
+        a.exp_ws_ints = ctx->gemm_exp_ints;
+        a.A = x;
+        a.lda = c.dim;
+        a.M = (int)nb;
+        a.N = 2 * c.heads * c.n_keys;
+        a.K = c.dim;
+        a.batch = 1;
+        a.b_exp_given = ctx->fold_exp;
+        a.b_presplit = ctx->fold_pieces;
+        a.ldb = c.dim;
+        a.C = scores;  // [nb][2H][n]
+        a.ldc = 2 * (int64_t)c.heads * c.n_keys;
+        a.stream_out = true;  // read once, by the select
+        a.col_bias = ctx->fold_bias;
+        a.exp_phase = stage == 0 ? 1 : 2;
+        return launched(pkm::launch_gemm_nt_f32(a, st), stage == 0 ? "row exponents" : "folded scoring");
+    }
     // Wq and the subkeys from their prepared form when p names the arrays
     // pkm_prepare took them from (the same pieces and exponents the tiles
     // would compute, so the same results)
-    const bool prep = ctx->prep_wq_src && ctx->prep_wq_src == p->wq && ctx->prep_sub_src == p->subkeys;
+    const bool prep = ctx->prep_mode == 1 && ctx->prep_wq_src == p->wq && ctx->prep_sub_src == p->subkeys;
     if (stage <= 1) {
         pkm::GemmArgs a = query_args(c, p, nb, x, ctx->qhat, ctx->gemm_exp, ctx->gemm_exp_ints);
         a.row_seg_max = ctx->qmax;
@@ -473,7 +527,7 @@ pkm_status forward_stage(const pkm_ctx *ctx, const pkm_params *p, int64_t nb, co
         return launched(pkm::launch_gemm_nt_f32(a, st), stage == 0 ? "row exponents" : "query projection");
     }
     if (stage == 2) {
-        pkm::GemmArgs a = score_args(c, p, nb, ctx->qhat, ctx->scores, ctx->gemm_exp, ctx->gemm_exp_ints);
+        pkm::GemmArgs a = score_args(c, p, nb, ctx->qhat, scores, ctx->gemm_exp, ctx->gemm_exp_ints);
         a.a_rowmax = ctx->qmax;
         a.a_rowmax_ld = 2 * c.heads;
         a.b_exp_given = prep ? ctx->prep_sub_exp : ctx->sub_exp;
@@ -481,12 +535,12 @@ pkm_status forward_stage(const pkm_ctx *ctx, const pkm_params *p, int64_t nb, co
         return launched(pkm::launch_gemm_nt_f32(a, st), "subkey scoring");
     }
     if (pkm::select_gather_fusable(c.heads, c.n_keys, c.k, c.value_type, c.dim))
-        return launched(pkm::launch_select_gather(ctx->scores, nb, c.heads, c.n_keys, c.k, p->values, p->value_scale,
+        return launched(pkm::launch_select_gather(scores, nb, c.heads, c.n_keys, c.k, p->values, p->value_scale,
                                                   c.value_type, c.dim, c.n_keys * c.n_keys, keep ? ci : nullptr,
                                                   keep ? cw : nullptr, out, st),
                         "select and gather");
     pkm_status s;
-    if ((s = launched(pkm::launch_select(ctx->scores, nb, c.heads, c.n_keys, c.k, ci, cw, st), "select"))) return s;
+    if ((s = launched(pkm::launch_select(scores, nb, c.heads, c.n_keys, c.k, ci, cw, st), "select"))) return s;
     return launched(pkm::launch_gather(p->values, p->value_scale, c.value_type, c.dim, c.n_keys * c.n_keys, nb,
                                        (int)(H * k), ci, cw, out, st),
                     "gather");
@@ -655,24 +709,68 @@ pkm_status pkm_forward(pkm_ctx *ctx, const pkm_params *p, int64_t B, const float
     return ok();
 }
 
-pkm_status pkm_prepare(pkm_ctx *ctx, const pkm_params *p, void *stream)
+pkm_status pkm_prepare(pkm_ctx *ctx, const pkm_params *p, int flags, void *stream)
 {
     pkm_status s;
     if ((s = check_ctx(ctx))) return s;
     ctx->prep_wq_src = ctx->prep_sub_src = nullptr;
+    for (auto &b : ctx->prep_bn_src) b = nullptr;
+    ctx->prep_mode = 0;
     if (!p) return ok();  // only dropped
+    if (flags != PKM_PREPARE_SPLIT && flags != PKM_PREPARE_FOLD) return fail(PKM_E_ARG, "unknown flags %d", flags);
     if ((s = need(p->wq, "wq")) || (s = need(p->subkeys, "subkeys"))) return s;
     const pkm_config &c = ctx->cfg;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if ((s = launched(pkm::launch_presplit(p->wq, 0, c.dim, c.heads * c.dim, c.dim, 1, ctx->prep_wq_exp, ctx->prep_wq,
-                                           st),
-                      "Wq split")) ||
-        (s = launched(pkm::launch_presplit(p->subkeys, (int64_t)c.n_keys * (c.dim / 2), c.dim / 2, c.n_keys,
-                                           c.dim / 2, 2 * c.heads, ctx->prep_sub_exp, ctx->prep_sub, st),
-                      "subkey split")))
-        return s;
+    if (flags == PKM_PREPARE_FOLD && ctx->fold_pieces) {
+        if ((s = check_query_params(p))) return s;
+        // the fp32 folded matrix is built where the split form would go
+        float *M = static_cast<float *>(ctx->prep_wq);
+        const int rows = 2 * c.heads * c.n_keys;
+        if ((s = launched(pkm::launch_fold(p->wq, p->bn_mean, p->bn_var, p->bn_gamma, p->bn_beta, c.bn_eps,
+                                           p->subkeys, c.dim, c.heads, c.n_keys, M, ctx->fold_bias, st),
+                          "fold")) ||
+            (s = launched(pkm::launch_presplit(M, 0, c.dim, rows, c.dim, 1, ctx->fold_exp, ctx->fold_pieces, st),
+                          "folded split")))
+            return s;
+        ctx->prep_bn_src[0] = p->bn_mean;
+        ctx->prep_bn_src[1] = p->bn_var;
+        ctx->prep_bn_src[2] = p->bn_gamma;
+        ctx->prep_bn_src[3] = p->bn_beta;
+        ctx->prep_mode = 2;
+    } else {
+        if ((s = launched(pkm::launch_presplit(p->wq, 0, c.dim, c.heads * c.dim, c.dim, 1, ctx->prep_wq_exp,
+                                               ctx->prep_wq, st),
+                          "Wq split")) ||
+            (s = launched(pkm::launch_presplit(p->subkeys, (int64_t)c.n_keys * (c.dim / 2), c.dim / 2, c.n_keys,
+                                               c.dim / 2, 2 * c.heads, ctx->prep_sub_exp, ctx->prep_sub, st),
+                          "subkey split")))
+            return s;
+        ctx->prep_mode = 1;
+    }
     ctx->prep_wq_src = p->wq;
     ctx->prep_sub_src = p->subkeys;
+    return ok();
+}
+
+pkm_status pkm_half_scores(pkm_ctx *ctx, const pkm_params *p, int64_t B, const float *x, float *scores,
+                           void *stream)
+{
+    pkm_status s;
+    if ((s = check_ctx(ctx)) || (s = check_batch(ctx->cfg, B))) return s;
+    if (B == 0) return ok();
+    if (!p) return fail(PKM_E_ARG, "params is NULL");
+    if ((s = check_query_params(p)) || (s = need(p->subkeys, "subkeys")) || (s = need(x, "x")) ||
+        (s = need(scores, "scores")))
+        return s;
+    const pkm_config &c = ctx->cfg;
+    const int64_t D = c.dim, per = 2 * (int64_t)c.heads * c.n_keys;
+    for (int64_t b0 = 0; b0 < B; b0 += c.max_batch) {
+        const int64_t nb = B - b0 < c.max_batch ? B - b0 : c.max_batch;
+        for (int stage = 0; stage < 3; ++stage)
+            if ((s = forward_stage(ctx, p, nb, x + b0 * D, nullptr, nullptr, nullptr, false, stage,
+                                   static_cast<hipStream_t>(stream), nullptr, scores + b0 * per)))
+                return s;
+    }
     return ok();
 }
 

@@ -76,6 +76,10 @@ struct GemmArgs {
     // launch_presplit (16-byte aligned), so the tiles copy them instead of
     // splitting B.  Bitwise the same results as splitting in the tiles.
     const void *b_presplit;
+    // Optional, with stream_out: a per-column term added to every result,
+    // col_bias[g * N + n] for batch entry g (the folded lookup's batch-norm
+    // shift).
+    const float *col_bias;
     // Optional: one more set of row exponents for a later contraction,
     // computed in this one's pre-pass (rows_per_batch * batch rows of K
     // floats, row m of entry g at base + g * stride + m * ld).
@@ -121,6 +125,13 @@ hipError_t launch_gemm_nt_f32(const GemmArgs &a, hipStream_t stream);
 int64_t gemm_presplit_bytes(int rows, int K, int batch);
 hipError_t launch_presplit(const float *B, int64_t stride, int64_t ld, int rows, int K, int batch, int32_t *exp,
                            void *out, hipStream_t stream);
+// The projection, inference batch-norm and subkeys folded, for the lookup
+// with fixed statistics: M [2H][n][D] and bias [2H][n] fp32 (fp64
+// accumulation, one rounding) with, for g = 2h + p, the half scores
+// s[b][g][j] = x[b] . M[g][j] + bias[g][j].  D % 64 == 0.
+hipError_t launch_fold(const float *wq, const float *mean, const float *var, const float *gamma, const float *beta,
+                       float eps, const float *subkeys, int D, int H, int n, float *M, float *bias,
+                       hipStream_t stream);
 // The same contraction with a product-key B operand (b_split required) and
 // 32 x 256 tiles, suited to a few dozen rows of A (the flat exact search
 // over all keys).

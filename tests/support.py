@@ -187,3 +187,10 @@ def weights_by_index(idx, w, ref_idx):
     sorted_w = np.take_along_axis(w, order, -1)
     inv = np.argsort(ref_order, -1)
     return np.take_along_axis(sorted_w, inv, -1)
+
+
+def to_device(a):
+    """A numpy array as a contiguous tensor on the GPU."""
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device())

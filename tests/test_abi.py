@@ -89,6 +89,9 @@ def test_workspace_bytes():
     # prepared weights: Wq's and the subkeys' row exponents, and both split
     # into two fp16 pieces (as many bytes as the fp32 arrays)
     prepared = H * D * 4 + sub_exp + H * D * D * 4 + H * 2 * n * (D // 2) * 4
+    # the folded form (n_keys <= D): row exponents, shifts and fp16 pieces of
+    # the [2H n, D] folded matrix
+    prepared += 2 * H * n * 4 * 2 + 2 * H * n * D * 4
     assert (pk.workspace_bytes(cfg) ==
             4 * mb * H * (D + 2 * n + 2 * k) + stat_part + exps + qmax + sub_exp + prepared)
     with pytest.raises(pk.PkmError):
@@ -171,7 +174,8 @@ def test_null_arguments_rejected_before_any_launch():
     assert lib.pkm_backward(null, ctypes.byref(params), 1, null, null, null, null, ctypes.byref(grads), null, 0,
                             null) == pk.PKM_E_ARG
     assert lib.pkm_forward_train(null, ctypes.byref(params), 1, null, null, null, null, null, null) == pk.PKM_E_ARG
-    assert lib.pkm_prepare(null, ctypes.byref(params), null) == pk.PKM_E_ARG
+    assert lib.pkm_prepare(null, ctypes.byref(params), 0, null) == pk.PKM_E_ARG
+    assert lib.pkm_half_scores(null, ctypes.byref(params), 1, null, null, null) == pk.PKM_E_ARG
     assert lib.pkm_backward_with_q(null, ctypes.byref(params), 1, null, null, null, null, null, ctypes.byref(grads),
                                    null, 0, null) == pk.PKM_E_ARG
     good = pk.make_config(**GOOD)

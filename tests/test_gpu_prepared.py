@@ -116,7 +116,7 @@ def test_prepared_only_for_the_prepared_arrays(torch):
     mem.prepare(P)
     bad = pk._binding.ParamsStruct(*[getattr(P.struct, f) for f, _ in pk._binding.ParamsStruct._fields_])
     bad.wq = None
-    assert mem.lib.pkm_prepare(mem._ctx, ctypes.byref(bad), None) == pk.PKM_E_ARG
+    assert mem.lib.pkm_prepare(mem._ctx, ctypes.byref(bad), 0, None) == pk.PKM_E_ARG
     P["wq"].mul_(2.0)
     after_fail = mem.forward(P, xt)
     mem.prepare(P)
