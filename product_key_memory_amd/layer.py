@@ -21,13 +21,17 @@ this module only allocates the gradient buffers and hands them to autograd.
   gradient), for optimisers that take sparse gradients.  E4M3, int8 and
   int4 tables (with their row scales) are buffers: looked up, not trained.
 
-- prepare_weights=True: the library keeps wq and the subkeys in the form
-  its contractions read (pkm_prepare), so each eval-mode forward skips
-  converting them; the copy is made again whenever either parameter has
-  changed in place since (torch's version counters: optimiser steps,
-  load_state_dict, copy_ under no_grad).  Changes that bypass the counters
-  (writing through .data) need refresh_prepared().  Same results bit for
-  bit.
+- prepare_weights=True (or "split"): the library keeps wq and the subkeys
+  in the form its contractions read (pkm_prepare), so each eval-mode
+  forward skips converting them; same results bit for bit.
+  prepare_weights="fold": eval-mode forwards without gradients run the
+  folded lookup (projection, batch-norm with the running statistics and
+  subkeys folded into one key matrix per half of a head; n_keys <= dim),
+  fp32-accurate rather than bitwise.  Either copy is made again whenever a
+  parameter it was made from has changed in place since (torch's version
+  counters: optimiser steps, load_state_dict, copy_ under no_grad; a
+  training-mode forward, which moves the running statistics).  Changes that
+  bypass the counters (writing through .data) need refresh_prepared().
 
 There is no CPU path: the module lives on a GPU, and every call raises if
 libpkm.so cannot be loaded.  Calls of one module must not overlap on
@@ -53,6 +57,7 @@ class _Lookup(torch.autograd.Function):
         if layer.training:
             out, idx, w, mean, var = mem.forward_batch_stats(
                 P, x, running=(layer.running_mean, layer.running_var), momentum=layer.momentum)
+            layer._prep_key = None  # the running statistics moved (behind torch's counters)
             ctx.save_for_backward(x, idx, w, mean, var)
         else:
             layer._sync_prepared(P)
@@ -143,7 +148,10 @@ class ProductKeyMemory(torch.nn.Module):
         self.dim, self.heads, self.n_keys, self.k = int(dim), int(heads), int(n_keys), int(k)
         self.value_type, self.bn_eps, self.momentum = value_type, float(bn_eps), float(momentum)
         self.max_batch, self.sparse_values = int(max_batch), bool(sparse_values)
-        self.prepare_weights, self._prep_key = bool(prepare_weights), None
+        if prepare_weights not in (False, True, "split", "fold"):
+            raise ValueError('prepare_weights must be False, True, "split" or "fold"')
+        self.prepare_weights = "split" if prepare_weights is True else prepare_weights
+        self._prep_key = None
         D, H, n = self.dim, self.heads, self.n_keys
         f32 = dict(dtype=torch.float32, device=device)
         self.wq = torch.nn.Parameter(torch.empty(H, D, D, **f32))
@@ -200,13 +208,17 @@ class ProductKeyMemory(torch.nn.Module):
         return self._mem
 
     def _sync_prepared(self, P):
-        """With prepare_weights: prepares wq and the subkeys again when
-        either changed since the last time (pointer or version counter)."""
+        """With prepare_weights: prepares again when an array the prepared
+        form was made from changed since the last time (pointer or version
+        counter)."""
         if not self.prepare_weights:
             return
-        key = (self.wq.data_ptr(), self.wq._version, self.subkeys.data_ptr(), self.subkeys._version)
+        arrays = (self.wq, self.subkeys)
+        if self.prepare_weights == "fold":
+            arrays += (self.running_mean, self.running_var, self.bn_gamma, self.bn_beta)
+        key = tuple((t.data_ptr(), t._version) for t in arrays)
         if key != self._prep_key:
-            self._memory().prepare(P)
+            self._memory().prepare(P, self.prepare_weights)
             self._prep_key = key
 
     def refresh_prepared(self):

@@ -4,7 +4,7 @@
  * Usage: pkm_forward_main <inputs> <outputs>
  *
  * <inputs> (little-endian, written by the test that runs this program):
- *   char[8] "PKMIN1\0\0"; int32 D, H, n_keys, k, value_type, pad;
+ *   char[8] "PKMIN1\0\0"; int32 D, H, n_keys, k, value_type, prepare;
  *   int64 B, max_batch;
  *   float wq[H*D*D], bn_mean[H*D], bn_var[H*D], bn_gamma[H*D], bn_beta[H*D],
  *         subkeys[H*2*n*(D/2)];
@@ -12,6 +12,9 @@
  *   float value_scale[N]    (E4M3, int8 and int4 tables only);
  *   float x[B*D].
  * <outputs>: float out[B*D]; int32 idx[B*H*k]; float weights[B*H*k].
+ *
+ * prepare: 0 none; 1 or 2 call pkm_prepare with PKM_PREPARE_SPLIT or
+ * PKM_PREPARE_FOLD before the lookup.
  *
  * Before the lookup it checks two calls that must not launch anything: a
  * negative B (PKM_E_ARG) and B = 0 (PKM_OK).  Exit status 0 on success. */
@@ -74,7 +77,8 @@ int main(int argc, char **argv)
     int64_t sizes[2];
     if (fread(magic, 1, 8, f) != 8 || memcmp(magic, "PKMIN1\0\0", 8) != 0) fail("bad magic");
     if (fread(hdr, sizeof hdr, 1, f) != 1 || fread(sizes, sizeof sizes, 1, f) != 1) fail("short header");
-    const int32_t D = hdr[0], H = hdr[1], n = hdr[2], k = hdr[3], vt = hdr[4];
+    const int32_t D = hdr[0], H = hdr[1], n = hdr[2], k = hdr[3], vt = hdr[4], prepare = hdr[5];
+    if (prepare < 0 || prepare > 2) fail("prepare must be 0, 1 or 2");
     const int64_t B = sizes[0];
 
     pkm_config cfg;
@@ -125,6 +129,13 @@ int main(int argc, char **argv)
     if (pkm_forward(ctx, &p, -1, x, out, idx, w, stream) != PKM_E_ARG) fail("B = -1 was accepted");
     if (pkm_forward(ctx, &p, 0, x, out, idx, w, stream) != PKM_OK) fail("B = 0 was rejected");
 
+    if (prepare) {
+        st = pkm_prepare(ctx, &p, prepare == 2 ? PKM_PREPARE_FOLD : PKM_PREPARE_SPLIT, stream);
+        if (st != PKM_OK) {
+            fprintf(stderr, "pkm_prepare: %s (%s)\n", pkm_status_str(st), pkm_last_error());
+            return 1;
+        }
+    }
     st = pkm_forward(ctx, &p, B, x, out, idx, w, stream);
     if (st != PKM_OK) {
         fprintf(stderr, "pkm_forward: %s (%s)\n", pkm_status_str(st), pkm_last_error());

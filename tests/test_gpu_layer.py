@@ -214,3 +214,45 @@ def test_prepared_weights_follow_the_parameters(torch):
     layer.refresh_prepared()
     with torch.no_grad():
         assert torch.equal(layer(x), ref_layer(x))
+
+
+def test_folded_layer_follows_the_parameters(torch):
+    """prepare_weights="fold": eval forwards without gradients match the
+    oracle (gap-clean inputs), and stay right after the running statistics
+    move (a training-mode forward) and after an optimiser step, where the
+    folded form is made again: the outputs then equal a fresh folded
+    lookup of the new parameters."""
+    D, H, n, k, B = 256, 2, 64, 8, 300
+    layer = make_layer(torch, D, H, n, k, "f32", seed=41, max_batch=512, prepare_weights="fold").eval()
+    _, dout = inputs(torch, B, D, 42)
+    wl = synthetic.Workload("layer", B, D, H, n, k, "f32", "random")
+    params = {"wq": layer.wq.detach().cpu().numpy(), "mean": layer.running_mean.cpu().numpy(),
+              "var": layer.running_var.cpu().numpy(), "gamma": layer.bn_gamma.detach().cpu().numpy(),
+              "beta": layer.bn_beta.detach().cpu().numpy(), "subkeys": layer.subkeys.detach().cpu().numpy(),
+              "values": layer.values.detach().cpu().numpy(), "scale": None}
+    xn = synthetic.make_x(wl, seed=42)
+    _, tau = support.gap_clean(wl, params, xn, seed=42, want_tau=True)
+    x = support.to_device(xn)
+    say("layer folded: eval vs oracle")
+    with torch.no_grad():
+        out, idx, w = layer(x, return_selection=True)
+    torch.cuda.synchronize()
+    r = oracle.run(support.model_for(wl, params), xn, want=("out", "idx", "top"))
+    support.check_indices(idx.cpu().numpy(), r["idx"], r["top"], tau)
+    assert support.rel_rowmax_err(out.cpu().numpy(), r["out"]).max() <= 1e-4
+
+    def fresh(lay):
+        mem = pk.Memory(D, H, n, k, "f32", max_batch=512)
+        P = direct_params(lay)
+        mem.prepare(P, "fold")
+        return mem.forward(P, x)[0]
+
+    say("layer folded: after a training-mode forward and an optimiser step")
+    layer.train()
+    (layer(x) * dout).sum().backward()  # moves the running statistics
+    layer.eval()
+    with torch.no_grad():
+        assert torch.equal(layer(x), fresh(layer))
+    torch.optim.SGD(layer.parameters(), lr=0.5).step()
+    with torch.no_grad():
+        assert torch.equal(layer(x), fresh(layer))
