@@ -157,12 +157,14 @@ __device__ __forceinline__ void split8(const fx4 (&v)[2], int ex, float one, u4 
 // (dwords) with the stride between stages.  Product-key B rows come already
 // split (split_rows_kernel): a B unit copies its lane's two 16-byte pieces
 // of each chunk, from the first subkey set's row (src) and from chunk kch
-// on from the second set's (src2), both pointing at pieces.  SPLIT_B: a
+// on from the second set's (src2), both pointing at pieces.  SPLIT >= 1: a
 // plain B operand split ahead of the call (weights split once, when they are
-// prepared), copied the same way from src alone.
-template <typename T, bool PRODUCT_B, bool SPLIT_B = false>
+// prepared), copied the same way from src alone; SPLIT == 2: the A operand
+// as well (rows split by the pass that takes their exponents).
+template <typename T, bool PRODUCT_B, int SPLIT = 0>
 struct Stager {
-    static constexpr bool PIECES_B = PRODUCT_B || SPLIT_B;
+    static constexpr bool PIECES_B = PRODUCT_B || SPLIT >= 1;
+    static constexpr bool PIECES_A = SPLIT == 2;
     // When the A rows and the B rows each fill whole rounds of the waves'
     // groups (both 256x256 and 128x128 tiles), unit u of every wave is an
     // A group for u < BM / 32 / WAVES and a B group after, and every unit
@@ -170,7 +172,7 @@ struct Stager {
     static constexpr bool STATIC_UNITS = (T::BM / 32) % T::WAVES == 0 && (T::BN / 32) % T::WAVES == 0;
     const float *src[T::UNITS];
     const float *src2[PRODUCT_B ? T::UNITS : 1];
-    bool is_b[PIECES_B && !STATIC_UNITS ? T::UNITS : 1];
+    bool is_b[(PIECES_A || PIECES_B) && !STATIC_UNITS ? T::UNITS : 1];
     int kch;
     int lds[T::UNITS], stage_stride[T::UNITS], ex[T::UNITS];
     bool valid[STATIC_UNITS ? 1 : T::UNITS];
@@ -186,14 +188,22 @@ struct Stager {
         if constexpr (STATIC_UNITS) return true;
         else return valid[u];
     }
+    // unit u copies pieces (its operand was split beforehand)
+    __device__ __forceinline__ bool copies(int u) const
+    {
+        if constexpr (PIECES_A && PIECES_B) return true;
+        else if constexpr (PIECES_B) return b_unit(u);
+        else if constexpr (PIECES_A) return !b_unit(u);
+        else return false;
+    }
 
     __device__ __forceinline__ void load(int kt)
     {
 #pragma unroll
         for (int u = 0; u < T::UNITS; ++u) {
             if (!in_range(u)) continue;
-            if constexpr (PIECES_B) {
-                if (b_unit(u)) {
+            if constexpr (PIECES_A || PIECES_B) {
+                if (copies(u)) {
                     const u4 *q;
                     if constexpr (PRODUCT_B)
                         q = kt < kch ? reinterpret_cast<const u4 *>(src[u]) + (int64_t)kt * 128
@@ -221,8 +231,8 @@ struct Stager {
 #pragma unroll
         for (int u = 0; u < T::UNITS; ++u) {
             if (!in_range(u)) continue;
-            if constexpr (PIECES_B) {
-                if (b_unit(u)) {  // pieces as loaded
+            if constexpr (PIECES_A || PIECES_B) {
+                if (copies(u)) {  // pieces as loaded
                     uint32_t *dst = smem + lds[u] + s * stage_stride[u];
 #pragma unroll
                     for (int p = 0; p < kPieces; ++p)
@@ -276,15 +286,17 @@ __device__ __forceinline__ void mfma_frags(floatx16 (&acc)[T::TM][T::TN], const 
 
 // One BM x BN tile (tm, tn) of batch entry g and K range z.  KEEP_PRE: the
 // BN epilogue also stores the values before BN (a.C_pre).
-// SPLIT_B: B's rows come split into fp16 pieces (a.b_presplit, scaled by
-// a.b_exp_given), and the tile copies them.
+// SPLIT >= 1: B's rows come split into fp16 pieces (a.b_presplit, scaled by
+// a.b_exp_given), and the tile copies them; SPLIT == 2: A's rows as well
+// (a.a_presplit, scaled by the exponents in the row-exponent workspace).
 template <typename T, bool BN_EPILOGUE, bool STREAM_OUT, bool PRODUCT_B, bool ACCUMULATE, bool KEEP_PRE = false,
-          bool SPLIT_B = false>
+          int SPLIT = 0>
 __device__ __forceinline__ void gemm_tile(const GemmArgs &a, int tm, int tn, int g, int z, uint32_t *smem)
 {
     static_assert(!KEEP_PRE || (BN_EPILOGUE && !STREAM_OUT), "values before BN: the staged BN epilogue");
     static_assert(!PRODUCT_B || (!STREAM_OUT && !BN_EPILOGUE && !ACCUMULATE), "product-key B: plain staged epilogue");
-    static_assert(!(PRODUCT_B && SPLIT_B), "one form of pre-split B");
+    static_assert(!(PRODUCT_B && SPLIT), "one form of pre-split B");
+    constexpr bool SPLIT_B = SPLIT >= 1;
     uint32_t *As = smem;
     uint32_t *Bs = smem + T::STAGES * T::BM * kRowDw;
     // split-K: this block's range of K (the operands are K-contiguous)
@@ -311,7 +323,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, int tm, int tn, int
 
     // Rows past the matrix edge re-read the last row; their results are
     // never stored.
-    Stager<T, PRODUCT_B, SPLIT_B> st;
+    Stager<T, PRODUCT_B, SPLIT> st;
     st.kch = a.split_k / kBK;
     // pre-split plain B: this batch entry's rows, from this K range's first
     // chunk (pieces of rows past N are zero)
@@ -319,6 +331,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, int tm, int tn, int
     const u4 *bsplit = SPLIT_B ? reinterpret_cast<const u4 *>(a.b_presplit) +
                                      ((int64_t)g * ((a.N + 31) / 32) * kt_all + kbeg / kBK) * 128
                                : nullptr;
+    const u4 *asplit = SPLIT == 2 ? reinterpret_cast<const u4 *>(a.a_presplit) +
+                                        ((int64_t)g * ((a.M + 31) / 32) * kt_all + kbeg / kBK) * 128
+                                  : nullptr;
     // product-key B: the split rows of this batch entry's two subkey sets
     const int kgroups = (a.key_n + 31) / 32;
     const u4 *set0 =
@@ -329,10 +344,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, int tm, int tn, int
         const int grp = wave + T::WAVES * u;
         if constexpr (!decltype(st)::STATIC_UNITS) st.valid[u] = grp < T::GROUPS;
         const int r = min(grp, T::GROUPS - 1) * 32 + il;  // row of the A tile, then of the B tile
-        if constexpr ((PRODUCT_B || SPLIT_B) && !decltype(st)::STATIC_UNITS) st.is_b[u] = r >= T::BM;
+        if constexpr ((PRODUCT_B || SPLIT) && !decltype(st)::STATIC_UNITS) st.is_b[u] = r >= T::BM;
         if (decltype(st)::STATIC_UNITS ? !st.b_unit(u) : r < T::BM) {
             const int m = min(m0 + r, a.M - 1);
-            st.src[u] = A + (int64_t)m * a.lda + kk * 8;
+            if constexpr (SPLIT == 2)  // lane (kk, m % 32) of row m's group
+                st.src[u] = reinterpret_cast<const float *>(asplit + (int64_t)(m / 32) * kt_all * 128 + kk * 32 + m % 32);
+            else
+                st.src[u] = A + (int64_t)m * a.lda + kk * 8;
             if constexpr (PRODUCT_B) st.src2[u] = nullptr;
             st.ex[u] = row_exp(m);
             st.lds[u] = r * kRowDw + kk * 4;
@@ -616,7 +634,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, int tm, int tn, int
 // entry major), a barrier between tiles; otherwise one tile per workgroup,
 // grid (tiles, batch, K ranges).
 template <typename T, bool BN_EPILOGUE, bool STREAM_OUT, bool PRODUCT_B = false, bool ACCUMULATE = false,
-          bool PERSIST = false, bool KEEP_PRE = false, bool SPLIT_B = false>
+          bool PERSIST = false, bool KEEP_PRE = false, int SPLIT = 0>
 __global__ __launch_bounds__(T::THREADS) void gemm_nt_f32_kernel(GemmArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
@@ -642,12 +660,12 @@ __global__ __launch_bounds__(T::THREADS) void gemm_nt_f32_kernel(GemmArgs a)
             const int j = (int)(e / tiles_n), tn = (int)(e - (int64_t)j * tiles_n);
             const int r = by_rows ? xcd + kXcds * j : j;  // (batch entry, row tile) pair
             const int g = r / tiles_m;
-            gemm_tile<T, BN_EPILOGUE, STREAM_OUT, PRODUCT_B, ACCUMULATE, KEEP_PRE, SPLIT_B>(a, r - g * tiles_m, tn, g,
-                                                                                            0, smem);
+            gemm_tile<T, BN_EPILOGUE, STREAM_OUT, PRODUCT_B, ACCUMULATE, KEEP_PRE, SPLIT>(a, r - g * tiles_m, tn, g, 0,
+                                                                                          smem);
             __syncthreads();
         }
     } else {
-        gemm_tile<T, BN_EPILOGUE, STREAM_OUT, PRODUCT_B, ACCUMULATE, KEEP_PRE, SPLIT_B>(
+        gemm_tile<T, BN_EPILOGUE, STREAM_OUT, PRODUCT_B, ACCUMULATE, KEEP_PRE, SPLIT>(
             a, blockIdx.x / tiles_n, blockIdx.x % tiles_n, blockIdx.y, blockIdx.z, smem);
     }
 }
@@ -941,11 +959,11 @@ int64_t tile_count(const GemmArgs &a)
 }
 
 template <typename T, bool BN_EPILOGUE, bool STREAM_OUT, bool PRODUCT_B = false, bool ACCUMULATE = false,
-          bool PERSIST = false, bool KEEP_PRE = false, bool SPLIT_B = false>
+          bool PERSIST = false, bool KEEP_PRE = false, int SPLIT = 0>
 hipError_t launch_variant(const GemmArgs &a, hipStream_t stream)
 {
     const auto kernel =
-        &gemm_nt_f32_kernel<T, BN_EPILOGUE, STREAM_OUT, PRODUCT_B, ACCUMULATE, PERSIST, KEEP_PRE, SPLIT_B>;
+        &gemm_nt_f32_kernel<T, BN_EPILOGUE, STREAM_OUT, PRODUCT_B, ACCUMULATE, PERSIST, KEEP_PRE, SPLIT>;
     if (T::LDS_BYTES > 65536) {
         // Dynamic LDS above 64 KiB must be allowed per kernel (gfx950 has
         // 160 KiB per CU); done once per kernel and device.
@@ -975,43 +993,53 @@ hipError_t launch_variant(const GemmArgs &a, hipStream_t stream)
     return hipGetLastError();
 }
 
-template <typename T, bool SPLIT_B>
+template <typename T, int SPLIT>
 hipError_t launch_tile_form(const GemmArgs &a, hipStream_t stream)
 {
     if (tile_count<T>(a) > 0x7FFFFFFF || a.batch > 65535) return hipErrorInvalidConfiguration;
     if (a.C_pre && (!a.bn_mean || a.stream_out || a.accumulate || a.k_chunk ||
                     (reinterpret_cast<uintptr_t>(a.C_pre) & 15) != 0 || (reinterpret_cast<uintptr_t>(a.C) & 15) != 0))
         return hipErrorInvalidValue;
-    if (a.accumulate) {
-        if (a.bn_mean || a.stream_out || SPLIT_B) return hipErrorInvalidValue;
-        if constexpr (!SPLIT_B) return launch_variant<T, false, false, false, true>(a, stream);
-    }
     // At least as many 256x256 tiles as CUs: one workgroup per CU walks its
     // tiles in the XCD-aware order, and the stores of one tile drain while
     // the next one computes
     const bool persist = T::PING_PONG && !a.k_chunk && tile_count<T>(a) * a.batch >= kCUs;
-    if (a.C_pre) {  // the BN epilogue keeping the values before BN (checked above)
-        if (persist) return launch_variant<T, true, false, false, false, true, true, SPLIT_B>(a, stream);
-        return launch_variant<T, true, false, false, false, false, true, SPLIT_B>(a, stream);
+    if constexpr (SPLIT == 2) {
+        // both operands split beforehand: the streamed epilogue only (the
+        // folded lookup's scores)
+        if (!a.stream_out || a.bn_mean || a.accumulate || a.C_pre) return hipErrorInvalidValue;
+        if (persist) return launch_variant<T, false, true, false, false, true, false, 2>(a, stream);
+        return launch_variant<T, false, true, false, false, false, false, 2>(a, stream);
+    } else {
+        if (a.accumulate) {
+            if (a.bn_mean || a.stream_out || SPLIT) return hipErrorInvalidValue;
+            if constexpr (!SPLIT) return launch_variant<T, false, false, false, true>(a, stream);
+        }
+        if (a.C_pre) {  // the BN epilogue keeping the values before BN (checked above)
+            if (persist) return launch_variant<T, true, false, false, false, true, true, SPLIT>(a, stream);
+            return launch_variant<T, true, false, false, false, false, true, SPLIT>(a, stream);
+        }
+        if (a.bn_mean) {
+            if (a.stream_out) return launch_variant<T, true, true, false, false, false, false, SPLIT>(a, stream);
+            if (persist) return launch_variant<T, true, false, false, false, true, false, SPLIT>(a, stream);
+            return launch_variant<T, true, false, false, false, false, false, SPLIT>(a, stream);
+        }
+        if (a.stream_out) {
+            if (persist) return launch_variant<T, false, true, false, false, true, false, SPLIT>(a, stream);
+            return launch_variant<T, false, true, false, false, false, false, SPLIT>(a, stream);
+        }
+        return launch_variant<T, false, false, false, false, false, false, SPLIT>(a, stream);
     }
-    if (a.bn_mean) {
-        if (a.stream_out) return launch_variant<T, true, true, false, false, false, false, SPLIT_B>(a, stream);
-        if (persist) return launch_variant<T, true, false, false, false, true, false, SPLIT_B>(a, stream);
-        return launch_variant<T, true, false, false, false, false, false, SPLIT_B>(a, stream);
-    }
-    if (a.stream_out) {
-        if (persist) return launch_variant<T, false, true, false, false, true, false, SPLIT_B>(a, stream);
-        return launch_variant<T, false, true, false, false, false, false, SPLIT_B>(a, stream);
-    }
-    return launch_variant<T, false, false, false, false, false, false, SPLIT_B>(a, stream);
 }
 
-// B split ahead of the call (b_presplit) or in every tile
+// Operands split ahead of the call (a_presplit with b_presplit, or
+// b_presplit alone) or in every tile
 template <typename T>
 hipError_t launch_tile(const GemmArgs &a, hipStream_t stream)
 {
-    if (a.b_presplit) return launch_tile_form<T, true>(a, stream);
-    return launch_tile_form<T, false>(a, stream);
+    if (a.a_presplit) return launch_tile_form<T, 2>(a, stream);
+    if (a.b_presplit) return launch_tile_form<T, 1>(a, stream);
+    return launch_tile_form<T, 0>(a, stream);
 }
 
 // C[g][m][n] (+)= sum over s of P[s][g][m][n], s in order: the split-K
@@ -1065,6 +1093,79 @@ hipError_t launch_presplit(const float *B, int64_t stride, int64_t ld, int rows,
     return hipGetLastError();
 }
 
+// A plain A operand's rows, exponents and fp16 pieces in one pass (the
+// folded lookup's x): one workgroup of eight waves per group of 32 rows.
+// First each wave takes four rows' largest magnitudes (every load of a
+// 1024-wide block in flight before the maxima) and their exponents (to
+// exp_out and LDS); then the group's pieces are written as
+// split_rows_kernel writes them, lane l of a wave splitting row l % 32's
+// k = 16 c + 8 (l / 32) .. + 7 of chunk c, the chunks dealt to the waves in
+// turn.  Rows past M get exponent 0 and zero pieces.
+__global__ __launch_bounds__(512) void exp_split_rows_kernel(const float *A, int64_t lda, int M, int K,
+                                                             int32_t *exp_out, u4 *out)
+{
+    __shared__ int ex_lds[32];
+    const int grp = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int r0 = grp * 32 + wave * 4;
+    float mx[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int base = 0; base < K; base += 1024) {
+        fx4 v[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int c = base + 256 * q + 4 * lane;
+                v[i][q] = r0 + i < M && c < K ? *reinterpret_cast<const fx4 *>(A + (int64_t)(r0 + i) * lda + c)
+                                              : fx4{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                mx[i] = fmaxf(fmaxf(mx[i], fmaxf(fabsf(v[i][q][0]), fabsf(v[i][q][1]))),
+                              fmaxf(fabsf(v[i][q][2]), fabsf(v[i][q][3])));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float m = wave_max(mx[i]);
+        if (lane == i) {
+            const int e = r0 + i < M ? row_exponent(m) : 0;
+            ex_lds[wave * 4 + i] = e;
+            if (r0 + i < M) exp_out[r0 + i] = e;
+        }
+    }
+    __syncthreads();
+    const int kch = K / kBK, rr = lane & 31, row = grp * 32 + rr;
+    const int ex = ex_lds[rr];
+    float one = 1.0f;
+    asm volatile("" : "+v"(one));
+    for (int c = wave; c < kch; c += 8) {
+        fx4 v[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+        if (row < M) {
+            const float *src = A + (int64_t)row * lda + c * kBK + (lane >> 5) * 8;
+            v[0] = *reinterpret_cast<const fx4 *>(src);
+            v[1] = *reinterpret_cast<const fx4 *>(src + 4);
+        }
+        u4 hi, lo;
+        split8(v, ex, one, hi, lo);
+        u4 *dst = out + ((int64_t)grp * kch + c) * 128 + lane;
+        dst[0] = hi;
+        dst[64] = lo;
+    }
+}
+
+hipError_t launch_exp_split(const float *A, int64_t lda, int M, int K, int32_t *exp_out, void *out,
+                            hipStream_t stream)
+{
+    if (M <= 0) return hipSuccess;
+    if (K % 32 != 0 || lda % 4 != 0 || (reinterpret_cast<uintptr_t>(A) & 15) != 0 ||
+        (reinterpret_cast<uintptr_t>(out) & 15) != 0)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(exp_split_rows_kernel, dim3((unsigned)((M + 31) / 32)), dim3(512), 0, stream, A, lda, M, K,
+                       exp_out, reinterpret_cast<u4 *>(out));
+    return hipGetLastError();
+}
+
 hipError_t launch_fold(const float *wq, const float *mean, const float *var, const float *gamma, const float *beta,
                        float eps, const float *subkeys, int D, int H, int n, float *M, float *bias, hipStream_t stream)
 {
@@ -1079,6 +1180,9 @@ hipError_t launch_gemm_nt_f32(const GemmArgs &args, hipStream_t stream)
     if (args.M <= 0 || args.N <= 0 || args.batch <= 0) return hipSuccess;
     if (args.K % 32 != 0 || args.k_chunk != 0 || args.B2) return hipErrorInvalidValue;
     if (args.b_presplit && (!args.b_exp_given || args.accumulate || (reinterpret_cast<uintptr_t>(args.b_presplit) & 15)))
+        return hipErrorInvalidValue;
+    if (args.a_presplit && (!args.b_presplit || args.a_rowmax || args.batch != 1 || !args.stream_out ||
+                            (reinterpret_cast<uintptr_t>(args.a_presplit) & 15)))
         return hipErrorInvalidValue;
     GemmArgs a = args;
     hipError_t e = prepare_exponents(a, false, stream);

@@ -42,6 +42,7 @@ struct pkm_ctx {
     int32_t *fold_exp;  // [2H * n]
     float *fold_bias;   // [2H * n]
     void *fold_pieces;
+    void *x_pieces;  // a chunk of x as fp16 pieces, for the folded contraction
     const float *prep_bn_src[4];  // mean, var, gamma, beta
 };
 
@@ -95,7 +96,7 @@ int64_t forward_exp_ints(const pkm_config &c)
 // GEMM row exponents, q^'s per-half maxima and the subkeys' row exponents;
 // then (only with prepared) the prepared weights: Wq's and the subkeys' row
 // exponents and fp16 pieces.  False on size overflow.
-constexpr int kPieces = 15;
+constexpr int kPieces = 16;
 bool workspace_layout(const pkm_config &c, size_t sizes[kPieces], bool batch_stats = true, bool prepared = true)
 {
     const double mb = (double)c.max_batch;
@@ -120,6 +121,7 @@ bool workspace_layout(const pkm_config &c, size_t sizes[kPieces], bool batch_sta
     sizes[12] = fold ? round_up(2 * H * (size_t)c.n_keys * sizeof(int32_t)) : 0;
     sizes[13] = fold ? round_up(2 * H * (size_t)c.n_keys * sizeof(float)) : 0;
     sizes[14] = fold ? round_up((size_t)pkm::gemm_presplit_bytes(2 * c.heads * c.n_keys, c.dim, 1)) : 0;
+    sizes[15] = fold ? round_up((size_t)pkm::gemm_presplit_bytes((int)c.max_batch, c.dim, 1)) : 0;
     return true;
 }
 
@@ -149,6 +151,7 @@ void assign_workspace(pkm_ctx *ctx, char *w, const size_t sizes[kPieces])
     ctx->fold_exp = sizes[12] ? reinterpret_cast<int32_t *>(piece[12]) : nullptr;
     ctx->fold_bias = sizes[13] ? reinterpret_cast<float *>(piece[13]) : nullptr;
     ctx->fold_pieces = sizes[14] ? piece[14] : nullptr;
+    ctx->x_pieces = sizes[15] ? piece[15] : nullptr;
     for (auto &b : ctx->prep_bn_src) b = nullptr;
 }
 
@@ -476,10 +479,13 @@ pkm_status forward_stage(const pkm_ctx *ctx, const pkm_params *p, int64_t nb, co
     const int64_t H = c.heads, k = c.k;
     float *scores = scores_out ? scores_out : ctx->scores;
     // Folded (and no projection wanted): the half scores in one contraction
-    // of x with the folded matrix, stage 0 x's row exponents, stage 1 the
-    // contraction, stage 2 nothing.
+    // of x with the folded matrix, stage 0 x's row exponents and fp16
+    // pieces, stage 1 the contraction, stage 2 nothing.
     if (!q_pre && folded_for(ctx, p) && stage <= 2) {
         if (stage == 2) return PKM_OK;
+        if (stage == 0)
+            return launched(pkm::launch_exp_split(x, c.dim, (int)nb, c.dim, ctx->gemm_exp, ctx->x_pieces, st),
+                            "row exponents and split");
         pkm::GemmArgs a{};
         a.exp_ws = ctx->gemm_exp;
         a.exp_ws_ints = ctx->gemm_exp_ints;
@@ -491,13 +497,14 @@ pkm_status forward_stage(const pkm_ctx *ctx, const pkm_params *p, int64_t nb, co
         a.batch = 1;
         a.b_exp_given = ctx->fold_exp;
         a.b_presplit = ctx->fold_pieces;
+        a.a_presplit = ctx->x_pieces;
         a.ldb = c.dim;
         a.C = scores;  // [nb][2H][n]
         a.ldc = 2 * (int64_t)c.heads * c.n_keys;
         a.stream_out = true;  // read once, by the select
         a.col_bias = ctx->fold_bias;
-        a.exp_phase = stage == 0 ? 1 : 2;
-        return launched(pkm::launch_gemm_nt_f32(a, st), stage == 0 ? "row exponents" : "folded scoring");
+        a.exp_phase = 2;  // x's exponents written by stage 0
+        return launched(pkm::launch_gemm_nt_f32(a, st), "folded scoring");
     }
     // Wq and the subkeys from their prepared form when p names the arrays
     // pkm_prepare took them from (the same pieces and exponents the tiles

@@ -76,6 +76,10 @@ struct GemmArgs {
     // launch_presplit (16-byte aligned), so the tiles copy them instead of
     // splitting B.  Bitwise the same results as splitting in the tiles.
     const void *b_presplit;
+    // Optional, with b_presplit, stream_out and batch 1: A's rows split the
+    // same way by launch_exp_split, which also wrote their exponents to the
+    // start of exp_ws (run the contraction with exp_phase 2).
+    const void *a_presplit;
     // Optional, with stream_out: a per-column term added to every result,
     // col_bias[g * N + n] for batch entry g (the folded lookup's batch-norm
     // shift).
@@ -125,6 +129,11 @@ hipError_t launch_gemm_nt_f32(const GemmArgs &a, hipStream_t stream);
 int64_t gemm_presplit_bytes(int rows, int K, int batch);
 hipError_t launch_presplit(const float *B, int64_t stride, int64_t ld, int rows, int K, int batch, int32_t *exp,
                            void *out, hipStream_t stream);
+// A plain A operand [M][K] (row stride lda): its row exponents (exp_out [M])
+// and fp16 pieces (out, gemm_presplit_bytes(M, K, 1) bytes, 16-byte
+// aligned) in one pass, for GemmArgs::a_presplit.  K % 32 == 0.
+hipError_t launch_exp_split(const float *A, int64_t lda, int M, int K, int32_t *exp_out, void *out,
+                            hipStream_t stream);
 // The projection, inference batch-norm and subkeys folded, for the lookup
 // with fixed statistics: M [2H][n][D] and bias [2H][n] fp32 (fp64
 // accumulation, one rounding) with, for g = 2h + p, the half scores

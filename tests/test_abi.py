@@ -92,6 +92,7 @@ def test_workspace_bytes():
     # the folded form (n_keys <= D): row exponents, shifts and fp16 pieces of
     # the [2H n, D] folded matrix
     prepared += 2 * H * n * 4 * 2 + 2 * H * n * D * 4
+    prepared += mb * D * 4  # a chunk of x as fp16 pieces (folded lookup)
     assert (pk.workspace_bytes(cfg) ==
             4 * mb * H * (D + 2 * n + 2 * k) + stat_part + exps + qmax + sub_exp + prepared)
     with pytest.raises(pk.PkmError):
