@@ -952,6 +952,79 @@ __global__ __launch_bounds__(256) void fold_kernel(const float *wq, const float 
     }
 }
 
+// A plain A operand's rows, exponents and fp16 pieces in one pass (the
+// folded lookup's x): one workgroup of eight waves per group of 32 rows.
+// First each wave takes four rows' largest magnitudes (every load of a
+// 1024-wide block in flight before the maxima) and their exponents (to
+// exp_out and LDS); then the group's pieces are written as
+// split_rows_kernel writes them, lane l of a wave splitting row l % 32's
+// k = 16 c + 8 (l / 32) .. + 7 of chunk c, the chunks dealt to the waves in
+// turn.  Rows past M get exponent 0 and zero pieces.
+__global__ __launch_bounds__(512) void exp_split_rows_kernel(const float *A, int64_t lda, int M, int K,
+                                                             int32_t *exp_out, u4 *out)
+{
+    __shared__ int ex_lds[32];
+    const int grp = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int r0 = grp * 32 + wave * 4;
+    float mx[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int base = 0; base < K; base += 1024) {
+        fx4 v[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int c = base + 256 * q + 4 * lane;
+                v[i][q] = r0 + i < M && c < K ? *reinterpret_cast<const fx4 *>(A + (int64_t)(r0 + i) * lda + c)
+                                              : fx4{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                mx[i] = fmaxf(fmaxf(mx[i], fmaxf(fabsf(v[i][q][0]), fabsf(v[i][q][1]))),
+                              fmaxf(fabsf(v[i][q][2]), fabsf(v[i][q][3])));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float m = wave_max(mx[i]);
+        if (lane == i) {
+            const int e = r0 + i < M ? row_exponent(m) : 0;
+            ex_lds[wave * 4 + i] = e;
+            if (r0 + i < M) exp_out[r0 + i] = e;
+        }
+    }
+    __syncthreads();
+    const int kch = K / kBK, rr = lane & 31, row = grp * 32 + rr;
+    const int ex = ex_lds[rr];
+    float one = 1.0f;
+    asm volatile("" : "+v"(one));
+    // eight of the wave's chunks at a time, every load in flight before the
+    // first split
+    for (int c0 = wave; c0 < kch; c0 += 64) {
+        fx4 v[8][2];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int c = c0 + 8 * i;
+            v[i][0] = v[i][1] = fx4{0.0f, 0.0f, 0.0f, 0.0f};
+            if (row < M && c < kch) {
+                const float *src = A + (int64_t)row * lda + c * kBK + (lane >> 5) * 8;
+                v[i][0] = *reinterpret_cast<const fx4 *>(src);
+                v[i][1] = *reinterpret_cast<const fx4 *>(src + 4);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int c = c0 + 8 * i;
+            if (c >= kch) break;
+            u4 hi, lo;
+            split8(v[i], ex, one, hi, lo);
+            u4 *dst = out + ((int64_t)grp * kch + c) * 128 + lane;
+            dst[0] = hi;
+            dst[64] = lo;
+        }
+    }
+}
+
 template <typename T>
 int64_t tile_count(const GemmArgs &a)
 {
@@ -1091,67 +1164,6 @@ hipError_t launch_presplit(const float *B, int64_t stride, int64_t ld, int rows,
     hipLaunchKernelGGL(split_rows_kernel, dim3((unsigned)((per_set + 255) / 256), batch), dim3(256), 0, stream, B,
                        nullptr, stride, ld, rows, kch, exp, nullptr, reinterpret_cast<u4 *>(out));
     return hipGetLastError();
-}
-
-// A plain A operand's rows, exponents and fp16 pieces in one pass (the
-// folded lookup's x): one workgroup of eight waves per group of 32 rows.
-// First each wave takes four rows' largest magnitudes (every load of a
-// 1024-wide block in flight before the maxima) and their exponents (to
-// exp_out and LDS); then the group's pieces are written as
-// split_rows_kernel writes them, lane l of a wave splitting row l % 32's
-// k = 16 c + 8 (l / 32) .. + 7 of chunk c, the chunks dealt to the waves in
-// turn.  Rows past M get exponent 0 and zero pieces.
-__global__ __launch_bounds__(512) void exp_split_rows_kernel(const float *A, int64_t lda, int M, int K,
-                                                             int32_t *exp_out, u4 *out)
-{
-    __shared__ int ex_lds[32];
-    const int grp = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int r0 = grp * 32 + wave * 4;
-    float mx[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int base = 0; base < K; base += 1024) {
-        fx4 v[4][4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int c = base + 256 * q + 4 * lane;
-                v[i][q] = r0 + i < M && c < K ? *reinterpret_cast<const fx4 *>(A + (int64_t)(r0 + i) * lda + c)
-                                              : fx4{0.0f, 0.0f, 0.0f, 0.0f};
-            }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                mx[i] = fmaxf(fmaxf(mx[i], fmaxf(fabsf(v[i][q][0]), fabsf(v[i][q][1]))),
-                              fmaxf(fabsf(v[i][q][2]), fabsf(v[i][q][3])));
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float m = wave_max(mx[i]);
-        if (lane == i) {
-            const int e = r0 + i < M ? row_exponent(m) : 0;
-            ex_lds[wave * 4 + i] = e;
-            if (r0 + i < M) exp_out[r0 + i] = e;
-        }
-    }
-    __syncthreads();
-    const int kch = K / kBK, rr = lane & 31, row = grp * 32 + rr;
-    const int ex = ex_lds[rr];
-    float one = 1.0f;
-    asm volatile("" : "+v"(one));
-    for (int c = wave; c < kch; c += 8) {
-        fx4 v[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
-        if (row < M) {
-            const float *src = A + (int64_t)row * lda + c * kBK + (lane >> 5) * 8;
-            v[0] = *reinterpret_cast<const fx4 *>(src);
-            v[1] = *reinterpret_cast<const fx4 *>(src + 4);
-        }
-        u4 hi, lo;
-        split8(v, ex, one, hi, lo);
-        u4 *dst = out + ((int64_t)grp * kch + c) * 128 + lane;
-        dst[0] = hi;
-        dst[64] = lo;
-    }
 }
 
 hipError_t launch_exp_split(const float *A, int64_t lda, int M, int K, int32_t *exp_out, void *out,
