@@ -644,16 +644,21 @@ __global__ __launch_bounds__(T::THREADS) void gemm_nt_f32_kernel(GemmArgs a)
         // kXcds, each XCD with its own L2).  Each XCD takes whole rows of
         // tiles -- (batch entry, row tile) pairs r with r % kXcds its own --
         // so a block of A rows is fetched into one L2 for all its column
-        // tiles instead of into every XCD's.  Where that would leave XCDs
-        // short of rows (fewer rounds of tiles in plain order), the tiles go
-        // round-robin instead.  Every tile is computed once, the same way,
-        // whichever workgroup takes it.
+        // tiles instead of into every XCD's: each XCD streams all of B and
+        // an eighth of A.  That is the better split while B has no more rows
+        // than A (per batch entry); with a wider B (the folded lookup's
+        // 2H n keys against a few thousand tokens) and where whole rows
+        // would leave XCDs short of work, the tiles go round-robin instead,
+        // which deals the column tiles to the XCDs in turn (with a multiple
+        // of 8 column tiles each XCD keeps its eighth of B in its L2 and
+        // streams A).  Every tile is computed once, the same way, whichever
+        // workgroup takes it.
         const int tiles_m = (a.M + T::BM - 1) / T::BM;
         const int rows = tiles_m * a.batch;
         const int64_t total = (int64_t)rows * tiles_n;
         const int xcd = blockIdx.x % kXcds, per_xcd = gridDim.x / kXcds;
         const int64_t rows_rounds = ((int64_t)((rows + kXcds - 1) / kXcds) * tiles_n + per_xcd - 1) / per_xcd;
-        const bool by_rows = rows_rounds <= (total + gridDim.x - 1) / gridDim.x;
+        const bool by_rows = a.N <= a.M && rows_rounds <= (total + gridDim.x - 1) / gridDim.x;
         const int64_t count = by_rows ? (int64_t)((rows - xcd + kXcds - 1) / kXcds) * tiles_n : total;
         const int64_t step = by_rows ? per_xcd : gridDim.x;
         for (int64_t e = by_rows ? blockIdx.x / kXcds : blockIdx.x; e < count; e += step) {
