@@ -177,6 +177,8 @@ struct Stager {
     int lds[T::UNITS], stage_stride[T::UNITS], ex[T::UNITS];
     bool valid[STATIC_UNITS ? 1 : T::UNITS];
     fx4 v[T::UNITS][2];
+    // a second chunk in flight, where the contraction fetches two ahead
+    fx4 v2[SPLIT == 2 && T::PING_PONG ? T::UNITS : 1][2];
 
     __device__ __forceinline__ bool b_unit(int u) const
     {
@@ -197,7 +199,11 @@ struct Stager {
         else return false;
     }
 
-    __device__ __forceinline__ void load(int kt)
+    __device__ __forceinline__ void load(int kt) { load_into(v, kt); }
+    __device__ __forceinline__ void store(uint32_t *smem, int s) const { store_from(v, smem, s); }
+
+    template <typename Buf>
+    __device__ __forceinline__ void load_into(Buf &v, int kt)
     {
 #pragma unroll
         for (int u = 0; u < T::UNITS; ++u) {
@@ -224,7 +230,8 @@ struct Stager {
     // Scale the 8 values by the row's power of two and split them into
     // their two fp16 pieces; each piece's 16 bytes go to that piece's part of
     // the LDS row.
-    __device__ __forceinline__ void store(uint32_t *smem, int s) const
+    template <typename Buf>
+    __device__ __forceinline__ void store_from(const Buf &v, uint32_t *smem, int s) const
     {
         float one = 1.0f;
         asm volatile("" : "+v"(one));
@@ -387,10 +394,23 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, int tm, int tn, int
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
+    // Both operands split beforehand (pure copies): two chunks ride in
+    // registers ahead of the one being staged, so a fetch has two chunks'
+    // time to arrive (the register budget allows the second buffer here).
+    constexpr bool DEEP = SPLIT == 2 && T::PING_PONG;
     const int KT = klen / kBK;
     st.load(0);
     st.store(smem, 0);
-    if (KT > 1) st.load(1);
+    if constexpr (DEEP) {
+        // unconditional fetches (past the end: the last chunk again), in a
+        // fixed order, so the count of loads behind each buffer's is the
+        // same on every path and a stage waits only for its own chunk
+        st.load(min(1, KT - 1));
+        asm volatile("" ::: "memory");
+        st.load_into(st.v2, min(2, KT - 1));
+    } else if (KT > 1) {
+        st.load(1);
+    }
     __syncthreads();
     const bool late = T::PING_PONG && wave >= T::WAVES / 2;
     if (late) __builtin_amdgcn_s_barrier();
@@ -417,7 +437,30 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, int tm, int tn, int
             }
         }
     };
-    if constexpr (PRODUCT_B) {
+    if constexpr (DEEP) {
+        // chunk kt + 1 is staged from v (kt even) or v2 (kt odd), which then
+        // fetches chunk kt + 3
+        // (the last step's store goes to a stage no one reads again, and
+        // fetches past the end re-read the last chunk)
+        const auto step = [&](int kt, auto &buf) {
+            const int s = kt & 1;
+            hx8 af[T::TM][kPieces], bf[T::TN][kPieces];
+            read_frags<T>(af, bf, As + s * T::BM * kRowDw, Bs + s * T::BN * kRowDw, wm, wn, il, kk);
+            st.store_from(buf, smem, s ^ 1);
+            st.load_into(buf, min(kt + 3, KT - 1));
+            __syncthreads();
+            __builtin_amdgcn_s_setprio(1);
+            mfma_frags<T>(acc, af, bf);
+            __builtin_amdgcn_s_setprio(0);
+            __syncthreads();
+        };
+        // K is a multiple of 32, so the chunks come in pairs (and the loop
+        // body is straight-line code)
+        for (int kt = 0; kt < KT; kt += 2) {
+            step(kt, st.v);
+            step(kt + 1, st.v2);
+        }
+    } else if constexpr (PRODUCT_B) {
         // Product-key B: the two halves of K carry their own key-row
         // exponents e0 (first subkey) and e1 (second).  After the first
         // half the sums of column n are moved from scale 2^e0 to 2^e1
