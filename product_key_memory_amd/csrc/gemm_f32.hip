@@ -1001,19 +1001,23 @@ __global__ __launch_bounds__(256) void fold_kernel(const float *wq, const float 
 }
 
 // A plain A operand's rows, exponents and fp16 pieces in one pass (the
-// folded lookup's x): one workgroup of eight waves per group of 32 rows.
+// folded lookup's x): one workgroup of four waves per half group (16 rows).
 // First each wave takes four rows' largest magnitudes (every load of a
 // 1024-wide block in flight before the maxima) and their exponents (to
-// exp_out and LDS); then the group's pieces are written as
-// split_rows_kernel writes them, lane l of a wave splitting row l % 32's
-// k = 16 c + 8 (l / 32) .. + 7 of chunk c, the chunks dealt to the waves in
-// turn.  Rows past M get exponent 0 and zero pieces.
-__global__ __launch_bounds__(512) void exp_split_rows_kernel(const float *A, int64_t lda, int M, int K,
+// exp_out and LDS); then it writes the half group's share of the pieces as
+// split_rows_kernel lays them out -- two chunks per wave at a time, lane l
+// splitting row l % 16 of the half, k = 16 c + 8 ((l / 16) % 2) .. + 7 of
+// chunk c = c0 + l / 32, into the lane slot that row and k half have in the
+// 32-row group (16-lane runs of 256 bytes).  Rows past M get exponent 0 and
+// zero pieces.
+__global__ __launch_bounds__(256) void exp_split_rows_kernel(const float *A, int64_t lda, int M, int K,
                                                              int32_t *exp_out, u4 *out)
 {
-    __shared__ int ex_lds[32];
-    const int grp = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int r0 = grp * 32 + wave * 4;
+    __shared__ int ex_lds[16];
+    const int grp = blockIdx.x >> 1, half = blockIdx.x & 1;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int row0 = grp * 32 + half * 16;
+    const int r0 = row0 + wave * 4;
     float mx[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int base = 0; base < K; base += 1024) {
         fx4 v[4][4];
@@ -1042,33 +1046,34 @@ __global__ __launch_bounds__(512) void exp_split_rows_kernel(const float *A, int
         }
     }
     __syncthreads();
-    const int kch = K / kBK, rr = lane & 31, row = grp * 32 + rr;
+    const int kch = K / kBK, rr = lane & 15, kh = (lane >> 4) & 1, ci = lane >> 5;
+    const int row = row0 + rr, slot = kh * 32 + half * 16 + rr;
     const int ex = ex_lds[rr];
     float one = 1.0f;
     asm volatile("" : "+v"(one));
-    // eight of the wave's chunks at a time, every load in flight before the
-    // first split
-    for (int c0 = wave; c0 < kch; c0 += 64) {
-        fx4 v[8][2];
+    // the waves take pairs of chunks in turn, four pairs' loads in flight
+    for (int p0 = wave; 2 * p0 < kch; p0 += 16) {
+        fx4 v[4][2];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int c = c0 + 8 * i;
+        for (int i = 0; i < 4; ++i) {
+            const int c = 2 * (p0 + 4 * i) + ci;
             v[i][0] = v[i][1] = fx4{0.0f, 0.0f, 0.0f, 0.0f};
             if (row < M && c < kch) {
-                const float *src = A + (int64_t)row * lda + c * kBK + (lane >> 5) * 8;
+                const float *src = A + (int64_t)row * lda + c * kBK + kh * 8;
                 v[i][0] = *reinterpret_cast<const fx4 *>(src);
                 v[i][1] = *reinterpret_cast<const fx4 *>(src + 4);
             }
         }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int c = c0 + 8 * i;
-            if (c >= kch) break;
-            u4 hi, lo;
-            split8(v[i], ex, one, hi, lo);
-            u4 *dst = out + ((int64_t)grp * kch + c) * 128 + lane;
-            dst[0] = hi;
-            dst[64] = lo;
+        for (int i = 0; i < 4; ++i) {
+            const int c = 2 * (p0 + 4 * i) + ci;
+            if (c < kch) {
+                u4 hi, lo;
+                split8(v[i], ex, one, hi, lo);
+                u4 *dst = out + ((int64_t)grp * kch + c) * 128 + slot;
+                dst[0] = hi;
+                dst[64] = lo;
+            }
         }
     }
 }
@@ -1221,7 +1226,7 @@ hipError_t launch_exp_split(const float *A, int64_t lda, int M, int K, int32_t *
     if (K % 32 != 0 || lda % 4 != 0 || (reinterpret_cast<uintptr_t>(A) & 15) != 0 ||
         (reinterpret_cast<uintptr_t>(out) & 15) != 0)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL(exp_split_rows_kernel, dim3((unsigned)((M + 31) / 32)), dim3(512), 0, stream, A, lda, M, K,
+    hipLaunchKernelGGL(exp_split_rows_kernel, dim3((unsigned)((M + 31) / 32 * 2)), dim3(256), 0, stream, A, lda, M, K,
                        exp_out, reinterpret_cast<u4 *>(out));
     return hipGetLastError();
 }
