@@ -75,3 +75,51 @@ def test_forward_and_backward_graph_replays(torch, table, n, D):
             assert torch.equal(t, grads_e[name]), (rep, name)
         mem.forward(P, x)  # other eager work between replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("form", ["split", "fold"])
+def test_prepare_and_prepared_forward_graph_replays(torch, form):
+    """pkm_prepare only launches kernels too: a graph holding the prepare
+    and two prepared forwards (three chunks each) replays to the eager
+    prepared results, with eager unprepared lookups between replays."""
+    dev = support.device()
+    wl = synthetic.Workload("graph", 300, 512, 2, 256, 16, "bf16", "random")
+    params = synthetic.make_params(wl, 5)
+    P = pk.params_to_device(params, wl.table, dev)
+    mem = pk.Memory(wl.D, wl.H, wl.n, wl.k, wl.table, max_batch=128)
+    x = torch.from_numpy(np.ascontiguousarray(synthetic.make_x(wl, 5))).to(dev)
+    say("graph prepared", form, "eager reference")
+    mem.prepare(P, form)
+    ref = mem.forward(P, x)
+    mem.prepare(None)
+    torch.cuda.synchronize()
+    outs = [tuple(torch.empty_like(t) for t in ref) for _ in range(2)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        mem.prepare(P, form)
+        for o in outs:
+            mem.forward(P, x, *o)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    say("graph prepared", form, "capture")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        mem.prepare(P, form)
+        for o in outs:
+            mem.forward(P, x, *o)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        say("graph prepared", form, "replay", rep)
+        for o in outs:
+            for t in o:
+                t.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o in outs:
+            assert all(torch.equal(a, b) for a, b in zip(o, ref)), rep
+        mem.prepare(None)
+        mem.forward(P, x)  # eager unprepared work between replays
+        torch.cuda.synchronize()
+        mem.prepare(P, form)  # the host-side record the captured forwards rely on
