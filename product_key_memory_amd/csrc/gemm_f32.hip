@@ -54,6 +54,15 @@
 // reaches HBM during this compute-bound kernel rather than being written
 // back from the caches while the memory-bound gather runs.
 //
+// Operands split ahead of the call.  Weights that stay fixed between calls
+// can be split once (launch_presplit: row exponents, then the pieces in the
+// order a staging lane copies them), and so can the tokens (launch_exp_split:
+// exponents and pieces in one pass); a tile then copies pieces instead of
+// splitting, with the same bits.  With both operands split (the folded
+// lookup: x against the folded projection, batch-norm and subkeys, summed
+// in fp64 by fold_kernel) the staging is a pure copy and two chunks ride in
+// registers ahead of the one being staged.
+//
 // Flat exact search (the comparator for the product search of
 // §Factorising the key space: every one of the n^2 concatenated keys
 // scored by one full-length dot product).  The B operand is the virtual
