@@ -188,3 +188,20 @@ def test_folded_stages_and_which_path(torch):
     got = mem2.forward(P3, x2)
     torch.cuda.synchronize()
     assert _same(got, ref)
+
+
+@pytest.mark.slow
+def test_folded_forward_large_batch(torch):
+    """The large-batch configuration (65,536 tokens in one call) through the
+    folded forward, every 4th token against the oracle (the unfolded
+    forward is checked on every token elsewhere)."""
+    wl, params, x, tau, _, _, _ = _full_size("large_batch")
+    mem = pk.Memory(wl.D, wl.H, wl.n, wl.k, wl.table, max_batch=wl.B)
+    P = pk.params_to_device(params, wl.table, support.device())
+    mem.prepare(P, "fold")
+    say("folded forward, large batch")
+    out, idx, w = support.gpu_forward(wl, params, x, mem=mem, dev_params=P)
+    invariants(wl, idx, w)
+    tokens = np.arange(0, wl.B, 4)
+    err = compare(wl, params, x, out, idx, w, tokens=tokens, tau=tau[tokens])
+    print(f"folded large_batch: max row error {err.max():.3g}", flush=True)
