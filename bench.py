@@ -570,7 +570,8 @@ def main():
         "timing": dict(step_stats, statistic="median of per-step event pairs"),
         "data": "synthetic",
         "config": {"workload": wl.name, "tokens_per_step": B, "dim": wl.D, "heads": wl.H, "n_keys": wl.n,
-                   "rows": wl.N, "k": wl.k, "value_table": wl.table, "seed": 0, "max_batch": max_batch},
+                   "rows": wl.N, "k": wl.k, "value_table": wl.table, "seed": 0, "max_batch": max_batch,
+                   "weights_prepared": form},
         "roofline": roof(dominant),
         "gather_roofline": roof("gather"),
         "hbm_measured": dict(hbm, gather_frac_of_sequential=round(rl["gather"][1] / hbm["gather_sequential_rows_gbs"],
