@@ -525,18 +525,30 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, int tm, int tn, int
         // from the accumulators, non-temporally.  32x32 accumulator layout:
         // register v of lane l holds row 8*(v/4) + 4*(l/32) + v%4, column
         // l%32 of its block.
+        // The columns' parameters are all loaded first and made ready once:
+        // vmcnt counts stores as well as loads, so a wait for a load issued
+        // after some stores (or one the compiler cannot place exactly, behind
+        // the per-row branches) would also wait for those stores to land.
+        int ecol[T::TN];
+        float mean[T::TN], mul[T::TN], beta[T::TN], bias[T::TN];
+#pragma unroll
+        for (int j = 0; j < T::TN; ++j) {
+            const int col = min(n0 + wn * T::TN * 32 + j * 32 + il, a.N - 1);
+            ecol[j] = ex_lds[T::BM + col - n0];
+            mean[j] = 0.0f, mul[j] = 1.0f, beta[j] = 0.0f;
+            if (BN_EPILOGUE) {
+                mean[j] = a.bn_mean[col];
+                mul[j] = a.bn_gamma[col] / sqrtf(a.bn_var[col] + a.bn_eps);
+                beta[j] = a.bn_beta[col];
+            }
+            bias[j] = a.col_bias ? a.col_bias[(int64_t)g * a.N + col] : 0.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < T::TN; ++j) asm volatile("" : "+v"(mean[j]), "+v"(mul[j]), "+v"(beta[j]), "+v"(bias[j]));
 #pragma unroll
         for (int j = 0; j < T::TN; ++j) {
             const int col = n0 + wn * T::TN * 32 + j * 32 + il;
             if (col >= a.N) continue;
-            const int ecol = ex_lds[T::BM + col - n0];
-            float mean = 0.0f, mul = 1.0f, beta = 0.0f;
-            if (BN_EPILOGUE) {
-                mean = a.bn_mean[col];
-                mul = a.bn_gamma[col] / sqrtf(a.bn_var[col] + a.bn_eps);
-                beta = a.bn_beta[col];
-            }
-            const float bias = a.col_bias ? a.col_bias[(int64_t)g * a.N + col] : 0.0f;
 #pragma unroll
             for (int i = 0; i < T::TM; ++i) {
 #pragma unroll
@@ -548,9 +560,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, int tm, int tn, int
                     for (int e = 0; e < 4; ++e) {
                         const int row = rb + e;
                         if (row < a.M) {
-                            float c = __builtin_ldexpf(acc[i][j][v4 * 4 + e], -(er[e] + ecol));
-                            if (BN_EPILOGUE) c = (c - mean) * mul + beta;
-                            if (a.col_bias) c += bias;
+                            float c = __builtin_ldexpf(acc[i][j][v4 * 4 + e], -(er[e] + ecol[j]));
+                            if (BN_EPILOGUE) c = (c - mean[j]) * mul[j] + beta[j];
+                            if (a.col_bias) c += bias[j];
                             __builtin_nontemporal_store(c, &C[(int64_t)row * a.ldc + col]);
                         }
                     }
@@ -1010,28 +1022,29 @@ __global__ __launch_bounds__(256) void fold_kernel(const float *wq, const float 
 }
 
 // A plain A operand's rows, exponents and fp16 pieces in one pass (the
-// folded lookup's x): one workgroup of four waves per half group (16 rows).
-// First each wave takes four rows' largest magnitudes (every load of a
-// 1024-wide block in flight before the maxima) and their exponents (to
-// exp_out and LDS); then it writes the half group's share of the pieces as
-// split_rows_kernel lays them out -- two chunks per wave at a time, lane l
-// splitting row l % 16 of the half, k = 16 c + 8 ((l / 16) % 2) .. + 7 of
-// chunk c = c0 + l / 32, into the lane slot that row and k half have in the
-// 32-row group (16-lane runs of 256 bytes).  Rows past M get exponent 0 and
-// zero pieces.
+// folded lookup's x): one workgroup of four waves per quarter group (8 rows,
+// four workgroups per 32-row group, so a call of a few thousand rows still
+// gives every CU several workgroups).  First each wave takes two rows'
+// largest magnitudes (every load of a 1024-wide block in flight before the
+// maxima) and their exponents (to exp_out and LDS); then it writes the
+// quarter's share of the pieces as split_rows_kernel lays them out -- four
+// chunks per wave at a time, lane l splitting row l % 8 of the quarter,
+// k = 16 c + 8 ((l / 8) % 2) .. + 7 of chunk c = c0 + l / 16, into the lane
+// slot that row and k half have in the 32-row group (8-lane runs of one
+// 128-byte line).  Rows past M get exponent 0 and zero pieces.
 __global__ __launch_bounds__(256) void exp_split_rows_kernel(const float *A, int64_t lda, int M, int K,
                                                              int32_t *exp_out, u4 *out)
 {
-    __shared__ int ex_lds[16];
-    const int grp = blockIdx.x >> 1, half = blockIdx.x & 1;
+    __shared__ int ex_lds[8];
+    const int grp = blockIdx.x >> 2, quarter = blockIdx.x & 3;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int row0 = grp * 32 + half * 16;
-    const int r0 = row0 + wave * 4;
-    float mx[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    const int row0 = grp * 32 + quarter * 8;
+    const int r0 = row0 + wave * 2;
+    float mx[2] = {0.0f, 0.0f};
     for (int base = 0; base < K; base += 1024) {
-        fx4 v[4][4];
+        fx4 v[2][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int c = base + 256 * q + 4 * lane;
@@ -1039,33 +1052,33 @@ __global__ __launch_bounds__(256) void exp_split_rows_kernel(const float *A, int
                                               : fx4{0.0f, 0.0f, 0.0f, 0.0f};
             }
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 mx[i] = fmaxf(fmaxf(mx[i], fmaxf(fabsf(v[i][q][0]), fabsf(v[i][q][1]))),
                               fmaxf(fabsf(v[i][q][2]), fabsf(v[i][q][3])));
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 2; ++i) {
         const float m = wave_max(mx[i]);
         if (lane == i) {
             const int e = r0 + i < M ? row_exponent(m) : 0;
-            ex_lds[wave * 4 + i] = e;
+            ex_lds[wave * 2 + i] = e;
             if (r0 + i < M) exp_out[r0 + i] = e;
         }
     }
     __syncthreads();
-    const int kch = K / kBK, rr = lane & 15, kh = (lane >> 4) & 1, ci = lane >> 5;
-    const int row = row0 + rr, slot = kh * 32 + half * 16 + rr;
+    const int kch = K / kBK, rr = lane & 7, kh = (lane >> 3) & 1, ci = lane >> 4;
+    const int row = row0 + rr, slot = kh * 32 + quarter * 8 + rr;
     const int ex = ex_lds[rr];
     float one = 1.0f;
     asm volatile("" : "+v"(one));
-    // the waves take pairs of chunks in turn, four pairs' loads in flight
-    for (int p0 = wave; 2 * p0 < kch; p0 += 16) {
+    // the waves take quads of chunks in turn, four quads' loads in flight
+    for (int p0 = wave; 4 * p0 < kch; p0 += 16) {
         fx4 v[4][2];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int c = 2 * (p0 + 4 * i) + ci;
+            const int c = 4 * (p0 + 4 * i) + ci;
             v[i][0] = v[i][1] = fx4{0.0f, 0.0f, 0.0f, 0.0f};
             if (row < M && c < kch) {
                 const float *src = A + (int64_t)row * lda + c * kBK + kh * 8;
@@ -1075,7 +1088,7 @@ __global__ __launch_bounds__(256) void exp_split_rows_kernel(const float *A, int
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int c = 2 * (p0 + 4 * i) + ci;
+            const int c = 4 * (p0 + 4 * i) + ci;
             if (c < kch) {
                 u4 hi, lo;
                 split8(v[i], ex, one, hi, lo);
@@ -1235,7 +1248,7 @@ hipError_t launch_exp_split(const float *A, int64_t lda, int M, int K, int32_t *
     if (K % 32 != 0 || lda % 4 != 0 || (reinterpret_cast<uintptr_t>(A) & 15) != 0 ||
         (reinterpret_cast<uintptr_t>(out) & 15) != 0)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL(exp_split_rows_kernel, dim3((unsigned)((M + 31) / 32 * 2)), dim3(256), 0, stream, A, lda, M, K,
+    hipLaunchKernelGGL(exp_split_rows_kernel, dim3((unsigned)((M + 31) / 32 * 4)), dim3(256), 0, stream, A, lda, M, K,
                        exp_out, reinterpret_cast<u4 *>(out));
     return hipGetLastError();
 }
