@@ -955,70 +955,75 @@ __global__ __launch_bounds__(256) void split_rows_kernel(const float *B, const f
 //   M[g][j][i] = sum_f C[g][j][f] m_f Wq[h][f][i],
 //   bias[g][j] = sum_f C[g][j][f] (beta_f - mean_f m_f),
 // f over the half's D/2 features (C = the half's subkeys).  Accumulated in
-// fp64 from the fp32 parameters and rounded once to fp32.  64 x 64 tiles of
-// (j, i), 256 threads of 4 x 4 outputs, f in steps of 16 through LDS.
+// fp64 from the fp32 parameters, f in order, and rounded once to fp32.
+// 128 x 128 tiles of (j, i), 256 threads of 8 x 8 outputs (rows
+// j0 + 16 r + ty, columns i0 + 16 c + tx, so the LDS reads of a wave are
+// consecutive), f in steps of 16 through LDS with the step's m_f and
+// beta_f - mean_f m_f computed once; the i = 0 tiles also sum the bias.
 __global__ __launch_bounds__(256) void fold_kernel(const float *wq, const float *mean, const float *var,
                                                    const float *gamma, const float *beta, double eps,
                                                    const float *sub, int D, int n, float *M, float *bias)
 {
     const int g = blockIdx.z, h = g >> 1, p = g & 1, half = D / 2;
-    const int j0 = blockIdx.y * 64, i0 = blockIdx.x * 64;
+    const int j0 = blockIdx.y * 128, i0 = blockIdx.x * 128;
     const int f_base = h * D + p * half;  // the half's first feature in [H][D]
     const float *C = sub + (int64_t)g * n * half;
-    __shared__ double As[16][65];  // [f][j]: C[j][f] m_f
-    __shared__ double Bs[16][65];  // [f][i]: Wq[h][f][i]
+    __shared__ double As[16][129];     // [f][j]: C[j][f] m_f
+    __shared__ double Bs[16][129];     // [f][i]: Wq[h][f][i]
+    __shared__ double ms[16], ts[16];  // m_f and beta_f - mean_f m_f of the step's features
     const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
-    double acc[4][4];
+    const bool with_bias = blockIdx.x == 0 && threadIdx.x < 128 && j0 + (int)threadIdx.x < n;
+    double acc[8][8], bsum = 0.0;
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int r = 0; r < 8; ++r)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc[r][c] = 0.0;
+        for (int c = 0; c < 8; ++c) acc[r][c] = 0.0;
     for (int f0 = 0; f0 < half; f0 += 16) {
-        for (int e = threadIdx.x; e < 1024; e += 256) {
+        if (threadIdx.x < 16) {
+            const int hf = f_base + f0 + threadIdx.x;
+            const double m = (double)gamma[hf] / sqrt((double)var[hf] + eps);
+            ms[threadIdx.x] = m;
+            ts[threadIdx.x] = (double)beta[hf] - (double)mean[hf] * m;
+        }
+        __syncthreads();
+        for (int e = threadIdx.x; e < 2048; e += 256) {
             const int jj = e / 16, ff = e % 16;  // C rows run along f
-            const int j = j0 + jj, f = f0 + ff;
-            double v = 0.0;
-            if (j < n) {
-                const int hf = f_base + f;
-                const double m = (double)gamma[hf] / sqrt((double)var[hf] + eps);
-                v = (double)C[(int64_t)j * half + f] * m;
-            }
-            As[ff][jj] = v;
-            const int ff2 = e / 64, ii = e % 64;  // Wq rows run along i
-            Bs[ff2][ii] = (double)wq[((int64_t)f_base + f0 + ff2) * D + i0 + ii];
+            const int j = j0 + jj;
+            As[ff][jj] = j < n ? (double)C[(int64_t)j * half + f0 + ff] * ms[ff] : 0.0;
+            const int ff2 = e / 128, ii = e % 128;  // Wq rows run along i
+            Bs[ff2][ii] = i0 + ii < D ? (double)wq[((int64_t)f_base + f0 + ff2) * D + i0 + ii] : 0.0;
+        }
+        if (with_bias) {
+            const float *crow = C + (int64_t)(j0 + threadIdx.x) * half + f0;
+#pragma unroll
+            for (int ff = 0; ff < 16; ++ff) bsum = fma((double)crow[ff], ts[ff], bsum);
         }
         __syncthreads();
 #pragma unroll
         for (int ff = 0; ff < 16; ++ff) {
-            double a[4], b[4];
+            double a[8], b[8];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) a[r] = As[ff][ty * 4 + r];
+            for (int r = 0; r < 8; ++r) a[r] = As[ff][16 * r + ty];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) b[c] = Bs[ff][tx * 4 + c];
+            for (int c = 0; c < 8; ++c) b[c] = Bs[ff][16 * c + tx];
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
+            for (int r = 0; r < 8; ++r)
 #pragma unroll
-                for (int c = 0; c < 4; ++c) acc[r][c] = fma(a[r], b[c], acc[r][c]);
+                for (int c = 0; c < 8; ++c) acc[r][c] = fma(a[r], b[c], acc[r][c]);
         }
         __syncthreads();
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int j = j0 + ty * 4 + r;
+    for (int r = 0; r < 8; ++r) {
+        const int j = j0 + 16 * r + ty;
         if (j >= n) continue;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) M[((int64_t)g * n + j) * D + i0 + tx * 4 + c] = (float)acc[r][c];
-    }
-    if (blockIdx.x == 0 && threadIdx.x < 64 && j0 + (int)threadIdx.x < n) {
-        const int j = j0 + threadIdx.x;
-        double b = 0.0;
-        for (int f = 0; f < half; ++f) {
-            const int hf = f_base + f;
-            const double m = (double)gamma[hf] / sqrt((double)var[hf] + eps);
-            b = fma((double)C[(int64_t)j * half + f], (double)beta[hf] - (double)mean[hf] * m, b);
+        for (int c = 0; c < 8; ++c) {
+            const int i = i0 + 16 * c + tx;
+            if (i < D) M[((int64_t)g * n + j) * D + i] = (float)acc[r][c];
         }
-        bias[(int64_t)g * n + j] = (float)b;
     }
+    if (with_bias) bias[(int64_t)g * n + j0 + threadIdx.x] = (float)bsum;
 }
 
 // A plain A operand's rows, exponents and fp16 pieces in one pass (the
@@ -1257,8 +1262,8 @@ hipError_t launch_fold(const float *wq, const float *mean, const float *var, con
                        float eps, const float *subkeys, int D, int H, int n, float *M, float *bias, hipStream_t stream)
 {
     if (D % 64 != 0 || D / 2 % 16 != 0 || H < 1 || n < 1 || 2 * H > 65535) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(fold_kernel, dim3(D / 64, (n + 63) / 64, 2 * H), dim3(256), 0, stream, wq, mean, var, gamma,
-                       beta, (double)eps, subkeys, D, n, M, bias);
+    hipLaunchKernelGGL(fold_kernel, dim3((D + 127) / 128, (n + 127) / 128, 2 * H), dim3(256), 0, stream, wq, mean, var,
+                       gamma, beta, (double)eps, subkeys, D, n, M, bias);
     return hipGetLastError();
 }
 
